@@ -1,0 +1,282 @@
+"""Seeded synthetic inputs for the low-rank latent-KV decode step.
+
+This module draws every random tensor that the GPU path and the CPU oracle
+consume, and nothing else: it holds none of the method's arithmetic (no
+quantisation, no reconstruction, no attention).  Both sides are always fed
+the very same tensors produced here.
+
+Random numbers come from SplitMix64 (Steele, Lea and Flood, "Fast splittable
+pseudorandom number generators", OOPSLA 2014), used as a counter-based
+generator: draw ``i`` of a stream with 64-bit key ``k`` is ``mix64(k + (i+1)·γ)``
+with γ = 0x9E3779B97F4A7C15, which is exactly the i-th output of a SplitMix64
+generator seeded with ``k``.  Normals use the Box–Muller transform in fp64
+(Box and Muller, 1958) on two consecutive draws, then rounding to fp32.
+Everything is written with torch int64/float64 elementwise ops so the same
+code runs on the CPU and on the GPU; int64 multiplication wraps modulo 2**64
+and the right shifts are made logical with a mask.
+
+The workload table (``WORKLOADS``) describes the five decode workloads: the
+shapes of LLaMA-7B-class attention layers as used by the WSVD and LASER
+vision-language-model decode experiments (image-prefix plus text contexts),
+with per-head rank-r factors ``W_h ≈ A_h B_h`` and latents ``c = x A_h``.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+GAMMA = 0x9E3779B97F4A7C15
+MIX1 = 0xBF58476D1CE4E5B9
+MIX2 = 0x94D049BB133111EB
+_U64 = (1 << 64) - 1
+
+
+def _s64(v: int) -> int:
+    """Two's-complement int64 view of an unsigned 64-bit constant."""
+    v &= _U64
+    return v - (1 << 64) if v >= (1 << 63) else v
+
+
+def mix64_int(z: int) -> int:
+    """SplitMix64 output function on a Python int (reference for the tensor version)."""
+    z &= _U64
+    z = ((z ^ (z >> 30)) * MIX1) & _U64
+    z = ((z ^ (z >> 27)) * MIX2) & _U64
+    return z ^ (z >> 31)
+
+
+def _lshr(z: torch.Tensor, k: int) -> torch.Tensor:
+    return (z >> k) & ((1 << (64 - k)) - 1)
+
+
+def mix64(z: torch.Tensor) -> torch.Tensor:
+    """SplitMix64 output function on an int64 tensor (bit pattern = uint64)."""
+    z = (z ^ _lshr(z, 30)) * _s64(MIX1)
+    z = (z ^ _lshr(z, 27)) * _s64(MIX2)
+    return z ^ _lshr(z, 31)
+
+
+def stream_key(seed: int, *ids: int) -> int:
+    """64-bit key of the stream named by ``(seed, *ids)``."""
+    k = mix64_int(seed + GAMMA)
+    for v in ids:
+        k = mix64_int(k + ((v + 1) * GAMMA))
+    return k
+
+
+def raw_draws(key: int, start: int, count: int, device="cpu") -> torch.Tensor:
+    """Draws ``start .. start+count-1`` of stream ``key`` as int64 bit patterns."""
+    i = torch.arange(start + 1, start + 1 + count, dtype=torch.int64, device=device)
+    return mix64(i * _s64(GAMMA) + _s64(key))
+
+
+def uniform53(z: torch.Tensor) -> torch.Tensor:
+    """Top 53 bits of a draw as a float64 in [0, 1)."""
+    return _lshr(z, 11).to(torch.float64) * (2.0 ** -53)
+
+
+_CHUNK = 1 << 24
+
+
+def normal(key: int, start: int, count: int, std: float = 1.0, device="cpu") -> torch.Tensor:
+    """Elements ``start .. start+count-1`` of a N(0, std²) stream, as fp32.
+
+    Element ``i`` uses draws ``2i`` and ``2i+1``:  sqrt(-2 ln U1) cos(2π U2)
+    with U1 in (0, 1] and U2 in [0, 1), evaluated in fp64, times ``std``,
+    rounded once to fp32.
+    """
+    out = torch.empty(count, dtype=torch.float32, device=device)
+    done = 0
+    while done < count:
+        n = min(_CHUNK, count - done)
+        z = raw_draws(key, 2 * (start + done), 2 * n, device).view(n, 2)
+        u1 = 1.0 - uniform53(z[:, 0])
+        u2 = uniform53(z[:, 1])
+        g = torch.sqrt(-2.0 * torch.log(u1)) * torch.cos((2.0 * math.pi) * u2)
+        out[done:done + n] = (g * std).to(torch.float32)
+        done += n
+    return out
+
+
+def uniform_index(key: int, start: int, count: int, n: int) -> List[int]:
+    """``count`` integers uniform on ``{0, .., n-1}``: floor(U53 · n)."""
+    u = uniform53(raw_draws(key, start, count))
+    return [int(math.floor(float(v) * n)) for v in u]
+
+
+# ---------------------------------------------------------------------------
+# Workloads
+# ---------------------------------------------------------------------------
+
+TAG_X, TAG_AK, TAG_AV, TAG_BK, TAG_BV, TAG_Q, TAG_OUTLIER, TAG_RANK = range(1, 9)
+
+QFMT_INT8 = 0   # symmetric int8, one fp32 scale per (token, head)
+QFMT_INT4 = 1   # symmetric int4, one fp16 scale per group of 32 ranks
+
+
+@dataclass
+class Workload:
+    """One synthetic decode workload (shapes, distributions, seed)."""
+    name: str
+    index: int
+    n_layers: int
+    batch: int
+    n_heads: int
+    head_dim: int
+    embed: int
+    qfmt: int
+    context: int          # tokens cached before the first decode step
+    prefix: int           # leading image-prefix tokens (x ~ N(0, prefix_var))
+    prefix_var: float
+    text_var: float
+    steps: int
+    n_outliers: int = 0   # x channels with std multiplied by outlier_scale
+    outlier_scale: float = 20.0
+    uniform_rank: Optional[int] = None   # rank of every head (K and V), or None = drawn
+    rank_choices: Tuple[int, ...] = ()
+    seed: int = 0
+    ranks_k: List[List[int]] = field(default_factory=list)
+    ranks_v: List[List[int]] = field(default_factory=list)
+
+    def __post_init__(self):
+        self.seed = 0x5EED0000 + self.index
+        if self.uniform_rank is not None:
+            self.ranks_k = [[self.uniform_rank] * self.n_heads for _ in range(self.n_layers)]
+            self.ranks_v = [[self.uniform_rank] * self.n_heads for _ in range(self.n_layers)]
+        else:
+            m = self.n_layers * self.n_heads
+            key = stream_key(self.seed, TAG_RANK)
+            idx = uniform_index(key, 0, 2 * m, len(self.rank_choices))
+            flat_k = [self.rank_choices[i] for i in idx[:m]]
+            flat_v = [self.rank_choices[i] for i in idx[m:]]
+            H = self.n_heads
+            self.ranks_k = [flat_k[l * H:(l + 1) * H] for l in range(self.n_layers)]
+            self.ranks_v = [flat_v[l * H:(l + 1) * H] for l in range(self.n_layers)]
+
+    @property
+    def capacity(self) -> int:
+        return self.context + self.steps
+
+    def x_std(self, t: int) -> float:
+        return math.sqrt(self.prefix_var if t < self.prefix else self.text_var)
+
+
+def _mk() -> List[Workload]:
+    return [
+        Workload("single-layer-b1-h8-r32-int8-ctx512", 0, n_layers=1, batch=1, n_heads=8,
+                 head_dim=128, embed=1024, qfmt=QFMT_INT8, context=512, prefix=0,
+                 prefix_var=1.0, text_var=1.0, steps=1, uniform_rank=32),
+        Workload("llama7b-layer-b16-r32-int8-ctx4096", 1, n_layers=1, batch=16, n_heads=32,
+                 head_dim=128, embed=4096, qfmt=QFMT_INT8, context=4096, prefix=576,
+                 prefix_var=1.5, text_var=1.0, steps=128, uniform_rank=32),
+        Workload("llama7b-layer-b64-r64-int4g32-ctx8192-outliers", 2, n_layers=1, batch=64,
+                 n_heads=32, head_dim=128, embed=4096, qfmt=QFMT_INT4, context=8192, prefix=576,
+                 prefix_var=1.5, text_var=1.0, steps=128, n_outliers=4, uniform_rank=64),
+        Workload("laser-32layer-b32-rank8to96-int8-ctx2048", 3, n_layers=32, batch=32,
+                 n_heads=32, head_dim=128, embed=4096, qfmt=QFMT_INT8, context=2048, prefix=576,
+                 prefix_var=1.5, text_var=1.0, steps=1,
+                 rank_choices=tuple(range(8, 97, 8))),
+        Workload("long-context-b8-r48-int4g32-ctx32768", 4, n_layers=1, batch=8, n_heads=32,
+                 head_dim=128, embed=4096, qfmt=QFMT_INT4, context=32768, prefix=2304,
+                 prefix_var=1.5, text_var=1.0, steps=64, uniform_rank=48),
+    ]
+
+
+WORKLOADS: List[Workload] = _mk()
+
+
+def workload(i: int) -> Workload:
+    return _mk()[i]
+
+
+# ---------------------------------------------------------------------------
+# Tensors of a workload
+# ---------------------------------------------------------------------------
+
+def outlier_channels(w: Workload, layer: int) -> List[int]:
+    """Distinct x channels whose std is scaled by ``outlier_scale`` (fixed per layer)."""
+    if w.n_outliers == 0:
+        return []
+    key = stream_key(w.seed, TAG_OUTLIER, layer)
+    chosen: List[int] = []
+    i = 0
+    while len(chosen) < w.n_outliers:
+        c = uniform_index(key, i, 1, w.embed)[0]
+        i += 1
+        if c not in chosen:
+            chosen.append(c)
+    return chosen
+
+
+def activations(w: Workload, layer: int, b: int, t0: int, t1: int, device="cpu") -> torch.Tensor:
+    """x[t0:t1] of batch row ``b`` at ``layer``: fp32 [t1-t0, E].
+
+    Tokens ``t < prefix`` are image-prefix tokens with variance ``prefix_var``,
+    the rest (including decode-step tokens) have ``text_var``.  Outlier
+    channels have their std multiplied by ``outlier_scale`` for every token.
+    """
+    E = w.embed
+    key = stream_key(w.seed, TAG_X, layer, b)
+    x = normal(key, t0 * E, (t1 - t0) * E, 1.0, device).view(t1 - t0, E)
+    scale = torch.full((t1 - t0, 1), math.sqrt(w.text_var), dtype=torch.float32, device=device)
+    npre = max(0, min(t1, w.prefix) - t0)
+    if npre > 0:
+        scale[:npre] = math.sqrt(w.prefix_var)
+    x = x * scale
+    oc = outlier_channels(w, layer)
+    if oc:
+        x[:, oc] *= w.outlier_scale
+    return x
+
+
+def down_factors(w: Workload, layer: int, kv: int, device="cpu") -> torch.Tensor:
+    """A for K (kv=0) or V (kv=1): fp32 [E, Σ_h r_h], head h in its own column block,
+    each A_h ~ N(0, 1/E) elementwise."""
+    ranks = w.ranks_k[layer] if kv == 0 else w.ranks_v[layer]
+    tag = TAG_AK if kv == 0 else TAG_AV
+    cols = []
+    for h, r in enumerate(ranks):
+        key = stream_key(w.seed, tag, layer, h)
+        cols.append(normal(key, 0, w.embed * r, 1.0 / math.sqrt(w.embed), device).view(w.embed, r))
+    return torch.cat(cols, dim=1)
+
+
+def up_factors(w: Workload, layer: int, kv: int, dtype=torch.bfloat16, device="cpu") -> torch.Tensor:
+    """B for K or V: [Σ_h r_h, d] with head h's r_h×d block B_h ~ N(0, 1/r_h),
+    drawn in fp32 and rounded to ``dtype``."""
+    ranks = w.ranks_k[layer] if kv == 0 else w.ranks_v[layer]
+    tag = TAG_BK if kv == 0 else TAG_BV
+    rows = []
+    for h, r in enumerate(ranks):
+        key = stream_key(w.seed, tag, layer, h)
+        rows.append(normal(key, 0, r * w.head_dim, 1.0 / math.sqrt(r), device).view(r, w.head_dim))
+    return torch.cat(rows, dim=0).to(dtype)
+
+
+def queries(w: Workload, layer: int, step: int, dtype=torch.bfloat16, device="cpu") -> torch.Tensor:
+    """q for one decode step: [B, H, d] ~ N(0, 1), rounded to ``dtype``."""
+    key = stream_key(w.seed, TAG_Q, layer, step)
+    n = w.batch * w.n_heads * w.head_dim
+    return normal(key, 0, n, 1.0, device).view(w.batch, w.n_heads, w.head_dim).to(dtype)
+
+
+def latents(w: Workload, layer: int, b: int, t0: int, t1: int,
+            a_k: torch.Tensor, a_v: torch.Tensor, device="cpu") -> Tuple[torch.Tensor, torch.Tensor]:
+    """fp32 latents c = x·A for tokens [t0, t1) of batch row ``b`` (K and V).
+
+    This is synthesis of the inputs (the projection that produces the cached
+    latents), done by a plain fp32 matmul; it is not part of the decode step.
+    """
+    x = activations(w, layer, b, t0, t1, device)
+    return x @ a_k, x @ a_v
+
+
+def head_offsets(ranks: Sequence[int]) -> List[int]:
+    out, acc = [], 0
+    for r in ranks:
+        out.append(acc)
+        acc += r
+    return out

@@ -1,0 +1,150 @@
+"""ctypes binding of the CPU oracle (``liblr_oracle.so``).
+
+TEST INFRASTRUCTURE: only ``tests/``, the package smoke check and the
+benchmark's CPU-baseline leg may import this module.  The GPU library never
+loads it, and it never loads the GPU library.
+
+The oracle computes the plain definition of the decode step of per-head
+low-rank attention over a quantised latent cache (WSVD page, "Fine-grained
+per-head SVD" and "System implementation (fused kernel)"; LASER page, "Hybrid
+SVD-quantisation", RTN): quantise each latent row, dequantise it, rebuild
+k_t = c~^K_t B^K_h and v_t = c~^V_t B^V_h, then softmax attention, in fp64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lr_oracle.cpp")
+_LIB_PATH = os.path.join(_HERE, "liblr_oracle.so")
+
+QFMT_INT8, QFMT_INT4, QFMT_NONE = 0, 1, 2
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with g++ (IEEE fp32/fp64, no contraction, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["g++", "-std=c++17", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC",
+               "-shared", "-o", tmp, _SRC]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        L = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        L.lro_f32_to_f16.argtypes = [ctypes.c_float]
+        L.lro_f32_to_f16.restype = ctypes.c_uint16
+        L.lro_f16_to_f32.argtypes = [ctypes.c_uint16]
+        L.lro_f16_to_f32.restype = ctypes.c_float
+        L.lro_quant_int8.argtypes = [P, ctypes.c_int, P, P]
+        L.lro_quant_int8.restype = None
+        L.lro_quant_int4.argtypes = [P, ctypes.c_int, P, P]
+        L.lro_quant_int4.restype = None
+        L.lro_attend.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_int, P, P, P, P, P, ctypes.c_double, P, P]
+        L.lro_attend.restype = ctypes.c_int
+        L.lro_attend_dequantised.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             P, P, P, P, P, ctypes.c_double, P, P]
+        L.lro_attend_dequantised.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def f32_to_f16_bits(x: float) -> int:
+    return int(lib().lro_f32_to_f16(ctypes.c_float(x)))
+
+
+def f16_bits_to_f32(h: int) -> float:
+    return float(lib().lro_f16_to_f32(ctypes.c_uint16(h)))
+
+
+def quant_int8(c: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Rows of ``c`` (fp32 [..., r]) -> (int8 values [..., r], fp32 scales [...])."""
+    c = np.ascontiguousarray(c, dtype=np.float32)
+    r = c.shape[-1]
+    rows = c.reshape(-1, r)
+    q = np.empty(rows.shape, dtype=np.int8)
+    s = np.empty(rows.shape[0], dtype=np.float32)
+    L = lib()
+    for i in range(rows.shape[0]):
+        L.lro_quant_int8(_ptr(rows[i]), r, _ptr(q[i]), s[i:i + 1].ctypes.data)
+    return q.reshape(c.shape), s.reshape(c.shape[:-1])
+
+
+def quant_int4(c: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Rows of ``c`` (fp32 [..., r]) -> (values in [-7, 7] as int8 [..., r],
+    fp16 scale bit patterns uint16 [..., ceil(r/32)])."""
+    c = np.ascontiguousarray(c, dtype=np.float32)
+    r = c.shape[-1]
+    ng = (r + 31) // 32
+    rows = c.reshape(-1, r)
+    q = np.empty(rows.shape, dtype=np.int8)
+    s = np.empty((rows.shape[0], ng), dtype=np.uint16)
+    L = lib()
+    for i in range(rows.shape[0]):
+        L.lro_quant_int4(_ptr(rows[i]), r, _ptr(q[i]), _ptr(s[i]))
+    return q.reshape(c.shape), s.reshape(c.shape[:-1] + (ng,))
+
+
+def attend(qfmt: int, ck: np.ndarray, cv: np.ndarray, q: np.ndarray, bk: np.ndarray,
+           bv: np.ndarray, scale: float, want_probs: bool = False):
+    """One attention unit: fp32 latents ck [T, rk], cv [T, rv]; q [d]; B^K [rk, d];
+    B^V [rv, d] (q and B widened exactly to fp64).  Returns o [d] (fp64), and the
+    softmax weights [T] when ``want_probs``."""
+    ck = np.ascontiguousarray(ck, dtype=np.float32)
+    cv = np.ascontiguousarray(cv, dtype=np.float32)
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    bk = np.ascontiguousarray(bk, dtype=np.float64)
+    bv = np.ascontiguousarray(bv, dtype=np.float64)
+    T, rk = ck.shape
+    T2, rv = cv.shape
+    d = q.shape[0]
+    assert T == T2 and bk.shape == (rk, d) and bv.shape == (rv, d)
+    out = np.zeros(d, dtype=np.float64)
+    probs = np.zeros(max(T, 1), dtype=np.float64) if want_probs else None
+    rc = lib().lro_attend(qfmt, T, rk, rv, d, _ptr(ck), _ptr(cv), _ptr(q), _ptr(bk), _ptr(bv),
+                          float(scale), _ptr(out), _ptr(probs) if want_probs else None)
+    if rc != 0:
+        raise ValueError("lro_attend rejected its arguments")
+    return (out, probs[:T]) if want_probs else out
+
+
+def attend_dequantised(ctk: np.ndarray, ctv: np.ndarray, q: np.ndarray, bk: np.ndarray,
+                       bv: np.ndarray, scale: float, want_probs: bool = False):
+    """One attention unit from already dequantised fp64 latents ctk [T, rk], ctv [T, rv]."""
+    ctk = np.ascontiguousarray(ctk, dtype=np.float64)
+    ctv = np.ascontiguousarray(ctv, dtype=np.float64)
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    bk = np.ascontiguousarray(bk, dtype=np.float64)
+    bv = np.ascontiguousarray(bv, dtype=np.float64)
+    T, rk = ctk.shape
+    T2, rv = ctv.shape
+    d = q.shape[0]
+    assert T == T2 and bk.shape == (rk, d) and bv.shape == (rv, d)
+    out = np.zeros(d, dtype=np.float64)
+    probs = np.zeros(max(T, 1), dtype=np.float64) if want_probs else None
+    rc = lib().lro_attend_dequantised(T, rk, rv, d, _ptr(ctk), _ptr(ctv), _ptr(q), _ptr(bk),
+                                      _ptr(bv), float(scale), _ptr(out),
+                                      _ptr(probs) if want_probs else None)
+    if rc != 0:
+        raise ValueError("lro_attend_dequantised rejected its arguments")
+    return (out, probs[:T]) if want_probs else out

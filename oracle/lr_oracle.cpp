@@ -1,0 +1,194 @@
+// lr_oracle.cpp -- CPU oracle for the decode step of per-head low-rank
+// attention over a quantised latent KV cache.
+//
+// TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT.  Only the tests, the package
+// smoke check and the benchmark's CPU-baseline leg may load this library.  It
+// shares no code, header, table or helper with the GPU library.
+//
+// It computes the plain definition, slowly and in the pages' order:
+//   * per head h, keys and values are kept only as rank-r latents c_t = x_t A_h
+//     (WSVD page, "Fine-grained per-head SVD": each head owns a small latent and
+//     its own factors, W_h ~ A_h B_h);
+//   * the latents are stored at low precision with round-to-nearest
+//     quantisation (LASER page, "Hybrid SVD-quantisation ... RTN"; WSVD page,
+//     "Quantisation": W8A8 / W8A4 activations);
+//   * at decode time K_h and V_h are rebuilt from the latents through B_h and
+//     ordinary softmax attention is taken: Q K^T, softmax, times V (WSVD page,
+//     "System implementation (fused kernel)": low-rank reconstruction followed
+//     by the QK product, softmax and V product).
+// It never uses the absorbed form, never tiles, never splits the context and
+// keeps every floating-point step after quantisation in fp64.  The quantiser
+// works in fp32 because its fp32 arithmetic is its definition:
+//   int8, per token:  m = max|c_i|, s = m / 127 (fp32 division),
+//                     q_i = clamp(rne(c_i / s), -127, 127), or 0 when s == 0.
+//   int4, group 32:   per group g of up to 32 consecutive ranks,
+//                     s_g = fp16_rne(m_g / 7), q_i = clamp(rne(c_i / s_g), -7, 7),
+//                     or 0 when s_g == 0 (also when m_g/7 underflows in fp16).
+// Readings of points the pages leave open (tie rule, clamp range, what is
+// divided, scale dtypes, group tail) are the plainest ones: round half to
+// even, symmetric ranges, division by the stored scale, fp32 per-token scale,
+// fp16 per-group scale, a short last group with its own scale.
+//
+// Build: g++ -O2 -fno-fast-math -ffp-contract=off -shared -fPIC (SSE math).
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+namespace {
+
+float clampf(float v, float lo, float hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+}  // namespace
+
+extern "C" {
+
+// IEEE-754 binary32 -> binary16, round to nearest, ties to even; subnormal
+// results are produced, magnitudes that round beyond 65504 give infinity, NaN
+// stays NaN.  Written from the format definition: a binary16 value is
+// (-1)^s * 2^(e-15) * (1 + f/1024) for 1 <= e <= 30, and 2^-14 * f/1024 for e = 0.
+uint16_t lro_f32_to_f16(float x) {
+  uint32_t bits;
+  std::memcpy(&bits, &x, 4);
+  const uint16_t sign = static_cast<uint16_t>((bits >> 16) & 0x8000u);
+  if (std::isnan(x)) return static_cast<uint16_t>(sign | 0x7e00u);
+  const double a = std::fabs(static_cast<double>(x));  // exact widening
+  if (std::isinf(x) || a >= 65520.0) return static_cast<uint16_t>(sign | 0x7c00u);
+  if (a < std::ldexp(1.0, -14)) {
+    // subnormal range: value = n * 2^-24, n = rne(a / 2^-24); n == 1024 is the
+    // smallest normal and has exactly that bit pattern.
+    const double n = std::nearbyint(a / std::ldexp(1.0, -24));
+    return static_cast<uint16_t>(sign | static_cast<uint16_t>(n));
+  }
+  int k;
+  (void)std::frexp(a, &k);            // a = f * 2^k, f in [0.5, 1)
+  int e = k - 1;                      // a in [2^e, 2^(e+1))
+  double n = std::nearbyint(a / std::ldexp(1.0, e - 10));  // in [1024, 2048]
+  if (n == 2048.0) { n = 1024.0; e += 1; }
+  if (e > 15) return static_cast<uint16_t>(sign | 0x7c00u);
+  return static_cast<uint16_t>(sign | ((e + 15) << 10) | (static_cast<int>(n) - 1024));
+}
+
+// binary16 -> binary32, exact.
+float lro_f16_to_f32(uint16_t h) {
+  const int s = (h >> 15) & 1, e = (h >> 10) & 0x1f, f = h & 0x3ff;
+  double v;
+  if (e == 0) v = std::ldexp(static_cast<double>(f), -24);
+  else if (e == 31) v = f ? NAN : INFINITY;
+  else v = std::ldexp(1024.0 + f, e - 25);
+  return static_cast<float>(s ? -v : v);
+}
+
+// Symmetric int8 quantisation of one latent row with one fp32 scale.
+void lro_quant_int8(const float* c, int r, int8_t* q, float* scale) {
+  float m = 0.0f;
+  for (int i = 0; i < r; ++i) m = std::fmax(m, std::fabs(c[i]));
+  const float s = m / 127.0f;
+  *scale = s;
+  for (int i = 0; i < r; ++i) {
+    if (s == 0.0f) { q[i] = 0; continue; }
+    q[i] = static_cast<int8_t>(clampf(std::nearbyint(c[i] / s), -127.0f, 127.0f));
+  }
+}
+
+// Symmetric int4 quantisation of one latent row, one fp16 scale per group of
+// 32 consecutive ranks (the last group may be shorter).  q holds one value
+// per element in [-7, 7]; scales holds ceil(r/32) binary16 bit patterns.
+void lro_quant_int4(const float* c, int r, int8_t* q, uint16_t* scales) {
+  for (int g = 0; g * 32 < r; ++g) {
+    const int lo = g * 32, hi = (lo + 32 < r) ? lo + 32 : r;
+    float m = 0.0f;
+    for (int i = lo; i < hi; ++i) m = std::fmax(m, std::fabs(c[i]));
+    const uint16_t sh = lro_f32_to_f16(m / 7.0f);
+    scales[g] = sh;
+    const float s = lro_f16_to_f32(sh);
+    for (int i = lo; i < hi; ++i) {
+      if (s == 0.0f) { q[i] = 0; continue; }
+      q[i] = static_cast<int8_t>(clampf(std::nearbyint(c[i] / s), -7.0f, 7.0f));
+    }
+  }
+}
+
+// Quantise and dequantise one row: out_i = scale * q_i in fp64 (exact).
+// qfmt: 0 = int8 per token, 1 = int4 group 32, 2 = no quantisation (out = c).
+static void dequantised_row(int qfmt, const float* c, int r, double* out) {
+  if (qfmt == 2) {
+    for (int i = 0; i < r; ++i) out[i] = static_cast<double>(c[i]);
+    return;
+  }
+  std::vector<int8_t> q(r);
+  if (qfmt == 0) {
+    float s;
+    lro_quant_int8(c, r, q.data(), &s);
+    for (int i = 0; i < r; ++i) out[i] = static_cast<double>(s) * q[i];
+  } else {
+    std::vector<uint16_t> sc((r + 31) / 32);
+    lro_quant_int4(c, r, q.data(), sc.data());
+    for (int i = 0; i < r; ++i) out[i] = static_cast<double>(lro_f16_to_f32(sc[i / 32])) * q[i];
+  }
+}
+
+// One attention unit (one layer, one sequence, one head) over T tokens whose
+// latents are already dequantised (fp64):
+//   ctk [T][rk], ctv [T][rv]   dequantised latents c~^K_t, c~^V_t
+//   q  [d]                     query
+//   bk [rk][d], bv [rv][d]     up-projection factors B^K_h, B^V_h
+//   out [d]                    o = sum_t p_t v_t
+//   probs [T] (optional)       the softmax weights p_t
+// k_t = c~^K_t B^K and v_t = c~^V_t B^V are rebuilt explicitly, one token at a
+// time; z_t = (q . k_t) * scale; p = softmax(z), taken as exp(z_t - max z)
+// over the sum of the same; o = sum_t p_t v_t.  T == 0 gives o = 0.
+// Returns 0, or -1 on bad sizes.
+int lro_attend_dequantised(int T, int rk, int rv, int d, const double* ctk, const double* ctv,
+                           const double* q, const double* bk, const double* bv, double scale,
+                           double* out, double* probs) {
+  if (T < 0 || rk < 1 || rv < 1 || d < 1) return -1;
+  for (int j = 0; j < d; ++j) out[j] = 0.0;
+  if (T == 0) return 0;
+
+  std::vector<double> vec(d), z(T);
+  for (int t = 0; t < T; ++t) {
+    const double* c = ctk + static_cast<size_t>(t) * rk;
+    for (int j = 0; j < d; ++j) {           // k_t = c~ B^K
+      double acc = 0.0;
+      for (int i = 0; i < rk; ++i) acc += c[i] * bk[static_cast<size_t>(i) * d + j];
+      vec[j] = acc;
+    }
+    double dot = 0.0;
+    for (int j = 0; j < d; ++j) dot += q[j] * vec[j];
+    z[t] = dot * scale;
+  }
+  double zmax = z[0];
+  for (int t = 1; t < T; ++t) zmax = z[t] > zmax ? z[t] : zmax;
+  double denom = 0.0;
+  for (int t = 0; t < T; ++t) denom += std::exp(z[t] - zmax);
+  for (int t = 0; t < T; ++t) {
+    const double p = std::exp(z[t] - zmax) / denom;
+    if (probs) probs[t] = p;
+    const double* c = ctv + static_cast<size_t>(t) * rv;
+    for (int j = 0; j < d; ++j) {           // v_t = c~ B^V, accumulated with weight p_t
+      double acc = 0.0;
+      for (int i = 0; i < rv; ++i) acc += c[i] * bv[static_cast<size_t>(i) * d + j];
+      out[j] += p * acc;
+    }
+  }
+  return 0;
+}
+
+// The same unit from fp32 latents ck [T][rk], cv [T][rv]: every row is first
+// quantised with qfmt (0 = int8 per token, 1 = int4 group 32, 2 = none) and
+// dequantised, then lro_attend_dequantised runs.  Returns 0, or -1.
+int lro_attend(int qfmt, int T, int rk, int rv, int d, const float* ck, const float* cv,
+               const double* q, const double* bk, const double* bv, double scale,
+               double* out, double* probs) {
+  if (T < 0 || rk < 1 || rv < 1 || d < 1 || qfmt < 0 || qfmt > 2) return -1;
+  std::vector<double> ctk(static_cast<size_t>(T) * rk), ctv(static_cast<size_t>(T) * rv);
+  for (int t = 0; t < T; ++t) {
+    dequantised_row(qfmt, ck + static_cast<size_t>(t) * rk, rk, ctk.data() + static_cast<size_t>(t) * rk);
+    dequantised_row(qfmt, cv + static_cast<size_t>(t) * rv, rv, ctv.data() + static_cast<size_t>(t) * rv);
+  }
+  return lro_attend_dequantised(T, rk, rv, d, ctk.data(), ctv.data(), q, bk, bv, scale, out, probs);
+}
+
+}  // extern "C"

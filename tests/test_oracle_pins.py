@@ -1,0 +1,319 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Nothing here compares the oracle with itself: each test checks it against a
+hand-derived value (``tests/golden``), an independent library routine
+(numpy's binary16 conversion, numpy's SVD), a closed form, or brute force,
+chosen so that a dropped term, a wrong sign or index, a transposed factor or
+a wrong rounding rule fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _val(v):
+    return math.ldexp(v[0], v[1]) if isinstance(v, list) else float(v)
+
+
+# --------------------------------------------------------------------------
+# binary16 conversion (used for the int4 group scales)
+# --------------------------------------------------------------------------
+
+def test_fp16_golden_encodings():
+    cases = json.load(open(os.path.join(GOLD, "fp16_rne.json")))["cases"]
+    for c in cases:
+        x = math.ldexp(c["m"], c["e"])
+        assert oracle.f32_to_f16_bits(x) == int(c["bits"], 16), c["why"]
+
+
+def test_fp16_matches_numpy_on_random_and_tie_values():
+    rng = np.random.default_rng(7)
+    mags = rng.standard_normal(20000) * np.exp2(rng.integers(-30, 18, 20000))
+    # exact ties: odd multiples of half an ulp at several binades, and in the subnormal range
+    ties = []
+    for e in range(-24, 16):
+        ulp = math.ldexp(1.0, max(e - 10, -24))
+        base = math.ldexp(1.0, e)
+        for k in range(1, 8):
+            ties.append(base + (2 * k + 1) * ulp / 2)
+    xs = np.concatenate([mags, np.array(ties), -np.array(ties)]).astype(np.float32)
+    xs = xs[np.isfinite(xs)]
+    with np.errstate(over="ignore"):
+        ref = xs.astype(np.float16).view(np.uint16)
+    mine = np.array([oracle.f32_to_f16_bits(float(v)) for v in xs], dtype=np.uint16)
+    assert np.array_equal(ref, mine)
+
+
+def test_fp16_decode_all_finite_patterns():
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = bits.view(np.float16)
+    finite = np.isfinite(vals)
+    ref = vals[finite].astype(np.float32)
+    mine = np.array([oracle.f16_bits_to_f32(int(b)) for b in bits[finite]], dtype=np.float32)
+    assert np.array_equal(ref.view(np.uint32), mine.view(np.uint32))
+
+
+# --------------------------------------------------------------------------
+# Quantisers
+# --------------------------------------------------------------------------
+
+QUANT = json.load(open(os.path.join(GOLD, "quant_cases.json")))
+
+
+@pytest.mark.parametrize("case", QUANT["int8"], ids=lambda c: c["name"])
+def test_quant_int8_golden(case):
+    row = np.array([_val(v) for v in case["row"]], dtype=np.float32)
+    q, s = oracle.quant_int8(row[None])
+    assert q[0].tolist() == case["q"], case["why"]
+    if case["scale"] == "m/127":
+        want = np.float32(np.abs(row).max()) / np.float32(127.0)
+    else:
+        want = np.array([int(case["scale"], 16)], dtype=np.uint32).view(np.float32)[0]
+    assert s[0].view(np.uint32) == np.float32(want).view(np.uint32)
+
+
+@pytest.mark.parametrize("case", QUANT["int4"], ids=lambda c: c["name"])
+def test_quant_int4_golden(case):
+    row = np.array([_val(v) for v in case["row"]], dtype=np.float32)
+    q, s = oracle.quant_int4(row[None])
+    assert q[0].tolist() == case["q"], case["why"]
+    assert [int(x) for x in s[0]] == [int(h, 16) for h in case["scale"]]
+
+
+def _rows(n, r, seed):
+    rng = np.random.default_rng(seed)
+    c = rng.standard_normal((n, r)) * np.exp2(rng.integers(-6, 6, (n, 1)))
+    return c.astype(np.float32)
+
+
+@pytest.mark.parametrize("r", [8, 32, 40, 96, 128])
+def test_quant_int8_error_bound_and_extremes(r):
+    c = _rows(300, r, r)
+    q, s = oracle.quant_int8(c)
+    m = np.abs(c).max(axis=1)
+    # the scale is the binary32 quotient m/127
+    assert np.array_equal(s, (m.astype(np.float32) / np.float32(127.0)).astype(np.float32))
+    # the largest-magnitude element maps to +-127 with its sign
+    idx = np.abs(c).argmax(axis=1)
+    assert np.array_equal(q[np.arange(len(c)), idx], np.sign(c[np.arange(len(c)), idx]) * 127)
+    # round-to-nearest: |s*q - c| <= s/2 (fp64, exact products), codes inside [-127, 127]
+    err = np.abs(s[:, None].astype(np.float64) * q - c.astype(np.float64))
+    assert np.all(err <= s[:, None].astype(np.float64) * (0.5 + 1e-6))
+    assert q.min() >= -127 and q.max() <= 127
+
+
+@pytest.mark.parametrize("r", [8, 32, 48, 64, 96, 128])
+def test_quant_int4_error_bound_and_groups(r):
+    c = _rows(300, r, 100 + r)
+    q, sb = oracle.quant_int4(c)
+    ng = (r + 31) // 32
+    assert sb.shape == (300, ng)
+    s = sb.view(np.float16).astype(np.float64)
+    for g in range(ng):
+        lo, hi = 32 * g, min(r, 32 * g + 32)
+        m = np.abs(c[:, lo:hi]).max(axis=1)
+        # each group's scale is the binary16 value nearest m/7 (numpy's conversion)
+        want = (m.astype(np.float32) / np.float32(7.0)).astype(np.float16)
+        assert np.array_equal(sb[:, g], want.view(np.uint16))
+        err = np.abs(s[:, g:g + 1] * q[:, lo:hi] - c[:, lo:hi].astype(np.float64))
+        # |c/s| <= 7 (1 + 2^-10), so rounding stays within half a step and never clamps
+        assert np.all(err <= s[:, g:g + 1] * (0.5 + 1e-6))
+    assert q.min() >= -7 and q.max() <= 7
+
+
+def test_quant_groups_are_independent():
+    c = _rows(1, 64, 3)
+    c2 = c.copy()
+    c2[0, 40] = 1000.0  # inflates group 1 only
+    q1, s1 = oracle.quant_int4(c)
+    q2, s2 = oracle.quant_int4(c2)
+    assert np.array_equal(q1[0, :32], q2[0, :32]) and s1[0, 0] == s2[0, 0]
+    assert s1[0, 1] != s2[0, 1]
+
+
+# --------------------------------------------------------------------------
+# Attention
+# --------------------------------------------------------------------------
+
+def _dense_mha(X, WK, WV, q, scale):
+    """softmax(q (X W_K)^T * scale) (X W_V) for one head, brute force fp64."""
+    K = X @ WK
+    V = X @ WV
+    z = (K @ q) * scale
+    e = np.exp(z - z.max())
+    p = e / e.sum()
+    return p @ V
+
+
+@pytest.mark.parametrize("T", [1, 2, 5, 7])
+def test_full_rank_unquantised_equals_dense_mha(T):
+    """At r = d with no quantisation, c_t = x_t A_h and k_t = c_t B_h rebuild
+    x_t W_h exactly (W_h = A_h B_h from its SVD), so the oracle must equal
+    dense multi-head attention (E=16, 2 heads, d=8)."""
+    rng = np.random.default_rng(11 + T)
+    E, H, d = 16, 2, 8
+    X = rng.standard_normal((T, E))
+    WK = rng.standard_normal((E, H * d)) / 4
+    WV = rng.standard_normal((E, H * d)) / 4
+    Q = rng.standard_normal((H, d))
+    scale = 1 / math.sqrt(d)
+    for h in range(H):
+        wk, wv = WK[:, h * d:(h + 1) * d], WV[:, h * d:(h + 1) * d]
+        fac = []
+        for w in (wk, wv):
+            U, S, Vt = np.linalg.svd(w, full_matrices=False)
+            A = U * np.sqrt(S)              # E x d
+            B = np.sqrt(S)[:, None] * Vt    # d x d
+            fac.append((A, B))
+        (AK, BK), (AV, BV) = fac
+        got = oracle.attend_dequantised(X @ AK, X @ AV, Q[h], BK, BV, scale)
+        want = _dense_mha(X, wk, wv, Q[h], scale)
+        assert np.max(np.abs(got - want)) <= 1e-12 * max(1.0, np.max(np.abs(want)))
+
+
+def test_eckart_young_truncation_error():
+    """Per-head factors from a rank-r truncated SVD of a random W_h (E x d):
+    rows of A_r B_r are rebuilt through the oracle's value path (T = 1, latent =
+    row of A_r, so o = v_0 = c B^V), and ||W - A_r B_r||_F must equal
+    sqrt(sum of the dropped sigma_i^2); the spectral error must equal sigma_{r+1}."""
+    rng = np.random.default_rng(5)
+    E, d = 24, 16
+    W = rng.standard_normal((E, d))
+    U, S, Vt = np.linalg.svd(W, full_matrices=False)
+    q = rng.standard_normal(d)
+    for r in range(1, d):
+        A = U[:, :r] * np.sqrt(S[:r])
+        B = np.sqrt(S[:r])[:, None] * Vt[:r]
+        Wr = np.stack([
+            oracle.attend_dequantised(A[j:j + 1], A[j:j + 1], q, B, B, 0.1) for j in range(E)])
+        fro = np.linalg.norm(W - Wr)
+        assert abs(fro - math.sqrt(np.sum(S[r:] ** 2))) <= 1e-10 * np.linalg.norm(W)
+        spec = np.linalg.norm(W - Wr, 2)
+        assert abs(spec - S[r]) <= 1e-10 * S[0]
+
+
+def _unit(T, rk, rv, d, seed):
+    rng = np.random.default_rng(seed)
+    ck = rng.standard_normal((T, rk)).astype(np.float32)
+    cv = rng.standard_normal((T, rv)).astype(np.float32)
+    q = rng.standard_normal(d)
+    bk = rng.standard_normal((rk, d)) / math.sqrt(rk)
+    bv = rng.standard_normal((rv, d)) / math.sqrt(rv)
+    return ck, cv, q, bk, bv
+
+
+@pytest.mark.parametrize("qfmt", [oracle.QFMT_INT8, oracle.QFMT_INT4, oracle.QFMT_NONE])
+def test_softmax_weights_sum_to_one(qfmt):
+    ck, cv, q, bk, bv = _unit(37, 32, 48, 128, 1)
+    _, p = oracle.attend(qfmt, ck, cv, q, bk, bv, 1 / math.sqrt(128), want_probs=True)
+    assert abs(p.sum() - 1.0) <= 1e-12 and np.all(p > 0)
+
+
+def test_single_token_returns_its_value():
+    ck, cv, q, bk, bv = _unit(1, 16, 16, 32, 2)
+    o = oracle.attend(oracle.QFMT_NONE, ck, cv, q, bk, bv, 0.3)
+    assert np.max(np.abs(o - cv[0].astype(np.float64) @ bv)) <= 1e-13
+
+
+def test_zero_query_gives_mean_value():
+    ck, cv, q, bk, bv = _unit(9, 16, 24, 32, 3)
+    o = oracle.attend(oracle.QFMT_NONE, ck, cv, np.zeros_like(q), bk, bv, 0.3)
+    want = (cv.astype(np.float64) @ bv).mean(axis=0)
+    assert np.max(np.abs(o - want)) <= 1e-13
+
+
+def test_token_permutation_invariance():
+    ck, cv, q, bk, bv = _unit(23, 32, 32, 64, 4)
+    perm = np.random.default_rng(0).permutation(23)
+    for qfmt in (oracle.QFMT_INT8, oracle.QFMT_INT4):
+        a = oracle.attend(qfmt, ck, cv, q, bk, bv, 0.125)
+        b = oracle.attend(qfmt, ck[perm], cv[perm], q, bk, bv, 0.125)
+        assert np.max(np.abs(a - b)) <= 1e-13
+
+
+def test_hand_worked_two_token_example():
+    """d = 2, r = 1.  B^K = [[ln 3, 0]], q = [1, 0], scale 1: with latents
+    c^K = (1, 0) the scores are (ln 3, 0), so p = (3/4, 1/4).  B^V = [[0, 1]]
+    and c^V = (4, 8) give v = ((0, 4), (0, 8)), hence o = (0, 3 + 2) = (0, 5)."""
+    o, p = oracle.attend_dequantised(np.array([[1.0], [0.0]]), np.array([[4.0], [8.0]]),
+                                     np.array([1.0, 0.0]), np.array([[math.log(3.0), 0.0]]),
+                                     np.array([[0.0, 1.0]]), 1.0, want_probs=True)
+    assert np.allclose(p, [0.75, 0.25], atol=1e-15, rtol=0)
+    assert np.allclose(o, [0.0, 5.0], atol=1e-14, rtol=0)
+
+
+def test_scale_multiplies_scores():
+    """Doubling the softmax scale equals doubling q."""
+    ck, cv, q, bk, bv = _unit(15, 16, 16, 32, 9)
+    a = oracle.attend(oracle.QFMT_INT8, ck, cv, q, bk, bv, 0.4)
+    b = oracle.attend(oracle.QFMT_INT8, ck, cv, 2 * q, bk, bv, 0.2)
+    assert np.max(np.abs(a - b)) <= 1e-13
+
+
+def _dequant(qfmt, c):
+    if qfmt == oracle.QFMT_INT8:
+        q, s = oracle.quant_int8(c)
+        return q.astype(np.float64) * s[:, None].astype(np.float64)
+    q, sb = oracle.quant_int4(c)
+    s = sb.view(np.float16).astype(np.float64)
+    return q.astype(np.float64) * np.repeat(s, 32, axis=1)[:, :c.shape[1]]
+
+
+@pytest.mark.parametrize("qfmt", [oracle.QFMT_INT8, oracle.QFMT_INT4])
+def test_quantised_attend_is_dequantise_then_attend(qfmt):
+    ck, cv, q, bk, bv = _unit(40, 48, 64, 128, 21)
+    a = oracle.attend(qfmt, ck, cv, q, bk, bv, 1 / math.sqrt(128))
+    b = oracle.attend_dequantised(_dequant(qfmt, ck), _dequant(qfmt, cv), q, bk, bv, 1 / math.sqrt(128))
+    assert np.array_equal(a, b)
+
+
+def test_absorbed_form_equals_explicit_oracle():
+    """The GPU computes q' = scale q B^K^T, scores s_t = q' . c~^K_t, and
+    o = (sum_t p_t c~^V_t) B^V.  In fp64 this must equal the oracle's explicit
+    reconstruction."""
+    for qfmt in (oracle.QFMT_INT8, oracle.QFMT_INT4):
+        ck, cv, q, bk, bv = _unit(300, 32, 48, 128, 31 + qfmt)
+        scale = 1 / math.sqrt(128)
+        ctk, ctv = _dequant(qfmt, ck), _dequant(qfmt, cv)
+        qp = scale * (bk @ q)
+        s = ctk @ qp
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        o = (p @ ctv) @ bv
+        ref = oracle.attend(qfmt, ck, cv, q, bk, bv, scale)
+        assert np.max(np.abs(o - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_split_context_merge_equals_unsplit():
+    """Flash-Decoding style partials (m_j, l_j, u_j) over any split of [0, T),
+    merged with m = max m_j, l = sum e^(m_j - m) l_j, u = sum e^(m_j - m) u_j,
+    give the unsplit result u / l."""
+    ck, cv, q, bk, bv = _unit(257, 32, 32, 64, 41)
+    scale = 0.125
+    ctk, ctv = _dequant(oracle.QFMT_INT8, ck), _dequant(oracle.QFMT_INT8, cv)
+    s = ctk @ (scale * (bk @ q))
+    ref = oracle.attend(oracle.QFMT_INT8, ck, cv, q, bk, bv, scale)
+    for cuts in ([0, 257], [0, 1, 257], [0, 64, 128, 192, 257], [0, 100, 101, 256, 257]):
+        parts = []
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            m = s[a:b].max()
+            e = np.exp(s[a:b] - m)
+            parts.append((m, e.sum(), e @ ctv[a:b]))
+        M = max(p[0] for p in parts)
+        L = sum(math.exp(p[0] - M) * p[1] for p in parts)
+        U = sum(math.exp(p[0] - M) * p[2] for p in parts)
+        o = (U / L) @ bv
+        assert np.max(np.abs(o - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_empty_context_gives_zero():
+    o = oracle.attend(oracle.QFMT_INT8, np.zeros((0, 8), np.float32), np.zeros((0, 8), np.float32),
+                      np.ones(16), np.ones((8, 16)), np.ones((8, 16)), 0.25)
+    assert np.array_equal(o, np.zeros(16))
