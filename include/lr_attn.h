@@ -1,0 +1,196 @@
+/* lr_attn.h -- C ABI of the MI355X (gfx950) library for the decode step of
+ * per-head low-rank attention over a quantised latent KV cache.
+ *
+ * The operation (WSVD page, "Fine-grained per-head SVD" and "System
+ * implementation (fused kernel)"; LASER page, "Hybrid SVD-quantisation" and
+ * "Loss-aware cross-layer rank allocation"): for layer l and head h the K and
+ * V projections are factorised per head, W^K_h ~ A^K_h B^K_h and
+ * W^V_h ~ A^V_h B^V_h, with A (E x r) and B (r x d).  The cache keeps only the
+ * per-head latents c^K_t = x_t A^K_h and c^V_t = x_t A^V_h, quantised
+ * round-to-nearest to int8 or int4.  A decode step rebuilds
+ * k_t = c~^K_t B^K_h, v_t = c~^V_t B^V_h and returns
+ *     o = softmax_t(scale * q . k_t) v_t
+ * over the cached tokens.  Ranks may differ per (layer, head) and between K
+ * and V (LASER's non-uniform rank allocation).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor arguments are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or synchronises, and never keeps a pointer.
+ *   - Every argument error is detected on the host before any launch and is
+ *     returned as a status; nothing is launched in that case.
+ *   - Launches are asynchronous on `stream` (a hipStream_t; NULL is the
+ *     default stream).  A failed launch returns LR_EHIP; the HIP error code
+ *     is then available from lr_attn_last_hip_error() on the same thread.
+ *   - A plan is immutable after creation and may be shared between threads.
+ *   - head_dim must be 128; 1 <= n_heads <= 128; every rank r satisfies
+ *     8 <= r <= 128 and r % 8 == 0.
+ */
+#ifndef LR_ATTN_H
+#define LR_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LR_OK = 0,
+  LR_EINVAL = 1,        /* bad argument: null pointer, bad size, misalignment */
+  LR_EUNSUPPORTED = 2,  /* valid but unsupported: head_dim != 128, rank rules */
+  LR_ERANGE = 3,        /* index or length out of range (layer, head, max_len) */
+  LR_EWORKSPACE = 4,    /* workspace missing or smaller than required */
+  LR_EHIP = 5           /* a HIP launch failed */
+} lr_status;
+
+/* Latent quantisation formats (LASER page, round-to-nearest quantisation;
+ * WSVD page, W8A8 / W8A4 activations).  Both are symmetric:
+ *   LR_Q_INT8_TOKEN: one fp32 scale s = max|c| / 127 per (token, head, K or V);
+ *                    codes clamp(rne(c / s), -127, 127), 0 when s == 0.
+ *   LR_Q_INT4_G32:   one fp16 scale s_g = fp16(max|c| / 7) per group of 32
+ *                    consecutive ranks (the last group may be 8, 16 or 24);
+ *                    codes clamp(rne(c / s_g), -7, 7), 0 when s_g == 0. */
+typedef enum { LR_Q_INT8_TOKEN = 0, LR_Q_INT4_G32 = 1 } lr_qfmt;
+
+/* Element type of q, the B factors and the output. */
+typedef enum { LR_DT_BF16 = 0, LR_DT_F32 = 1 } lr_dtype;
+
+#define LR_HEAD_DIM 128
+#define LR_MAX_HEADS 128
+#define LR_MAX_RANK 128
+#define LR_TILE_TOKENS 64
+
+typedef struct lr_attn_desc {
+  int32_t n_layers;      /* >= 1 */
+  int32_t batch;         /* B >= 1 */
+  int32_t n_heads;       /* H, 1..128 */
+  int32_t head_dim;      /* d, must be 128 */
+  int32_t capacity;      /* token slots per sequence, 1..16777216 */
+  int32_t qfmt;          /* lr_qfmt */
+  int32_t io_dtype;      /* lr_dtype of q, B^K, B^V and out */
+  int32_t max_splits;    /* 0 = automatic; n >= 1 caps the context splits per (b, h) */
+  const int32_t* rank_k; /* HOST [n_layers * n_heads], row-major (layer, head) */
+  const int32_t* rank_v; /* HOST [n_layers * n_heads] */
+} lr_attn_desc;
+
+typedef struct lr_attn_plan lr_attn_plan; /* opaque */
+
+/* Byte layout of one head's latent planes inside a layer's cache buffer.
+ * For head h and sequence b the K plane starts at
+ *     k_offset + b * plane_bytes_k
+ * and holds ceil(capacity / 64) tiles of tile_bytes_k bytes; token slot t
+ * lives in tile t / 64 at lane i = t % 64.  Inside a tile the row bytes come
+ * first, split in chunks of 16 bytes (the last chunk may be shorter, width
+ * w = row_bytes - 16 * c): chunk c of lane i is at 1024 * c + w_c * i.  int8
+ * codes are two's-complement bytes, rank index = 16 * c + byte.  int4 codes are
+ * two's-complement nibbles, rank index = 32 * c + 2 * byte (low nibble) or
+ * + 1 (high nibble).  The scales follow the rows at 64 * row_bytes: int8 one
+ * fp32 at + 4 * i; int4 fp16 per group g at + 2 * (64 * g + i).  V is the same
+ * with the _v fields. */
+typedef struct lr_attn_head_layout {
+  uint64_t k_offset, v_offset;         /* bytes from the cache base, 256-aligned */
+  uint64_t plane_bytes_k, plane_bytes_v;
+  int32_t rank_k, rank_v;
+  int32_t row_bytes_k, row_bytes_v;    /* code bytes per token */
+  int32_t scale_bytes_k, scale_bytes_v;/* scale bytes per token */
+  int32_t tile_bytes_k, tile_bytes_v;  /* 64 * (row_bytes + scale_bytes) */
+  int32_t latent_offset_k;             /* first element of head h in a token's K latent vector */
+  int32_t latent_offset_v;             /* ... and in a token's V latent vector */
+  int64_t factor_offset_k;             /* first element of B^K_h (r_k x d, row-major) in the K factor tensor */
+  int64_t factor_offset_v;
+} lr_attn_head_layout;
+
+/* Validate `desc` and build a host-only plan (no device memory is touched).
+ * Errors: LR_EINVAL (null desc/out/rank pointers, non-positive sizes, bad
+ * enum), LR_EUNSUPPORTED (head_dim != 128, n_heads > 128, rank not in
+ * {8, 16, ..., 128}), LR_ERANGE (capacity beyond 2^24). */
+lr_status lr_attn_plan_create(const lr_attn_desc* desc, lr_attn_plan** out);
+void lr_attn_plan_destroy(lr_attn_plan* plan);
+
+/* Bytes of one layer's cache buffer (0 on a bad plan or layer).  The caller
+ * allocates it with 256-byte alignment; its contents are only read at slots
+ * below len[b]. */
+size_t lr_attn_cache_bytes(const lr_attn_plan* plan, int32_t layer);
+/* Elements per token of the K (kv = 0) or V (kv = 1) latent vector of a
+ * layer: sum over heads of r_h (0 on bad arguments). */
+size_t lr_attn_latent_elems(const lr_attn_plan* plan, int32_t layer, int32_t kv);
+/* Elements of the K or V factor tensor of a layer: sum_h r_h * d.  Head h's
+ * B_h is the row-major r_h x d block at factor_offset (0 on bad arguments). */
+size_t lr_attn_factor_elems(const lr_attn_plan* plan, int32_t layer, int32_t kv);
+/* Layout of head `head` of layer `layer`.  Errors: LR_EINVAL, LR_ERANGE. */
+lr_status lr_attn_head_layout_get(const lr_attn_plan* plan, int32_t layer, int32_t head,
+                                  lr_attn_head_layout* out);
+
+/* Workspace bytes needed by lr_attn_decode for any layer when called with
+ * this max_len (0 means none is needed; the size is a multiple of 256).
+ * It holds per-(b, h) arrival counters and split-context partials (m, l, u)
+ * of Flash-Decoding-style context splitting. */
+size_t lr_attn_workspace_bytes(const lr_attn_plan* plan, int32_t max_len);
+/* Zero the workspace counters with a small kernel on `stream`.  Call it once
+ * after allocating a workspace; every completed decode call leaves the
+ * counters at zero again.  Errors: LR_EINVAL, LR_EHIP. */
+lr_status lr_attn_workspace_init(const lr_attn_plan* plan, void* workspace, size_t ws_bytes,
+                                 void* stream);
+
+/* Quantise fp32 latents and write them at token slots pos[b] .. pos[b]+n_new-1
+ * of every head of layer `layer` (LASER page, "System implementation": fused
+ * quantisation of the latent activations; WSVD page, per-head latents).
+ *   cache   device, lr_attn_cache_bytes(layer) bytes, 256-aligned
+ *   ck, cv  device fp32 [batch][n_new][latent_elems(kv)], 16-aligned; head h's
+ *           latent of a token is the r_h elements at latent_offset(h)
+ *   pos     device int32 [batch]; slots outside [0, capacity) are skipped
+ *   n_new   tokens per sequence, 0..capacity (0 is a no-op)
+ * The cache is only written; lengths are not tracked by the library.  The
+ * quantised codes and scales are bit-exact with the definition given at
+ * lr_qfmt (correctly rounded fp32 division, round-half-even, fp16 RNE).
+ * Errors: LR_EINVAL, LR_ERANGE, LR_EHIP. */
+lr_status lr_attn_append_latent(const lr_attn_plan* plan, int32_t layer, void* cache,
+                                const float* ck, const float* cv, const int32_t* pos,
+                                int32_t n_new, void* stream);
+
+/* One decode step of layer `layer` for every (b, h):
+ *     out[b][h][:] = sum_t p_t v_t,  p = softmax_t(softmax_scale * q[b][h] . k_t),
+ * over token slots t < len[b], with k_t = c~^K_t B^K_h and v_t = c~^V_t B^V_h
+ * rebuilt from the cache (WSVD page, "System implementation": reconstruction
+ * plus Flash-Decoding QK^T, softmax and PV in one kernel, with nothing rebuilt
+ * written to memory).  This entry point uses the absorbed form
+ * q' = softmax_scale * q B^K_h^T scored against the latents and applies B^V_h
+ * once to the accumulated latent, which is algebraically identical.
+ *   cache       device, written by lr_attn_append_latent
+ *   len         device int32 [batch]; values are clamped to [0, max_len]; a
+ *               sequence with len 0 gets a zero output
+ *   max_len     host upper bound of len[], 1..capacity; sizes the launch
+ *   q           device [batch][n_heads][128] io_dtype
+ *   bk, bv      device factor tensors (lr_attn_factor_elems) io_dtype
+ *   out         device [batch][n_heads][128] io_dtype
+ *   workspace   device, >= lr_attn_workspace_bytes(max_len) bytes, prepared
+ *               once by lr_attn_workspace_init; may be NULL when that is 0.
+ *               Concurrent calls must not share a workspace.
+ * All pointers 16-aligned.  Errors: LR_EINVAL, LR_ERANGE, LR_EWORKSPACE, LR_EHIP. */
+lr_status lr_attn_decode(const lr_attn_plan* plan, int32_t layer, const void* cache,
+                         const int32_t* len, int32_t max_len, const void* q, const void* bk,
+                         const void* bv, float softmax_scale, void* out, void* workspace,
+                         size_t ws_bytes, void* stream);
+
+/* The same result through explicit per-token reconstruction: every k_t and
+ * v_t (d = 128 values) is rebuilt on chip with matrix-core products of the
+ * dequantised latents and B_h, then scored and accumulated (WSVD page,
+ * "System implementation": K_h rebuilt in an on-chip buffer).  Same arguments,
+ * rules and errors as lr_attn_decode; it needs no workspace beyond what
+ * lr_attn_workspace_bytes reports. */
+lr_status lr_attn_decode_explicit(const lr_attn_plan* plan, int32_t layer, const void* cache,
+                                  const int32_t* len, int32_t max_len, const void* q,
+                                  const void* bk, const void* bv, float softmax_scale, void* out,
+                                  void* workspace, size_t ws_bytes, void* stream);
+
+/* Static description of a status. */
+const char* lr_attn_strerror(lr_status status);
+/* hipError_t of the last call on this thread that returned LR_EHIP (0 if none). */
+int32_t lr_attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LR_ATTN_H */

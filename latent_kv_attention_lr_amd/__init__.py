@@ -1,0 +1,179 @@
+"""Thin Python binding of ``liblr_attn.so`` (the C ABI in ``include/lr_attn.h``).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of the library.  Functions keep the C names; tensor arguments are
+torch tensors on the GPU (only their device pointers are passed), streams
+default to torch's current stream.  If the library has not been built the
+import fails: there is no other implementation to fall back to.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblr_attn.so")
+
+LR_OK, LR_EINVAL, LR_EUNSUPPORTED, LR_ERANGE, LR_EWORKSPACE, LR_EHIP = range(6)
+LR_Q_INT8_TOKEN, LR_Q_INT4_G32 = 0, 1
+LR_DT_BF16, LR_DT_F32 = 0, 1
+LR_HEAD_DIM = 128
+LR_TILE_TOKENS = 64
+
+
+class LrAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lr_attn_strerror(status)
+        if status == LR_EHIP:
+            msg += f" (hipError {lr_attn_last_hip_error()})"
+        super().__init__(f"{where}: {msg} [status {status}]")
+
+
+class lr_attn_desc(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("capacity", ctypes.c_int32), ("qfmt", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("max_splits", ctypes.c_int32),
+                ("rank_k", ctypes.POINTER(ctypes.c_int32)),
+                ("rank_v", ctypes.POINTER(ctypes.c_int32))]
+
+
+class lr_attn_head_layout(ctypes.Structure):
+    _fields_ = [("k_offset", ctypes.c_uint64), ("v_offset", ctypes.c_uint64),
+                ("plane_bytes_k", ctypes.c_uint64), ("plane_bytes_v", ctypes.c_uint64),
+                ("rank_k", ctypes.c_int32), ("rank_v", ctypes.c_int32),
+                ("row_bytes_k", ctypes.c_int32), ("row_bytes_v", ctypes.c_int32),
+                ("scale_bytes_k", ctypes.c_int32), ("scale_bytes_v", ctypes.c_int32),
+                ("tile_bytes_k", ctypes.c_int32), ("tile_bytes_v", ctypes.c_int32),
+                ("latent_offset_k", ctypes.c_int32), ("latent_offset_v", ctypes.c_int32),
+                ("factor_offset_k", ctypes.c_int64), ("factor_offset_v", ctypes.c_int64)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -c 'import __graft_entry__ as g; g.build()'` "
+                          "or `python latent_kv_attention_lr_amd/build.py`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    plan_pp = ctypes.POINTER(ctypes.c_void_p)
+    sig = {
+        "lr_attn_plan_create": (ctypes.c_int, [ctypes.POINTER(lr_attn_desc), plan_pp]),
+        "lr_attn_plan_destroy": (None, [P]),
+        "lr_attn_cache_bytes": (SZ, [P, I32]),
+        "lr_attn_latent_elems": (SZ, [P, I32, I32]),
+        "lr_attn_factor_elems": (SZ, [P, I32, I32]),
+        "lr_attn_head_layout_get": (ctypes.c_int, [P, I32, I32, ctypes.POINTER(lr_attn_head_layout)]),
+        "lr_attn_workspace_bytes": (SZ, [P, I32]),
+        "lr_attn_workspace_init": (ctypes.c_int, [P, P, SZ, P]),
+        "lr_attn_append_latent": (ctypes.c_int, [P, I32, P, P, P, P, I32, P]),
+        "lr_attn_decode": (ctypes.c_int, [P, I32, P, P, I32, P, P, P, ctypes.c_float, P, P, SZ, P]),
+        "lr_attn_decode_explicit": (ctypes.c_int, [P, I32, P, P, I32, P, P, P, ctypes.c_float, P, P, SZ, P]),
+        "lr_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+        "lr_attn_last_hip_error": (I32, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
+
+
+_lib = _load()
+
+
+def _ptr(x) -> Optional[int]:
+    """Device pointer of a tensor, or an int/None passed through."""
+    if x is None or isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str) -> None:
+    if status != LR_OK:
+        raise LrAttnError(status, where)
+
+
+def lr_attn_strerror(status: int) -> str:
+    return _lib.lr_attn_strerror(status).decode()
+
+
+def lr_attn_last_hip_error() -> int:
+    return int(_lib.lr_attn_last_hip_error())
+
+
+def lr_attn_plan_create(n_layers: int, batch: int, n_heads: int, capacity: int, qfmt: int,
+                        io_dtype: int, rank_k: Sequence[int], rank_v: Sequence[int],
+                        head_dim: int = LR_HEAD_DIM, max_splits: int = 0) -> int:
+    """Returns an opaque plan handle (int); raises LrAttnError on a bad description."""
+    n = n_layers * n_heads
+    rk = (ctypes.c_int32 * max(n, 1))(*[int(r) for r in rank_k])
+    rv = (ctypes.c_int32 * max(n, 1))(*[int(r) for r in rank_v])
+    d = lr_attn_desc(n_layers, batch, n_heads, head_dim, capacity, qfmt, io_dtype, max_splits,
+                     ctypes.cast(rk, ctypes.POINTER(ctypes.c_int32)),
+                     ctypes.cast(rv, ctypes.POINTER(ctypes.c_int32)))
+    h = ctypes.c_void_p()
+    _check(_lib.lr_attn_plan_create(ctypes.byref(d), ctypes.byref(h)), "lr_attn_plan_create")
+    return h.value
+
+
+def lr_attn_plan_destroy(plan: int) -> None:
+    _lib.lr_attn_plan_destroy(plan)
+
+
+def lr_attn_cache_bytes(plan: int, layer: int) -> int:
+    return int(_lib.lr_attn_cache_bytes(plan, layer))
+
+
+def lr_attn_latent_elems(plan: int, layer: int, kv: int) -> int:
+    return int(_lib.lr_attn_latent_elems(plan, layer, kv))
+
+
+def lr_attn_factor_elems(plan: int, layer: int, kv: int) -> int:
+    return int(_lib.lr_attn_factor_elems(plan, layer, kv))
+
+
+def lr_attn_head_layout_get(plan: int, layer: int, head: int) -> Dict[str, int]:
+    out = lr_attn_head_layout()
+    _check(_lib.lr_attn_head_layout_get(plan, layer, head, ctypes.byref(out)), "lr_attn_head_layout_get")
+    return {name: getattr(out, name) for name, _ in lr_attn_head_layout._fields_}
+
+
+def lr_attn_workspace_bytes(plan: int, max_len: int) -> int:
+    return int(_lib.lr_attn_workspace_bytes(plan, max_len))
+
+
+def lr_attn_workspace_init(plan: int, workspace, ws_bytes: int, stream=None) -> None:
+    _check(_lib.lr_attn_workspace_init(plan, _ptr(workspace), ws_bytes, _stream(stream)),
+           "lr_attn_workspace_init")
+
+
+def lr_attn_append_latent(plan: int, layer: int, cache, ck, cv, pos, n_new: int, stream=None) -> None:
+    _check(_lib.lr_attn_append_latent(plan, layer, _ptr(cache), _ptr(ck), _ptr(cv), _ptr(pos),
+                                      n_new, _stream(stream)), "lr_attn_append_latent")
+
+
+def lr_attn_decode(plan: int, layer: int, cache, length, max_len: int, q, bk, bv,
+                   softmax_scale: float, out, workspace, ws_bytes: int, stream=None) -> None:
+    _check(_lib.lr_attn_decode(plan, layer, _ptr(cache), _ptr(length), max_len, _ptr(q), _ptr(bk),
+                               _ptr(bv), softmax_scale, _ptr(out), _ptr(workspace), ws_bytes,
+                               _stream(stream)), "lr_attn_decode")
+
+
+def lr_attn_decode_explicit(plan: int, layer: int, cache, length, max_len: int, q, bk, bv,
+                            softmax_scale: float, out, workspace, ws_bytes: int, stream=None) -> None:
+    _check(_lib.lr_attn_decode_explicit(plan, layer, _ptr(cache), _ptr(length), max_len, _ptr(q),
+                                        _ptr(bk), _ptr(bv), softmax_scale, _ptr(out),
+                                        _ptr(workspace), ws_bytes, _stream(stream)),
+           "lr_attn_decode_explicit")

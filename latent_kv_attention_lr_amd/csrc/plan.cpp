@@ -1,0 +1,246 @@
+// plan.cpp -- host side of the C ABI: plan construction, layout queries,
+// argument validation and the context-split policy.  Nothing here touches the
+// GPU except through the launchers in kernels.hip.
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <numeric>
+
+#include "plan.h"
+
+namespace {
+
+thread_local int32_t g_last_hip = 0;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool rank_ok(int32_t r) { return r >= 8 && r <= LR_MAX_RANK && r % 8 == 0; }
+
+lr_status hip_status(int err) {
+  if (err == 0) return LR_OK;
+  g_last_hip = err;
+  return LR_EHIP;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+namespace lr {
+
+Split choose_split(const lr_attn_plan& p, int32_t max_len) {
+  // Flash-Decoding style: split each (b, h) context into equal runs of tiles so
+  // that the launch has enough work-groups to fill 256 CUs, but keep at least
+  // two tiles per wavefront so the per-group prologue (q' from B^K) and the
+  // partial merge stay small next to the streamed bytes.
+  Split s;
+  s.waves = 4;
+  const int64_t units = static_cast<int64_t>(p.desc.batch) * p.desc.n_heads;
+  const int64_t tiles = ceil_div(max_len, kTile);
+  const int64_t target_groups = 2048;
+  int64_t n = ceil_div(target_groups, units);
+  n = std::min<int64_t>(n, ceil_div(tiles, 2 * s.waves));
+  if (p.desc.max_splits > 0) n = std::min<int64_t>(n, p.desc.max_splits);
+  n = std::max<int64_t>(n, 1);
+  const int64_t tps = ceil_div(tiles, n);
+  s.tiles_per_split = static_cast<int32_t>(tps);
+  s.n_split = static_cast<int32_t>(ceil_div(tiles, tps));
+  return s;
+}
+
+size_t workspace_bytes(const lr_attn_plan& p, int32_t max_len) {
+  const Split s = choose_split(p, max_len);
+  if (s.n_split <= 1) return 0;
+  const size_t units = static_cast<size_t>(p.desc.batch) * p.desc.n_heads;
+  const size_t counters = (units * 4 + 255) / 256 * 256;
+  const size_t parts = units * s.n_split * kPartStride * sizeof(float);
+  return counters + (parts + 255) / 256 * 256;
+}
+
+}  // namespace lr
+
+extern "C" {
+
+lr_status lr_attn_plan_create(const lr_attn_desc* d, lr_attn_plan** out) {
+  if (!d || !out) return LR_EINVAL;
+  *out = nullptr;
+  if (!d->rank_k || !d->rank_v) return LR_EINVAL;
+  if (d->n_layers < 1 || d->batch < 1 || d->n_heads < 1 || d->capacity < 1) return LR_EINVAL;
+  if (d->qfmt != LR_Q_INT8_TOKEN && d->qfmt != LR_Q_INT4_G32) return LR_EINVAL;
+  if (d->io_dtype != LR_DT_BF16 && d->io_dtype != LR_DT_F32) return LR_EINVAL;
+  if (d->max_splits < 0) return LR_EINVAL;
+  if (d->head_dim != LR_HEAD_DIM) return LR_EUNSUPPORTED;
+  if (d->n_heads > LR_MAX_HEADS) return LR_EUNSUPPORTED;
+  if (d->capacity > (1 << 24)) return LR_ERANGE;
+  if (static_cast<int64_t>(d->batch) * d->n_heads > (1 << 24)) return LR_ERANGE;
+  const int64_t n = static_cast<int64_t>(d->n_layers) * d->n_heads;
+  for (int64_t i = 0; i < n; ++i)
+    if (!rank_ok(d->rank_k[i]) || !rank_ok(d->rank_v[i])) return LR_EUNSUPPORTED;
+
+  lr_attn_plan* p = new (std::nothrow) lr_attn_plan();
+  if (!p) return LR_EINVAL;
+  p->desc = *d;
+  p->desc.rank_k = nullptr;
+  p->desc.rank_v = nullptr;
+  p->n_tiles = lr::n_tiles(d->capacity);
+  const int H = d->n_heads;
+  p->layers.resize(d->n_layers);
+  for (int l = 0; l < d->n_layers; ++l) {
+    auto& L = p->layers[l];
+    std::memset(&L.tab, 0, sizeof(L.tab));
+    L.heads.resize(H);
+    uint64_t off = 0;
+    int32_t lk = 0, lv = 0;
+    L.rk_max = L.rv_max = 0;
+    for (int h = 0; h < H; ++h) {
+      const int rk = d->rank_k[static_cast<int64_t>(l) * H + h];
+      const int rv = d->rank_v[static_cast<int64_t>(l) * H + h];
+      auto& hl = L.heads[h];
+      hl.rank_k = rk;
+      hl.rank_v = rv;
+      hl.row_bytes_k = lr::row_bytes(d->qfmt, rk);
+      hl.row_bytes_v = lr::row_bytes(d->qfmt, rv);
+      hl.scale_bytes_k = lr::scale_bytes(d->qfmt, rk);
+      hl.scale_bytes_v = lr::scale_bytes(d->qfmt, rv);
+      hl.tile_bytes_k = lr::tile_bytes(d->qfmt, rk);
+      hl.tile_bytes_v = lr::tile_bytes(d->qfmt, rv);
+      hl.plane_bytes_k = static_cast<uint64_t>(p->n_tiles) * hl.tile_bytes_k;
+      hl.plane_bytes_v = static_cast<uint64_t>(p->n_tiles) * hl.tile_bytes_v;
+      hl.latent_offset_k = lk;
+      hl.latent_offset_v = lv;
+      hl.factor_offset_k = static_cast<int64_t>(lk) * LR_HEAD_DIM;
+      hl.factor_offset_v = static_cast<int64_t>(lv) * LR_HEAD_DIM;
+      hl.k_offset = off;
+      off += (hl.plane_bytes_k * d->batch + lr::kRegionAlign - 1) / lr::kRegionAlign * lr::kRegionAlign;
+      hl.v_offset = off;
+      off += (hl.plane_bytes_v * d->batch + lr::kRegionAlign - 1) / lr::kRegionAlign * lr::kRegionAlign;
+      if (off / lr::kRegionAlign > 0xffffffffull) { delete p; return LR_ERANGE; }
+      L.tab.kreg[h] = static_cast<uint32_t>(hl.k_offset / lr::kRegionAlign);
+      L.tab.vreg[h] = static_cast<uint32_t>(hl.v_offset / lr::kRegionAlign);
+      L.tab.loff_k[h] = static_cast<uint16_t>(lk);
+      L.tab.loff_v[h] = static_cast<uint16_t>(lv);
+      L.tab.rk[h] = static_cast<uint8_t>(rk);
+      L.tab.rv[h] = static_cast<uint8_t>(rv);
+      lk += rk;
+      lv += rv;
+      L.rk_max = std::max(L.rk_max, rk);
+      L.rv_max = std::max(L.rv_max, rv);
+    }
+    L.sum_rk = lk;
+    L.sum_rv = lv;
+    L.cache_bytes = off;
+    // Heavy heads (more bytes per token) are dispatched first so the tail of
+    // the launch is made of light work-groups (non-uniform ranks).
+    std::vector<int> order(H);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+      const int wa = L.heads[a].tile_bytes_k + L.heads[a].tile_bytes_v;
+      const int wb = L.heads[b].tile_bytes_k + L.heads[b].tile_bytes_v;
+      return wa > wb;
+    });
+    for (int i = 0; i < H; ++i) L.tab.order[i] = static_cast<uint8_t>(order[i]);
+  }
+  *out = p;
+  return LR_OK;
+}
+
+void lr_attn_plan_destroy(lr_attn_plan* p) { delete p; }
+
+size_t lr_attn_cache_bytes(const lr_attn_plan* p, int32_t layer) {
+  if (!p || layer < 0 || layer >= p->desc.n_layers) return 0;
+  return p->layers[layer].cache_bytes;
+}
+
+size_t lr_attn_latent_elems(const lr_attn_plan* p, int32_t layer, int32_t kv) {
+  if (!p || layer < 0 || layer >= p->desc.n_layers || (kv != 0 && kv != 1)) return 0;
+  return static_cast<size_t>(kv == 0 ? p->layers[layer].sum_rk : p->layers[layer].sum_rv);
+}
+
+size_t lr_attn_factor_elems(const lr_attn_plan* p, int32_t layer, int32_t kv) {
+  return lr_attn_latent_elems(p, layer, kv) * LR_HEAD_DIM;
+}
+
+lr_status lr_attn_head_layout_get(const lr_attn_plan* p, int32_t layer, int32_t head,
+                                  lr_attn_head_layout* out) {
+  if (!p || !out) return LR_EINVAL;
+  if (layer < 0 || layer >= p->desc.n_layers || head < 0 || head >= p->desc.n_heads)
+    return LR_ERANGE;
+  *out = p->layers[layer].heads[head];
+  return LR_OK;
+}
+
+size_t lr_attn_workspace_bytes(const lr_attn_plan* p, int32_t max_len) {
+  if (!p || max_len < 1 || max_len > p->desc.capacity) return 0;
+  return lr::workspace_bytes(*p, max_len);
+}
+
+lr_status lr_attn_workspace_init(const lr_attn_plan* p, void* ws, size_t ws_bytes, void* stream) {
+  if (!p || !ws || ws_bytes == 0 || !aligned(ws, 16)) return LR_EINVAL;
+  return hip_status(lr::launch_workspace_init(ws, ws_bytes, stream));
+}
+
+lr_status lr_attn_append_latent(const lr_attn_plan* p, int32_t layer, void* cache, const float* ck,
+                                const float* cv, const int32_t* pos, int32_t n_new, void* stream) {
+  if (!p) return LR_EINVAL;
+  if (layer < 0 || layer >= p->desc.n_layers) return LR_ERANGE;
+  if (n_new < 0) return LR_EINVAL;
+  if (n_new > p->desc.capacity) return LR_ERANGE;
+  if (!cache || !ck || !cv || !pos) return LR_EINVAL;
+  if (!aligned(cache, 256) || !aligned(ck, 16) || !aligned(cv, 16) || !aligned(pos, 4))
+    return LR_EINVAL;
+  if (n_new == 0) return LR_OK;
+  return hip_status(lr::launch_append(*p, layer, cache, ck, cv, pos, n_new, stream));
+}
+
+static lr_status decode_common(const lr_attn_plan* p, int32_t layer, const void* cache,
+                               const int32_t* len, int32_t max_len, const void* q,
+                               const void* bk, const void* bv, float scale, void* out,
+                               void* ws, size_t ws_bytes, void* stream, bool explicit_form) {
+  if (!p) return LR_EINVAL;
+  if (layer < 0 || layer >= p->desc.n_layers) return LR_ERANGE;
+  if (max_len < 1 || max_len > p->desc.capacity) return LR_ERANGE;
+  if (!cache || !len || !q || !bk || !bv || !out) return LR_EINVAL;
+  if (!std::isfinite(scale)) return LR_EINVAL;
+  if (!aligned(cache, 256) || !aligned(len, 4) || !aligned(q, 16) || !aligned(bk, 16) ||
+      !aligned(bv, 16) || !aligned(out, 16))
+    return LR_EINVAL;
+  const size_t need = lr::workspace_bytes(*p, max_len);
+  if (need > 0 && (!ws || ws_bytes < need)) return LR_EWORKSPACE;
+  if (ws && !aligned(ws, 16)) return LR_EINVAL;
+  return hip_status(lr::launch_decode(*p, layer, cache, len, max_len, q, bk, bv, scale, out,
+                                      need > 0 ? ws : nullptr, stream, explicit_form));
+}
+
+lr_status lr_attn_decode(const lr_attn_plan* p, int32_t layer, const void* cache,
+                         const int32_t* len, int32_t max_len, const void* q, const void* bk,
+                         const void* bv, float scale, void* out, void* ws, size_t ws_bytes,
+                         void* stream) {
+  return decode_common(p, layer, cache, len, max_len, q, bk, bv, scale, out, ws, ws_bytes, stream,
+                       false);
+}
+
+lr_status lr_attn_decode_explicit(const lr_attn_plan* p, int32_t layer, const void* cache,
+                                  const int32_t* len, int32_t max_len, const void* q,
+                                  const void* bk, const void* bv, float scale, void* out,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  return decode_common(p, layer, cache, len, max_len, q, bk, bv, scale, out, ws, ws_bytes, stream,
+                       true);
+}
+
+const char* lr_attn_strerror(lr_status s) {
+  switch (s) {
+    case LR_OK: return "ok";
+    case LR_EINVAL: return "invalid argument";
+    case LR_EUNSUPPORTED: return "unsupported configuration";
+    case LR_ERANGE: return "index or length out of range";
+    case LR_EWORKSPACE: return "workspace missing or too small";
+    case LR_EHIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t lr_attn_last_hip_error(void) { return g_last_hip; }
+
+}  // extern "C"

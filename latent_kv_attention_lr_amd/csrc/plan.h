@@ -1,0 +1,43 @@
+// plan.h -- internal: the plan object and the launch functions the C ABI calls.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "layout.h"
+
+struct lr_attn_plan {
+  lr_attn_desc desc;                 // copy; rank pointers cleared
+  int32_t n_tiles;                   // tiles per plane = ceil(capacity / 64)
+  struct Layer {
+    lr::HeadTab tab;
+    std::vector<lr_attn_head_layout> heads;
+    size_t cache_bytes;
+    int32_t sum_rk, sum_rv, rk_max, rv_max;
+  };
+  std::vector<Layer> layers;
+};
+
+namespace lr {
+
+// How a decode launch splits the context of each (b, h).
+struct Split {
+  int32_t n_split;          // work-groups per (b, h)
+  int32_t tiles_per_split;  // 64-token tiles per work-group
+  int32_t waves;            // wavefronts per work-group
+};
+Split choose_split(const lr_attn_plan& p, int32_t max_len);
+size_t workspace_bytes(const lr_attn_plan& p, int32_t max_len);
+
+// Kernel launchers (kernels.hip).  Arguments are already validated.  Each
+// returns the hipError_t of the launch (0 on success).
+int launch_append(const lr_attn_plan& p, int32_t layer, void* cache, const float* ck,
+                  const float* cv, const int32_t* pos, int32_t n_new, void* stream);
+int launch_decode(const lr_attn_plan& p, int32_t layer, const void* cache, const int32_t* len,
+                  int32_t max_len, const void* q, const void* bk, const void* bv, float scale,
+                  void* out, void* workspace, void* stream, bool explicit_form);
+int launch_workspace_init(void* workspace, size_t bytes, void* stream);
+
+}  // namespace lr

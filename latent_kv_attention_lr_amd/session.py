@@ -1,0 +1,99 @@
+"""Device state of a stack of low-rank latent-KV attention layers.
+
+A ``DecodeSession`` owns, per layer, the quantised latent cache and the B^K /
+B^V factor tensors, plus one split workspace and the per-sequence lengths.
+torch provides the device allocations and the stream; all computation is in
+``liblr_attn.so`` through the binding.
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence
+
+import torch
+
+from . import (LR_DT_BF16, LR_DT_F32, LR_HEAD_DIM, lr_attn_append_latent, lr_attn_cache_bytes,
+               lr_attn_decode, lr_attn_decode_explicit, lr_attn_factor_elems,
+               lr_attn_head_layout_get, lr_attn_latent_elems, lr_attn_plan_create,
+               lr_attn_plan_destroy, lr_attn_workspace_bytes, lr_attn_workspace_init)
+
+
+class DecodeSession:
+    def __init__(self, n_layers: int, batch: int, n_heads: int, capacity: int, qfmt: int,
+                 io_dtype: int, ranks_k: Sequence[Sequence[int]], ranks_v: Sequence[Sequence[int]],
+                 device="cuda", max_splits: int = 0):
+        self.n_layers, self.batch, self.n_heads, self.capacity = n_layers, batch, n_heads, capacity
+        self.qfmt, self.io_dtype = qfmt, io_dtype
+        self.device = torch.device(device)
+        self.ranks_k = [list(r) for r in ranks_k]
+        self.ranks_v = [list(r) for r in ranks_v]
+        flat_k = [r for row in self.ranks_k for r in row]
+        flat_v = [r for row in self.ranks_v for r in row]
+        self.plan = lr_attn_plan_create(n_layers, batch, n_heads, capacity, qfmt, io_dtype,
+                                        flat_k, flat_v, max_splits=max_splits)
+        self.torch_dtype = torch.bfloat16 if io_dtype == LR_DT_BF16 else torch.float32
+        self.caches: List[torch.Tensor] = [
+            torch.zeros(lr_attn_cache_bytes(self.plan, l), dtype=torch.uint8, device=self.device)
+            for l in range(n_layers)]
+        self.bk: List[Optional[torch.Tensor]] = [None] * n_layers
+        self.bv: List[Optional[torch.Tensor]] = [None] * n_layers
+        self.ws_bytes = lr_attn_workspace_bytes(self.plan, capacity)
+        self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
+        lr_attn_workspace_init(self.plan, self.workspace, self.workspace.numel())
+        self.lengths = torch.zeros(batch, dtype=torch.int32, device=self.device)
+
+    def __del__(self):
+        plan = getattr(self, "plan", None)
+        if plan:
+            lr_attn_plan_destroy(plan)
+            self.plan = None
+
+    # -- layout -------------------------------------------------------------
+    def latent_elems(self, layer: int, kv: int) -> int:
+        return lr_attn_latent_elems(self.plan, layer, kv)
+
+    def factor_elems(self, layer: int, kv: int) -> int:
+        return lr_attn_factor_elems(self.plan, layer, kv)
+
+    def head_layout(self, layer: int, head: int) -> dict:
+        return lr_attn_head_layout_get(self.plan, layer, head)
+
+    # -- state --------------------------------------------------------------
+    def set_factors(self, layer: int, bk: torch.Tensor, bv: torch.Tensor) -> None:
+        for t, kv in ((bk, 0), (bv, 1)):
+            if t.numel() != self.factor_elems(layer, kv) or t.dtype != self.torch_dtype:
+                raise ValueError("factor tensor has the wrong size or dtype")
+            if t.device != self.device or not t.is_contiguous():
+                raise ValueError("factor tensor must be contiguous on the session device")
+        self.bk[layer] = bk
+        self.bv[layer] = bv
+
+    def append(self, layer: int, ck: torch.Tensor, cv: torch.Tensor, pos: torch.Tensor,
+               stream=None) -> None:
+        """Quantise and write fp32 latents ck/cv [B, n_new, latent_elems] at pos[b].."""
+        n_new = ck.shape[1]
+        if ck.dtype != torch.float32 or cv.dtype != torch.float32:
+            raise ValueError("latents must be fp32")
+        if ck.shape != (self.batch, n_new, self.latent_elems(layer, 0)) or \
+                cv.shape != (self.batch, n_new, self.latent_elems(layer, 1)):
+            raise ValueError("latent tensors have the wrong shape")
+        if not (ck.is_contiguous() and cv.is_contiguous() and pos.is_contiguous()):
+            raise ValueError("latent and pos tensors must be contiguous")
+        lr_attn_append_latent(self.plan, layer, self.caches[layer], ck, cv, pos, n_new, stream)
+
+    def decode(self, layer: int, q: torch.Tensor, out: torch.Tensor, max_len: int,
+               lengths: Optional[torch.Tensor] = None, softmax_scale: Optional[float] = None,
+               explicit: bool = False, stream=None) -> None:
+        """out[b, h] = attention of q[b, h] over the first lengths[b] cached tokens."""
+        if self.bk[layer] is None:
+            raise ValueError("factors of this layer are not set")
+        shape = (self.batch, self.n_heads, LR_HEAD_DIM)
+        if q.shape != shape or out.shape != shape or q.dtype != self.torch_dtype or out.dtype != self.torch_dtype:
+            raise ValueError("q/out must be [B, H, 128] of the session dtype")
+        if not (q.is_contiguous() and out.is_contiguous()):
+            raise ValueError("q and out must be contiguous")
+        scale = 1.0 / math.sqrt(LR_HEAD_DIM) if softmax_scale is None else softmax_scale
+        fn = lr_attn_decode_explicit if explicit else lr_attn_decode
+        fn(self.plan, layer, self.caches[layer], self.lengths if lengths is None else lengths,
+           max_len, q, self.bk[layer], self.bv[layer], scale, out, self.workspace,
+           self.workspace.numel(), stream)

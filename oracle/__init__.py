@@ -55,6 +55,10 @@ def lib() -> ctypes.CDLL:
         L.lro_quant_int8.restype = None
         L.lro_quant_int4.argtypes = [P, ctypes.c_int, P, P]
         L.lro_quant_int4.restype = None
+        L.lro_quant_int8_rows.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P]
+        L.lro_quant_int8_rows.restype = None
+        L.lro_quant_int4_rows.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P]
+        L.lro_quant_int4_rows.restype = None
         L.lro_attend.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_int, P, P, P, P, P, ctypes.c_double, P, P]
         L.lro_attend.restype = ctypes.c_int
@@ -84,9 +88,7 @@ def quant_int8(c: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     rows = c.reshape(-1, r)
     q = np.empty(rows.shape, dtype=np.int8)
     s = np.empty(rows.shape[0], dtype=np.float32)
-    L = lib()
-    for i in range(rows.shape[0]):
-        L.lro_quant_int8(_ptr(rows[i]), r, _ptr(q[i]), s[i:i + 1].ctypes.data)
+    lib().lro_quant_int8_rows(_ptr(rows), rows.shape[0], r, _ptr(q), _ptr(s))
     return q.reshape(c.shape), s.reshape(c.shape[:-1])
 
 
@@ -99,9 +101,7 @@ def quant_int4(c: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     rows = c.reshape(-1, r)
     q = np.empty(rows.shape, dtype=np.int8)
     s = np.empty((rows.shape[0], ng), dtype=np.uint16)
-    L = lib()
-    for i in range(rows.shape[0]):
-        L.lro_quant_int4(_ptr(rows[i]), r, _ptr(q[i]), _ptr(s[i]))
+    lib().lro_quant_int4_rows(_ptr(rows), rows.shape[0], r, _ptr(q), _ptr(s))
     return q.reshape(c.shape), s.reshape(c.shape[:-1] + (ng,))
 
 

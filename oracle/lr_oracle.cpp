@@ -110,6 +110,19 @@ void lro_quant_int4(const float* c, int r, int8_t* q, uint16_t* scales) {
   }
 }
 
+// The two quantisers applied to n consecutive rows of r values (a plain loop).
+void lro_quant_int8_rows(const float* c, int n, int r, int8_t* q, float* scales) {
+  for (int i = 0; i < n; ++i)
+    lro_quant_int8(c + static_cast<size_t>(i) * r, r, q + static_cast<size_t>(i) * r, scales + i);
+}
+
+void lro_quant_int4_rows(const float* c, int n, int r, int8_t* q, uint16_t* scales) {
+  const int ng = (r + 31) / 32;
+  for (int i = 0; i < n; ++i)
+    lro_quant_int4(c + static_cast<size_t>(i) * r, r, q + static_cast<size_t>(i) * r,
+                   scales + static_cast<size_t>(i) * ng);
+}
+
 // Quantise and dequantise one row: out_i = scale * q_i in fp64 (exact).
 // qfmt: 0 = int8 per token, 1 = int4 group 32, 2 = no quantisation (out = c).
 static void dequantised_row(int qfmt, const float* c, int r, double* out) {

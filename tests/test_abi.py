@@ -1,0 +1,192 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+and validates its arguments on the host before any launch.  No call here
+reaches a kernel (every call either has an invalid argument or touches no
+device memory), so the file is safe with or without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import latent_kv_attention_lr_amd as lr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lr_attn.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lr_attn_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_expected_entry_points():
+    names = declared_functions()
+    for must in ("lr_attn_append_latent", "lr_attn_decode", "lr_attn_decode_explicit",
+                 "lr_attn_plan_create", "lr_attn_workspace_bytes"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(lr.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def _plan(**kw):
+    args = dict(n_layers=1, batch=2, n_heads=4, capacity=300, qfmt=lr.LR_Q_INT8_TOKEN,
+                io_dtype=lr.LR_DT_BF16, rank_k=[32, 16, 8, 128], rank_v=[40, 96, 64, 8])
+    args.update(kw)
+    return lr.lr_attn_plan_create(**args)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(head_dim=64), lr.LR_EUNSUPPORTED),
+    (dict(n_heads=129, rank_k=[32] * 129, rank_v=[32] * 129), lr.LR_EUNSUPPORTED),
+    (dict(rank_k=[32, 16, 8, 136]), lr.LR_EUNSUPPORTED),
+    (dict(rank_k=[32, 16, 0, 128]), lr.LR_EUNSUPPORTED),
+    (dict(rank_v=[40, 96, 64, 12]), lr.LR_EUNSUPPORTED),
+    (dict(batch=0), lr.LR_EINVAL),
+    (dict(capacity=0), lr.LR_EINVAL),
+    (dict(capacity=(1 << 24) + 1), lr.LR_ERANGE),
+    (dict(qfmt=7), lr.LR_EINVAL),
+    (dict(io_dtype=9), lr.LR_EINVAL),
+    (dict(max_splits=-1), lr.LR_EINVAL),
+])
+def test_plan_create_rejects(bad, status):
+    with pytest.raises(lr.LrAttnError) as e:
+        _plan(**bad)
+    assert e.value.status == status
+
+
+def test_plan_layout_is_consistent():
+    for qfmt in (lr.LR_Q_INT8_TOKEN, lr.LR_Q_INT4_G32):
+        p = _plan(qfmt=qfmt)
+        try:
+            total = lr.lr_attn_cache_bytes(p, 0)
+            assert lr.lr_attn_latent_elems(p, 0, 0) == 32 + 16 + 8 + 128
+            assert lr.lr_attn_latent_elems(p, 0, 1) == 40 + 96 + 64 + 8
+            assert lr.lr_attn_factor_elems(p, 0, 1) == (40 + 96 + 64 + 8) * 128
+            regions = []
+            lk = lv = 0
+            for h in range(4):
+                hl = lr.lr_attn_head_layout_get(p, 0, h)
+                for kv in "kv":
+                    r = hl["rank_" + kv]
+                    rb = r if qfmt == lr.LR_Q_INT8_TOKEN else r // 2
+                    sb = 4 if qfmt == lr.LR_Q_INT8_TOKEN else 2 * ((r + 31) // 32)
+                    assert hl["row_bytes_" + kv] == rb and hl["scale_bytes_" + kv] == sb
+                    assert hl["tile_bytes_" + kv] == 64 * (rb + sb)
+                    assert hl["plane_bytes_" + kv] == 5 * 64 * (rb + sb)  # ceil(300 / 64) tiles
+                    off = hl[kv + "_offset"]
+                    assert off % 256 == 0
+                    regions.append((off, off + 2 * hl["plane_bytes_" + kv]))
+                assert hl["latent_offset_k"] == lk and hl["latent_offset_v"] == lv
+                assert hl["factor_offset_k"] == lk * 128 and hl["factor_offset_v"] == lv * 128
+                lk += hl["rank_k"]
+                lv += hl["rank_v"]
+            regions.sort()
+            for (a0, a1), (b0, b1) in zip(regions, regions[1:]):
+                assert a1 <= b0
+            assert regions[-1][1] <= total
+        finally:
+            lr.lr_attn_plan_destroy(p)
+
+
+def test_query_functions_reject_bad_indices():
+    p = _plan()
+    try:
+        assert lr.lr_attn_cache_bytes(p, 1) == 0
+        assert lr.lr_attn_latent_elems(p, 0, 2) == 0
+        assert lr.lr_attn_workspace_bytes(p, 0) == 0
+        assert lr.lr_attn_workspace_bytes(p, 301) == 0
+        with pytest.raises(lr.LrAttnError) as e:
+            lr.lr_attn_head_layout_get(p, 0, 4)
+        assert e.value.status == lr.LR_ERANGE
+    finally:
+        lr.lr_attn_plan_destroy(p)
+
+
+def test_workspace_grows_with_context_and_is_aligned():
+    p = lr.lr_attn_plan_create(1, 8, 32, 40000, lr.LR_Q_INT4_G32, lr.LR_DT_BF16, [48] * 32, [48] * 32)
+    try:
+        sizes = [lr.lr_attn_workspace_bytes(p, n) for n in (1, 64, 600, 4096, 32832, 40000)]
+        assert all(s % 256 == 0 for s in sizes)
+        assert sizes == sorted(sizes)
+        assert sizes[-1] > 0
+    finally:
+        lr.lr_attn_plan_destroy(p)
+
+
+FAKE = 1 << 20  # a 256-aligned non-null address that is never dereferenced
+
+
+def _append(p, **kw):
+    a = dict(layer=0, cache=FAKE, ck=FAKE, cv=FAKE, pos=FAKE, n_new=1)
+    a.update(kw)
+    return lr._lib.lr_attn_append_latent(p, a["layer"], a["cache"], a["ck"], a["cv"], a["pos"],
+                                         a["n_new"], None)
+
+
+def _decode(p, fn="lr_attn_decode", **kw):
+    a = dict(layer=0, cache=FAKE, len=FAKE, max_len=100, q=FAKE, bk=FAKE, bv=FAKE, scale=0.088,
+             out=FAKE, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return getattr(lr._lib, fn)(p, a["layer"], a["cache"], a["len"], a["max_len"], a["q"], a["bk"],
+                                a["bv"], a["scale"], a["out"], a["ws"], a["ws_bytes"], None)
+
+
+def test_append_argument_errors_before_launch():
+    p = _plan()
+    try:
+        assert _append(None) == lr.LR_EINVAL
+        assert _append(p, layer=1) == lr.LR_ERANGE
+        assert _append(p, layer=-1) == lr.LR_ERANGE
+        assert _append(p, cache=None) == lr.LR_EINVAL
+        assert _append(p, ck=None) == lr.LR_EINVAL
+        assert _append(p, pos=None) == lr.LR_EINVAL
+        assert _append(p, n_new=-1) == lr.LR_EINVAL
+        assert _append(p, n_new=301) == lr.LR_ERANGE
+        assert _append(p, cache=FAKE + 16) == lr.LR_EINVAL   # cache must be 256-aligned
+        assert _append(p, ck=FAKE + 4) == lr.LR_EINVAL       # latents 16-aligned
+        assert _append(p, n_new=0) == lr.LR_OK               # no-op, no launch
+    finally:
+        lr.lr_attn_plan_destroy(p)
+
+
+@pytest.mark.parametrize("fn", ["lr_attn_decode", "lr_attn_decode_explicit"])
+def test_decode_argument_errors_before_launch(fn):
+    p = _plan(capacity=3000)
+    try:
+        assert _decode(None, fn) == lr.LR_EINVAL
+        assert _decode(p, fn, layer=3) == lr.LR_ERANGE
+        assert _decode(p, fn, max_len=0) == lr.LR_ERANGE
+        assert _decode(p, fn, max_len=3001) == lr.LR_ERANGE
+        for name in ("cache", "len", "q", "bk", "bv", "out"):
+            assert _decode(p, fn, **{name: None}) == lr.LR_EINVAL, name
+        assert _decode(p, fn, scale=float("nan")) == lr.LR_EINVAL
+        assert _decode(p, fn, scale=float("inf")) == lr.LR_EINVAL
+        assert _decode(p, fn, q=FAKE + 8) == lr.LR_EINVAL
+        assert _decode(p, fn, cache=FAKE + 64) == lr.LR_EINVAL
+        need = lr.lr_attn_workspace_bytes(p, 3000)
+        assert need > 0
+        assert _decode(p, fn, max_len=3000, ws=None) == lr.LR_EWORKSPACE
+        assert _decode(p, fn, max_len=3000, ws_bytes=need - 1) == lr.LR_EWORKSPACE
+    finally:
+        lr.lr_attn_plan_destroy(p)
+
+
+def test_strerror_covers_every_status():
+    seen = {lr.lr_attn_strerror(s) for s in range(6)}
+    assert len(seen) == 6 and "unknown status" not in seen
+    assert lr.lr_attn_strerror(99) == "unknown status"
+
+
+def test_product_package_never_loads_the_oracle():
+    pkg = os.path.join(ROOT, "latent_kv_attention_lr_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f
+    assert "oracle" not in open(HEADER).read().lower()

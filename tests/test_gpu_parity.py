@@ -1,0 +1,270 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+* quantised latents: bit-exact codes and scale bits (hand-derived rows, random
+  rows of every rank, and sampled rows of the five workloads' caches);
+* decode outputs: |o_gpu - o_ref| <= 1e-2 max|o_ref| + 1e-3 (bf16) or
+  <= 1e-4 max|o_ref| (fp32) on every unit of the small workload, on ragged
+  and degenerate lengths, and on seeded samples of (layer, b, h) units of the
+  four large workloads at their first, middle and last decode steps, in the
+  launch configuration the benchmark uses.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import harness
+import lrgen
+import oracle
+from latent_kv_attention_lr_amd import LR_DT_BF16, LR_DT_F32, LR_Q_INT4_G32, LR_Q_INT8_TOKEN
+from latent_kv_attention_lr_amd.session import DecodeSession
+from gpu_util import TOL_BF16, TOL_F32, oracle_many, oracle_quant, read_codes, within
+
+pytestmark = pytest.mark.gpu
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def _val(v):
+    return math.ldexp(v[0], v[1]) if isinstance(v, list) else float(v)
+
+
+# ---------------------------------------------------------------------------
+# quantise + append, bit-exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", ["int8", "int4"])
+def test_append_golden_rows_bitexact(fmt):
+    cases = json.load(open(os.path.join(GOLD, "quant_cases.json")))[fmt]
+    qfmt = LR_Q_INT8_TOKEN if fmt == "int8" else LR_Q_INT4_G32
+    for c in cases:
+        row = np.array([_val(v) for v in c["row"]], dtype=np.float32)
+        r = len(row)
+        say(f"append golden {fmt} {c['name']} r={r}")
+        s = DecodeSession(1, 1, 1, 130, qfmt, LR_DT_BF16, [[r]], [[r]], device=DEV)
+        ck = torch.from_numpy(row).view(1, 1, r).to(DEV)
+        cv = torch.from_numpy(-row).view(1, 1, r).to(DEV)
+        pos = torch.tensor([70], dtype=torch.int32, device=DEV)
+        s.append(0, ck, cv, pos)
+        torch.cuda.synchronize()
+        cache = s.caches[0].cpu().numpy()
+        hl = s.head_layout(0, 0)
+        kq, ks = read_codes(cache, hl, qfmt, 0, [70], "k")
+        vq, vs = read_codes(cache, hl, qfmt, 0, [70], "v")
+        assert kq[0].tolist() == c["q"], c["why"]
+        assert vq[0].tolist() == [-x for x in c["q"]], c["why"]
+        if fmt == "int8":
+            want = np.float32(np.abs(row).max()) / np.float32(127) if c["scale"] == "m/127" \
+                else np.array([int(c["scale"], 16)], np.uint32).view(np.float32)[0]
+            assert ks[0] == np.float32(want).view(np.uint32) and vs[0] == ks[0]
+        else:
+            assert [int(x) for x in ks[0]] == [int(h, 16) for h in c["scale"]]
+            assert np.array_equal(vs, ks)
+
+
+def _mixed_rows(rng, n, r):
+    """Random rows over 40 binades, plus zero rows, rows with exact .5 ties at
+    scale 1, and rows small enough that int4 group scales are fp16 subnormals
+    or underflow."""
+    c = rng.standard_normal((n, r)) * np.exp2(rng.integers(-30, 10, (n, 1)))
+    c[0] = 0.0
+    c[1] = np.round(rng.uniform(-126, 126, r)) + 0.5
+    c[1, 0] = 127.0
+    c[2] = np.round(rng.uniform(-6, 6, r)) + 0.5
+    c[2, 0] = 7.0
+    c[3] *= 1e-38
+    c[4] = rng.standard_normal(r) * 1e-7
+    c[5] = rng.standard_normal(r) * 3e-9
+    return c.astype(np.float32)
+
+
+@pytest.mark.parametrize("qfmt", [LR_Q_INT8_TOKEN, LR_Q_INT4_G32])
+def test_append_random_rows_bitexact(qfmt):
+    rng = np.random.default_rng(100 + qfmt)
+    rk, rv = [8, 24, 48, 96, 128], [16, 40, 64, 88, 120]
+    B, n_new, cap = 3, 70, 200
+    s = DecodeSession(1, B, 5, cap, qfmt, LR_DT_BF16, [rk], [rv], device=DEV)
+    ck = np.concatenate([_mixed_rows(rng, B * n_new, r) for r in rk], axis=1).reshape(B, n_new, sum(rk))
+    cv = np.concatenate([_mixed_rows(rng, B * n_new, r) for r in rv], axis=1).reshape(B, n_new, sum(rv))
+    pos = [0, 65, 180]  # row 2 runs past capacity: slots 200.. are dropped
+    say(f"append random qfmt={qfmt}")
+    s.append(0, torch.from_numpy(ck).to(DEV), torch.from_numpy(cv).to(DEV),
+             torch.tensor(pos, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    cache = s.caches[0].cpu().numpy()
+    ok, ov = lrgen.head_offsets(rk), lrgen.head_offsets(rv)
+    for h in range(5):
+        hl = s.head_layout(0, h)
+        for b in range(B):
+            n = min(n_new, cap - pos[b])
+            slots = np.arange(pos[b], pos[b] + n)
+            for kv, lat, off, r in (("k", ck, ok[h], rk[h]), ("v", cv, ov[h], rv[h])):
+                got_q, got_s = read_codes(cache, hl, qfmt, b, slots, kv)
+                want_q, want_s = oracle_quant(qfmt, lat[b, :n, off:off + r])
+                assert np.array_equal(got_q, want_q), (h, b, kv)
+                assert np.array_equal(got_s, want_s), (h, b, kv)
+            if pos[b] + n_new > cap:  # the padding slots of the last tile stay untouched
+                pad = np.arange(cap, 4 * 64)
+                zq, zs = read_codes(cache, hl, qfmt, b, pad, "k")
+                assert not zq.any() and not np.asarray(zs).any()
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+def _check_units(run, units, s, tol, out):
+    jobs = [run.unit_inputs(u, s) for u in units]
+    refs = oracle_many(run.w.qfmt, jobs, run.scale)
+    got = out.double().cpu().numpy()
+    worst = 0.0
+    for u, ref in zip(units, refs):
+        _, b, h = u
+        g = got[b, h]
+        err = float(np.max(np.abs(g - ref)))
+        bound = tol[0] * float(np.max(np.abs(ref))) + tol[1]
+        worst = max(worst, err / bound)
+        assert err <= bound, (u, s, err, bound)
+    return worst
+
+
+@pytest.mark.parametrize("io", [LR_DT_BF16, LR_DT_F32])
+def test_decode_small_workload_every_unit(io):
+    w = lrgen.workload(0)
+    units = [(0, 0, h) for h in range(w.n_heads)]
+    say(f"decode small workload io={io}")
+    run = harness.WorkloadRun(w, io_dtype=io, device=DEV, keep=units).setup()
+    out = run.run_step(0, 0)
+    torch.cuda.synchronize()
+    _check_units(run, units, 0, TOL_BF16 if io == LR_DT_BF16 else TOL_F32, out)
+
+
+def _ragged_session(qfmt, io, max_splits, rng):
+    rk, rv = [32, 8, 96], [64, 16, 40]
+    B, cap = 6, 700
+    s = DecodeSession(1, B, 3, cap, qfmt, io, [rk], [rv], device=DEV, max_splits=max_splits)
+    ck = (rng.standard_normal((B, cap, sum(rk))) * 1.3).astype(np.float32)
+    cv = (rng.standard_normal((B, cap, sum(rv))) * 0.8).astype(np.float32)
+    s.append(0, torch.from_numpy(ck).to(DEV), torch.from_numpy(cv).to(DEV),
+             torch.zeros(B, dtype=torch.int32, device=DEV))
+    dt = torch.bfloat16 if io == LR_DT_BF16 else torch.float32
+    bk = (torch.from_numpy(rng.standard_normal((sum(rk), 128))) / 5).to(dt).to(DEV)
+    bv = (torch.from_numpy(rng.standard_normal((sum(rv), 128))) / 5).to(dt).to(DEV)
+    s.set_factors(0, bk.contiguous(), bv.contiguous())
+    q = torch.from_numpy(rng.standard_normal((B, 3, 128)) * 2).to(dt).to(DEV).contiguous()
+    return s, rk, rv, ck, cv, bk, bv, q
+
+
+@pytest.mark.parametrize("qfmt", [LR_Q_INT8_TOKEN, LR_Q_INT4_G32])
+@pytest.mark.parametrize("io", [LR_DT_BF16, LR_DT_F32])
+@pytest.mark.parametrize("max_splits", [0, 1])
+def test_decode_ragged_and_degenerate_lengths(qfmt, io, max_splits):
+    rng = np.random.default_rng(7 + 2 * qfmt + io)
+    s, rk, rv, ck, cv, bk, bv, q = _ragged_session(qfmt, io, max_splits, rng)
+    lens = [0, 1, 63, 64, 65, 700]
+    s.lengths.copy_(torch.tensor(lens, dtype=torch.int32))
+    out = torch.full_like(q, float("nan"))
+    say(f"decode ragged qfmt={qfmt} io={io} max_splits={max_splits}")
+    s.decode(0, q, out, max_len=700)
+    torch.cuda.synchronize()
+    got = out.double().cpu().numpy()
+    ok, ov = lrgen.head_offsets(rk), lrgen.head_offsets(rv)
+    tol = TOL_BF16 if io == LR_DT_BF16 else TOL_F32
+    qn, bkn, bvn = q.double().cpu().numpy(), bk.double().cpu().numpy(), bv.double().cpu().numpy()
+    jobs, keys = [], []
+    for b, T in enumerate(lens):
+        for h in range(3):
+            jobs.append((ck[b, :T, ok[h]:ok[h] + rk[h]], cv[b, :T, ov[h]:ov[h] + rv[h]], qn[b, h],
+                         bkn[ok[h]:ok[h] + rk[h]], bvn[ov[h]:ov[h] + rv[h]]))
+            keys.append((b, h))
+    refs = oracle_many(qfmt, jobs, 1 / math.sqrt(128))
+    for (b, h), ref in zip(keys, refs):
+        if lens[b] == 0:
+            assert np.array_equal(got[b, h], np.zeros(128)), "empty context must give zeros"
+        else:
+            assert within(got[b, h], ref, tol), (b, h, lens[b])
+
+
+def test_decode_max_len_clamps_longer_lengths():
+    rng = np.random.default_rng(3)
+    s, rk, rv, ck, cv, bk, bv, q = _ragged_session(LR_Q_INT8_TOKEN, LR_DT_F32, 0, rng)
+    s.lengths.fill_(700)
+    a = torch.empty_like(q)
+    b = torch.empty_like(q)
+    say("decode max_len clamp")
+    s.decode(0, q, a, max_len=300)            # len 700 is clamped to max_len 300
+    s.lengths.fill_(300)
+    s.decode(0, q, b, max_len=300)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_decode_is_deterministic_and_leaves_counters_zero():
+    rng = np.random.default_rng(11)
+    s, rk, rv, ck, cv, bk, bv, q = _ragged_session(LR_Q_INT4_G32, LR_DT_BF16, 0, rng)
+    s.lengths.fill_(700)
+    assert s.ws_bytes > 0
+    outs = []
+    say("decode determinism")
+    for _ in range(3):
+        o = torch.empty_like(q)
+        s.decode(0, q, o, max_len=700)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+    counters = s.workspace[: 6 * 3 * 4].view(torch.int32)
+    assert int(counters.abs().sum()) == 0
+
+
+# ---------------------------------------------------------------------------
+# the four large workloads at full size, sampled units
+# ---------------------------------------------------------------------------
+
+STEPS_CHECKED = {1: [0, 63, 127], 2: [0, 63, 127], 3: [0], 4: [0, 31, 63]}
+N_EXTRA = {1: 16, 2: 16, 3: 32, 4: 8}
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+def test_workload_parity_full_size(idx):
+    w = lrgen.workload(idx)
+    units = harness.sample_units(w, N_EXTRA[idx], seed=1000 + idx)
+    say(f"workload {idx} ({w.name}): setup, {len(units)} sampled units")
+    run = harness.WorkloadRun(w, io_dtype=LR_DT_BF16, device=DEV, keep=units).setup()
+    # quantised cache rows of the sampled units: bit-exact against the oracle
+    rng = np.random.default_rng(idx)
+    host_cache = {}
+    for u in units[:: max(1, len(units) // 12)]:
+        l, b, h = u
+        hl = run.sess.head_layout(l, h)
+        if l not in host_cache:
+            host_cache[l] = run.sess.caches[l].cpu().numpy()
+        cache = host_cache[l]
+        ck, cv, _, _, _ = run.unit_inputs(u, run.steps - 1 if run.steps else 0)
+        slots = np.unique(np.concatenate([rng.integers(0, run.context, 2048),
+                                          np.arange(run.context - 3, run.context)]))
+        for kv, lat in (("k", ck), ("v", cv)):
+            got_q, got_s = read_codes(cache, hl, w.qfmt, b, slots, kv)
+            want_q, want_s = oracle_quant(w.qfmt, lat[slots])
+            assert np.array_equal(got_q, want_q), (u, kv)
+            assert np.array_equal(got_s, want_s), (u, kv)
+    del host_cache
+    checked = STEPS_CHECKED[idx]
+    worst = 0.0
+    by_layer = {}
+    for u in units:
+        by_layer.setdefault(u[0], []).append(u)
+    for l in range(w.n_layers):
+        for s in range(w.steps):
+            out = run.run_step(l, s)
+            if s in checked and l in by_layer:
+                torch.cuda.synchronize()
+                say(f"workload {idx}: layer {l} step {s} check {len(by_layer[l])} units")
+                worst = max(worst, _check_units(run, by_layer[l], s, TOL_BF16, out))
+    say(f"workload {idx}: worst error / bound = {worst:.3g}")
