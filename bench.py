@@ -1,0 +1,246 @@
+"""Decode-attention throughput of the low-rank latent-KV path on one MI355X.
+
+One step = append one token's latents to every sequence (quantise + pack)
+and one decode step over the whole cache of the layer, on synthetic inputs
+shaped like a LLaMA-7B-class attention layer serving a vision-language
+decode (batch 16, 32 heads, head_dim 128, rank-32 per-head latents, int8 per
+token, 4096 cached tokens of which 576 are image-prefix tokens, 128 decode
+steps).  Prints one JSON line.
+
+  value        whole-job tokens/s = batch * steps / wall time of the steps
+  roofline     the decode kernel's algorithmic HBM bytes per launch divided
+               by its average duration (HIP events on the launch stream)
+  cpu_baseline the CPU oracle (plain fp64) timed on this host's cores on a
+               sample of one step's (b, h) units, scaled to the whole step
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: the workload's)")
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", type=int, default=1, help="index in the workload table")
+    ap.add_argument("--explicit", action="store_true", help="time the explicit-reconstruction decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=16,
+                    help="extra untimed-in-value steps with the 256 MiB last-level cache flushed before each")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="only run warmup + this many steps (for rocprofv3); no CPU baseline")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w, lens, rk, rv):
+    """HBM bytes one decode launch must move at least: every cached code and
+    scale of every (b, h) read once, both factor tensors, q and the output."""
+    qf = w.qfmt
+    per_tok = 0
+    for h in range(w.n_heads):
+        for r in (rk[h], rv[h]):
+            rb = r if qf == 0 else r // 2
+            sb = 4 if qf == 0 else 2 * ((r + 31) // 32)
+            per_tok += rb + sb
+    cache = sum(lens) * per_tok
+    factors = (sum(rk) + sum(rv)) * w.head_dim * 2
+    q_out = 2 * w.batch * w.n_heads * w.head_dim * 2
+    return cache + factors + q_out, per_tok
+
+
+def append_bytes(w, rk, rv):
+    qf = w.qfmt
+    row = 0
+    for h in range(w.n_heads):
+        for r in (rk[h], rv[h]):
+            rb = r if qf == 0 else r // 2
+            sb = 4 if qf == 0 else 2 * ((r + 31) // 32)
+            row += 4 * r + rb + sb
+    return w.batch * row
+
+
+def cpu_baseline(run, n_units_target=128):
+    """Time the oracle over a sample of step-0 units on the host's cores."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle
+
+    w = run.w
+    units = sorted(run.keep)[:n_units_target]
+    jobs = [run.unit_inputs(u, 0) for u in units]
+    threads = max(1, min(16, os.cpu_count() or 1))
+    with ThreadPoolExecutor(threads) as pool:
+        t0 = time.perf_counter()
+        list(pool.map(lambda j: oracle.attend(w.qfmt, *j, run.scale), jobs))
+        wall = time.perf_counter() - t0
+    units_total = w.n_layers * w.batch * w.n_heads
+    step_s = wall * units_total / len(units)
+    return {"value": w.batch / step_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(units)} of {units_total} (b,h) units of decode step 0 "
+                      f"(T={run.context + 1}), fp64 explicit reconstruction; "
+                      f"{wall:.2f} s wall scaled x{units_total / len(units):.1f} to one step",
+            "step_s": step_s}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; multi-GPU sharding is a design note, "
+              "not an implemented path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import harness
+    import lrgen
+    from latent_kv_attention_lr_amd import LR_DT_BF16
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = lrgen.workload(args.workload)
+    steps = w.steps if args.steps is None else args.steps
+    warm = args.warmup
+    if args.profile_steps:
+        steps = args.profile_steps
+    n_cpu = 4 * w.n_heads if w.batch >= 4 else w.batch * w.n_heads
+    keep = [] if (args.no_cpu_baseline or args.profile_steps) else \
+        [(0, b, h) for b in range(min(w.batch, n_cpu // w.n_heads)) for h in range(w.n_heads)]
+    nsteps_inputs = max(steps, warm, 1)
+    print(f"[bench] setting up {w.name}", file=sys.stderr, flush=True)
+    run = harness.WorkloadRun(w, io_dtype=LR_DT_BF16, device=dev, keep=keep,
+                              steps=nsteps_inputs).setup()
+    sess = run.sess
+    L = w.n_layers
+    ctx = run.context
+    # every step's inputs are resident before timing: latents, q, pos, len
+    per = []
+    for s in range(nsteps_inputs):
+        layers = []
+        for l in range(L):
+            ck, cv, q, pos = run.step_tensors(l, s)
+            layers.append((ck, cv, q))
+        ln = torch.full((w.batch,), ctx + s + 1, dtype=torch.int32, device=dev)
+        pos = torch.full((w.batch,), ctx + s, dtype=torch.int32, device=dev)
+        per.append((layers, pos, ln))
+    out = torch.empty(w.batch, w.n_heads, w.head_dim, dtype=torch.bfloat16, device=dev)
+
+    def step(s, ev=None):
+        layers, pos, ln = per[s]
+        for l in range(L):
+            ck, cv, q = layers[l]
+            sess.append(l, ck, cv, pos)
+            if ev is not None:
+                ev[0].record()
+            sess.decode(l, q, out, ctx + s + 1, lengths=ln, explicit=args.explicit)
+            if ev is not None:
+                ev[1].record()
+
+    print(f"[bench] warmup {warm} steps", file=sys.stderr, flush=True)
+    for s in range(warm):
+        step(s)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` steps from the configured context
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps * L)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        for l in range(L):
+            layers, pos, ln = per[s]
+            ck, cv, q = layers[l]
+            sess.append(l, ck, cv, pos)
+            evs[s * L + l][0].record()
+            sess.decode(l, q, out, ctx + s + 1, lengths=ln, explicit=args.explicit)
+            evs[s * L + l][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"[bench] timed {steps} steps in {wall * 1e3:.2f} ms", file=sys.stderr, flush=True)
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
+
+    rk_all = w.ranks_k
+    rv_all = w.ranks_v
+    bytes_launch = 0.0
+    per_tok_bytes = 0
+    for s in range(steps):
+        for l in range(L):
+            b_, per_tok_bytes = algorithmic_bytes(w, [ctx + s + 1] * w.batch, rk_all[l], rv_all[l])
+            bytes_launch += b_
+    bytes_launch /= steps * L
+    achieved = bytes_launch / dec_avg_s / 1e9
+
+    result = {
+        "metric": "decode attention tokens/sec (1 GPU) + achieved HBM GB/s as % of MI355X peak",
+        "value": w.batch * steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": wall / steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "layers": L, "batch": w.batch, "heads": w.n_heads, "head_dim": w.head_dim,
+            "rank": "per-head table" if w.uniform_rank is None else w.uniform_rank,
+            "context": ctx, "image_prefix": w.prefix,
+            "latents": "int8 per-token fp32 scale" if w.qfmt == 0 else "int4 group-32 fp16 scale",
+            "q_factors_out": "bf16", "accumulation": "f32",
+            "decode_form": "explicit" if args.explicit else "absorbed",
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+            "kernel": "k_decode", "bytes_per_launch": bytes_launch,
+            "bytes_per_token_per_bh": per_tok_bytes / w.n_heads,
+            "avg_launch_us": dec_avg_s * 1e6,
+        },
+    }
+
+    # ---- MALL-cold decode timing (outside the timed region): flush first
+    if args.cold_steps and not args.profile_steps:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold = []
+        for s in range(min(args.cold_steps, steps)):
+            for l in range(L):
+                layers, pos, ln = per[s]
+                ck, cv, q = layers[l]
+                sess.append(l, ck, cv, pos)
+                flush.fill_(s & 0xff)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                sess.decode(l, q, out, ctx + s + 1, lengths=ln, explicit=args.explicit)
+                b.record()
+                cold.append((a, b))
+        torch.cuda.synchronize()
+        cold_s = sum(a.elapsed_time(b) for a, b in cold) / len(cold) / 1e3
+        result["roofline"]["cold_avg_launch_us"] = cold_s * 1e6
+        result["roofline"]["cold_achieved"] = bytes_launch / cold_s / 1e9
+        del flush
+
+    if keep:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cb = cpu_baseline(run, n_cpu)
+        cb.pop("step_s")
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -51,12 +51,29 @@ class lr_attn_head_layout(ctypes.Structure):
                 ("factor_offset_k", ctypes.c_int64), ("factor_offset_v", ctypes.c_int64)]
 
 
+def _hip_runtimes():
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({l.split()[-1] for l in f if "libamdhip64" in l})
+    except OSError:
+        return []
+
+
 def _load() -> ctypes.CDLL:
+    # torch (device memory and streams) brings its own HIP runtime.  It must be
+    # loaded first so that the library binds to that same runtime (both carry
+    # the soname libamdhip64.so.7); two runtimes in one process do not share
+    # devices, streams or allocations.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python -c 'import __graft_entry__ as g; g.build()'` "
                           "or `python latent_kv_attention_lr_amd/build.py`")
     L = ctypes.CDLL(LIB_PATH)
+    rt = _hip_runtimes()
+    if len(rt) > 1:
+        raise ImportError(f"more than one HIP runtime is loaded ({rt}); import torch before "
+                          "anything that loads /opt/rocm's libamdhip64")
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     plan_pp = ctypes.POINTER(ctypes.c_void_p)
     sig = {

@@ -90,6 +90,8 @@ __device__ __forceinline__ float lane63(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+__device__ __forceinline__ int uniform_i(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 __device__ __forceinline__ float uniform(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
 }
@@ -168,9 +170,10 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a, HeadTab ht) {
   const int kv = int(idx / a.H);
   const int slot = a.pos[b] + j;
   if (slot < 0 || slot >= a.capacity) return;
-  const int r = kv ? ht.rv[h] : ht.rk[h];
+  const uint32_t rr = ht.ranks[h], lo = ht.loff[h];
+  const int r = int(kv ? rr >> 16 : rr & 0xffffu);
   const int sum_r = kv ? a.sum_rv : a.sum_rk;
-  const float* src = (kv ? a.cv : a.ck) + (int64_t(b) * a.n_new + j) * sum_r + (kv ? ht.loff_v[h] : ht.loff_k[h]);
+  const float* src = (kv ? a.cv : a.ck) + (int64_t(b) * a.n_new + j) * sum_r + int(kv ? lo >> 16 : lo & 0xffffu);
   const int rb = row_bytes(QF, r);
   const int tb = tile_bytes(QF, r);
   uint8_t* tile = a.cache + uint64_t(kv ? ht.vreg[h] : ht.kreg[h]) * kRegionAlign +
@@ -304,8 +307,11 @@ __global__ __launch_bounds__(NW * 64) void k_decode(DecodeArgs a, HeadTab ht) {
   const int split = idx % a.n_split;
   idx /= a.n_split;
   const int b = idx % a.B;
-  const int h = ht.order[idx / a.B];
-  const int rk = ht.rk[h], rv = ht.rv[h];
+  const int h = uniform_i(int(ht.order[idx / a.B]));
+  const uint32_t rr = uniform_i(int(ht.ranks[h])), lo = uniform_i(int(ht.loff[h]));
+  const int rk = int(rr & 0xffffu), rv = int(rr >> 16);
+  const int loff_k = int(lo & 0xffffu), loff_v = int(lo >> 16);
+  const uint32_t kreg = uniform_i(int(ht.kreg[h])), vreg = uniform_i(int(ht.vreg[h]));
   const int rbk = row_bytes(QF, rk), rbv = row_bytes(QF, rv);
   const int tbk = tile_bytes(QF, rk), tbv = tile_bytes(QF, rv);
   const int len = min(max(a.len[b], 0), a.max_len);
@@ -324,7 +330,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode(DecodeArgs a, HeadTab ht) {
   {
     const IOT* qrow = reinterpret_cast<const IOT*>(a.q) + size_t(unit) * kHeadDim;
     const float q0 = E::ld(qrow, 2 * lane), q1 = E::ld(qrow, 2 * lane + 1);
-    const IOT* bkh = reinterpret_cast<const IOT*>(a.bk) + size_t(ht.loff_k[h]) * kHeadDim;
+    const IOT* bkh = reinterpret_cast<const IOT*>(a.bk) + size_t(loff_k) * kHeadDim;
     for (int i = wid; i < R; i += NW) {
       float v = 0.0f;
       if (i < rk) {
@@ -341,8 +347,8 @@ __global__ __launch_bounds__(NW * 64) void k_decode(DecodeArgs a, HeadTab ht) {
   for (int i = 0; i < R; ++i) qp[i] = uniform(s_q[i]);
 
   // ---- stream this split's tiles: one token per lane, online softmax
-  const uint8_t* kplane = a.cache + uint64_t(ht.kreg[h]) * kRegionAlign + uint64_t(b) * a.n_tiles * tbk;
-  const uint8_t* vplane = a.cache + uint64_t(ht.vreg[h]) * kRegionAlign + uint64_t(b) * a.n_tiles * tbv;
+  const uint8_t* kplane = a.cache + uint64_t(kreg) * kRegionAlign + uint64_t(b) * a.n_tiles * tbk;
+  const uint8_t* vplane = a.cache + uint64_t(vreg) * kRegionAlign + uint64_t(b) * a.n_tiles * tbv;
   float m = -__builtin_inff(), l = 0.0f;
   float u[R];
 #pragma unroll
@@ -455,7 +461,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode(DecodeArgs a, HeadTab ht) {
   __syncthreads();
   if (tid < rv) s_u[0][tid] = (L > 0.0f) ? ui / L : 0.0f;
   __syncthreads();
-  const IOT* bvh = reinterpret_cast<const IOT*>(a.bv) + size_t(ht.loff_v[h]) * kHeadDim;
+  const IOT* bvh = reinterpret_cast<const IOT*>(a.bv) + size_t(loff_v) * kHeadDim;
   IOT* o = reinterpret_cast<IOT*>(a.out) + size_t(unit) * kHeadDim;
   for (int j = tid; j < kHeadDim; j += NW * 64) {
     float acc = 0.0f;

@@ -30,14 +30,15 @@ LR_HD int n_tiles(int capacity) { return (capacity + kTile - 1) / kTile; }
 // Per-layer table handed to every kernel by value (kernel-argument segment).
 // Offsets of the K and V regions are in units of kRegionAlign bytes; head h's
 // plane of sequence b starts at region + b * n_tiles(capacity) * tile_bytes.
+// Every field is a 32-bit word: with narrower fields the compiler may fold a
+// 2-byte-aligned element address into the base of a scalar load, and the
+// scalar unit ignores the low two bits of that base.
 struct HeadTab {
   uint32_t kreg[LR_MAX_HEADS];
   uint32_t vreg[LR_MAX_HEADS];
-  uint16_t loff_k[LR_MAX_HEADS];   // latent element offset == factor row offset
-  uint16_t loff_v[LR_MAX_HEADS];
-  uint8_t rk[LR_MAX_HEADS];
-  uint8_t rv[LR_MAX_HEADS];
-  uint8_t order[LR_MAX_HEADS];     // dispatch order: heads by bytes per token, largest first
+  uint32_t ranks[LR_MAX_HEADS];    // r_k | r_v << 16
+  uint32_t loff[LR_MAX_HEADS];     // latent (== factor row) offset: K | V << 16
+  uint32_t order[LR_MAX_HEADS];    // dispatch order: heads by bytes per token, largest first
 };
 
 }  // namespace lr

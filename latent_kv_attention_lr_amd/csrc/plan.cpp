@@ -119,10 +119,8 @@ lr_status lr_attn_plan_create(const lr_attn_desc* d, lr_attn_plan** out) {
       if (off / lr::kRegionAlign > 0xffffffffull) { delete p; return LR_ERANGE; }
       L.tab.kreg[h] = static_cast<uint32_t>(hl.k_offset / lr::kRegionAlign);
       L.tab.vreg[h] = static_cast<uint32_t>(hl.v_offset / lr::kRegionAlign);
-      L.tab.loff_k[h] = static_cast<uint16_t>(lk);
-      L.tab.loff_v[h] = static_cast<uint16_t>(lv);
-      L.tab.rk[h] = static_cast<uint8_t>(rk);
-      L.tab.rv[h] = static_cast<uint8_t>(rv);
+      L.tab.ranks[h] = static_cast<uint32_t>(rk) | (static_cast<uint32_t>(rv) << 16);
+      L.tab.loff[h] = static_cast<uint32_t>(lk) | (static_cast<uint32_t>(lv) << 16);
       lk += rk;
       lv += rv;
       L.rk_max = std::max(L.rk_max, rk);
@@ -140,7 +138,7 @@ lr_status lr_attn_plan_create(const lr_attn_desc* d, lr_attn_plan** out) {
       const int wb = L.heads[b].tile_bytes_k + L.heads[b].tile_bytes_v;
       return wa > wb;
     });
-    for (int i = 0; i < H; ++i) L.tab.order[i] = static_cast<uint8_t>(order[i]);
+    for (int i = 0; i < H; ++i) L.tab.order[i] = static_cast<uint32_t>(order[i]);
   }
   *out = p;
   return LR_OK;

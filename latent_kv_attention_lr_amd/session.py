@@ -42,11 +42,17 @@ class DecodeSession:
         lr_attn_workspace_init(self.plan, self.workspace, self.workspace.numel())
         self.lengths = torch.zeros(batch, dtype=torch.int32, device=self.device)
 
-    def __del__(self):
+    def close(self) -> None:
         plan = getattr(self, "plan", None)
         if plan:
             lr_attn_plan_destroy(plan)
             self.plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # interpreter shutdown: module globals may be gone
+            pass
 
     # -- layout -------------------------------------------------------------
     def latent_elems(self, layer: int, kv: int) -> int:
