@@ -40,6 +40,8 @@ def parse():
                     help="extra untimed-in-value steps with the 256 MiB last-level cache flushed before each")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="only run warmup + this many steps (for rocprofv3); no CPU baseline")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch the timed steps eagerly instead of replaying one HIP graph")
     return ap.parse_args()
 
 
@@ -151,24 +153,57 @@ def main():
         step(s)
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly `steps` steps from the configured context
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps * L)]
+    # ---- the timed steps: exactly `steps` steps from the configured context,
+    # launched as one HIP graph (append + decode per step and layer) so the
+    # host issues nothing per step.
+    use_graph = not args.no_graph
+
+    def timed_steps():
+        for s in range(steps):
+            layers, pos, ln = per[s]
+            for l in range(L):
+                ck, cv, q = layers[l]
+                sess.append(l, ck, cv, pos)
+                sess.decode(l, q, out, ctx + s + 1, lengths=ln, explicit=args.explicit)
+
+    def decodes_only():
+        for s in range(steps):
+            layers, pos, ln = per[s]
+            for l in range(L):
+                sess.decode(l, layers[l][2], out, ctx + s + 1, lengths=ln, explicit=args.explicit)
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                fn()
+        torch.cuda.current_stream().wait_stream(cap)
+        g.replay()                          # the first replay uploads the graph: untimed
+        torch.cuda.synchronize()
+        return g
+
+    run_timed = capture(timed_steps).replay if use_graph else timed_steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(steps):
-        for l in range(L):
-            layers, pos, ln = per[s]
-            ck, cv, q = layers[l]
-            sess.append(l, ck, cv, pos)
-            evs[s * L + l][0].record()
-            sess.decode(l, q, out, ctx + s + 1, lengths=ln, explicit=args.explicit)
-            evs[s * L + l][1].record()
+    run_timed()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    print(f"[bench] timed {steps} steps in {wall * 1e3:.2f} ms", file=sys.stderr, flush=True)
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
-    dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
+    print(f"[bench] timed {steps} steps in {wall * 1e3:.2f} ms ({'graph' if use_graph else 'eager'})",
+          file=sys.stderr, flush=True)
+
+    # ---- the decode kernel alone: the same `steps` decode launches (each with
+    # its step's lengths) back to back, between two HIP events on the launch
+    # stream; average launch duration = elapsed / launches.
+    run_dec = capture(decodes_only).replay if use_graph else decodes_only
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    run_dec()
+    e1.record()
+    torch.cuda.synchronize()
+    dec_avg_s = e0.elapsed_time(e1) / (steps * L) / 1e3
 
     rk_all = w.ranks_k
     rv_all = w.ranks_v
@@ -203,6 +238,7 @@ def main():
             "q_factors_out": "bf16", "accumulation": "f32",
             "decode_form": "explicit" if args.explicit else "absorbed",
             "parallelism": "single GPU",
+            "launch": "hip graph of all timed steps" if use_graph else "eager",
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -215,14 +251,14 @@ def main():
 
     # ---- MALL-cold decode timing (outside the timed region): flush first
     if args.cold_steps and not args.profile_steps:
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)  # 512 MiB, read to evict
         cold = []
         for s in range(min(args.cold_steps, steps)):
             for l in range(L):
                 layers, pos, ln = per[s]
                 ck, cv, q = layers[l]
                 sess.append(l, ck, cv, pos)
-                flush.fill_(s & 0xff)
+                flush.sum()                      # reads 512 MiB: the 256 MiB last-level cache holds none of the cache
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record()
                 sess.decode(l, q, out, ctx + s + 1, lengths=ln, explicit=args.explicit)

@@ -70,6 +70,9 @@ typedef struct lr_attn_desc {
   int32_t qfmt;          /* lr_qfmt */
   int32_t io_dtype;      /* lr_dtype of q, B^K, B^V and out */
   int32_t max_splits;    /* 0 = automatic; n >= 1 caps the context splits per (b, h) */
+  int32_t wg_waves;      /* 0 = automatic; 4, 8 or 16 forces the wavefronts per work-group
+                            (16 is lowered to 8 for layers with a rank above 32) */
+  int32_t reserved;      /* must be 0 */
   const int32_t* rank_k; /* HOST [n_layers * n_heads], row-major (layer, head) */
   const int32_t* rank_v; /* HOST [n_layers * n_heads] */
 } lr_attn_desc;
@@ -102,8 +105,10 @@ typedef struct lr_attn_head_layout {
 } lr_attn_head_layout;
 
 /* Validate `desc` and build a host-only plan (no device memory is touched).
+ * max_splits and wg_waves only shape the decode launch; results agree to
+ * rounding whatever their values.
  * Errors: LR_EINVAL (null desc/out/rank pointers, non-positive sizes, bad
- * enum), LR_EUNSUPPORTED (head_dim != 128, n_heads > 128, rank not in
+ * enum, wg_waves not in {0, 4, 8, 16}, reserved != 0), LR_EUNSUPPORTED (head_dim != 128, n_heads > 128, rank not in
  * {8, 16, ..., 128}), LR_ERANGE (capacity beyond 2^24). */
 lr_status lr_attn_plan_create(const lr_attn_desc* desc, lr_attn_plan** out);
 void lr_attn_plan_destroy(lr_attn_plan* plan);
@@ -123,15 +128,11 @@ lr_status lr_attn_head_layout_get(const lr_attn_plan* plan, int32_t layer, int32
                                   lr_attn_head_layout* out);
 
 /* Workspace bytes needed by lr_attn_decode for any layer when called with
- * this max_len (0 means none is needed; the size is a multiple of 256).
- * It holds per-(b, h) arrival counters and split-context partials (m, l, u)
- * of Flash-Decoding-style context splitting. */
+ * this max_len (0 means none is needed; the size is a multiple of 256).  It
+ * holds the per-split partials (m, l, u) when a launch splits the context of
+ * each (b, h) Flash-Decoding style (few sequences and heads, long contexts).
+ * Its contents need no initialisation and are scratch between calls. */
 size_t lr_attn_workspace_bytes(const lr_attn_plan* plan, int32_t max_len);
-/* Zero the workspace counters with a small kernel on `stream`.  Call it once
- * after allocating a workspace; every completed decode call leaves the
- * counters at zero again.  Errors: LR_EINVAL, LR_EHIP. */
-lr_status lr_attn_workspace_init(const lr_attn_plan* plan, void* workspace, size_t ws_bytes,
-                                 void* stream);
 
 /* Quantise fp32 latents and write them at token slots pos[b] .. pos[b]+n_new-1
  * of every head of layer `layer` (LASER page, "System implementation": fused
@@ -164,9 +165,8 @@ lr_status lr_attn_append_latent(const lr_attn_plan* plan, int32_t layer, void* c
  *   q           device [batch][n_heads][128] io_dtype
  *   bk, bv      device factor tensors (lr_attn_factor_elems) io_dtype
  *   out         device [batch][n_heads][128] io_dtype
- *   workspace   device, >= lr_attn_workspace_bytes(max_len) bytes, prepared
- *               once by lr_attn_workspace_init; may be NULL when that is 0.
- *               Concurrent calls must not share a workspace.
+ *   workspace   device, >= lr_attn_workspace_bytes(max_len) bytes; may be
+ *               NULL when that is 0.  Concurrent calls must not share one.
  * All pointers 16-aligned.  Errors: LR_EINVAL, LR_ERANGE, LR_EWORKSPACE, LR_EHIP. */
 lr_status lr_attn_decode(const lr_attn_plan* plan, int32_t layer, const void* cache,
                          const int32_t* len, int32_t max_len, const void* q, const void* bk,

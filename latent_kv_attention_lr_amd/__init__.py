@@ -36,6 +36,7 @@ class lr_attn_desc(ctypes.Structure):
                 ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("qfmt", ctypes.c_int32),
                 ("io_dtype", ctypes.c_int32), ("max_splits", ctypes.c_int32),
+                ("wg_waves", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("rank_k", ctypes.POINTER(ctypes.c_int32)),
                 ("rank_v", ctypes.POINTER(ctypes.c_int32))]
 
@@ -84,7 +85,6 @@ def _load() -> ctypes.CDLL:
         "lr_attn_factor_elems": (SZ, [P, I32, I32]),
         "lr_attn_head_layout_get": (ctypes.c_int, [P, I32, I32, ctypes.POINTER(lr_attn_head_layout)]),
         "lr_attn_workspace_bytes": (SZ, [P, I32]),
-        "lr_attn_workspace_init": (ctypes.c_int, [P, P, SZ, P]),
         "lr_attn_append_latent": (ctypes.c_int, [P, I32, P, P, P, P, I32, P]),
         "lr_attn_decode": (ctypes.c_int, [P, I32, P, P, I32, P, P, P, ctypes.c_float, P, P, SZ, P]),
         "lr_attn_decode_explicit": (ctypes.c_int, [P, I32, P, P, I32, P, P, P, ctypes.c_float, P, P, SZ, P]),
@@ -132,13 +132,14 @@ def lr_attn_last_hip_error() -> int:
 
 def lr_attn_plan_create(n_layers: int, batch: int, n_heads: int, capacity: int, qfmt: int,
                         io_dtype: int, rank_k: Sequence[int], rank_v: Sequence[int],
-                        head_dim: int = LR_HEAD_DIM, max_splits: int = 0) -> int:
+                        head_dim: int = LR_HEAD_DIM, max_splits: int = 0,
+                        wg_waves: int = 0) -> int:
     """Returns an opaque plan handle (int); raises LrAttnError on a bad description."""
     n = n_layers * n_heads
     rk = (ctypes.c_int32 * max(n, 1))(*[int(r) for r in rank_k])
     rv = (ctypes.c_int32 * max(n, 1))(*[int(r) for r in rank_v])
     d = lr_attn_desc(n_layers, batch, n_heads, head_dim, capacity, qfmt, io_dtype, max_splits,
-                     ctypes.cast(rk, ctypes.POINTER(ctypes.c_int32)),
+                     wg_waves, 0, ctypes.cast(rk, ctypes.POINTER(ctypes.c_int32)),
                      ctypes.cast(rv, ctypes.POINTER(ctypes.c_int32)))
     h = ctypes.c_void_p()
     _check(_lib.lr_attn_plan_create(ctypes.byref(d), ctypes.byref(h)), "lr_attn_plan_create")
@@ -169,11 +170,6 @@ def lr_attn_head_layout_get(plan: int, layer: int, head: int) -> Dict[str, int]:
 
 def lr_attn_workspace_bytes(plan: int, max_len: int) -> int:
     return int(_lib.lr_attn_workspace_bytes(plan, max_len))
-
-
-def lr_attn_workspace_init(plan: int, workspace, ws_bytes: int, stream=None) -> None:
-    _check(_lib.lr_attn_workspace_init(plan, _ptr(workspace), ws_bytes, _stream(stream)),
-           "lr_attn_workspace_init")
 
 
 def lr_attn_append_latent(plan: int, layer: int, cache, ck, cv, pos, n_new: int, stream=None) -> None:

@@ -7,7 +7,8 @@
 //                     K/V latent codes of each (b, h) once from HBM, online
 //                     softmax in registers, accumulate the V latent, merge the
 //                     context splits, apply B^V_h once.
-//   k_ws_init         zero the split counters of a workspace.
+//   k_merge           merge the context-split partials of each (b, h) and
+//                     apply B^V_h (only when a launch splits the context).
 //
 // Cache tiles hold 64 tokens, one per lane of a wavefront; every lane load
 // is a 16-byte chunk and a wavefront load instruction reads 1 KiB of
@@ -92,6 +93,15 @@ __device__ __forceinline__ float lane63(float v) {
 
 __device__ __forceinline__ int uniform_i(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// A zero the compiler cannot see through: an address offset by it cannot be
+// hoisted out of a loop, so loop-invariant LDS reads stay where they are used
+// instead of occupying registers for the whole loop.
+__device__ __forceinline__ int opaque_zero() {
+  int z;
+  asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+  return z;
+}
+
 __device__ __forceinline__ float uniform(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
 }
@@ -109,117 +119,88 @@ struct AppendArgs {
   int64_t rows;
 };
 
-// int8: 16 values -> 16 bytes (or 8 -> 8 for a half chunk)
-template <int NV>
-__device__ __forceinline__ void pack_int8(const float* src, float s, uint32_t* w) {
-#pragma unroll
-  for (int j = 0; j < NV / 4; ++j) {
-    const float4 v = *reinterpret_cast<const float4*>(src + 4 * j);
-    const float vv[4] = {v.x, v.y, v.z, v.w};
-    uint32_t word = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      int q = 0;
-      if (s != 0.0f) q = int(fminf(fmaxf(rintf(vv[k] / s), -127.0f), 127.0f));
-      word |= (uint32_t(q) & 0xffu) << (8 * k);
-    }
-    w[j] = word;
-  }
+// max over the 16 lanes of a DPP row (every lane receives the result)
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<0xb1>(v, 0.f));
+  v = fmaxf(v, dpp<0x4e>(v, 0.f));
+  v = fmaxf(v, dpp<0x141>(v, 0.f));
+  v = fmaxf(v, dpp<0x140>(v, 0.f));
+  return v;
+}
+// max over the 4 lanes of a quad
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, dpp<0xb1>(v, 0.f));
+  v = fmaxf(v, dpp<0x4e>(v, 0.f));
+  return v;
 }
 
-// int4: NV values (8..32) of one group -> NV/2 bytes, element 2j in the low nibble
-template <int NV>
-__device__ __forceinline__ void pack_int4(const float* src, float s, uint32_t* w) {
-#pragma unroll
-  for (int j = 0; j < NV / 8; ++j) {
-    const float4 a = *reinterpret_cast<const float4*>(src + 8 * j);
-    const float4 b = *reinterpret_cast<const float4*>(src + 8 * j + 4);
-    const float vv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    uint32_t word = 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      int q = 0;
-      if (s != 0.0f) q = int(fminf(fmaxf(rintf(vv[k] / s), -7.0f), 7.0f));
-      word |= (uint32_t(q) & 0xfu) << (4 * k);
-    }
-    w[j] = word;
-  }
-}
-
-template <int NV>
-__device__ __forceinline__ float absmax(const float* src, float m) {
-#pragma unroll
-  for (int j = 0; j < NV / 4; ++j) {
-    const float4 v = *reinterpret_cast<const float4*>(src + 4 * j);
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-  }
-  return m;
-}
-
+// One latent row (one token, one head, K or V) per 16 lanes; lane s of the row
+// owns values [8s, 8s + 8), so a row of rank r uses r/8 lanes.  Magnitudes are
+// reduced with DPP inside the row (int8) or inside the quad that holds one
+// group of 32 ranks (int4); each lane then quantises and stores its 8 values.
 template <int QF>
 __global__ __launch_bounds__(256) void k_append(AppendArgs a, HeadTab ht) {
-  int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= a.rows) return;
-  // row order: (kv, h, b, j) with j fastest so neighbouring threads write
-  // neighbouring token slots of one plane
+  const int64_t gid = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int seg = threadIdx.x & 15;
+  int64_t idx = gid >> 4;                 // row: (kv, h, b, j), j fastest
+  const bool row_ok = idx < a.rows;
+  if (!row_ok) idx = 0;                   // keep the lanes of a row together for DPP
   const int j = int(idx % a.n_new);
   idx /= a.n_new;
   const int b = int(idx % a.B);
   idx /= a.B;
   const int h = int(idx % a.H);
   const int kv = int(idx / a.H);
-  const int slot = a.pos[b] + j;
-  if (slot < 0 || slot >= a.capacity) return;
   const uint32_t rr = ht.ranks[h], lo = ht.loff[h];
   const int r = int(kv ? rr >> 16 : rr & 0xffffu);
-  const int sum_r = kv ? a.sum_rv : a.sum_rk;
-  const float* src = (kv ? a.cv : a.ck) + (int64_t(b) * a.n_new + j) * sum_r + int(kv ? lo >> 16 : lo & 0xffffu);
-  const int rb = row_bytes(QF, r);
-  const int tb = tile_bytes(QF, r);
-  uint8_t* tile = a.cache + uint64_t(kv ? ht.vreg[h] : ht.kreg[h]) * kRegionAlign +
-                  (uint64_t(b) * a.n_tiles + (slot >> 6)) * tb;
-  const int lane = slot & 63;
+  const int slot = a.pos[b] + j;
+  const bool active = row_ok && 8 * seg < r && slot >= 0 && slot < a.capacity;
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (active) {
+    const int sum_r = kv ? a.sum_rv : a.sum_rk;
+    const float* src = (kv ? a.cv : a.ck) + (int64_t(b) * a.n_new + j) * sum_r +
+                       int(kv ? lo >> 16 : lo & 0xffffu) + 8 * seg;
+    const float4 x0 = *reinterpret_cast<const float4*>(src);
+    const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+    v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+    v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
+  m = QF == LR_Q_INT8_TOKEN ? row16_max(m) : quad_max(m);
+  if (!active) return;
 
+  const int rb = row_bytes(QF, r);
+  uint8_t* tile = a.cache + uint64_t(kv ? ht.vreg[h] : ht.kreg[h]) * kRegionAlign +
+                  (uint64_t(b) * a.n_tiles + (slot >> 6)) * tile_bytes(QF, r);
+  const int t = slot & 63;
   if constexpr (QF == LR_Q_INT8_TOKEN) {
-    float m = 0.0f;
-    for (int c = 0; c < r; c += 8) m = absmax<8>(src + c, m);
     const float s = m / 127.0f;
-    *reinterpret_cast<float*>(tile + 64 * rb + 4 * lane) = s;
-    for (int c = 0; 16 * c < r; ++c) {
-      uint32_t w[4];
-      if (16 * c + 16 <= r) {
-        pack_int8<16>(src + 16 * c, s, w);
-        *reinterpret_cast<uint4*>(tile + 1024 * c + 16 * lane) = make_uint4(w[0], w[1], w[2], w[3]);
-      } else {
-        pack_int8<8>(src + 16 * c, s, w);
-        *reinterpret_cast<uint2*>(tile + 1024 * c + 8 * lane) = make_uint2(w[0], w[1]);
-      }
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int q = s != 0.0f ? int(fminf(fmaxf(rintf(v[k] / s), -127.0f), 127.0f)) : 0;
+      w[k >> 2] |= (uint32_t(q) & 0xffu) << (8 * (k & 3));
     }
+    const int c = seg >> 1;                       // 16-byte chunk of this lane's 8 bytes
+    const int wc = min(16, rb - 16 * c);          // chunk width: 16, or 8 for the tail
+    *reinterpret_cast<uint2*>(tile + 1024 * c + wc * t + 8 * (seg & 1)) = make_uint2(w[0], w[1]);
+    if (seg == 0) *reinterpret_cast<float*>(tile + 64 * rb + 4 * t) = s;
   } else {
-    for (int g = 0; 32 * g < r; ++g) {
-      const int nv = min(32, r - 32 * g);
-      const float* gs = src + 32 * g;
-      float m = 0.0f;
-      for (int c = 0; c < nv; c += 8) m = absmax<8>(gs + c, m);
-      const _Float16 sh = _Float16(m / 7.0f);
-      const float s = float(sh);
-      *reinterpret_cast<uint16_t*>(tile + 64 * rb + 2 * (64 * g + lane)) = __builtin_bit_cast(uint16_t, sh);
-      uint32_t w[4];
-      uint8_t* dst = tile + 1024 * g;
-      if (nv == 32) {
-        pack_int4<32>(gs, s, w);
-        *reinterpret_cast<uint4*>(dst + 16 * lane) = make_uint4(w[0], w[1], w[2], w[3]);
-      } else if (nv == 24) {
-        pack_int4<24>(gs, s, w);
-        *reinterpret_cast<uint3*>(dst + 12 * lane) = make_uint3(w[0], w[1], w[2]);
-      } else if (nv == 16) {
-        pack_int4<16>(gs, s, w);
-        *reinterpret_cast<uint2*>(dst + 8 * lane) = make_uint2(w[0], w[1]);
-      } else {
-        pack_int4<8>(gs, s, w);
-        *reinterpret_cast<uint32_t*>(dst + 4 * lane) = w[0];
-      }
+    const _Float16 sh = _Float16(m / 7.0f);
+    const float s = float(sh);
+    uint32_t w = 0u;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int q = s != 0.0f ? int(fminf(fmaxf(rintf(v[k] / s), -7.0f), 7.0f)) : 0;
+      w |= (uint32_t(q) & 0xfu) << (4 * k);
     }
+    const int g = seg >> 2;                       // group of 32 ranks == 16-byte chunk
+    const int wc = min(16, rb - 16 * g);          // 16, or 4, 8, 12 for the tail group
+    *reinterpret_cast<uint32_t*>(tile + 1024 * g + wc * t + 4 * (seg & 3)) = w;
+    if ((seg & 3) == 0)
+      *reinterpret_cast<uint16_t*>(tile + 64 * rb + 2 * (64 * g + t)) = __builtin_bit_cast(uint16_t, sh);
   }
 }
 
@@ -234,8 +215,7 @@ struct DecodeArgs {
   const void* bk;
   const void* bv;
   void* out;
-  float* part;       // workspace partials [B*H][n_split][kPartStride]
-  int32_t* cnt;      // workspace counters [B*H]
+  float* part;       // workspace partials [B*H][n_split][kPartStride] (split launches only)
   float qscale;      // softmax scale * log2(e)
   int32_t B, H, n_tiles, max_len, n_split, tps;
 };
@@ -270,36 +250,102 @@ __device__ __forceinline__ void load_codes(const uint8_t* tile, int lane, int rb
 __device__ __forceinline__ float i8(uint32_t w, int k) { return float(int8_t(w >> (8 * k))); }
 __device__ __forceinline__ float i4(uint32_t w, int k) { return float(int32_t(w << (28 - 4 * k)) >> 28); }
 
-// sum_k qp[k] * code_k over one chunk (16 int8 or 32 int4 values)
-template <int QF>
-__device__ __forceinline__ float dot_chunk(const uint32_t* w, const float* qp) {
-  float acc = 0.0f;
-  if constexpr (QF == LR_Q_INT8_TOKEN) {
-#pragma unroll
-    for (int k = 0; k < 16; ++k) acc = fmaf(qp[k], i8(w[k >> 2], k & 3), acc);
-  } else {
-#pragma unroll
-    for (int k = 0; k < 32; ++k) acc = fmaf(qp[k], i4(w[k >> 3], k & 7), acc);
-  }
-  return acc;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ half2_t as_h2(uint32_t x) { return __builtin_bit_cast(half2_t, x); }
+
+// Eight two's-complement nibbles -> four packed fp16 pairs of exact codes.
+// (w & m) ^ k with k = 0x6408 / 0x6480 per half puts 1024 + (n ^ 8) = 1032 + c
+// (or 1024 + 16 (c + 8)) in each fp16 half, and one packed add removes the
+// bias.  Pairs: (c0, c4), (16 c1, 16 c5), (c2, c6), (16 c3, 16 c7).
+__device__ __forceinline__ void nibbles_to_h2(uint32_t w, half2_t* o) {
+  const uint32_t w8 = w >> 8;
+  const half2_t b1 = {_Float16(-1032.0f), _Float16(-1032.0f)};
+  const half2_t b16 = {_Float16(-1152.0f), _Float16(-1152.0f)};
+  o[0] = as_h2((w & 0x000F000Fu) ^ 0x64086408u) + b1;
+  o[1] = as_h2((w & 0x00F000F0u) ^ 0x64806480u) + b16;
+  o[2] = as_h2((w8 & 0x000F000Fu) ^ 0x64086408u) + b1;
+  o[3] = as_h2((w8 & 0x00F000F0u) ^ 0x64806480u) + b16;
 }
 
-template <int QF>
-__device__ __forceinline__ void acc_chunk(float* u, const uint32_t* w, float wt) {
+// Everything one lane needs from one 64-token tile: its token's K and V codes
+// and scales.
+template <int NC, int NG>
+struct TileRegs {
+  uint32_t kw[4 * NC], vw[4 * NC];
+  float sk[NG], sv[NG];
+};
+
+template <int QF, int NC, int NG>
+__device__ __forceinline__ void load_k(const uint8_t* kt, int lane, int rk, int rbk, TileRegs<NC, NG>& x) {
+  load_codes<NC>(kt, lane, rbk, x.kw);
   if constexpr (QF == LR_Q_INT8_TOKEN) {
-#pragma unroll
-    for (int k = 0; k < 16; ++k) u[k] = fmaf(wt, i8(w[k >> 2], k & 3), u[k]);
+    x.sk[0] = *reinterpret_cast<const float*>(kt + 64 * rbk + 4 * lane);
   } else {
 #pragma unroll
-    for (int k = 0; k < 32; ++k) u[k] = fmaf(wt, i4(w[k >> 3], k & 7), u[k]);
+    for (int g = 0; g < NG; ++g)
+      x.sk[g] = 32 * g < rk ? half_bits_to_f32(*reinterpret_cast<const uint16_t*>(kt + 64 * rbk + 2 * (64 * g + lane))) : 0.0f;
   }
+}
+
+template <int QF, int NC, int NG>
+__device__ __forceinline__ void load_v(const uint8_t* vt, int lane, int rv, int rbv, TileRegs<NC, NG>& x) {
+  load_codes<NC>(vt, lane, rbv, x.vw);
+  if constexpr (QF == LR_Q_INT8_TOKEN) {
+    x.sv[0] = *reinterpret_cast<const float*>(vt + 64 * rbv + 4 * lane);
+  } else {
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+      x.sv[g] = 32 * g < rv ? half_bits_to_f32(*reinterpret_cast<const uint16_t*>(vt + 64 * rbv + 2 * (64 * g + lane))) : 0.0f;
+  }
+}
+
+// The absorbed query q' as 32-bit words: fp32 values, or (packed int4 path)
+// fp16 pairs in the order nibbles_to_h2 produces.  Small operands live in
+// scalar registers (uniform across the wavefront); large ones are read from
+// LDS with broadcast loads where they are used.
+template <int QW, bool IN_REGS>
+struct QOperand {
+  uint32_t r[IN_REGS ? QW : 1];
+  const uint32_t* lds;
+  __device__ __forceinline__ uint32_t word(int i) const {
+    if constexpr (IN_REGS) return r[i];
+    else return lds[i];
+  }
+  __device__ __forceinline__ float f(int i) const { return __uint_as_float(word(i)); }
+};
+
+// One work-group per (b, h, split).  NW wavefronts take the split's 64-token
+// tiles round-robin; each lane owns one token of a tile.  Without context
+// splitting the group finishes the output itself; with it, the group writes
+// its partial (m, l, u) and k_merge combines them.
+//
+// int8 codes: the score is sum_i q'_i c_i (one SDWA convert + one FMA per
+// value), the V latent u_i += w c_i.  int4 codes with bf16 I/O: codes become
+// exact fp16 pairs (nibbles_to_h2), scores use 2-way fp16 dot products with
+// fp32 accumulation against q' rounded to fp16, and u accumulates with mixed
+// fp16 x fp32 FMAs.  int4 with fp32 I/O keeps q' in fp32 (bit-field extract +
+// convert + FMA) so it can be held to the tighter tolerance.
+// Waves per SIMD the register allocation must allow: enough bytes in flight
+// per CU to cover HBM latency without spilling.
+template <int QF, int R>
+constexpr int decode_occupancy() {
+  return R <= 32 ? 5 : R <= 64 ? (QF == LR_Q_INT8_TOKEN ? 3 : 4) : 2;
 }
 
 template <int QF, typename IOT, int R, int NW>
-__global__ __launch_bounds__(NW * 64) void k_decode(DecodeArgs a, HeadTab ht) {
-  constexpr int VPC = QF == LR_Q_INT8_TOKEN ? 16 : 32;  // values per 16-byte chunk
-  constexpr int NC = R / VPC;                            // chunks per row in the bucket
-  constexpr int NG = QF == LR_Q_INT8_TOKEN ? 1 : NC;     // scales per token
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(decode_occupancy<QF, R>(), decode_occupancy<QF, R>())))
+void k_decode(DecodeArgs a, HeadTab ht) {
+  constexpr bool INT8 = QF == LR_Q_INT8_TOKEN;
+  constexpr bool PACKED = !INT8 && sizeof(IOT) == 2;
+  constexpr int VPC = INT8 ? 16 : 32;                  // values per 16-byte chunk
+  constexpr int NC = R / VPC;                          // chunks per row in the bucket
+  constexpr int NG = INT8 ? 1 : NC;                    // scales per token
+  constexpr int QW = PACKED ? R / 2 : R;               // 32-bit words of q'
+  constexpr bool Q_IN_REGS = R <= 32;                  // 32 scalar registers at most
+  constexpr int RPW = (R + NW - 1) / NW;               // B rows per wavefront
+  constexpr bool PREFETCH_BV = RPW <= 4;
   using E = Elem<IOT>;
 
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
@@ -322,66 +368,116 @@ __global__ __launch_bounds__(NW * 64) void k_decode(DecodeArgs a, HeadTab ht) {
   const int unit = b * a.H + h;
 
   __shared__ float s_q[R];
+  __shared__ uint32_t s_qw[PACKED ? QW : 1];
   __shared__ float s_m[NW], s_l[NW];
   __shared__ float s_u[NW][R];
-  __shared__ int s_last;
+  __shared__ float s_o[NW][kHeadDim];
 
-  // ---- q'_i = scale * log2(e) * sum_j q_j B^K_h[i][j]  (one wavefront per i)
+  // ---- the first tile's loads go out before the prologue so their latency
+  //      overlaps the q' computation; so do this wavefront's B^V rows
+  const uint8_t* kplane = a.cache + uint64_t(kreg) * kRegionAlign + uint64_t(b) * a.n_tiles * tbk;
+  const uint8_t* vplane = a.cache + uint64_t(vreg) * kRegionAlign + uint64_t(b) * a.n_tiles * tbv;
+  TileRegs<NC, NG> cur;
+  int t = t0 + wid;
+  if (t < t1) {
+    load_k<QF>(kplane + size_t(t) * tbk, lane, rk, rbk, cur);
+    load_v<QF>(vplane + size_t(t) * tbv, lane, rv, rbv, cur);
+  }
+  const IOT* bvh = reinterpret_cast<const IOT*>(a.bv) + size_t(loff_v) * kHeadDim;
+  float bv0[RPW], bv1[RPW];
+  if constexpr (PREFETCH_BV) {
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) {
+      const int i = wid + k * NW;
+      bv0[k] = i < rv ? E::ld(bvh, size_t(i) * kHeadDim + 2 * lane) : 0.0f;
+      bv1[k] = i < rv ? E::ld(bvh, size_t(i) * kHeadDim + 2 * lane + 1) : 0.0f;
+    }
+  }
+
+  // ---- q'_i = scale * log2(e) * sum_j q_j B^K_h[i][j]: wavefront w takes
+  //      rows i = w, w + NW, ..., lane j columns 2j and 2j+1; all of a
+  //      wavefront's row loads are issued before any is used
   {
     const IOT* qrow = reinterpret_cast<const IOT*>(a.q) + size_t(unit) * kHeadDim;
     const float q0 = E::ld(qrow, 2 * lane), q1 = E::ld(qrow, 2 * lane + 1);
     const IOT* bkh = reinterpret_cast<const IOT*>(a.bk) + size_t(loff_k) * kHeadDim;
-    for (int i = wid; i < R; i += NW) {
-      float v = 0.0f;
-      if (i < rk) {
-        v = q0 * E::ld(bkh, size_t(i) * kHeadDim + 2 * lane);
-        v = fmaf(q1, E::ld(bkh, size_t(i) * kHeadDim + 2 * lane + 1), v);
-        v = wave_sum63(v);
+    float b0[RPW], b1[RPW];
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) {
+      const int i = wid + k * NW;
+      b0[k] = i < rk ? E::ld(bkh, size_t(i) * kHeadDim + 2 * lane) : 0.0f;
+      b1[k] = i < rk ? E::ld(bkh, size_t(i) * kHeadDim + 2 * lane + 1) : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) {
+      const int i = wid + k * NW;
+      if (i < R) {
+        const float v = wave_sum63(fmaf(q1, b1[k], q0 * b0[k]));
+        if (lane == 63) s_q[i] = v * a.qscale;
       }
-      if (lane == 63) s_q[i] = v * a.qscale;
     }
   }
   __syncthreads();
-  float qp[R];
+  QOperand<QW, Q_IN_REGS> qo;
+  if constexpr (PACKED) {
+    // word 4j + k of the packed operand pairs values 8j + k and 8j + k + 4,
+    // divided by 16 for odd k (those nibbles sit 4 bits higher)
+    if (tid < QW) {
+      const int j = tid >> 2, k = tid & 3;
+      const float sc = (k & 1) ? 0.0625f : 1.0f;
+      const half2_t hp = {_Float16(s_q[8 * j + k] * sc), _Float16(s_q[8 * j + k + 4] * sc)};
+      s_qw[tid] = __builtin_bit_cast(uint32_t, hp);
+    }
+    __syncthreads();
+    qo.lds = s_qw;
+  } else {
+    qo.lds = reinterpret_cast<const uint32_t*>(s_q);
+  }
+  if constexpr (Q_IN_REGS) {
 #pragma unroll
-  for (int i = 0; i < R; ++i) qp[i] = uniform(s_q[i]);
+    for (int i = 0; i < QW; ++i) qo.r[i] = uniform_i(int(qo.lds[i]));
+  }
 
   // ---- stream this split's tiles: one token per lane, online softmax
-  const uint8_t* kplane = a.cache + uint64_t(kreg) * kRegionAlign + uint64_t(b) * a.n_tiles * tbk;
-  const uint8_t* vplane = a.cache + uint64_t(vreg) * kRegionAlign + uint64_t(b) * a.n_tiles * tbv;
   float m = -__builtin_inff(), l = 0.0f;
   float u[R];
 #pragma unroll
   for (int i = 0; i < R; ++i) u[i] = 0.0f;
 
-  for (int t = t0 + wid; t < t1; t += NW) {
-    const uint8_t* kt = kplane + size_t(t) * tbk;
-    const uint8_t* vt = vplane + size_t(t) * tbv;
+  for (; t < t1; t += NW) {
     const bool valid = t * 64 + lane < len;
-    uint32_t kw[4 * NC], vw[4 * NC];
-    load_codes<NC>(kt, lane, rbk, kw);
-    load_codes<NC>(vt, lane, rbv, vw);
-    float sk[NG], sv[NG];
-    if constexpr (QF == LR_Q_INT8_TOKEN) {
-      sk[0] = *reinterpret_cast<const float*>(kt + 64 * rbk + 4 * lane);
-      sv[0] = *reinterpret_cast<const float*>(vt + 64 * rbv + 4 * lane);
-    } else {
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        sk[g] = 32 * g < rk ? half_bits_to_f32(*reinterpret_cast<const uint16_t*>(kt + 64 * rbk + 2 * (64 * g + lane))) : 0.0f;
-        sv[g] = 32 * g < rv ? half_bits_to_f32(*reinterpret_cast<const uint16_t*>(vt + 64 * rbv + 2 * (64 * g + lane))) : 0.0f;
-      }
-    }
+    if constexpr (!Q_IN_REGS) qo.lds = (PACKED ? s_qw : reinterpret_cast<const uint32_t*>(s_q)) + opaque_zero();
     float s = 0.0f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       if (c * VPC < rk) {
-        const float part = dot_chunk<QF>(kw + 4 * c, qp + c * VPC);
-        if constexpr (QF == LR_Q_INT8_TOKEN) s += part;
-        else s = fmaf(sk[c], part, s);
+        float part = 0.0f;
+        if constexpr (INT8) {
+#pragma unroll
+          for (int k = 0; k < 16; ++k) part = fmaf(qo.f(16 * c + k), i8(cur.kw[4 * c + (k >> 2)], k & 3), part);
+          s += part;
+        } else if constexpr (PACKED) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (32 * c + 8 * j < rk) {
+              half2_t hp[4];
+              nibbles_to_h2(cur.kw[4 * c + j], hp);
+#pragma unroll
+              for (int k = 0; k < 4; ++k)
+                part = __builtin_amdgcn_fdot2(hp[k], as_h2(qo.word(16 * c + 4 * j + k)), part, false);
+            }
+          }
+          s = fmaf(cur.sk[c], part, s);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 32; ++k) part = fmaf(qo.f(32 * c + k), i4(cur.kw[4 * c + (k >> 3)], k & 7), part);
+          s = fmaf(cur.sk[c], part, s);
+        }
       }
     }
-    if constexpr (QF == LR_Q_INT8_TOKEN) s *= sk[0];
+    if constexpr (INT8) s *= cur.sk[0];
+    const bool more = t + NW < t1;
+    if (more) load_k<QF>(kplane + size_t(t + NW) * tbk, lane, rk, rbk, cur);   // K regs are free now
     s = valid ? s : -__builtin_inff();
     if (s > m + kTau) {  // rare after the first tile: rescale the running sums
       const float al = __builtin_amdgcn_exp2f(m - s);
@@ -395,18 +491,43 @@ __global__ __launch_bounds__(NW * 64) void k_decode(DecodeArgs a, HeadTab ht) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       if (c * VPC < rv) {
-        const float wt = valid ? p * sv[QF == LR_Q_INT8_TOKEN ? 0 : c] : 0.0f;
-        acc_chunk<QF>(u + c * VPC, vw + 4 * c, wt);
+        const float wt = valid ? p * cur.sv[INT8 ? 0 : c] : 0.0f;
+        if constexpr (INT8) {
+#pragma unroll
+          for (int k = 0; k < 16; ++k) u[16 * c + k] = fmaf(wt, i8(cur.vw[4 * c + (k >> 2)], k & 3), u[16 * c + k]);
+        } else if constexpr (PACKED) {
+          const float wt16 = wt * 0.0625f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (32 * c + 8 * j < rv) {
+              half2_t hp[4];
+              nibbles_to_h2(cur.vw[4 * c + j], hp);
+              float* uu = u + 32 * c + 8 * j;
+              uu[0] = fmaf(float(hp[0].x), wt, uu[0]);
+              uu[4] = fmaf(float(hp[0].y), wt, uu[4]);
+              uu[1] = fmaf(float(hp[1].x), wt16, uu[1]);
+              uu[5] = fmaf(float(hp[1].y), wt16, uu[5]);
+              uu[2] = fmaf(float(hp[2].x), wt, uu[2]);
+              uu[6] = fmaf(float(hp[2].y), wt, uu[6]);
+              uu[3] = fmaf(float(hp[3].x), wt16, uu[3]);
+              uu[7] = fmaf(float(hp[3].y), wt16, uu[7]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 32; ++k) u[32 * c + k] = fmaf(wt, i4(cur.vw[4 * c + (k >> 3)], k & 7), u[32 * c + k]);
+        }
       }
     }
+    if (more) load_v<QF>(vplane + size_t(t + NW) * tbv, lane, rv, rbv, cur);   // V regs are free now
   }
 
-  // ---- merge the 64 lanes, then the NW wavefronts
+  // ---- merge the 64 lanes of each wavefront (DPP), publish per wavefront
   {
-    const float M = lane63(wave_max63(m));
-    const float f = (m == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+    const float Mw = lane63(wave_max63(m));
+    const float f = (m == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m - Mw);
     const float lw = wave_sum63(l * f);
-    if (lane == 63) { s_m[wid] = M; s_l[wid] = lw; }
+    if (lane == 63) { s_m[wid] = Mw; s_l[wid] = lw; }
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       if (i < rv) {
@@ -426,70 +547,139 @@ __global__ __launch_bounds__(NW * 64) void k_decode(DecodeArgs a, HeadTab ht) {
     fw[w] = (s_m[w] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(s_m[w] - M);
     L = fmaf(fw[w], s_l[w], L);
   }
-  float ui = 0.0f;
-  if (tid < rv) {
-#pragma unroll
-    for (int w = 0; w < NW; ++w) ui = fmaf(fw[w], s_u[w][tid], ui);
-  }
 
-  if (n_live > 1) {
-    // ---- publish this split's partial; the last split of (b, h) merges all
+  if (a.n_split > 1) {  // partial for k_merge (the kernel boundary orders it)
     float* part = a.part + (size_t(unit) * a.n_split + split) * kPartStride;
     if (tid == 0) { part[0] = M; part[1] = L; }
-    if (tid < rv) part[2 + tid] = ui;
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(a.cnt + unit, 1) == n_live - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    const float* pu = a.part + size_t(unit) * a.n_split * kPartStride;
-    M = -__builtin_inff();
-    for (int s2 = 0; s2 < n_live; ++s2) M = fmaxf(M, pu[size_t(s2) * kPartStride]);
-    L = 0.0f;
-    ui = 0.0f;
-    for (int s2 = 0; s2 < n_live; ++s2) {
-      const float* ps = pu + size_t(s2) * kPartStride;
-      const float fs = __builtin_amdgcn_exp2f(ps[0] - M);  // every live split saw a token
-      L = fmaf(fs, ps[1], L);
-      if (tid < rv) ui = fmaf(fs, ps[2 + tid], ui);
+    if (tid < rv) {
+      float ui = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) ui = fmaf(fw[w], s_u[w][tid], ui);
+      part[2 + tid] = ui;
     }
-    if (tid == 0) a.cnt[unit] = 0;  // leave the counter ready for the next call
+    return;
   }
 
-  // ---- o = (u / l) B^V_h
+  // ---- o = (u / l) B^V_h: wavefront w finishes u_i for its rows
+  //      i = w, w + NW, ... and multiplies them into columns 2j, 2j+1
+  const float inv_l = L > 0.0f ? 1.0f / L : 0.0f;
+  if constexpr (!PREFETCH_BV) {
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) {
+      const int i = wid + k * NW;
+      bv0[k] = i < rv ? E::ld(bvh, size_t(i) * kHeadDim + 2 * lane) : 0.0f;
+      bv1[k] = i < rv ? E::ld(bvh, size_t(i) * kHeadDim + 2 * lane + 1) : 0.0f;
+    }
+  }
+  float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+  for (int k = 0; k < RPW; ++k) {
+    const int i = wid + k * NW;
+    if (i < rv) {
+      float ui = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) ui = fmaf(fw[w], s_u[w][i], ui);
+      ui *= inv_l;
+      a0 = fmaf(ui, bv0[k], a0);
+      a1 = fmaf(ui, bv1[k], a1);
+    }
+  }
+  s_o[wid][2 * lane] = a0;
+  s_o[wid][2 * lane + 1] = a1;
   __syncthreads();
-  if (tid < rv) s_u[0][tid] = (L > 0.0f) ? ui / L : 0.0f;
-  __syncthreads();
-  const IOT* bvh = reinterpret_cast<const IOT*>(a.bv) + size_t(loff_v) * kHeadDim;
-  IOT* o = reinterpret_cast<IOT*>(a.out) + size_t(unit) * kHeadDim;
-  for (int j = tid; j < kHeadDim; j += NW * 64) {
+  if (tid < kHeadDim) {
     float acc = 0.0f;
-    for (int i = 0; i < rv; ++i) acc = fmaf(s_u[0][i], E::ld(bvh, size_t(i) * kHeadDim + j), acc);
-    E::st(o, j, acc);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) acc += s_o[w][tid];
+    E::st(reinterpret_cast<IOT*>(a.out) + size_t(unit) * kHeadDim, tid, acc);
   }
 }
 
-__global__ void k_ws_init(uint32_t* p, int64_t n) {
-  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
+// o[j] = sum_i v[i] B^V_h[i][j] for j < 128, v = u / l already in LDS (s_v),
+// for the split merge.  Wavefront w takes rows i = w, w + NW, ... < rv and
+// lane j columns 2j, 2j+1; the NW partial rows meet in LDS (s_o).
+template <typename IOT, int R, int NW>
+__device__ __forceinline__ void project_out(const float* s_v, float (*s_o)[kHeadDim], int rv,
+                                            const IOT* bvh, IOT* o, int tid) {
+  constexpr int RPW = (R + NW - 1) / NW;
+  const int wid = tid >> 6, lane = tid & 63;
+  float b0[RPW], b1[RPW];
+#pragma unroll
+  for (int k = 0; k < RPW; ++k) {
+    const int i = wid + k * NW;
+    b0[k] = i < rv ? Elem<IOT>::ld(bvh, size_t(i) * kHeadDim + 2 * lane) : 0.0f;
+    b1[k] = i < rv ? Elem<IOT>::ld(bvh, size_t(i) * kHeadDim + 2 * lane + 1) : 0.0f;
+  }
+  float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+  for (int k = 0; k < RPW; ++k) {
+    const int i = wid + k * NW;
+    if (i < rv) {
+      a0 = fmaf(s_v[i], b0[k], a0);
+      a1 = fmaf(s_v[i], b1[k], a1);
+    }
+  }
+  s_o[wid][2 * lane] = a0;
+  s_o[wid][2 * lane + 1] = a1;
+  __syncthreads();
+  if (tid < kHeadDim) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) acc += s_o[w][tid];
+    Elem<IOT>::st(o, tid, acc);
+  }
 }
 
-int rank_bucket(int r) { return r <= 32 ? 32 : r <= 64 ? 64 : r <= 96 ? 96 : 128; }
+// Flash-Decoding merge of the split partials of one (b, h), then o = (u/l) B^V_h:
+//   M = max_s m_s,  l = sum_s 2^(m_s - M) l_s,  u = sum_s 2^(m_s - M) u_s.
+template <typename IOT>
+__global__ __launch_bounds__(512) void k_merge(DecodeArgs a, HeadTab ht) {
+  const int tid = threadIdx.x;
+  const int unit = blockIdx.x;
+  const int b = unit / a.H, h = unit % a.H;
+  const int rv = int(uniform_i(int(ht.ranks[h])) >> 16);
+  const int loff_v = int(uniform_i(int(ht.loff[h])) >> 16);
+  const int len = min(max(a.len[b], 0), a.max_len);
+  const int n_live = max(1, ((len + 63) / 64 + a.tps - 1) / a.tps);
+  const float* pu = a.part + size_t(unit) * a.n_split * kPartStride;
+  __shared__ float s_v[LR_MAX_RANK];
+  __shared__ float s_o[8][kHeadDim];
+  float M = -__builtin_inff();
+  for (int s = 0; s < n_live; ++s) M = fmaxf(M, pu[size_t(s) * kPartStride]);
+  float L = 0.0f, ui = 0.0f;
+  for (int s = 0; s < n_live; ++s) {
+    const float* ps = pu + size_t(s) * kPartStride;
+    const float fs = (ps[0] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(ps[0] - M);
+    L = fmaf(fs, ps[1], L);
+    if (tid < rv) ui = fmaf(fs, ps[2 + tid], ui);
+  }
+  if (tid < rv) s_v[tid] = (L > 0.0f) ? ui / L : 0.0f;
+  __syncthreads();
+  project_out<IOT, LR_MAX_RANK, 8>(s_v, s_o, rv, reinterpret_cast<const IOT*>(a.bv) + size_t(loff_v) * kHeadDim,
+                                   reinterpret_cast<IOT*>(a.out) + size_t(unit) * kHeadDim, tid);
+}
 
 template <int QF, typename IOT, int R>
-hipError_t launch_decode_t(dim3 grid, hipStream_t st, const DecodeArgs& a, const HeadTab& t) {
-  hipLaunchKernelGGL((k_decode<QF, IOT, R, 4>), grid, dim3(256), 0, st, a, t);
+hipError_t launch_decode_r(int waves, dim3 grid, hipStream_t st, const DecodeArgs& a, const HeadTab& t) {
+  if constexpr (R <= 32) {
+    if (waves == 16) {
+      hipLaunchKernelGGL((k_decode<QF, IOT, R, 16>), grid, dim3(1024), 0, st, a, t);
+      return hipGetLastError();
+    }
+  }
+  if (waves == 8) hipLaunchKernelGGL((k_decode<QF, IOT, R, 8>), grid, dim3(512), 0, st, a, t);
+  else hipLaunchKernelGGL((k_decode<QF, IOT, R, 4>), grid, dim3(256), 0, st, a, t);
   return hipGetLastError();
 }
 
 template <int QF, typename IOT>
-hipError_t dispatch_rank(int bucket, dim3 grid, hipStream_t st, const DecodeArgs& a, const HeadTab& t) {
+hipError_t launch_decode_q(int bucket, int waves, dim3 grid, hipStream_t st, const DecodeArgs& a,
+                           const HeadTab& t) {
   switch (bucket) {
-    case 32: return launch_decode_t<QF, IOT, 32>(grid, st, a, t);
-    case 64: return launch_decode_t<QF, IOT, 64>(grid, st, a, t);
-    case 96: return launch_decode_t<QF, IOT, 96>(grid, st, a, t);
-    default: return launch_decode_t<QF, IOT, 128>(grid, st, a, t);
+    case 32: return launch_decode_r<QF, IOT, 32>(waves, grid, st, a, t);
+    case 64: return launch_decode_r<QF, IOT, 64>(waves, grid, st, a, t);
+    case 96: return launch_decode_r<QF, IOT, 96>(waves, grid, st, a, t);
+    default: return launch_decode_r<QF, IOT, 128>(waves, grid, st, a, t);
   }
 }
 
@@ -511,7 +701,7 @@ int launch_append(const lr_attn_plan& p, int32_t layer, void* cache, const float
   a.sum_rk = L.sum_rk;
   a.sum_rv = L.sum_rv;
   a.rows = int64_t(2) * a.H * a.B * n_new;
-  const dim3 grid(unsigned((a.rows + 255) / 256));
+  const dim3 grid(unsigned((a.rows * 16 + 255) / 256));
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (p.desc.qfmt == LR_Q_INT8_TOKEN)
     hipLaunchKernelGGL(k_append<LR_Q_INT8_TOKEN>, grid, dim3(256), 0, st, a, L.tab);
@@ -525,7 +715,7 @@ int launch_decode(const lr_attn_plan& p, int32_t layer, const void* cache, const
                   void* out, void* workspace, void* stream, bool explicit_form) {
   if (explicit_form) return int(hipErrorNotSupported);
   const auto& L = p.layers[layer];
-  const Split sp = choose_split(p, max_len);
+  const Split sp = choose_split(p, layer, max_len);
   DecodeArgs a;
   a.cache = static_cast<const uint8_t*>(cache);
   a.len = len;
@@ -533,10 +723,7 @@ int launch_decode(const lr_attn_plan& p, int32_t layer, const void* cache, const
   a.bk = bk;
   a.bv = bv;
   a.out = out;
-  const size_t units = size_t(p.desc.batch) * p.desc.n_heads;
-  a.cnt = static_cast<int32_t*>(workspace);
-  a.part = workspace ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + (units * 4 + 255) / 256 * 256)
-                     : nullptr;
+  a.part = static_cast<float*>(workspace);
   a.qscale = scale * kLog2e;
   a.B = p.desc.batch;
   a.H = p.desc.n_heads;
@@ -544,24 +731,21 @@ int launch_decode(const lr_attn_plan& p, int32_t layer, const void* cache, const
   a.max_len = max_len;
   a.n_split = sp.n_split;
   a.tps = sp.tiles_per_split;
-  const dim3 grid(unsigned(units * sp.n_split));
+  const unsigned units = unsigned(p.desc.batch) * unsigned(p.desc.n_heads);
+  const dim3 grid(units * unsigned(sp.n_split));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int bucket = rank_bucket(L.rk_max > L.rv_max ? L.rk_max : L.rv_max);
+  const int bucket = layer_bucket(L);
+  const bool bf = p.desc.io_dtype == LR_DT_BF16;
   hipError_t e;
-  if (p.desc.qfmt == LR_Q_INT8_TOKEN) {
-    e = p.desc.io_dtype == LR_DT_BF16 ? dispatch_rank<LR_Q_INT8_TOKEN, uint16_t>(bucket, grid, st, a, L.tab)
-                                      : dispatch_rank<LR_Q_INT8_TOKEN, float>(bucket, grid, st, a, L.tab);
-  } else {
-    e = p.desc.io_dtype == LR_DT_BF16 ? dispatch_rank<LR_Q_INT4_G32, uint16_t>(bucket, grid, st, a, L.tab)
-                                      : dispatch_rank<LR_Q_INT4_G32, float>(bucket, grid, st, a, L.tab);
-  }
-  return int(e);
-}
-
-int launch_workspace_init(void* workspace, size_t bytes, void* stream) {
-  const int64_t n = int64_t(bytes / 4);
-  hipLaunchKernelGGL(k_ws_init, dim3(unsigned((n + 255) / 256)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), static_cast<uint32_t*>(workspace), n);
+  if (p.desc.qfmt == LR_Q_INT8_TOKEN)
+    e = bf ? launch_decode_q<LR_Q_INT8_TOKEN, uint16_t>(bucket, sp.waves, grid, st, a, L.tab)
+           : launch_decode_q<LR_Q_INT8_TOKEN, float>(bucket, sp.waves, grid, st, a, L.tab);
+  else
+    e = bf ? launch_decode_q<LR_Q_INT4_G32, uint16_t>(bucket, sp.waves, grid, st, a, L.tab)
+           : launch_decode_q<LR_Q_INT4_G32, float>(bucket, sp.waves, grid, st, a, L.tab);
+  if (e != hipSuccess || sp.n_split == 1) return int(e);
+  if (bf) hipLaunchKernelGGL(k_merge<uint16_t>, dim3(units), dim3(512), 0, st, a, L.tab);
+  else hipLaunchKernelGGL(k_merge<float>, dim3(units), dim3(512), 0, st, a, L.tab);
   return int(hipGetLastError());
 }
 

@@ -30,18 +30,30 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 namespace lr {
 
-Split choose_split(const lr_attn_plan& p, int32_t max_len) {
-  // Flash-Decoding style: split each (b, h) context into equal runs of tiles so
-  // that the launch has enough work-groups to fill 256 CUs, but keep at least
-  // two tiles per wavefront so the per-group prologue (q' from B^K) and the
-  // partial merge stay small next to the streamed bytes.
+Split choose_split(const lr_attn_plan& p, int32_t layer, int32_t max_len) {
+  // Parallelism first comes from more wavefronts per (b, h) work-group: the
+  // smallest of 4, 8, 16 that puts >= 4096 wavefronts (16 per CU) in flight,
+  // 16 only for the rank-32 bucket (the only one that fits 128 VGPRs).  When that is still short of
+  // 4096 wavefronts (few sequences and heads, long contexts) the context of
+  // each (b, h) is split Flash-Decoding style and a second kernel merges the
+  // partials; every split keeps at least two tiles per wavefront.
   Split s;
-  s.waves = 4;
   const int64_t units = static_cast<int64_t>(p.desc.batch) * p.desc.n_heads;
   const int64_t tiles = ceil_div(max_len, kTile);
-  const int64_t target_groups = 2048;
-  int64_t n = ceil_div(target_groups, units);
-  n = std::min<int64_t>(n, ceil_div(tiles, 2 * s.waves));
+  const int nw_max = layer_bucket(p.layers[layer]) <= 32 ? 16 : 8;
+  int nw = 4;
+  if (p.desc.wg_waves > 0) {
+    nw = std::min(p.desc.wg_waves, nw_max);
+  } else {
+    while (nw < nw_max && units * nw < 4096) nw *= 2;
+    while (nw > 4 && (nw / 2) >= tiles) nw /= 2;   // no wavefront without a tile
+  }
+  s.waves = nw;
+  int64_t n = 1;
+  if (units * nw < 4096) {
+    n = ceil_div(4096, units * nw);
+    n = std::min<int64_t>(n, tiles / (2 * nw));
+  }
   if (p.desc.max_splits > 0) n = std::min<int64_t>(n, p.desc.max_splits);
   n = std::max<int64_t>(n, 1);
   const int64_t tps = ceil_div(tiles, n);
@@ -51,12 +63,14 @@ Split choose_split(const lr_attn_plan& p, int32_t max_len) {
 }
 
 size_t workspace_bytes(const lr_attn_plan& p, int32_t max_len) {
-  const Split s = choose_split(p, max_len);
-  if (s.n_split <= 1) return 0;
   const size_t units = static_cast<size_t>(p.desc.batch) * p.desc.n_heads;
-  const size_t counters = (units * 4 + 255) / 256 * 256;
-  const size_t parts = units * s.n_split * kPartStride * sizeof(float);
-  return counters + (parts + 255) / 256 * 256;
+  size_t need = 0;
+  for (int l = 0; l < p.desc.n_layers; ++l) {
+    const Split s = choose_split(p, l, max_len);
+    if (s.n_split > 1)
+      need = std::max(need, units * s.n_split * kPartStride * sizeof(float));
+  }
+  return (need + 255) / 256 * 256;
 }
 
 }  // namespace lr
@@ -71,6 +85,8 @@ lr_status lr_attn_plan_create(const lr_attn_desc* d, lr_attn_plan** out) {
   if (d->qfmt != LR_Q_INT8_TOKEN && d->qfmt != LR_Q_INT4_G32) return LR_EINVAL;
   if (d->io_dtype != LR_DT_BF16 && d->io_dtype != LR_DT_F32) return LR_EINVAL;
   if (d->max_splits < 0) return LR_EINVAL;
+  if (d->wg_waves != 0 && d->wg_waves != 4 && d->wg_waves != 8 && d->wg_waves != 16) return LR_EINVAL;
+  if (d->reserved != 0) return LR_EINVAL;
   if (d->head_dim != LR_HEAD_DIM) return LR_EUNSUPPORTED;
   if (d->n_heads > LR_MAX_HEADS) return LR_EUNSUPPORTED;
   if (d->capacity > (1 << 24)) return LR_ERANGE;
@@ -172,11 +188,6 @@ lr_status lr_attn_head_layout_get(const lr_attn_plan* p, int32_t layer, int32_t 
 size_t lr_attn_workspace_bytes(const lr_attn_plan* p, int32_t max_len) {
   if (!p || max_len < 1 || max_len > p->desc.capacity) return 0;
   return lr::workspace_bytes(*p, max_len);
-}
-
-lr_status lr_attn_workspace_init(const lr_attn_plan* p, void* ws, size_t ws_bytes, void* stream) {
-  if (!p || !ws || ws_bytes == 0 || !aligned(ws, 16)) return LR_EINVAL;
-  return hip_status(lr::launch_workspace_init(ws, ws_bytes, stream));
 }
 
 lr_status lr_attn_append_latent(const lr_attn_plan* p, int32_t layer, void* cache, const float* ck,

@@ -22,13 +22,18 @@ struct lr_attn_plan {
 
 namespace lr {
 
-// How a decode launch splits the context of each (b, h).
+// Shape of a decode launch.
 struct Split {
-  int32_t n_split;          // work-groups per (b, h)
+  int32_t n_split;          // work-groups per (b, h): context splits
   int32_t tiles_per_split;  // 64-token tiles per work-group
-  int32_t waves;            // wavefronts per work-group
+  int32_t waves;            // wavefronts per work-group: 4, 8 or 16
 };
-Split choose_split(const lr_attn_plan& p, int32_t max_len);
+// Register bucket of a layer: the largest rank rounded up to 32, 64, 96 or 128.
+inline int layer_bucket(const lr_attn_plan::Layer& L) {
+  const int r = L.rk_max > L.rv_max ? L.rk_max : L.rv_max;
+  return r <= 32 ? 32 : r <= 64 ? 64 : r <= 96 ? 96 : 128;
+}
+Split choose_split(const lr_attn_plan& p, int32_t layer, int32_t max_len);
 size_t workspace_bytes(const lr_attn_plan& p, int32_t max_len);
 
 // Kernel launchers (kernels.hip).  Arguments are already validated.  Each
@@ -38,6 +43,5 @@ int launch_append(const lr_attn_plan& p, int32_t layer, void* cache, const float
 int launch_decode(const lr_attn_plan& p, int32_t layer, const void* cache, const int32_t* len,
                   int32_t max_len, const void* q, const void* bk, const void* bv, float scale,
                   void* out, void* workspace, void* stream, bool explicit_form);
-int launch_workspace_init(void* workspace, size_t bytes, void* stream);
 
 }  // namespace lr

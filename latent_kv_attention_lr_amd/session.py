@@ -15,13 +15,13 @@ import torch
 from . import (LR_DT_BF16, LR_DT_F32, LR_HEAD_DIM, lr_attn_append_latent, lr_attn_cache_bytes,
                lr_attn_decode, lr_attn_decode_explicit, lr_attn_factor_elems,
                lr_attn_head_layout_get, lr_attn_latent_elems, lr_attn_plan_create,
-               lr_attn_plan_destroy, lr_attn_workspace_bytes, lr_attn_workspace_init)
+               lr_attn_plan_destroy, lr_attn_workspace_bytes)
 
 
 class DecodeSession:
     def __init__(self, n_layers: int, batch: int, n_heads: int, capacity: int, qfmt: int,
                  io_dtype: int, ranks_k: Sequence[Sequence[int]], ranks_v: Sequence[Sequence[int]],
-                 device="cuda", max_splits: int = 0):
+                 device="cuda", max_splits: int = 0, wg_waves: int = 0):
         self.n_layers, self.batch, self.n_heads, self.capacity = n_layers, batch, n_heads, capacity
         self.qfmt, self.io_dtype = qfmt, io_dtype
         self.device = torch.device(device)
@@ -30,7 +30,7 @@ class DecodeSession:
         flat_k = [r for row in self.ranks_k for r in row]
         flat_v = [r for row in self.ranks_v for r in row]
         self.plan = lr_attn_plan_create(n_layers, batch, n_heads, capacity, qfmt, io_dtype,
-                                        flat_k, flat_v, max_splits=max_splits)
+                                        flat_k, flat_v, max_splits=max_splits, wg_waves=wg_waves)
         self.torch_dtype = torch.bfloat16 if io_dtype == LR_DT_BF16 else torch.float32
         self.caches: List[torch.Tensor] = [
             torch.zeros(lr_attn_cache_bytes(self.plan, l), dtype=torch.uint8, device=self.device)
@@ -39,7 +39,6 @@ class DecodeSession:
         self.bv: List[Optional[torch.Tensor]] = [None] * n_layers
         self.ws_bytes = lr_attn_workspace_bytes(self.plan, capacity)
         self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
-        lr_attn_workspace_init(self.plan, self.workspace, self.workspace.numel())
         self.lengths = torch.zeros(batch, dtype=torch.int32, device=self.device)
 
     def close(self) -> None:

@@ -52,6 +52,8 @@ def _plan(**kw):
     (dict(qfmt=7), lr.LR_EINVAL),
     (dict(io_dtype=9), lr.LR_EINVAL),
     (dict(max_splits=-1), lr.LR_EINVAL),
+    (dict(wg_waves=6), lr.LR_EINVAL),
+    (dict(wg_waves=32), lr.LR_EINVAL),
 ])
 def test_plan_create_rejects(bad, status):
     with pytest.raises(lr.LrAttnError) as e:
@@ -108,12 +110,22 @@ def test_query_functions_reject_bad_indices():
 
 
 def test_workspace_grows_with_context_and_is_aligned():
-    p = lr.lr_attn_plan_create(1, 8, 32, 40000, lr.LR_Q_INT4_G32, lr.LR_DT_BF16, [48] * 32, [48] * 32)
+    # one sequence, 8 heads: few work-groups, so long contexts are split
+    p = lr.lr_attn_plan_create(1, 1, 8, 40000, lr.LR_Q_INT4_G32, lr.LR_DT_BF16, [48] * 8, [48] * 8)
     try:
         sizes = [lr.lr_attn_workspace_bytes(p, n) for n in (1, 64, 600, 4096, 32832, 40000)]
         assert all(s % 256 == 0 for s in sizes)
         assert sizes == sorted(sizes)
-        assert sizes[-1] > 0
+        assert sizes[0] == 0 and sizes[-1] > 0
+    finally:
+        lr.lr_attn_plan_destroy(p)
+
+
+def test_many_sequences_need_no_workspace():
+    # 16 x 32 (b, h) work-groups fill the GPU without splitting the context
+    p = lr.lr_attn_plan_create(1, 16, 32, 4224, lr.LR_Q_INT8_TOKEN, lr.LR_DT_BF16, [32] * 32, [32] * 32)
+    try:
+        assert lr.lr_attn_workspace_bytes(p, 4224) == 0
     finally:
         lr.lr_attn_plan_destroy(p)
 

@@ -19,7 +19,8 @@ import torch
 import harness
 import lrgen
 import oracle
-from latent_kv_attention_lr_amd import LR_DT_BF16, LR_DT_F32, LR_Q_INT4_G32, LR_Q_INT8_TOKEN
+from latent_kv_attention_lr_amd import (LR_DT_BF16, LR_DT_F32, LR_Q_INT4_G32, LR_Q_INT8_TOKEN,
+                                        lr_attn_workspace_bytes)
 from latent_kv_attention_lr_amd.session import DecodeSession
 from gpu_util import TOL_BF16, TOL_F32, oracle_many, oracle_quant, read_codes, within
 
@@ -146,10 +147,10 @@ def test_decode_small_workload_every_unit(io):
     _check_units(run, units, 0, TOL_BF16 if io == LR_DT_BF16 else TOL_F32, out)
 
 
-def _ragged_session(qfmt, io, max_splits, rng):
-    rk, rv = [32, 8, 96], [64, 16, 40]
-    B, cap = 6, 700
-    s = DecodeSession(1, B, 3, cap, qfmt, io, [rk], [rv], device=DEV, max_splits=max_splits)
+def _session(qfmt, io, max_splits, rng, B, cap, rk, rv):
+    """A session with random latents in every slot, random factors and q."""
+    H = len(rk)
+    s = DecodeSession(1, B, H, cap, qfmt, io, [rk], [rv], device=DEV, max_splits=max_splits)
     ck = (rng.standard_normal((B, cap, sum(rk))) * 1.3).astype(np.float32)
     cv = (rng.standard_normal((B, cap, sum(rv))) * 0.8).astype(np.float32)
     s.append(0, torch.from_numpy(ck).to(DEV), torch.from_numpy(cv).to(DEV),
@@ -158,29 +159,33 @@ def _ragged_session(qfmt, io, max_splits, rng):
     bk = (torch.from_numpy(rng.standard_normal((sum(rk), 128))) / 5).to(dt).to(DEV)
     bv = (torch.from_numpy(rng.standard_normal((sum(rv), 128))) / 5).to(dt).to(DEV)
     s.set_factors(0, bk.contiguous(), bv.contiguous())
-    q = torch.from_numpy(rng.standard_normal((B, 3, 128)) * 2).to(dt).to(DEV).contiguous()
+    q = torch.from_numpy(rng.standard_normal((B, H, 128)) * 2).to(dt).to(DEV).contiguous()
     return s, rk, rv, ck, cv, bk, bv, q
 
 
-@pytest.mark.parametrize("qfmt", [LR_Q_INT8_TOKEN, LR_Q_INT4_G32])
-@pytest.mark.parametrize("io", [LR_DT_BF16, LR_DT_F32])
-@pytest.mark.parametrize("max_splits", [0, 1])
-def test_decode_ragged_and_degenerate_lengths(qfmt, io, max_splits):
-    rng = np.random.default_rng(7 + 2 * qfmt + io)
-    s, rk, rv, ck, cv, bk, bv, q = _ragged_session(qfmt, io, max_splits, rng)
-    lens = [0, 1, 63, 64, 65, 700]
+def _ragged_session(qfmt, io, max_splits, rng):
+    return _session(qfmt, io, max_splits, rng, 6, 700, [32, 8, 96], [64, 16, 40])
+
+
+def _long_session(qfmt, io, max_splits, rng):
+    # 3 sequences x 2 heads over 8192 slots: few work-groups, so the launch
+    # splits each context and merges the partials in a second kernel
+    return _session(qfmt, io, max_splits, rng, 3, 8192, [32, 64], [48, 64])
+
+
+def _check_session(s, rk, rv, ck, cv, bk, bv, q, lens, qfmt, io, max_len):
     s.lengths.copy_(torch.tensor(lens, dtype=torch.int32))
     out = torch.full_like(q, float("nan"))
-    say(f"decode ragged qfmt={qfmt} io={io} max_splits={max_splits}")
-    s.decode(0, q, out, max_len=700)
+    s.decode(0, q, out, max_len=max_len)
     torch.cuda.synchronize()
     got = out.double().cpu().numpy()
     ok, ov = lrgen.head_offsets(rk), lrgen.head_offsets(rv)
     tol = TOL_BF16 if io == LR_DT_BF16 else TOL_F32
     qn, bkn, bvn = q.double().cpu().numpy(), bk.double().cpu().numpy(), bv.double().cpu().numpy()
+    H = len(rk)
     jobs, keys = [], []
     for b, T in enumerate(lens):
-        for h in range(3):
+        for h in range(H):
             jobs.append((ck[b, :T, ok[h]:ok[h] + rk[h]], cv[b, :T, ov[h]:ov[h] + rv[h]], qn[b, h],
                          bkn[ok[h]:ok[h] + rk[h]], bvn[ov[h]:ov[h] + rv[h]]))
             keys.append((b, h))
@@ -190,6 +195,29 @@ def test_decode_ragged_and_degenerate_lengths(qfmt, io, max_splits):
             assert np.array_equal(got[b, h], np.zeros(128)), "empty context must give zeros"
         else:
             assert within(got[b, h], ref, tol), (b, h, lens[b])
+    return out
+
+
+@pytest.mark.parametrize("qfmt", [LR_Q_INT8_TOKEN, LR_Q_INT4_G32])
+@pytest.mark.parametrize("io", [LR_DT_BF16, LR_DT_F32])
+@pytest.mark.parametrize("max_splits", [0, 1])
+def test_decode_ragged_and_degenerate_lengths(qfmt, io, max_splits):
+    rng = np.random.default_rng(7 + 2 * qfmt + io)
+    say(f"decode ragged qfmt={qfmt} io={io} max_splits={max_splits}")
+    sess = _ragged_session(qfmt, io, max_splits, rng)
+    _check_session(*sess, [0, 1, 63, 64, 65, 700], qfmt, io, 700)
+
+
+@pytest.mark.parametrize("qfmt", [LR_Q_INT8_TOKEN, LR_Q_INT4_G32])
+@pytest.mark.parametrize("io", [LR_DT_BF16, LR_DT_F32])
+def test_decode_context_split_path(qfmt, io):
+    rng = np.random.default_rng(30 + 2 * qfmt + io)
+    sess = _long_session(qfmt, io, 0, rng)
+    assert lr_attn_workspace_bytes(sess[0].plan, 8192) > 0, "this shape must split the context"
+    say(f"decode split path qfmt={qfmt} io={io}")
+    # one sequence within a single split, one ending inside a later split, one full
+    _check_session(*sess, [100, 3001, 8192], qfmt, io, 8192)
+    _check_session(*sess, [0, 8191, 2048], qfmt, io, 8192)
 
 
 def test_decode_max_len_clamps_longer_lengths():
@@ -206,21 +234,21 @@ def test_decode_max_len_clamps_longer_lengths():
     assert torch.equal(a, b)
 
 
-def test_decode_is_deterministic_and_leaves_counters_zero():
+@pytest.mark.parametrize("which", ["ragged", "split"])
+def test_decode_is_deterministic(which):
     rng = np.random.default_rng(11)
-    s, rk, rv, ck, cv, bk, bv, q = _ragged_session(LR_Q_INT4_G32, LR_DT_BF16, 0, rng)
-    s.lengths.fill_(700)
-    assert s.ws_bytes > 0
+    mk = _ragged_session if which == "ragged" else _long_session
+    s, rk, rv, ck, cv, bk, bv, q = mk(LR_Q_INT4_G32, LR_DT_BF16, 0, rng)
+    cap = s.capacity
+    s.lengths.fill_(cap)
     outs = []
-    say("decode determinism")
+    say(f"decode determinism {which}")
     for _ in range(3):
         o = torch.empty_like(q)
-        s.decode(0, q, o, max_len=700)
+        s.decode(0, q, o, max_len=cap)
         outs.append(o)
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
-    counters = s.workspace[: 6 * 3 * 4].view(torch.int32)
-    assert int(counters.abs().sum()) == 0
 
 
 # ---------------------------------------------------------------------------
@@ -268,3 +296,45 @@ def test_workload_parity_full_size(idx):
                 say(f"workload {idx}: layer {l} step {s} check {len(by_layer[l])} units")
                 worst = max(worst, _check_units(run, by_layer[l], s, TOL_BF16, out))
     say(f"workload {idx}: worst error / bound = {worst:.3g}")
+
+
+def test_graph_replay_matches_eager():
+    """Append + decode steps captured in one HIP graph reproduce the eager
+    outputs bit for bit on every replay (replays separated by eager work and
+    synchronisations)."""
+    w = lrgen.workload(0)
+    steps = 4
+    run = harness.WorkloadRun(w, io_dtype=LR_DT_BF16, device=DEV, steps=steps).setup()
+    sess = run.sess
+    ins = [run.step_tensors(0, s) for s in range(steps)]
+    lens = [torch.full((w.batch,), run.context + s + 1, dtype=torch.int32, device=DEV)
+            for s in range(steps)]
+    outs = [torch.empty(w.batch, w.n_heads, 128, dtype=torch.bfloat16, device=DEV)
+            for _ in range(steps)]
+
+    def steps_fn():
+        for s in range(steps):
+            ck, cv, q, pos = ins[s]
+            sess.append(0, ck, cv, pos)
+            sess.decode(0, q, outs[s], run.context + s + 1, lengths=lens[s])
+
+    say("graph: eager reference")
+    steps_fn()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            steps_fn()
+    torch.cuda.current_stream().wait_stream(cap)
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))          # eager work between replays
+        torch.cuda.synchronize()
+        say(f"graph: replay {rep}")
+        graph.replay()
+        torch.cuda.synchronize()
+        for s in range(steps):
+            assert torch.equal(outs[s], ref[s]), (rep, s)
