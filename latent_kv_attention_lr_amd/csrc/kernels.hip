@@ -659,6 +659,228 @@ __global__ __launch_bounds__(512) void k_merge(DecodeArgs a, HeadTab ht) {
                                    reinterpret_cast<IOT*>(a.out) + size_t(unit) * kHeadDim, tid);
 }
 
+// ---------------------------------------------------------------------------
+// decode, explicit reconstruction (matrix cores)
+// ---------------------------------------------------------------------------
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ uint32_t f32_to_bf16_exact(float v) { return __float_as_uint(v) >> 16; }
+
+// 8 codes (ranks k0 .. k0+7 of this lane's token) as the bf16 B operand of
+// v_mfma_f32_32x32x16_bf16; codes of magnitude <= 127 are exact in bf16.
+template <int QF>
+__device__ __forceinline__ bf16x8_t codes_to_bf16(const uint32_t* w, int k0) {
+  float v[8];
+  if constexpr (QF == LR_Q_INT8_TOKEN) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = i8(w[(k0 + e) >> 2], (k0 + e) & 3);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = i4(w[(k0 + e) >> 3], (k0 + e) & 7);
+  }
+  uint32_t p[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) p[e] = f32_to_bf16_exact(v[2 * e]) | (f32_to_bf16_exact(v[2 * e + 1]) << 16);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(p[0], p[1], p[2], p[3]));
+}
+
+// Codes of ranks [16 kb + 8 hl, +8) of token ti of a tile (kb: 16-rank block,
+// hl: which half of the block this lane holds), zero beyond the row width.
+template <int QF>
+__device__ __forceinline__ void load_codes8(const uint8_t* tile, int rb, int kb, int hl, int ti, uint32_t* w) {
+  if constexpr (QF == LR_Q_INT8_TOKEN) {
+    const int c = kb, wc = min(16, rb - 16 * c), off = 8 * hl;   // 8 bytes
+    if (off + 8 <= wc) {
+      const uint2 v = *reinterpret_cast<const uint2*>(tile + 1024 * c + wc * ti + off);
+      w[0] = v.x; w[1] = v.y;
+    } else { w[0] = 0; w[1] = 0; }
+  } else {
+    const int c = kb >> 1, wc = min(16, rb - 16 * c), off = 8 * (kb & 1) + 4 * hl;   // 4 bytes
+    w[0] = off + 4 <= wc ? *reinterpret_cast<const uint32_t*>(tile + 1024 * c + wc * ti + off) : 0u;
+    w[1] = 0;
+  }
+}
+
+// One work-group per (b, h); NW wavefronts take 64-token tiles round-robin and
+// treat each as two halves of 32 tokens.  For every 32-row block of d,
+// K^T = B^K^T C^T and V^T = B^V^T C^T are formed with
+// v_mfma_f32_32x32x16_bf16 (B^T staged in LDS, codes as exact bf16): lane l
+// then holds 16 rows of column (token) l % 32.  Scores are the dot of K^T with
+// q over d (two lanes per token, halves added with a cross-half swap), and
+// o^T accumulates p_t V^T.  int4 group scales are applied per group to the
+// fp32 accumulators, so nothing is rounded beyond fp32.
+template <int QF, int R, int NW>
+__global__ __launch_bounds__(NW * 64) void k_decode_explicit(DecodeArgs a, HeadTab ht) {
+  constexpr bool INT8 = QF == LR_Q_INT8_TOKEN;
+  constexpr int VPC = INT8 ? 16 : 32;
+  constexpr int NC = R / VPC;
+  constexpr int NG = INT8 ? 1 : NC;
+  constexpr int KB = R / 16;                 // 16-rank blocks
+  constexpr int LDR = R + 8;                 // padded LDS row (bf16 elements)
+  using E = Elem<uint16_t>;
+
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int b = int(blockIdx.x) % a.B;
+  const int h = uniform_i(int(ht.order[int(blockIdx.x) / a.B]));
+  const uint32_t rr = uniform_i(int(ht.ranks[h])), lo = uniform_i(int(ht.loff[h]));
+  const int rk = int(rr & 0xffffu), rv = int(rr >> 16);
+  const int loff_k = int(lo & 0xffffu), loff_v = int(lo >> 16);
+  const uint32_t kreg = uniform_i(int(ht.kreg[h])), vreg = uniform_i(int(ht.vreg[h]));
+  const int rbk = row_bytes(QF, rk), rbv = row_bytes(QF, rv);
+  const int tbk = tile_bytes(QF, rk), tbv = tile_bytes(QF, rv);
+  const int len = min(max(a.len[b], 0), a.max_len);
+  const int ntiles = (len + 63) >> 6;
+  const int unit = b * a.H + h;
+
+  __shared__ uint16_t s_bt[2][kHeadDim * LDR];   // B^K^T, B^V^T: [d][rank]
+  __shared__ float s_q[kHeadDim];
+  __shared__ float s_m[NW], s_l[NW];
+  __shared__ float s_o[NW][kHeadDim];
+
+  // ---- stage B^K^T and B^V^T (zero beyond the ranks) and q * scale * log2(e)
+  {
+    const uint16_t* bk = reinterpret_cast<const uint16_t*>(a.bk) + size_t(loff_k) * kHeadDim;
+    const uint16_t* bv = reinterpret_cast<const uint16_t*>(a.bv) + size_t(loff_v) * kHeadDim;
+    for (int e = tid; e < R * kHeadDim; e += NW * 64) {
+      const int k = e / kHeadDim, d = e % kHeadDim;
+      s_bt[0][d * LDR + k] = k < rk ? bk[size_t(k) * kHeadDim + d] : uint16_t(0);
+      s_bt[1][d * LDR + k] = k < rv ? bv[size_t(k) * kHeadDim + d] : uint16_t(0);
+    }
+    if (tid < kHeadDim)
+      s_q[tid] = E::ld(reinterpret_cast<const uint16_t*>(a.q) + size_t(unit) * kHeadDim, tid) * a.qscale;
+  }
+  __syncthreads();
+
+  const uint8_t* kplane = a.cache + uint64_t(kreg) * kRegionAlign + uint64_t(b) * a.n_tiles * tbk;
+  const uint8_t* vplane = a.cache + uint64_t(vreg) * kRegionAlign + uint64_t(b) * a.n_tiles * tbv;
+  const int hl = lane >> 5, col = lane & 31;
+  float m = -__builtin_inff(), l = 0.0f;
+  float o[4][16];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+
+  for (int t = wid; t < ntiles; t += NW) {
+    const uint8_t* kt = kplane + size_t(t) * tbk;
+    const uint8_t* vt = vplane + size_t(t) * tbv;
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+      const int ti = 32 * half + col;              // token of this lane within the tile
+      const bool valid = t * 64 + ti < len;
+      uint32_t kw[KB][2], vw[KB][2];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        load_codes8<QF>(kt, rbk, kb, hl, ti, kw[kb]);
+        load_codes8<QF>(vt, rbv, kb, hl, ti, vw[kb]);
+      }
+      float sk[NG], sv[NG];
+      if constexpr (INT8) {
+        sk[0] = *reinterpret_cast<const float*>(kt + 64 * rbk + 4 * ti);
+        sv[0] = *reinterpret_cast<const float*>(vt + 64 * rbv + 4 * ti);
+      } else {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          sk[g] = 32 * g < rk ? half_bits_to_f32(*reinterpret_cast<const uint16_t*>(kt + 64 * rbk + 2 * (64 * g + ti))) : 0.0f;
+          sv[g] = 32 * g < rv ? half_bits_to_f32(*reinterpret_cast<const uint16_t*>(vt + 64 * rbv + 2 * (64 * g + ti))) : 0.0f;
+        }
+      }
+      // ---- k_t rebuilt block by block, dotted with q
+      float s = 0.0f;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        float kd[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) kd[r] = 0.0f;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          f32x16_t acc = {};
+#pragma unroll
+          for (int kb = (INT8 ? 0 : 2 * g); kb < (INT8 ? KB : 2 * g + 2); ++kb) {
+            if (16 * kb < rk) {
+              const bf16x8_t bt = __builtin_bit_cast(bf16x8_t,
+                  *reinterpret_cast<const uint4*>(&s_bt[0][(32 * db + col) * LDR + 16 * kb + 8 * hl]));
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bt, codes_to_bf16<QF>(kw[kb], 0), acc, 0, 0, 0);
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) kd[r] = fmaf(sk[g], acc[r], kd[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s = fmaf(kd[r], s_q[32 * db + 8 * (r >> 2) + 4 * hl + (r & 3)], s);
+      }
+      s += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (lane ^ 32), __builtin_bit_cast(int, s)));
+      s = valid ? s : -__builtin_inff();
+      if (s > m + kTau) {
+        const float al = __builtin_amdgcn_exp2f(m - s);
+        l *= al;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= al;
+        m = s;
+      }
+      const float p = valid ? __builtin_amdgcn_exp2f(s - m) : 0.0f;
+      l += p;
+      // ---- v_t rebuilt block by block, accumulated with weight p_t
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          f32x16_t acc = {};
+#pragma unroll
+          for (int kb = (INT8 ? 0 : 2 * g); kb < (INT8 ? KB : 2 * g + 2); ++kb) {
+            if (16 * kb < rv) {
+              const bf16x8_t bt = __builtin_bit_cast(bf16x8_t,
+                  *reinterpret_cast<const uint4*>(&s_bt[1][(32 * db + col) * LDR + 16 * kb + 8 * hl]));
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bt, codes_to_bf16<QF>(vw[kb], 0), acc, 0, 0, 0);
+            }
+          }
+          const float wt = valid ? p * sv[g] : 0.0f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] = fmaf(wt, acc[r], o[db][r]);
+        }
+      }
+    }
+  }
+
+  // ---- merge: lanes of one half hold the same tokens' d-rows; both halves
+  //      saw the same scores, so m and l are taken from the lower half
+  const float Mw = lane63(wave_max63(m));
+  const float f = (m == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m - Mw);
+  const float lw = wave_sum63(hl == 1 ? l * f : 0.0f);
+  if (lane == 63) { s_m[wid] = Mw; s_l[wid] = lw; }
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v = o[db][r] * f;                       // sum over the 32 lanes of this half
+      v += dpp<0xb1>(v, 0.f);
+      v += dpp<0x4e>(v, 0.f);
+      v += dpp<0x141>(v, 0.f);
+      v += dpp<0x140>(v, 0.f);
+      v += dpp<0x142, 0xa>(v, 0.f);                 // lanes 31 and 63 hold the half sums
+      if (col == 31) s_o[wid][32 * db + 8 * (r >> 2) + 4 * hl + (r & 3)] = v;
+    }
+  }
+  __syncthreads();
+  if (tid < kHeadDim) {
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w]);
+    float L = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float fw = (s_m[w] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(s_m[w] - M);
+      L = fmaf(fw, s_l[w], L);
+      acc = fmaf(fw, s_o[w][tid], acc);
+    }
+    E::st(reinterpret_cast<uint16_t*>(a.out) + size_t(unit) * kHeadDim, tid, L > 0.0f ? acc / L : 0.0f);
+  }
+}
+
 template <int QF, typename IOT, int R>
 hipError_t launch_decode_r(int waves, dim3 grid, hipStream_t st, const DecodeArgs& a, const HeadTab& t) {
   if constexpr (R <= 32) {
@@ -710,12 +932,27 @@ int launch_append(const lr_attn_plan& p, int32_t layer, void* cache, const float
   return int(hipGetLastError());
 }
 
+template <int QF>
+hipError_t launch_explicit_q(int bucket, int waves, dim3 grid, hipStream_t st, const DecodeArgs& a,
+                             const HeadTab& t) {
+#define LR_EXPLICIT(RR)                                                                       \
+  if (waves == 8) hipLaunchKernelGGL((k_decode_explicit<QF, RR, 8>), grid, dim3(512), 0, st, a, t); \
+  else hipLaunchKernelGGL((k_decode_explicit<QF, RR, 4>), grid, dim3(256), 0, st, a, t);
+  switch (bucket) {
+    case 32: LR_EXPLICIT(32) break;
+    case 64: LR_EXPLICIT(64) break;
+    case 96: LR_EXPLICIT(96) break;
+    default: LR_EXPLICIT(128) break;
+  }
+#undef LR_EXPLICIT
+  return hipGetLastError();
+}
+
 int launch_decode(const lr_attn_plan& p, int32_t layer, const void* cache, const int32_t* len,
                   int32_t max_len, const void* q, const void* bk, const void* bv, float scale,
                   void* out, void* workspace, void* stream, bool explicit_form) {
-  if (explicit_form) return int(hipErrorNotSupported);
   const auto& L = p.layers[layer];
-  const Split sp = choose_split(p, layer, max_len);
+  const Split sp = explicit_form ? explicit_split(p, layer, max_len) : choose_split(p, layer, max_len);
   DecodeArgs a;
   a.cache = static_cast<const uint8_t*>(cache);
   a.len = len;
@@ -737,6 +974,11 @@ int launch_decode(const lr_attn_plan& p, int32_t layer, const void* cache, const
   const int bucket = layer_bucket(L);
   const bool bf = p.desc.io_dtype == LR_DT_BF16;
   hipError_t e;
+  if (explicit_form) {
+    e = p.desc.qfmt == LR_Q_INT8_TOKEN ? launch_explicit_q<LR_Q_INT8_TOKEN>(bucket, sp.waves, grid, st, a, L.tab)
+                                       : launch_explicit_q<LR_Q_INT4_G32>(bucket, sp.waves, grid, st, a, L.tab);
+    return int(e);
+  }
   if (p.desc.qfmt == LR_Q_INT8_TOKEN)
     e = bf ? launch_decode_q<LR_Q_INT8_TOKEN, uint16_t>(bucket, sp.waves, grid, st, a, L.tab)
            : launch_decode_q<LR_Q_INT8_TOKEN, float>(bucket, sp.waves, grid, st, a, L.tab);

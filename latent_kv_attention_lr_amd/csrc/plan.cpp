@@ -62,6 +62,18 @@ Split choose_split(const lr_attn_plan& p, int32_t layer, int32_t max_len) {
   return s;
 }
 
+Split explicit_split(const lr_attn_plan& p, int32_t layer, int32_t max_len) {
+  (void)layer;
+  Split s;
+  const int64_t units = static_cast<int64_t>(p.desc.batch) * p.desc.n_heads;
+  const int64_t tiles = ceil_div(max_len, kTile);
+  s.waves = (units * 4 < 4096 && tiles >= 8) ? 8 : 4;
+  if (p.desc.wg_waves == 4 || p.desc.wg_waves == 8) s.waves = p.desc.wg_waves;
+  s.n_split = 1;
+  s.tiles_per_split = static_cast<int32_t>(tiles);
+  return s;
+}
+
 size_t workspace_bytes(const lr_attn_plan& p, int32_t max_len) {
   const size_t units = static_cast<size_t>(p.desc.batch) * p.desc.n_heads;
   size_t need = 0;
@@ -215,7 +227,8 @@ static lr_status decode_common(const lr_attn_plan* p, int32_t layer, const void*
   if (!aligned(cache, 256) || !aligned(len, 4) || !aligned(q, 16) || !aligned(bk, 16) ||
       !aligned(bv, 16) || !aligned(out, 16))
     return LR_EINVAL;
-  const size_t need = lr::workspace_bytes(*p, max_len);
+  if (explicit_form && p->desc.io_dtype != LR_DT_BF16) return LR_EUNSUPPORTED;
+  const size_t need = explicit_form ? 0 : lr::workspace_bytes(*p, max_len);
   if (need > 0 && (!ws || ws_bytes < need)) return LR_EWORKSPACE;
   if (ws && !aligned(ws, 16)) return LR_EINVAL;
   return hip_status(lr::launch_decode(*p, layer, cache, len, max_len, q, bk, bv, scale, out,

@@ -34,6 +34,8 @@ inline int layer_bucket(const lr_attn_plan::Layer& L) {
   return r <= 32 ? 32 : r <= 64 ? 64 : r <= 96 ? 96 : 128;
 }
 Split choose_split(const lr_attn_plan& p, int32_t layer, int32_t max_len);
+// The explicit-reconstruction kernel never splits the context: 4 or 8 waves.
+Split explicit_split(const lr_attn_plan& p, int32_t layer, int32_t max_len);
 size_t workspace_bytes(const lr_attn_plan& p, int32_t max_len);
 
 // Kernel launchers (kernels.hip).  Arguments are already validated.  Each

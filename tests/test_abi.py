@@ -180,10 +180,19 @@ def test_decode_argument_errors_before_launch(fn):
         assert _decode(p, fn, scale=float("inf")) == lr.LR_EINVAL
         assert _decode(p, fn, q=FAKE + 8) == lr.LR_EINVAL
         assert _decode(p, fn, cache=FAKE + 64) == lr.LR_EINVAL
-        need = lr.lr_attn_workspace_bytes(p, 3000)
-        assert need > 0
-        assert _decode(p, fn, max_len=3000, ws=None) == lr.LR_EWORKSPACE
-        assert _decode(p, fn, max_len=3000, ws_bytes=need - 1) == lr.LR_EWORKSPACE
+        if fn == "lr_attn_decode":   # the explicit form needs no workspace
+            need = lr.lr_attn_workspace_bytes(p, 3000)
+            assert need > 0
+            assert _decode(p, fn, max_len=3000, ws=None) == lr.LR_EWORKSPACE
+            assert _decode(p, fn, max_len=3000, ws_bytes=need - 1) == lr.LR_EWORKSPACE
+    finally:
+        lr.lr_attn_plan_destroy(p)
+
+
+def test_explicit_form_rejects_fp32_io_before_launch():
+    p = _plan(io_dtype=lr.LR_DT_F32)
+    try:
+        assert _decode(p, "lr_attn_decode_explicit") == lr.LR_EUNSUPPORTED
     finally:
         lr.lr_attn_plan_destroy(p)
 

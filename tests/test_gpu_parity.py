@@ -19,8 +19,8 @@ import torch
 import harness
 import lrgen
 import oracle
-from latent_kv_attention_lr_amd import (LR_DT_BF16, LR_DT_F32, LR_Q_INT4_G32, LR_Q_INT8_TOKEN,
-                                        lr_attn_workspace_bytes)
+from latent_kv_attention_lr_amd import (LR_DT_BF16, LR_DT_F32, LR_EUNSUPPORTED, LR_Q_INT4_G32,
+                                        LR_Q_INT8_TOKEN, LrAttnError, lr_attn_workspace_bytes)
 from latent_kv_attention_lr_amd.session import DecodeSession
 from gpu_util import TOL_BF16, TOL_F32, oracle_many, oracle_quant, read_codes, within
 
@@ -173,10 +173,10 @@ def _long_session(qfmt, io, max_splits, rng):
     return _session(qfmt, io, max_splits, rng, 3, 8192, [32, 64], [48, 64])
 
 
-def _check_session(s, rk, rv, ck, cv, bk, bv, q, lens, qfmt, io, max_len):
+def _check_session(s, rk, rv, ck, cv, bk, bv, q, lens, qfmt, io, max_len, explicit=False):
     s.lengths.copy_(torch.tensor(lens, dtype=torch.int32))
     out = torch.full_like(q, float("nan"))
-    s.decode(0, q, out, max_len=max_len)
+    s.decode(0, q, out, max_len=max_len, explicit=explicit)
     torch.cuda.synchronize()
     got = out.double().cpu().numpy()
     ok, ov = lrgen.head_offsets(rk), lrgen.head_offsets(rv)
@@ -206,6 +206,24 @@ def test_decode_ragged_and_degenerate_lengths(qfmt, io, max_splits):
     say(f"decode ragged qfmt={qfmt} io={io} max_splits={max_splits}")
     sess = _ragged_session(qfmt, io, max_splits, rng)
     _check_session(*sess, [0, 1, 63, 64, 65, 700], qfmt, io, 700)
+
+
+@pytest.mark.parametrize("qfmt", [LR_Q_INT8_TOKEN, LR_Q_INT4_G32])
+def test_decode_explicit_ragged_and_degenerate_lengths(qfmt):
+    rng = np.random.default_rng(50 + qfmt)
+    say(f"decode explicit ragged qfmt={qfmt}")
+    sess = _ragged_session(qfmt, LR_DT_BF16, 0, rng)
+    _check_session(*sess, [0, 1, 63, 64, 65, 700], qfmt, LR_DT_BF16, 700, explicit=True)
+    sess = _long_session(qfmt, LR_DT_BF16, 0, rng)
+    _check_session(*sess, [100, 3001, 8192], qfmt, LR_DT_BF16, 8192, explicit=True)
+
+
+def test_decode_explicit_rejects_fp32_io():
+    rng = np.random.default_rng(1)
+    s, rk, rv, ck, cv, bk, bv, q = _ragged_session(LR_Q_INT8_TOKEN, LR_DT_F32, 0, rng)
+    with pytest.raises(LrAttnError) as e:
+        s.decode(0, q, torch.empty_like(q), max_len=700, explicit=True)
+    assert e.value.status == LR_EUNSUPPORTED
 
 
 @pytest.mark.parametrize("qfmt", [LR_Q_INT8_TOKEN, LR_Q_INT4_G32])
@@ -295,6 +313,13 @@ def test_workload_parity_full_size(idx):
                 torch.cuda.synchronize()
                 say(f"workload {idx}: layer {l} step {s} check {len(by_layer[l])} units")
                 worst = max(worst, _check_units(run, by_layer[l], s, TOL_BF16, out))
+                if s == checked[0]:
+                    _, _, q, _ = run.step_tensors(l, s)
+                    ex = torch.empty_like(out)
+                    run.sess.decode(l, q, ex, run.context + s + 1, explicit=True)
+                    torch.cuda.synchronize()
+                    say(f"workload {idx}: layer {l} step {s} explicit form")
+                    worst = max(worst, _check_units(run, by_layer[l], s, TOL_BF16, ex))
     say(f"workload {idx}: worst error / bound = {worst:.3g}")
 
 
