@@ -26,6 +26,22 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "latent_kv_attention_lr_amd", "csrc", "kernels.hip")
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+
+
+def measured_traffic(workload_name, kernel_form):
+    """HBM bytes per decode launch from committed counter runs, if they were
+    taken on the current kernel source (else None)."""
+    import glob
+    import hashlib
+    src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    for f in glob.glob(os.path.join(TRAFFIC_DIR, "traffic_*.json")):
+        d = json.load(open(f))
+        if d.get("workload") == workload_name and d.get("decode_form") == kernel_form \
+                and d.get("kernels_hip_sha256") == src:
+            return d["hbm_bytes_per_launch"]
+    return None
 
 
 def parse():
@@ -42,6 +58,9 @@ def parse():
                     help="only run warmup + this many steps (for rocprofv3); no CPU baseline")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch the timed steps eagerly instead of replaying one HIP graph")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one device copy of this many MiB first (reads and writes that many "
+                         "bytes), the reference for scaling FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
 
 
@@ -136,6 +155,13 @@ def main():
         pos = torch.full((w.batch,), ctx + s, dtype=torch.int32, device=dev)
         per.append((layers, pos, ln))
     out = torch.empty(w.batch, w.n_heads, w.head_dim, dtype=torch.bfloat16, device=dev)
+    if args.copy_calibration_mib:
+        src = torch.ones(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(s, ev=None):
         layers, pos, ln = per[s]
@@ -242,7 +268,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": measured_traffic(w.name, "explicit" if args.explicit else "absorbed"),
             "kernel": "k_decode", "bytes_per_launch": bytes_launch,
             "bytes_per_token_per_bh": per_tok_bytes / w.n_heads,
             "avg_launch_us": dec_avg_s * 1e6,
