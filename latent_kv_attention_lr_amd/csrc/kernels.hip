@@ -221,29 +221,22 @@ struct DecodeArgs {
 };
 
 // Codes of one 64-token tile for this lane: NC chunks of 16 bytes.  The
-// runtime row width rb (bytes) may end inside the bucket; missing chunks are
-// zero and the tail chunk may be 4, 8 or 12 bytes wide.
+// runtime row width rb (bytes) may end inside the bucket.  Every load is
+// issued unconditionally at an in-bounds address, so that no load sits under a
+// branch: a conditional load makes the compiler merge old and new register
+// values at the loop latch and wait there for every load in flight.  A tail
+// chunk (4, 8 or 12 bytes per lane) is read 16 bytes wide: the extra words are
+// neighbouring lanes' codes, or the tile's scales for the last lane; a chunk
+// past the row reads the tile's first bytes.  Those codes are finite and only
+// meet q' entries that are zero (K) or accumulators that are never read (V).
 template <int NC>
 __device__ __forceinline__ void load_codes(const uint8_t* tile, int lane, int rb, uint32_t* w) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int wc = rb - 16 * c;
-    const uint8_t* p = tile + 1024 * c;
-    if (wc >= 16) {
-      const uint4 v = *reinterpret_cast<const uint4*>(p + 16 * lane);
-      w[4 * c] = v.x; w[4 * c + 1] = v.y; w[4 * c + 2] = v.z; w[4 * c + 3] = v.w;
-    } else if (wc == 12) {
-      const uint3 v = *reinterpret_cast<const uint3*>(p + 12 * lane);
-      w[4 * c] = v.x; w[4 * c + 1] = v.y; w[4 * c + 2] = v.z; w[4 * c + 3] = 0;
-    } else if (wc == 8) {
-      const uint2 v = *reinterpret_cast<const uint2*>(p + 8 * lane);
-      w[4 * c] = v.x; w[4 * c + 1] = v.y; w[4 * c + 2] = 0; w[4 * c + 3] = 0;
-    } else if (wc == 4) {
-      w[4 * c] = *reinterpret_cast<const uint32_t*>(p + 4 * lane);
-      w[4 * c + 1] = 0; w[4 * c + 2] = 0; w[4 * c + 3] = 0;
-    } else {
-      w[4 * c] = 0; w[4 * c + 1] = 0; w[4 * c + 2] = 0; w[4 * c + 3] = 0;
-    }
+    const int off = wc > 0 ? 1024 * c + min(wc, 16) * lane : 0;
+    const uint4 v = *reinterpret_cast<const uint4*>(tile + off);
+    w[4 * c] = v.x; w[4 * c + 1] = v.y; w[4 * c + 2] = v.z; w[4 * c + 3] = v.w;
   }
 }
 
@@ -276,6 +269,8 @@ struct TileRegs {
   float sk[NG], sv[NG];
 };
 
+// Groups past the row (int4) re-read the last group's scale: it only
+// multiplies partial sums over zero q' entries or unread accumulators.
 template <int QF, int NC, int NG>
 __device__ __forceinline__ void load_k(const uint8_t* kt, int lane, int rk, int rbk, TileRegs<NC, NG>& x) {
   load_codes<NC>(kt, lane, rbk, x.kw);
@@ -284,7 +279,7 @@ __device__ __forceinline__ void load_k(const uint8_t* kt, int lane, int rk, int 
   } else {
 #pragma unroll
     for (int g = 0; g < NG; ++g)
-      x.sk[g] = 32 * g < rk ? half_bits_to_f32(*reinterpret_cast<const uint16_t*>(kt + 64 * rbk + 2 * (64 * g + lane))) : 0.0f;
+      x.sk[g] = half_bits_to_f32(*reinterpret_cast<const uint16_t*>(kt + 64 * rbk + 2 * (64 * min(g, (rk - 1) >> 5) + lane)));
   }
 }
 
@@ -296,7 +291,7 @@ __device__ __forceinline__ void load_v(const uint8_t* vt, int lane, int rv, int 
   } else {
 #pragma unroll
     for (int g = 0; g < NG; ++g)
-      x.sv[g] = 32 * g < rv ? half_bits_to_f32(*reinterpret_cast<const uint16_t*>(vt + 64 * rbv + 2 * (64 * g + lane))) : 0.0f;
+      x.sv[g] = half_bits_to_f32(*reinterpret_cast<const uint16_t*>(vt + 64 * rbv + 2 * (64 * min(g, (rv - 1) >> 5) + lane)));
   }
 }
 
@@ -373,48 +368,46 @@ void k_decode(DecodeArgs a, HeadTab ht) {
   __shared__ float s_u[NW][R];
   __shared__ float s_o[NW][kHeadDim];
 
-  // ---- the first tile's loads go out before the prologue so their latency
-  //      overlaps the q' computation; so do this wavefront's B^V rows
+  // ---- loads first, in the order their data is needed: q and this
+  //      wavefront's B^K rows, the first tile, this wavefront's B^V rows.  Row
+  //      indices are clamped instead of tested so no load sits under a branch.
+  const IOT* qrow = reinterpret_cast<const IOT*>(a.q) + size_t(unit) * kHeadDim;
+  const float q0 = E::ld(qrow, 2 * lane), q1 = E::ld(qrow, 2 * lane + 1);
+  const IOT* bkh = reinterpret_cast<const IOT*>(a.bk) + size_t(loff_k) * kHeadDim;
+  float b0[RPW], b1[RPW];
+#pragma unroll
+  for (int k = 0; k < RPW; ++k) {
+    const size_t i = min(wid + k * NW, rk - 1);
+    b0[k] = E::ld(bkh, i * kHeadDim + 2 * lane);
+    b1[k] = E::ld(bkh, i * kHeadDim + 2 * lane + 1);
+  }
   const uint8_t* kplane = a.cache + uint64_t(kreg) * kRegionAlign + uint64_t(b) * a.n_tiles * tbk;
   const uint8_t* vplane = a.cache + uint64_t(vreg) * kRegionAlign + uint64_t(b) * a.n_tiles * tbv;
+  // a wavefront with no tile, or past its last, re-reads tile t1 - 1 (or 0)
+  const int tlast = max(t1 - 1, 0);
   TileRegs<NC, NG> cur;
   int t = t0 + wid;
-  if (t < t1) {
-    load_k<QF>(kplane + size_t(t) * tbk, lane, rk, rbk, cur);
-    load_v<QF>(vplane + size_t(t) * tbv, lane, rv, rbv, cur);
-  }
+  load_k<QF>(kplane + size_t(min(t, tlast)) * tbk, lane, rk, rbk, cur);
+  load_v<QF>(vplane + size_t(min(t, tlast)) * tbv, lane, rv, rbv, cur);
   const IOT* bvh = reinterpret_cast<const IOT*>(a.bv) + size_t(loff_v) * kHeadDim;
   float bv0[RPW], bv1[RPW];
   if constexpr (PREFETCH_BV) {
 #pragma unroll
     for (int k = 0; k < RPW; ++k) {
-      const int i = wid + k * NW;
-      bv0[k] = i < rv ? E::ld(bvh, size_t(i) * kHeadDim + 2 * lane) : 0.0f;
-      bv1[k] = i < rv ? E::ld(bvh, size_t(i) * kHeadDim + 2 * lane + 1) : 0.0f;
+      const size_t i = min(wid + k * NW, rv - 1);
+      bv0[k] = E::ld(bvh, i * kHeadDim + 2 * lane);
+      bv1[k] = E::ld(bvh, i * kHeadDim + 2 * lane + 1);
     }
   }
 
   // ---- q'_i = scale * log2(e) * sum_j q_j B^K_h[i][j]: wavefront w takes
-  //      rows i = w, w + NW, ..., lane j columns 2j and 2j+1; all of a
-  //      wavefront's row loads are issued before any is used
-  {
-    const IOT* qrow = reinterpret_cast<const IOT*>(a.q) + size_t(unit) * kHeadDim;
-    const float q0 = E::ld(qrow, 2 * lane), q1 = E::ld(qrow, 2 * lane + 1);
-    const IOT* bkh = reinterpret_cast<const IOT*>(a.bk) + size_t(loff_k) * kHeadDim;
-    float b0[RPW], b1[RPW];
+  //      rows i = w, w + NW, ..., lane j columns 2j and 2j+1; q'_i = 0 past r_k
 #pragma unroll
-    for (int k = 0; k < RPW; ++k) {
-      const int i = wid + k * NW;
-      b0[k] = i < rk ? E::ld(bkh, size_t(i) * kHeadDim + 2 * lane) : 0.0f;
-      b1[k] = i < rk ? E::ld(bkh, size_t(i) * kHeadDim + 2 * lane + 1) : 0.0f;
-    }
-#pragma unroll
-    for (int k = 0; k < RPW; ++k) {
-      const int i = wid + k * NW;
-      if (i < R) {
-        const float v = wave_sum63(fmaf(q1, b1[k], q0 * b0[k]));
-        if (lane == 63) s_q[i] = v * a.qscale;
-      }
+  for (int k = 0; k < RPW; ++k) {
+    const int i = wid + k * NW;
+    if (i < R) {
+      const float v = wave_sum63(fmaf(q1, b1[k], q0 * b0[k]));
+      if (lane == 63) s_q[i] = i < rk ? v * a.qscale : 0.0f;
     }
   }
   __syncthreads();
@@ -476,8 +469,8 @@ void k_decode(DecodeArgs a, HeadTab ht) {
       }
     }
     if constexpr (INT8) s *= cur.sk[0];
-    const bool more = t + NW < t1;
-    if (more) load_k<QF>(kplane + size_t(t + NW) * tbk, lane, rk, rbk, cur);   // K regs are free now
+    const int tn = min(t + NW, tlast);
+    load_k<QF>(kplane + size_t(tn) * tbk, lane, rk, rbk, cur);   // K regs are free now
     s = valid ? s : -__builtin_inff();
     if (s > m + kTau) {  // rare after the first tile: rescale the running sums
       const float al = __builtin_amdgcn_exp2f(m - s);
@@ -519,7 +512,7 @@ void k_decode(DecodeArgs a, HeadTab ht) {
         }
       }
     }
-    if (more) load_v<QF>(vplane + size_t(t + NW) * tbv, lane, rv, rbv, cur);   // V regs are free now
+    load_v<QF>(vplane + size_t(tn) * tbv, lane, rv, rbv, cur);   // V regs are free now
   }
 
   // ---- merge the 64 lanes of each wavefront (DPP), publish per wavefront
@@ -567,8 +560,8 @@ void k_decode(DecodeArgs a, HeadTab ht) {
 #pragma unroll
     for (int k = 0; k < RPW; ++k) {
       const int i = wid + k * NW;
-      bv0[k] = i < rv ? E::ld(bvh, size_t(i) * kHeadDim + 2 * lane) : 0.0f;
-      bv1[k] = i < rv ? E::ld(bvh, size_t(i) * kHeadDim + 2 * lane + 1) : 0.0f;
+      bv0[k] = E::ld(bvh, size_t(min(i, rv - 1)) * kHeadDim + 2 * lane);
+      bv1[k] = E::ld(bvh, size_t(min(i, rv - 1)) * kHeadDim + 2 * lane + 1);
     }
   }
   float a0 = 0.0f, a1 = 0.0f;
@@ -607,8 +600,8 @@ __device__ __forceinline__ void project_out(const float* s_v, float (*s_o)[kHead
 #pragma unroll
   for (int k = 0; k < RPW; ++k) {
     const int i = wid + k * NW;
-    b0[k] = i < rv ? Elem<IOT>::ld(bvh, size_t(i) * kHeadDim + 2 * lane) : 0.0f;
-    b1[k] = i < rv ? Elem<IOT>::ld(bvh, size_t(i) * kHeadDim + 2 * lane + 1) : 0.0f;
+    b0[k] = Elem<IOT>::ld(bvh, size_t(min(i, rv - 1)) * kHeadDim + 2 * lane);
+    b1[k] = Elem<IOT>::ld(bvh, size_t(min(i, rv - 1)) * kHeadDim + 2 * lane + 1);
   }
   float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll

@@ -208,6 +208,28 @@ def test_decode_ragged_and_degenerate_lengths(qfmt, io, max_splits):
     _check_session(*sess, [0, 1, 63, 64, 65, 700], qfmt, io, 700)
 
 
+# Every tail width of the last 16-byte code chunk (int8 rows: 8 or 16 bytes;
+# int4 rows: 4, 8, 12 or 16 bytes) and every int4 partial group, in the
+# smallest and the largest rank bucket.
+TAIL_RANKS = {
+    32: ([8, 16, 24, 32], [24, 8, 32, 16]),
+    128: ([8, 16, 24, 32, 56, 72, 112, 120], [120, 104, 88, 64, 48, 40, 16, 8]),
+}
+
+
+@pytest.mark.parametrize("qfmt", [LR_Q_INT8_TOKEN, LR_Q_INT4_G32])
+@pytest.mark.parametrize("io", [LR_DT_BF16, LR_DT_F32])
+@pytest.mark.parametrize("bucket", [32, 128])
+def test_decode_every_row_tail_width(qfmt, io, bucket):
+    rng = np.random.default_rng(90 + 4 * qfmt + 2 * io + (bucket == 128))
+    rk, rv = TAIL_RANKS[bucket]
+    say(f"decode tail widths qfmt={qfmt} io={io} bucket={bucket}")
+    sess = _session(qfmt, io, 0, rng, 4, 300, rk, rv)
+    _check_session(*sess, [1, 64, 130, 300], qfmt, io, 300)
+    if io == LR_DT_BF16:
+        _check_session(*sess, [1, 64, 130, 300], qfmt, io, 300, explicit=True)
+
+
 @pytest.mark.parametrize("qfmt", [LR_Q_INT8_TOKEN, LR_Q_INT4_G32])
 def test_decode_explicit_ragged_and_degenerate_lengths(qfmt):
     rng = np.random.default_rng(50 + qfmt)
