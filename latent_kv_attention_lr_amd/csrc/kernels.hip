@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "plan.h"
 
 namespace lr {
@@ -90,6 +92,55 @@ __device__ __forceinline__ float wave_max63(float v) {
 __device__ __forceinline__ float lane63(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
+
+// Sum over the 64 lanes of 32 values per lane, transposed: each step pairs
+// lanes across one lane bit, every lane keeps half of its values and adds
+// its partner's copy of that half, so 32 values cost 31 adds plus the moves.
+// Bits 5 and 4 use the gfx950 half-wave swaps, bits 3, 1, 0 DPP with
+// selects, and a last DPP add folds bit 2.  Afterwards lane l with
+// (l & 4) == 0 holds the total of value (l & 3) | ((l >> 1) & 0x1c).
+// (Both swap results are read into unsigned locals first: bit-casting the
+// second element of the returned pair directly is miscompiled to a second
+// read of the first.)
+__device__ __forceinline__ float swap_sum32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  return __uint_as_float(r0) + __uint_as_float(r1);
+}
+__device__ __forceinline__ float swap_sum16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  return __uint_as_float(r0) + __uint_as_float(r1);
+}
+__device__ __forceinline__ float wave_sum32_transposed(float* x, int lane) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) x[k] = swap_sum32(x[k], x[k + 16]);     // keeps k + 16 bit5
+#pragma unroll
+  for (int k = 0; k < 8; ++k) x[k] = swap_sum16(x[k], x[k + 8]);       // keeps k + 8 bit4
+  {
+    const bool hi = lane & 8;                                            // row_ror:8 = lane ^ 8
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float send = hi ? x[k] : x[k + 4], keep = hi ? x[k + 4] : x[k];
+      x[k] = keep + dpp<0x128>(send, 0.0f);
+    }
+  }
+  {
+    const bool hi = lane & 2;                                            // quad_perm [2,3,0,1]
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const float send = hi ? x[k] : x[k + 2], keep = hi ? x[k + 2] : x[k];
+      x[k] = keep + dpp<0x4e>(send, 0.0f);
+    }
+  }
+  {
+    const bool hi = lane & 1;                                            // quad_perm [1,0,3,2]
+    const float send = hi ? x[0] : x[1], keep = hi ? x[1] : x[0];
+    x[0] = keep + dpp<0xb1>(send, 0.0f);
+  }
+  return x[0] + dpp<0x12c>(x[0], 0.0f);                                  // row_ror:12 reads lane i + 4
+}
+__device__ __forceinline__ int transposed_index(int lane) { return (lane & 3) | ((lane >> 1) & 0x1c); }
 
 __device__ __forceinline__ int uniform_i(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -383,7 +434,7 @@ void k_decode(DecodeArgs a, HeadTab ht) {
   }
   const uint8_t* kplane = a.cache + uint64_t(kreg) * kRegionAlign + uint64_t(b) * a.n_tiles * tbk;
   const uint8_t* vplane = a.cache + uint64_t(vreg) * kRegionAlign + uint64_t(b) * a.n_tiles * tbv;
-  // a wavefront with no tile, or past its last, re-reads tile t1 - 1 (or 0)
+  // a wavefront with no tile of its own reads tile t1 - 1 (or 0) and ignores it
   const int tlast = max(t1 - 1, 0);
   TileRegs<NC, NG> cur;
   int t = t0 + wid;
@@ -437,7 +488,12 @@ void k_decode(DecodeArgs a, HeadTab ht) {
 #pragma unroll
   for (int i = 0; i < R; ++i) u[i] = 0.0f;
 
-  for (; t < t1; t += NW) {
+  // One tile of this wavefront; PF: also fetch the wavefront's next tile into
+  // the registers just consumed.  The last tile is peeled off (PF false) so
+  // that no load is in flight when the loop ends: the merge below waits for
+  // every outstanding load before it can use the prefetched B^V rows.
+  auto tile_step = [&](const int t, auto pf) {
+    constexpr bool PF = decltype(pf)::value;
     const bool valid = t * 64 + lane < len;
     if constexpr (!Q_IN_REGS) qo.lds = (PACKED ? s_qw : reinterpret_cast<const uint32_t*>(s_q)) + opaque_zero();
     float s = 0.0f;
@@ -469,8 +525,7 @@ void k_decode(DecodeArgs a, HeadTab ht) {
       }
     }
     if constexpr (INT8) s *= cur.sk[0];
-    const int tn = min(t + NW, tlast);
-    load_k<QF>(kplane + size_t(tn) * tbk, lane, rk, rbk, cur);   // K regs are free now
+    if constexpr (PF) load_k<QF>(kplane + size_t(t + NW) * tbk, lane, rk, rbk, cur);   // K regs are free now
     s = valid ? s : -__builtin_inff();
     if (s > m + kTau) {  // rare after the first tile: rescale the running sums
       const float al = __builtin_amdgcn_exp2f(m - s);
@@ -512,20 +567,26 @@ void k_decode(DecodeArgs a, HeadTab ht) {
         }
       }
     }
-    load_v<QF>(vplane + size_t(tn) * tbv, lane, rv, rbv, cur);   // V regs are free now
-  }
+    if constexpr (PF) load_v<QF>(vplane + size_t(t + NW) * tbv, lane, rv, rbv, cur);   // V regs are free now
+  };
+  for (; t + NW < t1; t += NW) tile_step(t, std::true_type{});
+  if (t < t1) tile_step(t, std::false_type{});
 
-  // ---- merge the 64 lanes of each wavefront (DPP), publish per wavefront
+  // ---- merge the 64 lanes of each wavefront, publish per wavefront: the
+  //      V latent in transposed groups of 32 ranks (one LDS write per lane)
   {
     const float Mw = lane63(wave_max63(m));
     const float f = (m == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m - Mw);
     const float lw = wave_sum63(l * f);
     if (lane == 63) { s_m[wid] = Mw; s_l[wid] = lw; }
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      if (i < rv) {
-        const float ui = wave_sum63(u[i] * f);
-        if (lane == 63) s_u[wid][i] = ui;
+    for (int g = 0; g < R; g += 32) {
+      if (g < rv) {
+        float x[32];
+#pragma unroll
+        for (int k = 0; k < 32; ++k) x[k] = u[g + k] * f;
+        const float sum = wave_sum32_transposed(x, lane);
+        if ((lane & 4) == 0) s_u[wid][g + transposed_index(lane)] = sum;
       }
     }
   }
