@@ -937,7 +937,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_explicit(DecodeArgs a, HeadT
 
 template <int QF, typename IOT, int R>
 hipError_t launch_decode_r(int waves, dim3 grid, hipStream_t st, const DecodeArgs& a, const HeadTab& t) {
-  if constexpr (R <= 32) {
+  if constexpr (R <= 32 || (R <= 64 && QF == LR_Q_INT4_G32)) {   // 16 waves fit 128 VGPRs
     if (waves == 16) {
       hipLaunchKernelGGL((k_decode<QF, IOT, R, 16>), grid, dim3(1024), 0, st, a, t);
       return hipGetLastError();

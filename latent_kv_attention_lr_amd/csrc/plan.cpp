@@ -31,17 +31,22 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 namespace lr {
 
 Split choose_split(const lr_attn_plan& p, int32_t layer, int32_t max_len) {
-  // Parallelism first comes from more wavefronts per (b, h) work-group: the
-  // smallest of 4, 8, 16 that puts >= 4096 wavefronts (16 per CU) in flight,
-  // 16 only for the rank-32 bucket (the only one that fits 128 VGPRs).  When that is still short of
-  // 4096 wavefronts (few sequences and heads, long contexts) the context of
-  // each (b, h) is split Flash-Decoding style and a second kernel merges the
-  // partials; every split keeps at least two tiles per wavefront.
+  // Wavefronts per (b, h) work-group: 8 where the registers leave room for
+  // two such work-groups per compute unit (rank 32 at 5 waves per SIMD, int4
+  // rank 64 at 4), else 4 (int8 rank 64 at 3, ranks above 64 at 2).  Several
+  // work-groups per compute unit run out of phase, so one group's prologue and
+  // merge overlap another's streaming.  With few (b, h) units the count
+  // doubles, up to 16 where 128 VGPRs suffice, until 4096 wavefronts (16 per
+  // CU) are in flight; beyond that the context of each (b, h) is split
+  // Flash-Decoding style and a second kernel merges the partials (every
+  // split keeps at least two tiles per wavefront).
   Split s;
   const int64_t units = static_cast<int64_t>(p.desc.batch) * p.desc.n_heads;
   const int64_t tiles = ceil_div(max_len, kTile);
-  const int nw_max = layer_bucket(p.layers[layer]) <= 32 ? 16 : 8;
-  int nw = 4;
+  const int bucket = layer_bucket(p.layers[layer]);
+  const bool wide = bucket <= 32 || (bucket <= 64 && p.desc.qfmt == LR_Q_INT4_G32);
+  const int nw_max = wide ? 16 : 8;
+  int nw = wide ? 8 : 4;
   if (p.desc.wg_waves > 0) {
     nw = std::min(p.desc.wg_waves, nw_max);
   } else {
