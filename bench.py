@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", type=int, default=1, help="index in the workload table")
     ap.add_argument("--explicit", action="store_true", help="time the explicit-reconstruction decode")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="append and decode as two launches (default: one fused launch per step and layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=16,
                     help="extra untimed-in-value steps with the 256 MiB last-level cache flushed before each")
@@ -168,16 +170,24 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def step(s, ev=None):
+    fused = not (args.explicit or args.separate_append)
+
+    def one_layer(l, s, append=True):
+        """Step s of layer l: append the step's token and attend (one fused launch), or
+        with append=False (separate launches only) just the decode launch."""
         layers, pos, ln = per[s]
-        for l in range(L):
-            ck, cv, q = layers[l]
+        ck, cv, q = layers[l]
+        if fused:
+            sess.append_decode(l, ck.view(w.batch, -1), cv.view(w.batch, -1), pos, q, out,
+                               ctx + s + 1, lengths=ln)
+            return
+        if append:
             sess.append(l, ck, cv, pos)
-            if ev is not None:
-                ev[0].record()
-            sess.decode(l, q, out, ctx + s + 1, lengths=ln, explicit=args.explicit)
-            if ev is not None:
-                ev[1].record()
+        sess.decode(l, q, out, ctx + s + 1, lengths=ln, explicit=args.explicit)
+
+    def step(s):
+        for l in range(L):
+            one_layer(l, s)
 
     print(f"[bench] warmup {warm} steps", file=sys.stderr, flush=True)
     for s in range(warm):
@@ -191,17 +201,12 @@ def main():
 
     def timed_steps():
         for s in range(steps):
-            layers, pos, ln = per[s]
-            for l in range(L):
-                ck, cv, q = layers[l]
-                sess.append(l, ck, cv, pos)
-                sess.decode(l, q, out, ctx + s + 1, lengths=ln, explicit=args.explicit)
+            step(s)
 
     def decodes_only():
         for s in range(steps):
-            layers, pos, ln = per[s]
             for l in range(L):
-                sess.decode(l, layers[l][2], out, ctx + s + 1, lengths=ln, explicit=args.explicit)
+                one_layer(l, s, append=False)
 
     def capture(fn):
         g = torch.cuda.CUDAGraph()
@@ -225,8 +230,8 @@ def main():
           file=sys.stderr, flush=True)
 
     # ---- the decode kernel alone: the same `steps` decode launches (each with
-    # its step's lengths) back to back, between two HIP events on the launch
-    # stream; average launch duration = elapsed / launches.
+    # its step's lengths; fused: with its append) back to back, between two HIP
+    # events on the launch stream; average launch duration = elapsed / launches.
     run_dec = capture(decodes_only).replay if use_graph else decodes_only
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -243,7 +248,7 @@ def main():
     for s in range(steps):
         for l in range(L):
             b_, per_tok_bytes = algorithmic_bytes(w, [ctx + s + 1] * w.batch, rk_all[l], rv_all[l])
-            bytes_launch += b_
+            bytes_launch += b_ + (append_bytes(w, rk_all[l], rv_all[l]) if fused else 0)
     bytes_launch /= steps * L
     achieved = bytes_launch / dec_avg_s / 1e9
 
@@ -268,6 +273,7 @@ def main():
             "latents": "int8 per-token fp32 scale" if w.qfmt == 0 else "int4 group-32 fp16 scale",
             "q_factors_out": "bf16", "accumulation": "f32",
             "decode_form": "explicit" if args.explicit else "absorbed",
+            "step": "append fused into the decode launch" if fused else "append launch + decode launch",
             "parallelism": "single GPU",
             "launch": "hip graph of all timed steps" if use_graph else "eager",
         },
@@ -289,11 +295,12 @@ def main():
             for l in range(L):
                 layers, pos, ln = per[s]
                 ck, cv, q = layers[l]
-                sess.append(l, ck, cv, pos)
+                if not fused:
+                    sess.append(l, ck, cv, pos)
                 flush.sum()                      # reads 512 MiB: the 256 MiB last-level cache holds none of the cache
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record()
-                sess.decode(l, q, out, ctx + s + 1, lengths=ln, explicit=args.explicit)
+                one_layer(l, s, append=False)
                 b.record()
                 cold.append((a, b))
         torch.cuda.synchronize()

@@ -99,15 +99,20 @@ class WorkloadRun:
         return ck, cv, q, pos
 
     def run_step(self, layer: int, s: int, out: Optional[torch.Tensor] = None,
-                 explicit: bool = False) -> torch.Tensor:
-        """Append step s's token to every sequence, then attend over context + s + 1."""
+                 explicit: bool = False, fused: bool = True) -> torch.Tensor:
+        """Append step s's token to every sequence, then attend over context + s + 1
+        (one fused call unless explicit or fused=False)."""
         ck, cv, q, pos = self.step_tensors(layer, s)
-        self.sess.append(layer, ck, cv, pos)
         self.sess.lengths.fill_(self.context + s + 1)
         if out is None:
             out = torch.empty(self.w.batch, self.w.n_heads, self.w.head_dim, dtype=self.dtype,
                               device=self.device)
-        self.sess.decode(layer, q, out, self.context + s + 1, explicit=explicit)
+        if fused and not explicit:
+            self.sess.append_decode(layer, ck.view(self.w.batch, -1), cv.view(self.w.batch, -1),
+                                    pos, q, out, self.context + s + 1)
+        else:
+            self.sess.append(layer, ck, cv, pos)
+            self.sess.decode(layer, q, out, self.context + s + 1, explicit=explicit)
         return out
 
     # -- oracle inputs ----------------------------------------------------------

@@ -174,6 +174,24 @@ lr_status lr_attn_decode(const lr_attn_plan* plan, int32_t layer, const void* ca
                          const void* bv, float softmax_scale, void* out, void* workspace,
                          size_t ws_bytes, void* stream);
 
+/* lr_attn_append_latent with n_new = 1 followed by lr_attn_decode, in one
+ * launch (two when the context is split): for every sequence b the new
+ * token's latents are quantised and written at slot pos[b], then every (b, h)
+ * attends over slots t < len[b], the new one included when pos[b] < len[b]
+ * (LASER page, "System implementation": quantisation fused into the kernel).
+ * The cache bytes written and the output are bit-identical to the two calls.
+ *   cache       device, as for both calls; written at slot pos[b] only
+ *   ck, cv      device fp32 [batch][latent_elems(kv)], 16-aligned
+ *   pos         device int32 [batch]; a slot outside [0, capacity) is neither
+ *               written nor substituted (the decode then reads the cache as is)
+ *   len ... ws  as for lr_attn_decode
+ * Errors: LR_EINVAL, LR_ERANGE, LR_EWORKSPACE, LR_EHIP. */
+lr_status lr_attn_append_decode(const lr_attn_plan* plan, int32_t layer, void* cache,
+                                const float* ck, const float* cv, const int32_t* pos,
+                                const int32_t* len, int32_t max_len, const void* q,
+                                const void* bk, const void* bv, float softmax_scale, void* out,
+                                void* workspace, size_t ws_bytes, void* stream);
+
 /* The same result through explicit per-token reconstruction: every k_t and
  * v_t (d = 128 values) is rebuilt on chip with matrix-core products of the
  * dequantised latents and B_h, then scored and accumulated (WSVD page,

@@ -88,6 +88,8 @@ def _load() -> ctypes.CDLL:
         "lr_attn_append_latent": (ctypes.c_int, [P, I32, P, P, P, P, I32, P]),
         "lr_attn_decode": (ctypes.c_int, [P, I32, P, P, I32, P, P, P, ctypes.c_float, P, P, SZ, P]),
         "lr_attn_decode_explicit": (ctypes.c_int, [P, I32, P, P, I32, P, P, P, ctypes.c_float, P, P, SZ, P]),
+        "lr_attn_append_decode": (ctypes.c_int, [P, I32, P, P, P, P, P, I32, P, P, P, ctypes.c_float,
+                                                 P, P, SZ, P]),
         "lr_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "lr_attn_last_hip_error": (I32, []),
     }
@@ -182,6 +184,16 @@ def lr_attn_decode(plan: int, layer: int, cache, length, max_len: int, q, bk, bv
     _check(_lib.lr_attn_decode(plan, layer, _ptr(cache), _ptr(length), max_len, _ptr(q), _ptr(bk),
                                _ptr(bv), softmax_scale, _ptr(out), _ptr(workspace), ws_bytes,
                                _stream(stream)), "lr_attn_decode")
+
+
+def lr_attn_append_decode(plan: int, layer: int, cache, ck, cv, pos, lengths, max_len: int, q, bk,
+                          bv, softmax_scale: float, out, workspace=None, ws_bytes: int = 0,
+                          stream=None) -> None:
+    """lr_attn_append_latent (one token per sequence) then lr_attn_decode, fused."""
+    _check(_lib.lr_attn_append_decode(plan, layer, _ptr(cache), _ptr(ck), _ptr(cv), _ptr(pos),
+                                      _ptr(lengths), max_len, _ptr(q), _ptr(bk), _ptr(bv),
+                                      float(softmax_scale), _ptr(out), _ptr(workspace), ws_bytes,
+                                      _stream(stream)), "lr_attn_append_decode")
 
 
 def lr_attn_decode_explicit(plan: int, layer: int, cache, length, max_len: int, q, bk, bv,

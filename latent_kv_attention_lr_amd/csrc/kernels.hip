@@ -185,10 +185,65 @@ __device__ __forceinline__ float quad_max(float v) {
   return v;
 }
 
+// One lane's segment of a latent row: 8 values quantised round-half-even
+// against the row's (int8) or its group's (int4) absmax scale.  The absmax is
+// reduced with DPP inside the 16-lane row (int8) or the quad that holds one
+// group of 32 ranks (int4), so every lane of those rows must take part.
+struct SegCodes {
+  uint32_t w[2];   // int8: 8 bytes; int4: 8 nibbles in w[0]
+  float s;         // the scale as stored (int4: fp16 widened)
+  uint16_t sh;     // int4: the fp16 scale bits
+};
+
+template <int QF>
+__device__ __forceinline__ SegCodes quantise_seg(const float* v) {
+  float m = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
+  m = QF == LR_Q_INT8_TOKEN ? row16_max(m) : quad_max(m);
+  SegCodes c;
+  c.w[0] = 0u;
+  c.w[1] = 0u;
+  c.sh = 0;
+  if constexpr (QF == LR_Q_INT8_TOKEN) {
+    c.s = m / 127.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int q = c.s != 0.0f ? int(fminf(fmaxf(rintf(v[k] / c.s), -127.0f), 127.0f)) : 0;
+      c.w[k >> 2] |= (uint32_t(q) & 0xffu) << (8 * (k & 3));
+    }
+  } else {
+    const _Float16 sh = _Float16(m / 7.0f);
+    c.s = float(sh);
+    c.sh = __builtin_bit_cast(uint16_t, sh);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int q = c.s != 0.0f ? int(fminf(fmaxf(rintf(v[k] / c.s), -7.0f), 7.0f)) : 0;
+      c.w[0] |= (uint32_t(q) & 0xfu) << (4 * k);
+    }
+  }
+  return c;
+}
+
+// Store one lane's quantised segment (seg = lane within its 16-lane row) at
+// token slot t of its tile; rb = the row's code bytes.
+template <int QF>
+__device__ __forceinline__ void store_seg(uint8_t* tile, int rb, int t, int seg, const SegCodes& c) {
+  if constexpr (QF == LR_Q_INT8_TOKEN) {
+    const int ch = seg >> 1;                      // 16-byte chunk of this lane's 8 bytes
+    const int wc = min(16, rb - 16 * ch);         // chunk width: 16, or 8 for the tail
+    *reinterpret_cast<uint2*>(tile + 1024 * ch + wc * t + 8 * (seg & 1)) = make_uint2(c.w[0], c.w[1]);
+    if (seg == 0) *reinterpret_cast<float*>(tile + 64 * rb + 4 * t) = c.s;
+  } else {
+    const int g = seg >> 2;                       // group of 32 ranks == 16-byte chunk
+    const int wc = min(16, rb - 16 * g);          // 16, or 4, 8, 12 for the tail group
+    *reinterpret_cast<uint32_t*>(tile + 1024 * g + wc * t + 4 * (seg & 3)) = c.w[0];
+    if ((seg & 3) == 0) *reinterpret_cast<uint16_t*>(tile + 64 * rb + 2 * (64 * g + t)) = c.sh;
+  }
+}
+
 // One latent row (one token, one head, K or V) per 16 lanes; lane s of the row
-// owns values [8s, 8s + 8), so a row of rank r uses r/8 lanes.  Magnitudes are
-// reduced with DPP inside the row (int8) or inside the quad that holds one
-// group of 32 ranks (int4); each lane then quantises and stores its 8 values.
+// owns values [8s, 8s + 8), so a row of rank r uses r/8 lanes.
 template <int QF>
 __global__ __launch_bounds__(256) void k_append(AppendArgs a, HeadTab ht) {
   const int64_t gid = int64_t(blockIdx.x) * 256 + threadIdx.x;
@@ -216,43 +271,11 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a, HeadTab ht) {
     v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
     v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
   }
-  float m = 0.0f;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
-  m = QF == LR_Q_INT8_TOKEN ? row16_max(m) : quad_max(m);
+  const SegCodes c = quantise_seg<QF>(v);
   if (!active) return;
-
-  const int rb = row_bytes(QF, r);
   uint8_t* tile = a.cache + uint64_t(kv ? ht.vreg[h] : ht.kreg[h]) * kRegionAlign +
                   (uint64_t(b) * a.n_tiles + (slot >> 6)) * tile_bytes(QF, r);
-  const int t = slot & 63;
-  if constexpr (QF == LR_Q_INT8_TOKEN) {
-    const float s = m / 127.0f;
-    uint32_t w[2] = {0u, 0u};
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int q = s != 0.0f ? int(fminf(fmaxf(rintf(v[k] / s), -127.0f), 127.0f)) : 0;
-      w[k >> 2] |= (uint32_t(q) & 0xffu) << (8 * (k & 3));
-    }
-    const int c = seg >> 1;                       // 16-byte chunk of this lane's 8 bytes
-    const int wc = min(16, rb - 16 * c);          // chunk width: 16, or 8 for the tail
-    *reinterpret_cast<uint2*>(tile + 1024 * c + wc * t + 8 * (seg & 1)) = make_uint2(w[0], w[1]);
-    if (seg == 0) *reinterpret_cast<float*>(tile + 64 * rb + 4 * t) = s;
-  } else {
-    const _Float16 sh = _Float16(m / 7.0f);
-    const float s = float(sh);
-    uint32_t w = 0u;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int q = s != 0.0f ? int(fminf(fmaxf(rintf(v[k] / s), -7.0f), 7.0f)) : 0;
-      w |= (uint32_t(q) & 0xfu) << (4 * k);
-    }
-    const int g = seg >> 2;                       // group of 32 ranks == 16-byte chunk
-    const int wc = min(16, rb - 16 * g);          // 16, or 4, 8, 12 for the tail group
-    *reinterpret_cast<uint32_t*>(tile + 1024 * g + wc * t + 4 * (seg & 3)) = w;
-    if ((seg & 3) == 0)
-      *reinterpret_cast<uint16_t*>(tile + 64 * rb + 2 * (64 * g + t)) = __builtin_bit_cast(uint16_t, sh);
-  }
+  store_seg<QF>(tile, row_bytes(QF, r), slot & 63, seg, c);
 }
 
 // ---------------------------------------------------------------------------
@@ -269,6 +292,13 @@ struct DecodeArgs {
   float* part;       // workspace partials [B*H][n_split][kPartStride] (split launches only)
   float qscale;      // softmax scale * log2(e)
   int32_t B, H, n_tiles, max_len, n_split, tps;
+  // fused append (ck == nullptr: none): quantise and write one token per
+  // sequence at slot pos[b] before attending
+  uint8_t* wcache;
+  const float* ck;
+  const float* cv;
+  const int32_t* pos;
+  int32_t capacity, sum_rk, sum_rv;
 };
 
 // Codes of one 64-token tile for this lane: NC chunks of 16 bytes.  The
@@ -451,6 +481,50 @@ void k_decode(DecodeArgs a, HeadTab ht) {
     }
   }
 
+  // ---- fused append: wavefront 0 quantises the new token's K row (lanes
+  //      0-15) and V row (lanes 16-31) exactly as the append kernel does, parks
+  //      the codes in LDS in tile-register order for the wavefront that meets
+  //      their slot, and (split 0) writes them to the cache
+  __shared__ uint32_t s_nw[2][4 * NC];
+  __shared__ float s_ns[2][NG];
+  int tnew = -1, lnew = 0;                             // tile and lane of the new token
+  if (a.ck) {
+    const int pos = a.pos[b];
+    if (pos >= 0 && pos < a.capacity) {
+      tnew = pos >> 6;
+      lnew = pos & 63;
+    }
+    if (wid == 0 && tnew >= 0) {
+      const int kv = (lane >> 4) & 1, seg = lane & 15;
+      const int r = kv ? rv : rk;
+      const bool active = lane < 32 && 8 * seg < r;
+      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (active) {
+        const float* src = kv ? a.cv + size_t(b) * a.sum_rv + loff_v : a.ck + size_t(b) * a.sum_rk + loff_k;
+        const float4 x0 = *reinterpret_cast<const float4*>(src + 8 * seg);
+        const float4 x1 = *reinterpret_cast<const float4*>(src + 8 * seg + 4);
+        v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+        v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+      }
+      const SegCodes c = quantise_seg<QF>(v);
+      if (lane < 32 && 8 * seg < R) {
+        if constexpr (INT8) {
+          s_nw[kv][4 * (seg >> 1) + 2 * (seg & 1)] = c.w[0];
+          s_nw[kv][4 * (seg >> 1) + 2 * (seg & 1) + 1] = c.w[1];
+          if (seg == 0) s_ns[kv][0] = c.s;
+        } else {
+          s_nw[kv][4 * (seg >> 2) + (seg & 3)] = c.w[0];
+          if ((seg & 3) == 0) s_ns[kv][seg >> 2] = c.s;
+        }
+      }
+      if (split == 0 && active) {
+        uint8_t* tile = a.wcache + uint64_t(kv ? vreg : kreg) * kRegionAlign +
+                        (uint64_t(b) * a.n_tiles + tnew) * (kv ? tbv : tbk);
+        store_seg<QF>(tile, kv ? rbv : rbk, lnew, seg, c);
+      }
+    }
+  }
+
   // ---- q'_i = scale * log2(e) * sum_j q_j B^K_h[i][j]: wavefront w takes
   //      rows i = w, w + NW, ..., lane j columns 2j and 2j+1; q'_i = 0 past r_k
 #pragma unroll
@@ -495,6 +569,19 @@ void k_decode(DecodeArgs a, HeadTab ht) {
   auto tile_step = [&](const int t, auto pf) {
     constexpr bool PF = decltype(pf)::value;
     const bool valid = t * 64 + lane < len;
+    if (t == tnew && lane == lnew) {   // fused append: the new token's codes come from LDS
+      const int z = opaque_zero();     // keeps these reads here, not hoisted out of the loop
+#pragma unroll
+      for (int i = 0; i < 4 * NC; ++i) {
+        cur.kw[i] = s_nw[0][i + z];
+        cur.vw[i] = s_nw[1][i + z];
+      }
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        cur.sk[g] = s_ns[0][g + z];
+        cur.sv[g] = s_ns[1][g + z];
+      }
+    }
     if constexpr (!Q_IN_REGS) qo.lds = (PACKED ? s_qw : reinterpret_cast<const uint32_t*>(s_q)) + opaque_zero();
     float s = 0.0f;
 #pragma unroll
@@ -1004,7 +1091,8 @@ hipError_t launch_explicit_q(int bucket, int waves, dim3 grid, hipStream_t st, c
 
 int launch_decode(const lr_attn_plan& p, int32_t layer, const void* cache, const int32_t* len,
                   int32_t max_len, const void* q, const void* bk, const void* bv, float scale,
-                  void* out, void* workspace, void* stream, bool explicit_form) {
+                  void* out, void* workspace, void* stream, bool explicit_form,
+                  const AppendInputs* app) {
   const auto& L = p.layers[layer];
   const Split sp = explicit_form ? explicit_split(p, layer, max_len) : choose_split(p, layer, max_len);
   DecodeArgs a;
@@ -1022,6 +1110,13 @@ int launch_decode(const lr_attn_plan& p, int32_t layer, const void* cache, const
   a.max_len = max_len;
   a.n_split = sp.n_split;
   a.tps = sp.tiles_per_split;
+  a.wcache = app ? static_cast<uint8_t*>(app->cache) : nullptr;
+  a.ck = app ? app->ck : nullptr;
+  a.cv = app ? app->cv : nullptr;
+  a.pos = app ? app->pos : nullptr;
+  a.capacity = p.desc.capacity;
+  a.sum_rk = L.sum_rk;
+  a.sum_rv = L.sum_rv;
   const unsigned units = unsigned(p.desc.batch) * unsigned(p.desc.n_heads);
   const dim3 grid(units * unsigned(sp.n_split));
   hipStream_t st = static_cast<hipStream_t>(stream);

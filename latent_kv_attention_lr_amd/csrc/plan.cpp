@@ -223,7 +223,8 @@ lr_status lr_attn_append_latent(const lr_attn_plan* p, int32_t layer, void* cach
 static lr_status decode_common(const lr_attn_plan* p, int32_t layer, const void* cache,
                                const int32_t* len, int32_t max_len, const void* q,
                                const void* bk, const void* bv, float scale, void* out,
-                               void* ws, size_t ws_bytes, void* stream, bool explicit_form) {
+                               void* ws, size_t ws_bytes, void* stream, bool explicit_form,
+                               const lr::AppendInputs* app = nullptr) {
   if (!p) return LR_EINVAL;
   if (layer < 0 || layer >= p->desc.n_layers) return LR_ERANGE;
   if (max_len < 1 || max_len > p->desc.capacity) return LR_ERANGE;
@@ -237,7 +238,7 @@ static lr_status decode_common(const lr_attn_plan* p, int32_t layer, const void*
   if (need > 0 && (!ws || ws_bytes < need)) return LR_EWORKSPACE;
   if (ws && !aligned(ws, 16)) return LR_EINVAL;
   return hip_status(lr::launch_decode(*p, layer, cache, len, max_len, q, bk, bv, scale, out,
-                                      need > 0 ? ws : nullptr, stream, explicit_form));
+                                      need > 0 ? ws : nullptr, stream, explicit_form, app));
 }
 
 lr_status lr_attn_decode(const lr_attn_plan* p, int32_t layer, const void* cache,
@@ -246,6 +247,19 @@ lr_status lr_attn_decode(const lr_attn_plan* p, int32_t layer, const void* cache
                          void* stream) {
   return decode_common(p, layer, cache, len, max_len, q, bk, bv, scale, out, ws, ws_bytes, stream,
                        false);
+}
+
+lr_status lr_attn_append_decode(const lr_attn_plan* p, int32_t layer, void* cache, const float* ck,
+                                const float* cv, const int32_t* pos, const int32_t* len,
+                                int32_t max_len, const void* q, const void* bk, const void* bv,
+                                float scale, void* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!p) return LR_EINVAL;
+  if (layer < 0 || layer >= p->desc.n_layers) return LR_ERANGE;
+  if (!ck || !cv || !pos) return LR_EINVAL;
+  if (!aligned(ck, 16) || !aligned(cv, 16) || !aligned(pos, 4)) return LR_EINVAL;
+  const lr::AppendInputs app{cache, ck, cv, pos};
+  return decode_common(p, layer, cache, len, max_len, q, bk, bv, scale, out, ws, ws_bytes, stream,
+                       false, &app);
 }
 
 lr_status lr_attn_decode_explicit(const lr_attn_plan* p, int32_t layer, const void* cache,

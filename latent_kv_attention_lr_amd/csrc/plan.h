@@ -42,8 +42,16 @@ size_t workspace_bytes(const lr_attn_plan& p, int32_t max_len);
 // returns the hipError_t of the launch (0 on success).
 int launch_append(const lr_attn_plan& p, int32_t layer, void* cache, const float* ck,
                   const float* cv, const int32_t* pos, int32_t n_new, void* stream);
+// The token a fused append writes before the decode attends (one per sequence).
+struct AppendInputs {
+  void* cache;
+  const float* ck;
+  const float* cv;
+  const int32_t* pos;
+};
 int launch_decode(const lr_attn_plan& p, int32_t layer, const void* cache, const int32_t* len,
                   int32_t max_len, const void* q, const void* bk, const void* bv, float scale,
-                  void* out, void* workspace, void* stream, bool explicit_form);
+                  void* out, void* workspace, void* stream, bool explicit_form,
+                  const AppendInputs* app = nullptr);
 
 }  // namespace lr

@@ -12,7 +12,8 @@ from typing import List, Optional, Sequence
 
 import torch
 
-from . import (LR_DT_BF16, LR_DT_F32, LR_HEAD_DIM, lr_attn_append_latent, lr_attn_cache_bytes,
+from . import (LR_DT_BF16, LR_DT_F32, LR_HEAD_DIM, lr_attn_append_decode, lr_attn_append_latent,
+               lr_attn_cache_bytes,
                lr_attn_decode, lr_attn_decode_explicit, lr_attn_factor_elems,
                lr_attn_head_layout_get, lr_attn_latent_elems, lr_attn_plan_create,
                lr_attn_plan_destroy, lr_attn_workspace_bytes)
@@ -102,3 +103,26 @@ class DecodeSession:
         fn(self.plan, layer, self.caches[layer], self.lengths if lengths is None else lengths,
            max_len, q, self.bk[layer], self.bv[layer], scale, out, self.workspace,
            self.workspace.numel(), stream)
+
+    def append_decode(self, layer: int, ck: torch.Tensor, cv: torch.Tensor, pos: torch.Tensor,
+                      q: torch.Tensor, out: torch.Tensor, max_len: int,
+                      lengths: Optional[torch.Tensor] = None,
+                      softmax_scale: Optional[float] = None, stream=None) -> None:
+        """append() of one token per sequence, then decode(), in one fused call."""
+        if self.bk[layer] is None:
+            raise ValueError("factors of this layer are not set")
+        if ck.dtype != torch.float32 or cv.dtype != torch.float32:
+            raise ValueError("latents must be fp32")
+        if ck.numel() != self.batch * self.latent_elems(layer, 0) or \
+                cv.numel() != self.batch * self.latent_elems(layer, 1):
+            raise ValueError("latent tensors must hold one token per sequence")
+        shape = (self.batch, self.n_heads, LR_HEAD_DIM)
+        if q.shape != shape or out.shape != shape or q.dtype != self.torch_dtype or out.dtype != self.torch_dtype:
+            raise ValueError("q/out must be [B, H, 128] of the session dtype")
+        if not all(t.is_contiguous() for t in (ck, cv, pos, q, out)):
+            raise ValueError("all tensors must be contiguous")
+        scale = 1.0 / math.sqrt(LR_HEAD_DIM) if softmax_scale is None else softmax_scale
+        lr_attn_append_decode(self.plan, layer, self.caches[layer], ck, cv, pos,
+                              self.lengths if lengths is None else lengths, max_len, q,
+                              self.bk[layer], self.bv[layer], scale, out, self.workspace,
+                              self.workspace.numel(), stream)

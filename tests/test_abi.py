@@ -189,6 +189,35 @@ def test_decode_argument_errors_before_launch(fn):
         lr.lr_attn_plan_destroy(p)
 
 
+def _append_decode(p, **kw):
+    a = dict(layer=0, cache=FAKE, ck=FAKE, cv=FAKE, pos=FAKE, len=FAKE, max_len=100, q=FAKE,
+             bk=FAKE, bv=FAKE, scale=0.088, out=FAKE, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return lr._lib.lr_attn_append_decode(p, a["layer"], a["cache"], a["ck"], a["cv"], a["pos"],
+                                         a["len"], a["max_len"], a["q"], a["bk"], a["bv"],
+                                         a["scale"], a["out"], a["ws"], a["ws_bytes"], None)
+
+
+def test_append_decode_argument_errors_before_launch():
+    p = _plan(capacity=3000)
+    try:
+        assert _append_decode(None) == lr.LR_EINVAL
+        assert _append_decode(p, layer=3) == lr.LR_ERANGE
+        assert _append_decode(p, max_len=0) == lr.LR_ERANGE
+        assert _append_decode(p, max_len=3001) == lr.LR_ERANGE
+        for name in ("cache", "ck", "cv", "pos", "len", "q", "bk", "bv", "out"):
+            assert _append_decode(p, **{name: None}) == lr.LR_EINVAL, name
+        assert _append_decode(p, ck=FAKE + 4) == lr.LR_EINVAL      # latents 16-aligned
+        assert _append_decode(p, pos=FAKE + 2) == lr.LR_EINVAL     # pos 4-aligned
+        assert _append_decode(p, cache=FAKE + 64) == lr.LR_EINVAL
+        assert _append_decode(p, scale=float("nan")) == lr.LR_EINVAL
+        need = lr.lr_attn_workspace_bytes(p, 3000)
+        assert _append_decode(p, max_len=3000, ws=None) == lr.LR_EWORKSPACE
+        assert _append_decode(p, max_len=3000, ws_bytes=need - 1) == lr.LR_EWORKSPACE
+    finally:
+        lr.lr_attn_plan_destroy(p)
+
+
 def test_explicit_form_rejects_fp32_io_before_launch():
     p = _plan(io_dtype=lr.LR_DT_F32)
     try:

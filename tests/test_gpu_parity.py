@@ -260,6 +260,48 @@ def test_decode_context_split_path(qfmt, io):
     _check_session(*sess, [0, 8191, 2048], qfmt, io, 8192)
 
 
+def _fused_equals_separate(sess, lens, pos, max_len, seed):
+    """append + decode and the fused append_decode write the same cache bytes
+    and give the same outputs, bit for bit."""
+    s, rk, rv, ck, cv, bk, bv, q = sess
+    rng = np.random.default_rng(seed)
+    B = s.batch
+    nk = torch.from_numpy((rng.standard_normal((B, 1, sum(rk))) * 1.1).astype(np.float32)).to(DEV)
+    nv = torch.from_numpy((rng.standard_normal((B, 1, sum(rv))) * 0.9).astype(np.float32)).to(DEV)
+    posd = torch.tensor(pos, dtype=torch.int32, device=DEV)
+    s.lengths.copy_(torch.tensor(lens, dtype=torch.int32))
+    before = s.caches[0].clone()
+    out_a = torch.full_like(q, float("nan"))
+    s.append(0, nk, nv, posd)
+    s.decode(0, q, out_a, max_len=max_len)
+    torch.cuda.synchronize()
+    cache_a = s.caches[0].clone()
+    s.caches[0].copy_(before)
+    out_b = torch.full_like(q, float("nan"))
+    s.append_decode(0, nk.view(B, -1), nv.view(B, -1), posd, q, out_b, max_len=max_len)
+    torch.cuda.synchronize()
+    assert torch.equal(s.caches[0], cache_a), "fused append wrote different cache bytes"
+    assert torch.equal(out_a, out_b), "fused decode differs from append + decode"
+    return out_a
+
+
+@pytest.mark.parametrize("qfmt", [LR_Q_INT8_TOKEN, LR_Q_INT4_G32])
+@pytest.mark.parametrize("io", [LR_DT_BF16, LR_DT_F32])
+def test_append_decode_fused_equals_separate(qfmt, io):
+    rng = np.random.default_rng(70 + 2 * qfmt + io)
+    say(f"append_decode fused qfmt={qfmt} io={io}")
+    sess = _ragged_session(qfmt, io, 0, rng)
+    # the new token is the last attended one: slot 0, tile boundaries, the end
+    lens = [1, 2, 64, 65, 300, 700]
+    _fused_equals_separate(sess, lens, [n - 1 for n in lens], 700, 1)
+    # slots outside the cache are skipped; a slot at or past len is written, not attended
+    _fused_equals_separate(sess, [10, 700, 6, 50, 700, 1], [-1, 700, 5, 100, 699, 0], 700, 2)
+    # context splits: the new token's tile in a later split of its (b, h)
+    sess = _long_session(qfmt, io, 0, rng)
+    lens = [100, 3001, 8192]
+    _fused_equals_separate(sess, lens, [n - 1 for n in lens], 8192, 3)
+
+
 def test_decode_max_len_clamps_longer_lengths():
     rng = np.random.default_rng(3)
     s, rk, rv, ck, cv, bk, bv, q = _ragged_session(LR_Q_INT8_TOKEN, LR_DT_F32, 0, rng)
