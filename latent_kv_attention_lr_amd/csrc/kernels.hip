@@ -449,6 +449,28 @@ void k_decode(DecodeArgs a, HeadTab ht) {
   __shared__ float s_u[NW][R];
   __shared__ float s_o[NW][kHeadDim];
 
+  // ---- fused append: the new token of sequence b (slot pos[b]); its
+  //      latents are fetched first so their latency overlaps the prologue
+  int tnew = -1, lnew = 0;                             // tile and lane of the new token
+  const int nkv = (lane >> 4) & 1, nseg = lane & 15;   // wavefront 0: K row, V row
+  bool nactive = false;
+  float nv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (a.ck) {
+    const int pos = a.pos[b];
+    if (pos >= 0 && pos < a.capacity) {
+      tnew = pos >> 6;
+      lnew = pos & 63;
+    }
+    nactive = wid == 0 && tnew >= 0 && lane < 32 && 8 * nseg < (nkv ? rv : rk);
+    if (nactive) {
+      const float* src = nkv ? a.cv + size_t(b) * a.sum_rv + loff_v : a.ck + size_t(b) * a.sum_rk + loff_k;
+      const float4 x0 = *reinterpret_cast<const float4*>(src + 8 * nseg);
+      const float4 x1 = *reinterpret_cast<const float4*>(src + 8 * nseg + 4);
+      nv[0] = x0.x; nv[1] = x0.y; nv[2] = x0.z; nv[3] = x0.w;
+      nv[4] = x1.x; nv[5] = x1.y; nv[6] = x1.z; nv[7] = x1.w;
+    }
+  }
+
   // ---- loads first, in the order their data is needed: q and this
   //      wavefront's B^K rows, the first tile, this wavefront's B^V rows.  Row
   //      indices are clamped instead of tested so no load sits under a branch.
@@ -481,50 +503,6 @@ void k_decode(DecodeArgs a, HeadTab ht) {
     }
   }
 
-  // ---- fused append: wavefront 0 quantises the new token's K row (lanes
-  //      0-15) and V row (lanes 16-31) exactly as the append kernel does, parks
-  //      the codes in LDS in tile-register order for the wavefront that meets
-  //      their slot, and (split 0) writes them to the cache
-  __shared__ uint32_t s_nw[2][4 * NC];
-  __shared__ float s_ns[2][NG];
-  int tnew = -1, lnew = 0;                             // tile and lane of the new token
-  if (a.ck) {
-    const int pos = a.pos[b];
-    if (pos >= 0 && pos < a.capacity) {
-      tnew = pos >> 6;
-      lnew = pos & 63;
-    }
-    if (wid == 0 && tnew >= 0) {
-      const int kv = (lane >> 4) & 1, seg = lane & 15;
-      const int r = kv ? rv : rk;
-      const bool active = lane < 32 && 8 * seg < r;
-      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (active) {
-        const float* src = kv ? a.cv + size_t(b) * a.sum_rv + loff_v : a.ck + size_t(b) * a.sum_rk + loff_k;
-        const float4 x0 = *reinterpret_cast<const float4*>(src + 8 * seg);
-        const float4 x1 = *reinterpret_cast<const float4*>(src + 8 * seg + 4);
-        v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
-        v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
-      }
-      const SegCodes c = quantise_seg<QF>(v);
-      if (lane < 32 && 8 * seg < R) {
-        if constexpr (INT8) {
-          s_nw[kv][4 * (seg >> 1) + 2 * (seg & 1)] = c.w[0];
-          s_nw[kv][4 * (seg >> 1) + 2 * (seg & 1) + 1] = c.w[1];
-          if (seg == 0) s_ns[kv][0] = c.s;
-        } else {
-          s_nw[kv][4 * (seg >> 2) + (seg & 3)] = c.w[0];
-          if ((seg & 3) == 0) s_ns[kv][seg >> 2] = c.s;
-        }
-      }
-      if (split == 0 && active) {
-        uint8_t* tile = a.wcache + uint64_t(kv ? vreg : kreg) * kRegionAlign +
-                        (uint64_t(b) * a.n_tiles + tnew) * (kv ? tbv : tbk);
-        store_seg<QF>(tile, kv ? rbv : rbk, lnew, seg, c);
-      }
-    }
-  }
-
   // ---- q'_i = scale * log2(e) * sum_j q_j B^K_h[i][j]: wavefront w takes
   //      rows i = w, w + NW, ..., lane j columns 2j and 2j+1; q'_i = 0 past r_k
 #pragma unroll
@@ -533,6 +511,31 @@ void k_decode(DecodeArgs a, HeadTab ht) {
     if (i < R) {
       const float v = wave_sum63(fmaf(q1, b1[k], q0 * b0[k]));
       if (lane == 63) s_q[i] = i < rk ? v * a.qscale : 0.0f;
+    }
+  }
+
+  // ---- fused append (continued): wavefront 0 quantises the new token's K row
+  //      (lanes 0-15) and V row (lanes 16-31) exactly as the append kernel
+  //      does, parks the codes in LDS in tile-register order for the
+  //      wavefront that meets their slot, and (split 0) writes them to the cache
+  __shared__ uint32_t s_nw[2][4 * NC];
+  __shared__ float s_ns[2][NG];
+  if (wid == 0 && tnew >= 0) {
+    const SegCodes c = quantise_seg<QF>(nv);
+    if (lane < 32 && 8 * nseg < R) {
+      if constexpr (INT8) {
+        s_nw[nkv][4 * (nseg >> 1) + 2 * (nseg & 1)] = c.w[0];
+        s_nw[nkv][4 * (nseg >> 1) + 2 * (nseg & 1) + 1] = c.w[1];
+        if (nseg == 0) s_ns[nkv][0] = c.s;
+      } else {
+        s_nw[nkv][4 * (nseg >> 2) + (nseg & 3)] = c.w[0];
+        if ((nseg & 3) == 0) s_ns[nkv][nseg >> 2] = c.s;
+      }
+    }
+    if (split == 0 && nactive) {
+      uint8_t* tile = a.wcache + uint64_t(nkv ? vreg : kreg) * kRegionAlign +
+                      (uint64_t(b) * a.n_tiles + tnew) * (nkv ? tbv : tbk);
+      store_seg<QF>(tile, nkv ? rbv : rbk, lnew, nseg, c);
     }
   }
   __syncthreads();
