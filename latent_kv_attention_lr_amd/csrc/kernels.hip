@@ -516,26 +516,22 @@ void k_decode(DecodeArgs a, HeadTab ht) {
 
   // ---- fused append (continued): wavefront 0 quantises the new token's K row
   //      (lanes 0-15) and V row (lanes 16-31) exactly as the append kernel
-  //      does, parks the codes in LDS in tile-register order for the
-  //      wavefront that meets their slot, and (split 0) writes them to the cache
+  //      does and parks the codes in LDS in tile-register order for the
+  //      wavefront that meets their slot; split 0 writes them to the cache
   __shared__ uint32_t s_nw[2][4 * NC];
   __shared__ float s_ns[2][NG];
+  SegCodes nc{};
   if (wid == 0 && tnew >= 0) {
-    const SegCodes c = quantise_seg<QF>(nv);
+    nc = quantise_seg<QF>(nv);
     if (lane < 32 && 8 * nseg < R) {
       if constexpr (INT8) {
-        s_nw[nkv][4 * (nseg >> 1) + 2 * (nseg & 1)] = c.w[0];
-        s_nw[nkv][4 * (nseg >> 1) + 2 * (nseg & 1) + 1] = c.w[1];
-        if (nseg == 0) s_ns[nkv][0] = c.s;
+        s_nw[nkv][4 * (nseg >> 1) + 2 * (nseg & 1)] = nc.w[0];
+        s_nw[nkv][4 * (nseg >> 1) + 2 * (nseg & 1) + 1] = nc.w[1];
+        if (nseg == 0) s_ns[nkv][0] = nc.s;
       } else {
-        s_nw[nkv][4 * (nseg >> 2) + (nseg & 3)] = c.w[0];
-        if ((nseg & 3) == 0) s_ns[nkv][nseg >> 2] = c.s;
+        s_nw[nkv][4 * (nseg >> 2) + (nseg & 3)] = nc.w[0];
+        if ((nseg & 3) == 0) s_ns[nkv][nseg >> 2] = nc.s;
       }
-    }
-    if (split == 0 && nactive) {
-      uint8_t* tile = a.wcache + uint64_t(nkv ? vreg : kreg) * kRegionAlign +
-                      (uint64_t(b) * a.n_tiles + tnew) * (nkv ? tbv : tbk);
-      store_seg<QF>(tile, nkv ? rbv : rbk, lnew, nseg, c);
     }
   }
   __syncthreads();
@@ -557,6 +553,15 @@ void k_decode(DecodeArgs a, HeadTab ht) {
   if constexpr (Q_IN_REGS) {
 #pragma unroll
     for (int i = 0; i < QW; ++i) qo.r[i] = uniform_i(int(qo.lds[i]));
+  }
+
+  // the fused append's cache write goes out after the prologue's barriers (a
+  // barrier waits for the wavefront's outstanding stores); the lane that
+  // meets the new slot in this launch takes its codes from LDS, not memory
+  if (split == 0 && nactive) {
+    uint8_t* tile = a.wcache + uint64_t(nkv ? vreg : kreg) * kRegionAlign +
+                    (uint64_t(b) * a.n_tiles + tnew) * (nkv ? tbv : tbk);
+    store_seg<QF>(tile, nkv ? rbv : rbk, lnew, nseg, nc);
   }
 
   // ---- stream this split's tiles: one token per lane, online softmax
