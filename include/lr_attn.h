@@ -71,8 +71,8 @@ typedef struct lr_attn_desc {
   int32_t io_dtype;      /* lr_dtype of q, B^K, B^V and out */
   int32_t max_splits;    /* 0 = automatic; n >= 1 caps the context splits per (b, h) */
   int32_t wg_waves;      /* 0 = automatic; 4, 8 or 16 forces the wavefronts per work-group
-                            (16 is lowered to 8 for layers with an int8 rank above 32 or
-                            an int4 rank above 64) */
+                            (16 is lowered to 8 for layers whose largest rank is an
+                            int8 rank of 33-64 or 97-128, or an int4 rank above 64) */
   int32_t reserved;      /* must be 0 */
   const int32_t* rank_k; /* HOST [n_layers * n_heads], row-major (layer, head) */
   const int32_t* rank_v; /* HOST [n_layers * n_heads] */

@@ -112,9 +112,10 @@ __device__ __forceinline__ float swap_sum16(float a, float b) {
   const unsigned r0 = r[0], r1 = r[1];
   return __uint_as_float(r0) + __uint_as_float(r1);
 }
-__device__ __forceinline__ float wave_sum32_transposed(float* x, int lane) {
-#pragma unroll
-  for (int k = 0; k < 16; ++k) x[k] = swap_sum32(x[k], x[k + 16]);     // keeps k + 16 bit5
+// The same over each 32-lane half separately, 16 values per lane (bit 5 is
+// not reduced): lane l with (l & 4) == 0 holds its half's total of value
+// (l & 3) | ((l >> 1) & 0xc).
+__device__ __forceinline__ float half_sum16_transposed(float* x, int lane) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) x[k] = swap_sum16(x[k], x[k + 8]);       // keeps k + 8 bit4
   {
@@ -139,6 +140,11 @@ __device__ __forceinline__ float wave_sum32_transposed(float* x, int lane) {
     x[0] = keep + dpp<0xb1>(send, 0.0f);
   }
   return x[0] + dpp<0x12c>(x[0], 0.0f);                                  // row_ror:12 reads lane i + 4
+}
+__device__ __forceinline__ float wave_sum32_transposed(float* x, int lane) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) x[k] = swap_sum32(x[k], x[k + 16]);     // keeps k + 16 bit5
+  return half_sum16_transposed(x, lane);
 }
 __device__ __forceinline__ int transposed_index(int lane) { return (lane & 3) | ((lane >> 1) & 0x1c); }
 
@@ -310,12 +316,15 @@ struct DecodeArgs {
 // neighbouring lanes' codes, or the tile's scales for the last lane; a chunk
 // past the row reads the tile's first bytes.  Those codes are finite and only
 // meet q' entries that are zero (K) or accumulators that are never read (V).
-template <int NC>
-__device__ __forceinline__ void load_codes(const uint8_t* tile, int lane, int rb, uint32_t* w) {
+// With LPT = 2 lanes per token, lane half `half` takes the row's chunks
+// half, half + 2, half + 4, ... (NC of them) of token `tok`.
+template <int NC, int LPT>
+__device__ __forceinline__ void load_codes(const uint8_t* tile, int tok, int half, int rb, uint32_t* w) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const int wc = rb - 16 * c;
-    const int off = wc > 0 ? 1024 * c + min(wc, 16) * lane : 0;
+    const int cg = LPT * c + half;
+    const int wc = rb - 16 * cg;
+    const int off = wc > 0 ? 1024 * cg + min(wc, 16) * tok : 0;
     const uint4 v = *reinterpret_cast<const uint4*>(tile + off);
     w[4 * c] = v.x; w[4 * c + 1] = v.y; w[4 * c + 2] = v.z; w[4 * c + 3] = v.w;
   }
@@ -352,27 +361,27 @@ struct TileRegs {
 
 // Groups past the row (int4) re-read the last group's scale: it only
 // multiplies partial sums over zero q' entries or unread accumulators.
-template <int QF, int NC, int NG>
-__device__ __forceinline__ void load_k(const uint8_t* kt, int lane, int rk, int rbk, TileRegs<NC, NG>& x) {
-  load_codes<NC>(kt, lane, rbk, x.kw);
+template <int QF, int LPT, int NC, int NG>
+__device__ __forceinline__ void load_k(const uint8_t* kt, int tok, int half, int rk, int rbk, TileRegs<NC, NG>& x) {
+  load_codes<NC, LPT>(kt, tok, half, rbk, x.kw);
   if constexpr (QF == LR_Q_INT8_TOKEN) {
-    x.sk[0] = *reinterpret_cast<const float*>(kt + 64 * rbk + 4 * lane);
+    x.sk[0] = *reinterpret_cast<const float*>(kt + 64 * rbk + 4 * tok);
   } else {
 #pragma unroll
     for (int g = 0; g < NG; ++g)
-      x.sk[g] = half_bits_to_f32(*reinterpret_cast<const uint16_t*>(kt + 64 * rbk + 2 * (64 * min(g, (rk - 1) >> 5) + lane)));
+      x.sk[g] = half_bits_to_f32(*reinterpret_cast<const uint16_t*>(kt + 64 * rbk + 2 * (64 * min(g, (rk - 1) >> 5) + tok)));
   }
 }
 
-template <int QF, int NC, int NG>
-__device__ __forceinline__ void load_v(const uint8_t* vt, int lane, int rv, int rbv, TileRegs<NC, NG>& x) {
-  load_codes<NC>(vt, lane, rbv, x.vw);
+template <int QF, int LPT, int NC, int NG>
+__device__ __forceinline__ void load_v(const uint8_t* vt, int tok, int half, int rv, int rbv, TileRegs<NC, NG>& x) {
+  load_codes<NC, LPT>(vt, tok, half, rbv, x.vw);
   if constexpr (QF == LR_Q_INT8_TOKEN) {
-    x.sv[0] = *reinterpret_cast<const float*>(vt + 64 * rbv + 4 * lane);
+    x.sv[0] = *reinterpret_cast<const float*>(vt + 64 * rbv + 4 * tok);
   } else {
 #pragma unroll
     for (int g = 0; g < NG; ++g)
-      x.sv[g] = half_bits_to_f32(*reinterpret_cast<const uint16_t*>(vt + 64 * rbv + 2 * (64 * min(g, (rv - 1) >> 5) + lane)));
+      x.sv[g] = half_bits_to_f32(*reinterpret_cast<const uint16_t*>(vt + 64 * rbv + 2 * (64 * min(g, (rv - 1) >> 5) + tok)));
   }
 }
 
@@ -402,29 +411,39 @@ struct QOperand {
 // fp32 accumulation against q' rounded to fp16, and u accumulates with mixed
 // fp16 x fp32 FMAs.  int4 with fp32 I/O keeps q' in fp32 (bit-field extract +
 // convert + FMA) so it can be held to the tighter tolerance.
+//
+// LPT = 2 (int8, ranks above 64): two lanes share a token, each holding
+// every other 16-byte chunk of its row and half of the V accumulators; the
+// two partial scores meet with one half-wave swap, so both lanes run the same
+// softmax.  A wavefront then takes 32 tokens per step with half the
+// registers, which doubles the wavefronts a compute unit can hold.
 // Waves per SIMD the register allocation must allow: enough bytes in flight
 // per CU to cover HBM latency without spilling.
-template <int QF, int R>
+template <int QF, int R, int LPT>
 constexpr int decode_occupancy() {
-  return R <= 32 ? 5 : R <= 64 ? (QF == LR_Q_INT8_TOKEN ? 3 : 4) : 2;
+  return LPT == 2 ? (R <= 96 ? 4 : 3) : R <= 32 ? 5 : R <= 64 ? (QF == LR_Q_INT8_TOKEN ? 3 : 4) : 2;
 }
 
-template <int QF, typename IOT, int R, int NW>
+template <int QF, typename IOT, int R, int NW, int LPT>
 __global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(decode_occupancy<QF, R>(), decode_occupancy<QF, R>())))
+__attribute__((amdgpu_waves_per_eu(decode_occupancy<QF, R, LPT>(), decode_occupancy<QF, R, LPT>())))
 void k_decode(DecodeArgs a, HeadTab ht) {
   constexpr bool INT8 = QF == LR_Q_INT8_TOKEN;
   constexpr bool PACKED = !INT8 && sizeof(IOT) == 2;
   constexpr int VPC = INT8 ? 16 : 32;                  // values per 16-byte chunk
   constexpr int NC = R / VPC;                          // chunks per row in the bucket
+  constexpr int NCL = NC / LPT;                        // chunks per lane
   constexpr int NG = INT8 ? 1 : NC;                    // scales per token
   constexpr int QW = PACKED ? R / 2 : R;               // 32-bit words of q'
-  constexpr bool Q_IN_REGS = R <= 32;                  // 32 scalar registers at most
+  constexpr bool Q_IN_REGS = R <= 32 && LPT == 1;      // 32 scalar registers at most
   constexpr int RPW = (R + NW - 1) / NW;               // B rows per wavefront
   constexpr bool PREFETCH_BV = RPW <= 4;
+  constexpr int TPS = 64 / LPT;                        // tokens per wavefront step
+  static_assert(LPT == 1 || (LPT == 2 && INT8 && NC % 2 == 0), "two lanes per token: int8 only");
   using E = Elem<IOT>;
 
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int half = LPT == 2 ? lane >> 5 : 0, tok = lane & (TPS - 1);
   int idx = blockIdx.x;
   const int split = idx % a.n_split;
   idx /= a.n_split;
@@ -486,12 +505,16 @@ void k_decode(DecodeArgs a, HeadTab ht) {
   }
   const uint8_t* kplane = a.cache + uint64_t(kreg) * kRegionAlign + uint64_t(b) * a.n_tiles * tbk;
   const uint8_t* vplane = a.cache + uint64_t(vreg) * kRegionAlign + uint64_t(b) * a.n_tiles * tbv;
-  // a wavefront with no tile of its own reads tile t1 - 1 (or 0) and ignores it
-  const int tlast = max(t1 - 1, 0);
-  TileRegs<NC, NG> cur;
-  int t = t0 + wid;
-  load_k<QF>(kplane + size_t(min(t, tlast)) * tbk, lane, rk, rbk, cur);
-  load_v<QF>(vplane + size_t(min(t, tlast)) * tbv, lane, rv, rbv, cur);
+  // wavefront steps of 64 / LPT tokens (step s: tile s / LPT); a wavefront
+  // with no step of its own reads the split's last one (or tile 0) and ignores it
+  const int s0 = t0 * LPT, s1 = min(t1 * LPT, (len + TPS - 1) / TPS);
+  TileRegs<NCL, NG> cur;
+  int t = s0 + wid;
+  {
+    const int sl = min(t, max(s1 - 1, 0));
+    load_k<QF, LPT>(kplane + size_t(sl / LPT) * tbk, (sl % LPT) * TPS + tok, half, rk, rbk, cur);
+    load_v<QF, LPT>(vplane + size_t(sl / LPT) * tbv, (sl % LPT) * TPS + tok, half, rv, rbv, cur);
+  }
   const IOT* bvh = reinterpret_cast<const IOT*>(a.bv) + size_t(loff_v) * kHeadDim;
   float bv0[RPW], bv1[RPW];
   if constexpr (PREFETCH_BV) {
@@ -566,23 +589,25 @@ void k_decode(DecodeArgs a, HeadTab ht) {
 
   // ---- stream this split's tiles: one token per lane, online softmax
   float m = -__builtin_inff(), l = 0.0f;
-  float u[R];
+  constexpr int LR = R / LPT;                          // V accumulators per lane
+  float u[LR];
 #pragma unroll
-  for (int i = 0; i < R; ++i) u[i] = 0.0f;
+  for (int i = 0; i < LR; ++i) u[i] = 0.0f;
 
-  // One tile of this wavefront; PF: also fetch the wavefront's next tile into
-  // the registers just consumed.  The last tile is peeled off (PF false) so
+  // One step of this wavefront; PF: also fetch the wavefront's next step into
+  // the registers just consumed.  The last step is peeled off (PF false) so
   // that no load is in flight when the loop ends: the merge below waits for
   // every outstanding load before it can use the prefetched B^V rows.
   auto tile_step = [&](const int t, auto pf) {
     constexpr bool PF = decltype(pf)::value;
-    const bool valid = t * 64 + lane < len;
-    if (t == tnew && lane == lnew) {   // fused append: the new token's codes come from LDS
+    const bool valid = t * TPS + tok < len;
+    if (t * TPS + tok == tnew * 64 + lnew) {   // fused append: the new token's codes come from LDS
       const int z = opaque_zero();     // keeps these reads here, not hoisted out of the loop
 #pragma unroll
-      for (int i = 0; i < 4 * NC; ++i) {
-        cur.kw[i] = s_nw[0][i + z];
-        cur.vw[i] = s_nw[1][i + z];
+      for (int i = 0; i < 4 * NCL; ++i) {
+        const int j = 4 * (LPT * (i >> 2) + half) + (i & 3);
+        cur.kw[i] = s_nw[0][j + z];
+        cur.vw[i] = s_nw[1][j + z];
       }
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
@@ -593,12 +618,13 @@ void k_decode(DecodeArgs a, HeadTab ht) {
     if constexpr (!Q_IN_REGS) qo.lds = (PACKED ? s_qw : reinterpret_cast<const uint32_t*>(s_q)) + opaque_zero();
     float s = 0.0f;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (c * VPC < rk) {
+    for (int c = 0; c < NCL; ++c) {
+      if (LPT * c * VPC < rk) {   // uniform: tested on the lower half's chunk
         float part = 0.0f;
         if constexpr (INT8) {
+          const int cg = LPT * c + half;
 #pragma unroll
-          for (int k = 0; k < 16; ++k) part = fmaf(qo.f(16 * c + k), i8(cur.kw[4 * c + (k >> 2)], k & 3), part);
+          for (int k = 0; k < 16; ++k) part = fmaf(qo.f(16 * cg + k), i8(cur.kw[4 * c + (k >> 2)], k & 3), part);
           s += part;
         } else if constexpr (PACKED) {
 #pragma unroll
@@ -619,21 +645,23 @@ void k_decode(DecodeArgs a, HeadTab ht) {
         }
       }
     }
+    if constexpr (LPT == 2) s = swap_sum32(s, s);   // both lanes of the token: full score
     if constexpr (INT8) s *= cur.sk[0];
-    if constexpr (PF) load_k<QF>(kplane + size_t(t + NW) * tbk, lane, rk, rbk, cur);   // K regs are free now
+    const int tn = t + NW;   // K regs are free now: the next step's K codes
+    if constexpr (PF) load_k<QF, LPT>(kplane + size_t(tn / LPT) * tbk, (tn % LPT) * TPS + tok, half, rk, rbk, cur);
     s = valid ? s : -__builtin_inff();
     if (s > m + kTau) {  // rare after the first tile: rescale the running sums
       const float al = __builtin_amdgcn_exp2f(m - s);
       l *= al;
 #pragma unroll
-      for (int i = 0; i < R; ++i) u[i] *= al;
+      for (int i = 0; i < LR; ++i) u[i] *= al;
       m = s;
     }
     const float p = valid ? __builtin_amdgcn_exp2f(s - m) : 0.0f;
     l += p;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (c * VPC < rv) {
+    for (int c = 0; c < NCL; ++c) {
+      if (LPT * c * VPC < rv) {
         const float wt = valid ? p * cur.sv[INT8 ? 0 : c] : 0.0f;
         if constexpr (INT8) {
 #pragma unroll
@@ -662,26 +690,40 @@ void k_decode(DecodeArgs a, HeadTab ht) {
         }
       }
     }
-    if constexpr (PF) load_v<QF>(vplane + size_t(t + NW) * tbv, lane, rv, rbv, cur);   // V regs are free now
+    if constexpr (PF) load_v<QF, LPT>(vplane + size_t(tn / LPT) * tbv, (tn % LPT) * TPS + tok, half, rv, rbv, cur);
   };
-  for (; t + NW < t1; t += NW) tile_step(t, std::true_type{});
-  if (t < t1) tile_step(t, std::false_type{});
+  for (; t + NW < s1; t += NW) tile_step(t, std::true_type{});
+  if (t < s1) tile_step(t, std::false_type{});
 
-  // ---- merge the 64 lanes of each wavefront, publish per wavefront: the
-  //      V latent in transposed groups of 32 ranks (one LDS write per lane)
+  // ---- merge the lanes of each wavefront, publish per wavefront: the V
+  //      latent in transposed groups of 32 ranks, or with two lanes per token
+  //      16-rank chunks per half (one LDS write per lane)
   {
     const float Mw = lane63(wave_max63(m));
     const float f = (m == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m - Mw);
-    const float lw = wave_sum63(l * f);
+    const float lw = wave_sum63(half ? 0.0f : l * f);   // each token's l counted once
     if (lane == 63) { s_m[wid] = Mw; s_l[wid] = lw; }
+    if constexpr (LPT == 1) {
 #pragma unroll
-    for (int g = 0; g < R; g += 32) {
-      if (g < rv) {
-        float x[32];
+      for (int g = 0; g < R; g += 32) {
+        if (g < rv) {
+          float x[32];
 #pragma unroll
-        for (int k = 0; k < 32; ++k) x[k] = u[g + k] * f;
-        const float sum = wave_sum32_transposed(x, lane);
-        if ((lane & 4) == 0) s_u[wid][g + transposed_index(lane)] = sum;
+          for (int k = 0; k < 32; ++k) x[k] = u[g + k] * f;
+          const float sum = wave_sum32_transposed(x, lane);
+          if ((lane & 4) == 0) s_u[wid][g + transposed_index(lane)] = sum;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < NCL; ++c) {
+        if (LPT * c * 16 < rv) {
+          float x[16];
+#pragma unroll
+          for (int k = 0; k < 16; ++k) x[k] = u[16 * c + k] * f;
+          const float sum = half_sum16_transposed(x, lane);
+          if ((lane & 4) == 0) s_u[wid][16 * (LPT * c + half) + ((lane & 3) | ((lane >> 1) & 0xc))] = sum;
+        }
       }
     }
   }
@@ -1032,14 +1074,15 @@ __global__ __launch_bounds__(NW * 64) void k_decode_explicit(DecodeArgs a, HeadT
 
 template <int QF, typename IOT, int R>
 hipError_t launch_decode_r(int waves, dim3 grid, hipStream_t st, const DecodeArgs& a, const HeadTab& t) {
-  if constexpr (R <= 32 || (R <= 64 && QF == LR_Q_INT4_G32)) {   // 16 waves fit 128 VGPRs
+  constexpr int LPT = pair_lanes(QF, R) ? 2 : 1;
+  if constexpr (max_wg_waves(QF, R) == 16) {
     if (waves == 16) {
-      hipLaunchKernelGGL((k_decode<QF, IOT, R, 16>), grid, dim3(1024), 0, st, a, t);
+      hipLaunchKernelGGL((k_decode<QF, IOT, R, 16, LPT>), grid, dim3(1024), 0, st, a, t);
       return hipGetLastError();
     }
   }
-  if (waves == 8) hipLaunchKernelGGL((k_decode<QF, IOT, R, 8>), grid, dim3(512), 0, st, a, t);
-  else hipLaunchKernelGGL((k_decode<QF, IOT, R, 4>), grid, dim3(256), 0, st, a, t);
+  if (waves == 8) hipLaunchKernelGGL((k_decode<QF, IOT, R, 8, LPT>), grid, dim3(512), 0, st, a, t);
+  else hipLaunchKernelGGL((k_decode<QF, IOT, R, 4, LPT>), grid, dim3(256), 0, st, a, t);
   return hipGetLastError();
 }
 

@@ -33,7 +33,8 @@ namespace lr {
 Split choose_split(const lr_attn_plan& p, int32_t layer, int32_t max_len) {
   // Wavefronts per (b, h) work-group: 8 where the registers leave room for
   // two such work-groups per compute unit (rank 32 at 5 waves per SIMD, int4
-  // rank 64 at 4), else 4 (int8 rank 64 at 3, ranks above 64 at 2).  Several
+  // rank 64 and int8 ranks 65-96 (two lanes per token) at 4), else 4 (int8
+  // rank 64 and ranks 97-128 at 3, int4 ranks above 64 at 2).  Several
   // work-groups per compute unit run out of phase, so one group's prologue and
   // merge overlap another's streaming.  With few (b, h) units the count
   // doubles, up to 16 where 128 VGPRs suffice, until 4096 wavefronts (16 per
@@ -44,8 +45,8 @@ Split choose_split(const lr_attn_plan& p, int32_t layer, int32_t max_len) {
   const int64_t units = static_cast<int64_t>(p.desc.batch) * p.desc.n_heads;
   const int64_t tiles = ceil_div(max_len, kTile);
   const int bucket = layer_bucket(p.layers[layer]);
-  const bool wide = bucket <= 32 || (bucket <= 64 && p.desc.qfmt == LR_Q_INT4_G32);
-  const int nw_max = wide ? 16 : 8;
+  const int nw_max = max_wg_waves(p.desc.qfmt, bucket);
+  const bool wide = nw_max == 16;
   int nw = wide ? 8 : 4;
   if (p.desc.wg_waves > 0) {
     nw = std::min(p.desc.wg_waves, nw_max);

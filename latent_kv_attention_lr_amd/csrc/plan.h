@@ -33,6 +33,15 @@ inline int layer_bucket(const lr_attn_plan::Layer& L) {
   const int r = L.rk_max > L.rv_max ? L.rk_max : L.rv_max;
   return r <= 32 ? 32 : r <= 64 ? 64 : r <= 96 ? 96 : 128;
 }
+// Buckets whose decode kernel puts two lanes on each token (int8 ranks above
+// 64): half the registers per lane, twice the wavefronts per compute unit.
+constexpr bool pair_lanes(int qfmt, int bucket) { return qfmt == LR_Q_INT8_TOKEN && bucket > 64; }
+// Largest work-group of a bucket's decode kernel: 16 wavefronts where 128
+// VGPRs per lane suffice (four wavefronts per SIMD), else 8.
+constexpr int max_wg_waves(int qfmt, int bucket) {
+  return (bucket <= 32 || (bucket <= 64 && qfmt == LR_Q_INT4_G32) || (pair_lanes(qfmt, bucket) && bucket <= 96))
+             ? 16 : 8;
+}
 Split choose_split(const lr_attn_plan& p, int32_t layer, int32_t max_len);
 // The explicit-reconstruction kernel never splits the context: 4 or 8 waves.
 Split explicit_split(const lr_attn_plan& p, int32_t layer, int32_t max_len);

@@ -167,10 +167,14 @@ def _ragged_session(qfmt, io, max_splits, rng):
     return _session(qfmt, io, max_splits, rng, 6, 700, [32, 8, 96], [64, 16, 40])
 
 
-def _long_session(qfmt, io, max_splits, rng):
+def _long_session(qfmt, io, max_splits, rng, rk=(32, 64), rv=(48, 64)):
     # 3 sequences x 2 heads over 8192 slots: few work-groups, so the launch
     # splits each context and merges the partials in a second kernel
-    return _session(qfmt, io, max_splits, rng, 3, 8192, [32, 64], [48, 64])
+    return _session(qfmt, io, max_splits, rng, 3, 8192, list(rk), list(rv))
+
+
+# ranks 65-96: the int8 kernel puts two lanes on each token
+WIDE_RANKS = ((96, 40), (72, 96))
 
 
 def _check_session(s, rk, rv, ck, cv, bk, bv, q, lens, qfmt, io, max_len, explicit=False):
@@ -210,18 +214,20 @@ def test_decode_ragged_and_degenerate_lengths(qfmt, io, max_splits):
 
 # Every tail width of the last 16-byte code chunk (int8 rows: 8 or 16 bytes;
 # int4 rows: 4, 8, 12 or 16 bytes) and every int4 partial group, in the
-# smallest and the largest rank bucket.
+# smallest, the paired-lane (int8) and the largest rank bucket.  In the 96
+# bucket the int8 tail chunk falls to either lane of a token's pair.
 TAIL_RANKS = {
     32: ([8, 16, 24, 32], [24, 8, 32, 16]),
+    96: ([8, 24, 40, 56, 72, 80, 88, 96], [96, 88, 72, 64, 48, 32, 16, 8]),
     128: ([8, 16, 24, 32, 56, 72, 112, 120], [120, 104, 88, 64, 48, 40, 16, 8]),
 }
 
 
 @pytest.mark.parametrize("qfmt", [LR_Q_INT8_TOKEN, LR_Q_INT4_G32])
 @pytest.mark.parametrize("io", [LR_DT_BF16, LR_DT_F32])
-@pytest.mark.parametrize("bucket", [32, 128])
+@pytest.mark.parametrize("bucket", [32, 96, 128])
 def test_decode_every_row_tail_width(qfmt, io, bucket):
-    rng = np.random.default_rng(90 + 4 * qfmt + 2 * io + (bucket == 128))
+    rng = np.random.default_rng(90 + 4 * qfmt + 2 * io + (bucket == 128) + 8 * (bucket == 96))
     rk, rv = TAIL_RANKS[bucket]
     say(f"decode tail widths qfmt={qfmt} io={io} bucket={bucket}")
     sess = _session(qfmt, io, 0, rng, 4, 300, rk, rv)
@@ -258,6 +264,9 @@ def test_decode_context_split_path(qfmt, io):
     # one sequence within a single split, one ending inside a later split, one full
     _check_session(*sess, [100, 3001, 8192], qfmt, io, 8192)
     _check_session(*sess, [0, 8191, 2048], qfmt, io, 8192)
+    sess = _long_session(qfmt, io, 0, rng, *WIDE_RANKS)
+    assert lr_attn_workspace_bytes(sess[0].plan, 8192) > 0, "this shape must split the context"
+    _check_session(*sess, [8192, 33, 4097], qfmt, io, 8192)
 
 
 def _fused_equals_separate(sess, lens, pos, max_len, seed):
@@ -300,6 +309,9 @@ def test_append_decode_fused_equals_separate(qfmt, io):
     sess = _long_session(qfmt, io, 0, rng)
     lens = [100, 3001, 8192]
     _fused_equals_separate(sess, lens, [n - 1 for n in lens], 8192, 3)
+    sess = _long_session(qfmt, io, 0, rng, *WIDE_RANKS)
+    lens = [97, 4096, 8000]
+    _fused_equals_separate(sess, lens, [n - 1 for n in lens], 8192, 4)
 
 
 def test_decode_max_len_clamps_longer_lengths():
