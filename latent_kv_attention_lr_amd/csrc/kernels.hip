@@ -316,13 +316,13 @@ struct DecodeArgs {
 // neighbouring lanes' codes, or the tile's scales for the last lane; a chunk
 // past the row reads the tile's first bytes.  Those codes are finite and only
 // meet q' entries that are zero (K) or accumulators that are never read (V).
-// With LPT = 2 lanes per token, lane half `half` takes the row's chunks
-// half, half + 2, half + 4, ... (NC of them) of token `tok`.
-template <int NC, int LPT>
-__device__ __forceinline__ void load_codes(const uint8_t* tile, int tok, int half, int rb, uint32_t* w) {
+// With lm = 2 lanes per token, lane half hf takes the row's chunks hf,
+// hf + 2, hf + 4, ... (NC of them) of token `tok`; with lm = 1 chunks 0..NC-1.
+template <int NC>
+__device__ __forceinline__ void load_codes(const uint8_t* tile, int tok, int lm, int hf, int rb, uint32_t* w) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const int cg = LPT * c + half;
+    const int cg = lm * c + hf;
     const int wc = rb - 16 * cg;
     const int off = wc > 0 ? 1024 * cg + min(wc, 16) * tok : 0;
     const uint4 v = *reinterpret_cast<const uint4*>(tile + off);
@@ -361,9 +361,9 @@ struct TileRegs {
 
 // Groups past the row (int4) re-read the last group's scale: it only
 // multiplies partial sums over zero q' entries or unread accumulators.
-template <int QF, int LPT, int NC, int NG>
-__device__ __forceinline__ void load_k(const uint8_t* kt, int tok, int half, int rk, int rbk, TileRegs<NC, NG>& x) {
-  load_codes<NC, LPT>(kt, tok, half, rbk, x.kw);
+template <int QF, int NC, int NG>
+__device__ __forceinline__ void load_k(const uint8_t* kt, int tok, int lm, int hf, int rk, int rbk, TileRegs<NC, NG>& x) {
+  load_codes<NC>(kt, tok, lm, hf, rbk, x.kw);
   if constexpr (QF == LR_Q_INT8_TOKEN) {
     x.sk[0] = *reinterpret_cast<const float*>(kt + 64 * rbk + 4 * tok);
   } else {
@@ -373,9 +373,9 @@ __device__ __forceinline__ void load_k(const uint8_t* kt, int tok, int half, int
   }
 }
 
-template <int QF, int LPT, int NC, int NG>
-__device__ __forceinline__ void load_v(const uint8_t* vt, int tok, int half, int rv, int rbv, TileRegs<NC, NG>& x) {
-  load_codes<NC, LPT>(vt, tok, half, rbv, x.vw);
+template <int QF, int NC, int NG>
+__device__ __forceinline__ void load_v(const uint8_t* vt, int tok, int lm, int hf, int rv, int rbv, TileRegs<NC, NG>& x) {
+  load_codes<NC>(vt, tok, lm, hf, rbv, x.vw);
   if constexpr (QF == LR_Q_INT8_TOKEN) {
     x.sv[0] = *reinterpret_cast<const float*>(vt + 64 * rbv + 4 * tok);
   } else {
@@ -416,7 +416,10 @@ struct QOperand {
 // every other 16-byte chunk of its row and half of the V accumulators; the
 // two partial scores meet with one half-wave swap, so both lanes run the same
 // softmax.  A wavefront then takes 32 tokens per step with half the
-// registers, which doubles the wavefronts a compute unit can hold.
+// registers, which doubles the wavefronts a compute unit can hold.  A head
+// whose rows fit in half of the bucket keeps one lane per token in the same
+// registers (64 tokens, twice the bytes per step: light heads are bound by
+// the bytes each wavefront has in flight).  The choice is per work-group.
 // Waves per SIMD the register allocation must allow: enough bytes in flight
 // per CU to cover HBM latency without spilling.
 template <int QF, int R, int LPT>
@@ -438,12 +441,10 @@ void k_decode(DecodeArgs a, HeadTab ht) {
   constexpr bool Q_IN_REGS = R <= 32 && LPT == 1;      // 32 scalar registers at most
   constexpr int RPW = (R + NW - 1) / NW;               // B rows per wavefront
   constexpr bool PREFETCH_BV = RPW <= 4;
-  constexpr int TPS = 64 / LPT;                        // tokens per wavefront step
   static_assert(LPT == 1 || (LPT == 2 && INT8 && NC % 2 == 0), "two lanes per token: int8 only");
   using E = Elem<IOT>;
 
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
-  const int half = LPT == 2 ? lane >> 5 : 0, tok = lane & (TPS - 1);
   int idx = blockIdx.x;
   const int split = idx % a.n_split;
   idx /= a.n_split;
@@ -455,6 +456,11 @@ void k_decode(DecodeArgs a, HeadTab ht) {
   const uint32_t kreg = uniform_i(int(ht.kreg[h])), vreg = uniform_i(int(ht.vreg[h]));
   const int rbk = row_bytes(QF, rk), rbv = row_bytes(QF, rv);
   const int tbk = tile_bytes(QF, rk), tbv = tile_bytes(QF, rv);
+  // lanes per token in this work-group (uniform), lane half, log2 of the
+  // tokens per wavefront step, and this lane's token within a step
+  const int lm = (LPT == 2 && max(rk, rv) > R / 2) ? 2 : 1;
+  const int hf = lm == 2 ? lane >> 5 : 0, tsh = lm == 2 ? 5 : 6;
+  const int tok = lane & ((1 << tsh) - 1);
   const int len = min(max(a.len[b], 0), a.max_len);
   const int ntiles = (len + 63) >> 6;
   const int n_live = max(1, (ntiles + a.tps - 1) / a.tps);
@@ -505,15 +511,17 @@ void k_decode(DecodeArgs a, HeadTab ht) {
   }
   const uint8_t* kplane = a.cache + uint64_t(kreg) * kRegionAlign + uint64_t(b) * a.n_tiles * tbk;
   const uint8_t* vplane = a.cache + uint64_t(vreg) * kRegionAlign + uint64_t(b) * a.n_tiles * tbv;
-  // wavefront steps of 64 / LPT tokens (step s: tile s / LPT); a wavefront
+  // wavefront steps of 64 / lm tokens (step s: tile s / lm); a wavefront
   // with no step of its own reads the split's last one (or tile 0) and ignores it
-  const int s0 = t0 * LPT, s1 = min(t1 * LPT, (len + TPS - 1) / TPS);
+  const int s0 = t0 * lm, s1 = min(t1 * lm, (len + (1 << tsh) - 1) >> tsh);
+  auto step_tile = [&](int st) { return size_t(st >> (lm - 1)); };
+  auto step_tok = [&](int st) { return ((st & (lm - 1)) << tsh) + tok; };
   TileRegs<NCL, NG> cur;
   int t = s0 + wid;
   {
     const int sl = min(t, max(s1 - 1, 0));
-    load_k<QF, LPT>(kplane + size_t(sl / LPT) * tbk, (sl % LPT) * TPS + tok, half, rk, rbk, cur);
-    load_v<QF, LPT>(vplane + size_t(sl / LPT) * tbv, (sl % LPT) * TPS + tok, half, rv, rbv, cur);
+    load_k<QF>(kplane + step_tile(sl) * tbk, step_tok(sl), lm, hf, rk, rbk, cur);
+    load_v<QF>(vplane + step_tile(sl) * tbv, step_tok(sl), lm, hf, rv, rbv, cur);
   }
   const IOT* bvh = reinterpret_cast<const IOT*>(a.bv) + size_t(loff_v) * kHeadDim;
   float bv0[RPW], bv1[RPW];
@@ -600,12 +608,12 @@ void k_decode(DecodeArgs a, HeadTab ht) {
   // every outstanding load before it can use the prefetched B^V rows.
   auto tile_step = [&](const int t, auto pf) {
     constexpr bool PF = decltype(pf)::value;
-    const bool valid = t * TPS + tok < len;
-    if (t * TPS + tok == tnew * 64 + lnew) {   // fused append: the new token's codes come from LDS
+    const bool valid = (t << tsh) + tok < len;
+    if ((t << tsh) + tok == tnew * 64 + lnew) {   // fused append: the new token's codes come from LDS
       const int z = opaque_zero();     // keeps these reads here, not hoisted out of the loop
 #pragma unroll
       for (int i = 0; i < 4 * NCL; ++i) {
-        const int j = 4 * (LPT * (i >> 2) + half) + (i & 3);
+        const int j = 4 * (lm * (i >> 2) + hf) + (i & 3);
         cur.kw[i] = s_nw[0][j + z];
         cur.vw[i] = s_nw[1][j + z];
       }
@@ -619,10 +627,10 @@ void k_decode(DecodeArgs a, HeadTab ht) {
     float s = 0.0f;
 #pragma unroll
     for (int c = 0; c < NCL; ++c) {
-      if (LPT * c * VPC < rk) {   // uniform: tested on the lower half's chunk
+      if (lm * c * VPC < rk) {   // uniform: tested on the lower half's chunk
         float part = 0.0f;
         if constexpr (INT8) {
-          const int cg = LPT * c + half;
+          const int cg = lm * c + hf;
 #pragma unroll
           for (int k = 0; k < 16; ++k) part = fmaf(qo.f(16 * cg + k), i8(cur.kw[4 * c + (k >> 2)], k & 3), part);
           s += part;
@@ -645,10 +653,13 @@ void k_decode(DecodeArgs a, HeadTab ht) {
         }
       }
     }
-    if constexpr (LPT == 2) s = swap_sum32(s, s);   // both lanes of the token: full score
+    if constexpr (LPT == 2) {   // both lanes of a token: the full score
+      const float both = swap_sum32(s, s);
+      s = lm == 2 ? both : s;
+    }
     if constexpr (INT8) s *= cur.sk[0];
     const int tn = t + NW;   // K regs are free now: the next step's K codes
-    if constexpr (PF) load_k<QF, LPT>(kplane + size_t(tn / LPT) * tbk, (tn % LPT) * TPS + tok, half, rk, rbk, cur);
+    if constexpr (PF) load_k<QF>(kplane + step_tile(tn) * tbk, step_tok(tn), lm, hf, rk, rbk, cur);
     s = valid ? s : -__builtin_inff();
     if (s > m + kTau) {  // rare after the first tile: rescale the running sums
       const float al = __builtin_amdgcn_exp2f(m - s);
@@ -661,7 +672,7 @@ void k_decode(DecodeArgs a, HeadTab ht) {
     l += p;
 #pragma unroll
     for (int c = 0; c < NCL; ++c) {
-      if (LPT * c * VPC < rv) {
+      if (lm * c * VPC < rv) {
         const float wt = valid ? p * cur.sv[INT8 ? 0 : c] : 0.0f;
         if constexpr (INT8) {
 #pragma unroll
@@ -690,7 +701,7 @@ void k_decode(DecodeArgs a, HeadTab ht) {
         }
       }
     }
-    if constexpr (PF) load_v<QF, LPT>(vplane + size_t(tn / LPT) * tbv, (tn % LPT) * TPS + tok, half, rv, rbv, cur);
+    if constexpr (PF) load_v<QF>(vplane + step_tile(tn) * tbv, step_tok(tn), lm, hf, rv, rbv, cur);
   };
   for (; t + NW < s1; t += NW) tile_step(t, std::true_type{});
   if (t < s1) tile_step(t, std::false_type{});
@@ -701,7 +712,7 @@ void k_decode(DecodeArgs a, HeadTab ht) {
   {
     const float Mw = lane63(wave_max63(m));
     const float f = (m == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m - Mw);
-    const float lw = wave_sum63(half ? 0.0f : l * f);   // each token's l counted once
+    const float lw = wave_sum63(hf ? 0.0f : l * f);   // each token's l counted once
     if (lane == 63) { s_m[wid] = Mw; s_l[wid] = lw; }
     if constexpr (LPT == 1) {
 #pragma unroll
@@ -717,12 +728,17 @@ void k_decode(DecodeArgs a, HeadTab ht) {
     } else {
 #pragma unroll
       for (int c = 0; c < NCL; ++c) {
-        if (LPT * c * 16 < rv) {
+        if (lm * c * 16 < rv) {
           float x[16];
 #pragma unroll
           for (int k = 0; k < 16; ++k) x[k] = u[16 * c + k] * f;
+          if (lm == 1) {   // one token per lane: the halves hold the same ranks
+#pragma unroll
+            for (int k = 0; k < 16; ++k) x[k] = swap_sum32(x[k], x[k]);
+          }
           const float sum = half_sum16_transposed(x, lane);
-          if ((lane & 4) == 0) s_u[wid][16 * (LPT * c + half) + ((lane & 3) | ((lane >> 1) & 0xc))] = sum;
+          if ((lane & 4) == 0 && (lm == 2 || lane < 32))
+            s_u[wid][16 * (lm * c + hf) + ((lane & 3) | ((lane >> 1) & 0xc))] = sum;
         }
       }
     }

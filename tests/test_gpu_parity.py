@@ -173,8 +173,9 @@ def _long_session(qfmt, io, max_splits, rng, rk=(32, 64), rv=(48, 64)):
     return _session(qfmt, io, max_splits, rng, 3, 8192, list(rk), list(rv))
 
 
-# ranks 65-96: the int8 kernel puts two lanes on each token
-WIDE_RANKS = ((96, 40), (72, 96))
+# ranks 65-96: the int8 kernel puts two lanes on each token, except for a
+# head whose ranks are at most 48 (the third), which keeps one lane per token
+WIDE_RANKS = ((96, 40, 24), (72, 96, 48))
 
 
 def _check_session(s, rk, rv, ck, cv, bk, bv, q, lens, qfmt, io, max_len, explicit=False):
@@ -215,10 +216,11 @@ def test_decode_ragged_and_degenerate_lengths(qfmt, io, max_splits):
 # Every tail width of the last 16-byte code chunk (int8 rows: 8 or 16 bytes;
 # int4 rows: 4, 8, 12 or 16 bytes) and every int4 partial group, in the
 # smallest, the paired-lane (int8) and the largest rank bucket.  In the 96
-# bucket the int8 tail chunk falls to either lane of a token's pair.
+# bucket the int8 tail chunk falls to either lane of a token's pair, and the
+# heads with both ranks at most 48 run one lane per token.
 TAIL_RANKS = {
     32: ([8, 16, 24, 32], [24, 8, 32, 16]),
-    96: ([8, 24, 40, 56, 72, 80, 88, 96], [96, 88, 72, 64, 48, 32, 16, 8]),
+    96: ([8, 24, 40, 56, 72, 96, 16, 48, 88], [40, 16, 8, 88, 64, 8, 48, 24, 96]),
     128: ([8, 16, 24, 32, 56, 72, 112, 120], [120, 104, 88, 64, 48, 40, 16, 8]),
 }
 
