@@ -549,11 +549,11 @@ void k_decode(DecodeArgs a, HeadTab ht) {
   //      (lanes 0-15) and V row (lanes 16-31) exactly as the append kernel
   //      does and parks the codes in LDS in tile-register order for the
   //      wavefront that meets their slot; split 0 writes them to the cache
+  //      when it is done (store_new)
   __shared__ uint32_t s_nw[2][4 * NC];
   __shared__ float s_ns[2][NG];
-  SegCodes nc{};
   if (wid == 0 && tnew >= 0) {
-    nc = quantise_seg<QF>(nv);
+    const SegCodes nc = quantise_seg<QF>(nv);
     if (lane < 32 && 8 * nseg < R) {
       if constexpr (INT8) {
         s_nw[nkv][4 * (nseg >> 1) + 2 * (nseg & 1)] = nc.w[0];
@@ -586,14 +586,28 @@ void k_decode(DecodeArgs a, HeadTab ht) {
     for (int i = 0; i < QW; ++i) qo.r[i] = uniform_i(int(qo.lds[i]));
   }
 
-  // the fused append's cache write goes out after the prologue's barriers (a
-  // barrier waits for the wavefront's outstanding stores); the lane that
-  // meets the new slot in this launch takes its codes from LDS, not memory
-  if (split == 0 && nactive) {
-    uint8_t* tile = a.wcache + uint64_t(nkv ? vreg : kreg) * kRegionAlign +
-                    (uint64_t(b) * a.n_tiles + tnew) * (nkv ? tbv : tbk);
-    store_seg<QF>(tile, nkv ? rbv : rbk, lnew, nseg, nc);
-  }
+  // The fused append's cache write is the work-group's last act (store_new
+  // below): this launch takes the new token's codes from LDS, and on this GPU
+  // stores count in the same vmcnt as loads, so a store issued before the
+  // loop makes every later load wait of wavefront 0 wait for it as well, and
+  // a store queued behind the stream of reads completes late.  A barrier also
+  // waits for outstanding stores, so the write follows the last barrier.
+  auto store_new = [&]() {
+    if (split == 0 && nactive) {
+      SegCodes c{};
+      if constexpr (INT8) {
+        c.w[0] = s_nw[nkv][4 * (nseg >> 1) + 2 * (nseg & 1)];
+        c.w[1] = s_nw[nkv][4 * (nseg >> 1) + 2 * (nseg & 1) + 1];
+        c.s = s_ns[nkv][0];
+      } else {
+        c.w[0] = s_nw[nkv][4 * (nseg >> 2) + (nseg & 3)];
+        c.sh = __builtin_bit_cast(uint16_t, _Float16(s_ns[nkv][nseg >> 2]));   // exact: an fp16 value
+      }
+      uint8_t* tile = a.wcache + uint64_t(nkv ? vreg : kreg) * kRegionAlign +
+                      (uint64_t(b) * a.n_tiles + tnew) * (nkv ? tbv : tbk);
+      store_seg<QF>(tile, nkv ? rbv : rbk, lnew, nseg, c);
+    }
+  };
 
   // ---- stream this split's tiles: one token per lane, online softmax
   float m = -__builtin_inff(), l = 0.0f;
@@ -764,6 +778,7 @@ void k_decode(DecodeArgs a, HeadTab ht) {
       for (int w = 0; w < NW; ++w) ui = fmaf(fw[w], s_u[w][tid], ui);
       part[2 + tid] = ui;
     }
+    store_new();
     return;
   }
 
@@ -800,6 +815,7 @@ void k_decode(DecodeArgs a, HeadTab ht) {
     for (int w = 0; w < NW; ++w) acc += s_o[w][tid];
     E::st(reinterpret_cast<IOT*>(a.out) + size_t(unit) * kHeadDim, tid, acc);
   }
+  store_new();
 }
 
 // o[j] = sum_i v[i] B^V_h[i][j] for j < 128, v = u / l already in LDS (s_v),
