@@ -400,10 +400,11 @@ struct QOperand {
   __device__ __forceinline__ float f(int i) const { return __uint_as_float(word(i)); }
 };
 
-// One work-group per (b, h, split).  NW wavefronts take the split's 64-token
-// tiles round-robin; each lane owns one token of a tile.  Without context
-// splitting the group finishes the output itself; with it, the group writes
-// its partial (m, l, u) and k_merge combines them.
+// One work-group per (b, h, split).  NW wavefronts take the split's steps
+// round-robin: a step is one 64-token tile with one token per lane, or (two
+// lanes per token, below) half a tile.  Without context splitting the group
+// finishes the output itself; with it, the group writes its partial (m, l, u)
+// and k_merge combines them.
 //
 // int8 codes: the score is sum_i q'_i c_i (one SDWA convert + one FMA per
 // value), the V latent u_i += w c_i.  int4 codes with bf16 I/O: codes become
@@ -420,6 +421,7 @@ struct QOperand {
 // whose rows fit in half of the bucket keeps one lane per token in the same
 // registers (64 tokens, twice the bytes per step: light heads are bound by
 // the bytes each wavefront has in flight).  The choice is per work-group.
+//
 // Waves per SIMD the register allocation must allow: enough bytes in flight
 // per CU to cover HBM latency without spilling.
 template <int QF, int R, int LPT>
@@ -444,7 +446,8 @@ void k_decode(DecodeArgs a, HeadTab ht) {
   static_assert(LPT == 1 || (LPT == 2 && INT8 && NC % 2 == 0), "two lanes per token: int8 only");
   using E = Elem<IOT>;
 
-  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  // wid is uniform: step indices and loop control live in scalar registers
+  const int tid = threadIdx.x, wid = uniform_i(tid >> 6), lane = tid & 63;
   int idx = blockIdx.x;
   const int split = idx % a.n_split;
   idx /= a.n_split;
@@ -587,7 +590,7 @@ void k_decode(DecodeArgs a, HeadTab ht) {
   }
 
   // The fused append's cache write is the work-group's last act (store_new
-  // below): this launch takes the new token's codes from LDS, and on this GPU
+  // below): this launch takes the new token's codes from LDS, and on gfx950
   // stores count in the same vmcnt as loads, so a store issued before the
   // loop makes every later load wait of wavefront 0 wait for it as well, and
   // a store queued behind the stream of reads completes late.  A barrier also
@@ -609,7 +612,7 @@ void k_decode(DecodeArgs a, HeadTab ht) {
     }
   };
 
-  // ---- stream this split's tiles: one token per lane, online softmax
+  // ---- stream this split's steps (one token per lane or lane pair), online softmax
   float m = -__builtin_inff(), l = 0.0f;
   constexpr int LR = R / LPT;                          // V accumulators per lane
   float u[LR];
