@@ -309,6 +309,28 @@ def main():
         result["roofline"]["cold_achieved"] = bytes_launch / cold_s / 1e9
         del flush
 
+    # ---- practical read roof on this GPU (context for roofline.frac): a plain
+    # streaming read of 1 GiB, which no last-level cache holds
+    if not args.profile_steps:
+        from latent_kv_attention_lr_amd import lr_attn_probe_read
+        buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            lr_attn_probe_read(buf, buf.numel(), sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            lr_attn_probe_read(buf, buf.numel(), sink)
+        e1.record()
+        torch.cuda.synchronize()
+        probe_gbs = buf.numel() * 10 / (e0.elapsed_time(e1) / 1e3) / 1e9
+        result["roofline"]["stream_read_probe"] = {
+            "value": probe_gbs, "unit": "GB/s", "frac_of_peak": probe_gbs / PEAK_HBM_GBS,
+            "kernel": "lr_attn_probe_read", "bytes": buf.numel(),
+            "achieved_vs_probe": achieved / probe_gbs}
+        del buf, sink
+
     if keep:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cb = cpu_baseline(run, n_cpu)

@@ -203,6 +203,16 @@ lr_status lr_attn_decode_explicit(const lr_attn_plan* plan, int32_t layer, const
                                   const void* bk, const void* bv, float softmax_scale, void* out,
                                   void* workspace, size_t ws_bytes, void* stream);
 
+/* Measurement aid, not part of the decode path: streams bytes / 16 16-byte
+ * words from device memory src (16-byte aligned, bytes >= 16; a trailing
+ * partial word is not read) with a plain grid-stride read kernel, the
+ * practical HBM read roof that the decode kernels' achieved bandwidth is set
+ * against.  sink: device pointer to one uint32_t, written only in a case that
+ * does not occur in practice (it keeps the reads from being optimised away).
+ * Asynchronous on stream.  Errors: LR_EINVAL (null pointer, bytes < 16,
+ * misaligned src or sink), LR_EHIP (launch failed). */
+lr_status lr_attn_probe_read(const void* src, size_t bytes, void* sink, void* stream);
+
 /* Static description of a status. */
 const char* lr_attn_strerror(lr_status status);
 /* hipError_t of the last call on this thread that returned LR_EHIP (0 if none). */

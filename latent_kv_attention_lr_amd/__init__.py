@@ -90,6 +90,7 @@ def _load() -> ctypes.CDLL:
         "lr_attn_decode_explicit": (ctypes.c_int, [P, I32, P, P, I32, P, P, P, ctypes.c_float, P, P, SZ, P]),
         "lr_attn_append_decode": (ctypes.c_int, [P, I32, P, P, P, P, P, I32, P, P, P, ctypes.c_float,
                                                  P, P, SZ, P]),
+        "lr_attn_probe_read": (ctypes.c_int, [P, SZ, P, P]),
         "lr_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "lr_attn_last_hip_error": (I32, []),
     }
@@ -202,3 +203,10 @@ def lr_attn_decode_explicit(plan: int, layer: int, cache, length, max_len: int, 
                                         _ptr(bk), _ptr(bv), softmax_scale, _ptr(out),
                                         _ptr(workspace), ws_bytes, _stream(stream)),
            "lr_attn_decode_explicit")
+
+
+def lr_attn_probe_read(src, nbytes: int, sink, stream=None) -> None:
+    """Measurement aid: stream ``nbytes`` of device memory ``src`` with a plain
+    read kernel (``sink``: a device int32/uint32 the kernel practically never
+    writes)."""
+    _check(_lib.lr_attn_probe_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "lr_attn_probe_read")

@@ -285,4 +285,9 @@ const char* lr_attn_strerror(lr_status s) {
 
 int32_t lr_attn_last_hip_error(void) { return g_last_hip; }
 
+lr_status lr_attn_probe_read(const void* src, size_t bytes, void* sink, void* stream) {
+  if (!src || !sink || bytes < 16 || !aligned(src, 16) || !aligned(sink, 4)) return LR_EINVAL;
+  return hip_status(lr::launch_probe_read(src, bytes, sink, stream));
+}
+
 }  // extern "C"

@@ -62,5 +62,7 @@ int launch_decode(const lr_attn_plan& p, int32_t layer, const void* cache, const
                   int32_t max_len, const void* q, const void* bk, const void* bv, float scale,
                   void* out, void* workspace, void* stream, bool explicit_form,
                   const AppendInputs* app = nullptr);
+// probe.hip: stream bytes / 16 16-byte words from src (read only).
+int launch_probe_read(const void* src, size_t bytes, void* sink, void* stream);
 
 }  // namespace lr

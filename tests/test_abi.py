@@ -240,3 +240,16 @@ def test_product_package_never_loads_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f
     assert "oracle" not in open(HEADER).read().lower()
+
+
+@pytest.mark.parametrize("src,nbytes,sink", [
+    (None, 1 << 20, 0x1000),        # null source
+    (0x1000, 1 << 20, None),        # null sink
+    (0x1000, 8, 0x2000),            # fewer than 16 bytes
+    (0x1008, 1 << 20, 0x2000),      # source not 16-byte aligned
+    (0x1000, 1 << 20, 0x2002),      # sink not 4-byte aligned
+])
+def test_probe_read_rejects_bad_arguments(src, nbytes, sink):
+    # rejected on the host: these addresses are never dereferenced
+    st = lr._lib.lr_attn_probe_read(src, nbytes, sink, None)
+    assert st == lr.LR_EINVAL

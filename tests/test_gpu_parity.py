@@ -441,3 +441,23 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for s in range(steps):
             assert torch.equal(outs[s], ref[s]), (rep, s)
+
+
+def test_probe_read_runs_and_leaves_memory_alone():
+    """The streaming read probe (bandwidth context for the benchmark) reads
+    every word of a buffer with a ragged tail and writes nothing else."""
+    from latent_kv_attention_lr_amd import lr_attn_probe_read
+    say("probe read")
+    n = (1 << 20) + 48                      # not a multiple of the grid's 8 KiB stride
+    buf = (torch.arange(n, device=DEV) % 251).to(torch.uint8)
+    before = buf.clone()
+    sink = torch.zeros(4, dtype=torch.int32, device=DEV)
+    lr_attn_probe_read(buf, n, sink)
+    lr_attn_probe_read(buf, 16, sink)
+    torch.cuda.synchronize()
+    assert torch.equal(buf, before)
+    # the sink is written only if the XOR of everything read equals the probe's
+    # sentinel value; check that against the host's XOR of the same words
+    words = before.cpu().numpy()[: n // 16 * 16].view("<u4")
+    x = int(np.bitwise_xor.reduce(words))
+    assert int(sink[0].item()) & 0xffffffff == (x if x == 0x9e3779b9 else 0)
