@@ -461,3 +461,57 @@ def test_probe_read_runs_and_leaves_memory_alone():
     words = before.cpu().numpy()[: n // 16 * 16].view("<u4")
     x = int(np.bitwise_xor.reduce(words))
     assert int(sink[0].item()) & 0xffffffff == (x if x == 0x9e3779b9 else 0)
+
+
+# ---------------------------------------------------------------------------
+# maximum sizes
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("qfmt", [LR_Q_INT8_TOKEN, LR_Q_INT4_G32])
+def test_decode_all_128_heads(qfmt):
+    """The largest head count a plan takes, with ranks 8..128 spread over the
+    heads (K and V apart), so the layer runs the rank-128 kernel with every
+    row width and, for int8, heads in both lane modes."""
+    rng = np.random.default_rng(200 + qfmt)
+    ranks = list(range(8, 129, 8))
+    rk = [ranks[i % 16] for i in range(128)]
+    rv = [ranks[(5 * i + 3) % 16] for i in range(128)]
+    say(f"decode 128 heads qfmt={qfmt}")
+    sess = _session(qfmt, LR_DT_BF16, 0, rng, 2, 200, rk, rv)
+    _check_session(*sess, [200, 77], qfmt, LR_DT_BF16, 200)
+
+
+@pytest.mark.parametrize("qfmt", [LR_Q_INT8_TOKEN, LR_Q_INT4_G32])
+def test_decode_at_maximum_capacity(qfmt):
+    """A context of 2^24 tokens, the largest capacity a plan takes: byte
+    offsets past 4 GiB, hundreds of context splits and their merge.  Every K
+    row is the same row, so all weights are equal; the V rows alternate
+    between two rows, so the exact result is the oracle's for the two-token
+    context made of those rows."""
+    cap, r = 1 << 24, 128
+    rng = np.random.default_rng(300 + qfmt)
+    say(f"decode at capacity 2^24 qfmt={qfmt}")
+    s = DecodeSession(1, 1, 1, cap, qfmt, LR_DT_BF16, [[r]], [[r]], device=DEV)
+    assert lr_attn_workspace_bytes(s.plan, cap) > 0, "this shape must split the context"
+    krow = (rng.standard_normal(r) * 1.3).astype(np.float32)
+    vrows = (rng.standard_normal((2, r)) * 0.8).astype(np.float32)
+    kd, vd = torch.from_numpy(krow).to(DEV), torch.from_numpy(vrows).to(DEV)
+    chunk = 1 << 22
+    for c0 in range(0, cap, chunk):
+        ck = kd.view(1, 1, r).expand(1, chunk, r).contiguous()
+        cv = vd.repeat(chunk // 2, 1).view(1, chunk, r)
+        s.append(0, ck, cv, torch.tensor([c0], dtype=torch.int32, device=DEV))
+        del ck, cv
+    bk = (torch.from_numpy(rng.standard_normal((r, 128))) / 5).to(torch.bfloat16).to(DEV).contiguous()
+    bv = (torch.from_numpy(rng.standard_normal((r, 128))) / 5).to(torch.bfloat16).to(DEV).contiguous()
+    s.set_factors(0, bk, bv)
+    q = torch.from_numpy(rng.standard_normal((1, 1, 128)) * 2).to(torch.bfloat16).to(DEV).contiguous()
+    s.lengths.fill_(cap)
+    out = torch.full_like(q, float("nan"))
+    s.decode(0, q, out, cap)
+    torch.cuda.synchronize()
+    ref = oracle_many(qfmt, [(np.stack([krow, krow]), vrows, q.double().cpu().numpy()[0, 0],
+                              bk.double().cpu().numpy(), bv.double().cpu().numpy())],
+                      1 / math.sqrt(128))[0]
+    assert within(out.double().cpu().numpy()[0, 0], ref, TOL_BF16)
+    s.close()
