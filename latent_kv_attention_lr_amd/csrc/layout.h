@@ -39,6 +39,7 @@ struct HeadTab {
   uint32_t ranks[LR_MAX_HEADS];    // r_k | r_v << 16
   uint32_t loff[LR_MAX_HEADS];     // latent (== factor row) offset: K | V << 16
   uint32_t order[LR_MAX_HEADS];    // dispatch order: heads by bytes per token, largest first
+  uint32_t xorder[LR_MAX_HEADS];   // the same heads dealt to the 8 XCDs: entry 8r + x is XCD x's r-th head
 };
 
 }  // namespace lr

@@ -173,6 +173,13 @@ lr_status lr_attn_plan_create(const lr_attn_desc* d, lr_attn_plan** out) {
       return wa > wb;
     });
     for (int i = 0; i < H; ++i) L.tab.order[i] = static_cast<uint32_t>(order[i]);
+    // The same order dealt to the XCDs in a snake (0..7, then 7..0, ...): equal
+    // head counts per XCD and near-equal bytes (used when H % 8 == 0).
+    for (int i = 0; i < H; ++i) {
+      const int r = i / 8, x = i % 8;
+      const int src = (H % 8 == 0) ? r * 8 + ((r & 1) ? 7 - x : x) : i;
+      L.tab.xorder[i] = static_cast<uint32_t>(order[src]);
+    }
   }
   *out = p;
   return LR_OK;
