@@ -298,7 +298,7 @@ struct DecodeArgs {
   float* part;       // workspace partials [B*H][n_split][kPartStride] (split launches only)
   float qscale;      // softmax scale * log2(e)
   int32_t B, H, n_tiles, max_len, n_split, tps;
-  // 1: keep each head's work-groups on one XCD (see k_decode); 0: plain order
+  // 1: keep each head's work-groups on one XCD (see unit_of); 0: plain order
   int32_t xcd_groups;
   // fused append (ck == nullptr: none): quantise and write one token per
   // sequence at slot pos[b] before attending
@@ -308,6 +308,23 @@ struct DecodeArgs {
   const int32_t* pos;
   int32_t capacity, sum_rk, sum_rv;
 };
+
+// Sequence b and head h of work-group (unit) idx.  Work-group i runs on XCD
+// i % 8, each XCD with its own L2.  With xcd_groups, the B work-groups of one
+// head all land on one XCD (heads dealt to the XCDs by xorder), so each L2
+// fetches only its own heads' factors; otherwise (b, h) in dispatch order.
+__device__ __forceinline__ void unit_of(const DecodeArgs& a, const HeadTab& ht, int idx, int& b, int& h) {
+  int hp;
+  if (a.xcd_groups) {
+    const int x = idx & 7, k = idx >> 3;
+    hp = (k / a.B) * 8 + x;
+    b = k % a.B;
+  } else {
+    b = idx % a.B;
+    hp = idx / a.B;
+  }
+  h = uniform_i(int(a.xcd_groups ? ht.xorder[hp] : ht.order[hp]));
+}
 
 // Codes of one 64-token tile for this lane: NC chunks of 16 bytes.  The
 // runtime row width rb (bytes) may end inside the bucket.  Every load is
@@ -453,19 +470,8 @@ void k_decode(DecodeArgs a, HeadTab ht) {
   int idx = blockIdx.x;
   const int split = idx % a.n_split;
   idx /= a.n_split;
-  // Work-group i runs on XCD i % 8.  With xcd_groups, the B work-groups of
-  // one head all land on one XCD (heads dealt to XCDs by xorder), so each
-  // XCD's L2 fetches only its own heads' factors; otherwise (b, h) in order.
-  int b, hp;
-  if (a.xcd_groups) {
-    const int x = idx & 7, k = idx >> 3;
-    hp = (k / a.B) * 8 + x;
-    b = k % a.B;
-  } else {
-    b = idx % a.B;
-    hp = idx / a.B;
-  }
-  const int h = uniform_i(int(a.xcd_groups ? ht.xorder[hp] : ht.order[hp]));
+  int b, h;
+  unit_of(a, ht, idx, b, h);
   const uint32_t rr = uniform_i(int(ht.ranks[h])), lo = uniform_i(int(ht.loff[h]));
   const int rk = int(rr & 0xffffu), rv = int(rr >> 16);
   const int loff_k = int(lo & 0xffffu), loff_v = int(lo >> 16);
@@ -961,8 +967,8 @@ __global__ __launch_bounds__(NW * 64) void k_decode_explicit(DecodeArgs a, HeadT
   using E = Elem<uint16_t>;
 
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
-  const int b = int(blockIdx.x) % a.B;
-  const int h = uniform_i(int(ht.order[int(blockIdx.x) / a.B]));
+  int b, h;
+  unit_of(a, ht, int(blockIdx.x), b, h);
   const uint32_t rr = uniform_i(int(ht.ranks[h])), lo = uniform_i(int(ht.loff[h]));
   const int rk = int(rr & 0xffffu), rv = int(rr >> 16);
   const int loff_k = int(lo & 0xffffu), loff_v = int(lo >> 16);
@@ -1209,7 +1215,7 @@ int launch_decode(const lr_attn_plan& p, int32_t layer, const void* cache, const
   a.max_len = max_len;
   a.n_split = sp.n_split;
   a.tps = sp.tiles_per_split;
-  a.xcd_groups = (sp.n_split == 1 && p.desc.n_heads % 8 == 0 && !explicit_form) ? 1 : 0;
+  a.xcd_groups = (sp.n_split == 1 && p.desc.n_heads % 8 == 0) ? 1 : 0;
   a.wcache = app ? static_cast<uint8_t*>(app->cache) : nullptr;
   a.ck = app ? app->ck : nullptr;
   a.cv = app ? app->cv : nullptr;
