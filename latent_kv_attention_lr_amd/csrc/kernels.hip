@@ -9,13 +9,10 @@
 //                     context splits, apply B^V_h once.
 //   k_merge           merge the context-split partials of each (b, h) and
 //                     apply B^V_h (only when a launch splits the context).
-//   k_decode_explicit the same result by rebuilding every k_t and v_t from
-//                     B^K_h, B^V_h staged in LDS on the matrix cores (the
-//                     comparison form; the absorbed k_decode is the default).
 //
-// Cache tiles hold 64 tokens, one per lane of a wavefront (or one per lane
-// pair); every lane load is a 16-byte chunk and a wavefront load instruction
-// reads 1 KiB (or two 512-byte runs) of contiguous memory.
+// Cache tiles hold 64 tokens, one per lane of a wavefront; every lane load
+// is a 16-byte chunk and a wavefront load instruction reads 1 KiB of
+// contiguous memory.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -522,7 +519,7 @@ void k_decode(DecodeArgs a, HeadTab ht) {
   }
 
   // ---- loads first, in the order their data is needed: q and this
-  //      wavefront's B^K rows, its first step, this wavefront's B^V rows.  Row
+  //      wavefront's B^K rows, the first tile, this wavefront's B^V rows.  Row
   //      indices are clamped instead of tested so no load sits under a branch.
   const IOT* qrow = reinterpret_cast<const IOT*>(a.q) + size_t(unit) * kHeadDim;
   const float q0 = E::ld(qrow, 2 * lane), q1 = E::ld(qrow, 2 * lane + 1);
@@ -700,7 +697,7 @@ void k_decode(DecodeArgs a, HeadTab ht) {
     const int tn = t + NW;   // K regs are free now: the next step's K codes
     if constexpr (PF) load_k<QF>(kplane + step_tile(tn) * tbk, step_tok(tn), lm, hf, rk, rbk, cur);
     s = valid ? s : -__builtin_inff();
-    if (s > m + kTau) {  // rare after the first step: rescale the running sums
+    if (s > m + kTau) {  // rare after the first tile: rescale the running sums
       const float al = __builtin_amdgcn_exp2f(m - s);
       l *= al;
 #pragma unroll
