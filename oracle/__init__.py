@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.lro_attend_dequantised.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                              P, P, P, P, P, ctypes.c_double, P, P]
         L.lro_attend_dequantised.restype = ctypes.c_int
+        L.lro_latents.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P]
+        L.lro_latents.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -148,3 +150,16 @@ def attend_dequantised(ctk: np.ndarray, ctv: np.ndarray, q: np.ndarray, bk: np.n
     if rc != 0:
         raise ValueError("lro_attend_dequantised rejected its arguments")
     return (out, probs[:T]) if want_probs else out
+
+
+def latents(x: np.ndarray, a: np.ndarray) -> np.ndarray:
+    """Latent generation c = x A in fp64: x [T, E], A [E, N] (heads side by side)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    T, E = x.shape
+    E2, N = a.shape
+    assert E == E2
+    c = np.zeros((T, N), dtype=np.float64)
+    if lib().lro_latents(T, E, N, _ptr(x), _ptr(a), _ptr(c)) != 0:
+        raise ValueError("lro_latents rejected its arguments")
+    return c

@@ -6,9 +6,10 @@
 // shares no code, header, table or helper with the GPU library.
 //
 // It computes the plain definition, slowly and in the pages' order:
-//   * per head h, keys and values are kept only as rank-r latents c_t = x_t A_h
-//     (WSVD page, "Fine-grained per-head SVD": each head owns a small latent and
-//     its own factors, W_h ~ A_h B_h);
+//   * per head h, keys and values are kept only as rank-r latents c_t = x_t A_h,
+//     generated from the activations by lro_latents (WSVD page, "Fine-grained
+//     per-head SVD": each head owns a small latent and its own factors,
+//     W_h ~ A_h B_h);
 //   * the latents are stored at low precision with round-to-nearest
 //     quantisation (LASER page, "Hybrid SVD-quantisation ... RTN"; WSVD page,
 //     "Quantisation": W8A8 / W8A4 activations);
@@ -121,6 +122,25 @@ void lro_quant_int4_rows(const float* c, int n, int r, int8_t* q, uint16_t* scal
   for (int i = 0; i < n; ++i)
     lro_quant_int4(c + static_cast<size_t>(i) * r, r, q + static_cast<size_t>(i) * r,
                    scales + static_cast<size_t>(i) * ng);
+}
+
+// Latent generation (WSVD page, "Fine-grained per-head SVD": the cached
+// latent of token t for head h is c_t = x_t A_h, A_h the E x r down-projection
+// factor):  c[t][n] = sum_e x[t][e] * a[e][n]  for x [T][E], a [E][N], in fp64,
+// e ascending.  Heads side by side in a (head h's r_h columns after those of
+// heads 0 .. h-1) give every head's latent of a token at once.
+// Returns 0, or -1 on bad sizes.
+int lro_latents(int T, int E, int N, const double* x, const double* a, double* c) {
+  if (T < 0 || E < 1 || N < 1) return -1;
+  for (int t = 0; t < T; ++t) {
+    for (int n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int e = 0; e < E; ++e)
+        acc += x[static_cast<size_t>(t) * E + e] * a[static_cast<size_t>(e) * N + n];
+      c[static_cast<size_t>(t) * N + n] = acc;
+    }
+  }
+  return 0;
 }
 
 // Quantise and dequantise one row: out_i = scale * q_i in fp64 (exact).

@@ -178,6 +178,75 @@ def test_full_rank_unquantised_equals_dense_mha(T):
         assert np.max(np.abs(got - want)) <= 1e-12 * max(1.0, np.max(np.abs(want)))
 
 
+def test_full_rank_through_generated_latents_equals_dense_mha():
+    """The same pin with the latents made by the oracle's own latent generation
+    (c = x A from the activations) rather than by a matrix product here."""
+    rng = np.random.default_rng(23)
+    E, H, d, T = 16, 2, 8, 6
+    X = rng.standard_normal((T, E))
+    WK = rng.standard_normal((E, H * d)) / 4
+    WV = rng.standard_normal((E, H * d)) / 4
+    Q = rng.standard_normal((H, d))
+    scale = 1 / math.sqrt(d)
+    fac = {}
+    for name, W in (("k", WK), ("v", WV)):
+        As, Bs = [], []
+        for h in range(H):
+            U, S, Vt = np.linalg.svd(W[:, h * d:(h + 1) * d], full_matrices=False)
+            As.append(U * np.sqrt(S))
+            Bs.append(np.sqrt(S)[:, None] * Vt)
+        fac[name] = (np.concatenate(As, axis=1), Bs)   # heads side by side
+    CK = oracle.latents(X, fac["k"][0])
+    CV = oracle.latents(X, fac["v"][0])
+    for h in range(H):
+        got = oracle.attend_dequantised(CK[:, h * d:(h + 1) * d], CV[:, h * d:(h + 1) * d], Q[h],
+                                        fac["k"][1][h], fac["v"][1][h], scale)
+        want = _dense_mha(X, WK[:, h * d:(h + 1) * d], WV[:, h * d:(h + 1) * d], Q[h], scale)
+        assert np.max(np.abs(got - want)) <= 1e-12 * max(1.0, np.max(np.abs(want)))
+
+
+def test_latents_exact_on_small_integers():
+    """Integer inputs make every fp64 sum exact: the result must equal the
+    brute-force integer product (non-square shapes catch a transposed factor,
+    the full range of e catches a dropped term)."""
+    rng = np.random.default_rng(3)
+    for T, E, N in [(1, 1, 1), (3, 5, 2), (4, 7, 9), (2, 33, 17)]:
+        x = rng.integers(-9, 10, size=(T, E))
+        a = rng.integers(-9, 10, size=(E, N))
+        want = [[sum(int(x[t, e]) * int(a[e, n]) for e in range(E)) for n in range(N)]
+                for t in range(T)]
+        got = oracle.latents(x.astype(np.float64), a.astype(np.float64))
+        assert got.tolist() == [[float(v) for v in row] for row in want]
+
+
+def test_latents_one_hot_rows_pick_factor_rows():
+    """x_t = e_j gives c_t = row j of A, bit for bit."""
+    rng = np.random.default_rng(4)
+    E, N = 24, 40
+    a = rng.standard_normal((E, N))
+    idx = [0, 5, 23, 7]
+    x = np.zeros((len(idx), E))
+    x[np.arange(len(idx)), idx] = 1.0
+    assert np.array_equal(oracle.latents(x, a), a[idx])
+
+
+def test_latents_of_stacked_heads_are_per_head_latents():
+    """Heads side by side in A give each head's own latent in its columns, and
+    rows of x are independent tokens."""
+    rng = np.random.default_rng(6)
+    E, T = 32, 5
+    ranks = [8, 16, 24]
+    As = [rng.standard_normal((E, r)) for r in ranks]
+    x = rng.standard_normal((T, E))
+    full = oracle.latents(x, np.concatenate(As, axis=1))
+    o = 0
+    for A, r in zip(As, ranks):
+        assert np.array_equal(full[:, o:o + r], oracle.latents(x, A))
+        o += r
+    for t in range(T):
+        assert np.array_equal(full[t:t + 1], oracle.latents(x[t:t + 1], np.concatenate(As, axis=1)))
+
+
 def test_eckart_young_truncation_error():
     """Per-head factors from a rank-r truncated SVD of a random W_h (E x d):
     rows of A_r B_r are rebuilt through the oracle's value path (T = 1, latent =
