@@ -53,6 +53,11 @@ def parse():
     ap.add_argument("--explicit", action="store_true", help="time the explicit-reconstruction decode")
     ap.add_argument("--separate-append", action="store_true",
                     help="append and decode as two launches (default: one fused launch per step and layer)")
+    ap.add_argument("--with-projection", action="store_true",
+                    help="each step also generates the new token's latents from activations "
+                         "(lr_attn_project_latent) before the fused append + decode")
+    ap.add_argument("--no-projection-leg", action="store_true",
+                    help="skip the separate latent-generation measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=16,
                     help="extra untimed-in-value steps with the 256 MiB last-level cache flushed before each")
@@ -91,6 +96,14 @@ def append_bytes(w, rk, rv):
             sb = 4 if qf == 0 else 2 * ((r + 31) // 32)
             row += 4 * r + rb + sb
     return w.batch * row
+
+
+def projection_bytes(w, rk, rv, tokens):
+    """Algorithmic HBM bytes of one latent-generation launch: the bf16 factors
+    (E x sum r, K and V) once, the bf16 activations of the new tokens, and the
+    fp32 latents written."""
+    n = sum(rk) + sum(rv)
+    return 2 * w.embed * n + 2 * tokens * w.embed + 4 * tokens * n
 
 
 def cpu_baseline(run, n_units_target=128):
@@ -171,12 +184,35 @@ def main():
         del src, dst
 
     fused = not (args.explicit or args.separate_append)
+    if args.with_projection and not fused:
+        print("bench.py: --with-projection times the fused step only", file=sys.stderr)
+        sys.exit(2)
 
-    def one_layer(l, s, append=True):
+    # latent generation: per layer the factors as [sum r, E] bf16 (A transposed),
+    # per step and layer the new tokens' activations [B, E] bf16, and the fp32
+    # latent buffers the projection writes
+    proj = None
+    if args.with_projection or not (args.no_projection_leg or args.profile_steps):
+        wts = []
+        for l in range(L):
+            wts.append(tuple(lrgen.down_factors(w, l, kv, device=dev).t().contiguous().to(torch.bfloat16)
+                             for kv in (0, 1)))
+        xs = [[torch.cat([lrgen.activations(w, l, b, ctx + s, ctx + s + 1, device=dev)
+                          for b in range(w.batch)]).to(torch.bfloat16).contiguous()
+               for l in range(L)] for s in range(nsteps_inputs)]
+        lat = [(torch.empty(w.batch, sess.latent_elems(l, 0), dtype=torch.float32, device=dev),
+                torch.empty(w.batch, sess.latent_elems(l, 1), dtype=torch.float32, device=dev))
+               for l in range(L)]
+        proj = (wts, xs, lat)
+
+    def one_layer(l, s, append=True, project=args.with_projection):
         """Step s of layer l: append the step's token and attend (one fused launch), or
         with append=False (separate launches only) just the decode launch."""
         layers, pos, ln = per[s]
         ck, cv, q = layers[l]
+        if project:
+            wts, xs, lat = proj
+            ck, cv = sess.project(l, xs[s][l], wts[l][0], wts[l][1], ck=lat[l][0], cv=lat[l][1])
         if fused:
             sess.append_decode(l, ck.view(w.batch, -1), cv.view(w.batch, -1), pos, q, out,
                                ctx + s + 1, lengths=ln)
@@ -206,7 +242,7 @@ def main():
     def decodes_only():
         for s in range(steps):
             for l in range(L):
-                one_layer(l, s, append=False)
+                one_layer(l, s, append=False, project=False)
 
     def capture(fn):
         g = torch.cuda.CUDAGraph()
@@ -286,6 +322,69 @@ def main():
             "avg_launch_us": dec_avg_s * 1e6,
         },
     }
+
+    # ---- latent generation alone (outside the timed region): the projection
+    # of each step's new tokens, every layer, back to back in a graph between
+    # two HIP events (warm: the factors stay in the last-level cache), then
+    # one launch at a time after a flush (cold, as when the factors of other
+    # layers have been read in between).
+    if proj is not None and not args.profile_steps:
+        import latent_kv_attention_lr_amd as lrb
+        wts, xs, lat = proj
+        nrep = max(1, min(steps, 64))
+
+        def proj_launch(s, l):
+            # the current stream: torch's, or the capture stream inside capture()
+            rc = lrb._lib.lr_attn_project_latent(
+                sess.plan, l, xs[s][l].data_ptr(), w.batch, w.embed, wts[l][0].data_ptr(),
+                wts[l][1].data_ptr(), lat[l][0].data_ptr(), lat[l][1].data_ptr(),
+                torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"projection launch failed: {lrb.lr_attn_strerror(rc)}")
+
+        def projections():
+            for s in range(nrep):
+                for l in range(L):
+                    proj_launch(s, l)
+
+        projections()
+        run_proj = capture(projections).replay if use_graph else projections
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        run_proj()
+        e1.record()
+        torch.cuda.synchronize()
+        pw_s = e0.elapsed_time(e1) / (nrep * L) / 1e3
+        pbytes = sum(projection_bytes(w, rk_all[l], rv_all[l], w.batch) for l in range(L)) / L
+        flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)
+        cold = []
+        for s in range(min(16, nrep)):
+            for l in range(L):
+                flush.sum()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                proj_launch(s, l)
+                b.record()
+                cold.append((a, b))
+        torch.cuda.synchronize()
+        pc_s = sum(a.elapsed_time(b) for a, b in cold) / len(cold) / 1e3
+        del flush
+        result["latent_generation"] = {
+            "kernel": "k_project", "entry_point": "lr_attn_project_latent",
+            "bound": "hbm", "unit": "GB/s", "peak": PEAK_HBM_GBS,
+            "tokens_per_launch": w.batch, "embed": w.embed,
+            "bytes_per_launch": pbytes,
+            "avg_launch_us": pw_s * 1e6, "achieved": pbytes / pw_s / 1e9,
+            "frac": pbytes / pw_s / 1e9 / PEAK_HBM_GBS,
+            "cold_avg_launch_us": pc_s * 1e6, "cold_achieved": pbytes / pc_s / 1e9,
+            "cold_frac": pbytes / pc_s / 1e9 / PEAK_HBM_GBS,
+            "flops_per_launch": 2.0 * w.batch * w.embed * sum(sum(rk_all[l]) + sum(rv_all[l])
+                                                              for l in range(L)) / L,
+        }
+        if args.with_projection:
+            result["config"]["step"] = ("latent generation from activations, then append fused "
+                                        "into the decode launch")
 
     # ---- MALL-cold decode timing (outside the timed region): flush first.
     # The launch between the two events goes straight to the C ABI with its

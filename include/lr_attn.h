@@ -203,6 +203,48 @@ lr_status lr_attn_decode_explicit(const lr_attn_plan* plan, int32_t layer, const
                                   const void* bk, const void* bv, float softmax_scale, void* out,
                                   void* workspace, size_t ws_bytes, void* stream);
 
+/* Latent generation for every head of layer `layer` at once (WSVD page,
+ * "Fine-grained per-head SVD": the cached latent of a token is c_t = x_t A_h;
+ * LASER page, "System implementation": the latent activations are generated
+ * in a GPU kernel ahead of the fused quantisation):
+ *     ck[t][:] = x[t] A^K,   cv[t][:] = x[t] A^V,   t < n_tokens,
+ * where A^K (E x latent_elems(0)) is A^K_h of every head side by side, head
+ * h's r_h columns at its latent_offset_k, and A^V likewise.  The factors are
+ * passed TRANSPOSED, one row of `embed` values per latent dimension (the
+ * layout of a linear layer's weight).  The products run on the matrix cores:
+ * bf16 inputs, exact products, fp32 sums in an order that is the same on
+ * every call (results are deterministic, not bitwise equal to any other
+ * summation order).  The plan's io_dtype does not apply.
+ *   x         device bf16 [n_tokens][embed], 16-aligned
+ *   n_tokens  0 (no-op) or more; rows of x are tokens in any order
+ *   embed     E: a multiple of 32, >= 32
+ *   wk, wv    device bf16 [latent_elems(kv)][embed], 16-aligned
+ *   ck, cv    device fp32 [n_tokens][latent_elems(kv)], 16-aligned, written
+ * Errors: LR_EINVAL (null or misaligned pointer, bad embed, n_tokens < 0),
+ * LR_ERANGE (layer), LR_EHIP. */
+lr_status lr_attn_project_latent(const lr_attn_plan* plan, int32_t layer, const void* x,
+                                 int32_t n_tokens, int32_t embed, const void* wk, const void* wv,
+                                 float* ck, float* cv, void* stream);
+
+/* Workspace bytes of lr_attn_project_append for any layer with this n_new
+ * (the fp32 latents of batch * n_new tokens, K and V); 0 on bad arguments. */
+size_t lr_attn_project_workspace_bytes(const lr_attn_plan* plan, int32_t n_new);
+
+/* lr_attn_project_latent followed by lr_attn_append_latent, on the same
+ * stream: the new tokens' latents are generated from x into the workspace,
+ * then quantised and written at slots pos[b] .. pos[b] + n_new - 1.  The
+ * cache bytes are identical to those two calls.
+ *   x          device bf16 [batch][n_new][embed]
+ *   embed, wk, wv  as for lr_attn_project_latent
+ *   pos, n_new as for lr_attn_append_latent (n_new = 0 is a no-op)
+ *   workspace  device, >= lr_attn_project_workspace_bytes(n_new) bytes,
+ *              256-aligned, scratch; concurrent calls must not share one
+ * Errors: LR_EINVAL, LR_ERANGE, LR_EWORKSPACE, LR_EHIP. */
+lr_status lr_attn_project_append(const lr_attn_plan* plan, int32_t layer, void* cache,
+                                 const void* x, int32_t embed, const void* wk, const void* wv,
+                                 const int32_t* pos, int32_t n_new, void* workspace,
+                                 size_t ws_bytes, void* stream);
+
 /* Measurement aid, not part of the decode path: streams bytes / 16 16-byte
  * words from device memory src (16-byte aligned, bytes >= 16; a trailing
  * partial word is not read) with a plain grid-stride read kernel, the

@@ -90,6 +90,9 @@ def _load() -> ctypes.CDLL:
         "lr_attn_decode_explicit": (ctypes.c_int, [P, I32, P, P, I32, P, P, P, ctypes.c_float, P, P, SZ, P]),
         "lr_attn_append_decode": (ctypes.c_int, [P, I32, P, P, P, P, P, I32, P, P, P, ctypes.c_float,
                                                  P, P, SZ, P]),
+        "lr_attn_project_latent": (ctypes.c_int, [P, I32, P, I32, I32, P, P, P, P, P]),
+        "lr_attn_project_workspace_bytes": (SZ, [P, I32]),
+        "lr_attn_project_append": (ctypes.c_int, [P, I32, P, P, I32, P, P, P, I32, P, SZ, P]),
         "lr_attn_probe_read": (ctypes.c_int, [P, SZ, P, P]),
         "lr_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "lr_attn_last_hip_error": (I32, []),
@@ -203,6 +206,27 @@ def lr_attn_decode_explicit(plan: int, layer: int, cache, length, max_len: int, 
                                         _ptr(bk), _ptr(bv), softmax_scale, _ptr(out),
                                         _ptr(workspace), ws_bytes, _stream(stream)),
            "lr_attn_decode_explicit")
+
+
+def lr_attn_project_latent(plan: int, layer: int, x, n_tokens: int, embed: int, wk, wv, ck, cv,
+                           stream=None) -> None:
+    """ck/cv [n_tokens, latent_elems] (fp32) = x [n_tokens, embed] (bf16) times the
+    factors wk/wv given as [latent_elems, embed] bf16 (A transposed)."""
+    _check(_lib.lr_attn_project_latent(plan, layer, _ptr(x), n_tokens, embed, _ptr(wk), _ptr(wv),
+                                       _ptr(ck), _ptr(cv), _stream(stream)),
+           "lr_attn_project_latent")
+
+
+def lr_attn_project_workspace_bytes(plan: int, n_new: int) -> int:
+    return int(_lib.lr_attn_project_workspace_bytes(plan, n_new))
+
+
+def lr_attn_project_append(plan: int, layer: int, cache, x, embed: int, wk, wv, pos, n_new: int,
+                           workspace, ws_bytes: int, stream=None) -> None:
+    """lr_attn_project_latent of x [batch, n_new, embed] then lr_attn_append_latent."""
+    _check(_lib.lr_attn_project_append(plan, layer, _ptr(cache), _ptr(x), embed, _ptr(wk), _ptr(wv),
+                                       _ptr(pos), n_new, _ptr(workspace), ws_bytes, _stream(stream)),
+           "lr_attn_project_append")
 
 
 def lr_attn_probe_read(src, nbytes: int, sink, stream=None) -> None:

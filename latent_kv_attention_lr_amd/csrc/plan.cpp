@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdint>
 #include <cstring>
 #include <new>
 #include <numeric>
@@ -225,6 +226,68 @@ lr_status lr_attn_append_latent(const lr_attn_plan* p, int32_t layer, void* cach
   if (!aligned(cache, 256) || !aligned(ck, 16) || !aligned(cv, 16) || !aligned(pos, 4))
     return LR_EINVAL;
   if (n_new == 0) return LR_OK;
+  return hip_status(lr::launch_append(*p, layer, cache, ck, cv, pos, n_new, stream));
+}
+
+namespace {
+
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Bytes of the fp32 latents of n tokens of one layer, K then V, each 256-aligned.
+size_t latent_ws_bytes(const lr_attn_plan::Layer& L, size_t n) {
+  return round256(n * L.sum_rk * sizeof(float)) + round256(n * L.sum_rv * sizeof(float));
+}
+
+lr_status check_project(const lr_attn_plan* p, int32_t layer, const void* x, int32_t embed,
+                        const void* wk, const void* wv) {
+  if (!p) return LR_EINVAL;
+  if (layer < 0 || layer >= p->desc.n_layers) return LR_ERANGE;
+  if (embed < 32 || embed % 32 != 0) return LR_EINVAL;
+  if (!x || !wk || !wv) return LR_EINVAL;
+  if (!aligned(x, 16) || !aligned(wk, 16) || !aligned(wv, 16)) return LR_EINVAL;
+  return LR_OK;
+}
+
+}  // namespace
+
+lr_status lr_attn_project_latent(const lr_attn_plan* p, int32_t layer, const void* x,
+                                 int32_t n_tokens, int32_t embed, const void* wk, const void* wv,
+                                 float* ck, float* cv, void* stream) {
+  const lr_status st = check_project(p, layer, x, embed, wk, wv);
+  if (st != LR_OK) return st;
+  if (n_tokens < 0 || !ck || !cv || !aligned(ck, 16) || !aligned(cv, 16)) return LR_EINVAL;
+  if (n_tokens == 0) return LR_OK;
+  return hip_status(lr::launch_project(*p, layer, x, n_tokens, embed, wk, wv, ck, cv, stream));
+}
+
+size_t lr_attn_project_workspace_bytes(const lr_attn_plan* p, int32_t n_new) {
+  if (!p || n_new < 1 || n_new > p->desc.capacity) return 0;
+  size_t best = 0;
+  const size_t n = static_cast<size_t>(p->desc.batch) * static_cast<size_t>(n_new);
+  for (const auto& L : p->layers) best = std::max(best, latent_ws_bytes(L, n));
+  return best;
+}
+
+lr_status lr_attn_project_append(const lr_attn_plan* p, int32_t layer, void* cache, const void* x,
+                                 int32_t embed, const void* wk, const void* wv,
+                                 const int32_t* pos, int32_t n_new, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  const lr_status st = check_project(p, layer, x, embed, wk, wv);
+  if (st != LR_OK) return st;
+  if (n_new < 0) return LR_EINVAL;
+  if (n_new > p->desc.capacity) return LR_ERANGE;
+  if (!cache || !pos || !aligned(cache, 256) || !aligned(pos, 4)) return LR_EINVAL;
+  if (n_new == 0) return LR_OK;
+  const auto& L = p->layers[layer];
+  const size_t n = static_cast<size_t>(p->desc.batch) * static_cast<size_t>(n_new);
+  if (n > static_cast<size_t>(INT32_MAX)) return LR_ERANGE;
+  if (!ws || ws_bytes < latent_ws_bytes(L, n)) return LR_EWORKSPACE;
+  if (!aligned(ws, 256)) return LR_EINVAL;
+  float* ck = static_cast<float*>(ws);
+  float* cv = reinterpret_cast<float*>(static_cast<char*>(ws) + round256(n * L.sum_rk * sizeof(float)));
+  const lr_status s1 = hip_status(lr::launch_project(*p, layer, x, static_cast<int32_t>(n), embed,
+                                                     wk, wv, ck, cv, stream));
+  if (s1 != LR_OK) return s1;
   return hip_status(lr::launch_append(*p, layer, cache, ck, cv, pos, n_new, stream));
 }
 

@@ -62,6 +62,11 @@ int launch_decode(const lr_attn_plan& p, int32_t layer, const void* cache, const
                   int32_t max_len, const void* q, const void* bk, const void* bv, float scale,
                   void* out, void* workspace, void* stream, bool explicit_form,
                   const AppendInputs* app = nullptr);
+// project.hip: fp32 latents ck [n_tokens][sum_rk] = x W^K^T and cv likewise,
+// x bf16 [n_tokens][embed], W bf16 [sum_r][embed].  n_tokens >= 1, embed % 32 == 0.
+int launch_project(const lr_attn_plan& p, int32_t layer, const void* x, int32_t n_tokens,
+                   int32_t embed, const void* wk, const void* wv, float* ck, float* cv,
+                   void* stream);
 // probe.hip: stream bytes / 16 16-byte words from src (read only).
 int launch_probe_read(const void* src, size_t bytes, void* sink, void* stream);
 

@@ -16,7 +16,8 @@ from . import (LR_DT_BF16, LR_DT_F32, LR_HEAD_DIM, lr_attn_append_decode, lr_att
                lr_attn_cache_bytes,
                lr_attn_decode, lr_attn_decode_explicit, lr_attn_factor_elems,
                lr_attn_head_layout_get, lr_attn_latent_elems, lr_attn_plan_create,
-               lr_attn_plan_destroy, lr_attn_workspace_bytes)
+               lr_attn_plan_destroy, lr_attn_project_append, lr_attn_project_latent,
+               lr_attn_project_workspace_bytes, lr_attn_workspace_bytes)
 
 
 class DecodeSession:
@@ -41,6 +42,7 @@ class DecodeSession:
         self.ws_bytes = lr_attn_workspace_bytes(self.plan, capacity)
         self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
         self.lengths = torch.zeros(batch, dtype=torch.int32, device=self.device)
+        self._proj_ws: Optional[torch.Tensor] = None   # latents of project_append, grown on demand
 
     def close(self) -> None:
         plan = getattr(self, "plan", None)
@@ -126,3 +128,48 @@ class DecodeSession:
                               self.lengths if lengths is None else lengths, max_len, q,
                               self.bk[layer], self.bv[layer], scale, out, self.workspace,
                               self.workspace.numel(), stream)
+
+    # -- latent generation ---------------------------------------------------
+    def _check_projection(self, layer: int, x: torch.Tensor, wk: torch.Tensor, wv: torch.Tensor) -> int:
+        E = x.shape[-1]
+        if x.dtype != torch.bfloat16 or wk.dtype != torch.bfloat16 or wv.dtype != torch.bfloat16:
+            raise ValueError("x and the down-projection factors must be bf16")
+        if wk.shape != (self.latent_elems(layer, 0), E) or wv.shape != (self.latent_elems(layer, 1), E):
+            raise ValueError("factors must be [latent_elems, embed] (A transposed)")
+        if not all(t.is_contiguous() and t.device == self.device for t in (x, wk, wv)):
+            raise ValueError("x and factors must be contiguous on the session device")
+        return E
+
+    def project(self, layer: int, x: torch.Tensor, wk: torch.Tensor, wv: torch.Tensor,
+                ck: Optional[torch.Tensor] = None, cv: Optional[torch.Tensor] = None, stream=None):
+        """fp32 latents of x [..., embed]: (x A^K, x A^V) with the factors given as
+        wk/wv [latent_elems, embed]; returns (ck, cv) shaped [..., latent_elems]."""
+        E = self._check_projection(layer, x, wk, wv)
+        lead = tuple(x.shape[:-1])
+        n = x.numel() // E
+        if ck is None:
+            ck = torch.empty(lead + (self.latent_elems(layer, 0),), dtype=torch.float32, device=self.device)
+        if cv is None:
+            cv = torch.empty(lead + (self.latent_elems(layer, 1),), dtype=torch.float32, device=self.device)
+        if ck.numel() != n * self.latent_elems(layer, 0) or cv.numel() != n * self.latent_elems(layer, 1) \
+                or ck.dtype != torch.float32 or cv.dtype != torch.float32 \
+                or not (ck.is_contiguous() and cv.is_contiguous()):
+            raise ValueError("ck/cv must be contiguous fp32 with one latent vector per row of x")
+        lr_attn_project_latent(self.plan, layer, x, n, E, wk, wv, ck, cv, stream)
+        return ck, cv
+
+    def project_append(self, layer: int, x: torch.Tensor, wk: torch.Tensor, wv: torch.Tensor,
+                       pos: torch.Tensor, stream=None) -> None:
+        """Generate the latents of x [B, n_new, embed] and append them at pos[b].."""
+        E = self._check_projection(layer, x, wk, wv)
+        if x.dim() != 3 or x.shape[0] != self.batch:
+            raise ValueError("x must be [batch, n_new, embed]")
+        if not pos.is_contiguous():
+            raise ValueError("pos must be contiguous")
+        n_new = x.shape[1]
+        need = lr_attn_project_workspace_bytes(self.plan, n_new) if n_new > 0 else 0
+        if need > 0 and (self._proj_ws is None or self._proj_ws.numel() < need):
+            self._proj_ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        ws = self._proj_ws
+        lr_attn_project_append(self.plan, layer, self.caches[layer], x, E, wk, wv, pos, n_new,
+                               ws, 0 if ws is None else ws.numel(), stream)

@@ -218,6 +218,74 @@ def test_append_decode_argument_errors_before_launch():
         lr.lr_attn_plan_destroy(p)
 
 
+def _project(p, **kw):
+    a = dict(layer=0, x=FAKE, n=16, embed=4096, wk=FAKE, wv=FAKE, ck=FAKE, cv=FAKE)
+    a.update(kw)
+    return lr._lib.lr_attn_project_latent(p, a["layer"], a["x"], a["n"], a["embed"], a["wk"],
+                                          a["wv"], a["ck"], a["cv"], None)
+
+
+def _project_append(p, **kw):
+    a = dict(layer=0, cache=FAKE, x=FAKE, embed=4096, wk=FAKE, wv=FAKE, pos=FAKE, n_new=1,
+             ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return lr._lib.lr_attn_project_append(p, a["layer"], a["cache"], a["x"], a["embed"], a["wk"],
+                                          a["wv"], a["pos"], a["n_new"], a["ws"], a["ws_bytes"],
+                                          None)
+
+
+def test_project_argument_errors_before_launch():
+    p = _plan()
+    try:
+        assert _project(None) == lr.LR_EINVAL
+        assert _project(p, layer=1) == lr.LR_ERANGE
+        for name in ("x", "wk", "wv", "ck", "cv"):
+            assert _project(p, **{name: None}) == lr.LR_EINVAL, name
+            assert _project(p, **{name: FAKE + 8}) == lr.LR_EINVAL, name   # 16-aligned
+        for e in (0, 16, 48, 4095, -32):
+            assert _project(p, embed=e) == lr.LR_EINVAL, e                  # multiple of 32, >= 32
+        assert _project(p, n=-1) == lr.LR_EINVAL
+        assert _project(p, n=0) == lr.LR_OK                                 # no-op, no launch
+    finally:
+        lr.lr_attn_plan_destroy(p)
+
+
+def test_project_workspace_bytes():
+    p = _plan()
+    try:
+        # rank_k sums to 184, rank_v to 208; batch 2
+        for n_new in (1, 3, 300):
+            n = 2 * n_new
+            want = -(-n * 184 * 4 // 256) * 256 + -(-n * 208 * 4 // 256) * 256
+            assert lr.lr_attn_project_workspace_bytes(p, n_new) == want
+        assert lr.lr_attn_project_workspace_bytes(p, 0) == 0
+        assert lr.lr_attn_project_workspace_bytes(p, 301) == 0
+        assert lr.lr_attn_project_workspace_bytes(None, 1) == 0
+    finally:
+        lr.lr_attn_plan_destroy(p)
+
+
+def test_project_append_argument_errors_before_launch():
+    p = _plan()
+    try:
+        assert _project_append(None) == lr.LR_EINVAL
+        assert _project_append(p, layer=2) == lr.LR_ERANGE
+        for name in ("cache", "x", "wk", "wv", "pos"):
+            assert _project_append(p, **{name: None}) == lr.LR_EINVAL, name
+        assert _project_append(p, cache=FAKE + 16) == lr.LR_EINVAL
+        assert _project_append(p, pos=FAKE + 2) == lr.LR_EINVAL
+        assert _project_append(p, embed=40) == lr.LR_EINVAL
+        assert _project_append(p, n_new=-1) == lr.LR_EINVAL
+        assert _project_append(p, n_new=301) == lr.LR_ERANGE
+        need = lr.lr_attn_project_workspace_bytes(p, 5)
+        assert _project_append(p, n_new=5, ws=None) == lr.LR_EWORKSPACE
+        assert _project_append(p, n_new=5, ws_bytes=need - 1) == lr.LR_EWORKSPACE
+        assert _project_append(p, n_new=5, ws=FAKE + 16) == lr.LR_EINVAL   # 256-aligned
+        assert _project_append(p, n_new=0) == lr.LR_OK                     # no-op, no launch
+    finally:
+        lr.lr_attn_plan_destroy(p)
+
+
 def test_explicit_form_rejects_fp32_io_before_launch():
     p = _plan(io_dtype=lr.LR_DT_F32)
     try:

@@ -1,0 +1,264 @@
+"""GPU parity of latent generation (c = x A on the matrix cores) and of the
+generate-then-append entry point, through the C ABI, against the CPU oracle.
+
+* inputs whose every fp32 sum is exact in any order (small integers, one-hot
+  rows): bit-exact latents;
+* random bf16 inputs of the workloads' shapes and distributions (outlier
+  channels included): every latent within the worst-case fp32 summation bound
+  2 (E-1) u sum_e |x_e a_e| (u = 2^-24; the factor 2 also covers additions
+  that truncate), and an RMS error within 8 sqrt(E) u of the RMS latent, which
+  a dropped or doubled term exceeds by orders of magnitude;
+* lr_attn_project_append writes exactly the bytes of project + append; its
+  codes are valid roundings of the oracle's latents; decode over a cache
+  built from activations matches the oracle's whole chain within the decode
+  tolerance.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import lrgen
+import oracle
+from latent_kv_attention_lr_amd import LR_DT_BF16, LR_Q_INT4_G32, LR_Q_INT8_TOKEN
+from latent_kv_attention_lr_amd.session import DecodeSession
+from gpu_util import TOL_BF16, read_codes, within
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+U32 = 2.0 ** -24
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def _session(ranks_k, ranks_v, qfmt=LR_Q_INT8_TOKEN, batch=1, cap=64):
+    return DecodeSession(1, batch, len(ranks_k), cap, qfmt, LR_DT_BF16, [list(ranks_k)],
+                         [list(ranks_v)], device=DEV)
+
+
+def _factors(E, ranks, key, std):
+    """Down-projection factor A [E, sum r] ~ N(0, std^2), rounded to bf16 (fp32 array)."""
+    n = E * sum(ranks)
+    a = lrgen.normal(key, 0, n, std).view(E, sum(ranks)).to(torch.bfloat16).float()
+    return a
+
+
+def _gpu_project(s, x_bf, ak, av):
+    """Run lr_attn_project_latent; factors are passed transposed ([N, E])."""
+    wk = ak.t().contiguous().to(torch.bfloat16).to(DEV)
+    wv = av.t().contiguous().to(torch.bfloat16).to(DEV)
+    ck, cv = s.project(0, x_bf.to(DEV).contiguous(), wk, wv)
+    torch.cuda.synchronize()
+    return ck.cpu().numpy(), cv.cpu().numpy(), wk, wv
+
+
+def _check_bound(got, x, a, rows=None):
+    """Worst-case and RMS rounding checks of fp32 latents against the oracle."""
+    x64 = x.double().numpy() if rows is None else x.double().numpy()[rows]
+    a64 = a.double().numpy()
+    E = x64.shape[1]
+    ref = oracle.latents(x64, a64)
+    mag = oracle.latents(np.abs(x64), np.abs(a64))
+    g = got if rows is None else got[rows]
+    err = np.abs(g.astype(np.float64) - ref)
+    bound = 2.0 * (E - 1) * U32 * mag * 1.01 + U32 * np.abs(ref)
+    assert np.all(err <= bound), float(np.max(err / np.maximum(bound, 1e-300)))
+    rms_ref = math.sqrt(float(np.mean(ref ** 2)))
+    rms_err = math.sqrt(float(np.mean(err ** 2)))
+    assert rms_err <= 8.0 * math.sqrt(E) * U32 * rms_ref, (rms_err, rms_ref)
+    return ref
+
+
+@pytest.mark.parametrize("E,T", [(32, 1), (96, 5), (1024, 16), (1024, 17), (1024, 64), (1024, 65),
+                                 (1024, 130), (4096, 3)])
+def test_project_integer_inputs_bitexact(E, T):
+    """Small-integer x and A (exact in bf16) keep every partial sum an integer
+    below 2^24, so any summation order gives the exact product."""
+    ranks_k, ranks_v = [8, 32, 24], [16, 40, 8]
+    say(f"project integers E={E} T={T}")
+    rng = np.random.default_rng(E * 1000 + T)
+    s = _session(ranks_k, ranks_v)
+    x = torch.from_numpy(rng.integers(-3, 4, (T, E)).astype(np.float32))
+    ak = torch.from_numpy(rng.integers(-3, 4, (E, sum(ranks_k))).astype(np.float32))
+    av = torch.from_numpy(rng.integers(-3, 4, (E, sum(ranks_v))).astype(np.float32))
+    ck, cv, _, _ = _gpu_project(s, x.to(torch.bfloat16), ak, av)
+    assert np.array_equal(ck, oracle.latents(x.double().numpy(), ak.double().numpy()).astype(np.float32))
+    assert np.array_equal(cv, oracle.latents(x.double().numpy(), av.double().numpy()).astype(np.float32))
+
+
+def test_project_one_hot_rows_pick_factor_rows():
+    """x_t = e_j gives row j of A exactly: every token and every latent lands
+    at its own place (tokens across column tiles, rows across row tiles)."""
+    E, ranks_k, ranks_v = 256, [32, 8, 56, 16, 8], [8, 8, 8, 8, 40]
+    s = _session(ranks_k, ranks_v)
+    idx = [(7 * t + 3) % E for t in range(70)]
+    x = torch.zeros(len(idx), E)
+    x[torch.arange(len(idx)), torch.tensor(idx)] = 1.0
+    ak = _factors(E, ranks_k, lrgen.stream_key(9, 1), 1.0)
+    av = _factors(E, ranks_v, lrgen.stream_key(9, 2), 1.0)
+    ck, cv, _, _ = _gpu_project(s, x.to(torch.bfloat16), ak, av)
+    assert np.array_equal(ck, ak.numpy()[idx])
+    assert np.array_equal(cv, av.numpy()[idx])
+
+
+def _workload_inputs(idx, T, layer=0):
+    w = lrgen.workload(idx)
+    x = torch.cat([lrgen.activations(w, layer, b, w.context, w.context + 1) for b in range(T)])
+    ak = lrgen.down_factors(w, layer, 0).to(torch.bfloat16).float()
+    av = lrgen.down_factors(w, layer, 1).to(torch.bfloat16).float()
+    return w, x.to(torch.bfloat16), ak, av
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+def test_project_workload_shapes_within_rounding_bound(idx):
+    """Each workload's layer (E, ranks) with one new token per sequence, as in
+    a decode step (batch tokens; workload 2 has its 20x outlier channels);
+    oracle on every token for the small batches, on 8 sampled tokens else."""
+    w = lrgen.workload(idx)
+    say(f"project workload {idx} E={w.embed} T={w.batch}")
+    w, x, ak, av = _workload_inputs(idx, w.batch)
+    s = _session(w.ranks_k[0], w.ranks_v[0], w.qfmt, batch=w.batch)
+    ck, cv, _, _ = _gpu_project(s, x, ak, av)
+    rows = None if w.batch <= 16 else np.random.default_rng(idx).choice(w.batch, 8, replace=False)
+    _check_bound(ck, x.float(), ak, rows)
+    _check_bound(cv, x.float(), av, rows)
+
+
+def test_project_many_tokens_and_is_deterministic():
+    """A prefill-sized call (several token blocks, a ragged last one) and
+    bitwise-identical results on a second call."""
+    E, ranks_k, ranks_v, T = 1024, [32] * 8, [24, 40] * 4, 1000
+    s = _session(ranks_k, ranks_v)
+    x = lrgen.normal(lrgen.stream_key(12, 0), 0, T * E, 1.0).view(T, E).to(torch.bfloat16)
+    ak = _factors(E, ranks_k, lrgen.stream_key(12, 1), 1 / math.sqrt(E))
+    av = _factors(E, ranks_v, lrgen.stream_key(12, 2), 1 / math.sqrt(E))
+    ck, cv, wk, wv = _gpu_project(s, x, ak, av)
+    rows = np.random.default_rng(0).choice(T, 24, replace=False)
+    rows = np.concatenate([rows, [0, 63, 64, 999]])
+    _check_bound(ck, x.float(), ak, rows)
+    _check_bound(cv, x.float(), av, rows)
+    ck2, cv2 = s.project(0, x.to(DEV), wk, wv)
+    torch.cuda.synchronize()
+    assert np.array_equal(ck, ck2.cpu().numpy()) and np.array_equal(cv, cv2.cpu().numpy())
+
+
+@pytest.mark.parametrize("qfmt", [LR_Q_INT8_TOKEN, LR_Q_INT4_G32])
+def test_project_append_equals_project_then_append(qfmt):
+    """The combined entry point writes exactly the bytes of the two calls,
+    for one and for several new tokens per sequence."""
+    E, ranks_k, ranks_v, B = 512, [8, 64, 32, 96], [40, 16, 128, 8], 3
+    ak = _factors(E, ranks_k, lrgen.stream_key(13, 1), 1 / math.sqrt(E))
+    av = _factors(E, ranks_v, lrgen.stream_key(13, 2), 1 / math.sqrt(E))
+    wk = ak.t().contiguous().to(torch.bfloat16).to(DEV)
+    wv = av.t().contiguous().to(torch.bfloat16).to(DEV)
+    for n_new in (1, 5, 70):
+        say(f"project_append qfmt={qfmt} n_new={n_new}")
+        x = lrgen.normal(lrgen.stream_key(13, n_new), 0, B * n_new * E, 1.0).view(B, n_new, E)
+        x = x.to(torch.bfloat16).to(DEV)
+        pos = torch.tensor([0, 3, 60][:B], dtype=torch.int32, device=DEV)
+        a = _session(ranks_k, ranks_v, qfmt, batch=B, cap=140)
+        b = _session(ranks_k, ranks_v, qfmt, batch=B, cap=140)
+        a.project_append(0, x, wk, wv, pos)
+        ck, cv = b.project(0, x, wk, wv)
+        b.append(0, ck, cv, pos)
+        torch.cuda.synchronize()
+        assert torch.equal(a.caches[0], b.caches[0])
+
+
+@pytest.mark.parametrize("qfmt", [LR_Q_INT8_TOKEN, LR_Q_INT4_G32])
+def test_project_append_codes_are_roundings_of_oracle_latents(qfmt):
+    """Codes and scales written from activations, against the oracle's
+    latents c_ref: with e the latent error bound, each scale is within
+    max(e)/L (plus its own rounding) of the oracle's, and each code within
+    1/2 + e/s (plus the division's rounding) of clip(c_ref / s, -L, L), L =
+    127 or 7."""
+    w = lrgen.workload(2 if qfmt == LR_Q_INT4_G32 else 1)
+    B = 16
+    w, x, ak, av = _workload_inputs(w.index, B)
+    ranks_k, ranks_v = w.ranks_k[0], w.ranks_v[0]
+    s = _session(ranks_k, ranks_v, qfmt, batch=B, cap=64)
+    wk = ak.t().contiguous().to(torch.bfloat16).to(DEV)
+    wv = av.t().contiguous().to(torch.bfloat16).to(DEV)
+    pos = torch.full((B,), 5, dtype=torch.int32, device=DEV)
+    s.project_append(0, x.view(B, 1, -1).to(DEV), wk, wv, pos)
+    torch.cuda.synchronize()
+    cache = s.caches[0].cpu().numpy()
+    E = w.embed
+    x64 = x.double().numpy()
+    lim = 127 if qfmt == LR_Q_INT8_TOKEN else 7
+    srel = 2 * U32 if qfmt == LR_Q_INT8_TOKEN else 2.0 ** -10   # fp32 / fp16 scale rounding
+    for kv, a, offs, ranks in (("k", ak, lrgen.head_offsets(ranks_k), ranks_k),
+                               ("v", av, lrgen.head_offsets(ranks_v), ranks_v)):
+        ref = oracle.latents(x64, a.double().numpy())
+        mag = oracle.latents(np.abs(x64), np.abs(a.double().numpy()))
+        bound = 2.0 * (E - 1) * U32 * mag * 1.01 + U32 * np.abs(ref)
+        for h in range(0, len(ranks), 5):
+            o, r = offs[h], ranks[h]
+            hl = s.head_layout(0, h)
+            for b in range(B):
+                q, sc = read_codes(cache, hl, qfmt, b, [5], kv)
+                c = ref[b, o:o + r]
+                e = bound[b, o:o + r]
+                if qfmt == LR_Q_INT8_TOKEN:
+                    scale = np.full(r, float(sc.view(np.float32)[0]))
+                    groups = [(0, r)]
+                else:
+                    g = np.array([oracle.f16_bits_to_f32(int(v)) for v in sc[0]], np.float64)
+                    scale = np.repeat(g, 32)[:r]
+                    groups = [(lo, min(r, lo + 32)) for lo in range(0, r, 32)]
+                for lo, hi in groups:
+                    s_ref = float(np.max(np.abs(c[lo:hi]))) / lim
+                    tol = float(np.max(e[lo:hi])) / lim + srel * max(s_ref, scale[lo])
+                    assert abs(scale[lo] - s_ref) <= tol, (kv, h, b, lo, scale[lo], s_ref)
+                want = np.clip(c / scale, -lim, lim)
+                slack = e / scale + 2 * lim * U32
+                assert np.all(np.abs(q[0].astype(np.float64) - want) <= 0.5 + slack), (kv, h, b)
+
+
+def test_decode_over_generated_latents_matches_oracle_chain():
+    """Cache built by project_append from activations (prefill in chunks, then
+    decode steps generating the new token's latents and attending with the
+    fused append): outputs match the oracle's chain x -> latents -> quantise ->
+    attend within the decode tolerance."""
+    w = lrgen.workload(0)
+    E, H, B, ctx, steps = w.embed, w.n_heads, 2, 100, 3
+    rk, rv = w.ranks_k[0], w.ranks_v[0]
+    s = DecodeSession(1, B, H, ctx + steps, w.qfmt, LR_DT_BF16, [rk], [rv], device=DEV)
+    ak = lrgen.down_factors(w, 0, 0).to(torch.bfloat16).float()
+    av = lrgen.down_factors(w, 0, 1).to(torch.bfloat16).float()
+    bk = lrgen.up_factors(w, 0, 0).to(DEV).contiguous()
+    bv = lrgen.up_factors(w, 0, 1).to(DEV).contiguous()
+    s.set_factors(0, bk, bv)
+    wk = ak.t().contiguous().to(torch.bfloat16).to(DEV)
+    wv = av.t().contiguous().to(torch.bfloat16).to(DEV)
+    xs = torch.stack([lrgen.activations(w, 0, b, 0, ctx + steps) for b in range(B)]).to(torch.bfloat16)
+    for t0 in range(0, ctx, 40):
+        t1 = min(ctx, t0 + 40)
+        pos = torch.full((B,), t0, dtype=torch.int32, device=DEV)
+        s.project_append(0, xs[:, t0:t1].contiguous().to(DEV), wk, wv, pos)
+    ref_k = [oracle.latents(xs[b].double().numpy(), ak.double().numpy()).astype(np.float32) for b in range(B)]
+    ref_v = [oracle.latents(xs[b].double().numpy(), av.double().numpy()).astype(np.float32) for b in range(B)]
+    scale = 1.0 / math.sqrt(w.head_dim)
+    offk, offv = lrgen.head_offsets(rk), lrgen.head_offsets(rv)
+    for st in range(steps):
+        T = ctx + st + 1
+        q = lrgen.normal(lrgen.stream_key(w.seed, lrgen.TAG_Q, 0, st), 0, B * H * w.head_dim, 1.0)
+        q = q.view(B, H, w.head_dim).to(torch.bfloat16).to(DEV).contiguous()
+        ck, cv = s.project(0, xs[:, ctx + st].contiguous().to(DEV), wk, wv)
+        pos = torch.full((B,), ctx + st, dtype=torch.int32, device=DEV)
+        out = torch.empty(B, H, w.head_dim, dtype=torch.bfloat16, device=DEV)
+        s.lengths.fill_(T)
+        s.append_decode(0, ck, cv, pos, q, out, T)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy()
+        for b in range(B):
+            for h in range(H):
+                ref = oracle.attend(w.qfmt, ref_k[b][:T, offk[h]:offk[h] + rk[h]],
+                                    ref_v[b][:T, offv[h]:offv[h] + rv[h]],
+                                    q[b, h].double().cpu().numpy(),
+                                    bk[offk[h]:offk[h] + rk[h]].double().cpu().numpy(),
+                                    bv[offv[h]:offv[h] + rv[h]].double().cpu().numpy(), scale)
+                assert within(got[b, h], ref, TOL_BF16), (st, b, h)
