@@ -101,7 +101,8 @@ def append_bytes(w, rk, rv):
 def projection_bytes(w, rk, rv, tokens):
     """Algorithmic HBM bytes of one latent-generation launch: the bf16 factors
     (E x sum r, K and V) once, the bf16 activations of the new tokens, and the
-    fp32 latents written."""
+    fp32 latents written (the packed factors' zero rows past a multiple of 16
+    are not counted)."""
     n = sum(rk) + sum(rv)
     return 2 * w.embed * n + 2 * tokens * w.embed + 4 * tokens * n
 
@@ -193,10 +194,12 @@ def main():
     # latent buffers the projection writes
     proj = None
     if args.with_projection or not (args.no_projection_leg or args.profile_steps):
-        wts = []
         for l in range(L):
-            wts.append(tuple(lrgen.down_factors(w, l, kv, device=dev).t().contiguous().to(torch.bfloat16)
-                             for kv in (0, 1)))
+            wk, wv = (lrgen.down_factors(w, l, kv, device=dev).t().contiguous().to(torch.bfloat16)
+                      for kv in (0, 1))
+            sess.set_projection(l, wk, wv)     # packed once per layer, as in serving
+            del wk, wv
+        wts = [sess.proj[l][1] for l in range(L)]
         xs = [[torch.cat([lrgen.activations(w, l, b, ctx + s, ctx + s + 1, device=dev)
                           for b in range(w.batch)]).to(torch.bfloat16).contiguous()
                for l in range(L)] for s in range(nsteps_inputs)]
@@ -212,7 +215,7 @@ def main():
         ck, cv, q = layers[l]
         if project:
             wts, xs, lat = proj
-            ck, cv = sess.project(l, xs[s][l], wts[l][0], wts[l][1], ck=lat[l][0], cv=lat[l][1])
+            ck, cv = sess.project(l, xs[s][l], ck=lat[l][0], cv=lat[l][1])
         if fused:
             sess.append_decode(l, ck.view(w.batch, -1), cv.view(w.batch, -1), pos, q, out,
                                ctx + s + 1, lengths=ln)
@@ -336,9 +339,8 @@ def main():
         def proj_launch(s, l):
             # the current stream: torch's, or the capture stream inside capture()
             rc = lrb._lib.lr_attn_project_latent(
-                sess.plan, l, xs[s][l].data_ptr(), w.batch, w.embed, wts[l][0].data_ptr(),
-                wts[l][1].data_ptr(), lat[l][0].data_ptr(), lat[l][1].data_ptr(),
-                torch.cuda.current_stream().cuda_stream)
+                sess.plan, l, xs[s][l].data_ptr(), w.batch, w.embed, wts[l].data_ptr(),
+                lat[l][0].data_ptr(), lat[l][1].data_ptr(), torch.cuda.current_stream().cuda_stream)
             if rc != 0:
                 raise RuntimeError(f"projection launch failed: {lrb.lr_attn_strerror(rc)}")
 

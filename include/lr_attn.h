@@ -209,22 +209,44 @@ lr_status lr_attn_decode_explicit(const lr_attn_plan* plan, int32_t layer, const
  * in a GPU kernel ahead of the fused quantisation):
  *     ck[t][:] = x[t] A^K,   cv[t][:] = x[t] A^V,   t < n_tokens,
  * where A^K (E x latent_elems(0)) is A^K_h of every head side by side, head
- * h's r_h columns at its latent_offset_k, and A^V likewise.  The factors are
- * passed TRANSPOSED, one row of `embed` values per latent dimension (the
- * layout of a linear layer's weight).  The products run on the matrix cores:
- * bf16 inputs, exact products, fp32 sums in an order that is the same on
- * every call (results are deterministic, not bitwise equal to any other
- * summation order).  The plan's io_dtype does not apply.
+ * h's r_h columns at its latent_offset_k, and A^V likewise.
+ *
+ * The factors are given once, TRANSPOSED (one row of E values per latent
+ * dimension: the layout of a linear layer's weight) and packed by
+ * lr_attn_pack_projection into matrix-core operand blocks; the packed buffer
+ * depends only on the factors, so it is made once per layer and reused.
+ * Packed layout (bf16 elements): tiles r = 0 .. k_tiles + v_tiles - 1 of 16
+ * latent rows (k_tiles = ceil(latent_elems(0) / 16), K tiles first), each of
+ * E / 32 steps of 512 elements; element 8 l + i of step c of tile r is row
+ * 16 r' + (l % 16) of W^K (r' = r) or W^V (r' = r - k_tiles), column
+ * 32 c + 8 (l / 16) + i (l < 64, i < 8); rows past the last are zero. */
+
+/* Elements of the packed factor buffer of a layer for this embed (0 on bad
+ * arguments: embed must be a positive multiple of 32). */
+size_t lr_attn_packed_projection_elems(const lr_attn_plan* plan, int32_t layer, int32_t embed);
+
+/* Pack the row-major factors of layer `layer`:
+ *   wk, wv   device bf16 [latent_elems(kv)][embed] (W^K = A^K transposed), 16-aligned
+ *   packed   device bf16, lr_attn_packed_projection_elems elements, 16-aligned
+ * Errors: LR_EINVAL (null or misaligned pointer, bad embed), LR_ERANGE
+ * (layer), LR_EHIP. */
+lr_status lr_attn_pack_projection(const lr_attn_plan* plan, int32_t layer, int32_t embed,
+                                  const void* wk, const void* wv, void* packed, void* stream);
+
+/* The latents of n_tokens tokens, on the matrix cores: bf16 inputs, exact
+ * products, fp32 sums in an order that is the same on every call (results are
+ * deterministic; they are not bitwise equal to other summation orders).  The
+ * plan's io_dtype does not apply.
  *   x         device bf16 [n_tokens][embed], 16-aligned
  *   n_tokens  0 (no-op) or more; rows of x are tokens in any order
- *   embed     E: a multiple of 32, >= 32
- *   wk, wv    device bf16 [latent_elems(kv)][embed], 16-aligned
+ *   embed     E: a multiple of 32, >= 32, the value the factors were packed with
+ *   packed    device, from lr_attn_pack_projection
  *   ck, cv    device fp32 [n_tokens][latent_elems(kv)], 16-aligned, written
  * Errors: LR_EINVAL (null or misaligned pointer, bad embed, n_tokens < 0),
  * LR_ERANGE (layer), LR_EHIP. */
 lr_status lr_attn_project_latent(const lr_attn_plan* plan, int32_t layer, const void* x,
-                                 int32_t n_tokens, int32_t embed, const void* wk, const void* wv,
-                                 float* ck, float* cv, void* stream);
+                                 int32_t n_tokens, int32_t embed, const void* packed, float* ck,
+                                 float* cv, void* stream);
 
 /* Workspace bytes of lr_attn_project_append for any layer with this n_new
  * (the fp32 latents of batch * n_new tokens, K and V); 0 on bad arguments. */
@@ -235,13 +257,13 @@ size_t lr_attn_project_workspace_bytes(const lr_attn_plan* plan, int32_t n_new);
  * then quantised and written at slots pos[b] .. pos[b] + n_new - 1.  The
  * cache bytes are identical to those two calls.
  *   x          device bf16 [batch][n_new][embed]
- *   embed, wk, wv  as for lr_attn_project_latent
+ *   embed, packed  as for lr_attn_project_latent
  *   pos, n_new as for lr_attn_append_latent (n_new = 0 is a no-op)
  *   workspace  device, >= lr_attn_project_workspace_bytes(n_new) bytes,
  *              256-aligned, scratch; concurrent calls must not share one
  * Errors: LR_EINVAL, LR_ERANGE, LR_EWORKSPACE, LR_EHIP. */
 lr_status lr_attn_project_append(const lr_attn_plan* plan, int32_t layer, void* cache,
-                                 const void* x, int32_t embed, const void* wk, const void* wv,
+                                 const void* x, int32_t embed, const void* packed,
                                  const int32_t* pos, int32_t n_new, void* workspace,
                                  size_t ws_bytes, void* stream);
 

@@ -90,9 +90,11 @@ def _load() -> ctypes.CDLL:
         "lr_attn_decode_explicit": (ctypes.c_int, [P, I32, P, P, I32, P, P, P, ctypes.c_float, P, P, SZ, P]),
         "lr_attn_append_decode": (ctypes.c_int, [P, I32, P, P, P, P, P, I32, P, P, P, ctypes.c_float,
                                                  P, P, SZ, P]),
-        "lr_attn_project_latent": (ctypes.c_int, [P, I32, P, I32, I32, P, P, P, P, P]),
+        "lr_attn_packed_projection_elems": (SZ, [P, I32, I32]),
+        "lr_attn_pack_projection": (ctypes.c_int, [P, I32, I32, P, P, P, P]),
+        "lr_attn_project_latent": (ctypes.c_int, [P, I32, P, I32, I32, P, P, P, P]),
         "lr_attn_project_workspace_bytes": (SZ, [P, I32]),
-        "lr_attn_project_append": (ctypes.c_int, [P, I32, P, P, I32, P, P, P, I32, P, SZ, P]),
+        "lr_attn_project_append": (ctypes.c_int, [P, I32, P, P, I32, P, P, I32, P, SZ, P]),
         "lr_attn_probe_read": (ctypes.c_int, [P, SZ, P, P]),
         "lr_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "lr_attn_last_hip_error": (I32, []),
@@ -208,11 +210,21 @@ def lr_attn_decode_explicit(plan: int, layer: int, cache, length, max_len: int, 
            "lr_attn_decode_explicit")
 
 
-def lr_attn_project_latent(plan: int, layer: int, x, n_tokens: int, embed: int, wk, wv, ck, cv,
+def lr_attn_packed_projection_elems(plan: int, layer: int, embed: int) -> int:
+    return int(_lib.lr_attn_packed_projection_elems(plan, layer, embed))
+
+
+def lr_attn_pack_projection(plan: int, layer: int, embed: int, wk, wv, packed, stream=None) -> None:
+    """Pack the factors wk/wv ([latent_elems, embed] bf16, A transposed) for the projection."""
+    _check(_lib.lr_attn_pack_projection(plan, layer, embed, _ptr(wk), _ptr(wv), _ptr(packed),
+                                        _stream(stream)), "lr_attn_pack_projection")
+
+
+def lr_attn_project_latent(plan: int, layer: int, x, n_tokens: int, embed: int, packed, ck, cv,
                            stream=None) -> None:
     """ck/cv [n_tokens, latent_elems] (fp32) = x [n_tokens, embed] (bf16) times the
-    factors wk/wv given as [latent_elems, embed] bf16 (A transposed)."""
-    _check(_lib.lr_attn_project_latent(plan, layer, _ptr(x), n_tokens, embed, _ptr(wk), _ptr(wv),
+    packed factors."""
+    _check(_lib.lr_attn_project_latent(plan, layer, _ptr(x), n_tokens, embed, _ptr(packed),
                                        _ptr(ck), _ptr(cv), _stream(stream)),
            "lr_attn_project_latent")
 
@@ -221,10 +233,10 @@ def lr_attn_project_workspace_bytes(plan: int, n_new: int) -> int:
     return int(_lib.lr_attn_project_workspace_bytes(plan, n_new))
 
 
-def lr_attn_project_append(plan: int, layer: int, cache, x, embed: int, wk, wv, pos, n_new: int,
+def lr_attn_project_append(plan: int, layer: int, cache, x, embed: int, packed, pos, n_new: int,
                            workspace, ws_bytes: int, stream=None) -> None:
     """lr_attn_project_latent of x [batch, n_new, embed] then lr_attn_append_latent."""
-    _check(_lib.lr_attn_project_append(plan, layer, _ptr(cache), _ptr(x), embed, _ptr(wk), _ptr(wv),
+    _check(_lib.lr_attn_project_append(plan, layer, _ptr(cache), _ptr(x), embed, _ptr(packed),
                                        _ptr(pos), n_new, _ptr(workspace), ws_bytes, _stream(stream)),
            "lr_attn_project_append")
 

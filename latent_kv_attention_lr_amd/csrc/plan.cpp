@@ -239,25 +239,40 @@ size_t latent_ws_bytes(const lr_attn_plan::Layer& L, size_t n) {
 }
 
 lr_status check_project(const lr_attn_plan* p, int32_t layer, const void* x, int32_t embed,
-                        const void* wk, const void* wv) {
+                        const void* packed) {
   if (!p) return LR_EINVAL;
   if (layer < 0 || layer >= p->desc.n_layers) return LR_ERANGE;
   if (embed < 32 || embed % 32 != 0) return LR_EINVAL;
-  if (!x || !wk || !wv) return LR_EINVAL;
-  if (!aligned(x, 16) || !aligned(wk, 16) || !aligned(wv, 16)) return LR_EINVAL;
+  if (!x || !packed) return LR_EINVAL;
+  if (!aligned(x, 16) || !aligned(packed, 16)) return LR_EINVAL;
   return LR_OK;
 }
 
 }  // namespace
 
+size_t lr_attn_packed_projection_elems(const lr_attn_plan* p, int32_t layer, int32_t embed) {
+  if (!p || layer < 0 || layer >= p->desc.n_layers || embed < 32 || embed % 32 != 0) return 0;
+  return lr::packed_projection_elems(*p, layer, embed);
+}
+
+lr_status lr_attn_pack_projection(const lr_attn_plan* p, int32_t layer, int32_t embed, const void* wk,
+                                  const void* wv, void* packed, void* stream) {
+  if (!p) return LR_EINVAL;
+  if (layer < 0 || layer >= p->desc.n_layers) return LR_ERANGE;
+  if (embed < 32 || embed % 32 != 0) return LR_EINVAL;
+  if (!wk || !wv || !packed) return LR_EINVAL;
+  if (!aligned(wk, 16) || !aligned(wv, 16) || !aligned(packed, 16)) return LR_EINVAL;
+  return hip_status(lr::launch_pack_projection(*p, layer, embed, wk, wv, packed, stream));
+}
+
 lr_status lr_attn_project_latent(const lr_attn_plan* p, int32_t layer, const void* x,
-                                 int32_t n_tokens, int32_t embed, const void* wk, const void* wv,
-                                 float* ck, float* cv, void* stream) {
-  const lr_status st = check_project(p, layer, x, embed, wk, wv);
+                                 int32_t n_tokens, int32_t embed, const void* packed, float* ck,
+                                 float* cv, void* stream) {
+  const lr_status st = check_project(p, layer, x, embed, packed);
   if (st != LR_OK) return st;
   if (n_tokens < 0 || !ck || !cv || !aligned(ck, 16) || !aligned(cv, 16)) return LR_EINVAL;
   if (n_tokens == 0) return LR_OK;
-  return hip_status(lr::launch_project(*p, layer, x, n_tokens, embed, wk, wv, ck, cv, stream));
+  return hip_status(lr::launch_project(*p, layer, x, n_tokens, embed, packed, ck, cv, stream));
 }
 
 size_t lr_attn_project_workspace_bytes(const lr_attn_plan* p, int32_t n_new) {
@@ -269,10 +284,9 @@ size_t lr_attn_project_workspace_bytes(const lr_attn_plan* p, int32_t n_new) {
 }
 
 lr_status lr_attn_project_append(const lr_attn_plan* p, int32_t layer, void* cache, const void* x,
-                                 int32_t embed, const void* wk, const void* wv,
-                                 const int32_t* pos, int32_t n_new, void* ws, size_t ws_bytes,
-                                 void* stream) {
-  const lr_status st = check_project(p, layer, x, embed, wk, wv);
+                                 int32_t embed, const void* packed, const int32_t* pos,
+                                 int32_t n_new, void* ws, size_t ws_bytes, void* stream) {
+  const lr_status st = check_project(p, layer, x, embed, packed);
   if (st != LR_OK) return st;
   if (n_new < 0) return LR_EINVAL;
   if (n_new > p->desc.capacity) return LR_ERANGE;
@@ -286,7 +300,7 @@ lr_status lr_attn_project_append(const lr_attn_plan* p, int32_t layer, void* cac
   float* ck = static_cast<float*>(ws);
   float* cv = reinterpret_cast<float*>(static_cast<char*>(ws) + round256(n * L.sum_rk * sizeof(float)));
   const lr_status s1 = hip_status(lr::launch_project(*p, layer, x, static_cast<int32_t>(n), embed,
-                                                     wk, wv, ck, cv, stream));
+                                                     packed, ck, cv, stream));
   if (s1 != LR_OK) return s1;
   return hip_status(lr::launch_append(*p, layer, cache, ck, cv, pos, n_new, stream));
 }

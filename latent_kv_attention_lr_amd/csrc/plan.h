@@ -62,11 +62,14 @@ int launch_decode(const lr_attn_plan& p, int32_t layer, const void* cache, const
                   int32_t max_len, const void* q, const void* bk, const void* bv, float scale,
                   void* out, void* workspace, void* stream, bool explicit_form,
                   const AppendInputs* app = nullptr);
-// project.hip: fp32 latents ck [n_tokens][sum_rk] = x W^K^T and cv likewise,
-// x bf16 [n_tokens][embed], W bf16 [sum_r][embed].  n_tokens >= 1, embed % 32 == 0.
+// project.hip: packing of the down-projection factors (row-major W [sum_r][E]
+// bf16 -> MFMA step blocks) and fp32 latents ck [n_tokens][sum_rk] = x W^K^T
+// (cv likewise) from bf16 x [n_tokens][embed].  n_tokens >= 1, embed % 32 == 0.
+size_t packed_projection_elems(const lr_attn_plan& p, int32_t layer, int32_t embed);
+int launch_pack_projection(const lr_attn_plan& p, int32_t layer, int32_t embed, const void* wk,
+                           const void* wv, void* packed, void* stream);
 int launch_project(const lr_attn_plan& p, int32_t layer, const void* x, int32_t n_tokens,
-                   int32_t embed, const void* wk, const void* wv, float* ck, float* cv,
-                   void* stream);
+                   int32_t embed, const void* packed, float* ck, float* cv, void* stream);
 // probe.hip: stream bytes / 16 16-byte words from src (read only).
 int launch_probe_read(const void* src, size_t bytes, void* sink, void* stream);
 

@@ -5,11 +5,19 @@
 // kernel), in fp32 from bf16 activations and factors, for the quantised append
 // that follows.
 //
-// The factors come as W = A^T, one row of E values per latent dimension (the
-// layout of a linear layer's weight), heads concatenated in the order of the
-// latent vector; both MFMA operands are then contiguous 16-byte loads.  At
-// decode sizes (a few dozen tokens) the product is bound by reading W once from
-// HBM: 2 E bytes per latent dimension, against 2 T flops per byte.
+// At decode sizes (one token per sequence, a few dozen tokens) the product is
+// bound by moving the factors (2 E bytes per latent dimension) from HBM and by
+// feeding every work-group the same small activation block; two layout
+// choices follow from measurement on MI355X:
+//   * the factors are packed once (k_pack) so that the 16 x 32 operand block
+//     of one MFMA step is 1 KB contiguous: lane l of the packed block holds
+//     row l & 15, elements 8 (l >> 4) .. 8 (l >> 4) + 7 of the step.  Read in
+//     row-major order the same step touches 16 rows at 64 bytes each, which
+//     measured 1.7x slower;
+//   * activations are read with plain coalesced 16-byte loads into LDS, a
+//     phase of at most 128 KB at a time, and the MFMA operands are read from
+//     there; the next phase's factors and activations are loaded into
+//     registers while the current phase is multiplied.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -21,96 +29,133 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kProjWaves = 8;     // wavefronts per work-group, each on 1/8 of E
-constexpr int kMaxColTiles = 4;   // 16-token column tiles per work-group
+constexpr int kLdsBytes = 128 * 1024 + 64 * 16;   // activation phase + row padding
+
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 struct ProjArgs {
   const uint16_t* x;   // bf16 [T][E]
-  const uint16_t* wk;  // bf16 [nk][E]
-  const uint16_t* wv;  // bf16 [nv][E]
+  const uint16_t* wp;  // packed factors: [k_tiles + v_tiles][E / 32][64 lanes][8]
   float* ck;           // fp32 [T][nk]
   float* cv;           // fp32 [T][nv]
   int32_t T, E, nk, nv;
-  int32_t k_tiles, row_tiles;     // 16-row tiles of W^K, of W^K and W^V together
-  int32_t t_blocks, tb_stride;    // token blocks of 16 NT; blocks per grid column
+  int32_t k_tiles, row_tiles;   // 16-row tiles of W^K; of W^K and W^V together
+  int32_t t_blocks, tb_stride;  // token blocks; token blocks per grid pass
 };
 
-__device__ __forceinline__ bf16x8_t load8(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
-}
+// Work-group (16-row tile, block of 16 NT tokens) over all of E:
+//   c[t][n] = sum_e x[t][e] w[n][e]
+// with v_mfma_f32_16x16x32_bf16 (latent rows = MFMA rows, tokens = columns;
+// lane (i, g) = (lane & 15, lane >> 4) supplies row/column i, elements 8 g ..
+// 8 g + 7 of a step, and receives rows 4 g .. 4 g + 3 of column i).  E is
+// walked in phases of PS = NW * SPW steps; in a phase wavefront w multiplies
+// steps w SPW .. w SPW + SPW - 1, its partial tile is summed with the other
+// wavefronts' through LDS in wavefront order at the end, so the result is the
+// same on every call.  Rows and tokens past the ends are never stored.
+template <int NT, int NW, int SPW>
+__global__ __launch_bounds__(NW * 64) void k_project(ProjArgs a) {
+  constexpr int TOK = 16 * NT;                 // tokens per block
+  constexpr int PS = NW * SPW;                 // steps per phase
+  constexpr int EP = 32 * PS;                  // embedding elements per phase
+  constexpr int RS = EP * 2 + 16;              // LDS bytes per token row (padded)
+  constexpr int XV = TOK * EP / 8;             // 16-byte activation pieces per phase
+  constexpr int XPT = (XV + NW * 64 - 1) / (NW * 64);
+  static_assert(TOK * RS <= kLdsBytes, "activation phase exceeds LDS");
+  static_assert(NW * NT * 64 * 16 <= kLdsBytes, "reduction exceeds LDS");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
 
-// Work-group (row tile, token block): c[t][n] = sum_e x[t][e] w[n][e] for 16
-// latent rows n and 16 NT tokens t, with v_mfma_f32_16x16x32_bf16 -- latent
-// rows are the MFMA rows, tokens its columns.  Lane (i, g) = (lane & 15,
-// lane >> 4) supplies row i of w and of each x column tile, eight consecutive
-// embedding elements 8 g .. 8 g + 7 of every 32-wide step (the same elements
-// on both sides, which is all the product needs), and receives rows 4 g .. 4 g
-// + 3 of column i.  The eight wavefronts take contiguous eighths of the
-// embedding; their partial tiles are summed through LDS in wavefront order, so
-// the result is the same on every call.  Rows and tokens past the ends are
-// read at the last valid row and never stored.
-template <int NT>
-__global__ __launch_bounds__(kProjWaves * 64) void k_project(ProjArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop control
   const int li = lane & 15, lg = lane >> 4;
   const int rt = blockIdx.x % a.row_tiles;
   const bool isv = rt >= a.k_tiles;
   const int n0 = 16 * (isv ? rt - a.k_tiles : rt);
   const int N = isv ? a.nv : a.nk;
-  const uint16_t* wr = (isv ? a.wv : a.wk) + size_t(min(n0 + li, N - 1)) * a.E + 8 * lg;
   float* out = isv ? a.cv : a.ck;
+  const int steps = a.E >> 5, phases = (steps + PS - 1) / PS;
+  const uint16_t* wl = a.wp + size_t(rt) * steps * 512 + 8 * lane;
 
-  const int steps = a.E >> 5, per = (steps + kProjWaves - 1) / kProjWaves;
-  const int c0 = wid * per, c1 = min(steps, c0 + per);
-
-  __shared__ f32x4_t s_red[kProjWaves][NT][64];
   for (int tb = blockIdx.x / a.row_tiles; tb < a.t_blocks; tb += a.tb_stride) {
-    const int t0 = 16 * NT * tb;
-    const uint16_t* xr[NT];
+    const int t0 = TOK * tb;
+    uint4 wb[2][SPW];
+    uint4 xb[XPT];
+    // factors of phase p for this wavefront's steps (clamped: a step past E is
+    // loaded at the last step and not multiplied)
+    auto load_w = [&](int p, uint4 (&dst)[SPW]) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j) xr[j] = a.x + size_t(min(t0 + 16 * j + li, a.T - 1)) * a.E + 8 * lg;
-
+      for (int u = 0; u < SPW; ++u) dst[u] = ld16(wl + size_t(min(p * PS + wid * SPW + u, steps - 1)) * 512);
+    };
+    // activations of phase p, piece q = row * (EP / 8) + col: token t0 + row,
+    // elements p EP + 8 col .. + 7 (clamped into the row and the token range)
+    auto load_x = [&](int p) {
+#pragma unroll
+      for (int m = 0; m < XPT; ++m) {
+        const int q = min(tid + m * NW * 64, XV - 1);
+        const int row = q / (EP / 8), col = q % (EP / 8);
+        xb[m] = ld16(a.x + size_t(min(t0 + row, a.T - 1)) * a.E + min(p * EP + 8 * col, a.E - 8));
+      }
+    };
+    auto store_x = [&]() {
+#pragma unroll
+      for (int m = 0; m < XPT; ++m) {
+        const int q = tid + m * NW * 64;
+        if (q < XV) *reinterpret_cast<uint4*>(lds + (q / (EP / 8)) * RS + 16 * (q % (EP / 8))) = xb[m];
+      }
+    };
     f32x4_t acc[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // U steps of loads are issued before their products, so that U (NT + 1)
-    // 16-byte loads per lane are in flight; the remainder goes one step at a time.
-    constexpr int U = NT <= 2 ? 8 : 4;
-    int c = c0;
-    for (; c + U <= c1; c += U) {
-      bf16x8_t av[U], bv[U][NT];
+    auto compute = [&](int p, const uint4 (&w)[SPW]) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        av[u] = load8(wr + 32 * (c + u));
+      for (int u = 0; u < SPW; ++u) {
+        const int cl = wid * SPW + u;
+        if (p * PS + cl < steps) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) bv[u][j] = load8(xr[j] + 32 * (c + u));
+          for (int j = 0; j < NT; ++j) {
+            const bf16x8_t bv = __builtin_bit_cast(
+                bf16x8_t, *reinterpret_cast<const uint4*>(lds + (16 * j + li) * RS + 64 * cl + 16 * lg));
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w[u]), bv, acc[j],
+                                                            0, 0, 0);
+          }
+        }
       }
-      __builtin_amdgcn_sched_barrier(0);  // keep every load of the batch ahead of the products
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[u][j], acc[j], 0, 0, 0);
-    }
-    for (; c < c1; ++c) {
-      const bf16x8_t av = load8(wr + 32 * c);
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, load8(xr[j] + 32 * c), acc[j], 0, 0, 0);
+    };
+
+    // two phases per trip so that the factor registers alternate statically
+    load_w(0, wb[0]);
+    load_x(0);
+    for (int p = 0; p < phases; p += 2) {
+      store_x();
+      __syncthreads();
+      if (p + 1 < phases) {
+        load_w(p + 1, wb[1]);
+        load_x(p + 1);
+      }
+      compute(p, wb[0]);
+      __syncthreads();
+      if (p + 1 < phases) {
+        store_x();
+        __syncthreads();
+        if (p + 2 < phases) {
+          load_w(p + 2, wb[0]);
+          load_x(p + 2);
+        }
+        compute(p + 1, wb[1]);
+        __syncthreads();
+      }
     }
 
+    f32x4_t* s_red = reinterpret_cast<f32x4_t*>(lds);   // [NW][NT][64]
 #pragma unroll
-    for (int j = 0; j < NT; ++j) s_red[wid][j][lane] = acc[j];
+    for (int j = 0; j < NT; ++j) s_red[(wid * NT + j) * 64 + lane] = acc[j];
     __syncthreads();
-    // one output per thread per pass: token tt of the block, row nn of the tile,
-    // consecutive threads on consecutive rows of one token
-    for (int i = tid; i < NT * 256; i += kProjWaves * 64) {
+    // token tt, row nn: consecutive threads on consecutive rows of one token
+    for (int i = tid; i < NT * 256; i += NW * 64) {
       const int tt = i >> 4, nn = i & 15;
       const int j = tt >> 4, src = (tt & 15) + 16 * (nn >> 2), e = nn & 3;
       float v = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kProjWaves; ++w) v += s_red[w][j][src][e];
+      for (int w = 0; w < NW; ++w) v += s_red[(w * NT + j) * 64 + src][e];
       const int t = t0 + tt, n = n0 + nn;
       if (t < a.T && n < N) out[size_t(t) * N + n] = v;
     }
@@ -118,18 +163,55 @@ __global__ __launch_bounds__(kProjWaves * 64) void k_project(ProjArgs a) {
   }
 }
 
+// Packing of the factors: piece q (16 bytes) of the packed buffer is lane l =
+// q % 64 of step c = (q / 64) % (E / 32) of tile r = q / (64 E / 32): row
+// 16 r' + (l & 15) of W^K (r < k_tiles, r' = r) or W^V (r' = r - k_tiles),
+// elements 32 c + 8 (l >> 4) .. + 7; rows past the end are zeros.
+__global__ __launch_bounds__(256) void k_pack(const uint16_t* wk, const uint16_t* wv, uint16_t* wp, int32_t E,
+                                              int32_t nk, int32_t nv, int32_t k_tiles, size_t pieces) {
+  const int steps = E >> 5;
+  for (size_t q = size_t(blockIdx.x) * 256 + threadIdx.x; q < pieces; q += size_t(gridDim.x) * 256) {
+    const int l = int(q & 63);
+    const size_t cq = q >> 6;
+    const int c = int(cq % steps);
+    const int r = int(cq / steps);
+    const bool isv = r >= k_tiles;
+    const int row = 16 * (isv ? r - k_tiles : r) + (l & 15);
+    const int N = isv ? nv : nk;
+    uint4 v = uint4{0u, 0u, 0u, 0u};
+    if (row < N) v = ld16((isv ? wv : wk) + size_t(row) * E + 32 * c + 8 * (l >> 4));
+    *reinterpret_cast<uint4*>(wp + 8 * q) = v;
+  }
+}
+
 }  // namespace
 
 namespace lr {
 
+size_t packed_projection_elems(const lr_attn_plan& p, int32_t layer, int32_t embed) {
+  const auto& L = p.layers[layer];
+  return size_t((L.sum_rk + 15) / 16 + (L.sum_rv + 15) / 16) * 16 * size_t(embed);
+}
+
+int launch_pack_projection(const lr_attn_plan& p, int32_t layer, int32_t embed, const void* wk,
+                           const void* wv, void* packed, void* stream) {
+  const auto& L = p.layers[layer];
+  const size_t pieces = packed_projection_elems(p, layer, embed) / 8;
+  const size_t groups = (pieces + 255) / 256;
+  const unsigned grid = unsigned(groups < 65536 ? groups : 65536);
+  hipLaunchKernelGGL(k_pack, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint16_t*>(wk), static_cast<const uint16_t*>(wv),
+                     static_cast<uint16_t*>(packed), embed, L.sum_rk, L.sum_rv, (L.sum_rk + 15) / 16,
+                     pieces);
+  return int(hipGetLastError());
+}
+
 int launch_project(const lr_attn_plan& p, int32_t layer, const void* x, int32_t n_tokens,
-                   int32_t embed, const void* wk, const void* wv, float* ck, float* cv,
-                   void* stream) {
+                   int32_t embed, const void* packed, float* ck, float* cv, void* stream) {
   const auto& L = p.layers[layer];
   ProjArgs a;
   a.x = static_cast<const uint16_t*>(x);
-  a.wk = static_cast<const uint16_t*>(wk);
-  a.wv = static_cast<const uint16_t*>(wv);
+  a.wp = static_cast<const uint16_t*>(packed);
   a.ck = ck;
   a.cv = cv;
   a.T = n_tokens;
@@ -138,19 +220,22 @@ int launch_project(const lr_attn_plan& p, int32_t layer, const void* x, int32_t 
   a.nv = L.sum_rv;
   a.k_tiles = (L.sum_rk + 15) / 16;
   a.row_tiles = a.k_tiles + (L.sum_rv + 15) / 16;
+  // tokens per work-group: 16, 32, 48 or 64 (the fewest 16-token tiles that
+  // cover n_tokens, at most four); larger calls loop over token blocks
   const int col_tiles = (n_tokens + 15) / 16;
-  const int nt = col_tiles < kMaxColTiles ? col_tiles : kMaxColTiles;
+  const int nt = col_tiles < 4 ? col_tiles : 4;
   a.t_blocks = (col_tiles + nt - 1) / nt;
-  // at most 2^20 work-groups; the rest of the token blocks are looped over
-  const int max_tb = (1 << 20) / a.row_tiles;
+  const int max_tb = (1 << 20) / a.row_tiles;   // at most 2^20 work-groups
   a.tb_stride = a.t_blocks < max_tb ? a.t_blocks : max_tb;
-  const dim3 grid(unsigned(a.row_tiles) * unsigned(a.tb_stride)), block(kProjWaves * 64);
+  const dim3 grid(unsigned(a.row_tiles) * unsigned(a.tb_stride));
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // shapes measured on MI355X at E = 4096: 2048-element activation phases up
+  // to 32 tokens, 1024-element ones above, with 16 wavefronts at 64 tokens
   switch (nt) {
-    case 1: hipLaunchKernelGGL(k_project<1>, grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL(k_project<2>, grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL(k_project<3>, grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL(k_project<4>, grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_project<1, 8, 8>), grid, dim3(512), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_project<2, 8, 8>), grid, dim3(512), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_project<3, 8, 4>), grid, dim3(512), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_project<4, 16, 2>), grid, dim3(1024), 0, s, a); break;
   }
   return int(hipGetLastError());
 }

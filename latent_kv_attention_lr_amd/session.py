@@ -16,8 +16,9 @@ from . import (LR_DT_BF16, LR_DT_F32, LR_HEAD_DIM, lr_attn_append_decode, lr_att
                lr_attn_cache_bytes,
                lr_attn_decode, lr_attn_decode_explicit, lr_attn_factor_elems,
                lr_attn_head_layout_get, lr_attn_latent_elems, lr_attn_plan_create,
-               lr_attn_plan_destroy, lr_attn_project_append, lr_attn_project_latent,
-               lr_attn_project_workspace_bytes, lr_attn_workspace_bytes)
+               lr_attn_pack_projection, lr_attn_packed_projection_elems, lr_attn_plan_destroy,
+               lr_attn_project_append, lr_attn_project_latent, lr_attn_project_workspace_bytes,
+               lr_attn_workspace_bytes)
 
 
 class DecodeSession:
@@ -43,6 +44,7 @@ class DecodeSession:
         self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
         self.lengths = torch.zeros(batch, dtype=torch.int32, device=self.device)
         self._proj_ws: Optional[torch.Tensor] = None   # latents of project_append, grown on demand
+        self.proj: List[Optional[tuple]] = [None] * n_layers   # (embed, packed factors) per layer
 
     def close(self) -> None:
         plan = getattr(self, "plan", None)
@@ -130,21 +132,38 @@ class DecodeSession:
                               self.workspace.numel(), stream)
 
     # -- latent generation ---------------------------------------------------
-    def _check_projection(self, layer: int, x: torch.Tensor, wk: torch.Tensor, wv: torch.Tensor) -> int:
-        E = x.shape[-1]
-        if x.dtype != torch.bfloat16 or wk.dtype != torch.bfloat16 or wv.dtype != torch.bfloat16:
-            raise ValueError("x and the down-projection factors must be bf16")
-        if wk.shape != (self.latent_elems(layer, 0), E) or wv.shape != (self.latent_elems(layer, 1), E):
+    def set_projection(self, layer: int, wk: torch.Tensor, wv: torch.Tensor) -> None:
+        """Pack the down-projection factors of a layer, given as wk/wv
+        [latent_elems, embed] bf16 (A transposed), into a session-owned buffer."""
+        if wk.dim() != 2 or wv.dim() != 2 or wk.shape[1] != wv.shape[1]:
+            raise ValueError("factors must be [latent_elems, embed] with one embed")
+        E = wk.shape[1]
+        if wk.dtype != torch.bfloat16 or wv.dtype != torch.bfloat16:
+            raise ValueError("factors must be bf16")
+        if wk.shape[0] != self.latent_elems(layer, 0) or wv.shape[0] != self.latent_elems(layer, 1):
             raise ValueError("factors must be [latent_elems, embed] (A transposed)")
-        if not all(t.is_contiguous() and t.device == self.device for t in (x, wk, wv)):
-            raise ValueError("x and factors must be contiguous on the session device")
+        if not all(t.is_contiguous() and t.device == self.device for t in (wk, wv)):
+            raise ValueError("factors must be contiguous on the session device")
+        packed = torch.empty(lr_attn_packed_projection_elems(self.plan, layer, E), dtype=torch.bfloat16,
+                             device=self.device)
+        lr_attn_pack_projection(self.plan, layer, E, wk, wv, packed)
+        self.proj[layer] = (E, packed)
+
+    def _projection_input(self, layer: int, x: torch.Tensor) -> int:
+        if self.proj[layer] is None:
+            raise ValueError("projection factors of this layer are not set")
+        E = self.proj[layer][0]
+        if x.dtype != torch.bfloat16 or x.shape[-1] != E:
+            raise ValueError("x must be bf16 with the embed of the packed factors")
+        if not (x.is_contiguous() and x.device == self.device):
+            raise ValueError("x must be contiguous on the session device")
         return E
 
-    def project(self, layer: int, x: torch.Tensor, wk: torch.Tensor, wv: torch.Tensor,
-                ck: Optional[torch.Tensor] = None, cv: Optional[torch.Tensor] = None, stream=None):
-        """fp32 latents of x [..., embed]: (x A^K, x A^V) with the factors given as
-        wk/wv [latent_elems, embed]; returns (ck, cv) shaped [..., latent_elems]."""
-        E = self._check_projection(layer, x, wk, wv)
+    def project(self, layer: int, x: torch.Tensor, ck: Optional[torch.Tensor] = None,
+                cv: Optional[torch.Tensor] = None, stream=None):
+        """fp32 latents of x [..., embed]: (x A^K, x A^V); returns (ck, cv)
+        shaped [..., latent_elems]."""
+        E = self._projection_input(layer, x)
         lead = tuple(x.shape[:-1])
         n = x.numel() // E
         if ck is None:
@@ -155,13 +174,12 @@ class DecodeSession:
                 or ck.dtype != torch.float32 or cv.dtype != torch.float32 \
                 or not (ck.is_contiguous() and cv.is_contiguous()):
             raise ValueError("ck/cv must be contiguous fp32 with one latent vector per row of x")
-        lr_attn_project_latent(self.plan, layer, x, n, E, wk, wv, ck, cv, stream)
+        lr_attn_project_latent(self.plan, layer, x, n, E, self.proj[layer][1], ck, cv, stream)
         return ck, cv
 
-    def project_append(self, layer: int, x: torch.Tensor, wk: torch.Tensor, wv: torch.Tensor,
-                       pos: torch.Tensor, stream=None) -> None:
+    def project_append(self, layer: int, x: torch.Tensor, pos: torch.Tensor, stream=None) -> None:
         """Generate the latents of x [B, n_new, embed] and append them at pos[b].."""
-        E = self._check_projection(layer, x, wk, wv)
+        E = self._projection_input(layer, x)
         if x.dim() != 3 or x.shape[0] != self.batch:
             raise ValueError("x must be [batch, n_new, embed]")
         if not pos.is_contiguous():
@@ -171,5 +189,5 @@ class DecodeSession:
         if need > 0 and (self._proj_ws is None or self._proj_ws.numel() < need):
             self._proj_ws = torch.empty(need, dtype=torch.uint8, device=self.device)
         ws = self._proj_ws
-        lr_attn_project_append(self.plan, layer, self.caches[layer], x, E, wk, wv, pos, n_new,
-                               ws, 0 if ws is None else ws.numel(), stream)
+        lr_attn_project_append(self.plan, layer, self.caches[layer], x, E, self.proj[layer][1], pos,
+                               n_new, ws, 0 if ws is None else ws.numel(), stream)

@@ -219,19 +219,19 @@ def test_append_decode_argument_errors_before_launch():
 
 
 def _project(p, **kw):
-    a = dict(layer=0, x=FAKE, n=16, embed=4096, wk=FAKE, wv=FAKE, ck=FAKE, cv=FAKE)
+    a = dict(layer=0, x=FAKE, n=16, embed=4096, packed=FAKE, ck=FAKE, cv=FAKE)
     a.update(kw)
-    return lr._lib.lr_attn_project_latent(p, a["layer"], a["x"], a["n"], a["embed"], a["wk"],
-                                          a["wv"], a["ck"], a["cv"], None)
+    return lr._lib.lr_attn_project_latent(p, a["layer"], a["x"], a["n"], a["embed"], a["packed"],
+                                          a["ck"], a["cv"], None)
 
 
 def _project_append(p, **kw):
-    a = dict(layer=0, cache=FAKE, x=FAKE, embed=4096, wk=FAKE, wv=FAKE, pos=FAKE, n_new=1,
+    a = dict(layer=0, cache=FAKE, x=FAKE, embed=4096, packed=FAKE, pos=FAKE, n_new=1,
              ws=FAKE, ws_bytes=1 << 30)
     a.update(kw)
-    return lr._lib.lr_attn_project_append(p, a["layer"], a["cache"], a["x"], a["embed"], a["wk"],
-                                          a["wv"], a["pos"], a["n_new"], a["ws"], a["ws_bytes"],
-                                          None)
+    return lr._lib.lr_attn_project_append(p, a["layer"], a["cache"], a["x"], a["embed"],
+                                          a["packed"], a["pos"], a["n_new"], a["ws"],
+                                          a["ws_bytes"], None)
 
 
 def test_project_argument_errors_before_launch():
@@ -239,13 +239,34 @@ def test_project_argument_errors_before_launch():
     try:
         assert _project(None) == lr.LR_EINVAL
         assert _project(p, layer=1) == lr.LR_ERANGE
-        for name in ("x", "wk", "wv", "ck", "cv"):
+        for name in ("x", "packed", "ck", "cv"):
             assert _project(p, **{name: None}) == lr.LR_EINVAL, name
             assert _project(p, **{name: FAKE + 8}) == lr.LR_EINVAL, name   # 16-aligned
         for e in (0, 16, 48, 4095, -32):
             assert _project(p, embed=e) == lr.LR_EINVAL, e                  # multiple of 32, >= 32
         assert _project(p, n=-1) == lr.LR_EINVAL
         assert _project(p, n=0) == lr.LR_OK                                 # no-op, no launch
+    finally:
+        lr.lr_attn_plan_destroy(p)
+
+
+def test_pack_projection_size_and_argument_errors():
+    p = _plan()
+    try:
+        # rank_k sums to 184 (12 tiles of 16 rows), rank_v to 208 (13 tiles)
+        assert lr.lr_attn_packed_projection_elems(p, 0, 64) == (12 + 13) * 16 * 64
+        assert lr.lr_attn_packed_projection_elems(p, 0, 4096) == 25 * 16 * 4096
+        for e in (0, 16, 100):
+            assert lr.lr_attn_packed_projection_elems(p, 0, e) == 0
+        assert lr.lr_attn_packed_projection_elems(p, 1, 64) == 0
+        assert lr.lr_attn_packed_projection_elems(None, 0, 64) == 0
+        pack = lr._lib.lr_attn_pack_projection
+        assert pack(None, 0, 64, FAKE, FAKE, FAKE, None) == lr.LR_EINVAL
+        assert pack(p, 1, 64, FAKE, FAKE, FAKE, None) == lr.LR_ERANGE
+        assert pack(p, 0, 48, FAKE, FAKE, FAKE, None) == lr.LR_EINVAL
+        assert pack(p, 0, 64, None, FAKE, FAKE, None) == lr.LR_EINVAL
+        assert pack(p, 0, 64, FAKE, FAKE + 2, FAKE, None) == lr.LR_EINVAL
+        assert pack(p, 0, 64, FAKE, FAKE, None, None) == lr.LR_EINVAL
     finally:
         lr.lr_attn_plan_destroy(p)
 
@@ -270,7 +291,7 @@ def test_project_append_argument_errors_before_launch():
     try:
         assert _project_append(None) == lr.LR_EINVAL
         assert _project_append(p, layer=2) == lr.LR_ERANGE
-        for name in ("cache", "x", "wk", "wv", "pos"):
+        for name in ("cache", "x", "packed", "pos"):
             assert _project_append(p, **{name: None}) == lr.LR_EINVAL, name
         assert _project_append(p, cache=FAKE + 16) == lr.LR_EINVAL
         assert _project_append(p, pos=FAKE + 2) == lr.LR_EINVAL

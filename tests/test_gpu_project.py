@@ -46,13 +46,20 @@ def _factors(E, ranks, key, std):
     return a
 
 
-def _gpu_project(s, x_bf, ak, av):
-    """Run lr_attn_project_latent; factors are passed transposed ([N, E])."""
+def _set_factors(s, ak, av):
+    """Pack A^K, A^V (fp32 arrays holding bf16 values, [E, N]) through the library."""
     wk = ak.t().contiguous().to(torch.bfloat16).to(DEV)
     wv = av.t().contiguous().to(torch.bfloat16).to(DEV)
-    ck, cv = s.project(0, x_bf.to(DEV).contiguous(), wk, wv)
+    s.set_projection(0, wk, wv)
+    return wk, wv
+
+
+def _gpu_project(s, x_bf, ak, av):
+    """Pack the factors, run lr_attn_project_latent, return host latents."""
+    _set_factors(s, ak, av)
+    ck, cv = s.project(0, x_bf.to(DEV).contiguous())
     torch.cuda.synchronize()
-    return ck.cpu().numpy(), cv.cpu().numpy(), wk, wv
+    return ck.cpu().numpy(), cv.cpu().numpy()
 
 
 def _check_bound(got, x, a, rows=None):
@@ -72,8 +79,8 @@ def _check_bound(got, x, a, rows=None):
     return ref
 
 
-@pytest.mark.parametrize("E,T", [(32, 1), (96, 5), (1024, 16), (1024, 17), (1024, 64), (1024, 65),
-                                 (1024, 130), (4096, 3)])
+@pytest.mark.parametrize("E,T", [(32, 1), (96, 5), (1024, 16), (1024, 17), (1024, 40), (1024, 64),
+                                 (1024, 65), (1024, 130), (4096, 3), (4128, 33), (2080, 48)])
 def test_project_integer_inputs_bitexact(E, T):
     """Small-integer x and A (exact in bf16) keep every partial sum an integer
     below 2^24, so any summation order gives the exact product."""
@@ -84,7 +91,7 @@ def test_project_integer_inputs_bitexact(E, T):
     x = torch.from_numpy(rng.integers(-3, 4, (T, E)).astype(np.float32))
     ak = torch.from_numpy(rng.integers(-3, 4, (E, sum(ranks_k))).astype(np.float32))
     av = torch.from_numpy(rng.integers(-3, 4, (E, sum(ranks_v))).astype(np.float32))
-    ck, cv, _, _ = _gpu_project(s, x.to(torch.bfloat16), ak, av)
+    ck, cv = _gpu_project(s, x.to(torch.bfloat16), ak, av)
     assert np.array_equal(ck, oracle.latents(x.double().numpy(), ak.double().numpy()).astype(np.float32))
     assert np.array_equal(cv, oracle.latents(x.double().numpy(), av.double().numpy()).astype(np.float32))
 
@@ -99,9 +106,36 @@ def test_project_one_hot_rows_pick_factor_rows():
     x[torch.arange(len(idx)), torch.tensor(idx)] = 1.0
     ak = _factors(E, ranks_k, lrgen.stream_key(9, 1), 1.0)
     av = _factors(E, ranks_v, lrgen.stream_key(9, 2), 1.0)
-    ck, cv, _, _ = _gpu_project(s, x.to(torch.bfloat16), ak, av)
+    ck, cv = _gpu_project(s, x.to(torch.bfloat16), ak, av)
     assert np.array_equal(ck, ak.numpy()[idx])
     assert np.array_equal(cv, av.numpy()[idx])
+
+
+def test_pack_layout_matches_its_definition():
+    """The packed buffer holds, for tile r, step c, lane l, element i: row
+    16 r' + l % 16 of W^K (or W^V past the K tiles), column 32 c + 8 (l / 16)
+    + i, zeros past the last row -- checked byte for byte."""
+    E, ranks_k, ranks_v = 96, [8, 24, 40], [16, 8, 8]
+    s = _session(ranks_k, ranks_v)
+    rng = np.random.default_rng(7)
+    wk = rng.integers(0, 1 << 16, (sum(ranks_k), E)).astype(np.uint16)
+    wv = rng.integers(0, 1 << 16, (sum(ranks_v), E)).astype(np.uint16)
+    wk_t = torch.from_numpy(wk.view(np.int16)).view(torch.bfloat16).to(DEV)
+    wv_t = torch.from_numpy(wv.view(np.int16)).view(torch.bfloat16).to(DEV)
+    s.set_projection(0, wk_t, wv_t)
+    torch.cuda.synchronize()
+    got = s.proj[0][1].view(torch.int16).cpu().numpy().view(np.uint16)
+    want = []
+    for w in (wk, wv):
+        tiles = -(-w.shape[0] // 16)
+        wpad = np.zeros((tiles * 16, E), np.uint16)
+        wpad[:w.shape[0]] = w
+        for r in range(tiles):
+            for c in range(E // 32):
+                for l in range(64):
+                    row, col = 16 * r + l % 16, 32 * c + 8 * (l // 16)
+                    want.append(wpad[row, col:col + 8])
+    assert np.array_equal(got, np.concatenate(want))
 
 
 def _workload_inputs(idx, T, layer=0):
@@ -121,7 +155,7 @@ def test_project_workload_shapes_within_rounding_bound(idx):
     say(f"project workload {idx} E={w.embed} T={w.batch}")
     w, x, ak, av = _workload_inputs(idx, w.batch)
     s = _session(w.ranks_k[0], w.ranks_v[0], w.qfmt, batch=w.batch)
-    ck, cv, _, _ = _gpu_project(s, x, ak, av)
+    ck, cv = _gpu_project(s, x, ak, av)
     rows = None if w.batch <= 16 else np.random.default_rng(idx).choice(w.batch, 8, replace=False)
     _check_bound(ck, x.float(), ak, rows)
     _check_bound(cv, x.float(), av, rows)
@@ -135,12 +169,12 @@ def test_project_many_tokens_and_is_deterministic():
     x = lrgen.normal(lrgen.stream_key(12, 0), 0, T * E, 1.0).view(T, E).to(torch.bfloat16)
     ak = _factors(E, ranks_k, lrgen.stream_key(12, 1), 1 / math.sqrt(E))
     av = _factors(E, ranks_v, lrgen.stream_key(12, 2), 1 / math.sqrt(E))
-    ck, cv, wk, wv = _gpu_project(s, x, ak, av)
+    ck, cv = _gpu_project(s, x, ak, av)
     rows = np.random.default_rng(0).choice(T, 24, replace=False)
     rows = np.concatenate([rows, [0, 63, 64, 999]])
     _check_bound(ck, x.float(), ak, rows)
     _check_bound(cv, x.float(), av, rows)
-    ck2, cv2 = s.project(0, x.to(DEV), wk, wv)
+    ck2, cv2 = s.project(0, x.to(DEV))
     torch.cuda.synchronize()
     assert np.array_equal(ck, ck2.cpu().numpy()) and np.array_equal(cv, cv2.cpu().numpy())
 
@@ -152,8 +186,6 @@ def test_project_append_equals_project_then_append(qfmt):
     E, ranks_k, ranks_v, B = 512, [8, 64, 32, 96], [40, 16, 128, 8], 3
     ak = _factors(E, ranks_k, lrgen.stream_key(13, 1), 1 / math.sqrt(E))
     av = _factors(E, ranks_v, lrgen.stream_key(13, 2), 1 / math.sqrt(E))
-    wk = ak.t().contiguous().to(torch.bfloat16).to(DEV)
-    wv = av.t().contiguous().to(torch.bfloat16).to(DEV)
     for n_new in (1, 5, 70):
         say(f"project_append qfmt={qfmt} n_new={n_new}")
         x = lrgen.normal(lrgen.stream_key(13, n_new), 0, B * n_new * E, 1.0).view(B, n_new, E)
@@ -161,8 +193,10 @@ def test_project_append_equals_project_then_append(qfmt):
         pos = torch.tensor([0, 3, 60][:B], dtype=torch.int32, device=DEV)
         a = _session(ranks_k, ranks_v, qfmt, batch=B, cap=140)
         b = _session(ranks_k, ranks_v, qfmt, batch=B, cap=140)
-        a.project_append(0, x, wk, wv, pos)
-        ck, cv = b.project(0, x, wk, wv)
+        _set_factors(a, ak, av)
+        _set_factors(b, ak, av)
+        a.project_append(0, x, pos)
+        ck, cv = b.project(0, x)
         b.append(0, ck, cv, pos)
         torch.cuda.synchronize()
         assert torch.equal(a.caches[0], b.caches[0])
@@ -180,10 +214,9 @@ def test_project_append_codes_are_roundings_of_oracle_latents(qfmt):
     w, x, ak, av = _workload_inputs(w.index, B)
     ranks_k, ranks_v = w.ranks_k[0], w.ranks_v[0]
     s = _session(ranks_k, ranks_v, qfmt, batch=B, cap=64)
-    wk = ak.t().contiguous().to(torch.bfloat16).to(DEV)
-    wv = av.t().contiguous().to(torch.bfloat16).to(DEV)
+    _set_factors(s, ak, av)
     pos = torch.full((B,), 5, dtype=torch.int32, device=DEV)
-    s.project_append(0, x.view(B, 1, -1).to(DEV), wk, wv, pos)
+    s.project_append(0, x.view(B, 1, -1).to(DEV), pos)
     torch.cuda.synchronize()
     cache = s.caches[0].cpu().numpy()
     E = w.embed
@@ -232,13 +265,12 @@ def test_decode_over_generated_latents_matches_oracle_chain():
     bk = lrgen.up_factors(w, 0, 0).to(DEV).contiguous()
     bv = lrgen.up_factors(w, 0, 1).to(DEV).contiguous()
     s.set_factors(0, bk, bv)
-    wk = ak.t().contiguous().to(torch.bfloat16).to(DEV)
-    wv = av.t().contiguous().to(torch.bfloat16).to(DEV)
+    _set_factors(s, ak, av)
     xs = torch.stack([lrgen.activations(w, 0, b, 0, ctx + steps) for b in range(B)]).to(torch.bfloat16)
     for t0 in range(0, ctx, 40):
         t1 = min(ctx, t0 + 40)
         pos = torch.full((B,), t0, dtype=torch.int32, device=DEV)
-        s.project_append(0, xs[:, t0:t1].contiguous().to(DEV), wk, wv, pos)
+        s.project_append(0, xs[:, t0:t1].contiguous().to(DEV), pos)
     ref_k = [oracle.latents(xs[b].double().numpy(), ak.double().numpy()).astype(np.float32) for b in range(B)]
     ref_v = [oracle.latents(xs[b].double().numpy(), av.double().numpy()).astype(np.float32) for b in range(B)]
     scale = 1.0 / math.sqrt(w.head_dim)
@@ -247,7 +279,7 @@ def test_decode_over_generated_latents_matches_oracle_chain():
         T = ctx + st + 1
         q = lrgen.normal(lrgen.stream_key(w.seed, lrgen.TAG_Q, 0, st), 0, B * H * w.head_dim, 1.0)
         q = q.view(B, H, w.head_dim).to(torch.bfloat16).to(DEV).contiguous()
-        ck, cv = s.project(0, xs[:, ctx + st].contiguous().to(DEV), wk, wv)
+        ck, cv = s.project(0, xs[:, ctx + st].contiguous().to(DEV))
         pos = torch.full((B,), ctx + st, dtype=torch.int32, device=DEV)
         out = torch.empty(B, H, w.head_dim, dtype=torch.bfloat16, device=DEV)
         s.lengths.fill_(T)
