@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCE = os.path.join(ROOT, "latent_kv_attention_lr_amd", "csrc", "kernels.hip")
+PROJECT_SOURCE = os.path.join(ROOT, "latent_kv_attention_lr_amd", "csrc", "project.hip")
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -40,6 +41,19 @@ def measured_traffic(workload_name, kernel_form):
         d = json.load(open(f))
         if d.get("workload") == workload_name and d.get("decode_form") == kernel_form \
                 and d.get("kernels_hip_sha256") == src:
+            return d["hbm_bytes_per_launch"]
+    return None
+
+
+def measured_projection_traffic(workload_name):
+    """HBM bytes per latent-generation launch from committed counter runs, if
+    they were taken on the current projection source (else None)."""
+    import hashlib
+    src = hashlib.sha256(open(PROJECT_SOURCE, "rb").read()).hexdigest()
+    f = os.path.join(TRAFFIC_DIR, f"traffic_{workload_name}_project.json")
+    if os.path.exists(f):
+        d = json.load(open(f))
+        if d.get("project_hip_sha256") == src:
             return d["hbm_bytes_per_launch"]
     return None
 
@@ -381,6 +395,7 @@ def main():
             "frac": pbytes / pw_s / 1e9 / PEAK_HBM_GBS,
             "cold_avg_launch_us": pc_s * 1e6, "cold_achieved": pbytes / pc_s / 1e9,
             "cold_frac": pbytes / pc_s / 1e9 / PEAK_HBM_GBS,
+            "traffic": measured_projection_traffic(w.name),
             "flops_per_launch": 2.0 * w.batch * w.embed * sum(sum(rk_all[l]) + sum(rv_all[l])
                                                               for l in range(L)) / L,
         }
