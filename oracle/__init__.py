@@ -67,6 +67,12 @@ def lib() -> ctypes.CDLL:
         L.lro_attend_dequantised.restype = ctypes.c_int
         L.lro_latents.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P]
         L.lro_latents.restype = ctypes.c_int
+        L.lro_hadamard.argtypes = [ctypes.c_int, P]
+        L.lro_hadamard.restype = ctypes.c_int
+        L.lro_block_rotation.argtypes = [ctypes.c_int, ctypes.c_int, P]
+        L.lro_block_rotation.restype = ctypes.c_int
+        L.lro_rotate_factors.argtypes = [ctypes.c_int] * 4 + [P] * 4
+        L.lro_rotate_factors.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -163,3 +169,34 @@ def latents(x: np.ndarray, a: np.ndarray) -> np.ndarray:
     if lib().lro_latents(T, E, N, _ptr(x), _ptr(a), _ptr(c)) != 0:
         raise ValueError("lro_latents rejected its arguments")
     return c
+
+
+def hadamard(n: int) -> np.ndarray:
+    """Normalised Sylvester-Hadamard matrix of order n (a power of two)."""
+    h = np.zeros((n, n), dtype=np.float64)
+    if lib().lro_hadamard(n, _ptr(h)) != 0:
+        raise ValueError("n must be a power of two")
+    return h
+
+
+def block_rotation(r: int, block: int) -> Tuple[np.ndarray, int]:
+    """(S, g): the r x r block-diagonal Hadamard rotation of a rank-r head and its block."""
+    s = np.zeros((r, r), dtype=np.float64)
+    g = lib().lro_block_rotation(r, block, _ptr(s))
+    if g < 0:
+        raise ValueError("bad rank or block")
+    return s, g
+
+
+def rotate_factors(a: np.ndarray, b: np.ndarray, block: int) -> Tuple[np.ndarray, np.ndarray]:
+    """(A S, S^T B) for one head: A [E, r], B [r, d]."""
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    b = np.ascontiguousarray(b, dtype=np.float64)
+    E, r = a.shape
+    r2, d = b.shape
+    assert r == r2
+    ao = np.zeros_like(a)
+    bo = np.zeros_like(b)
+    if lib().lro_rotate_factors(E, r, d, block, _ptr(a), _ptr(b), _ptr(ao), _ptr(bo)) < 0:
+        raise ValueError("lro_rotate_factors rejected its arguments")
+    return ao, bo

@@ -143,6 +143,73 @@ int lro_latents(int T, int E, int N, const double* x, const double* a, double* c
   return 0;
 }
 
+// Outlier smoothing by an orthogonal rotation between the factors (WSVD page,
+// "Quantisation": orthogonal S_1, S_2 with S_1 a Hadamard matrix smooth
+// channel outliers of the latent; LASER page, "Hybrid SVD-quantisation": a
+// rotation inserted between the SVD factors before RTN).  With S orthogonal,
+// W = A B = (A S)(S^T B): the latent becomes c S and the product is unchanged.
+//
+// Normalised Sylvester-Hadamard matrix of order n (a power of two):
+// H_1 = [1], H_2k = [[H_k, H_k], [H_k, -H_k]], then scaled by 1/sqrt(n), so
+// that H H^T = I.  Returns 0, or -1 if n is not a power of two.
+int lro_hadamard(int n, double* h) {
+  if (n < 1 || (n & (n - 1)) != 0) return -1;
+  h[0] = 1.0;
+  for (int k = 1; k < n; k *= 2) {
+    // grow the top-left k x k block (row stride n) into 2k x 2k
+    for (int i = 0; i < k; ++i)
+      for (int j = 0; j < k; ++j) {
+        const double v = h[static_cast<size_t>(i) * n + j];
+        h[static_cast<size_t>(i) * n + j + k] = v;
+        h[static_cast<size_t>(i + k) * n + j] = v;
+        h[static_cast<size_t>(i + k) * n + j + k] = -v;
+      }
+  }
+  const double sc = 1.0 / std::sqrt(static_cast<double>(n));
+  for (size_t i = 0; i < static_cast<size_t>(n) * n; ++i) h[i] *= sc;
+  return 0;
+}
+
+// The rotation of a rank-r head: block-diagonal with blocks H_g, g the
+// largest power of two that divides r and does not exceed `block` (a power of
+// two); s is r x r.  Returns g, or -1 on bad arguments.
+int lro_block_rotation(int r, int block, double* s) {
+  if (r < 1 || block < 1 || (block & (block - 1)) != 0) return -1;
+  int g = 1;
+  while (g * 2 <= block && r % (g * 2) == 0) g *= 2;
+  std::vector<double> h(static_cast<size_t>(g) * g);
+  lro_hadamard(g, h.data());
+  for (size_t i = 0; i < static_cast<size_t>(r) * r; ++i) s[i] = 0.0;
+  for (int b0 = 0; b0 < r; b0 += g)
+    for (int i = 0; i < g; ++i)
+      for (int j = 0; j < g; ++j)
+        s[static_cast<size_t>(b0 + i) * r + b0 + j] = h[static_cast<size_t>(i) * g + j];
+  return g;
+}
+
+// The rotated factors of one head: a_out = a S (E x r), b_out = S^T b (r x d),
+// S = lro_block_rotation(r, block), by plain products in fp64.  Returns g, or -1.
+int lro_rotate_factors(int E, int r, int d, int block, const double* a, const double* b,
+                       double* a_out, double* b_out) {
+  if (E < 1 || d < 1) return -1;
+  std::vector<double> s(static_cast<size_t>(r) * r);
+  const int g = lro_block_rotation(r, block, s.data());
+  if (g < 0) return -1;
+  for (int e = 0; e < E; ++e)
+    for (int j = 0; j < r; ++j) {
+      double acc = 0.0;
+      for (int i = 0; i < r; ++i) acc += a[static_cast<size_t>(e) * r + i] * s[static_cast<size_t>(i) * r + j];
+      a_out[static_cast<size_t>(e) * r + j] = acc;
+    }
+  for (int i = 0; i < r; ++i)
+    for (int c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int j = 0; j < r; ++j) acc += s[static_cast<size_t>(j) * r + i] * b[static_cast<size_t>(j) * d + c];
+      b_out[static_cast<size_t>(i) * d + c] = acc;
+    }
+  return g;
+}
+
 // Quantise and dequantise one row: out_i = scale * q_i in fp64 (exact).
 // qfmt: 0 = int8 per token, 1 = int4 group 32, 2 = no quantisation (out = c).
 static void dequantised_row(int qfmt, const float* c, int r, double* out) {

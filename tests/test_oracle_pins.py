@@ -386,3 +386,65 @@ def test_empty_context_gives_zero():
     o = oracle.attend(oracle.QFMT_INT8, np.zeros((0, 8), np.float32), np.zeros((0, 8), np.float32),
                       np.ones(16), np.ones((8, 16)), np.ones((8, 16)), 0.25)
     assert np.array_equal(o, np.zeros(16))
+
+
+# --------------------------------------------------------------------------
+# Rotation between the factors (Hadamard outlier smoothing)
+# --------------------------------------------------------------------------
+
+def test_hadamard_small_orders_by_hand():
+    s2 = 1 / math.sqrt(2)
+    assert np.array_equal(oracle.hadamard(1), np.array([[1.0]]))
+    assert np.allclose(oracle.hadamard(2), np.array([[s2, s2], [s2, -s2]]), rtol=0, atol=1e-16)
+    h4 = np.array([[1, 1, 1, 1], [1, -1, 1, -1], [1, 1, -1, -1], [1, -1, -1, 1]]) / 2.0
+    assert np.array_equal(oracle.hadamard(4), h4)
+    with pytest.raises(ValueError):
+        oracle.hadamard(12)
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16, 32, 64, 128])
+def test_hadamard_is_orthogonal_and_matches_scipy(n):
+    import scipy.linalg
+    h = oracle.hadamard(n)
+    assert np.max(np.abs(h @ h.T - np.eye(n))) <= 1e-14
+    assert np.all(np.abs(np.abs(h) * math.sqrt(n) - 1.0) <= 1e-14)
+    assert np.allclose(h, scipy.linalg.hadamard(n) / math.sqrt(n), rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("r,block,g", [(8, 32, 8), (16, 32, 16), (24, 32, 8), (40, 32, 8), (48, 32, 16),
+                                       (64, 32, 32), (96, 32, 32), (128, 32, 32), (128, 128, 128),
+                                       (96, 128, 32), (64, 8, 8)])
+def test_block_rotation_structure(r, block, g):
+    """Blocks of the largest power of two dividing r, capped at the block size;
+    block-diagonal, orthogonal, zero off the blocks."""
+    s, got = oracle.block_rotation(r, block)
+    assert got == g
+    assert np.max(np.abs(s @ s.T - np.eye(r))) <= 1e-14
+    h = oracle.hadamard(g)
+    for b0 in range(0, r, g):
+        assert np.array_equal(s[b0:b0 + g, b0:b0 + g], h)
+    mask = np.kron(np.eye(r // g), np.ones((g, g))).astype(bool)
+    assert np.all(s[~mask] == 0.0)
+
+
+def test_rotated_factors_keep_the_product_and_rotate_the_latent():
+    """(A S)(S^T B) = A B, the latent becomes c S, and full-rank unquantised
+    attention through the rotated factors still equals dense attention."""
+    rng = np.random.default_rng(31)
+    E, r, d, T = 64, 48, 48, 5
+    a = rng.standard_normal((E, r))
+    b = rng.standard_normal((r, d))
+    ar, br = oracle.rotate_factors(a, b, 32)
+    s, _ = oracle.block_rotation(r, 32)
+    assert np.max(np.abs(ar @ br - a @ b)) <= 1e-12 * np.max(np.abs(a @ b))
+    x = rng.standard_normal((T, E))
+    assert np.max(np.abs(oracle.latents(x, ar) - oracle.latents(x, a) @ s)) <= 1e-12 * 10
+    # full rank (r = d): rotated, unquantised attention equals dense attention
+    W = rng.standard_normal((E, d)) / 4
+    U, S, Vt = np.linalg.svd(W, full_matrices=False)
+    A, B = U * np.sqrt(S), np.sqrt(S)[:, None] * Vt
+    Ar, Br = oracle.rotate_factors(A, B, 32)
+    q = rng.standard_normal(d)
+    got = oracle.attend_dequantised(oracle.latents(x, Ar), oracle.latents(x, Ar), q, Br, Br, 0.2)
+    want = _dense_mha(x, W, W, q, 0.2)
+    assert np.max(np.abs(got - want)) <= 1e-12 * max(1.0, np.max(np.abs(want)))
