@@ -267,6 +267,32 @@ lr_status lr_attn_project_append(const lr_attn_plan* plan, int32_t layer, void* 
                                  const int32_t* pos, int32_t n_new, void* workspace,
                                  size_t ws_bytes, void* stream);
 
+/* Outlier smoothing by a rotation between the factors (WSVD page,
+ * "Quantisation": orthogonal S_1, S_2, S_1 a Hadamard matrix, smooth channel
+ * outliers of the latent; LASER page, "Hybrid SVD-quantisation": a rotation
+ * inserted between the SVD factors before RTN).  For an orthogonal S,
+ * A B = (A S)(S^T B): folded into the factors once, the cached latent becomes
+ * c S and no kernel changes.  S is block-diagonal per head with normalised
+ * Sylvester-Hadamard blocks H_g (entries +-1/sqrt(g), H_g = H_g^T), g the
+ * largest power of two that divides the head's rank and is <= block.  Host
+ * functions (no device memory, no stream); they are meant for the offline
+ * factors, before conversion to bf16. */
+
+/* g for head `head` of layer `layer`, K (kv = 0) or V (kv = 1); 0 on bad
+ * arguments (block must be a power of two in [8, 128]). */
+int32_t lr_attn_hadamard_block(const lr_attn_plan* plan, int32_t layer, int32_t kv, int32_t head,
+                               int32_t block);
+
+/* Replace every head's rows of `rows` (HOST fp32, [latent_elems(kv)][cols]
+ * row-major, head h's r_h rows at its latent offset) by S_h^T times them, in
+ * fp64, rounded once to fp32.  Applied to A^T ([latent_elems][E], the layout
+ * lr_attn_pack_projection takes) and to B ([latent_elems][128], the decode
+ * factors) it folds the rotation: latents c S, product unchanged.  Applying
+ * it twice restores the rows (S^2 = I) up to rounding.
+ * Errors: LR_EINVAL (null pointer, kv, block, cols < 1), LR_ERANGE (layer). */
+lr_status lr_attn_hadamard_rotate_rows(const lr_attn_plan* plan, int32_t layer, int32_t kv,
+                                       int32_t block, float* rows, int64_t cols);
+
 /* Measurement aid, not part of the decode path: streams bytes / 16 16-byte
  * words from device memory src (16-byte aligned, bytes >= 16; a trailing
  * partial word is not read) with a plain grid-stride read kernel, the

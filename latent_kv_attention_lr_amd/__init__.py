@@ -95,6 +95,8 @@ def _load() -> ctypes.CDLL:
         "lr_attn_project_latent": (ctypes.c_int, [P, I32, P, I32, I32, P, P, P, P]),
         "lr_attn_project_workspace_bytes": (SZ, [P, I32]),
         "lr_attn_project_append": (ctypes.c_int, [P, I32, P, P, I32, P, P, I32, P, SZ, P]),
+        "lr_attn_hadamard_block": (I32, [P, I32, I32, I32, I32]),
+        "lr_attn_hadamard_rotate_rows": (ctypes.c_int, [P, I32, I32, I32, P, ctypes.c_int64]),
         "lr_attn_probe_read": (ctypes.c_int, [P, SZ, P, P]),
         "lr_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "lr_attn_last_hip_error": (I32, []),
@@ -239,6 +241,30 @@ def lr_attn_project_append(plan: int, layer: int, cache, x, embed: int, packed, 
     _check(_lib.lr_attn_project_append(plan, layer, _ptr(cache), _ptr(x), embed, _ptr(packed),
                                        _ptr(pos), n_new, _ptr(workspace), ws_bytes, _stream(stream)),
            "lr_attn_project_append")
+
+
+def lr_attn_hadamard_block(plan: int, layer: int, kv: int, head: int, block: int) -> int:
+    return int(_lib.lr_attn_hadamard_block(plan, layer, kv, head, block))
+
+
+def lr_attn_hadamard_rotate_rows(plan: int, layer: int, kv: int, block: int, rows) -> None:
+    """Fold the per-head block-Hadamard rotation into host fp32 rows
+    [latent_elems(kv), cols] in place (a numpy array or a CPU torch tensor)."""
+    import numpy as np
+    if isinstance(rows, np.ndarray):
+        if rows.dtype != np.float32 or rows.ndim != 2 or not rows.flags.c_contiguous:
+            raise ValueError("rows must be a C-contiguous float32 [latent_elems, cols] array")
+        ptr, cols = rows.ctypes.data, rows.shape[1]
+    else:
+        import torch
+        if rows.device.type != "cpu" or rows.dtype != torch.float32 or rows.dim() != 2 \
+                or not rows.is_contiguous():
+            raise ValueError("rows must be a contiguous CPU float32 [latent_elems, cols] tensor")
+        ptr, cols = rows.data_ptr(), rows.shape[1]
+    if rows.shape[0] != lr_attn_latent_elems(plan, layer, kv):
+        raise ValueError("rows must have latent_elems(kv) rows")
+    _check(_lib.lr_attn_hadamard_rotate_rows(plan, layer, kv, block, ptr, cols),
+           "lr_attn_hadamard_rotate_rows")
 
 
 def lr_attn_probe_read(src, nbytes: int, sink, stream=None) -> None:

@@ -256,6 +256,24 @@ def up_factors(w: Workload, layer: int, kv: int, dtype=torch.bfloat16, device="c
     return torch.cat(rows, dim=0).to(dtype)
 
 
+def svd_like_factors(w: Workload, layer: int, kv: int, alpha: float = 1.0,
+                     device="cpu") -> Tuple[torch.Tensor, torch.Tensor]:
+    """Factors shaped like a truncated SVD, A_h = G_h diag(sqrt(s)), B_h =
+    diag(sqrt(s)) G'_h, with G, G' the workload's own draws (down_factors,
+    fp32 up_factors) and singular values s_j proportional to (j + 1)^-alpha,
+    normalised to mean 1 per head.  Returns (A [E, sum r] fp32, B [sum r, d] fp32).
+    alpha = 0 gives the workload's iid factors."""
+    ranks = w.ranks_k[layer] if kv == 0 else w.ranks_v[layer]
+    a = down_factors(w, layer, kv, device)
+    b = up_factors(w, layer, kv, dtype=torch.float32, device=device)
+    scale = []
+    for r in ranks:
+        s = torch.arange(1, r + 1, dtype=torch.float64) ** (-alpha)
+        scale.append(torch.sqrt(s / s.mean()))
+    sc = torch.cat(scale).to(torch.float32).to(device)
+    return a * sc[None, :], b * sc[:, None]
+
+
 def queries(w: Workload, layer: int, step: int, dtype=torch.bfloat16, device="cpu") -> torch.Tensor:
     """q for one decode step: [B, H, d] ~ N(0, 1), rounded to ``dtype``."""
     key = stream_key(w.seed, TAG_Q, layer, step)
