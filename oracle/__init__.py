@@ -73,6 +73,9 @@ def lib() -> ctypes.CDLL:
         L.lro_block_rotation.restype = ctypes.c_int
         L.lro_rotate_factors.argtypes = [ctypes.c_int] * 4 + [P] * 4
         L.lro_rotate_factors.restype = ctypes.c_int
+        L.lro_allocate_ranks.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_double,
+                                         ctypes.c_double, P]
+        L.lro_allocate_ranks.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -200,3 +203,17 @@ def rotate_factors(a: np.ndarray, b: np.ndarray, block: int) -> Tuple[np.ndarray
     if lib().lro_rotate_factors(E, r, d, block, _ptr(a), _ptr(b), _ptr(ao), _ptr(bo)) < 0:
         raise ValueError("lro_rotate_factors rejected its arguments")
     return ao, bo
+
+
+def allocate_ranks(scores: np.ndarray, step: int, cost_per_component: float, budget: float) -> np.ndarray:
+    """Greedy rank allocation: scores [n_units, max_rank] (fp64) -> ranks [n_units] (int)."""
+    scores = np.ascontiguousarray(scores, dtype=np.float64)
+    n, m = scores.shape
+    ranks = np.zeros(n, dtype=np.int32)
+    rc = lib().lro_allocate_ranks(n, m, step, _ptr(scores), float(cost_per_component), float(budget),
+                                  _ptr(ranks))
+    if rc == -2:
+        raise ValueError("budget below one block per unit")
+    if rc != 0:
+        raise ValueError("lro_allocate_ranks rejected its arguments")
+    return ranks

@@ -210,6 +210,45 @@ int lro_rotate_factors(int E, int r, int d, int block, const double* a, const do
   return g;
 }
 
+// Greedy global rank allocation (LASER page, "Loss-aware cross-layer rank
+// allocation": singular components are chosen greedily by importance score
+// per parameter cost until a parameter budget is met, giving non-uniform
+// ranks across layers and heads).  Units: (layer, head, K or V), n_units of
+// them, each with up to max_rank components scored scores[u * max_rank + j]
+// (component j of unit u, in the head's singular-value order).  Readings:
+// a unit's rank is a prefix of its components, taken in blocks of `step`
+// components (the kernels' rank granularity) whose score is the sum of the
+// block's component scores; every unit starts at one block; a block costs
+// step * cost_per_component parameters.  Each round takes, over all units,
+// the next block with the highest score per parameter (ties: the lowest unit
+// index), as long as it fits in what is left of the budget; the first block
+// that does not fit ends the allocation.  ranks[u] receives the rank.
+// Returns 0, or -1 on bad sizes, -2 if the budget is below one block per unit.
+int lro_allocate_ranks(int n_units, int max_rank, int step, const double* scores,
+                       double cost_per_component, double budget, int* ranks) {
+  if (n_units < 1 || step < 1 || max_rank < step || max_rank % step != 0 || !(cost_per_component > 0))
+    return -1;
+  const double block_cost = step * cost_per_component;
+  double used = n_units * block_cost;
+  if (used > budget) return -2;
+  for (int u = 0; u < n_units; ++u) ranks[u] = step;
+  for (;;) {
+    int best = -1;
+    double best_v = 0.0;
+    for (int u = 0; u < n_units; ++u) {
+      if (ranks[u] >= max_rank) continue;
+      double v = 0.0;
+      for (int j = ranks[u]; j < ranks[u] + step; ++j) v += scores[static_cast<size_t>(u) * max_rank + j];
+      v /= block_cost;
+      if (best < 0 || v > best_v) { best = u; best_v = v; }
+    }
+    if (best < 0 || used + block_cost > budget) break;
+    ranks[best] += step;
+    used += block_cost;
+  }
+  return 0;
+}
+
 // Quantise and dequantise one row: out_i = scale * q_i in fp64 (exact).
 // qfmt: 0 = int8 per token, 1 = int4 group 32, 2 = no quantisation (out = c).
 static void dequantised_row(int qfmt, const float* c, int r, double* out) {

@@ -448,3 +448,68 @@ def test_rotated_factors_keep_the_product_and_rotate_the_latent():
     got = oracle.attend_dequantised(oracle.latents(x, Ar), oracle.latents(x, Ar), q, Br, Br, 0.2)
     want = _dense_mha(x, W, W, q, 0.2)
     assert np.max(np.abs(got - want)) <= 1e-12 * max(1.0, np.max(np.abs(want)))
+
+
+# --------------------------------------------------------------------------
+# Greedy global rank allocation
+# --------------------------------------------------------------------------
+
+def test_allocation_hand_worked():
+    """Units with block sums (10, 2) and (6, 4) at step 2: from one block each
+    (cost 4 of 6), the one block left goes to the larger next block (4 > 2);
+    with room for both, both; with room for nothing more, none."""
+    s = np.array([[5, 5, 1, 1], [3, 3, 2, 2.0]])
+    assert oracle.allocate_ranks(s, 2, 1.0, 6).tolist() == [2, 4]
+    assert oracle.allocate_ranks(s, 2, 1.0, 8).tolist() == [4, 4]
+    assert oracle.allocate_ranks(s, 2, 1.0, 5.9).tolist() == [2, 2]
+    with pytest.raises(ValueError):
+        oracle.allocate_ranks(s, 2, 1.0, 3.9)
+
+
+def test_allocation_ties_go_to_the_lowest_unit():
+    s = np.ones((3, 32))
+    assert oracle.allocate_ranks(s, 8, 1.0, 8 * 3 + 8 * 3).tolist() == [32, 8, 8]
+    assert oracle.allocate_ranks(s, 8, 1.0, 8 * 3 + 8 * 4).tolist() == [32, 16, 8]
+
+
+def _brute_force_best(block_vals, n_blocks, extra):
+    """Best total block value over all prefix assignments using at most `extra`
+    extra blocks (every unit keeps its first block)."""
+    import itertools
+    best = -1.0
+    n = len(block_vals)
+    for take in itertools.product(range(n_blocks), repeat=n):
+        if sum(take) > extra:
+            continue
+        best = max(best, sum(sum(block_vals[u][1:1 + take[u]]) for u in range(n)))
+    return best
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_allocation_is_optimal_for_non_increasing_scores(seed):
+    """With every unit's block values non-increasing (scores follow the
+    singular values) and equal block costs, greedy picks the best prefix
+    assignment: its total equals brute force over all assignments."""
+    rng = np.random.default_rng(seed)
+    n, step, m = 5, 2, 8                       # 5 units, 4 blocks each
+    comp = -np.sort(-rng.exponential(1.0, (n, m)), axis=1) * rng.uniform(0.2, 3.0, (n, 1))
+    blocks = comp.reshape(n, m // step, step).sum(axis=2)
+    for extra in range(0, n * (m // step - 1) + 1, 3):
+        ranks = oracle.allocate_ranks(comp, step, 1.0, step * (n + extra))
+        assert int(ranks.sum()) == step * (n + min(extra, n * (m // step - 1)))
+        got = sum(blocks[u, 1:ranks[u] // step].sum() for u in range(n))
+        assert abs(got - _brute_force_best(blocks.tolist(), m // step, extra)) <= 1e-12
+
+
+def test_allocation_grows_with_the_budget_and_respects_it():
+    rng = np.random.default_rng(9)
+    s = rng.exponential(1.0, (40, 128))          # not monotone within units
+    prev = None
+    for budget in np.linspace(40 * 8 * 136, 40 * 128 * 136, 13):
+        r = oracle.allocate_ranks(s, 8, 136.0, budget)
+        assert np.all(r % 8 == 0) and np.all(r >= 8) and np.all(r <= 128)
+        assert r.sum() * 136.0 <= budget + 1e-9
+        if prev is not None:
+            assert np.all(r >= prev)
+        prev = r
+    assert np.all(oracle.allocate_ranks(s, 8, 136.0, 40 * 128 * 136) == 128)
