@@ -72,6 +72,10 @@ def parse():
                          "(lr_attn_project_latent) before the fused append + decode")
     ap.add_argument("--no-projection-leg", action="store_true",
                     help="skip the separate latent-generation measurement")
+    ap.add_argument("--allocate-ranks", type=int, default=0, metavar="MEAN",
+                    help="replace the workload's rank table by the greedy allocation "
+                         "(lr_attn_allocate_ranks) of synthetic component scores under a budget "
+                         "of MEAN ranks per head and K/V")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=16,
                     help="extra untimed-in-value steps with the 256 MiB last-level cache flushed before each")
@@ -165,6 +169,21 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     w = lrgen.workload(args.workload)
+    alloc_info = None
+    if args.allocate_ranks:
+        from latent_kv_attention_lr_amd import lr_attn_allocate_ranks
+        cost = w.embed + w.head_dim
+        budget = w.n_layers * w.n_heads * 2 * args.allocate_ranks * cost
+        scores = lrgen.component_scores(w.seed, w.n_layers, w.n_heads).numpy()
+        t_alloc = time.perf_counter()
+        rk, rv = lr_attn_allocate_ranks(scores, cost, budget)
+        t_alloc = time.perf_counter() - t_alloc
+        w.ranks_k, w.ranks_v, w.uniform_rank = rk.tolist(), rv.tolist(), None
+        w.name += f"-allocated-mean{args.allocate_ranks}"
+        alloc_info = {"entry_point": "lr_attn_allocate_ranks", "scores": "synthetic (lrgen.component_scores)",
+                      "budget_params": budget, "mean_rank": args.allocate_ranks,
+                      "rank_min": int(min(rk.min(), rv.min())), "rank_max": int(max(rk.max(), rv.max())),
+                      "host_ms": t_alloc * 1e3}
     steps = w.steps if args.steps is None else args.steps
     warm = args.warmup
     if args.profile_steps:
@@ -321,7 +340,8 @@ def main():
         "config": {
             "workload": w.name,
             "layers": L, "batch": w.batch, "heads": w.n_heads, "head_dim": w.head_dim,
-            "rank": "per-head table" if w.uniform_rank is None else w.uniform_rank,
+            "rank": ("greedy allocation" if alloc_info else "per-head table") if w.uniform_rank is None
+                    else w.uniform_rank,
             "context": ctx, "image_prefix": w.prefix,
             "latents": "int8 per-token fp32 scale" if w.qfmt == 0 else "int4 group-32 fp16 scale",
             "q_factors_out": "bf16", "accumulation": "f32",
@@ -463,6 +483,8 @@ def main():
             "achieved_vs_probe": achieved / probe_gbs}
         del buf, sink
 
+    if alloc_info:
+        result["rank_allocation"] = alloc_info
     if keep:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cb = cpu_baseline(run, n_cpu)

@@ -293,6 +293,30 @@ int32_t lr_attn_hadamard_block(const lr_attn_plan* plan, int32_t layer, int32_t 
 lr_status lr_attn_hadamard_rotate_rows(const lr_attn_plan* plan, int32_t layer, int32_t kv,
                                        int32_t block, float* rows, int64_t cols);
 
+/* Greedy global rank allocation (LASER page, "Loss-aware cross-layer rank
+ * allocation": singular components are taken greedily by importance score
+ * per parameter cost until a parameter budget is met).  Host function; its
+ * output is the rank table of lr_attn_desc.
+ *   scores   HOST fp32 [n_layers][n_heads][2][max_rank]: the importance of
+ *            component j (in singular-value order) of K (index 0) or V (1) of
+ *            each head; finite
+ *   max_rank 8..128, a multiple of 8: components available per head
+ *   cost_per_rank  parameters one component costs (E + head_dim: a column of
+ *            A and a row of B), >= 1
+ *   budget   parameters for all K and V factors of all layers
+ *   rank_k, rank_v  HOST int32 [n_layers * n_heads], written
+ * Ranks are multiples of 8 (the kernels' granularity) and prefixes of the
+ * components: every head starts at 8; then, while the next block fits the
+ * budget, the block of 8 components with the highest summed score per
+ * parameter over all heads is added (ties: the lower (layer, head, K/V)
+ * index).  Allocation stops at the first best block that does not fit.
+ * Errors: LR_EINVAL (null pointer, non-finite score, sizes, cost < 1),
+ * LR_EUNSUPPORTED (max_rank), LR_ERANGE (budget below 8 components per head
+ * and K/V; more than 2^24 heads). */
+lr_status lr_attn_allocate_ranks(int32_t n_layers, int32_t n_heads, int32_t max_rank,
+                                 const float* scores, int64_t cost_per_rank, int64_t budget,
+                                 int32_t* rank_k, int32_t* rank_v);
+
 /* Measurement aid, not part of the decode path: streams bytes / 16 16-byte
  * words from device memory src (16-byte aligned, bytes >= 16; a trailing
  * partial word is not read) with a plain grid-stride read kernel, the

@@ -97,6 +97,7 @@ def _load() -> ctypes.CDLL:
         "lr_attn_project_append": (ctypes.c_int, [P, I32, P, P, I32, P, P, I32, P, SZ, P]),
         "lr_attn_hadamard_block": (I32, [P, I32, I32, I32, I32]),
         "lr_attn_hadamard_rotate_rows": (ctypes.c_int, [P, I32, I32, I32, P, ctypes.c_int64]),
+        "lr_attn_allocate_ranks": (ctypes.c_int, [I32, I32, I32, P, ctypes.c_int64, ctypes.c_int64, P, P]),
         "lr_attn_probe_read": (ctypes.c_int, [P, SZ, P, P]),
         "lr_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "lr_attn_last_hip_error": (I32, []),
@@ -265,6 +266,21 @@ def lr_attn_hadamard_rotate_rows(plan: int, layer: int, kv: int, block: int, row
         raise ValueError("rows must have latent_elems(kv) rows")
     _check(_lib.lr_attn_hadamard_rotate_rows(plan, layer, kv, block, ptr, cols),
            "lr_attn_hadamard_rotate_rows")
+
+
+def lr_attn_allocate_ranks(scores, cost_per_rank: int, budget: int):
+    """Greedy rank table from component scores (numpy float32 [L, H, 2, max_rank]):
+    returns (rank_k, rank_v) as int32 arrays [L, H]."""
+    import numpy as np
+    scores = np.ascontiguousarray(scores, dtype=np.float32)
+    if scores.ndim != 4 or scores.shape[2] != 2:
+        raise ValueError("scores must be [n_layers, n_heads, 2, max_rank]")
+    L, H, _, m = scores.shape
+    rk = np.zeros((L, H), dtype=np.int32)
+    rv = np.zeros((L, H), dtype=np.int32)
+    _check(_lib.lr_attn_allocate_ranks(L, H, m, scores.ctypes.data, int(cost_per_rank), int(budget),
+                                       rk.ctypes.data, rv.ctypes.data), "lr_attn_allocate_ranks")
+    return rk, rv
 
 
 def lr_attn_probe_read(src, nbytes: int, sink, stream=None) -> None:

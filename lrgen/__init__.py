@@ -274,6 +274,27 @@ def svd_like_factors(w: Workload, layer: int, kv: int, alpha: float = 1.0,
     return a * sc[None, :], b * sc[:, None]
 
 
+TAG_SCORE = 9
+
+
+def component_scores(seed: int, n_layers: int, n_heads: int, max_rank: int = 128) -> torch.Tensor:
+    """Synthetic importance scores standing in for empirical-Fisher ones:
+    fp32 [n_layers, n_heads, 2 (K, V), max_rank], component j of a head scored
+    g_l * a_h * (j + 1)^(-2 b_h) * n_j -- a per-layer sensitivity g_l and a
+    per-head gain a_h (both exp(N(0, 0.5^2))), a per-head spectral decay b_h
+    uniform in [0.3, 1.2] (squared singular values), and a per-component
+    factor n_j = exp(N(0, 0.2^2)) so that scores are only roughly monotone."""
+    key = stream_key(seed, TAG_SCORE)
+    L, H, m = n_layers, n_heads, max_rank
+    g = torch.exp(0.5 * normal(key, 0, L).double()).view(L, 1, 1, 1)
+    a = torch.exp(0.5 * normal(key, L, L * H * 2).double()).view(L, H, 2, 1)
+    u = uniform53(raw_draws(key, 10 ** 9, L * H * 2)).view(L, H, 2, 1)
+    b = 0.3 + 0.9 * u
+    j = torch.arange(1, m + 1, dtype=torch.float64).view(1, 1, 1, m)
+    n = torch.exp(0.2 * normal(key, L + L * H * 2, L * H * 2 * m).double()).view(L, H, 2, m)
+    return (g * a * j ** (-2.0 * b) * n).to(torch.float32)
+
+
 def queries(w: Workload, layer: int, step: int, dtype=torch.bfloat16, device="cpu") -> torch.Tensor:
     """q for one decode step: [B, H, d] ~ N(0, 1), rounded to ``dtype``."""
     key = stream_key(w.seed, TAG_Q, layer, step)
