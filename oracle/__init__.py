@@ -76,6 +76,10 @@ def lib() -> ctypes.CDLL:
         L.lro_allocate_ranks.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_double,
                                          ctypes.c_double, P]
         L.lro_allocate_ranks.restype = ctypes.c_int
+        L.lro_quant_act_groups.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P]
+        L.lro_quant_act_groups.restype = None
+        L.lro_ffn.argtypes = [ctypes.c_int] * 6 + [P] * 9
+        L.lro_ffn.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -217,3 +221,32 @@ def allocate_ranks(scores: np.ndarray, step: int, cost_per_component: float, bud
     if rc != 0:
         raise ValueError("lro_allocate_ranks rejected its arguments")
     return ranks
+
+
+def quant_act_groups(a: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Activations [T, K] -> (int8 codes [T, K], fp32 scales [T, ceil(K/64)]), one
+    scale per token per group of 64 elements."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    T, K = a.shape
+    q = np.empty((T, K), np.int8)
+    s = np.empty((T, (K + 63) // 64), np.float32)
+    lib().lro_quant_act_groups(_ptr(a), T, K, _ptr(q), _ptr(s))
+    return q, s
+
+
+def ffn(x, wg, wu, ag, au, bg, bu, wd, quantise: bool = True) -> np.ndarray:
+    """Hybrid FFN: x [T, E]; dense rows wg, wu [F-S, E]; factors ag, au [r, E],
+    bg, bu [S, r]; wd [E, F] (all fp32 values).  Returns y [T, E] in fp64."""
+    arrs = [np.ascontiguousarray(v, dtype=np.float32) for v in (x, wg, wu, ag, au, bg, bu, wd)]
+    x, wg, wu, ag, au, bg, bu, wd = arrs
+    T, E = x.shape
+    F = wd.shape[1]
+    S = bg.shape[0]
+    r = ag.shape[0]
+    assert wg.shape == (F - S, E) and wu.shape == (F - S, E) and wd.shape == (E, F)
+    assert ag.shape == (r, E) and au.shape == (r, E) and bg.shape == (S, r) and bu.shape == (S, r)
+    y = np.zeros((T, E), np.float64)
+    rc = lib().lro_ffn(0 if quantise else 1, T, E, F, S, r, *[_ptr(v) for v in arrs], _ptr(y))
+    if rc != 0:
+        raise ValueError("lro_ffn rejected its arguments")
+    return y

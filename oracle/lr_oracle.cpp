@@ -249,6 +249,135 @@ int lro_allocate_ranks(int n_units, int max_rank, int step, const double* scores
   return 0;
 }
 
+// ---------------------------------------------------------------------------
+// Hybrid low-rank / dense FFN with W8A8 round-to-nearest quantisation (LASER
+// page, "Hybrid SVD-quantisation for FFNs": SVD-friendly hidden channels of
+// the gate and up projections go through low-rank factors, the others stay
+// dense, and both branches are RTN-quantised; "System implementation": the
+// fused FFN kernel covers the input projection, the latent activations,
+// SwiGLU and quantisation / dequantisation).  Readings of what the pages
+// leave open: a LLaMA-style SwiGLU FFN y = W_d (silu(W_g x) * (W_u x)); hidden
+// channels [0, S) are the low-rank ones, W_g[S] ~ B_g A_g and W_u[S] ~ B_u A_u
+// with one rank r; W_d stays dense; weights are int8 with one fp32 scale per
+// row, activations (x, the latents z = A x, and h) are int8 with one fp32 scale
+// per token and per group of 64 consecutive elements along the reduction
+// dimension (the last group may be shorter); both use the int8 quantiser
+// above (s = max|v| / 127, rne, clamp).  Every dot product is taken group by
+// group: (exact integer sum) * activation scale, summed over groups, times the
+// weight scale.  z and h are rounded to fp32 before they are quantised.
+// qmode 0 = W8A8 as above, 1 = no quantisation anywhere (plain fp64 FFN).
+
+// Activations a [T][K] -> codes [T][K], scales [T][ceil(K / 64)].
+void lro_quant_act_groups(const float* a, int T, int K, int8_t* q, float* s) {
+  const int ng = (K + 63) / 64;
+  for (int t = 0; t < T; ++t)
+    for (int g = 0; g < ng; ++g) {
+      const int lo = 64 * g, n = (lo + 64 <= K ? 64 : K - lo);
+      lro_quant_int8(a + static_cast<size_t>(t) * K + lo, n, q + static_cast<size_t>(t) * K + lo,
+                     s + static_cast<size_t>(t) * ng + g);
+    }
+}
+
+namespace {
+
+// A quantised matrix (rows x cols, per-row scales) or its plain values.
+struct QMat {
+  int rows = 0, cols = 0;
+  std::vector<int8_t> q;
+  std::vector<float> s;
+  const float* w = nullptr;
+};
+
+QMat make_qmat(const float* w, int rows, int cols, int qmode) {
+  QMat m;
+  m.rows = rows;
+  m.cols = cols;
+  m.w = w;
+  if (qmode == 0) {
+    m.q.resize(static_cast<size_t>(rows) * cols);
+    m.s.resize(rows);
+    lro_quant_int8_rows(w, rows, cols, m.q.data(), m.s.data());
+  }
+  return m;
+}
+
+// out[t][n] = sum_k W[n][k] act[t][k] for an activation matrix act [T][K] given
+// as fp32 values; with qmode 0 the activations are quantised per (t, group)
+// and the products follow the group-by-group dequantisation above.
+void qmatmul(const QMat& W, const float* act, int T, int qmode, double* out) {
+  const int K = W.cols, N = W.rows, ng = (K + 63) / 64;
+  if (qmode == 1) {
+    for (int t = 0; t < T; ++t)
+      for (int n = 0; n < N; ++n) {
+        double acc = 0.0;
+        for (int k = 0; k < K; ++k)
+          acc += static_cast<double>(W.w[static_cast<size_t>(n) * K + k]) * act[static_cast<size_t>(t) * K + k];
+        out[static_cast<size_t>(t) * N + n] = acc;
+      }
+    return;
+  }
+  std::vector<int8_t> aq(static_cast<size_t>(T) * K);
+  std::vector<float> as(static_cast<size_t>(T) * ng);
+  lro_quant_act_groups(act, T, K, aq.data(), as.data());
+  for (int t = 0; t < T; ++t)
+    for (int n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int g = 0; g < ng; ++g) {
+        long long isum = 0;
+        for (int k = 64 * g; k < K && k < 64 * g + 64; ++k)
+          isum += static_cast<long long>(W.q[static_cast<size_t>(n) * K + k]) * aq[static_cast<size_t>(t) * K + k];
+        acc += static_cast<double>(isum) * as[static_cast<size_t>(t) * ng + g];
+      }
+      out[static_cast<size_t>(t) * N + n] = acc * W.s[n];
+    }
+}
+
+}  // namespace
+
+// Hybrid FFN on T tokens: x [T][E] (the activations' fp32 values), hidden F,
+// S low-rank channels of rank r.  Weights (row-major fp32, rows = outputs):
+// wg, wu [F - S][E] (dense gate / up rows of channels S..F-1), ag, au [r][E],
+// bg, bu [S][r], wd [E][F].  y [T][E] in fp64.  Returns 0, or -1 on bad sizes.
+int lro_ffn(int qmode, int T, int E, int F, int S, int r, const float* x, const float* wg,
+            const float* wu, const float* ag, const float* au, const float* bg, const float* bu,
+            const float* wd, double* y) {
+  if (T < 0 || E < 1 || F < 1 || S < 0 || S > F || (S > 0 && r < 1) || qmode < 0 || qmode > 1) return -1;
+  const int D = F - S;
+  std::vector<double> g(static_cast<size_t>(T) * F), u(static_cast<size_t>(T) * F);
+  std::vector<double> tmp;
+  // dense channels S..F-1
+  if (D > 0) {
+    tmp.resize(static_cast<size_t>(T) * D);
+    qmatmul(make_qmat(wg, D, E, qmode), x, T, qmode, tmp.data());
+    for (int t = 0; t < T; ++t)
+      for (int c = 0; c < D; ++c) g[static_cast<size_t>(t) * F + S + c] = tmp[static_cast<size_t>(t) * D + c];
+    qmatmul(make_qmat(wu, D, E, qmode), x, T, qmode, tmp.data());
+    for (int t = 0; t < T; ++t)
+      for (int c = 0; c < D; ++c) u[static_cast<size_t>(t) * F + S + c] = tmp[static_cast<size_t>(t) * D + c];
+  }
+  // low-rank channels 0..S-1: latent z = A x (rounded to fp32), then B z
+  if (S > 0) {
+    std::vector<double> z(static_cast<size_t>(T) * r);
+    std::vector<float> z32(static_cast<size_t>(T) * r);
+    tmp.resize(static_cast<size_t>(T) * S);
+    const float* A[2] = {ag, au};
+    const float* B[2] = {bg, bu};
+    std::vector<double>* dst[2] = {&g, &u};
+    for (int i = 0; i < 2; ++i) {
+      qmatmul(make_qmat(A[i], r, E, qmode), x, T, qmode, z.data());
+      for (size_t k = 0; k < z.size(); ++k) z32[k] = static_cast<float>(z[k]);
+      qmatmul(make_qmat(B[i], S, r, qmode), z32.data(), T, qmode, tmp.data());
+      for (int t = 0; t < T; ++t)
+        for (int c = 0; c < S; ++c) (*dst[i])[static_cast<size_t>(t) * F + c] = tmp[static_cast<size_t>(t) * S + c];
+    }
+  }
+  // SwiGLU: h = silu(g) * u, silu(v) = v / (1 + exp(-v)); rounded to fp32
+  std::vector<float> h(static_cast<size_t>(T) * F);
+  for (size_t k = 0; k < h.size(); ++k) h[k] = static_cast<float>(g[k] / (1.0 + std::exp(-g[k])) * u[k]);
+  qmatmul(make_qmat(wd, E, F, qmode), h.data(), T, qmode, y);
+  return 0;
+}
+
 // Quantise and dequantise one row: out_i = scale * q_i in fp64 (exact).
 // qfmt: 0 = int8 per token, 1 = int4 group 32, 2 = no quantisation (out = c).
 static void dequantised_row(int qfmt, const float* c, int r, double* out) {

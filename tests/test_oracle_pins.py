@@ -513,3 +513,105 @@ def test_allocation_grows_with_the_budget_and_respects_it():
             assert np.all(r >= prev)
         prev = r
     assert np.all(oracle.allocate_ranks(s, 8, 136.0, 40 * 128 * 136) == 128)
+
+
+# --------------------------------------------------------------------------
+# Hybrid low-rank / dense FFN, W8A8
+# --------------------------------------------------------------------------
+
+def _silu(v):
+    from scipy.special import expit
+    return v * expit(v)
+
+
+def test_activation_groups_are_int8_rows_of_64():
+    """Per-token, per-64-group activation scales are the int8 row quantiser
+    applied to each group (the last group shorter)."""
+    rng = np.random.default_rng(2)
+    a = (rng.standard_normal((3, 150)) * np.exp2(rng.integers(-8, 8, (3, 1)))).astype(np.float32)
+    q, s = oracle.quant_act_groups(a)
+    assert s.shape == (3, 3)
+    for t in range(3):
+        for g, (lo, hi) in enumerate([(0, 64), (64, 128), (128, 150)]):
+            q1, s1 = oracle.quant_int8(a[t, lo:hi])
+            assert np.array_equal(q[t, lo:hi], q1) and s[t, g] == s1
+
+
+def _ffn_case(rng, T=3, E=64, F=48, S=16, r=8):
+    f = lambda *sh: rng.standard_normal(sh).astype(np.float32)
+    return (f(T, E), f(F - S, E) / 8, f(F - S, E) / 8, f(r, E) / 8, f(r, E) / 8, f(S, r) / 3,
+            f(S, r) / 3, f(E, F) / 7)
+
+
+def test_ffn_unquantised_equals_brute_force():
+    """Without quantisation the oracle is the hybrid SwiGLU FFN: low-rank
+    channels through B A, dense ones through W, then W_d (numpy, fp64)."""
+    rng = np.random.default_rng(4)
+    x, wg, wu, ag, au, bg, bu, wd = [v.astype(np.float64) for v in _ffn_case(rng)]
+    G = np.concatenate([bg @ ag, wg], axis=0)     # rows = hidden channels, low-rank first
+    U = np.concatenate([bu @ au, wu], axis=0)
+    h = (_silu(x @ G.T) * (x @ U.T)).astype(np.float32).astype(np.float64)
+    want = h @ wd.T
+    got = oracle.ffn(x, wg, wu, ag, au, bg, bu, wd, quantise=False)
+    assert np.max(np.abs(got - want)) <= 1e-5 * np.max(np.abs(want))
+
+
+def test_ffn_w8a8_error_is_the_rounding_of_h_on_grid_inputs():
+    """All-dense (S = 0) with weights and x already on the int8 grid (integers
+    times a power of two per activation group, every row / group reaching
+    +-127, so every scale is a power of two and every code exact):
+    the only error left is the RTN of h, so |y_q - y| <= sum_c |W_d[e][c]|
+    (s_h(t, c) / 2 + fp32 rounding of h)."""
+    rng = np.random.default_rng(8)
+    T, E, F = 4, 128, 96
+
+    def grid(rows, cols, group):
+        m = rng.integers(-126, 127, (rows, cols)).astype(np.float32)
+        for lo in range(0, cols, group):
+            m[:, lo] = 127.0
+        return m
+    # x group g scaled by 2^(g - 1): scales 1/2, 1 differ per group, codes stay exact
+    x = grid(T, E, 64) * np.repeat(np.exp2(np.arange(E // 64) - 1.0), 64)[None, :].astype(np.float32)
+    wg, wu = grid(F, E, E), grid(F, E, E)
+    wd = grid(E, F, F)
+    z0 = np.zeros((0, E), np.float32)
+    zs = np.zeros((0, 0), np.float32)
+    yq = oracle.ffn(x, wg, wu, z0, z0, zs, zs, wd, quantise=True)
+    y = oracle.ffn(x, wg, wu, z0, z0, zs, zs, wd, quantise=False)
+    # h as the oracle forms it (fp32), its group scales, and the bound
+    g = x.astype(np.float64) @ wg.T.astype(np.float64)
+    u = x.astype(np.float64) @ wu.T.astype(np.float64)
+    h = (_silu(g) * u).astype(np.float32)
+    _, sh = oracle.quant_act_groups(h)
+    bound = np.zeros((T, E))
+    for c in range(F):
+        bound += np.abs(wd[:, c])[None, :] * (sh[:, c // 64] / 2 + 2.0 ** -24 * np.abs(h[:, c]))[:, None]
+    assert np.all(np.abs(yq - y) <= bound * 1.0001 + 1e-9)
+    assert np.max(np.abs(yq - y)) > 0          # the rounding of h does show
+
+
+def test_ffn_w8a8_scales_exactly_with_the_down_projection():
+    """Doubling W_d doubles y exactly (codes unchanged, scales doubled)."""
+    rng = np.random.default_rng(12)
+    x, wg, wu, ag, au, bg, bu, wd = _ffn_case(rng, T=2, E=128, F=80, S=32, r=64)
+    y1 = oracle.ffn(x, wg, wu, ag, au, bg, bu, wd)
+    y2 = oracle.ffn(x, wg, wu, ag, au, bg, bu, wd * 2)
+    assert np.array_equal(y2, 2 * y1)
+
+
+def test_ffn_identity_low_rank_branch_reproduces_the_dense_branch():
+    """S = F low-rank channels with A = I (r = E) and B = W give the dense
+    branch's result with W (x on the grid, so the latent z is x itself up to
+    the fp32 rounding of 127 * fl(1/127))."""
+    rng = np.random.default_rng(13)
+    T, E, F = 3, 64, 32
+    x = rng.integers(-126, 127, (T, E)).astype(np.float32)
+    x[:, 0] = 127.0
+    W_g = (rng.standard_normal((F, E)) / 8).astype(np.float32)
+    W_u = (rng.standard_normal((F, E)) / 8).astype(np.float32)
+    wd = (rng.standard_normal((E, F)) / 7).astype(np.float32)
+    I = np.eye(E, dtype=np.float32)
+    z0 = np.zeros((0, E), np.float32)
+    dense = oracle.ffn(x, W_g, W_u, z0, z0, np.zeros((0, 0), np.float32), np.zeros((0, 0), np.float32), wd)
+    lowrank = oracle.ffn(x, np.zeros((0, E), np.float32), np.zeros((0, E), np.float32), I, I, W_g, W_u, wd)
+    assert np.max(np.abs(lowrank - dense)) <= 1e-5 * np.max(np.abs(dense))
