@@ -76,6 +76,8 @@ def parse():
                     help="replace the workload's rank table by the greedy allocation "
                          "(lr_attn_allocate_ranks) of synthetic component scores under a budget "
                          "of MEAN ranks per head and K/V")
+    ap.add_argument("--ffn", action="store_true",
+                    help="time the hybrid low-rank/dense W8A8 FFN decode (lr_ffn_decode) instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=16,
                     help="extra untimed-in-value steps with the 256 MiB last-level cache flushed before each")
@@ -153,12 +155,83 @@ def cpu_baseline(run, n_units_target=128):
             "step_s": step_s}
 
 
+def ffn_bench(args):
+    """Hybrid FFN decode: `steps` evaluations of the LLaMA-7B-shaped hybrid FFN
+    on 16 tokens, each four launches, in one HIP graph."""
+    import torch
+    import lrgen
+    from latent_kv_attention_lr_amd.ffn import FfnLayer
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    f = lrgen.FFN_WORKLOADS[0]
+    steps = 128 if args.steps is None else args.steps
+    warm = args.warmup
+    print(f"[bench] setting up {f.name}", file=sys.stderr, flush=True)
+    w = lrgen.ffn_weights(f)
+    layer = FfnLayer(f.embed, f.hidden, f.n_lowrank, f.rank, device=dev)
+    layer.set_weights(*w)
+    xs = [lrgen.ffn_activations(lrgen.FfnWorkload(f.name, f.embed, f.hidden, f.n_lowrank, f.rank, f.tokens,
+                                                   f.seed + 1 + s), f.tokens).to(dev) for s in range(4)]
+    y = torch.empty(f.tokens, f.embed, dtype=torch.float32, device=dev)
+    layer(xs[0], y)
+    for s in range(warm):
+        layer(xs[s % 4], y)
+    torch.cuda.synchronize()
+
+    def run():
+        for s in range(steps):
+            layer(xs[s % 4], y)
+
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            run()
+    torch.cuda.current_stream().wait_stream(cap)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_s = e0.elapsed_time(e1) / 1e3 / steps
+    E, F, S, r, T = f.embed, f.hidden, f.n_lowrank, f.rank, f.tokens
+    Fp = (F + 63) // 64 * 64
+    weight_bytes = (2 * (F - S) * E + 2 * r * E + 2 * S * r + E * F) + 4 * (2 * (F - S) + 2 * r + 2 * S + E)
+    inter = 2 * (T * 2 * r * 4) + 2 * (T * F * 4) + 2 * (T * Fp + T * (Fp // 64) * 4)
+    step_bytes = weight_bytes + T * E * 2 + T * E * 4 + inter
+    achieved = step_bytes / step_s / 1e9
+    result = {
+        "metric": "hybrid low-rank/dense W8A8 FFN decode tokens/sec (1 GPU) + achieved HBM GB/s",
+        "value": T * steps / wall, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": wall / steps * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "i8", "data": "synthetic",
+        "config": {"workload": f.name, "embed": E, "hidden": F, "lowrank_channels": S, "rank": r,
+                   "tokens": T, "weights": "int8 per-row scale", "activations": "int8 per token per 64",
+                   "launches_per_step": 4, "launch": "hip graph of all timed steps"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": "k_ffn_in + k_ffn_mid + "
+                     "k_ffn_quant + k_ffn_out (one step)", "bytes_per_step": step_bytes,
+                     "weight_bytes": weight_bytes, "avg_step_us": step_s * 1e6},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; multi-GPU sharding is a design note, "
               "not an implemented path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.ffn:
+        ffn_bench(args)
+        return
     import torch
     import harness
     import lrgen

@@ -317,6 +317,57 @@ lr_status lr_attn_allocate_ranks(int32_t n_layers, int32_t n_heads, int32_t max_
                                  const float* scores, int64_t cost_per_rank, int64_t budget,
                                  int32_t* rank_k, int32_t* rank_v);
 
+/* Hybrid low-rank / dense SwiGLU FFN with W8A8 round-to-nearest
+ * quantisation, decode step (LASER page, "Hybrid SVD-quantisation for FFNs":
+ * SVD-friendly hidden channels of the gate and up projections are kept as
+ * low-rank factors, the others dense, both branches RTN-quantised; "System
+ * implementation": fused kernels for the input projection, latent
+ * activations, SwiGLU and quantisation).  For each token t:
+ *     g_c = (B_g A_g x_t)_c, u_c = (B_u A_u x_t)_c   for hidden channels c < S
+ *     g_c = (W_g x_t)_c,     u_c = (W_u x_t)_c       for S <= c < F
+ *     h = silu(g) * u,       y_t = W_d h
+ * Weights are int8 with one fp32 scale per row (s = max|w| / 127, codes
+ * clamp(rne(w / s), -127, 127)); the activations x, z = A x (per gate/up) and
+ * h are int8 with one fp32 scale per token and per group of 64 consecutive
+ * elements along the reduction dimension (the last group may be shorter),
+ * by the same rule; dot products are exact integer sums per group, scaled in
+ * fp32 by the group's activation scale and the row's weight scale. */
+typedef struct {
+  int32_t embed;      /* E: multiple of 64, 64..8192 */
+  int32_t hidden;     /* F: multiple of 16 */
+  int32_t n_lowrank;  /* S: hidden channels [0, S) are low-rank; multiple of 16, 0..F */
+  int32_t rank;       /* r of both gate and up factors: multiple of 64, 64..4096 (0 when S == 0) */
+  int32_t reserved;   /* 0 */
+} lr_ffn_desc;
+
+/* Bytes of the packed weights (0 on a bad description). */
+size_t lr_ffn_weight_bytes(const lr_ffn_desc* desc);
+
+/* Quantise and pack the weights on the host, from fp32 row-major HOST arrays
+ * (rows = outputs): wg, wu [F - S][E] (dense gate / up rows of channels
+ * S .. F - 1), ag, au [r][E], bg, bu [S][r], wd [E][F] (unused inputs may be
+ * NULL).  out: HOST buffer of lr_ffn_weight_bytes bytes, to be copied to
+ * device memory (256-aligned) as is.
+ * Errors: LR_EINVAL (null pointer, non-finite weight, reserved != 0),
+ * LR_EUNSUPPORTED (sizes outside the ranges above). */
+lr_status lr_ffn_prepare_weights(const lr_ffn_desc* desc, const float* wg, const float* wu,
+                                 const float* ag, const float* au, const float* bg, const float* bu,
+                                 const float* wd, void* out);
+
+/* Workspace bytes of lr_ffn_decode for n_tokens tokens (0 on bad arguments). */
+size_t lr_ffn_workspace_bytes(const lr_ffn_desc* desc, int32_t n_tokens);
+
+/* One FFN evaluation for n_tokens tokens (four launches on `stream`):
+ *   weights    device, the packed weights, 256-aligned
+ *   x          device bf16 [n_tokens][E], 16-aligned
+ *   y          device fp32 [n_tokens][E], 16-aligned, written
+ *   workspace  device, >= lr_ffn_workspace_bytes(n_tokens), 256-aligned, scratch
+ * Results are deterministic.  n_tokens = 0 is a no-op.
+ * Errors: LR_EINVAL, LR_EUNSUPPORTED, LR_ERANGE (n_tokens > 2^20),
+ * LR_EWORKSPACE, LR_EHIP. */
+lr_status lr_ffn_decode(const lr_ffn_desc* desc, const void* weights, const void* x, int32_t n_tokens,
+                        float* y, void* workspace, size_t ws_bytes, void* stream);
+
 /* Measurement aid, not part of the decode path: streams bytes / 16 16-byte
  * words from device memory src (16-byte aligned, bytes >= 16; a trailing
  * partial word is not read) with a plain grid-stride read kernel, the

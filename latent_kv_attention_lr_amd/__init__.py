@@ -52,6 +52,11 @@ class lr_attn_head_layout(ctypes.Structure):
                 ("factor_offset_k", ctypes.c_int64), ("factor_offset_v", ctypes.c_int64)]
 
 
+class lr_ffn_desc(ctypes.Structure):
+    _fields_ = [("embed", ctypes.c_int32), ("hidden", ctypes.c_int32), ("n_lowrank", ctypes.c_int32),
+                ("rank", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 def _hip_runtimes():
     try:
         with open("/proc/self/maps") as f:
@@ -98,6 +103,10 @@ def _load() -> ctypes.CDLL:
         "lr_attn_hadamard_block": (I32, [P, I32, I32, I32, I32]),
         "lr_attn_hadamard_rotate_rows": (ctypes.c_int, [P, I32, I32, I32, P, ctypes.c_int64]),
         "lr_attn_allocate_ranks": (ctypes.c_int, [I32, I32, I32, P, ctypes.c_int64, ctypes.c_int64, P, P]),
+        "lr_ffn_weight_bytes": (SZ, [ctypes.POINTER(lr_ffn_desc)]),
+        "lr_ffn_workspace_bytes": (SZ, [ctypes.POINTER(lr_ffn_desc), I32]),
+        "lr_ffn_prepare_weights": (ctypes.c_int, [ctypes.POINTER(lr_ffn_desc)] + [P] * 8),
+        "lr_ffn_decode": (ctypes.c_int, [ctypes.POINTER(lr_ffn_desc), P, P, I32, P, P, SZ, P]),
         "lr_attn_probe_read": (ctypes.c_int, [P, SZ, P, P]),
         "lr_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "lr_attn_last_hip_error": (I32, []),
@@ -281,6 +290,32 @@ def lr_attn_allocate_ranks(scores, cost_per_rank: int, budget: int):
     _check(_lib.lr_attn_allocate_ranks(L, H, m, scores.ctypes.data, int(cost_per_rank), int(budget),
                                        rk.ctypes.data, rv.ctypes.data), "lr_attn_allocate_ranks")
     return rk, rv
+
+
+def lr_ffn_weight_bytes(desc: lr_ffn_desc) -> int:
+    return int(_lib.lr_ffn_weight_bytes(ctypes.byref(desc)))
+
+
+def lr_ffn_workspace_bytes(desc: lr_ffn_desc, n_tokens: int) -> int:
+    return int(_lib.lr_ffn_workspace_bytes(ctypes.byref(desc), n_tokens))
+
+
+def lr_ffn_prepare_weights(desc: lr_ffn_desc, wg, wu, ag, au, bg, bu, wd):
+    """Quantise and pack host fp32 weights (numpy) -> numpy uint8 buffer."""
+    import numpy as np
+    arrs = []
+    for a in (wg, wu, ag, au, bg, bu, wd):
+        arrs.append(None if a is None or a.size == 0 else np.ascontiguousarray(a, dtype=np.float32))
+    out = np.zeros(lr_ffn_weight_bytes(desc), dtype=np.uint8)
+    ptrs = [None if a is None else a.ctypes.data for a in arrs]
+    _check(_lib.lr_ffn_prepare_weights(ctypes.byref(desc), *ptrs, out.ctypes.data), "lr_ffn_prepare_weights")
+    return out
+
+
+def lr_ffn_decode(desc: lr_ffn_desc, weights, x, n_tokens: int, y, workspace, ws_bytes: int,
+                  stream=None) -> None:
+    _check(_lib.lr_ffn_decode(ctypes.byref(desc), _ptr(weights), _ptr(x), n_tokens, _ptr(y),
+                              _ptr(workspace), ws_bytes, _stream(stream)), "lr_ffn_decode")
 
 
 def lr_attn_probe_read(src, nbytes: int, sink, stream=None) -> None:

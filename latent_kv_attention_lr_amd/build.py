@@ -1,7 +1,7 @@
 """Build ``liblr_attn.so`` in-tree for gfx950.
 
-``plan.cpp``, ``rotate.cpp`` and ``alloc.cpp`` (host-only C++) are compiled
-with g++; ``kernels.hip``,
+``plan.cpp``, ``rotate.cpp``, ``alloc.cpp`` and ``ffn_host.cpp`` (host-only
+C++) are compiled with g++; ``ffn.hip`` joins the hipcc sources; ``kernels.hip``,
 ``project.hip`` and ``probe.hip`` with hipcc for gfx950; hipcc links them into
 one shared library next to this file.
 """
@@ -40,6 +40,8 @@ def build(verbose: bool = False) -> str:
     plan_o = os.path.join(BUILD, "plan.o")
     rot_o = os.path.join(BUILD, "rotate.o")
     alloc_o = os.path.join(BUILD, "alloc.o")
+    ffnh_o = os.path.join(BUILD, "ffn_host.o")
+    ffn_o = os.path.join(BUILD, "ffn.o")
     kern_o = os.path.join(BUILD, "kernels.o")
     proj_o = os.path.join(BUILD, "project.o")
     probe_o = os.path.join(BUILD, "probe.o")
@@ -47,12 +49,14 @@ def build(verbose: bool = False) -> str:
         _run(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "plan.cpp"), "-o", plan_o]),
         _run(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "rotate.cpp"), "-o", rot_o]),
         _run(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "alloc.cpp"), "-o", alloc_o]),
+        _run(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "ffn_host.cpp"), "-o", ffnh_o]),
+        _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "ffn.hip"), "-o", ffn_o]),
         _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "kernels.hip"), "-o", kern_o]),
         _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "project.hip"), "-o", proj_o]),
         _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "probe.hip"), "-o", probe_o]),
     ]
     tmp = LIB + ".tmp"
-    outs.append(_run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp, plan_o, rot_o, alloc_o, kern_o,
+    outs.append(_run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp, plan_o, rot_o, alloc_o, ffnh_o, ffn_o, kern_o,
                       proj_o, probe_o]))
     os.replace(tmp, LIB)
     if verbose:

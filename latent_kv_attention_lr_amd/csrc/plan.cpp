@@ -30,6 +30,10 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 }  // namespace
 
 namespace lr {
+void set_last_hip_error(int err) { g_last_hip = err; }
+}  // namespace lr
+
+namespace lr {
 
 Split choose_split(const lr_attn_plan& p, int32_t layer, int32_t max_len) {
   // Wavefronts per (b, h) work-group: 8 where the registers leave room for

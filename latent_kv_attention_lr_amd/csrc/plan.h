@@ -70,6 +70,17 @@ int launch_pack_projection(const lr_attn_plan& p, int32_t layer, int32_t embed, 
                            const void* wv, void* packed, void* stream);
 int launch_project(const lr_attn_plan& p, int32_t layer, const void* x, int32_t n_tokens,
                    int32_t embed, const void* packed, float* ck, float* cv, void* stream);
+// Hybrid FFN (ffn.hip, ffn_host.cpp): byte offsets of the packed weight
+// sections and, for a call on T tokens, of the workspace buffers.
+struct FfnLayout {
+  int32_t E, F, S, r, Fp;                            // Fp = F rounded up to 64
+  size_t off_w1, off_w2, off_w3, off_s1, off_s2, off_s3, weight_bytes;
+  size_t ws_xq, ws_xs, ws_z, ws_zq, ws_zs, ws_h, ws_hq, ws_hs, ws_bytes;
+};
+// Records a HIP error for lr_attn_last_hip_error (this thread).
+void set_last_hip_error(int err);
+int launch_ffn(const FfnLayout& f, const void* weights, const void* x, int32_t n_tokens, float* y,
+               void* workspace, void* stream);
 // probe.hip: stream bytes / 16 16-byte words from src (read only).
 int launch_probe_read(const void* src, size_t bytes, void* sink, void* stream);
 

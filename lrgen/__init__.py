@@ -295,6 +295,45 @@ def component_scores(seed: int, n_layers: int, n_heads: int, max_rank: int = 128
     return (g * a * j ** (-2.0 * b) * n).to(torch.float32)
 
 
+TAG_FFN = 10
+
+
+@dataclass
+class FfnWorkload:
+    """One synthetic hybrid-FFN decode workload: LLaMA-7B FFN shape."""
+    name: str
+    embed: int
+    hidden: int
+    n_lowrank: int
+    rank: int
+    tokens: int
+    seed: int
+
+
+FFN_WORKLOADS = [
+    FfnWorkload("llama7b-ffn-b16-hybrid50-r1024-w8a8", 4096, 11008, 5504, 1024, 16, 0x5EEDF000),
+]
+
+
+def ffn_weights(f: FfnWorkload):
+    """fp32 weights of the hybrid FFN (numpy, row-major, rows = outputs):
+    wg, wu [F-S, E] ~ N(0, 1/E); ag, au [r, E] ~ N(0, 1/E); bg, bu [S, r] ~
+    N(0, 1/r); wd [E, F] ~ N(0, 1/F).  Each drawn from its own stream."""
+    E, F, S, r = f.embed, f.hidden, f.n_lowrank, f.rank
+    shapes = [(F - S, E, E), (F - S, E, E), (r, E, E), (r, E, E), (S, r, r), (S, r, r), (E, F, F)]
+    out = []
+    for i, (a, b, fan) in enumerate(shapes):
+        key = stream_key(f.seed, TAG_FFN, i)
+        out.append(normal(key, 0, a * b, 1.0 / math.sqrt(max(fan, 1))).view(a, b).numpy())
+    return out
+
+
+def ffn_activations(f: FfnWorkload, tokens: int, device="cpu") -> torch.Tensor:
+    """x [tokens, E] ~ N(0, 1), rounded to bf16."""
+    key = stream_key(f.seed, TAG_FFN, 100)
+    return normal(key, 0, tokens * f.embed, 1.0, device).view(tokens, f.embed).to(torch.bfloat16)
+
+
 def queries(w: Workload, layer: int, step: int, dtype=torch.bfloat16, device="cpu") -> torch.Tensor:
     """q for one decode step: [B, H, d] ~ N(0, 1), rounded to ``dtype``."""
     key = stream_key(w.seed, TAG_Q, layer, step)
