@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCE = os.path.join(ROOT, "latent_kv_attention_lr_amd", "csrc", "kernels.hip")
 PROJECT_SOURCE = os.path.join(ROOT, "latent_kv_attention_lr_amd", "csrc", "project.hip")
+FFN_SOURCE = os.path.join(ROOT, "latent_kv_attention_lr_amd", "csrc", "ffn.hip")
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -55,6 +56,18 @@ def measured_projection_traffic(workload_name):
         d = json.load(open(f))
         if d.get("project_hip_sha256") == src:
             return d["hbm_bytes_per_launch"]
+    return None
+
+
+def measured_ffn_traffic(workload_name):
+    """HBM bytes per FFN step from committed counter runs on the current ffn.hip (else None)."""
+    import hashlib
+    src = hashlib.sha256(open(FFN_SOURCE, "rb").read()).hexdigest()
+    f = os.path.join(TRAFFIC_DIR, f"traffic_{workload_name}_ffn.json")
+    if os.path.exists(f):
+        d = json.load(open(f))
+        if d.get("ffn_hip_sha256") == src:
+            return d["hbm_bytes_per_step"]
     return None
 
 
@@ -175,6 +188,13 @@ def ffn_bench(args):
     xs = [lrgen.ffn_activations(lrgen.FfnWorkload(f.name, f.embed, f.hidden, f.n_lowrank, f.rank, f.tokens,
                                                    f.seed + 1 + s), f.tokens).to(dev) for s in range(4)]
     y = torch.empty(f.tokens, f.embed, dtype=torch.float32, device=dev)
+    if args.copy_calibration_mib:
+        src = torch.ones(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     layer(xs[0], y)
     for s in range(warm):
         layer(xs[s % 4], y)
@@ -216,7 +236,8 @@ def ffn_bench(args):
                    "tokens": T, "weights": "int8 per-row scale", "activations": "int8 per token per 64",
                    "launches_per_step": 4, "launch": "hip graph of all timed steps"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": "k_ffn_in + k_ffn_mid + "
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": measured_ffn_traffic(f.name),
+                     "kernel": "k_ffn_in + k_ffn_mid + "
                      "k_ffn_quant + k_ffn_out (one step)", "bytes_per_step": step_bytes,
                      "weight_bytes": weight_bytes, "avg_step_us": step_s * 1e6},
     }
