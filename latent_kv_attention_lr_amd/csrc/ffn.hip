@@ -13,13 +13,15 @@
 // z = A x, h) are int8 with one fp32 scale per token and per group of 64
 // elements along the reduction dimension -- the k extent of one
 // v_mfma_i32_16x16x64_i8, so every product is an exact integer sum per group,
-// converted and scaled once per group in fp32.  Six launches:
+// converted and scaled once per group in fp32.  Six launches (seven when h
+// spans several chunks):
 //   k_ffn_quant x -> codes and group scales
 //   k_ffn_in    dense pairs: h = silu(g) u; and the latents z = [A_g; A_u] x
 //   k_ffn_quant z -> codes and group scales
 //   k_ffn_mid   low-rank pairs: h = silu(g) u
 //   k_ffn_quant h -> codes and group scales
-//   k_ffn_out   y = W_d h
+//   k_ffn_out   y = W_d h, the hidden dimension split in chunks of 4096 across
+//               work-groups (k_ffn_sum adds the chunks' partial sums in order)
 // Each activation is quantised once (one wavefront per token and group); the
 // GEMM launches copy 16 tokens' codes into LDS with coalesced loads.
 // At decode sizes every launch streams its int8 weights once from HBM (packed
@@ -268,40 +270,50 @@ struct OutArgs {
   const float* hs;            // [T][Fp / 64]
   const uint8_t* w;           // packed W_d tiles, k = Fp
   const float* ws;
-  float* y;                   // [T][E]
-  int32_t T, E, Fp, tiles;    // tiles = E / 16
+  float* y;                   // [T][E] when splits == 1, else partials [splits][T][E]
+  int32_t T, E, Fp, tiles, splits;   // tiles = E / 16; splits = ceil(Fp / CHUNK)
 };
 
-// Launch 6: work-group = (16 rows of W_d, block of 16 tokens); the codes of h
-// come through LDS in chunks of CHUNK.
+// Launch 6: work-group = (16 rows of W_d, one CHUNK of the hidden dimension,
+// block of 16 tokens); its chunk of h's codes comes through LDS.  With several
+// chunks each work-group writes its scaled partial sum, and k_ffn_sum adds
+// them in chunk order.
 template <int LDS, int CHUNK>
 __global__ __launch_bounds__(kThreads) void k_ffn_out(OutArgs a) {
   static_assert(lds_bytes(block_bytes(CHUNK)) <= LDS, "chunk exceeds LDS");
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
-  const int unit = blockIdx.x % a.tiles, t0 = 16 * (blockIdx.x / a.tiles);
+  const int unit = blockIdx.x % a.tiles, split = (blockIdx.x / a.tiles) % a.splits;
+  const int t0 = 16 * (blockIdx.x / (a.tiles * a.splits));
   const int steps = a.Fp / 64, kc = min(CHUNK, a.Fp);
   float* outv = reinterpret_cast<float*>(smem + code_area(block_bytes(kc)));
   const uint8_t* wt[1] = {a.w + size_t(unit) * steps * 1024};
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   f32x4_t acc[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
   int8_t* act = reinterpret_cast<int8_t*>(smem);
-  for (int k0 = 0; k0 < a.Fp; k0 += CHUNK) {
-    const int kn = min(CHUNK, a.Fp - k0), gn = kn / 64, rs = kn + kRowPad;
-    float* scale = reinterpret_cast<float*>(smem + 16 * rs);
-    const int cb = k0 / 64;
-    const int8_t* acts[1] = {act};
-    const float* scs[1] = {scale};
-    gemm_steps<1>(wt, cb + gn * wid / kWaves, cb + gn * (wid + 1) / kWaves, cb, acts, scs, rs, gn, acc, [&]() {
-      __syncthreads();   // the previous chunk is no longer read
-      stage_codes(a.hq, a.hs, a.Fp, k0, kn, a.T, t0, act, scale, rs);
-      __syncthreads();
-    });
-  }
+  const int k0 = split * CHUNK, kn = min(CHUNK, a.Fp - k0), gn = kn / 64, rs = kn + kRowPad;
+  float* scale = reinterpret_cast<float*>(smem + 16 * rs);
+  const int cb = k0 / 64;
+  const int8_t* acts[1] = {act};
+  const float* scs[1] = {scale};
+  gemm_steps<1>(wt, cb + gn * wid / kWaves, cb + gn * (wid + 1) / kWaves, cb, acts, scs, rs, gn, acc, [&]() {
+    stage_codes(a.hq, a.hs, a.Fp, k0, kn, a.T, t0, act, scale, rs);
+    __syncthreads();
+  });
   reduce_tiles<1>(acc, smem, outv);
+  float* dst = a.y + size_t(a.splits > 1 ? split : 0) * a.T * a.E;
   for (int i = threadIdx.x; i < 256; i += kThreads) {
     const int tt = i >> 4, nn = i & 15, t = t0 + tt;
-    if (t < a.T) a.y[size_t(t) * a.E + 16 * unit + nn] = outv[i] * a.ws[16 * unit + nn];
+    if (t < a.T) dst[size_t(t) * a.E + 16 * unit + nn] = outv[i] * a.ws[16 * unit + nn];
   }
+}
+
+// y[i] = sum over splits s = 0, 1, ... of yp[s][i] (in that order).
+__global__ __launch_bounds__(256) void k_ffn_sum(const float* yp, float* y, int32_t n, int32_t splits) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float v = 0.0f;
+  for (int s = 0; s < splits; ++s) v += yp[size_t(s) * n + i];
+  y[i] = v;
 }
 
 }  // namespace
@@ -352,10 +364,19 @@ int launch_ffn(const FfnLayout& f, const void* weights, const void* x, int32_t n
   }
   hipLaunchKernelGGL(k_ffn_quant<false>, quant_grid(f.Fp), dim3(256), 0, s, h, int64_t(f.F), f.F, T, f.Fp, hq, hs);
   if ((err = int(hipGetLastError())) != 0) return err;
-  OutArgs oa{hq, hs, w + f.off_w3, reinterpret_cast<const float*>(w + f.off_s3), y, T, f.E, f.Fp, f.E / 16};
-  const dim3 g(unsigned(oa.tiles) * tb), b(kThreads);
-  if (f.Fp <= 2048) hipLaunchKernelGGL((k_ffn_out<kLdsS, 2048>), g, b, 0, s, oa);
+  const int chunk = f.Fp <= 2048 ? 2048 : 4096;
+  const int splits = (f.Fp + chunk - 1) / chunk;
+  float* yp = reinterpret_cast<float*>(ws + f.ws_yp);
+  OutArgs oa{hq, hs, w + f.off_w3, reinterpret_cast<const float*>(w + f.off_s3), splits > 1 ? yp : y, T, f.E, f.Fp,
+             f.E / 16, splits};
+  const dim3 g(unsigned(oa.tiles) * unsigned(splits) * tb), b(kThreads);
+  if (chunk == 2048) hipLaunchKernelGGL((k_ffn_out<kLdsS, 2048>), g, b, 0, s, oa);
   else hipLaunchKernelGGL((k_ffn_out<kLdsM, 4096>), g, b, 0, s, oa);
+  if ((err = int(hipGetLastError())) != 0) return err;
+  if (splits > 1) {
+    const int n = T * f.E;
+    hipLaunchKernelGGL(k_ffn_sum, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, yp, y, n, splits);
+  }
   return int(hipGetLastError());
 }
 

@@ -51,6 +51,8 @@ void ffn_workspace(lr::FfnLayout* f, size_t T) {
   f->ws_h = take(T * F * 4);
   f->ws_hq = take(T * Fp);
   f->ws_hs = take(T * (Fp / 64) * 4);
+  const size_t chunk = Fp <= 2048 ? 2048 : 4096, splits = (Fp + chunk - 1) / chunk;
+  f->ws_yp = take(splits > 1 ? splits * T * E * 4 : 0);   // partial sums of the down projection
   f->ws_bytes = o;
 }
 

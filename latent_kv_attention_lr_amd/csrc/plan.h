@@ -75,7 +75,7 @@ int launch_project(const lr_attn_plan& p, int32_t layer, const void* x, int32_t 
 struct FfnLayout {
   int32_t E, F, S, r, Fp;                            // Fp = F rounded up to 64
   size_t off_w1, off_w2, off_w3, off_s1, off_s2, off_s3, weight_bytes;
-  size_t ws_xq, ws_xs, ws_z, ws_zq, ws_zs, ws_h, ws_hq, ws_hs, ws_bytes;
+  size_t ws_xq, ws_xs, ws_z, ws_zq, ws_zs, ws_h, ws_hq, ws_hs, ws_yp, ws_bytes;
 };
 // Records a HIP error for lr_attn_last_hip_error (this thread).
 void set_last_hip_error(int err);

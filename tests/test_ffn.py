@@ -48,6 +48,7 @@ def test_ffn_weight_and_workspace_sizes():
     T = 5
     ws = (r256(T * E) + r256(T * (E // 64) * 4) + r256(T * 2 * r * 4) + r256(T * 2 * r)
           + r256(T * (2 * r // 64) * 4) + r256(T * F * 4) + r256(T * Fp) + r256(T * (Fp // 64) * 4))
+    # (no partial sums: the hidden dimension fits one chunk of the down projection)
     assert lr.lr_ffn_workspace_bytes(_desc(E, F, S, r), T) == ws
     assert lr.lr_ffn_workspace_bytes(_desc(E, F, S, r), 0) == 0
 
