@@ -271,39 +271,46 @@ struct OutArgs {
   const uint8_t* w;           // packed W_d tiles, k = Fp
   const float* ws;
   float* y;                   // [T][E] when splits == 1, else partials [splits][T][E]
-  int32_t T, E, Fp, tiles, splits;   // tiles = E / 16; splits = ceil(Fp / CHUNK)
+  int32_t T, E, Fp, units, splits;   // units = E / (16 RT); splits = ceil(Fp / CHUNK)
 };
 
-// Launch 6: work-group = (16 rows of W_d, one CHUNK of the hidden dimension,
-// block of 16 tokens); its chunk of h's codes comes through LDS.  With several
-// chunks each work-group writes its scaled partial sum, and k_ffn_sum adds
-// them in chunk order.
-template <int LDS, int CHUNK>
+// Launch 6: work-group = (RT tiles of 16 rows of W_d, one CHUNK of the hidden
+// dimension, block of 16 tokens); its chunk of h's codes comes through LDS
+// once for all RT tiles.  With several chunks each work-group writes its
+// scaled partial sum, and k_ffn_sum adds them in chunk order.
+template <int LDS, int CHUNK, int RT>
 __global__ __launch_bounds__(kThreads) void k_ffn_out(OutArgs a) {
-  static_assert(lds_bytes(block_bytes(CHUNK)) <= LDS, "chunk exceeds LDS");
+  static_assert(lds_bytes(block_bytes(CHUNK)) <= LDS && RT <= 2, "chunk exceeds LDS");
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
-  const int unit = blockIdx.x % a.tiles, split = (blockIdx.x / a.tiles) % a.splits;
-  const int t0 = 16 * (blockIdx.x / (a.tiles * a.splits));
+  const int unit = blockIdx.x % a.units, split = (blockIdx.x / a.units) % a.splits;
+  const int t0 = 16 * (blockIdx.x / (a.units * a.splits));
   const int steps = a.Fp / 64, kc = min(CHUNK, a.Fp);
   float* outv = reinterpret_cast<float*>(smem + code_area(block_bytes(kc)));
-  const uint8_t* wt[1] = {a.w + size_t(unit) * steps * 1024};
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  f32x4_t acc[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  const uint8_t* wt[RT];
+  const int8_t* acts[RT];
+  const float* scs[RT];
+  f32x4_t acc[RT];
   int8_t* act = reinterpret_cast<int8_t*>(smem);
   const int k0 = split * CHUNK, kn = min(CHUNK, a.Fp - k0), gn = kn / 64, rs = kn + kRowPad;
   float* scale = reinterpret_cast<float*>(smem + 16 * rs);
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    wt[r] = a.w + size_t(RT * unit + r) * steps * 1024;
+    acts[r] = act;
+    scs[r] = scale;
+    acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int cb = k0 / 64;
-  const int8_t* acts[1] = {act};
-  const float* scs[1] = {scale};
-  gemm_steps<1>(wt, cb + gn * wid / kWaves, cb + gn * (wid + 1) / kWaves, cb, acts, scs, rs, gn, acc, [&]() {
+  gemm_steps<RT>(wt, cb + gn * wid / kWaves, cb + gn * (wid + 1) / kWaves, cb, acts, scs, rs, gn, acc, [&]() {
     stage_codes(a.hq, a.hs, a.Fp, k0, kn, a.T, t0, act, scale, rs);
     __syncthreads();
   });
-  reduce_tiles<1>(acc, smem, outv);
+  reduce_tiles<RT>(acc, smem, outv);
   float* dst = a.y + size_t(a.splits > 1 ? split : 0) * a.T * a.E;
-  for (int i = threadIdx.x; i < 256; i += kThreads) {
-    const int tt = i >> 4, nn = i & 15, t = t0 + tt;
-    if (t < a.T) dst[size_t(t) * a.E + 16 * unit + nn] = outv[i] * a.ws[16 * unit + nn];
+  for (int i = threadIdx.x; i < RT * 256; i += kThreads) {
+    const int r = i >> 8, tt = (i >> 4) & 15, nn = i & 15, t = t0 + tt, row = 16 * (RT * unit + r) + nn;
+    if (t < a.T) dst[size_t(t) * a.E + row] = outv[i] * a.ws[row];
   }
 }
 
@@ -364,14 +371,19 @@ int launch_ffn(const FfnLayout& f, const void* weights, const void* x, int32_t n
   }
   hipLaunchKernelGGL(k_ffn_quant<false>, quant_grid(f.Fp), dim3(256), 0, s, h, int64_t(f.F), f.F, T, f.Fp, hq, hs);
   if ((err = int(hipGetLastError())) != 0) return err;
+  // Chunks of 4096 (2048 for small hidden sizes); with several chunks a
+  // work-group takes two row tiles, so each staged chunk of h serves 32 rows
+  // of W_d (measured best on the LLaMA-7B FFN among chunks of 1, 2, 4 and 8 K
+  // with one or two tiles).
   const int chunk = f.Fp <= 2048 ? 2048 : 4096;
-  const int splits = (f.Fp + chunk - 1) / chunk;
+  const int splits = (f.Fp + chunk - 1) / chunk, rt = splits > 1 ? 2 : 1;
   float* yp = reinterpret_cast<float*>(ws + f.ws_yp);
   OutArgs oa{hq, hs, w + f.off_w3, reinterpret_cast<const float*>(w + f.off_s3), splits > 1 ? yp : y, T, f.E, f.Fp,
-             f.E / 16, splits};
-  const dim3 g(unsigned(oa.tiles) * unsigned(splits) * tb), b(kThreads);
-  if (chunk == 2048) hipLaunchKernelGGL((k_ffn_out<kLdsS, 2048>), g, b, 0, s, oa);
-  else hipLaunchKernelGGL((k_ffn_out<kLdsM, 4096>), g, b, 0, s, oa);
+             f.E / (16 * rt), splits};
+  const dim3 g(unsigned(oa.units) * unsigned(splits) * tb), b(kThreads);
+  if (chunk == 2048) hipLaunchKernelGGL((k_ffn_out<kLdsS, 2048, 1>), g, b, 0, s, oa);
+  else if (rt == 1) hipLaunchKernelGGL((k_ffn_out<kLdsM, 4096, 1>), g, b, 0, s, oa);
+  else hipLaunchKernelGGL((k_ffn_out<kLdsM, 4096, 2>), g, b, 0, s, oa);
   if ((err = int(hipGetLastError())) != 0) return err;
   if (splits > 1) {
     const int n = T * f.E;
