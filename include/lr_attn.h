@@ -142,11 +142,12 @@ size_t lr_attn_workspace_bytes(const lr_attn_plan* plan, int32_t max_len);
  *   ck, cv  device fp32 [batch][n_new][latent_elems(kv)], 16-aligned; head h's
  *           latent of a token is the r_h elements at latent_offset(h)
  *   pos     device int32 [batch]; slots outside [0, capacity) are skipped
- *   n_new   tokens per sequence, 0..capacity (0 is a no-op)
+ *   n_new   tokens per sequence, 0..capacity (0 is a no-op), with
+ *           batch x n_heads x n_new <= 2^26
  * The cache is only written; lengths are not tracked by the library.  The
  * quantised codes and scales are bit-exact with the definition given at
  * lr_qfmt (correctly rounded fp32 division, round-half-even, fp16 RNE).
- * Errors: LR_EINVAL, LR_ERANGE, LR_EHIP. */
+ * Errors: LR_EINVAL, LR_ERANGE (layer, n_new), LR_EHIP. */
 lr_status lr_attn_append_latent(const lr_attn_plan* plan, int32_t layer, void* cache,
                                 const float* ck, const float* cv, const int32_t* pos,
                                 int32_t n_new, void* stream);
@@ -354,10 +355,16 @@ lr_status lr_ffn_prepare_weights(const lr_ffn_desc* desc, const float* wg, const
                                  const float* ag, const float* au, const float* bg, const float* bu,
                                  const float* wd, void* out);
 
-/* Workspace bytes of lr_ffn_decode for n_tokens tokens (0 on bad arguments). */
+/* Workspace bytes of lr_ffn_decode for n_tokens tokens (0 on bad arguments,
+ * n_tokens < 1 or > 2^20).  Calls run the tokens in passes of at most 16 x
+ * floor(2^16 / u) tokens, u the largest work-group count per 16 tokens among
+ * the launches (max of E/16 x chunks, r/8, Fp/16, (F-S)/16 + r/16, S/16; Fp
+ * = F rounded up to 64, chunks = 1 if Fp <= 2048 else ceil(Fp / 4096)), and
+ * the workspace holds one pass. */
 size_t lr_ffn_workspace_bytes(const lr_ffn_desc* desc, int32_t n_tokens);
 
-/* One FFN evaluation for n_tokens tokens (four launches on `stream`):
+/* One FFN evaluation for n_tokens tokens (six or seven launches per pass of
+ * tokens, in order on `stream`):
  *   weights    device, the packed weights, 256-aligned
  *   x          device bf16 [n_tokens][E], 16-aligned
  *   y          device fp32 [n_tokens][E], 16-aligned, written

@@ -3,6 +3,7 @@
 // quantisation (int8, one fp32 scale per row, round to nearest even) and
 // packing into matrix-core step blocks, workspace sizes, the decode call.
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -56,6 +57,17 @@ void ffn_workspace(lr::FfnLayout* f, size_t T) {
   f->ws_bytes = o;
 }
 
+// Tokens per pass of the launches: a multiple of 16 such that no launch of a
+// pass has more than 2^16 work-groups.  Work-groups per 16 tokens, per launch:
+// quantise x E / 16, z r / 8, h Fp / 16; k_ffn_in (F - S) / 16 + r / 16;
+// k_ffn_mid S / 16; k_ffn_out at most E / 16 per chunk; the sum E / 16.
+size_t ffn_pass_tokens(const lr::FfnLayout& f) {
+  const size_t E = size_t(f.E), F = size_t(f.F), S = size_t(f.S), r = size_t(f.r), Fp = size_t(f.Fp);
+  const size_t chunks = Fp <= 2048 ? 1 : (Fp + 4095) / 4096;
+  const size_t u = std::max({E / 16 * chunks, r / 8, Fp / 16, (F - S) / 16 + r / 16, S / 16});
+  return 16 * std::max<size_t>(1, (size_t(1) << 16) / u);
+}
+
 // One row: s = max|w| / 127 (fp32), codes clamp(rne(w / s), -127, 127), 0 if s == 0.
 float quant_row(const float* w, int n, int8_t* q) {
   float m = 0.0f;
@@ -94,8 +106,8 @@ size_t lr_ffn_weight_bytes(const lr_ffn_desc* d) {
 
 size_t lr_ffn_workspace_bytes(const lr_ffn_desc* d, int32_t n_tokens) {
   lr::FfnLayout f;
-  if (ffn_layout(d, &f) != LR_OK || n_tokens < 1) return 0;
-  ffn_workspace(&f, size_t(n_tokens));
+  if (ffn_layout(d, &f) != LR_OK || n_tokens < 1 || n_tokens > (1 << 20)) return 0;
+  ffn_workspace(&f, std::min(size_t(n_tokens), ffn_pass_tokens(f)));
   return f.ws_bytes;
 }
 
@@ -159,13 +171,18 @@ lr_status lr_ffn_decode(const lr_ffn_desc* d, const void* weights, const void* x
   auto al = [](const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; };
   if (!al(weights, 256) || !al(x, 16) || !al(y, 16)) return LR_EINVAL;
   if (n_tokens == 0) return LR_OK;
-  ffn_workspace(&f, size_t(n_tokens));
+  const size_t T = size_t(n_tokens), pass = ffn_pass_tokens(f);
+  ffn_workspace(&f, std::min(T, pass));
   if (!workspace || ws_bytes < f.ws_bytes) return LR_EWORKSPACE;
   if (!al(workspace, 256)) return LR_EINVAL;
-  const int err = lr::launch_ffn(f, weights, x, n_tokens, y, workspace, stream);
-  if (err != 0) {
-    lr::set_last_hip_error(err);
-    return LR_EHIP;
+  // passes run in order on one stream and reuse the workspace
+  for (size_t t0 = 0; t0 < T; t0 += pass) {
+    const int err = lr::launch_ffn(f, weights, static_cast<const uint16_t*>(x) + t0 * size_t(f.E),
+                                   int32_t(std::min(pass, T - t0)), y + t0 * size_t(f.E), workspace, stream);
+    if (err != 0) {
+      lr::set_last_hip_error(err);
+      return LR_EHIP;
+    }
   }
   return LR_OK;
 }

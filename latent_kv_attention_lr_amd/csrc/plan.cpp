@@ -220,12 +220,21 @@ size_t lr_attn_workspace_bytes(const lr_attn_plan* p, int32_t max_len) {
   return lr::workspace_bytes(*p, max_len);
 }
 
+namespace {
+// The append launch has 32 threads per (kv, head, sequence, token) row in one
+// grid dimension, which holds fewer than 2^32 threads: batch x heads x n_new
+// is limited to 2^26.
+bool append_fits(const lr_attn_plan& p, int32_t n_new) {
+  return int64_t(p.desc.batch) * p.desc.n_heads * n_new <= (int64_t(1) << 26);
+}
+}  // namespace
+
 lr_status lr_attn_append_latent(const lr_attn_plan* p, int32_t layer, void* cache, const float* ck,
                                 const float* cv, const int32_t* pos, int32_t n_new, void* stream) {
   if (!p) return LR_EINVAL;
   if (layer < 0 || layer >= p->desc.n_layers) return LR_ERANGE;
   if (n_new < 0) return LR_EINVAL;
-  if (n_new > p->desc.capacity) return LR_ERANGE;
+  if (n_new > p->desc.capacity || !append_fits(*p, n_new)) return LR_ERANGE;
   if (!cache || !ck || !cv || !pos) return LR_EINVAL;
   if (!aligned(cache, 256) || !aligned(ck, 16) || !aligned(cv, 16) || !aligned(pos, 4))
     return LR_EINVAL;
@@ -293,7 +302,7 @@ lr_status lr_attn_project_append(const lr_attn_plan* p, int32_t layer, void* cac
   const lr_status st = check_project(p, layer, x, embed, packed);
   if (st != LR_OK) return st;
   if (n_new < 0) return LR_EINVAL;
-  if (n_new > p->desc.capacity) return LR_ERANGE;
+  if (n_new > p->desc.capacity || !append_fits(*p, n_new)) return LR_ERANGE;
   if (!cache || !pos || !aligned(cache, 256) || !aligned(pos, 4)) return LR_EINVAL;
   if (n_new == 0) return LR_OK;
   const auto& L = p->layers[layer];

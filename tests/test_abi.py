@@ -286,6 +286,16 @@ def test_project_workspace_bytes():
         lr.lr_attn_plan_destroy(p)
 
 
+def test_append_rejects_more_rows_than_one_grid_holds():
+    """batch x n_heads x n_new above 2^26 is a range error, not a launch."""
+    p = _plan(batch=1 << 17, n_heads=128, capacity=8, rank_k=[8] * 128, rank_v=[8] * 128)
+    try:
+        assert _append(p, n_new=5) == lr.LR_ERANGE
+        assert _project_append(p, n_new=5) == lr.LR_ERANGE
+    finally:
+        lr.lr_attn_plan_destroy(p)
+
+
 def test_project_append_argument_errors_before_launch():
     p = _plan()
     try:

@@ -53,6 +53,28 @@ def test_ffn_weight_and_workspace_sizes():
     assert lr.lr_ffn_workspace_bytes(_desc(E, F, S, r), 0) == 0
 
 
+def _pass_tokens(E, F, S, r):
+    """Tokens per pass of lr_ffn_decode, as documented with lr_ffn_workspace_bytes."""
+    Fp = -(-F // 64) * 64
+    chunks = 1 if Fp <= 2048 else -(-Fp // 4096)
+    u = max(E // 16 * chunks, r // 8, Fp // 16, (F - S) // 16 + r // 16, S // 16)
+    return 16 * max(1, (1 << 16) // u)
+
+
+def test_ffn_workspace_holds_one_pass():
+    """Above one pass of tokens the workspace stops growing; below it grows."""
+    d = _desc(512, 8208, 4096, 256)
+    p = _pass_tokens(512, 8208, 4096, 256)
+    assert p == 2032
+    assert lr.lr_ffn_workspace_bytes(d, p - 16) < lr.lr_ffn_workspace_bytes(d, p)
+    assert lr.lr_ffn_workspace_bytes(d, p) == lr.lr_ffn_workspace_bytes(d, 2100)
+    assert lr.lr_ffn_workspace_bytes(d, 1 << 20) == lr.lr_ffn_workspace_bytes(d, p)
+    assert lr.lr_ffn_workspace_bytes(d, (1 << 20) + 1) == 0
+    big = _desc(64, 1 << 20, 0, 0)   # the largest hidden size: passes of 16 tokens
+    assert _pass_tokens(64, 1 << 20, 0, 0) == 16
+    assert lr.lr_ffn_workspace_bytes(big, 1000) == lr.lr_ffn_workspace_bytes(big, 16)
+
+
 def _unpack(buf, rows, K, Kp, tiles_off, tile, scales_off):
     """Codes [16][K] and scales [16] of packed tile `tile` (documented layout)."""
     tb = Kp * 16
@@ -175,3 +197,18 @@ def test_ffn_decode_full_size_and_deterministic():
     print(f"worst relative error {worst:.2e}", flush=True)
     y2 = layer(x.to("cuda:0")).cpu().numpy()
     assert np.array_equal(y, y2)
+
+
+@pytest.mark.gpu
+def test_ffn_decode_in_several_passes():
+    """2100 tokens of a shape whose pass is 2032 tokens: two passes through one
+    workspace; tokens on both sides of the pass boundary and at both ends
+    against the oracle."""
+    E, F, S, r, T = 512, 8208, 4096, 256, 2100
+    assert _pass_tokens(E, F, S, r) == 2032
+    print(f"ffn passes E={E} F={F} S={S} r={r} T={T}", flush=True)
+    rows = [0, 1, 777, 2030, 2031, 2032, 2033, 2099]
+    y, ref, _, _ = _run_gpu(E, F, S, r, T, seed=99, tokens=rows)
+    for i, t in enumerate(rows):
+        err = float(np.max(np.abs(y[i] - ref[i])))
+        assert err <= TOL_FFN * float(np.max(np.abs(ref[i]))), (t, err)
