@@ -17,6 +17,8 @@ class FfnLayer:
             raise ValueError("unsupported FFN shape")
         self.E, self.F, self.S, self.r = embed, hidden, n_lowrank, rank
         self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:   # "cuda" means the current device
+            self.device = torch.device("cuda", torch.cuda.current_device())
         self.weights = None
         self.workspace = torch.empty(256, dtype=torch.uint8, device=self.device)
 
@@ -26,14 +28,20 @@ class FfnLayer:
         self.weights = torch.from_numpy(packed).to(self.device)
 
     def __call__(self, x: torch.Tensor, y: torch.Tensor = None, stream=None) -> torch.Tensor:
-        """y [T, E] fp32 = FFN(x [T, E] bf16)."""
+        """y [T, E] fp32 = FFN(x [T, E] bf16), launched on `stream` (default:
+        torch's current stream).  The layer's one workspace is reused by every
+        call, so calls on different streams must not overlap."""
         if self.weights is None:
             raise ValueError("weights are not set")
-        if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != self.E or not x.is_contiguous():
-            raise ValueError("x must be contiguous bf16 [T, E]")
+        if (x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != self.E or not x.is_contiguous()
+                or x.device != self.device):
+            raise ValueError(f"x must be contiguous bf16 [T, {self.E}] on {self.device}")
         T = x.shape[0]
         if y is None:
             y = torch.empty(T, self.E, dtype=torch.float32, device=self.device)
+        elif (y.dtype != torch.float32 or tuple(y.shape) != (T, self.E) or not y.is_contiguous()
+              or y.device != self.device):
+            raise ValueError(f"y must be contiguous fp32 [{T}, {self.E}] on {self.device}")
         need = lr_ffn_workspace_bytes(self.desc, T) if T > 0 else 0
         if need > self.workspace.numel():
             self.workspace = torch.empty(need, dtype=torch.uint8, device=self.device)

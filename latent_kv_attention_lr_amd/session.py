@@ -28,6 +28,8 @@ class DecodeSession:
         self.n_layers, self.batch, self.n_heads, self.capacity = n_layers, batch, n_heads, capacity
         self.qfmt, self.io_dtype = qfmt, io_dtype
         self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:   # "cuda" means the current device
+            self.device = torch.device("cuda", torch.cuda.current_device())
         self.ranks_k = [list(r) for r in ranks_k]
         self.ranks_v = [list(r) for r in ranks_v]
         flat_k = [r for row in self.ranks_k for r in row]
@@ -87,8 +89,9 @@ class DecodeSession:
         if ck.shape != (self.batch, n_new, self.latent_elems(layer, 0)) or \
                 cv.shape != (self.batch, n_new, self.latent_elems(layer, 1)):
             raise ValueError("latent tensors have the wrong shape")
-        if not (ck.is_contiguous() and cv.is_contiguous() and pos.is_contiguous()):
-            raise ValueError("latent and pos tensors must be contiguous")
+        if not (ck.is_contiguous() and cv.is_contiguous()) or ck.device != self.device or cv.device != self.device:
+            raise ValueError("latent tensors must be contiguous on the session device")
+        self._check_pos(pos)
         lr_attn_append_latent(self.plan, layer, self.caches[layer], ck, cv, pos, n_new, stream)
 
     def decode(self, layer: int, q: torch.Tensor, out: torch.Tensor, max_len: int,
@@ -149,6 +152,12 @@ class DecodeSession:
         lr_attn_pack_projection(self.plan, layer, E, wk, wv, packed)
         self.proj[layer] = (E, packed)
 
+    def _check_pos(self, pos: torch.Tensor) -> None:
+        """pos: the first slot of every sequence, int32 [batch] on the device."""
+        if pos.dtype != torch.int32 or pos.numel() != self.batch or not pos.is_contiguous() \
+                or pos.device != self.device:
+            raise ValueError(f"pos must be contiguous int32 [{self.batch}] on the session device")
+
     def _projection_input(self, layer: int, x: torch.Tensor) -> int:
         if self.proj[layer] is None:
             raise ValueError("projection factors of this layer are not set")
@@ -182,8 +191,7 @@ class DecodeSession:
         E = self._projection_input(layer, x)
         if x.dim() != 3 or x.shape[0] != self.batch:
             raise ValueError("x must be [batch, n_new, embed]")
-        if not pos.is_contiguous():
-            raise ValueError("pos must be contiguous")
+        self._check_pos(pos)
         n_new = x.shape[1]
         need = lr_attn_project_workspace_bytes(self.plan, n_new) if n_new > 0 else 0
         if need > 0 and (self._proj_ws is None or self._proj_ws.numel() < need):
