@@ -241,6 +241,23 @@ def ffn_bench(args):
                      "k_ffn_out + k_ffn_sum (one step)", "bytes_per_step": step_bytes,
                      "weight_bytes": weight_bytes, "avg_step_us": step_s * 1e6},
     }
+    if not args.no_cpu_baseline:
+        # the oracle as it stands (one call per step: it quantises the weights
+        # and the activations, then evaluates in fp64; one thread), repeated
+        # over whole steps until about 10 s of work are done
+        import oracle
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        xh = [xx.float().cpu().numpy() for xx in xs]
+        n, cpu_wall = 0, 0.0
+        while n == 0 or cpu_wall < 10.0:
+            t0 = time.perf_counter()
+            oracle.ffn(xh[n % len(xh)], *w)
+            cpu_wall += time.perf_counter() - t0
+            n += 1
+        result["cpu_baseline"] = {
+            "value": T * n / cpu_wall, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} whole steps of {T} tokens (lro_ffn: W8A8 quantisation of weights and "
+                      f"activations, then fp64), {cpu_wall:.2f} s on one thread"}
     print(json.dumps(result), flush=True)
 
 
