@@ -41,9 +41,10 @@ struct ProjArgs {
   int32_t T, E, nk, nv;
   int32_t k_tiles, row_tiles;   // 16-row tiles of W^K; of W^K and W^V together
   int32_t t_blocks, tb_stride;  // token blocks; token blocks per grid pass
+  int32_t units;                // work-groups per token block: ceil(row_tiles / RT)
 };
 
-// Work-group (16-row tile, block of 16 NT tokens) over all of E:
+// Work-group (RT 16-row tiles, block of 16 NT tokens) over all of E:
 //   c[t][n] = sum_e x[t][e] w[n][e]
 // with v_mfma_f32_16x16x32_bf16 (latent rows = MFMA rows, tokens = columns;
 // lane (i, g) = (lane & 15, lane >> 4) supplies row/column i, elements 8 g ..
@@ -52,7 +53,7 @@ struct ProjArgs {
 // steps w SPW .. w SPW + SPW - 1, its partial tile is summed with the other
 // wavefronts' through LDS in wavefront order at the end, so the result is the
 // same on every call.  Rows and tokens past the ends are never stored.
-template <int NT, int NW, int SPW>
+template <int NT, int NW, int SPW, int RT>
 __global__ __launch_bounds__(NW * 64) void k_project(ProjArgs a) {
   constexpr int TOK = 16 * NT;                 // tokens per block
   constexpr int PS = NW * SPW;                 // steps per phase
@@ -61,29 +62,32 @@ __global__ __launch_bounds__(NW * 64) void k_project(ProjArgs a) {
   constexpr int XV = TOK * EP / 8;             // 16-byte activation pieces per phase
   constexpr int XPT = (XV + NW * 64 - 1) / (NW * 64);
   static_assert(TOK * RS <= kLdsBytes, "activation phase exceeds LDS");
-  static_assert(NW * NT * 64 * 16 <= kLdsBytes, "reduction exceeds LDS");
+  static_assert(NW * RT * NT * 64 * 16 <= kLdsBytes, "reduction exceeds LDS");
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop control
   const int li = lane & 15, lg = lane >> 4;
-  const int rt = blockIdx.x % a.row_tiles;
-  const bool isv = rt >= a.k_tiles;
-  const int n0 = 16 * (isv ? rt - a.k_tiles : rt);
-  const int N = isv ? a.nv : a.nk;
-  float* out = isv ? a.cv : a.ck;
+  const int unit = blockIdx.x % a.units;
   const int steps = a.E >> 5, phases = (steps + PS - 1) / PS;
-  const uint16_t* wl = a.wp + size_t(rt) * steps * 512 + 8 * lane;
+  // row tiles RT unit .. RT unit + RT - 1 (a tile past the last is loaded as
+  // the last and never stored)
+  const uint16_t* wl[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+    wl[r] = a.wp + size_t(min(RT * unit + r, a.row_tiles - 1)) * steps * 512 + 8 * lane;
 
-  for (int tb = blockIdx.x / a.row_tiles; tb < a.t_blocks; tb += a.tb_stride) {
+  for (int tb = blockIdx.x / a.units; tb < a.t_blocks; tb += a.tb_stride) {
     const int t0 = TOK * tb;
-    uint4 wb[2][SPW];
+    uint4 wb[2][RT][SPW];
     uint4 xb[XPT];
     // factors of phase p for this wavefront's steps (clamped: a step past E is
     // loaded at the last step and not multiplied)
-    auto load_w = [&](int p, uint4 (&dst)[SPW]) {
+    auto load_w = [&](int p, uint4 (&dst)[RT][SPW]) {
 #pragma unroll
-      for (int u = 0; u < SPW; ++u) dst[u] = ld16(wl + size_t(min(p * PS + wid * SPW + u, steps - 1)) * 512);
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int u = 0; u < SPW; ++u) dst[r][u] = ld16(wl[r] + size_t(min(p * PS + wid * SPW + u, steps - 1)) * 512);
     };
     // activations of phase p, piece q = row * (EP / 8) + col: token t0 + row,
     // elements p EP + 8 col .. + 7 (clamped into the row and the token range)
@@ -102,10 +106,12 @@ __global__ __launch_bounds__(NW * 64) void k_project(ProjArgs a) {
         if (q < XV) *reinterpret_cast<uint4*>(lds + (q / (EP / 8)) * RS + 16 * (q % (EP / 8))) = xb[m];
       }
     };
-    f32x4_t acc[NT];
+    f32x4_t acc[RT][NT];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    auto compute = [&](int p, const uint4 (&w)[SPW]) {
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[r][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int p, const uint4 (&w)[RT][SPW]) {
 #pragma unroll
       for (int u = 0; u < SPW; ++u) {
         const int cl = wid * SPW + u;
@@ -114,8 +120,10 @@ __global__ __launch_bounds__(NW * 64) void k_project(ProjArgs a) {
           for (int j = 0; j < NT; ++j) {
             const bf16x8_t bv = __builtin_bit_cast(
                 bf16x8_t, *reinterpret_cast<const uint4*>(lds + (16 * j + li) * RS + 64 * cl + 16 * lg));
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w[u]), bv, acc[j],
-                                                            0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < RT; ++r)
+              acc[r][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w[r][u]), bv,
+                                                                  acc[r][j], 0, 0, 0);
           }
         }
       }
@@ -145,19 +153,24 @@ __global__ __launch_bounds__(NW * 64) void k_project(ProjArgs a) {
       }
     }
 
-    f32x4_t* s_red = reinterpret_cast<f32x4_t*>(lds);   // [NW][NT][64]
+    f32x4_t* s_red = reinterpret_cast<f32x4_t*>(lds);   // [NW][RT][NT][64]
 #pragma unroll
-    for (int j = 0; j < NT; ++j) s_red[(wid * NT + j) * 64 + lane] = acc[j];
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) s_red[((wid * RT + r) * NT + j) * 64 + lane] = acc[r][j];
     __syncthreads();
-    // token tt, row nn: consecutive threads on consecutive rows of one token
-    for (int i = tid; i < NT * 256; i += NW * 64) {
-      const int tt = i >> 4, nn = i & 15;
+    // tile r, token tt, row nn: consecutive threads on consecutive rows of one token
+    for (int i = tid; i < RT * NT * 256; i += NW * 64) {
+      const int r = i / (NT * 256), ii = i % (NT * 256);
+      const int tt = ii >> 4, nn = ii & 15;
       const int j = tt >> 4, src = (tt & 15) + 16 * (nn >> 2), e = nn & 3;
       float v = 0.0f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) v += s_red[(w * NT + j) * 64 + src][e];
-      const int t = t0 + tt, n = n0 + nn;
-      if (t < a.T && n < N) out[size_t(t) * N + n] = v;
+      for (int w = 0; w < NW; ++w) v += s_red[((w * RT + r) * NT + j) * 64 + src][e];
+      const int rt = RT * unit + r;
+      const bool isv = rt >= a.k_tiles;
+      const int t = t0 + tt, n = 16 * (isv ? rt - a.k_tiles : rt) + nn, N = isv ? a.nv : a.nk;
+      if (rt < a.row_tiles && t < a.T && n < N) (isv ? a.cv : a.ck)[size_t(t) * N + n] = v;
     }
     __syncthreads();
   }
@@ -220,23 +233,26 @@ int launch_project(const lr_attn_plan& p, int32_t layer, const void* x, int32_t 
   a.nv = L.sum_rv;
   a.k_tiles = (L.sum_rk + 15) / 16;
   a.row_tiles = a.k_tiles + (L.sum_rv + 15) / 16;
-  // tokens per work-group: 16, 32, 48 or 64 (the fewest 16-token tiles that
-  // cover n_tokens, at most four); larger calls loop over token blocks
-  const int col_tiles = (n_tokens + 15) / 16;
-  const int nt = col_tiles < 4 ? col_tiles : 4;
+  // Up to 48 tokens: one block of 16, 32 or 48 tokens per work-group and one
+  // row tile.  From 49 tokens on: blocks of 32 tokens and two row tiles per
+  // work-group, so that every staged activation serves 32 latent rows (the
+  // LDS re-reads of the activations bound this case: 64 tokens at E = 4096
+  // over 4096 rows measured 15.4 us with 64-token blocks and one tile, 12.7 us
+  // so).  Larger calls loop over token blocks.
+  const int col_tiles = (n_tokens + 15) / 16;   // n_tokens >= 1
+  const bool two = col_tiles >= 4;
+  const int nt = two ? 2 : col_tiles;
+  a.units = two ? (a.row_tiles + 1) / 2 : a.row_tiles;
   a.t_blocks = (col_tiles + nt - 1) / nt;
-  const int max_tb = (1 << 20) / a.row_tiles;   // at most 2^20 work-groups
+  const int max_tb = (1 << 20) / a.units;   // at most 2^20 work-groups
   a.tb_stride = a.t_blocks < max_tb ? a.t_blocks : max_tb;
-  const dim3 grid(unsigned(a.row_tiles) * unsigned(a.tb_stride));
+  const dim3 grid(unsigned(a.units) * unsigned(a.tb_stride));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // shapes measured on MI355X at E = 4096: 2048-element activation phases up
-  // to 32 tokens, 1024-element ones above, with 16 wavefronts at 64 tokens
-  switch (nt) {
-    case 1: hipLaunchKernelGGL((k_project<1, 8, 8>), grid, dim3(512), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_project<2, 8, 8>), grid, dim3(512), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_project<3, 8, 4>), grid, dim3(512), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_project<4, 16, 2>), grid, dim3(1024), 0, s, a); break;
-  }
+  // activation phases of 2048 elements up to 32 tokens, 1024 above
+  if (two) hipLaunchKernelGGL((k_project<2, 8, 4, 2>), grid, dim3(512), 0, s, a);
+  else if (nt == 1) hipLaunchKernelGGL((k_project<1, 8, 8, 1>), grid, dim3(512), 0, s, a);
+  else if (nt == 2) hipLaunchKernelGGL((k_project<2, 8, 8, 1>), grid, dim3(512), 0, s, a);
+  else hipLaunchKernelGGL((k_project<3, 8, 4, 1>), grid, dim3(512), 0, s, a);
   return int(hipGetLastError());
 }
 
