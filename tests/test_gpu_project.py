@@ -96,6 +96,24 @@ def test_project_integer_inputs_bitexact(E, T):
     assert np.array_equal(cv, oracle.latents(x.double().numpy(), av.double().numpy()).astype(np.float32))
 
 
+@pytest.mark.parametrize("T", [49, 64, 100])
+def test_project_two_tile_units_straddle_k_and_v(T):
+    """From 49 tokens on, a work-group takes two row tiles.  With 3 K tiles and
+    4 V tiles (the last one half full) one work-group holds K's last tile and
+    V's first, and the last work-group's second tile is past the end: every
+    latent still lands exactly where it belongs (integer inputs, exact)."""
+    E, ranks_k, ranks_v = 1024, [8, 24, 16], [16, 8, 32]
+    say(f"project two-tile units T={T}")
+    rng = np.random.default_rng(T)
+    s = _session(ranks_k, ranks_v)
+    x = torch.from_numpy(rng.integers(-3, 4, (T, E)).astype(np.float32))
+    ak = torch.from_numpy(rng.integers(-3, 4, (E, sum(ranks_k))).astype(np.float32))
+    av = torch.from_numpy(rng.integers(-3, 4, (E, sum(ranks_v))).astype(np.float32))
+    ck, cv = _gpu_project(s, x.to(torch.bfloat16), ak, av)
+    assert np.array_equal(ck, oracle.latents(x.double().numpy(), ak.double().numpy()).astype(np.float32))
+    assert np.array_equal(cv, oracle.latents(x.double().numpy(), av.double().numpy()).astype(np.float32))
+
+
 def test_project_one_hot_rows_pick_factor_rows():
     """x_t = e_j gives row j of A exactly: every token and every latent lands
     at its own place (tokens across column tiles, rows across row tiles)."""
