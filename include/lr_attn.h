@@ -235,9 +235,11 @@ lr_status lr_attn_pack_projection(const lr_attn_plan* plan, int32_t layer, int32
                                   const void* wk, const void* wv, void* packed, void* stream);
 
 /* The latents of n_tokens tokens, on the matrix cores: bf16 inputs, exact
- * products, fp32 sums in an order that is the same on every call (results are
- * deterministic; they are not bitwise equal to other summation orders).  The
- * plan's io_dtype does not apply.
+ * products, fp32 sums in a fixed order for a given n_tokens (results are
+ * deterministic; the work-group shape, and with it the summation order,
+ * depends on the token count, so a token's latents may differ in the last
+ * bits between calls with different n_tokens).  The plan's io_dtype does not
+ * apply.
  *   x         device bf16 [n_tokens][embed], 16-aligned
  *   n_tokens  0 (no-op) or more; rows of x are tokens in any order
  *   embed     E: a multiple of 32, >= 32, the value the factors were packed with
