@@ -167,12 +167,14 @@ def _run_gpu(E, F, S, r, T, seed, tokens=None):
 @pytest.mark.parametrize("E,F,S,r,T", [(128, 96, 32, 64, 1), (128, 96, 32, 64, 5), (256, 160, 64, 128, 16),
                                        (256, 160, 64, 128, 17), (128, 96, 0, 0, 40), (128, 96, 96, 64, 3),
                                        (8192, 64, 16, 64, 2), (512, 8208, 4096, 256, 3),
-                                       (512, 1296, 0, 0, 3), (512, 2064, 512, 128, 3), (512, 4112, 0, 0, 3)])
+                                       (512, 1296, 0, 0, 3), (512, 2064, 512, 128, 3), (512, 4112, 0, 0, 3),
+                                       (256, 160, 64, 2048, 3), (256, 160, 64, 4096, 2)])
 def test_ffn_decode_matches_oracle(E, F, S, r, T):
     """Small shapes across every path: T = 1 / ragged / several token blocks,
     all-dense and all-low-rank, the largest E, hidden sizes not a multiple of
     64, above one LDS chunk of the down projection, and between 1.3 K and 8 K
-    (where LDS sized per launch once gave all-zero outputs)."""
+    (where LDS sized per launch once gave all-zero outputs); ranks 2048 and
+    4096 take the medium and large LDS instances of the low-rank launch."""
     print(f"ffn E={E} F={F} S={S} r={r} T={T}", flush=True)
     y, ref, _, _ = _run_gpu(E, F, S, r, T, seed=E + F + S + r + T)
     for t in range(T):
