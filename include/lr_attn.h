@@ -193,6 +193,27 @@ lr_status lr_attn_append_decode(const lr_attn_plan* plan, int32_t layer, void* c
                                 const void* bk, const void* bv, float softmax_scale, void* out,
                                 void* workspace, size_t ws_bytes, void* stream);
 
+/* lr_attn_append_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same launches and the same results, bit for bit, with the
+ * context-split partials kept in a device array that the library holds, one
+ * per GPU, from the first call on that GPU until the process ends.  The
+ * array holds LR_NOALLOC_SCRATCH_BYTES (2 MiB); the partials of any plan fit
+ * in it (at most 1.06 MB), and a call whose lr_attn_workspace_bytes(max_len)
+ * would exceed it returns LR_EWORKSPACE before any launch.  No call allocates
+ * or frees memory.  Every call on one GPU uses that GPU's one array, which
+ * keeps the last call's contents (each launch writes every partial it later
+ * reads, so nothing needs clearing): calls that may run at the same time on
+ * one GPU (different streams or threads) race on it and must be serialised by
+ * the caller.  Arguments and errors as lr_attn_append_decode, without the
+ * workspace; LR_EHIP also when the array's address cannot be obtained. */
+#define LR_NOALLOC_SCRATCH_BYTES (2u << 20)
+lr_status lr_attn_append_decode_noalloc(const lr_attn_plan* plan, int32_t layer, void* cache,
+                                        const float* ck, const float* cv, const int32_t* pos,
+                                        const int32_t* len, int32_t max_len, const void* q,
+                                        const void* bk, const void* bv, float softmax_scale,
+                                        void* out, void* stream);
+
 /* The same result through explicit per-token reconstruction: every k_t and
  * v_t (d = 128 values) is rebuilt on chip with matrix-core products of the
  * dequantised latents and B_h, then scored and accumulated (WSVD page,

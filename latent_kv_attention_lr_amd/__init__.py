@@ -95,6 +95,8 @@ def _load() -> ctypes.CDLL:
         "lr_attn_decode_explicit": (ctypes.c_int, [P, I32, P, P, I32, P, P, P, ctypes.c_float, P, P, SZ, P]),
         "lr_attn_append_decode": (ctypes.c_int, [P, I32, P, P, P, P, P, I32, P, P, P, ctypes.c_float,
                                                  P, P, SZ, P]),
+        "lr_attn_append_decode_noalloc": (ctypes.c_int, [P, I32, P, P, P, P, P, I32, P, P, P,
+                                                         ctypes.c_float, P, P]),
         "lr_attn_packed_projection_elems": (SZ, [P, I32, I32]),
         "lr_attn_pack_projection": (ctypes.c_int, [P, I32, I32, P, P, P, P]),
         "lr_attn_project_latent": (ctypes.c_int, [P, I32, P, I32, I32, P, P, P, P]),
@@ -212,6 +214,15 @@ def lr_attn_append_decode(plan: int, layer: int, cache, ck, cv, pos, lengths, ma
                                       _ptr(lengths), max_len, _ptr(q), _ptr(bk), _ptr(bv),
                                       float(softmax_scale), _ptr(out), _ptr(workspace), ws_bytes,
                                       _stream(stream)), "lr_attn_append_decode")
+
+
+def lr_attn_append_decode_noalloc(plan: int, layer: int, cache, ck, cv, pos, lengths, max_len: int,
+                                  q, bk, bv, softmax_scale: float, out, stream=None) -> None:
+    """lr_attn_append_decode with the library's own device scratch: allocates nothing."""
+    _check(_lib.lr_attn_append_decode_noalloc(plan, layer, _ptr(cache), _ptr(ck), _ptr(cv), _ptr(pos),
+                                              _ptr(lengths), max_len, _ptr(q), _ptr(bk), _ptr(bv),
+                                              float(softmax_scale), _ptr(out), _stream(stream)),
+           "lr_attn_append_decode_noalloc")
 
 
 def lr_attn_decode_explicit(plan: int, layer: int, cache, length, max_len: int, q, bk, bv,

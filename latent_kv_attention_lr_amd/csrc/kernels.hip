@@ -17,6 +17,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "plan.h"
@@ -1151,7 +1152,34 @@ hipError_t launch_decode_q(int bucket, int waves, dim3 grid, hipStream_t st, con
   }
 }
 
+// Split partials of lr_attn_append_decode_noalloc, for callers that cannot
+// allocate: one array per device (each GPU the library runs on holds its own
+// copy until the process ends), shared by every such call on that device.
+// choose_split keeps units x splits below 2048, so the partials of any plan
+// need at most 2048 x kPartStride x 4 bytes (1.06 MB).  In host code the name
+// `scratch` is not a device address: only the address that
+// hipGetSymbolAddress returns for it (scratch_address) is passed to kernels.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 }  // namespace
+
+int scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return int(e);
+  if (dev < 0 || dev >= kMaxDevices) return int(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {   // once per device, with that device current
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return int(e);
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return 0;
+}
 
 int launch_append(const lr_attn_plan& p, int32_t layer, void* cache, const float* ck,
                   const float* cv, const int32_t* pos, int32_t n_new, void* stream) {

@@ -360,6 +360,22 @@ lr_status lr_attn_append_decode(const lr_attn_plan* p, int32_t layer, void* cach
                        false, &app);
 }
 
+lr_status lr_attn_append_decode_noalloc(const lr_attn_plan* p, int32_t layer, void* cache,
+                                        const float* ck, const float* cv, const int32_t* pos,
+                                        const int32_t* len, int32_t max_len, const void* q,
+                                        const void* bk, const void* bv, float scale, void* out,
+                                        void* stream) {
+  if (!p) return LR_EINVAL;
+  if (layer < 0 || layer >= p->desc.n_layers) return LR_ERANGE;
+  if (max_len < 1 || max_len > p->desc.capacity) return LR_ERANGE;
+  if (lr::workspace_bytes(*p, max_len) > lr::kScratchBytes) return LR_EWORKSPACE;
+  void* ws = nullptr;
+  const int e = lr::scratch_address(&ws);
+  if (e != 0) return hip_status(e);
+  return lr_attn_append_decode(p, layer, cache, ck, cv, pos, len, max_len, q, bk, bv, scale, out,
+                               ws, lr::kScratchBytes, stream);
+}
+
 lr_status lr_attn_decode_explicit(const lr_attn_plan* p, int32_t layer, const void* cache,
                                   const int32_t* len, int32_t max_len, const void* q,
                                   const void* bk, const void* bv, float scale, void* out,

@@ -81,6 +81,12 @@ struct FfnLayout {
 void set_last_hip_error(int err);
 int launch_ffn(const FfnLayout& f, const void* weights, const void* x, int32_t n_tokens, float* y,
                void* workspace, void* stream);
+// Device scratch of the allocation-free decode entry point (kernels.hip): a
+// static device array of kScratchBytes; scratch_address gives the current
+// device's copy (looked up once per device).  Returns a hipError_t.
+constexpr size_t kScratchBytes = LR_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+int scratch_address(void** out);
 // probe.hip: stream bytes / 16 16-byte words from src (read only).
 int launch_probe_read(const void* src, size_t bytes, void* sink, void* stream);
 

@@ -296,6 +296,62 @@ def test_append_rejects_more_rows_than_one_grid_holds():
         lr.lr_attn_plan_destroy(p)
 
 
+def _append_decode_noalloc(p, **kw):
+    a = dict(layer=0, cache=FAKE, ck=FAKE, cv=FAKE, pos=FAKE, len=FAKE, max_len=100, q=FAKE,
+             bk=FAKE, bv=FAKE, scale=0.088, out=FAKE)
+    a.update(kw)
+    return lr._lib.lr_attn_append_decode_noalloc(p, a["layer"], a["cache"], a["ck"], a["cv"], a["pos"],
+                                                 a["len"], a["max_len"], a["q"], a["bk"], a["bv"],
+                                                 a["scale"], a["out"], None)
+
+
+def test_append_decode_noalloc_argument_errors_before_launch():
+    p = _plan(capacity=3000)
+    try:
+        assert _append_decode_noalloc(None) == lr.LR_EINVAL
+        assert _append_decode_noalloc(p, layer=1) == lr.LR_ERANGE
+        assert _append_decode_noalloc(p, max_len=0) == lr.LR_ERANGE
+        assert _append_decode_noalloc(p, max_len=3001) == lr.LR_ERANGE
+    finally:
+        lr.lr_attn_plan_destroy(p)
+
+
+NOALLOC_SCRATCH_BYTES = 2 << 20   # LR_NOALLOC_SCRATCH_BYTES in the header
+
+
+def test_noalloc_scratch_size_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define\s+LR_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("qfmt", [lr.LR_Q_INT8_TOKEN, lr.LR_Q_INT4_G32])
+@pytest.mark.parametrize("rank", [8, 32, 64, 96, 128])
+def test_split_partials_of_any_plan_fit_the_noalloc_scratch(qfmt, rank):
+    """The context split keeps (b, h) units x splits below 2048 whatever the
+    shape, so every plan's workspace fits the allocation-free entry point's
+    array: checked over batch x heads from 1 to 4096 and contexts up to 2^24."""
+    worst = 0
+    for units in (1, 2, 3, 5, 8, 13, 32, 63, 64, 100, 255, 256, 511, 512, 1000, 1023, 1024, 4096):
+        heads = min(units, 128)
+        while units % heads:
+            heads -= 1
+        for cap in (64, 4097, 1 << 16, 1 << 24):
+            for waves in (0, 4, 8, 16):
+                try:   # caches past 2^40 bytes are a range error of the plan
+                    p = _plan(batch=units // heads, n_heads=heads, capacity=cap, qfmt=qfmt,
+                              rank_k=[rank] * heads, rank_v=[rank] * heads, wg_waves=waves)
+                except lr.LrAttnError as e:
+                    assert e.status == lr.LR_ERANGE
+                    continue
+                try:
+                    for ml in sorted({1, 64, 65, cap // 2 + 1, cap}):
+                        worst = max(worst, lr.lr_attn_workspace_bytes(p, ml))
+                finally:
+                    lr.lr_attn_plan_destroy(p)
+    assert 0 < worst <= NOALLOC_SCRATCH_BYTES, worst
+
+
 def test_project_append_argument_errors_before_launch():
     p = _plan()
     try:
