@@ -13,7 +13,8 @@ import os
 from typing import Dict, Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblr_attn.so")
+# LR_ATTN_LIB selects another build of the same library (the sanitizer build)
+LIB_PATH = os.environ.get("LR_ATTN_LIB") or os.path.join(_HERE, "liblr_attn.so")
 
 LR_OK, LR_EINVAL, LR_EUNSUPPORTED, LR_ERANGE, LR_EWORKSPACE, LR_EHIP = range(6)
 LR_Q_INT8_TOKEN, LR_Q_INT4_G32 = 0, 1

@@ -23,6 +23,13 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wall", "-Wno-unused-function"]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall"]
+# The host C++ under AddressSanitizer + UndefinedBehaviorSanitizer (gcc's
+# runtimes, preloaded by the process that loads liblr_attn_san.so); the
+# device code is the same.
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=all"]
+SAN_LIB = os.path.join(HERE, "liblr_attn_san.so")
+HOST_SOURCES = ["plan.cpp", "rotate.cpp", "alloc.cpp", "ffn_host.cpp"]
+HIP_SOURCES = ["ffn.hip", "kernels.hip", "project.hip", "probe.hip"]
 
 
 def _run(cmd):
@@ -66,5 +73,27 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_sanitized() -> str:
+    """liblr_attn_san.so: the host sources rebuilt with SANITIZE_FLAGS, linked
+    with the device objects of the last build() (built first if missing)."""
+    hip_objs = [os.path.join(BUILD, s.replace(".hip", ".o")) for s in HIP_SOURCES]
+    if not all(os.path.exists(o) for o in hip_objs):
+        build()
+    san = os.path.join(BUILD, "san")
+    os.makedirs(san, exist_ok=True)
+    objs = []
+    for s in HOST_SOURCES:
+        o = os.path.join(san, s.replace(".cpp", ".o"))
+        _run(["g++", *CXX_FLAGS, *SANITIZE_FLAGS, "-c", os.path.join(CSRC, s), "-o", o])
+        objs.append(o)
+    tmp = SAN_LIB + ".tmp"
+    _run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp, *objs, *hip_objs])
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized())
+    else:
+        print(build(verbose=True))

@@ -22,19 +22,25 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "lr_oracle.cpp")
 _LIB_PATH = os.path.join(_HERE, "liblr_oracle.so")
+_SAN_PATH = os.path.join(_HERE, "liblr_oracle_san.so")
+# AddressSanitizer + UndefinedBehaviorSanitizer build of the same source; a
+# process that loads it must preload the gcc sanitizer runtimes
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=all"]
 
 QFMT_INT8, QFMT_INT4, QFMT_NONE = 0, 1, 2
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with g++ (IEEE fp32/fp64, no contraction, no fast-math)."""
-    if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp"
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile the oracle with g++ (IEEE fp32/fp64, no contraction, no
+    fast-math); sanitize=True builds liblr_oracle_san.so with ASan and UBSan."""
+    path = _SAN_PATH if sanitize else _LIB_PATH
+    if force or not os.path.exists(path):
+        tmp = path + ".tmp"
         cmd = ["g++", "-std=c++17", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC",
-               "-shared", "-o", tmp, _SRC]
+               "-shared", *(SANITIZE_FLAGS if sanitize else []), "-o", tmp, _SRC]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+        os.replace(tmp, path)
+    return path
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -43,9 +49,10 @@ _lib: Optional[ctypes.CDLL] = None
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+        path = os.environ.get("LR_ORACLE_LIB") or _LIB_PATH   # e.g. the sanitizer build
+        if path == _LIB_PATH and not os.path.exists(_LIB_PATH):
             build(force=False)
-        L = ctypes.CDLL(_LIB_PATH)
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         L.lro_f32_to_f16.argtypes = [ctypes.c_float]
         L.lro_f32_to_f16.restype = ctypes.c_uint16
