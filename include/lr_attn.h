@@ -272,6 +272,30 @@ lr_status lr_attn_project_latent(const lr_attn_plan* plan, int32_t layer, const 
                                  int32_t n_tokens, int32_t embed, const void* packed, float* ck,
                                  float* cv, void* stream);
 
+/* The latents of n_tokens tokens as n_parts partial sums: E is split into
+ * n_parts ranges of consecutive 32-element steps, part q covering steps
+ * [q S / n_parts, (q + 1) S / n_parts) of S = embed / 32, and part q's sums
+ * are written to block q of ck and cv:
+ *     ck[q][t][:] = sum over e in part q of x[t][e] A^K[e][:]   (cv likewise)
+ * Adding the blocks in order q = 0, 1, .. gives the latents; the one-step
+ * entry point lr_attn_project_append_decode does exactly that inside its
+ * decode launch.  More parts give more work-groups: a decode-sized product
+ * (a few dozen tokens) then uses the whole GPU.
+ *   n_parts   1 .. 8 and at most embed / 32 (lr_attn_project_parts gives the
+ *             count the one-step entry point uses)
+ *   ck, cv    device fp32 [n_parts][n_tokens][latent_elems(kv)], 16-aligned
+ * Other arguments and errors as lr_attn_project_latent; n_parts out of range
+ * is LR_EINVAL.  With n_parts = 1 the result equals lr_attn_project_latent's
+ * bit for bit. */
+lr_status lr_attn_project_latent_parts(const lr_attn_plan* plan, int32_t layer, const void* x,
+                                       int32_t n_tokens, int32_t embed, const void* packed,
+                                       int32_t n_parts, float* ck, float* cv, void* stream);
+
+/* The part count lr_attn_project_append_decode uses for a call of n_tokens
+ * tokens (its batch) at this embed; 0 on bad arguments. */
+int32_t lr_attn_project_parts(const lr_attn_plan* plan, int32_t layer, int32_t n_tokens,
+                              int32_t embed);
+
 /* Workspace bytes of lr_attn_project_append for any layer with this n_new
  * (the fp32 latents of batch * n_new tokens, K and V); 0 on bad arguments. */
 size_t lr_attn_project_workspace_bytes(const lr_attn_plan* plan, int32_t n_new);
@@ -290,6 +314,39 @@ lr_status lr_attn_project_append(const lr_attn_plan* plan, int32_t layer, void* 
                                  const void* x, int32_t embed, const void* packed,
                                  const int32_t* pos, int32_t n_new, void* workspace,
                                  size_t ws_bytes, void* stream);
+
+/* Workspace bytes of lr_attn_project_append_decode for any layer of the plan
+ * at this max_len and embed: the projection's partial sums, then what
+ * lr_attn_decode needs; 0 on bad arguments. */
+size_t lr_attn_project_decode_workspace_bytes(const lr_attn_plan* plan, int32_t max_len,
+                                              int32_t embed);
+
+/* One whole decode step of a layer from activations: the new token of every
+ * sequence is projected to its latents (c = x A_h, every head; WSVD page,
+ * "Fine-grained per-head SVD"), quantised and written at slot pos[b], and
+ * every (b, h) attends over slots t < len[b] (LASER page, "System
+ * implementation": latent generation and quantisation fused ahead of the
+ * attention kernel).  Two launches on the stream: the projection, with E
+ * split into parts so that a decode-sized product fills the GPU, writes fp32
+ * partial sums to the workspace; the fused append + decode adds each
+ * latent's parts in a fixed order, then proceeds as lr_attn_append_decode.
+ * Results are deterministic; a latent equals lr_attn_project_latent's up to
+ * the order of its fp32 sums (exactly equal where those sums are exact).
+ *   x          device bf16 [batch][embed], 16-aligned: one token per sequence
+ *   embed      E, a multiple of 32, the value the factors were packed with
+ *   packed     device, from lr_attn_pack_projection
+ *   pos        device int32 [batch], as for lr_attn_append_decode
+ *   len ... out  as for lr_attn_decode
+ *   workspace  device, >= lr_attn_project_decode_workspace_bytes(max_len,
+ *              embed) bytes, 256-aligned; concurrent calls must not share one
+ * Errors: LR_EINVAL, LR_ERANGE, LR_EWORKSPACE, LR_EHIP; every argument error
+ * is reported before the first launch. */
+lr_status lr_attn_project_append_decode(const lr_attn_plan* plan, int32_t layer, void* cache,
+                                        const void* x, int32_t embed, const void* packed,
+                                        const int32_t* pos, const int32_t* len, int32_t max_len,
+                                        const void* q, const void* bk, const void* bv,
+                                        float softmax_scale, void* out, void* workspace,
+                                        size_t ws_bytes, void* stream);
 
 /* Outlier smoothing by a rotation between the factors (WSVD page,
  * "Quantisation": orthogonal S_1, S_2, S_1 a Hadamard matrix, smooth channel

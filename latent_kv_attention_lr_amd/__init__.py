@@ -103,6 +103,11 @@ def _load() -> ctypes.CDLL:
         "lr_attn_project_latent": (ctypes.c_int, [P, I32, P, I32, I32, P, P, P, P]),
         "lr_attn_project_workspace_bytes": (SZ, [P, I32]),
         "lr_attn_project_append": (ctypes.c_int, [P, I32, P, P, I32, P, P, I32, P, SZ, P]),
+        "lr_attn_project_latent_parts": (ctypes.c_int, [P, I32, P, I32, I32, P, I32, P, P, P]),
+        "lr_attn_project_parts": (I32, [P, I32, I32, I32]),
+        "lr_attn_project_decode_workspace_bytes": (SZ, [P, I32, I32]),
+        "lr_attn_project_append_decode": (ctypes.c_int, [P, I32, P, P, I32, P, P, P, I32, P, P, P,
+                                                         ctypes.c_float, P, P, SZ, P]),
         "lr_attn_hadamard_block": (I32, [P, I32, I32, I32, I32]),
         "lr_attn_hadamard_rotate_rows": (ctypes.c_int, [P, I32, I32, I32, P, ctypes.c_int64]),
         "lr_attn_allocate_ranks": (ctypes.c_int, [I32, I32, I32, P, ctypes.c_int64, ctypes.c_int64, P, P]),
@@ -263,6 +268,33 @@ def lr_attn_project_append(plan: int, layer: int, cache, x, embed: int, packed, 
     _check(_lib.lr_attn_project_append(plan, layer, _ptr(cache), _ptr(x), embed, _ptr(packed),
                                        _ptr(pos), n_new, _ptr(workspace), ws_bytes, _stream(stream)),
            "lr_attn_project_append")
+
+
+def lr_attn_project_latent_parts(plan: int, layer: int, x, n_tokens: int, embed: int, packed,
+                                 n_parts: int, ck, cv, stream=None) -> None:
+    """Latents of x as n_parts partial sums over ranges of E (blocks of ck, cv)."""
+    _check(_lib.lr_attn_project_latent_parts(plan, layer, _ptr(x), n_tokens, embed, _ptr(packed),
+                                             n_parts, _ptr(ck), _ptr(cv), _stream(stream)),
+           "lr_attn_project_latent_parts")
+
+
+def lr_attn_project_parts(plan: int, layer: int, n_tokens: int, embed: int) -> int:
+    return int(_lib.lr_attn_project_parts(plan, layer, n_tokens, embed))
+
+
+def lr_attn_project_decode_workspace_bytes(plan: int, max_len: int, embed: int) -> int:
+    return int(_lib.lr_attn_project_decode_workspace_bytes(plan, max_len, embed))
+
+
+def lr_attn_project_append_decode(plan: int, layer: int, cache, x, embed: int, packed, pos, lengths,
+                                  max_len: int, q, bk, bv, softmax_scale: float, out, workspace,
+                                  ws_bytes: int, stream=None) -> None:
+    """Latent generation from x, quantised append and decode: one step of a layer."""
+    _check(_lib.lr_attn_project_append_decode(plan, layer, _ptr(cache), _ptr(x), embed, _ptr(packed),
+                                              _ptr(pos), _ptr(lengths), max_len, _ptr(q), _ptr(bk),
+                                              _ptr(bv), float(softmax_scale), _ptr(out),
+                                              _ptr(workspace), ws_bytes, _stream(stream)),
+           "lr_attn_project_append_decode")
 
 
 def lr_attn_hadamard_block(plan: int, layer: int, kv: int, head: int, block: int) -> int:

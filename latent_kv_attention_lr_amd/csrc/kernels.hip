@@ -302,12 +302,13 @@ struct DecodeArgs {
   // 1: keep each head's work-groups on one XCD (see unit_of); 0: plain order
   int32_t xcd_groups;
   // fused append (ck == nullptr: none): quantise and write one token per
-  // sequence at slot pos[b] before attending
+  // sequence at slot pos[b] before attending; its latents are the sum, in
+  // block order, of n_parts blocks [B][sum_r] of ck (cv)
   uint8_t* wcache;
   const float* ck;
   const float* cv;
   const int32_t* pos;
-  int32_t capacity, sum_rk, sum_rv;
+  int32_t capacity, sum_rk, sum_rv, n_parts;
 };
 
 // Sequence b and head h of work-group (unit) idx.  Work-group i runs on XCD
@@ -512,10 +513,17 @@ void k_decode(DecodeArgs a, HeadTab ht) {
     nactive = wid == 0 && tnew >= 0 && lane < 32 && 8 * nseg < (nkv ? rv : rk);
     if (nactive) {
       const float* src = nkv ? a.cv + size_t(b) * a.sum_rv + loff_v : a.ck + size_t(b) * a.sum_rk + loff_k;
+      const size_t pstride = size_t(a.B) * (nkv ? a.sum_rv : a.sum_rk);
       const float4 x0 = *reinterpret_cast<const float4*>(src + 8 * nseg);
       const float4 x1 = *reinterpret_cast<const float4*>(src + 8 * nseg + 4);
       nv[0] = x0.x; nv[1] = x0.y; nv[2] = x0.z; nv[3] = x0.w;
       nv[4] = x1.x; nv[5] = x1.y; nv[6] = x1.z; nv[7] = x1.w;
+      for (int q = 1; q < a.n_parts; ++q) {   // further partial sums, added in order
+        const float4 y0 = *reinterpret_cast<const float4*>(src + q * pstride + 8 * nseg);
+        const float4 y1 = *reinterpret_cast<const float4*>(src + q * pstride + 8 * nseg + 4);
+        nv[0] += y0.x; nv[1] += y0.y; nv[2] += y0.z; nv[3] += y0.w;
+        nv[4] += y1.x; nv[5] += y1.y; nv[6] += y1.z; nv[7] += y1.w;
+      }
     }
   }
 
@@ -1251,6 +1259,7 @@ int launch_decode(const lr_attn_plan& p, int32_t layer, const void* cache, const
   a.capacity = p.desc.capacity;
   a.sum_rk = L.sum_rk;
   a.sum_rv = L.sum_rv;
+  a.n_parts = app ? app->n_parts : 1;
   const unsigned units = unsigned(p.desc.batch) * unsigned(p.desc.n_heads);
   const dim3 grid(units * unsigned(sp.n_split));
   hipStream_t st = static_cast<hipStream_t>(stream);

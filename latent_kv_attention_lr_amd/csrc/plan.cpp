@@ -288,6 +288,23 @@ lr_status lr_attn_project_latent(const lr_attn_plan* p, int32_t layer, const voi
   return hip_status(lr::launch_project(*p, layer, x, n_tokens, embed, packed, ck, cv, stream));
 }
 
+int32_t lr_attn_project_parts(const lr_attn_plan* p, int32_t layer, int32_t n_tokens, int32_t embed) {
+  if (!p || layer < 0 || layer >= p->desc.n_layers || n_tokens < 1 || embed < 32 || embed % 32 != 0)
+    return 0;
+  return lr::project_parts(*p, layer, n_tokens, embed);
+}
+
+lr_status lr_attn_project_latent_parts(const lr_attn_plan* p, int32_t layer, const void* x,
+                                       int32_t n_tokens, int32_t embed, const void* packed,
+                                       int32_t n_parts, float* ck, float* cv, void* stream) {
+  const lr_status st = check_project(p, layer, x, embed, packed);
+  if (st != LR_OK) return st;
+  if (n_tokens < 0 || !ck || !cv || !aligned(ck, 16) || !aligned(cv, 16)) return LR_EINVAL;
+  if (n_parts < 1 || n_parts > lr::kMaxProjectParts || n_parts > embed / 32) return LR_EINVAL;
+  if (n_tokens == 0) return LR_OK;
+  return hip_status(lr::launch_project(*p, layer, x, n_tokens, embed, packed, ck, cv, stream, n_parts));
+}
+
 size_t lr_attn_project_workspace_bytes(const lr_attn_plan* p, int32_t n_new) {
   if (!p || n_new < 1 || n_new > p->desc.capacity) return 0;
   size_t best = 0;
@@ -318,11 +335,24 @@ lr_status lr_attn_project_append(const lr_attn_plan* p, int32_t layer, void* cac
   return hip_status(lr::launch_append(*p, layer, cache, ck, cv, pos, n_new, stream));
 }
 
-static lr_status decode_common(const lr_attn_plan* p, int32_t layer, const void* cache,
-                               const int32_t* len, int32_t max_len, const void* q,
-                               const void* bk, const void* bv, float scale, void* out,
-                               void* ws, size_t ws_bytes, void* stream, bool explicit_form,
-                               const lr::AppendInputs* app = nullptr) {
+namespace {
+// A launch's threads are counted in 32 bits: the decode grid (units x splits
+// work-groups of waves x 64 threads) and the merge grid (units x 512) must
+// each hold fewer than 2^32 threads.
+bool decode_fits(const lr_attn_plan& p, int32_t layer, int32_t max_len, bool explicit_form) {
+  const lr::Split s = explicit_form ? lr::explicit_split(p, layer, max_len) : lr::choose_split(p, layer, max_len);
+  const uint64_t units = static_cast<uint64_t>(p.desc.batch) * static_cast<uint64_t>(p.desc.n_heads);
+  const uint64_t limit = 0xffffffffull;
+  if (units * static_cast<uint64_t>(s.n_split) * static_cast<uint64_t>(s.waves) * 64u > limit) return false;
+  return s.n_split == 1 || units * 512u <= limit;
+}
+}  // namespace
+
+// Every check of a decode call, in the order the errors are reported.
+static lr_status decode_check(const lr_attn_plan* p, int32_t layer, const void* cache,
+                              const int32_t* len, int32_t max_len, const void* q, const void* bk,
+                              const void* bv, float scale, void* out, void* ws, size_t ws_bytes,
+                              bool explicit_form) {
   if (!p) return LR_EINVAL;
   if (layer < 0 || layer >= p->desc.n_layers) return LR_ERANGE;
   if (max_len < 1 || max_len > p->desc.capacity) return LR_ERANGE;
@@ -332,9 +362,22 @@ static lr_status decode_common(const lr_attn_plan* p, int32_t layer, const void*
       !aligned(bv, 16) || !aligned(out, 16))
     return LR_EINVAL;
   if (explicit_form && p->desc.io_dtype != LR_DT_BF16) return LR_EUNSUPPORTED;
+  if (!decode_fits(*p, layer, max_len, explicit_form)) return LR_ERANGE;
   const size_t need = explicit_form ? 0 : lr::workspace_bytes(*p, max_len);
   if (need > 0 && (!ws || ws_bytes < need)) return LR_EWORKSPACE;
   if (ws && !aligned(ws, 16)) return LR_EINVAL;
+  return LR_OK;
+}
+
+static lr_status decode_common(const lr_attn_plan* p, int32_t layer, const void* cache,
+                               const int32_t* len, int32_t max_len, const void* q,
+                               const void* bk, const void* bv, float scale, void* out,
+                               void* ws, size_t ws_bytes, void* stream, bool explicit_form,
+                               const lr::AppendInputs* app = nullptr) {
+  const lr_status st = decode_check(p, layer, cache, len, max_len, q, bk, bv, scale, out, ws,
+                                    ws_bytes, explicit_form);
+  if (st != LR_OK) return st;
+  const size_t need = explicit_form ? 0 : lr::workspace_bytes(*p, max_len);
   return hip_status(lr::launch_decode(*p, layer, cache, len, max_len, q, bk, bv, scale, out,
                                       need > 0 ? ws : nullptr, stream, explicit_form, app));
 }
@@ -358,6 +401,50 @@ lr_status lr_attn_append_decode(const lr_attn_plan* p, int32_t layer, void* cach
   const lr::AppendInputs app{cache, ck, cv, pos};
   return decode_common(p, layer, cache, len, max_len, q, bk, bv, scale, out, ws, ws_bytes, stream,
                        false, &app);
+}
+
+namespace {
+// Bytes of the projection partials of one decode step of a layer (one token
+// per sequence): n_parts blocks of [batch][sum_r] fp32, K then V, 256-aligned.
+size_t step_partials_bytes(const lr_attn_plan& p, int32_t layer, int32_t embed) {
+  const size_t parts = static_cast<size_t>(lr::project_parts(p, layer, p.desc.batch, embed));
+  return latent_ws_bytes(p.layers[layer], parts * static_cast<size_t>(p.desc.batch));
+}
+}  // namespace
+
+size_t lr_attn_project_decode_workspace_bytes(const lr_attn_plan* p, int32_t max_len, int32_t embed) {
+  if (!p || max_len < 1 || max_len > p->desc.capacity || embed < 32 || embed % 32 != 0) return 0;
+  size_t best = 0;
+  for (int32_t l = 0; l < p->desc.n_layers; ++l) best = std::max(best, step_partials_bytes(*p, l, embed));
+  return best + lr::workspace_bytes(*p, max_len);
+}
+
+lr_status lr_attn_project_append_decode(const lr_attn_plan* p, int32_t layer, void* cache,
+                                        const void* x, int32_t embed, const void* packed,
+                                        const int32_t* pos, const int32_t* len, int32_t max_len,
+                                        const void* q, const void* bk, const void* bv, float scale,
+                                        void* out, void* ws, size_t ws_bytes, void* stream) {
+  lr_status st = check_project(p, layer, x, embed, packed);
+  if (st != LR_OK) return st;
+  if (!pos || !aligned(pos, 4)) return LR_EINVAL;
+  if (!ws || !aligned(ws, 256)) return ws ? LR_EINVAL : LR_EWORKSPACE;
+  const size_t pbytes = step_partials_bytes(*p, layer, embed);
+  if (ws_bytes < pbytes) return LR_EWORKSPACE;
+  void* dws = static_cast<char*>(ws) + pbytes;
+  st = decode_check(p, layer, cache, len, max_len, q, bk, bv, scale, out, dws, ws_bytes - pbytes, false);
+  if (st != LR_OK) return st;
+  const auto& L = p->layers[layer];
+  const int32_t B = p->desc.batch;
+  const int32_t parts = lr::project_parts(*p, layer, B, embed);
+  float* pk = static_cast<float*>(ws);
+  float* pv = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                       round256(static_cast<size_t>(parts) * B * L.sum_rk * sizeof(float)));
+  st = hip_status(lr::launch_project(*p, layer, x, B, embed, packed, pk, pv, stream, parts));
+  if (st != LR_OK) return st;
+  lr::AppendInputs app{cache, pk, pv, pos, parts};
+  const size_t need = lr::workspace_bytes(*p, max_len);
+  return hip_status(lr::launch_decode(*p, layer, cache, len, max_len, q, bk, bv, scale, out,
+                                      need > 0 ? dws : nullptr, stream, false, &app));
 }
 
 lr_status lr_attn_append_decode_noalloc(const lr_attn_plan* p, int32_t layer, void* cache,

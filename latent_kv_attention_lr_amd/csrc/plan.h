@@ -57,6 +57,9 @@ struct AppendInputs {
   const float* ck;
   const float* cv;
   const int32_t* pos;
+  // ck, cv hold n_parts blocks of [batch][sum_r] partial sums (stride batch x
+  // sum_r), added in block order to give the latents
+  int32_t n_parts = 1;
 };
 int launch_decode(const lr_attn_plan& p, int32_t layer, const void* cache, const int32_t* len,
                   int32_t max_len, const void* q, const void* bk, const void* bv, float scale,
@@ -68,8 +71,14 @@ int launch_decode(const lr_attn_plan& p, int32_t layer, const void* cache, const
 size_t packed_projection_elems(const lr_attn_plan& p, int32_t layer, int32_t embed);
 int launch_pack_projection(const lr_attn_plan& p, int32_t layer, int32_t embed, const void* wk,
                            const void* wv, void* packed, void* stream);
+// With n_parts > 1, E is split into n_parts ranges and part q's sums are
+// written at ck + q * n_tokens * sum_rk (cv likewise); their sum in part
+// order is the latent.  project_parts: the part count the fused step uses.
+constexpr int kMaxProjectParts = 8;
+int project_parts(const lr_attn_plan& p, int32_t layer, int32_t n_tokens, int32_t embed);
 int launch_project(const lr_attn_plan& p, int32_t layer, const void* x, int32_t n_tokens,
-                   int32_t embed, const void* packed, float* ck, float* cv, void* stream);
+                   int32_t embed, const void* packed, float* ck, float* cv, void* stream,
+                   int32_t n_parts = 1);
 // Hybrid FFN (ffn.hip, ffn_host.cpp): byte offsets of the packed weight
 // sections and, for a call on T tokens, of the workspace buffers.
 struct FfnLayout {

@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "plan.h"
 
 namespace {
@@ -29,23 +31,27 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kLdsBytes = 128 * 1024 + 64 * 16;   // activation phase + row padding
+constexpr int kLdsBytes = 128 * 1024 + 64 * 16;   // largest activation phase + row padding
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 struct ProjArgs {
   const uint16_t* x;   // bf16 [T][E]
   const uint16_t* wp;  // packed factors: [k_tiles + v_tiles][E / 32][64 lanes][8]
-  float* ck;           // fp32 [T][nk]
-  float* cv;           // fp32 [T][nv]
+  float* ck;           // fp32 [n_parts][T][nk]
+  float* cv;           // fp32 [n_parts][T][nv]
   int32_t T, E, nk, nv;
   int32_t k_tiles, row_tiles;   // 16-row tiles of W^K; of W^K and W^V together
   int32_t t_blocks, tb_stride;  // token blocks; token blocks per grid pass
-  int32_t units;                // work-groups per token block: ceil(row_tiles / RT)
+  int32_t units;                // work-groups per token block and part: ceil(row_tiles / RT)
+  int32_t n_parts;              // E is split into this many ranges of steps, each summed
+                                // into its own output block (1: the whole sum)
 };
 
-// Work-group (RT 16-row tiles, block of 16 NT tokens) over all of E:
-//   c[t][n] = sum_e x[t][e] w[n][e]
+// Work-group (RT 16-row tiles, block of 16 NT tokens, part q of E):
+//   c_q[t][n] = sum_{e in part q} x[t][e] w[n][e]
+// where part q covers steps [q S / n_parts, (q + 1) S / n_parts) of the
+// S = E / 32 MFMA steps (one part: all of E, and c_0 = c),
 // with v_mfma_f32_16x16x32_bf16 (latent rows = MFMA rows, tokens = columns;
 // lane (i, g) = (lane & 15, lane >> 4) supplies row/column i, elements 8 g ..
 // 8 g + 7 of a step, and receives rows 4 g .. 4 g + 3 of column i).  E is
@@ -61,23 +67,32 @@ __global__ __launch_bounds__(NW * 64) void k_project(ProjArgs a) {
   constexpr int RS = EP * 2 + 16;              // LDS bytes per token row (padded)
   constexpr int XV = TOK * EP / 8;             // 16-byte activation pieces per phase
   constexpr int XPT = (XV + NW * 64 - 1) / (NW * 64);
-  static_assert(TOK * RS <= kLdsBytes, "activation phase exceeds LDS");
-  static_assert(NW * RT * NT * 64 * 16 <= kLdsBytes, "reduction exceeds LDS");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  // LDS: one activation phase, reused for the wavefront partials at the end;
+  // sized per instance so that small instances leave room for more
+  // work-groups per compute unit
+  constexpr int LDSB = TOK * RS > NW * RT * NT * 64 * 16 ? TOK * RS : NW * RT * NT * 64 * 16;
+  static_assert(LDSB <= kLdsBytes, "activation phase exceeds LDS");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDSB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop control
   const int li = lane & 15, lg = lane >> 4;
   const int unit = blockIdx.x % a.units;
-  const int steps = a.E >> 5, phases = (steps + PS - 1) / PS;
+  const int part = (blockIdx.x / a.units) % a.n_parts;
+  const int all_steps = a.E >> 5;
+  const int sb = int(int64_t(part) * all_steps / a.n_parts);
+  const int steps = int(int64_t(part + 1) * all_steps / a.n_parts) - sb;   // >= 1
+  const int phases = (steps + PS - 1) / PS;
+  const uint16_t* xs = a.x + 32 * sb;          // the part's first element of every token row
+  const size_t osk = size_t(part) * a.T * a.nk, osv = size_t(part) * a.T * a.nv;
   // row tiles RT unit .. RT unit + RT - 1 (a tile past the last is loaded as
   // the last and never stored)
   const uint16_t* wl[RT];
 #pragma unroll
   for (int r = 0; r < RT; ++r)
-    wl[r] = a.wp + size_t(min(RT * unit + r, a.row_tiles - 1)) * steps * 512 + 8 * lane;
+    wl[r] = a.wp + (size_t(min(RT * unit + r, a.row_tiles - 1)) * all_steps + sb) * 512 + 8 * lane;
 
-  for (int tb = blockIdx.x / a.units; tb < a.t_blocks; tb += a.tb_stride) {
+  for (int tb = blockIdx.x / (a.units * a.n_parts); tb < a.t_blocks; tb += a.tb_stride) {
     const int t0 = TOK * tb;
     uint4 wb[2][RT][SPW];
     uint4 xb[XPT];
@@ -96,7 +111,7 @@ __global__ __launch_bounds__(NW * 64) void k_project(ProjArgs a) {
       for (int m = 0; m < XPT; ++m) {
         const int q = min(tid + m * NW * 64, XV - 1);
         const int row = q / (EP / 8), col = q % (EP / 8);
-        xb[m] = ld16(a.x + size_t(min(t0 + row, a.T - 1)) * a.E + min(p * EP + 8 * col, a.E - 8));
+        xb[m] = ld16(xs + size_t(min(t0 + row, a.T - 1)) * a.E + min(p * EP + 8 * col, 32 * steps - 8));
       }
     };
     auto store_x = [&]() {
@@ -170,7 +185,7 @@ __global__ __launch_bounds__(NW * 64) void k_project(ProjArgs a) {
       const int rt = RT * unit + r;
       const bool isv = rt >= a.k_tiles;
       const int t = t0 + tt, n = 16 * (isv ? rt - a.k_tiles : rt) + nn, N = isv ? a.nv : a.nk;
-      if (rt < a.row_tiles && t < a.T && n < N) (isv ? a.cv : a.ck)[size_t(t) * N + n] = v;
+      if (rt < a.row_tiles && t < a.T && n < N) (isv ? a.cv + osv : a.ck + osk)[size_t(t) * N + n] = v;
     }
     __syncthreads();
   }
@@ -219,8 +234,63 @@ int launch_pack_projection(const lr_attn_plan& p, int32_t layer, int32_t embed, 
   return int(hipGetLastError());
 }
 
+namespace {
+// Launch shape of the projection without an E split: token-block size in
+// 16-token tiles, whether work-groups take two row tiles, work-groups per
+// token block, token blocks.
+struct ProjShape {
+  int nt;
+  bool two;
+  int units, t_blocks;
+};
+ProjShape proj_shape(const lr_attn_plan::Layer& L, int32_t n_tokens) {
+  // Up to 48 tokens: one block of 16, 32 or 48 tokens per work-group and one
+  // row tile.  From 49 tokens on: blocks of 32 tokens and two row tiles per
+  // work-group, so that every staged activation serves 32 latent rows (the
+  // LDS re-reads of the activations bound this case: 64 tokens at E = 4096
+  // over 4096 rows measured 15.4 us with 64-token blocks and one tile, 12.7 us
+  // so).  Larger calls loop over token blocks.
+  const int row_tiles = (L.sum_rk + 15) / 16 + (L.sum_rv + 15) / 16;
+  const int col_tiles = (n_tokens + 15) / 16;   // n_tokens >= 1
+  ProjShape s;
+  s.two = col_tiles >= 4;
+  s.nt = s.two ? 2 : col_tiles;
+  s.units = s.two ? (row_tiles + 1) / 2 : row_tiles;
+  s.t_blocks = (col_tiles + s.nt - 1) / s.nt;
+  return s;
+}
+}  // namespace
+
+// Work-groups a split projection aims for: at decode sizes the product moves
+// each work-group's factor block (tens of KB) in about one memory round trip,
+// so it needs every compute unit busy with two or more resident work-groups,
+// not long work-groups.  Only the one-tile, 16-token instance is split: its
+// split parts use the 33 KB activation phase, so several work-groups share a
+// compute unit.  Measured on MI355X, MALL-cold (copies of the factors
+// cycled), E = 4096, us per launch for 1 / 2 / 3 / 4 / 8 parts:
+//   16 tokens, 128 row tiles  8.6 / 6.4 / 9.1 / 6.0 / 7.8
+//    8 tokens, 192 row tiles  9.0 / 9.8 / 12.7 / 8.3 / 10.8
+// while 32 and 64 tokens were fastest unsplit (11.3 and 14.7 us; 12.4 and
+// 16.8 with two parts): their larger activation blocks leave one work-group
+// per compute unit, so more work-groups only add rounds.  Uneven parts (3)
+// lose to the powers of two.
+#ifndef LR_PROJECT_TARGET_WGS
+#define LR_PROJECT_TARGET_WGS 512
+#endif
+
+int project_parts(const lr_attn_plan& p, int32_t layer, int32_t n_tokens, int32_t embed) {
+  const ProjShape s = proj_shape(p.layers[layer], n_tokens);
+  if (s.two || s.nt != 1) return 1;
+  const int64_t wgs = int64_t(s.units) * s.t_blocks;
+  const int64_t cap = std::min<int64_t>(kMaxProjectParts, embed / 32 / 8);   // >= 8 steps a part
+  int64_t parts = 1;
+  while (parts * 2 <= cap && parts * wgs < LR_PROJECT_TARGET_WGS) parts *= 2;
+  return int(parts);
+}
+
 int launch_project(const lr_attn_plan& p, int32_t layer, const void* x, int32_t n_tokens,
-                   int32_t embed, const void* packed, float* ck, float* cv, void* stream) {
+                   int32_t embed, const void* packed, float* ck, float* cv, void* stream,
+                   int32_t n_parts) {
   const auto& L = p.layers[layer];
   ProjArgs a;
   a.x = static_cast<const uint16_t*>(x);
@@ -233,25 +303,22 @@ int launch_project(const lr_attn_plan& p, int32_t layer, const void* x, int32_t 
   a.nv = L.sum_rv;
   a.k_tiles = (L.sum_rk + 15) / 16;
   a.row_tiles = a.k_tiles + (L.sum_rv + 15) / 16;
-  // Up to 48 tokens: one block of 16, 32 or 48 tokens per work-group and one
-  // row tile.  From 49 tokens on: blocks of 32 tokens and two row tiles per
-  // work-group, so that every staged activation serves 32 latent rows (the
-  // LDS re-reads of the activations bound this case: 64 tokens at E = 4096
-  // over 4096 rows measured 15.4 us with 64-token blocks and one tile, 12.7 us
-  // so).  Larger calls loop over token blocks.
-  const int col_tiles = (n_tokens + 15) / 16;   // n_tokens >= 1
-  const bool two = col_tiles >= 4;
-  const int nt = two ? 2 : col_tiles;
-  a.units = two ? (a.row_tiles + 1) / 2 : a.row_tiles;
-  a.t_blocks = (col_tiles + nt - 1) / nt;
-  const int max_tb = (1 << 20) / a.units;   // at most 2^20 work-groups
+  const ProjShape sh = proj_shape(L, n_tokens);
+  a.units = sh.units;
+  a.t_blocks = sh.t_blocks;
+  a.n_parts = n_parts;
+  const int max_tb = (1 << 20) / (a.units * n_parts);   // at most 2^20 work-groups
   a.tb_stride = a.t_blocks < max_tb ? a.t_blocks : max_tb;
-  const dim3 grid(unsigned(a.units) * unsigned(a.tb_stride));
+  const dim3 grid(unsigned(a.units) * unsigned(n_parts) * unsigned(a.tb_stride));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // activation phases of 2048 elements up to 32 tokens, 1024 above
-  if (two) hipLaunchKernelGGL((k_project<2, 8, 4, 2>), grid, dim3(512), 0, s, a);
-  else if (nt == 1) hipLaunchKernelGGL((k_project<1, 8, 8, 1>), grid, dim3(512), 0, s, a);
-  else if (nt == 2) hipLaunchKernelGGL((k_project<2, 8, 8, 1>), grid, dim3(512), 0, s, a);
+  // activation phases of 2048 elements up to 32 tokens (1024 where a part
+  // has at most 32 steps), 1024 above
+  const bool short_part = (embed / 32) / n_parts <= 32;
+  if (sh.two) hipLaunchKernelGGL((k_project<2, 8, 4, 2>), grid, dim3(512), 0, s, a);
+  else if (sh.nt == 1 && short_part) hipLaunchKernelGGL((k_project<1, 8, 4, 1>), grid, dim3(512), 0, s, a);
+  else if (sh.nt == 1) hipLaunchKernelGGL((k_project<1, 8, 8, 1>), grid, dim3(512), 0, s, a);
+  else if (sh.nt == 2 && short_part) hipLaunchKernelGGL((k_project<2, 8, 4, 1>), grid, dim3(512), 0, s, a);
+  else if (sh.nt == 2) hipLaunchKernelGGL((k_project<2, 8, 8, 1>), grid, dim3(512), 0, s, a);
   else hipLaunchKernelGGL((k_project<3, 8, 4, 1>), grid, dim3(512), 0, s, a);
   return int(hipGetLastError());
 }

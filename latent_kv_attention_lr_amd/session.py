@@ -17,8 +17,9 @@ from . import (LR_DT_BF16, LR_DT_F32, LR_HEAD_DIM, lr_attn_append_decode, lr_att
                lr_attn_decode, lr_attn_decode_explicit, lr_attn_factor_elems,
                lr_attn_head_layout_get, lr_attn_latent_elems, lr_attn_plan_create,
                lr_attn_pack_projection, lr_attn_packed_projection_elems, lr_attn_plan_destroy,
-               lr_attn_project_append, lr_attn_project_latent, lr_attn_project_workspace_bytes,
-               lr_attn_workspace_bytes)
+               lr_attn_project_append, lr_attn_project_append_decode,
+               lr_attn_project_decode_workspace_bytes, lr_attn_project_latent,
+               lr_attn_project_workspace_bytes, lr_attn_workspace_bytes)
 
 
 class DecodeSession:
@@ -46,6 +47,7 @@ class DecodeSession:
         self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
         self.lengths = torch.zeros(batch, dtype=torch.int32, device=self.device)
         self._proj_ws: Optional[torch.Tensor] = None   # latents of project_append, grown on demand
+        self._step_ws: Optional[torch.Tensor] = None   # workspace of project_append_decode
         self.proj: List[Optional[tuple]] = [None] * n_layers   # (embed, packed factors) per layer
 
     def close(self) -> None:
@@ -199,3 +201,28 @@ class DecodeSession:
         ws = self._proj_ws
         lr_attn_project_append(self.plan, layer, self.caches[layer], x, E, self.proj[layer][1], pos,
                                n_new, ws, 0 if ws is None else ws.numel(), stream)
+
+    def project_append_decode(self, layer: int, x: torch.Tensor, pos: torch.Tensor, q: torch.Tensor,
+                              out: torch.Tensor, max_len: int, lengths: Optional[torch.Tensor] = None,
+                              softmax_scale: Optional[float] = None, stream=None) -> None:
+        """One decode step from activations x [batch, embed]: generate the new
+        token's latents, append them at pos[b] and attend (two launches)."""
+        E = self._projection_input(layer, x)
+        if x.numel() != self.batch * E:
+            raise ValueError("x must hold one token per sequence: [batch, embed]")
+        self._check_pos(pos)
+        if self.bk[layer] is None:
+            raise ValueError("factors of this layer are not set")
+        shape = (self.batch, self.n_heads, LR_HEAD_DIM)
+        if q.shape != shape or out.shape != shape or q.dtype != self.torch_dtype or out.dtype != self.torch_dtype:
+            raise ValueError("q/out must be [B, H, 128] of the session dtype")
+        if not (q.is_contiguous() and out.is_contiguous()):
+            raise ValueError("q and out must be contiguous")
+        need = lr_attn_project_decode_workspace_bytes(self.plan, self.capacity, E)
+        if self._step_ws is None or self._step_ws.numel() < need:
+            self._step_ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        ws = self._step_ws
+        scale = 1.0 / math.sqrt(LR_HEAD_DIM) if softmax_scale is None else softmax_scale
+        lr_attn_project_append_decode(self.plan, layer, self.caches[layer], x, E, self.proj[layer][1],
+                                      pos, self.lengths if lengths is None else lengths, max_len, q,
+                                      self.bk[layer], self.bv[layer], scale, out, ws, ws.numel(), stream)

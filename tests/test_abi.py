@@ -352,6 +352,75 @@ def test_split_partials_of_any_plan_fit_the_noalloc_scratch(qfmt, rank):
     assert 0 < worst <= NOALLOC_SCRATCH_BYTES, worst
 
 
+def _project_append_decode(p, **kw):
+    a = dict(layer=0, cache=FAKE, x=FAKE, embed=4096, packed=FAKE, pos=FAKE, len=FAKE, max_len=100,
+             q=FAKE, bk=FAKE, bv=FAKE, scale=0.088, out=FAKE, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return lr._lib.lr_attn_project_append_decode(p, a["layer"], a["cache"], a["x"], a["embed"], a["packed"],
+                                                 a["pos"], a["len"], a["max_len"], a["q"], a["bk"],
+                                                 a["bv"], a["scale"], a["out"], a["ws"], a["ws_bytes"],
+                                                 None)
+
+
+def test_project_append_decode_argument_errors_before_launch():
+    p = _plan(capacity=3000)
+    try:
+        assert _project_append_decode(None) == lr.LR_EINVAL
+        assert _project_append_decode(p, layer=1) == lr.LR_ERANGE
+        for name in ("cache", "x", "packed", "pos", "len", "q", "bk", "bv", "out"):
+            assert _project_append_decode(p, **{name: None}) == lr.LR_EINVAL, name
+        assert _project_append_decode(p, x=FAKE + 8) == lr.LR_EINVAL
+        assert _project_append_decode(p, pos=FAKE + 2) == lr.LR_EINVAL
+        assert _project_append_decode(p, cache=FAKE + 16) == lr.LR_EINVAL
+        assert _project_append_decode(p, embed=40) == lr.LR_EINVAL
+        assert _project_append_decode(p, embed=0) == lr.LR_EINVAL
+        assert _project_append_decode(p, max_len=0) == lr.LR_ERANGE
+        assert _project_append_decode(p, max_len=3001) == lr.LR_ERANGE
+        assert _project_append_decode(p, scale=float("nan")) == lr.LR_EINVAL
+        need = lr.lr_attn_project_decode_workspace_bytes(p, 3000, 4096)
+        assert need >= lr.lr_attn_workspace_bytes(p, 3000) + 2 * 2 * 4 * (32 + 16 + 8 + 128)
+        assert _project_append_decode(p, max_len=3000, ws=None) == lr.LR_EWORKSPACE
+        assert _project_append_decode(p, max_len=3000, ws_bytes=need - 1) == lr.LR_EWORKSPACE
+        assert _project_append_decode(p, ws=FAKE + 16) == lr.LR_EINVAL   # 256-aligned
+        assert lr.lr_attn_project_decode_workspace_bytes(p, 3001, 4096) == 0
+        assert lr.lr_attn_project_decode_workspace_bytes(p, 100, 48) == 0
+    finally:
+        lr.lr_attn_plan_destroy(p)
+
+
+def test_project_latent_parts_argument_errors_before_launch():
+    p = _plan()
+    f = lr._lib.lr_attn_project_latent_parts
+    try:
+        assert lr.lr_attn_project_parts(p, 0, 2, 4096) >= 1
+        assert lr.lr_attn_project_parts(p, 1, 2, 4096) == 0
+        assert lr.lr_attn_project_parts(p, 0, 0, 4096) == 0
+        assert lr.lr_attn_project_parts(p, 0, 2, 48) == 0
+        assert lr.lr_attn_project_parts(p, 0, 2, 32) == 1       # never more parts than steps / 8
+        assert f(None, 0, FAKE, 2, 4096, FAKE, 2, FAKE, FAKE, None) == lr.LR_EINVAL
+        assert f(p, 1, FAKE, 2, 4096, FAKE, 2, FAKE, FAKE, None) == lr.LR_ERANGE
+        assert f(p, 0, FAKE, 2, 4096, FAKE, 0, FAKE, FAKE, None) == lr.LR_EINVAL
+        assert f(p, 0, FAKE, 2, 4096, FAKE, 9, FAKE, FAKE, None) == lr.LR_EINVAL
+        assert f(p, 0, FAKE, 2, 64, FAKE, 3, FAKE, FAKE, None) == lr.LR_EINVAL   # 2 steps of E
+        assert f(p, 0, FAKE, 2, 4096, FAKE, 2, FAKE + 4, FAKE, None) == lr.LR_EINVAL
+        assert f(p, 0, FAKE, -1, 4096, FAKE, 2, FAKE, FAKE, None) == lr.LR_EINVAL
+        assert f(p, 0, FAKE, 0, 4096, FAKE, 2, FAKE, FAKE, None) == lr.LR_OK   # no-op
+    finally:
+        lr.lr_attn_plan_destroy(p)
+
+
+def test_decode_rejects_more_threads_than_one_grid_holds():
+    """batch x n_heads work-groups of 512-1024 threads above 2^32 threads in
+    all is a range error for every decode entry point, not a launch."""
+    p = _plan(batch=1 << 18, n_heads=64, capacity=8, rank_k=[32] * 64, rank_v=[32] * 64)
+    try:
+        assert _decode(p, max_len=8) == lr.LR_ERANGE
+        assert _decode(p, fn="lr_attn_decode_explicit", max_len=8) == lr.LR_ERANGE
+        assert _append_decode(p, max_len=8) == lr.LR_ERANGE
+    finally:
+        lr.lr_attn_plan_destroy(p)
+
+
 def test_project_append_argument_errors_before_launch():
     p = _plan()
     try:

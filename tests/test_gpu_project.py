@@ -269,11 +269,171 @@ def test_project_append_codes_are_roundings_of_oracle_latents(qfmt):
                 assert np.all(np.abs(q[0].astype(np.float64) - want) <= 0.5 + slack), (kv, h, b)
 
 
-def test_decode_over_generated_latents_matches_oracle_chain():
+def _step_parts(s, E):
+    """Projection parts of the fused step, read back from the workspace size
+    (n_parts blocks of [batch][sum r] fp32 partials, K then V, 256-aligned)."""
+    from latent_kv_attention_lr_amd import (lr_attn_project_decode_workspace_bytes,
+                                            lr_attn_workspace_bytes)
+    pbytes = (lr_attn_project_decode_workspace_bytes(s.plan, s.capacity, E)
+              - lr_attn_workspace_bytes(s.plan, s.capacity))
+    nk, nv = s.latent_elems(0, 0), s.latent_elems(0, 1)
+    for parts in range(1, 9):
+        r256 = lambda n: (n + 255) // 256 * 256
+        if r256(parts * s.batch * nk * 4) + r256(parts * s.batch * nv * 4) == pbytes:
+            return parts
+    raise AssertionError(f"no part count gives {pbytes} bytes")
+
+
+@pytest.mark.parametrize("E,B,ranks_k,ranks_v,parts", [
+    (1024, 1, [8, 32, 24], [16, 40, 8], 4),
+    (2080, 5, [8, 64, 32, 96], [40, 16, 128, 8], 8),
+    (4096, 64, [8, 64, 32, 96], [40, 16, 128, 8], 1),
+    (4096, 16, [32] * 32, [32] * 32, 4),
+])
+def test_project_append_decode_integer_inputs_equal_two_calls(E, B, ranks_k, ranks_v, parts):
+    """With small-integer activations and factors every partial sum is exact,
+    so the split projection's parts, added in order inside the fused append,
+    give exactly lr_attn_project_latent's latents: cache bytes and outputs of
+    the one-step entry point equal project_latent + append_decode bit for bit
+    (part counts 1 to 8, one- and two-tile projection shapes)."""
+    say(f"project_append_decode integers E={E} B={B} heads={len(ranks_k)}")
+    rng = np.random.default_rng(E + B)
+    H, ctx = len(ranks_k), 150
+    a = _session(ranks_k, ranks_v, batch=B, cap=ctx + 1)
+    b = _session(ranks_k, ranks_v, batch=B, cap=ctx + 1)
+    assert _step_parts(a, E) == parts
+    ak = torch.from_numpy(rng.integers(-3, 4, (E, sum(ranks_k))).astype(np.float32))
+    av = torch.from_numpy(rng.integers(-3, 4, (E, sum(ranks_v))).astype(np.float32))
+    for s in (a, b):
+        _set_factors(s, ak, av)
+    bk = torch.from_numpy(rng.standard_normal((sum(ranks_k), 128)) / 6).to(torch.bfloat16).to(DEV)
+    bv = torch.from_numpy(rng.standard_normal((sum(ranks_v), 128)) / 6).to(torch.bfloat16).to(DEV)
+    pk = torch.from_numpy(rng.standard_normal((B, ctx, sum(ranks_k))).astype(np.float32)).to(DEV)
+    pv = torch.from_numpy(rng.standard_normal((B, ctx, sum(ranks_v))).astype(np.float32)).to(DEV)
+    for s in (a, b):
+        s.set_factors(0, bk, bv)
+        s.append(0, pk, pv, torch.zeros(B, dtype=torch.int32, device=DEV))
+    x = torch.from_numpy(rng.integers(-3, 4, (B, E)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    q = torch.from_numpy(rng.standard_normal((B, H, 128))).to(torch.bfloat16).to(DEV)
+    pos = torch.full((B,), ctx, dtype=torch.int32, device=DEV)
+    oa = torch.empty(B, H, 128, dtype=torch.bfloat16, device=DEV)
+    ob = torch.empty_like(oa)
+    a.lengths.fill_(ctx + 1)
+    b.lengths.fill_(ctx + 1)
+    a.project_append_decode(0, x, pos, q, oa, ctx + 1)
+    ck, cv = b.project(0, x)
+    b.append_decode(0, ck, cv, pos, q, ob, ctx + 1)
+    torch.cuda.synchronize()
+    assert torch.equal(a.caches[0], b.caches[0])
+    assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
+
+
+def test_project_append_decode_full_layer_shape_matches_oracle_chain():
+    """The one-step entry point at the int8 workload's layer shape (E 4096,
+    batch 16, 32 heads of rank 32, four projection parts): random activations
+    of the workload's distribution, a 300-token prefix generated the same way;
+    sampled units match the oracle's chain x -> latents -> quantise -> attend."""
+    w = lrgen.workload(1)
+    E, H, B, ctx = w.embed, w.n_heads, w.batch, 300
+    rk, rv = w.ranks_k[0], w.ranks_v[0]
+    s = DecodeSession(1, B, H, ctx + 1, w.qfmt, LR_DT_BF16, [rk], [rv], device=DEV)
+    assert _step_parts(s, E) == 4
+    ak = lrgen.down_factors(w, 0, 0).to(torch.bfloat16).float()
+    av = lrgen.down_factors(w, 0, 1).to(torch.bfloat16).float()
+    bk = lrgen.up_factors(w, 0, 0).to(DEV).contiguous()
+    bv = lrgen.up_factors(w, 0, 1).to(DEV).contiguous()
+    s.set_factors(0, bk, bv)
+    _set_factors(s, ak, av)
+    xs = torch.stack([lrgen.activations(w, 0, b, 0, ctx + 1) for b in range(B)]).to(torch.bfloat16)
+    s.project_append(0, xs[:, :ctx].contiguous().to(DEV), torch.zeros(B, dtype=torch.int32, device=DEV))
+    q = lrgen.queries(w, 0, 0).to(DEV).contiguous()
+    out = torch.empty(B, H, w.head_dim, dtype=torch.bfloat16, device=DEV)
+    s.lengths.fill_(ctx + 1)
+    s.project_append_decode(0, xs[:, ctx].contiguous().to(DEV),
+                            torch.full((B,), ctx, dtype=torch.int32, device=DEV), q, out, ctx + 1)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    scale = 1.0 / math.sqrt(w.head_dim)
+    offk, offv = lrgen.head_offsets(rk), lrgen.head_offsets(rv)
+    for b in (0, 11):
+        say(f"full-shape step, oracle chain row {b}")
+        ref_k = oracle.latents(xs[b].double().numpy(), ak.double().numpy()).astype(np.float32)
+        ref_v = oracle.latents(xs[b].double().numpy(), av.double().numpy()).astype(np.float32)
+        for h in range(0, H, 3):
+            ref = oracle.attend(w.qfmt, ref_k[:, offk[h]:offk[h] + rk[h]], ref_v[:, offv[h]:offv[h] + rv[h]],
+                                q[b, h].double().cpu().numpy(),
+                                bk[offk[h]:offk[h] + rk[h]].double().cpu().numpy(),
+                                bv[offv[h]:offv[h] + rv[h]].double().cpu().numpy(), scale)
+            assert within(got[b, h], ref, TOL_BF16), (b, h)
+
+
+@pytest.mark.parametrize("idx,T", [(1, 16), (4, 8), (2, 64)])
+def test_project_parts_sum_to_latents_within_rounding_bound(idx, T):
+    """lr_attn_project_latent_parts at a workload's decode shape (one- and
+    two-tile instances): one part is lr_attn_project_latent bit for bit; for
+    2 to 8 parts the parts added in order stay within the fp32 summation bound
+    of the oracle's latents."""
+    from latent_kv_attention_lr_amd import lr_attn_project_latent_parts
+    w, x, ak, av = _workload_inputs(idx, T)
+    s = _session(w.ranks_k[0], w.ranks_v[0], w.qfmt, batch=1, cap=64)
+    wk, wv = _set_factors(s, ak, av)
+    xd = x.to(torch.bfloat16).to(DEV).contiguous()
+    T, E = xd.shape
+    nk, nv = s.latent_elems(0, 0), s.latent_elems(0, 1)
+    ck1, cv1 = s.project(0, xd)
+    for parts in range(1, 9):
+        say(f"project parts workload {idx} parts={parts}")
+        pk = torch.empty(parts, T, nk, dtype=torch.float32, device=DEV)
+        pv = torch.empty(parts, T, nv, dtype=torch.float32, device=DEV)
+        lr_attn_project_latent_parts(s.plan, 0, xd, T, E, s.proj[0][1], parts, pk, pv)
+        torch.cuda.synchronize()
+        if parts == 1:
+            assert torch.equal(pk[0], ck1) and torch.equal(pv[0], cv1)
+        sk, sv = pk[0].clone(), pv[0].clone()
+        for q in range(1, parts):
+            sk += pk[q]
+            sv += pv[q]
+        _check_bound(sk.cpu().numpy(), x.to(torch.bfloat16).float(), ak)
+        _check_bound(sv.cpu().numpy(), x.to(torch.bfloat16).float(), av)
+
+
+@pytest.mark.parametrize("T", [1, 16, 40, 64, 100])
+def test_project_parts_integer_inputs_sum_exactly(T):
+    """Small-integer inputs: every part's sums are exact, so for any part
+    count the parts added in order equal the oracle's latents exactly (one-,
+    two- and three-block and two-tile instances, E of 65 steps so that parts
+    are uneven)."""
+    from latent_kv_attention_lr_amd import lr_attn_project_latent_parts
+    ranks_k, ranks_v, E = [8, 64, 32, 96], [40, 16, 128, 8], 2080
+    rng = np.random.default_rng(T)
+    s = _session(ranks_k, ranks_v)
+    x = torch.from_numpy(rng.integers(-3, 4, (T, E)).astype(np.float32))
+    ak = torch.from_numpy(rng.integers(-3, 4, (E, sum(ranks_k))).astype(np.float32))
+    av = torch.from_numpy(rng.integers(-3, 4, (E, sum(ranks_v))).astype(np.float32))
+    _set_factors(s, ak, av)
+    ref_k = oracle.latents(x.double().numpy(), ak.double().numpy()).astype(np.float32)
+    ref_v = oracle.latents(x.double().numpy(), av.double().numpy()).astype(np.float32)
+    xd = x.to(torch.bfloat16).to(DEV).contiguous()
+    for parts in (1, 2, 3, 5, 8):
+        say(f"project parts integers T={T} parts={parts}")
+        pk = torch.empty(parts, T, sum(ranks_k), dtype=torch.float32, device=DEV)
+        pv = torch.empty(parts, T, sum(ranks_v), dtype=torch.float32, device=DEV)
+        lr_attn_project_latent_parts(s.plan, 0, xd, T, E, s.proj[0][1], parts, pk, pv)
+        torch.cuda.synchronize()
+        sk, sv = pk[0].clone(), pv[0].clone()
+        for q in range(1, parts):
+            sk += pk[q]
+            sv += pv[q]
+        assert np.array_equal(sk.cpu().numpy(), ref_k) and np.array_equal(sv.cpu().numpy(), ref_v)
+
+
+@pytest.mark.parametrize("one_step", [False, True])
+def test_decode_over_generated_latents_matches_oracle_chain(one_step):
     """Cache built by project_append from activations (prefill in chunks, then
     decode steps generating the new token's latents and attending with the
-    fused append): outputs match the oracle's chain x -> latents -> quantise ->
-    attend within the decode tolerance."""
+    fused append, as two calls or through the one-step entry point): outputs
+    match the oracle's chain x -> latents -> quantise -> attend within the
+    decode tolerance."""
     w = lrgen.workload(0)
     E, H, B, ctx, steps = w.embed, w.n_heads, 2, 100, 3
     rk, rv = w.ranks_k[0], w.ranks_v[0]
@@ -297,11 +457,14 @@ def test_decode_over_generated_latents_matches_oracle_chain():
         T = ctx + st + 1
         q = lrgen.normal(lrgen.stream_key(w.seed, lrgen.TAG_Q, 0, st), 0, B * H * w.head_dim, 1.0)
         q = q.view(B, H, w.head_dim).to(torch.bfloat16).to(DEV).contiguous()
-        ck, cv = s.project(0, xs[:, ctx + st].contiguous().to(DEV))
         pos = torch.full((B,), ctx + st, dtype=torch.int32, device=DEV)
         out = torch.empty(B, H, w.head_dim, dtype=torch.bfloat16, device=DEV)
         s.lengths.fill_(T)
-        s.append_decode(0, ck, cv, pos, q, out, T)
+        if one_step:
+            s.project_append_decode(0, xs[:, ctx + st].contiguous().to(DEV), pos, q, out, T)
+        else:
+            ck, cv = s.project(0, xs[:, ctx + st].contiguous().to(DEV))
+            s.append_decode(0, ck, cv, pos, q, out, T)
         torch.cuda.synchronize()
         got = out.float().cpu().numpy()
         for b in range(B):
