@@ -7,11 +7,18 @@ decode (batch 16, 32 heads, head_dim 128, rank-32 per-head latents, int8 per
 token, 4096 cached tokens of which 576 are image-prefix tokens, 128 decode
 steps).  Prints one JSON line.
 
-  value        whole-job tokens/s = batch * steps / wall time of the steps
+The layer's cache (156 MB) is smaller than MI355X's 256 MiB last-level cache,
+so the timed steps cycle through copies of it, as the layers of a model do:
+every launch reads its cache from HBM (MALL-cold).  The same launches on one
+copy back to back are reported beside it as the warm figures.
+
+  value        whole-job tokens/s = batch * steps * copies / wall time
   roofline     the decode kernel's algorithmic HBM bytes per launch divided
-               by its average duration (HIP events on the launch stream)
-  cpu_baseline the CPU oracle (plain fp64) timed on this host's cores on a
-               sample of one step's (b, h) units, scaled to the whole step
+               by its average duration (HIP events on the launch stream
+               around the graph of the timed launches)
+  cpu_baseline the CPU oracle (plain fp64) timed on this host's threads on
+               step 0 of whole batch rows (all of them when they fit about
+               20 thread-seconds), scaled to the whole step
 """
 from __future__ import annotations
 
@@ -92,8 +99,12 @@ def parse():
     ap.add_argument("--ffn", action="store_true",
                     help="time the hybrid low-rank/dense W8A8 FFN decode (lr_ffn_decode) instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold-steps", type=int, default=16,
-                    help="extra untimed-in-value steps with the 256 MiB last-level cache flushed before each")
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="copies of the caches the timed steps cycle through (default: enough that "
+                         "each launch reads its cache from HBM; 1 = one copy, partly cache-warm for "
+                         "caches smaller than the 256 MiB last-level cache)")
+    ap.add_argument("--no-warm-leg", action="store_true",
+                    help="skip the warm measurement (one cache copy, launches back to back)")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="only run warmup + this many steps (for rocprofv3); no CPU baseline")
     ap.add_argument("--no-graph", action="store_true",
@@ -140,31 +151,74 @@ def projection_bytes(w, rk, rv, tokens):
     return 2 * w.embed * n + 2 * tokens * w.embed + 4 * tokens * n
 
 
-def cpu_baseline(run, n_units_target=128):
-    """Time the oracle over a sample of step-0 units on the host's cores."""
-    import numpy as np
+def host_threads():
+    """Threads for the CPU baseline: the CPUs this process may run on, capped
+    by OMP_NUM_THREADS where the host sets it (a shared host's CPU share)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# fp64 multiply-adds per second of one host thread running the oracle
+# (measured on an x86 host); only used to size the CPU sample beforehand
+ORACLE_FMA_PER_S = 1.3e9
+CPU_SAMPLE_THREAD_S = 20.0
+
+
+def cpu_sample_units(w):
+    """The (layer, b, h) units whose step-0 decode the oracle is timed on:
+    whole batch rows (every layer and head of them), as many as fit about
+    CPU_SAMPLE_THREAD_S thread-seconds of oracle work; all units when the
+    whole step fits.  Every batch row does the same work, so the time of the
+    rows scales exactly to the step."""
+    T = w.context + 1
+    row_fma = sum(T * (rk + rv) * w.head_dim
+                  for l in range(w.n_layers) for rk, rv in zip(w.ranks_k[l], w.ranks_v[l]))
+    rows = int(max(1, min(w.batch, CPU_SAMPLE_THREAD_S * ORACLE_FMA_PER_S // row_fma)))
+    return [(l, b, h) for l in range(w.n_layers) for b in range(rows) for h in range(w.n_heads)], rows
+
+
+def cpu_baseline(run, rows):
+    """Time the oracle on step 0 of the sampled batch rows, on the host's threads."""
     from concurrent.futures import ThreadPoolExecutor
     import oracle
 
     w = run.w
-    units = sorted(run.keep)[:n_units_target]
+    units = sorted(run.keep)
+    threads = host_threads()
     jobs = [run.unit_inputs(u, 0) for u in units]
-    threads = max(1, min(16, os.cpu_count() or 1))
-    # repeat the sample until about 16 thread-seconds of oracle work are done
-    passes, wall = 0, 0.0
+    # one untimed unit pages the oracle library and the inputs in
+    oracle.attend(w.qfmt, *jobs[0], run.scale)
     with ThreadPoolExecutor(threads) as pool:
-        while passes == 0 or wall * threads < 16.0:
-            t0 = time.perf_counter()
-            list(pool.map(lambda j: oracle.attend(w.qfmt, *j, run.scale), jobs))
-            wall += time.perf_counter() - t0
-            passes += 1
+        t0 = time.perf_counter()
+        list(pool.map(lambda j: oracle.attend(w.qfmt, *j, run.scale), jobs))
+        wall = time.perf_counter() - t0
+    step_s = wall * w.batch / rows
+    whole = rows == w.batch
     units_total = w.n_layers * w.batch * w.n_heads
-    step_s = wall / passes * units_total / len(units)
     return {"value": w.batch / step_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(units)} of {units_total} (b,h) units of decode step 0 "
-                      f"(T={run.context + 1}), fp64 explicit reconstruction, {passes} passes; "
-                      f"{wall:.2f} s wall on {threads} threads, per-pass time scaled "
-                      f"x{units_total / len(units):.1f} to one step",
+            "sample": (f"decode step 0 (T={run.context + 1}), {len(units)} of {units_total} "
+                       f"(layer, b, h) units = batch rows 0..{rows - 1} of {w.batch}"
+                       + ("" if whole else f", time scaled x{w.batch / rows:g} to the whole step "
+                                           "(every batch row does the same work)")
+                       + f"; fp64 explicit reconstruction; {wall:.2f} s wall on {threads} threads"),
+            "extrapolated": not whole,
+            "cpu_model": cpu_model(),
+            "host_cpus_visible": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
+            else os.cpu_count(),
             "step_s": step_s}
 
 
@@ -261,6 +315,22 @@ def ffn_bench(args):
     print(json.dumps(result), flush=True)
 
 
+MALL_BYTES = 256 << 20     # MI355X last-level cache (Infinity Cache)
+
+
+def choose_replicas(total_cache_bytes, requested):
+    """Copies of the layer stack's caches that the timed steps cycle through.
+    Between two visits of one copy the other copies are read, so with at
+    least twice the last-level cache of other bytes in between every launch
+    reads its cache from HBM, as a layer of a deep model does.  Caches that
+    are already that large need no copy."""
+    if requested:
+        return requested
+    if total_cache_bytes >= 2 * MALL_BYTES:
+        return 1
+    return int(min(64, math.ceil(2 * MALL_BYTES / total_cache_bytes) + 1))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -273,6 +343,7 @@ def main():
     import torch
     import harness
     import lrgen
+    import latent_kv_attention_lr_amd as lrb
     from latent_kv_attention_lr_amd import LR_DT_BF16
 
     if not torch.cuda.is_available():
@@ -299,9 +370,14 @@ def main():
     warm = args.warmup
     if args.profile_steps:
         steps = args.profile_steps
-    n_cpu = 4 * w.n_heads if w.batch >= 4 else w.batch * w.n_heads
-    keep = [] if (args.no_cpu_baseline or args.profile_steps) else \
-        [(0, b, h) for b in range(min(w.batch, n_cpu // w.n_heads)) for h in range(w.n_heads)]
+    fused = not (args.explicit or args.separate_append)
+    if args.with_projection and not fused:
+        print("bench.py: --with-projection times the fused step only", file=sys.stderr)
+        sys.exit(2)
+    cpu_rows = 0
+    keep = []
+    if not (args.no_cpu_baseline or args.profile_steps):
+        keep, cpu_rows = cpu_sample_units(w)
     nsteps_inputs = max(steps, warm, 1)
     print(f"[bench] setting up {w.name}", file=sys.stderr, flush=True)
     run = harness.WorkloadRun(w, io_dtype=LR_DT_BF16, device=dev, keep=keep,
@@ -309,6 +385,8 @@ def main():
     sess = run.sess
     L = w.n_layers
     ctx = run.context
+    B = w.batch
+    scale = 1.0 / math.sqrt(w.head_dim)
     # every step's inputs are resident before timing: latents, q, pos, len
     per = []
     for s in range(nsteps_inputs):
@@ -316,10 +394,10 @@ def main():
         for l in range(L):
             ck, cv, q, pos = run.step_tensors(l, s)
             layers.append((ck, cv, q))
-        ln = torch.full((w.batch,), ctx + s + 1, dtype=torch.int32, device=dev)
-        pos = torch.full((w.batch,), ctx + s, dtype=torch.int32, device=dev)
+        ln = torch.full((B,), ctx + s + 1, dtype=torch.int32, device=dev)
+        pos = torch.full((B,), ctx + s, dtype=torch.int32, device=dev)
         per.append((layers, pos, ln))
-    out = torch.empty(w.batch, w.n_heads, w.head_dim, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(B, w.n_heads, w.head_dim, dtype=torch.bfloat16, device=dev)
     if args.copy_calibration_mib:
         src = torch.ones(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -328,68 +406,119 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    fused = not (args.explicit or args.separate_append)
-    if args.with_projection and not fused:
-        print("bench.py: --with-projection times the fused step only", file=sys.stderr)
-        sys.exit(2)
+    # ---- copies of the prefilled caches: the timed steps visit copy 0, 1, ..,
+    # R-1 of every layer in turn, so each launch finds its cache outside the
+    # last-level cache (as layer l of a model does after the other layers ran)
+    total_cache = sum(sess.caches[l].numel() for l in range(L))
+    R = choose_replicas(total_cache, args.replicas)
+    caches = [[sess.caches[l]] + [sess.caches[l].clone() for _ in range(R - 1)] for l in range(L)]
+    reuse_bytes = R * total_cache     # cache bytes read between two reads of one byte
+    torch.cuda.synchronize()
 
-    # latent generation: per layer the factors as [sum r, E] bf16 (A transposed),
-    # per step and layer the new tokens' activations [B, E] bf16, and the fp32
-    # latent buffers the projection writes
+    # latent generation: per layer (and copy) the factors as [sum r, E] bf16
+    # (A transposed), packed once; per step and layer the new tokens'
+    # activations [B, E] bf16, and the fp32 latent buffers the projection writes
     proj = None
-    if args.with_projection or not (args.no_projection_leg or args.profile_steps):
+    want_proj = args.with_projection or not (args.no_projection_leg or args.profile_steps)
+    if want_proj:
+        packed = []
         for l in range(L):
             wk, wv = (lrgen.down_factors(w, l, kv, device=dev).t().contiguous().to(torch.bfloat16)
                       for kv in (0, 1))
             sess.set_projection(l, wk, wv)     # packed once per layer, as in serving
             del wk, wv
-        wts = [sess.proj[l][1] for l in range(L)]
+            packed.append(sess.proj[l][1])
         xs = [[torch.cat([lrgen.activations(w, l, b, ctx + s, ctx + s + 1, device=dev)
-                          for b in range(w.batch)]).to(torch.bfloat16).contiguous()
+                          for b in range(B)]).to(torch.bfloat16).contiguous()
                for l in range(L)] for s in range(nsteps_inputs)]
-        lat = [(torch.empty(w.batch, sess.latent_elems(l, 0), dtype=torch.float32, device=dev),
-                torch.empty(w.batch, sess.latent_elems(l, 1), dtype=torch.float32, device=dev))
+        lat = [(torch.empty(B, sess.latent_elems(l, 0), dtype=torch.float32, device=dev),
+                torch.empty(B, sess.latent_elems(l, 1), dtype=torch.float32, device=dev))
                for l in range(L)]
-        proj = (wts, xs, lat)
+        # the split projection of the one-step path: parts per layer, partial sums
+        parts = [lrb.lr_attn_project_parts(sess.plan, l, B, w.embed) for l in range(L)]
+        plat = [(torch.empty(parts[l], B, sess.latent_elems(l, 0), dtype=torch.float32, device=dev),
+                 torch.empty(parts[l], B, sess.latent_elems(l, 1), dtype=torch.float32, device=dev))
+                for l in range(L)]
+        step_ws = torch.empty(lrb.lr_attn_project_decode_workspace_bytes(sess.plan, sess.capacity, w.embed),
+                              dtype=torch.uint8, device=dev)
+        proj = (packed, xs, lat)
 
-    def one_layer(l, s, append=True, project=args.with_projection):
-        """Step s of layer l: append the step's token and attend (one fused launch), or
-        with append=False (separate launches only) just the decode launch."""
+    def check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed: {lrb.lr_attn_strerror(rc)}")
+
+    lib = lrb._lib
+    ws_ptr, ws_n = sess.workspace.data_ptr(), sess.workspace.numel()
+
+    def project(l, s, st, wts=None):
+        packed, xs, lat = proj
+        check(lib.lr_attn_project_latent(sess.plan, l, xs[s][l].data_ptr(), B, w.embed,
+                                         (wts or packed)[l].data_ptr(), lat[l][0].data_ptr(),
+                                         lat[l][1].data_ptr(), st), "lr_attn_project_latent")
+        return lat[l]
+
+    def project_split(l, s, st, wts):
+        packed, xs, lat = proj
+        check(lib.lr_attn_project_latent_parts(sess.plan, l, xs[s][l].data_ptr(), B, w.embed,
+                                               wts[l].data_ptr(), parts[l], plat[l][0].data_ptr(),
+                                               plat[l][1].data_ptr(), st), "lr_attn_project_latent_parts")
+
+    def one_step(l, s, r, st, wts):
+        """Step s of layer l on cache copy r from activations: lr_attn_project_append_decode."""
+        packed, xs, lat = proj
+        layers, pos, ln = per[s]
+        q = layers[l][2]
+        check(lib.lr_attn_project_append_decode(
+            sess.plan, l, caches[l][r].data_ptr(), xs[s][l].data_ptr(), w.embed, wts[l].data_ptr(),
+            pos.data_ptr(), ln.data_ptr(), ctx + s + 1, q.data_ptr(), sess.bk[l].data_ptr(),
+            sess.bv[l].data_ptr(), scale, out.data_ptr(), step_ws.data_ptr(), step_ws.numel(), st),
+            "lr_attn_project_append_decode")
+
+    def launch(l, s, r, st, append=True, project_first=False, wts=None):
+        """Step s of layer l on cache copy r, on stream st: append the step's token and
+        attend (one fused launch), or append and decode launches; with append=False
+        (separate launches only) just the decode launch.  project_first: the whole
+        step from activations (lr_attn_project_append_decode)."""
+        if project_first:
+            one_step(l, s, r, st, wts or proj[0])
+            return
         layers, pos, ln = per[s]
         ck, cv, q = layers[l]
-        if project:
-            wts, xs, lat = proj
-            ck, cv = sess.project(l, xs[s][l], ck=lat[l][0], cv=lat[l][1])
+        cache = caches[l][r].data_ptr()
+        common = (ln.data_ptr(), ctx + s + 1, q.data_ptr(), sess.bk[l].data_ptr(),
+                  sess.bv[l].data_ptr(), scale, out.data_ptr(), ws_ptr, ws_n, st)
         if fused:
-            sess.append_decode(l, ck.view(w.batch, -1), cv.view(w.batch, -1), pos, q, out,
-                               ctx + s + 1, lengths=ln)
+            check(lib.lr_attn_append_decode(sess.plan, l, cache, ck.data_ptr(), cv.data_ptr(),
+                                            pos.data_ptr(), *common), "lr_attn_append_decode")
             return
         if append:
-            sess.append(l, ck, cv, pos)
-        sess.decode(l, q, out, ctx + s + 1, lengths=ln, explicit=args.explicit)
+            check(lib.lr_attn_append_latent(sess.plan, l, cache, ck.data_ptr(), cv.data_ptr(),
+                                            pos.data_ptr(), 1, st), "lr_attn_append_latent")
+        fn = lib.lr_attn_decode_explicit if args.explicit else lib.lr_attn_decode
+        check(fn(sess.plan, l, cache, *common), "decode")
 
-    def step(s):
-        for l in range(L):
-            one_layer(l, s)
+    def cur():
+        return torch.cuda.current_stream().cuda_stream
 
-    print(f"[bench] warmup {warm} steps", file=sys.stderr, flush=True)
+    def steps_all(copies, **kw):
+        def fn():
+            st = cur()
+            for s in range(steps):
+                for l in range(L):
+                    for r in copies:
+                        launch(l, s, r, st, **kw)
+        return fn
+
+    print(f"[bench] warmup {warm} steps, {R} cache cop{'y' if R == 1 else 'ies'}", file=sys.stderr,
+          flush=True)
     for s in range(warm):
-        step(s)
+        st = cur()
+        for l in range(L):
+            for r in range(R):
+                launch(l, s, r, st, project_first=args.with_projection)
     torch.cuda.synchronize()
 
-    # ---- the timed steps: exactly `steps` steps from the configured context,
-    # launched as one HIP graph (append + decode per step and layer) so the
-    # host issues nothing per step.
     use_graph = not args.no_graph
-
-    def timed_steps():
-        for s in range(steps):
-            step(s)
-
-    def decodes_only():
-        for s in range(steps):
-            for l in range(L):
-                one_layer(l, s, append=False, project=False)
 
     def capture(fn):
         g = torch.cuda.CUDAGraph()
@@ -401,65 +530,80 @@ def main():
         torch.cuda.current_stream().wait_stream(cap)
         g.replay()                          # the first replay uploads the graph: untimed
         torch.cuda.synchronize()
-        return g
+        return g.replay
 
-    run_timed = capture(timed_steps).replay if use_graph else timed_steps
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    run_timed()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    print(f"[bench] timed {steps} steps in {wall * 1e3:.2f} ms ({'graph' if use_graph else 'eager'})",
-          file=sys.stderr, flush=True)
+    def timed(fn):
+        """(wall seconds, event seconds) of one call of fn, HIP events on the current stream."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, e0.elapsed_time(e1) / 1e3
 
-    # ---- the decode kernel alone: the same `steps` decode launches (each with
-    # its step's lengths; fused: with its append) back to back, between two HIP
-    # events on the launch stream; average launch duration = elapsed / launches.
-    run_dec = capture(decodes_only).replay if use_graph else decodes_only
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    run_dec()
-    e1.record()
-    torch.cuda.synchronize()
-    dec_avg_s = e0.elapsed_time(e1) / (steps * L) / 1e3
+    # ---- the timed steps: exactly `steps` steps of every cache copy from the
+    # configured context, as one HIP graph, so the host issues nothing per step
+    run_timed = steps_all(range(R), project_first=args.with_projection)
+    wall, ev = timed(capture(run_timed) if use_graph else run_timed)
+    launches = steps * L * R
+    print(f"[bench] timed {steps} steps x {R} copies in {wall * 1e3:.2f} ms "
+          f"({'graph' if use_graph else 'eager'})", file=sys.stderr, flush=True)
 
-    rk_all = w.ranks_k
-    rv_all = w.ranks_v
+    # ---- the decode kernel alone.  Fused: the timed launches are exactly the
+    # decode launches (with their appends).  Otherwise the same decode launches
+    # without the append launches, in a graph of their own.
+    if fused and not args.with_projection:
+        dec_s = ev / launches
+    else:
+        dec_only = steps_all(range(R), append=False)
+        if fused:
+            dec_only = steps_all(range(R))
+        _, ev_d = timed(capture(dec_only) if use_graph else dec_only)
+        dec_s = ev_d / launches
+    rk_all, rv_all = w.ranks_k, w.ranks_v
     bytes_launch = 0.0
     per_tok_bytes = 0
     for s in range(steps):
         for l in range(L):
-            b_, per_tok_bytes = algorithmic_bytes(w, [ctx + s + 1] * w.batch, rk_all[l], rv_all[l])
+            b_, per_tok_bytes = algorithmic_bytes(w, [ctx + s + 1] * B, rk_all[l], rv_all[l])
             bytes_launch += b_ + (append_bytes(w, rk_all[l], rv_all[l]) if fused else 0)
     bytes_launch /= steps * L
-    achieved = bytes_launch / dec_avg_s / 1e9
-
+    achieved = bytes_launch / dec_s / 1e9
+    lat_dtype = "int8" if w.qfmt == 0 else "int4"
     result = {
         "metric": "decode attention tokens/sec (1 GPU) + achieved HBM GB/s as % of MI355X peak",
-        "value": w.batch * steps / wall,
+        "value": B * steps * R / wall,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": steps,
         "warmup": warm,
-        "ms_per_step": wall / steps * 1e3,
+        "ms_per_step": wall / (steps * R) * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": f"{lat_dtype}-latent,bf16-io,f32-acc",
         "data": "synthetic",
         "config": {
             "workload": w.name,
-            "layers": L, "batch": w.batch, "heads": w.n_heads, "head_dim": w.head_dim,
+            "layers": L, "batch": B, "heads": w.n_heads, "head_dim": w.head_dim,
             "rank": ("greedy allocation" if alloc_info else "per-head table") if w.uniform_rank is None
                     else w.uniform_rank,
             "context": ctx, "image_prefix": w.prefix,
             "latents": "int8 per-token fp32 scale" if w.qfmt == 0 else "int4 group-32 fp16 scale",
             "q_factors_out": "bf16", "accumulation": "f32",
             "decode_form": "explicit" if args.explicit else "absorbed",
-            "step": "append fused into the decode launch" if fused else "append launch + decode launch",
+            "step": ("latent generation from activations, then append fused into the decode launch"
+                     if args.with_projection else
+                     "append fused into the decode launch" if fused else "append launch + decode launch"),
             "parallelism": "single GPU",
             "launch": "hip graph of all timed steps" if use_graph else "eager",
+            "cache_copies": R,
+            "mall": ("cold: a cache byte is read again only after %.0f MB of cache reads "
+                     "(last-level cache 268 MB)" % (reuse_bytes / 1e6)) if reuse_bytes >= 2 * MALL_BYTES
+                    else ("partly warm: a cache byte is read again after %.0f MB of cache reads"
+                          % (reuse_bytes / 1e6)),
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -467,110 +611,94 @@ def main():
             "traffic": measured_traffic(w.name, "explicit" if args.explicit else "absorbed"),
             "kernel": "k_decode_explicit" if args.explicit else "k_decode", "bytes_per_launch": bytes_launch,
             "bytes_per_token_per_bh": per_tok_bytes / w.n_heads,
-            "avg_launch_us": dec_avg_s * 1e6,
+            "avg_launch_us": dec_s * 1e6,
+            "mall": "cold" if reuse_bytes >= 2 * MALL_BYTES else "partly warm",
         },
     }
 
+    # ---- warm leg (outside the timed region): the same decode launches on one
+    # cache copy back to back, so part of a cache smaller than the last-level
+    # cache is still there from the previous step
+    if not (args.no_warm_leg or args.profile_steps) and R > 1 and total_cache < MALL_BYTES:
+        warm_fn = steps_all([0])
+        wall_w, ev_w = timed(capture(warm_fn) if use_graph else warm_fn)
+        if fused and not args.with_projection:
+            warm_s = ev_w / (steps * L)
+            result["roofline"]["warm_avg_launch_us"] = warm_s * 1e6
+            result["roofline"]["warm_achieved"] = bytes_launch / warm_s / 1e9
+            result["roofline"]["warm_frac"] = bytes_launch / warm_s / 1e9 / PEAK_HBM_GBS
+        result["warm_value"] = B * steps / wall_w
+
     # ---- latent generation alone (outside the timed region): the projection
-    # of each step's new tokens, every layer, back to back in a graph between
-    # two HIP events (warm: the factors stay in the last-level cache), then
-    # one launch at a time after a flush (cold, as when the factors of other
-    # layers have been read in between).
+    # of each step's new tokens on copies of the packed factors, cycled so that
+    # each launch reads its factors from HBM (cold), and on one copy back to
+    # back (warm: the factors stay in the last-level cache)
     if proj is not None and not args.profile_steps:
-        import latent_kv_attention_lr_amd as lrb
-        wts, xs, lat = proj
+        packed, xs, lat = proj
         nrep = max(1, min(steps, 64))
+        pbytes = sum(projection_bytes(w, rk_all[l], rv_all[l], B) for l in range(L)) / L
+        packed_total = sum(p.numel() * 2 for p in packed)
+        Rp = choose_replicas(packed_total, 0)
+        pcopies = [packed] + [[p.clone() for p in packed] for _ in range(Rp - 1)]
 
-        def proj_launch(s, l):
-            # the current stream: torch's, or the capture stream inside capture()
-            rc = lrb._lib.lr_attn_project_latent(
-                sess.plan, l, xs[s][l].data_ptr(), w.batch, w.embed, wts[l].data_ptr(),
-                lat[l][0].data_ptr(), lat[l][1].data_ptr(), torch.cuda.current_stream().cuda_stream)
-            if rc != 0:
-                raise RuntimeError(f"projection launch failed: {lrb.lr_attn_strerror(rc)}")
+        def projections(copies, fn1):
+            def fn():
+                st = cur()
+                for s in range(nrep):
+                    for l in range(L):
+                        for r in copies:
+                            fn1(l, s, st, pcopies[r])
+            return fn
 
-        def projections():
-            for s in range(nrep):
-                for l in range(L):
-                    proj_launch(s, l)
+        def cold_warm(fn1):
+            _, ev_c = timed(capture(projections(range(Rp), fn1)) if use_graph else projections(range(Rp), fn1))
+            _, ev_w = timed(capture(projections([0], fn1)) if use_graph else projections([0], fn1))
+            return ev_c / (nrep * L * Rp), ev_w / (nrep * L)
 
-        projections()
-        run_proj = capture(projections).replay if use_graph else projections
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        run_proj()
-        e1.record()
-        torch.cuda.synchronize()
-        pw_s = e0.elapsed_time(e1) / (nrep * L) / 1e3
-        pbytes = sum(projection_bytes(w, rk_all[l], rv_all[l], w.batch) for l in range(L)) / L
-        flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)
-        cold = []
-        for s in range(min(16, nrep)):
-            for l in range(L):
-                flush.sum()
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                proj_launch(s, l)
-                b.record()
-                cold.append((a, b))
-        torch.cuda.synchronize()
-        pc_s = sum(a.elapsed_time(b) for a, b in cold) / len(cold) / 1e3
-        del flush
+        pc_s, pw_s = cold_warm(project_split)
+        uc_s, uw_s = cold_warm(project)
+        # parts partial sums are written and read once more by the decode launch
+        pbytes_split = sum(projection_bytes(w, rk_all[l], rv_all[l], B * parts[l]) -
+                           2 * B * parts[l] * w.embed + 2 * B * w.embed for l in range(L)) / L
         result["latent_generation"] = {
-            "kernel": "k_project", "entry_point": "lr_attn_project_latent",
+            "kernel": "k_project", "entry_point": "lr_attn_project_latent_parts",
+            "parts": parts[0] if L == 1 else parts,
             "bound": "hbm", "unit": "GB/s", "peak": PEAK_HBM_GBS,
-            "tokens_per_launch": w.batch, "embed": w.embed,
-            "bytes_per_launch": pbytes,
-            "avg_launch_us": pw_s * 1e6, "achieved": pbytes / pw_s / 1e9,
-            "frac": pbytes / pw_s / 1e9 / PEAK_HBM_GBS,
-            "cold_avg_launch_us": pc_s * 1e6, "cold_achieved": pbytes / pc_s / 1e9,
-            "cold_frac": pbytes / pc_s / 1e9 / PEAK_HBM_GBS,
+            "tokens_per_launch": B, "embed": w.embed,
+            "bytes_per_launch": pbytes_split,
+            "avg_launch_us": pc_s * 1e6, "achieved": pbytes_split / pc_s / 1e9,
+            "frac": pbytes_split / pc_s / 1e9 / PEAK_HBM_GBS,
+            "mall": "cold", "factor_copies": Rp,
+            "warm_avg_launch_us": pw_s * 1e6, "warm_achieved": pbytes_split / pw_s / 1e9,
+            "warm_frac": pbytes_split / pw_s / 1e9 / PEAK_HBM_GBS,
             "traffic": measured_projection_traffic(w.name),
-            "flops_per_launch": 2.0 * w.batch * w.embed * sum(sum(rk_all[l]) + sum(rv_all[l])
-                                                              for l in range(L)) / L,
+            "flops_per_launch": 2.0 * B * w.embed * sum(sum(rk_all[l]) + sum(rv_all[l])
+                                                        for l in range(L)) / L,
+            "unsplit": {"entry_point": "lr_attn_project_latent", "bytes_per_launch": pbytes,
+                        "avg_launch_us": uc_s * 1e6, "frac": pbytes / uc_s / 1e9 / PEAK_HBM_GBS,
+                        "warm_avg_launch_us": uw_s * 1e6,
+                        "warm_frac": pbytes / uw_s / 1e9 / PEAK_HBM_GBS},
         }
-        if args.with_projection:
-            result["config"]["step"] = ("latent generation from activations, then append fused "
-                                        "into the decode launch")
-
-    # ---- MALL-cold decode timing (outside the timed region): flush first.
-    # The launch between the two events goes straight to the C ABI with its
-    # arguments prepared beforehand, so no host work sits between them.
-    if args.cold_steps and not args.profile_steps:
-        import latent_kv_attention_lr_amd as lrb
-        flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)  # 512 MiB, read to evict
-        stream = torch.cuda.current_stream().cuda_stream
-        scale = 1.0 / math.sqrt(w.head_dim)
-        cold = []
-        for s in range(min(args.cold_steps, steps)):
-            for l in range(L):
-                layers, pos, ln = per[s]
-                ck, cv, q = layers[l]
-                common = (ln.data_ptr(), ctx + s + 1, q.data_ptr(), sess.bk[l].data_ptr(),
-                          sess.bv[l].data_ptr(), scale, out.data_ptr(), sess.workspace.data_ptr(),
-                          sess.workspace.numel(), stream)
-                if fused:
-                    fn, cargs = lrb._lib.lr_attn_append_decode, (
-                        sess.plan, l, sess.caches[l].data_ptr(), ck.data_ptr(), cv.data_ptr(),
-                        pos.data_ptr()) + common
-                else:
-                    sess.append(l, ck, cv, pos)
-                    fn = lrb._lib.lr_attn_decode_explicit if args.explicit else lrb._lib.lr_attn_decode
-                    cargs = (sess.plan, l, sess.caches[l].data_ptr()) + common
-                flush.sum()                      # reads 512 MiB: the 256 MiB last-level cache holds none of the cache
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                rc = fn(*cargs)
-                b.record()
-                if rc != 0:
-                    raise RuntimeError(f"decode launch failed: {lrb.lr_attn_strerror(rc)}")
-                cold.append((a, b))
-        torch.cuda.synchronize()
-        cold_s = sum(a.elapsed_time(b) for a, b in cold) / len(cold) / 1e3
-        result["roofline"]["cold_avg_launch_us"] = cold_s * 1e6
-        result["roofline"]["cold_achieved"] = bytes_launch / cold_s / 1e9
-        del flush
+        # ---- a whole step from activations: latents generated from x, then
+        # the fused append + decode, every layer's factors and cache cold
+        if fused:
+            def from_x():
+                st = cur()
+                for s in range(steps):
+                    for l in range(L):
+                        for r in range(R):
+                            launch(l, s, r, st, project_first=True, wts=pcopies[r % Rp])
+            wall_x, ev_x = timed(capture(from_x) if use_graph else from_x)
+            step_x = ev_x / (steps * R)
+            xbytes = bytes_launch + pbytes
+            result["step_from_activations"] = {
+                "entry_point": "lr_attn_project_append_decode",
+                "tokens_per_s": B * steps * R / wall_x, "us_per_step": step_x * 1e6,
+                "launches_per_layer": 2, "bytes_per_layer": xbytes,
+                "achieved": xbytes * L / step_x / 1e9,
+                "frac": xbytes * L / step_x / 1e9 / PEAK_HBM_GBS,
+            }
+        del pcopies
 
     # ---- practical read roof on this GPU (context for roofline.frac): a plain
     # streaming read of 1 GiB, which no last-level cache holds
@@ -580,14 +708,8 @@ def main():
         sink = torch.zeros(1, dtype=torch.int32, device=dev)
         for _ in range(3):
             lr_attn_probe_read(buf, buf.numel(), sink)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(10):
-            lr_attn_probe_read(buf, buf.numel(), sink)
-        e1.record()
-        torch.cuda.synchronize()
-        probe_gbs = buf.numel() * 10 / (e0.elapsed_time(e1) / 1e3) / 1e9
+        _, ev_p = timed(lambda: [lr_attn_probe_read(buf, buf.numel(), sink) for _ in range(10)])
+        probe_gbs = buf.numel() * 10 / ev_p / 1e9
         result["roofline"]["stream_read_probe"] = {
             "value": probe_gbs, "unit": "GB/s", "frac_of_peak": probe_gbs / PEAK_HBM_GBS,
             "kernel": "lr_attn_probe_read", "bytes": buf.numel(),
@@ -598,7 +720,7 @@ def main():
         result["rank_allocation"] = alloc_info
     if keep:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cb = cpu_baseline(run, n_cpu)
+        cb = cpu_baseline(run, cpu_rows)
         cb.pop("step_s")
         result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)

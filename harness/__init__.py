@@ -55,13 +55,18 @@ class WorkloadRun:
         return torch.stack(cks).contiguous(), torch.stack(cvs).contiguous()
 
     def _keep(self, layer: int, ck: torch.Tensor, cv: torch.Tensor) -> None:
-        for (l, b, h) in self.keep:
-            if l != layer:
-                continue
+        units = [u for u in self.keep if u[0] == layer]
+        if not units:
+            return
+        rows = sorted({b for (_, b, _) in units})
+        # one copy per kept batch row of the chunk, sliced per head on the host
+        hk = {b: ck[b].cpu().numpy() for b in rows}
+        hv = {b: cv[b].cpu().numpy() for b in rows}
+        for (l, b, h) in units:
             rk, rv = self.w.ranks_k[l][h], self.w.ranks_v[l][h]
             ok, ov = self.off_k[l][h], self.off_v[l][h]
-            self.kept[(l, b, h)][0].append(ck[b, :, ok:ok + rk].cpu().numpy())
-            self.kept[(l, b, h)][1].append(cv[b, :, ov:ov + rv].cpu().numpy())
+            self.kept[(l, b, h)][0].append(hk[b][:, ok:ok + rk])
+            self.kept[(l, b, h)][1].append(hv[b][:, ov:ov + rv])
 
     def setup(self) -> "WorkloadRun":
         """Factors, prefill of the context, and the inputs of every decode step."""
