@@ -339,6 +339,24 @@ __device__ __forceinline__ void unit_of(const DecodeArgs& a, const HeadTab& ht, 
 // meet q' entries that are zero (K) or accumulators that are never read (V).
 // With lm = 2 lanes per token, lane half hf takes the row's chunks hf,
 // hf + 2, hf + 4, ... (NC of them) of token `tok`; with lm = 1 chunks 0..NC-1.
+#ifndef LR_DECODE_NT_LOADS
+#define LR_DECODE_NT_LOADS 1
+#endif
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Cache bytes are read once per launch: non-temporal loads (the cache
+// policy's streaming hint) let them pass through the caches without
+// displacing what is reused.
+__device__ __forceinline__ u32x4_t ld_stream16(const uint8_t* p) {
+  if constexpr (LR_DECODE_NT_LOADS) return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  else return *reinterpret_cast<const u32x4_t*>(p);
+}
+template <typename T>
+__device__ __forceinline__ T ld_stream(const uint8_t* p) {
+  if constexpr (LR_DECODE_NT_LOADS) return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+  else return *reinterpret_cast<const T*>(p);
+}
+
 template <int NC>
 __device__ __forceinline__ void load_codes(const uint8_t* tile, int tok, int lm, int hf, int rb, uint32_t* w) {
 #pragma unroll
@@ -346,7 +364,7 @@ __device__ __forceinline__ void load_codes(const uint8_t* tile, int tok, int lm,
     const int cg = lm * c + hf;
     const int wc = rb - 16 * cg;
     const int off = wc > 0 ? 1024 * cg + min(wc, 16) * tok : 0;
-    const uint4 v = *reinterpret_cast<const uint4*>(tile + off);
+    const u32x4_t v = ld_stream16(tile + off);
     w[4 * c] = v.x; w[4 * c + 1] = v.y; w[4 * c + 2] = v.z; w[4 * c + 3] = v.w;
   }
 }
@@ -386,11 +404,11 @@ template <int QF, int NC, int NG>
 __device__ __forceinline__ void load_k(const uint8_t* kt, int tok, int lm, int hf, int rk, int rbk, TileRegs<NC, NG>& x) {
   load_codes<NC>(kt, tok, lm, hf, rbk, x.kw);
   if constexpr (QF == LR_Q_INT8_TOKEN) {
-    x.sk[0] = *reinterpret_cast<const float*>(kt + 64 * rbk + 4 * tok);
+    x.sk[0] = ld_stream<float>(kt + 64 * rbk + 4 * tok);
   } else {
 #pragma unroll
     for (int g = 0; g < NG; ++g)
-      x.sk[g] = half_bits_to_f32(*reinterpret_cast<const uint16_t*>(kt + 64 * rbk + 2 * (64 * min(g, (rk - 1) >> 5) + tok)));
+      x.sk[g] = half_bits_to_f32(ld_stream<uint16_t>(kt + 64 * rbk + 2 * (64 * min(g, (rk - 1) >> 5) + tok)));
   }
 }
 
@@ -398,11 +416,11 @@ template <int QF, int NC, int NG>
 __device__ __forceinline__ void load_v(const uint8_t* vt, int tok, int lm, int hf, int rv, int rbv, TileRegs<NC, NG>& x) {
   load_codes<NC>(vt, tok, lm, hf, rbv, x.vw);
   if constexpr (QF == LR_Q_INT8_TOKEN) {
-    x.sv[0] = *reinterpret_cast<const float*>(vt + 64 * rbv + 4 * tok);
+    x.sv[0] = ld_stream<float>(vt + 64 * rbv + 4 * tok);
   } else {
 #pragma unroll
     for (int g = 0; g < NG; ++g)
-      x.sv[g] = half_bits_to_f32(*reinterpret_cast<const uint16_t*>(vt + 64 * rbv + 2 * (64 * min(g, (rv - 1) >> 5) + tok)));
+      x.sv[g] = half_bits_to_f32(ld_stream<uint16_t>(vt + 64 * rbv + 2 * (64 * min(g, (rv - 1) >> 5) + tok)));
   }
 }
 
@@ -456,12 +474,20 @@ __attribute__((amdgpu_waves_per_eu(decode_occupancy<QF, R, LPT>(), decode_occupa
 void k_decode(DecodeArgs a, HeadTab ht) {
   constexpr bool INT8 = QF == LR_Q_INT8_TOKEN;
   constexpr bool PACKED = !INT8 && sizeof(IOT) == 2;
+  // int8 codes with bf16 I/O: K scores as integer dot products against q'
+  // held as two int8 levels (v_dot4: 4 codes per instruction)
+#ifndef LR_DECODE_DOT4
+#define LR_DECODE_DOT4 1
+#endif
+  constexpr bool DOT = LR_DECODE_DOT4 && INT8 && sizeof(IOT) == 2;
+  constexpr int QD = R / 4;                            // 32-bit words of one int8 level of q'
+  constexpr bool QD_IN_REGS = DOT && R <= 64 && LPT == 1;
   constexpr int VPC = INT8 ? 16 : 32;                  // values per 16-byte chunk
   constexpr int NC = R / VPC;                          // chunks per row in the bucket
   constexpr int NCL = NC / LPT;                        // chunks per lane
   constexpr int NG = INT8 ? 1 : NC;                    // scales per token
   constexpr int QW = PACKED ? R / 2 : R;               // 32-bit words of q'
-  constexpr bool Q_IN_REGS = R <= 32 && LPT == 1;      // 32 scalar registers at most
+  constexpr bool Q_IN_REGS = !DOT && R <= 32 && LPT == 1;   // 32 scalar registers at most
   constexpr int RPW = (R + NW - 1) / NW;               // B rows per wavefront
   constexpr bool PREFETCH_BV = RPW <= 4;
   static_assert(LPT == 1 || (LPT == 2 && INT8 && NC % 2 == 0), "two lanes per token: int8 only");
@@ -494,6 +520,7 @@ void k_decode(DecodeArgs a, HeadTab ht) {
 
   __shared__ float s_q[R];
   __shared__ uint32_t s_qw[PACKED ? QW : 1];
+  __shared__ uint32_t s_qd[DOT && !QD_IN_REGS ? 2 * QD : 1];
   __shared__ float s_m[NW], s_l[NW];
   __shared__ float s_u[NW][R];
   __shared__ float s_o[NW][kHeadDim];
@@ -616,6 +643,45 @@ void k_decode(DecodeArgs a, HeadTab ht) {
 #pragma unroll
     for (int i = 0; i < QW; ++i) qo.r[i] = uniform_i(int(qo.lds[i]));
   }
+  // DOT: q' ~= qs1 qh + qs2 ql with int8 qh = rne(q' / qs1), qs1 = max|q'| / 127,
+  // and int8 ql = rne((q' - qs1 qh) / qs2), qs2 = qs1 / 254: the error is at
+  // most about max|q'| / 64516 per entry (entries past r_k stay 0).  Every
+  // wavefront derives the same words; lane k packs words k of both levels.
+  float qs1 = 0.0f, qs2 = 0.0f;
+  uint32_t qdh[QD_IN_REGS ? QD : 1], qdl[QD_IN_REGS ? QD : 1];
+  if constexpr (DOT) {
+    float mq = 0.0f;
+#pragma unroll
+    for (int i = 0; i < R; i += 64)
+      if (i + lane < R) mq = fmaxf(mq, fabsf(s_q[i + lane]));
+    mq = lane63(wave_max63(mq));
+    qs1 = mq / 127.0f;
+    qs2 = qs1 / 254.0f;
+    uint32_t wh = 0u, wl = 0u;
+    if (lane < QD && qs1 != 0.0f) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float v = s_q[4 * lane + k];
+        const float h = fminf(fmaxf(rintf(v / qs1), -127.0f), 127.0f);
+        const float lo = fminf(fmaxf(rintf(fmaf(-qs1, h, v) / qs2), -127.0f), 127.0f);
+        wh |= (uint32_t(int(h)) & 0xffu) << (8 * k);
+        wl |= (uint32_t(int(lo)) & 0xffu) << (8 * k);
+      }
+    }
+    if constexpr (QD_IN_REGS) {
+#pragma unroll
+      for (int k = 0; k < QD; ++k) {
+        qdh[k] = uint32_t(__builtin_amdgcn_readlane(int(wh), k));
+        qdl[k] = uint32_t(__builtin_amdgcn_readlane(int(wl), k));
+      }
+    } else {
+      if (wid == 0 && lane < QD) {
+        s_qd[lane] = wh;
+        s_qd[QD + lane] = wl;
+      }
+      __syncthreads();
+    }
+  }
 
   // The fused append's cache write is the work-group's last act (store_new
   // below): this launch takes the new token's codes from LDS, and on gfx950
@@ -669,12 +735,24 @@ void k_decode(DecodeArgs a, HeadTab ht) {
       }
     }
     if constexpr (!Q_IN_REGS) qo.lds = (PACKED ? s_qw : reinterpret_cast<const uint32_t*>(s_q)) + opaque_zero();
+    const uint32_t* qdw = s_qd;
+    if constexpr (DOT && !QD_IN_REGS) qdw = s_qd + opaque_zero();
     float s = 0.0f;
+    int ah = 0, al = 0;   // DOT: integer sums against the two levels of q' 
 #pragma unroll
     for (int c = 0; c < NCL; ++c) {
       if (lm * c * VPC < rk) {   // uniform: tested on the lower half's chunk
         float part = 0.0f;
-        if constexpr (INT8) {
+        if constexpr (DOT) {
+          const int cg = lm * c + hf;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t qh = QD_IN_REGS ? qdh[(4 * cg + k) % (QD_IN_REGS ? QD : 1)] : qdw[4 * cg + k];
+            const uint32_t ql = QD_IN_REGS ? qdl[(4 * cg + k) % (QD_IN_REGS ? QD : 1)] : qdw[QD + 4 * cg + k];
+            ah = __builtin_amdgcn_sdot4(int(qh), int(cur.kw[4 * c + k]), ah, false);
+            al = __builtin_amdgcn_sdot4(int(ql), int(cur.kw[4 * c + k]), al, false);
+          }
+        } else if constexpr (INT8) {
           const int cg = lm * c + hf;
 #pragma unroll
           for (int k = 0; k < 16; ++k) part = fmaf(qo.f(16 * cg + k), i8(cur.kw[4 * c + (k >> 2)], k & 3), part);
@@ -698,6 +776,7 @@ void k_decode(DecodeArgs a, HeadTab ht) {
         }
       }
     }
+    if constexpr (DOT) s = fmaf(qs1, float(ah), qs2 * float(al));   // |sums| < 2^21: exact in fp32
     if constexpr (LPT == 2) {   // both lanes of a token: the full score
       const float both = swap_sum32(s, s);
       s = lm == 2 ? both : s;
