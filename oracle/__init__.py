@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.lro_quant_act_groups.restype = None
         L.lro_ffn.argtypes = [ctypes.c_int] * 6 + [P] * 9
         L.lro_ffn.restype = ctypes.c_int
+        L.lro_ffn_trace.argtypes = [ctypes.c_int] * 6 + [P] * 13
+        L.lro_ffn_trace.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -257,3 +259,24 @@ def ffn(x, wg, wu, ag, au, bg, bu, wd, quantise: bool = True) -> np.ndarray:
     if rc != 0:
         raise ValueError("lro_ffn rejected its arguments")
     return y
+
+
+def ffn_trace(x, wg, wu, ag, au, bg, bu, wd, quantise: bool = True):
+    """ffn() and its intermediates: (y [T, E] fp64, z [T, 2r] fp32 latents (gate
+    then up), g, u [T, F] fp64 pre-activations, h [T, F] fp32)."""
+    arrs = [np.ascontiguousarray(v, dtype=np.float32) for v in (x, wg, wu, ag, au, bg, bu, wd)]
+    x, wg, wu, ag, au, bg, bu, wd = arrs
+    T, E = x.shape
+    F = wd.shape[1]
+    S = bg.shape[0]
+    r = ag.shape[0]
+    y = np.zeros((T, E), np.float64)
+    z = np.zeros((T, 2 * r), np.float32)
+    g = np.zeros((T, F), np.float64)
+    u = np.zeros((T, F), np.float64)
+    h = np.zeros((T, F), np.float32)
+    rc = lib().lro_ffn_trace(0 if quantise else 1, T, E, F, S, r, *[_ptr(v) for v in arrs], _ptr(y), _ptr(z),
+                             _ptr(g), _ptr(u), _ptr(h))
+    if rc != 0:
+        raise ValueError("lro_ffn_trace rejected its arguments")
+    return y, z, g, u, h

@@ -32,6 +32,7 @@
 //
 // Build: g++ -O2 -fno-fast-math -ffp-contract=off -shared -fPIC (SSE math).
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -334,13 +335,15 @@ void qmatmul(const QMat& W, const float* act, int T, int qmode, double* out) {
 
 }  // namespace
 
-// Hybrid FFN on T tokens: x [T][E] (the activations' fp32 values), hidden F,
-// S low-rank channels of rank r.  Weights (row-major fp32, rows = outputs):
-// wg, wu [F - S][E] (dense gate / up rows of channels S..F-1), ag, au [r][E],
-// bg, bu [S][r], wd [E][F].  y [T][E] in fp64.  Returns 0, or -1 on bad sizes.
-int lro_ffn(int qmode, int T, int E, int F, int S, int r, const float* x, const float* wg,
-            const float* wu, const float* ag, const float* au, const float* bg, const float* bu,
-            const float* wd, double* y) {
+namespace {
+
+// The hybrid FFN of lro_ffn; when the trace pointers are given it also
+// stores what it computed on the way: the latents z (fp32 as quantised, gate
+// then up, [T][2r]), the gate and up pre-activations g, u (fp64, [T][F]) and
+// h (fp32 as quantised, [T][F]).
+int ffn_eval(int qmode, int T, int E, int F, int S, int r, const float* x, const float* wg,
+             const float* wu, const float* ag, const float* au, const float* bg, const float* bu,
+             const float* wd, double* y, float* z_out, double* g_out, double* u_out, float* h_out) {
   if (T < 0 || E < 1 || F < 1 || S < 0 || S > F || (S > 0 && r < 1) || qmode < 0 || qmode > 1) return -1;
   const int D = F - S;
   std::vector<double> g(static_cast<size_t>(T) * F), u(static_cast<size_t>(T) * F);
@@ -366,6 +369,10 @@ int lro_ffn(int qmode, int T, int E, int F, int S, int r, const float* x, const 
     for (int i = 0; i < 2; ++i) {
       qmatmul(make_qmat(A[i], r, E, qmode), x, T, qmode, z.data());
       for (size_t k = 0; k < z.size(); ++k) z32[k] = static_cast<float>(z[k]);
+      if (z_out)
+        for (int t = 0; t < T; ++t)
+          for (int k = 0; k < r; ++k)
+            z_out[(static_cast<size_t>(t) * 2 + i) * r + k] = z32[static_cast<size_t>(t) * r + k];
       qmatmul(make_qmat(B[i], S, r, qmode), z32.data(), T, qmode, tmp.data());
       for (int t = 0; t < T; ++t)
         for (int c = 0; c < S; ++c) (*dst[i])[static_cast<size_t>(t) * F + c] = tmp[static_cast<size_t>(t) * S + c];
@@ -374,8 +381,33 @@ int lro_ffn(int qmode, int T, int E, int F, int S, int r, const float* x, const 
   // SwiGLU: h = silu(g) * u, silu(v) = v / (1 + exp(-v)); rounded to fp32
   std::vector<float> h(static_cast<size_t>(T) * F);
   for (size_t k = 0; k < h.size(); ++k) h[k] = static_cast<float>(g[k] / (1.0 + std::exp(-g[k])) * u[k]);
+  if (g_out) std::copy(g.begin(), g.end(), g_out);
+  if (u_out) std::copy(u.begin(), u.end(), u_out);
+  if (h_out) std::copy(h.begin(), h.end(), h_out);
   qmatmul(make_qmat(wd, E, F, qmode), h.data(), T, qmode, y);
   return 0;
+}
+
+}  // namespace
+
+// Hybrid FFN on T tokens: x [T][E] (the activations' fp32 values), hidden F,
+// S low-rank channels of rank r.  Weights (row-major fp32, rows = outputs):
+// wg, wu [F - S][E] (dense gate / up rows of channels S..F-1), ag, au [r][E],
+// bg, bu [S][r], wd [E][F].  y [T][E] in fp64.  Returns 0, or -1 on bad sizes.
+int lro_ffn(int qmode, int T, int E, int F, int S, int r, const float* x, const float* wg,
+            const float* wu, const float* ag, const float* au, const float* bg, const float* bu,
+            const float* wd, double* y) {
+  return ffn_eval(qmode, T, E, F, S, r, x, wg, wu, ag, au, bg, bu, wd, y, nullptr, nullptr, nullptr,
+                  nullptr);
+}
+
+// lro_ffn that also returns its intermediates: z [T][2r] (fp32 latents, gate
+// then up), g, u [T][F] (fp64 pre-activations), h [T][F] (fp32).
+int lro_ffn_trace(int qmode, int T, int E, int F, int S, int r, const float* x, const float* wg,
+                  const float* wu, const float* ag, const float* au, const float* bg,
+                  const float* bu, const float* wd, double* y, float* z, double* g, double* u,
+                  float* h) {
+  return ffn_eval(qmode, T, E, F, S, r, x, wg, wu, ag, au, bg, bu, wd, y, z, g, u, h);
 }
 
 // Quantise and dequantise one row: out_i = scale * q_i in fp64 (exact).

@@ -615,3 +615,55 @@ def test_ffn_identity_low_rank_branch_reproduces_the_dense_branch():
     dense = oracle.ffn(x, W_g, W_u, z0, z0, np.zeros((0, 0), np.float32), np.zeros((0, 0), np.float32), wd)
     lowrank = oracle.ffn(x, np.zeros((0, E), np.float32), np.zeros((0, E), np.float32), I, I, W_g, W_u, wd)
     assert np.max(np.abs(lowrank - dense)) <= 1e-5 * np.max(np.abs(dense))
+
+
+def test_ffn_trace_intermediates_unquantised_equal_brute_force():
+    """lro_ffn_trace without quantisation: z = fp32(A x), g, u = the
+    pre-activations of the hybrid layout (low-rank channels first, through
+    B z), h = fp32(silu(g) u), all against a numpy brute force; its y is
+    lro_ffn's bit for bit."""
+    rng = np.random.default_rng(21)
+    x, wg, wu, ag, au, bg, bu, wd = _ffn_case(rng, T=3, E=64, F=48, S=16, r=8)
+    y, z, g, u, h = oracle.ffn_trace(x, wg, wu, ag, au, bg, bu, wd, quantise=False)
+    x64 = x.astype(np.float64)
+    zg = (x64 @ ag.T.astype(np.float64)).astype(np.float32)
+    zu = (x64 @ au.T.astype(np.float64)).astype(np.float32)
+    assert np.max(np.abs(z - np.concatenate([zg, zu], axis=1))) <= 2.0 ** -23 * np.max(np.abs(z))
+    G = np.concatenate([zg.astype(np.float64) @ bg.T.astype(np.float64), x64 @ wg.T.astype(np.float64)], axis=1)
+    U = np.concatenate([zu.astype(np.float64) @ bu.T.astype(np.float64), x64 @ wu.T.astype(np.float64)], axis=1)
+    assert np.max(np.abs(g - G)) <= 1e-12 * np.max(np.abs(G))
+    assert np.max(np.abs(u - U)) <= 1e-12 * np.max(np.abs(U))
+    assert np.max(np.abs(h - (_silu(G) * U).astype(np.float32))) <= 2.0 ** -22 * np.max(np.abs(h))
+    for q in (False, True):
+        assert np.array_equal(oracle.ffn_trace(x, wg, wu, ag, au, bg, bu, wd, quantise=q)[0],
+                              oracle.ffn(x, wg, wu, ag, au, bg, bu, wd, quantise=q))
+
+
+def test_ffn_w8a8_low_rank_branch_with_two_latent_groups_equals_dense_branch():
+    """All channels low-rank at rank r = E = 128 with A = 127 I and B on the
+    int8 grid, against all channels dense with W = 127 B: the latent z = 127 x
+    has two groups of 64 whose scales differ (x's groups are scaled by 1 and
+    1/4), every scale is exact, so the quantised low-rank path must give the
+    dense path's y bit for bit -- a wrong latent group index or scale breaks
+    the equality."""
+    rng = np.random.default_rng(22)
+    T, E, F = 4, 128, 64
+
+    def grid(rows, cols, group, scales):
+        m = rng.integers(-126, 127, (rows, cols)).astype(np.float32)
+        for lo in range(0, cols, group):
+            m[:, lo] = 127.0
+        return m * np.repeat(np.asarray(scales, np.float32), group)[None, :]
+    x = grid(T, E, 64, [1.0, 0.25])
+    bg = grid(F, E, E, [2.0 ** -3])
+    bu = grid(F, E, E, [2.0 ** -2])
+    wd = (rng.standard_normal((E, F)) / 8).astype(np.float32)
+    A = (127.0 * np.eye(E)).astype(np.float32)
+    none_e = np.zeros((0, E), np.float32)
+    lowrank, z, _, _, _ = oracle.ffn_trace(x, none_e, none_e, A, A, bg, bu, wd)
+    dense = oracle.ffn(x, 127 * bg, 127 * bu, none_e, none_e, np.zeros((0, 0), np.float32),
+                       np.zeros((0, 0), np.float32), wd)
+    assert np.array_equal(z[:, :E], 127 * x) and np.array_equal(z[:, E:], 127 * x)
+    _, zs = oracle.quant_act_groups(z[:, :E])
+    assert np.all(zs[:, 0] == 4 * zs[:, 1])          # the two latent groups have different scales
+    assert np.array_equal(lowrank, dense)
