@@ -103,6 +103,8 @@ def parse():
                     help="copies of the caches the timed steps cycle through (default: enough that "
                          "each launch reads its cache from HBM; 1 = one copy, partly cache-warm for "
                          "caches smaller than the 256 MiB last-level cache)")
+    ap.add_argument("--wg-waves", type=int, default=0, choices=(0, 4, 8, 16),
+                    help="wavefronts per decode work-group (0: the library's choice)")
     ap.add_argument("--no-warm-leg", action="store_true",
                     help="skip the warm measurement (one cache copy, launches back to back)")
     ap.add_argument("--profile-steps", type=int, default=0,
@@ -381,7 +383,7 @@ def main():
     nsteps_inputs = max(steps, warm, 1)
     print(f"[bench] setting up {w.name}", file=sys.stderr, flush=True)
     run = harness.WorkloadRun(w, io_dtype=LR_DT_BF16, device=dev, keep=keep,
-                              steps=nsteps_inputs).setup()
+                              steps=nsteps_inputs, wg_waves=args.wg_waves).setup()
     sess = run.sess
     L = w.n_layers
     ctx = run.context
@@ -600,6 +602,7 @@ def main():
             "parallelism": "single GPU",
             "launch": "hip graph of all timed steps" if use_graph else "eager",
             "cache_copies": R,
+            **({"wg_waves": args.wg_waves} if args.wg_waves else {}),
             "mall": ("cold: a cache byte is read again only after %.0f MB of cache reads "
                      "(last-level cache 268 MB)" % (reuse_bytes / 1e6)) if reuse_bytes >= 2 * MALL_BYTES
                     else ("partly warm: a cache byte is read again after %.0f MB of cache reads"

@@ -36,14 +36,15 @@ void set_last_hip_error(int err) { g_last_hip = err; }
 namespace lr {
 
 Split choose_split(const lr_attn_plan& p, int32_t layer, int32_t max_len) {
-  // Wavefronts per (b, h) work-group: 8 where the registers leave room for
-  // two such work-groups per compute unit (rank 32 at 5 waves per SIMD, int4
-  // rank 64 and int8 ranks 65-96 (two lanes per token) at 4), else 4 (int8
-  // rank 64 and ranks 97-128 at 3, int4 ranks above 64 at 2).  Several
-  // work-groups per compute unit run out of phase, so one group's prologue and
-  // merge overlap another's streaming.  With few (b, h) units the count
-  // doubles, up to 16 where 128 VGPRs suffice, until 4096 wavefronts (16 per
-  // CU) are in flight; beyond that the context of each (b, h) is split
+  // Wavefronts per (b, h) work-group: 4, doubled while fewer than 4096
+  // wavefronts (16 per CU) would be in flight -- up to 16 where 128 VGPRs
+  // suffice, else 8.  Small work-groups let several run per compute unit out
+  // of phase (one group's prologue and merge overlap another's streaming) and
+  // let many (b, h) units fit in fewer rounds of resident work-groups:
+  // MALL-cold on MI355X, 32-layer mixed-rank workload (1024 units) 48.2 /
+  // 53.2 / 72.0 us per layer with 4 / 8 / 16 wavefronts, int4 rank-64 batch-64
+  // workload (2048 units) 208 / 212 / 265 us.  Beyond 4096 wavefronts with
+  // the largest work-group the context of each (b, h) is split
   // Flash-Decoding style and a second kernel merges the partials (every
   // split keeps at least two tiles per wavefront).
   Split s;
@@ -51,8 +52,7 @@ Split choose_split(const lr_attn_plan& p, int32_t layer, int32_t max_len) {
   const int64_t tiles = ceil_div(max_len, kTile);
   const int bucket = layer_bucket(p.layers[layer]);
   const int nw_max = max_wg_waves(p.desc.qfmt, bucket);
-  const bool wide = nw_max == 16;
-  int nw = wide ? 8 : 4;
+  int nw = 4;
   if (p.desc.wg_waves > 0) {
     nw = std::min(p.desc.wg_waves, nw_max);
   } else {
