@@ -25,7 +25,7 @@ Unit = Tuple[int, int, int]  # (layer, b, h)
 class WorkloadRun:
     def __init__(self, w: lrgen.Workload, io_dtype: int = LR_DT_BF16, device="cuda",
                  keep: Iterable[Unit] = (), max_splits: int = 0, steps: Optional[int] = None,
-                 context: Optional[int] = None, chunk_tokens: int = 1024):
+                 context: Optional[int] = None, chunk_tokens: int = 1024, wg_waves: int = 0):
         self.w = w
         self.io_dtype = io_dtype
         self.device = torch.device(device)
@@ -35,7 +35,8 @@ class WorkloadRun:
         self.chunk = chunk_tokens
         self.dtype = torch.bfloat16 if io_dtype == LR_DT_BF16 else torch.float32
         self.sess = DecodeSession(w.n_layers, w.batch, w.n_heads, self.capacity, w.qfmt, io_dtype,
-                                  w.ranks_k, w.ranks_v, device=self.device, max_splits=max_splits)
+                                  w.ranks_k, w.ranks_v, device=self.device, max_splits=max_splits,
+                                  wg_waves=wg_waves)
         self.keep = sorted(set(keep))
         self.kept: Dict[Unit, List[List[np.ndarray]]] = {u: [[], []] for u in self.keep}
         self.off_k = [lrgen.head_offsets(r) for r in w.ranks_k]
@@ -47,12 +48,9 @@ class WorkloadRun:
 
     # -- inputs ---------------------------------------------------------------
     def _latents_all_rows(self, layer: int, t0: int, t1: int, ak, av):
-        cks, cvs = [], []
-        for b in range(self.w.batch):
-            ck, cv = lrgen.latents(self.w, layer, b, t0, t1, ak, av, device=self.device)
-            cks.append(ck)
-            cvs.append(cv)
-        return torch.stack(cks).contiguous(), torch.stack(cvs).contiguous()
+        # every batch row's activations in one draw, one fp32 product for K and one for V
+        x = lrgen.activations_rows(self.w, layer, 0, self.w.batch, t0, t1, device=self.device)
+        return torch.matmul(x, ak).contiguous(), torch.matmul(x, av).contiguous()
 
     def _keep(self, layer: int, ck: torch.Tensor, cv: torch.Tensor) -> None:
         units = [u for u in self.keep if u[0] == layer]

@@ -101,6 +101,32 @@ def normal(key: int, start: int, count: int, std: float = 1.0, device="cpu") -> 
     return out
 
 
+def normal_keyed(keys: torch.Tensor, idx: torch.Tensor, std) -> torch.Tensor:
+    """Element-wise streams: element ``e`` is element ``idx[e]`` of the
+    N(0, std²) stream with key ``keys[e]`` -- exactly the value ``normal()``
+    gives for that stream and index -- as fp32.  ``keys`` (int64 bit
+    patterns), ``idx`` and ``std`` (a float or a float64 tensor) broadcast to
+    one shape; one pass of element-wise kernels draws the whole tensor."""
+    keys, idx = torch.broadcast_tensors(keys, idx)
+    if isinstance(std, torch.Tensor):
+        std = std.to(torch.float64).expand(keys.shape).reshape(-1)
+    shape = keys.shape
+    k = keys.reshape(-1)
+    i = idx.reshape(-1)
+    out = torch.empty(k.numel(), dtype=torch.float32, device=k.device)
+    step = _CHUNK
+    for lo in range(0, k.numel(), step):
+        hi = min(k.numel(), lo + step)
+        kk, ii = k[lo:hi], i[lo:hi]
+        z0 = mix64((2 * ii + 1) * _s64(GAMMA) + kk)     # draw 2i of the stream
+        z1 = mix64((2 * ii + 2) * _s64(GAMMA) + kk)     # draw 2i + 1
+        u1 = 1.0 - uniform53(z0)
+        u2 = uniform53(z1)
+        g = torch.sqrt(-2.0 * torch.log(u1)) * torch.cos((2.0 * math.pi) * u2)
+        out[lo:hi] = (g * (std[lo:hi] if isinstance(std, torch.Tensor) else std)).to(torch.float32)
+    return out.view(shape)
+
+
 def uniform_index(key: int, start: int, count: int, n: int) -> List[int]:
     """``count`` integers uniform on ``{0, .., n-1}``: floor(U53 · n)."""
     u = uniform53(raw_draws(key, start, count))
@@ -232,28 +258,58 @@ def activations(w: Workload, layer: int, b: int, t0: int, t1: int, device="cpu")
     return x
 
 
+def _head_blocks(w: Workload, layer: int, kv: int, tag: int, device):
+    """Per latent column c of a layer's K or V latents: its head's stream key,
+    the column's index within the head, and the head's rank (int64 [Σ_h r_h])."""
+    ranks = w.ranks_k[layer] if kv == 0 else w.ranks_v[layer]
+    keys, local, rank = [], [], []
+    for h, r in enumerate(ranks):
+        keys += [_s64(stream_key(w.seed, tag, layer, h))] * r
+        local += list(range(r))
+        rank += [r] * r
+    as_t = lambda v: torch.tensor(v, dtype=torch.int64, device=device)
+    return as_t(keys), as_t(local), as_t(rank)
+
+
+def activations_rows(w: Workload, layer: int, b0: int, b1: int, t0: int, t1: int,
+                     device="cpu") -> torch.Tensor:
+    """activations() of batch rows b0 .. b1-1 at once: fp32 [b1-b0, t1-t0, E],
+    the same values as the rows drawn one by one."""
+    E = w.embed
+    keys = torch.tensor([_s64(stream_key(w.seed, TAG_X, layer, b)) for b in range(b0, b1)],
+                        dtype=torch.int64, device=device)[:, None, None]
+    t = torch.arange(t0, t1, dtype=torch.int64, device=device)[None, :, None]
+    e = torch.arange(E, dtype=torch.int64, device=device)[None, None, :]
+    x = normal_keyed(keys, t * E + e, 1.0)
+    scale = torch.full((1, t1 - t0, 1), math.sqrt(w.text_var), dtype=torch.float32, device=device)
+    npre = max(0, min(t1, w.prefix) - t0)
+    if npre > 0:
+        scale[:, :npre] = math.sqrt(w.prefix_var)
+    x = x * scale
+    oc = outlier_channels(w, layer)
+    if oc:
+        x[:, :, oc] *= w.outlier_scale
+    return x
+
+
 def down_factors(w: Workload, layer: int, kv: int, device="cpu") -> torch.Tensor:
     """A for K (kv=0) or V (kv=1): fp32 [E, Σ_h r_h], head h in its own column block,
-    each A_h ~ N(0, 1/E) elementwise."""
-    ranks = w.ranks_k[layer] if kv == 0 else w.ranks_v[layer]
-    tag = TAG_AK if kv == 0 else TAG_AV
-    cols = []
-    for h, r in enumerate(ranks):
-        key = stream_key(w.seed, tag, layer, h)
-        cols.append(normal(key, 0, w.embed * r, 1.0 / math.sqrt(w.embed), device).view(w.embed, r))
-    return torch.cat(cols, dim=1)
+    each A_h ~ N(0, 1/E) elementwise (block h is stream (seed, A, layer, h) in
+    row-major order: element (e, j) is stream element e r_h + j)."""
+    keys, local, rank = _head_blocks(w, layer, kv, TAG_AK if kv == 0 else TAG_AV, device)
+    e = torch.arange(w.embed, dtype=torch.int64, device=device)[:, None]
+    return normal_keyed(keys[None, :], e * rank[None, :] + local[None, :], 1.0 / math.sqrt(w.embed))
 
 
 def up_factors(w: Workload, layer: int, kv: int, dtype=torch.bfloat16, device="cpu") -> torch.Tensor:
     """B for K or V: [Σ_h r_h, d] with head h's r_h×d block B_h ~ N(0, 1/r_h),
-    drawn in fp32 and rounded to ``dtype``."""
-    ranks = w.ranks_k[layer] if kv == 0 else w.ranks_v[layer]
-    tag = TAG_BK if kv == 0 else TAG_BV
-    rows = []
-    for h, r in enumerate(ranks):
-        key = stream_key(w.seed, tag, layer, h)
-        rows.append(normal(key, 0, r * w.head_dim, 1.0 / math.sqrt(r), device).view(r, w.head_dim))
-    return torch.cat(rows, dim=0).to(dtype)
+    drawn in fp32 and rounded to ``dtype`` (block h is stream (seed, B, layer,
+    h) in row-major order)."""
+    keys, local, rank = _head_blocks(w, layer, kv, TAG_BK if kv == 0 else TAG_BV, device)
+    d = torch.arange(w.head_dim, dtype=torch.int64, device=device)[None, :]
+    std = torch.tensor([1.0 / math.sqrt(int(r)) for r in rank.tolist()], dtype=torch.float64,
+                       device=device)[:, None]
+    return normal_keyed(keys[:, None], local[:, None] * w.head_dim + d, std).to(dtype)
 
 
 def svd_like_factors(w: Workload, layer: int, kv: int, alpha: float = 1.0,

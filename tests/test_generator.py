@@ -80,3 +80,31 @@ def test_factor_shapes_and_scales():
     r = w.ranks_v[5][h]
     blk = bv[off[h]:off[h] + r].double()
     assert abs(blk.var().item() * r - 1) < 0.25
+
+
+def test_vectorised_draws_equal_the_per_stream_definitions():
+    """normal_keyed draws element idx of stream key exactly as normal() does;
+    the factors and the batched activations built from it equal the same
+    tensors drawn one stream (head, batch row) at a time."""
+    import math
+    w = lrgen.workload(3)
+    l = 4
+    for kv, tag in ((0, lrgen.TAG_AK), (1, lrgen.TAG_AV)):
+        a = lrgen.down_factors(w, l, kv)
+        ranks = w.ranks_k[l] if kv == 0 else w.ranks_v[l]
+        off = 0
+        for h in (0, 7, 31):
+            off = sum(ranks[:h])
+            want = lrgen.normal(lrgen.stream_key(w.seed, tag, l, h), 0, w.embed * ranks[h],
+                                1.0 / math.sqrt(w.embed)).view(w.embed, ranks[h])
+            assert torch.equal(a[:, off:off + ranks[h]], want)
+    b = lrgen.up_factors(w, l, 1, dtype=torch.float32)
+    for h in (0, 13, 31):
+        off, r = sum(w.ranks_v[l][:h]), w.ranks_v[l][h]
+        want = lrgen.normal(lrgen.stream_key(w.seed, lrgen.TAG_BV, l, h), 0, r * w.head_dim,
+                            1.0 / math.sqrt(r)).view(r, w.head_dim)
+        assert torch.equal(b[off:off + r], want)
+    w2 = lrgen.workload(2)   # outlier channels and the image prefix boundary
+    x = lrgen.activations_rows(w2, 0, 3, 6, 570, 580)
+    for i, bb in enumerate(range(3, 6)):
+        assert torch.equal(x[i], lrgen.activations(w2, 0, bb, 570, 580))
