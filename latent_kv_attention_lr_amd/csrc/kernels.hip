@@ -474,14 +474,23 @@ __attribute__((amdgpu_waves_per_eu(decode_occupancy<QF, R, LPT>(), decode_occupa
 void k_decode(DecodeArgs a, HeadTab ht) {
   constexpr bool INT8 = QF == LR_Q_INT8_TOKEN;
   constexpr bool PACKED = !INT8 && sizeof(IOT) == 2;
-  // int8 codes with bf16 I/O: K scores as integer dot products against q'
-  // held as two int8 levels (v_dot4: 4 codes per instruction)
+  // bf16 I/O: K scores as integer dot products of the codes against q' held
+  // as NLV integer levels of the codes' width -- two int8 levels against int8
+  // codes (v_dot4: 4 codes per instruction), four int4 levels against int4
+  // codes (v_dot8: 8 codes per instruction).  fp32 I/O keeps fp32 q'.
 #ifndef LR_DECODE_DOT4
 #define LR_DECODE_DOT4 1
 #endif
-  constexpr bool DOT = LR_DECODE_DOT4 && INT8 && sizeof(IOT) == 2;
-  constexpr int QD = R / 4;                            // 32-bit words of one int8 level of q'
-  constexpr bool QD_IN_REGS = DOT && R <= 64 && LPT == 1;
+#ifndef LR_DECODE_DOT8
+#define LR_DECODE_DOT8 1
+#endif
+  constexpr bool DOT = (INT8 ? LR_DECODE_DOT4 : LR_DECODE_DOT8) && sizeof(IOT) == 2;
+  constexpr int CPW = INT8 ? 4 : 8;                    // codes per 32-bit word
+  constexpr int NLV = INT8 ? 2 : 4;                    // integer levels of q'
+  constexpr float QLIM = INT8 ? 127.0f : 7.0f;         // largest code of a level
+  constexpr float QSTEP = INT8 ? 254.0f : 14.0f;       // ratio of consecutive level scales
+  constexpr int QD = R / CPW;                          // 32-bit words of one level
+  constexpr bool QD_IN_REGS = DOT && NLV * QD <= 32 && LPT == 1;
   constexpr int VPC = INT8 ? 16 : 32;                  // values per 16-byte chunk
   constexpr int NC = R / VPC;                          // chunks per row in the bucket
   constexpr int NCL = NC / LPT;                        // chunks per lane
@@ -520,7 +529,7 @@ void k_decode(DecodeArgs a, HeadTab ht) {
 
   __shared__ float s_q[R];
   __shared__ uint32_t s_qw[PACKED ? QW : 1];
-  __shared__ uint32_t s_qd[DOT && !QD_IN_REGS ? 2 * QD : 1];
+  __shared__ uint32_t s_qd[DOT && !QD_IN_REGS ? NLV * QD : 1];
   __shared__ float s_m[NW], s_l[NW];
   __shared__ float s_u[NW][R];
   __shared__ float s_o[NW][kHeadDim];
@@ -625,7 +634,7 @@ void k_decode(DecodeArgs a, HeadTab ht) {
   }
   __syncthreads();
   QOperand<QW, Q_IN_REGS> qo;
-  if constexpr (PACKED) {
+  if constexpr (PACKED && !DOT) {
     // word 4j + k of the packed operand pairs values 8j + k and 8j + k + 4,
     // divided by 16 for odd k (those nibbles sit 4 bits higher)
     if (tid < QW) {
@@ -643,41 +652,47 @@ void k_decode(DecodeArgs a, HeadTab ht) {
 #pragma unroll
     for (int i = 0; i < QW; ++i) qo.r[i] = uniform_i(int(qo.lds[i]));
   }
-  // DOT: q' ~= qs1 qh + qs2 ql with int8 qh = rne(q' / qs1), qs1 = max|q'| / 127,
-  // and int8 ql = rne((q' - qs1 qh) / qs2), qs2 = qs1 / 254: the error is at
-  // most about max|q'| / 64516 per entry (entries past r_k stay 0).  Every
-  // wavefront derives the same words; lane k packs words k of both levels.
-  float qs1 = 0.0f, qs2 = 0.0f;
-  uint32_t qdh[QD_IN_REGS ? QD : 1], qdl[QD_IN_REGS ? QD : 1];
+  // DOT: q' ~= sum_L qsc[L] q_L with integer levels q_1 = rne(q' / qsc[0]),
+  // qsc[0] = max|q'| / QLIM, each next level rounding the remaining residual
+  // on a QSTEP times finer scale (codes clamped to +-QLIM).  The error is at
+  // most about max|q'| / 64516 per entry for two int8 levels and max|q'| /
+  // 38416 for four int4 levels (entries past r_k stay 0).  Every wavefront
+  // derives the same words; lane k packs word k of every level.
+  float qsc[NLV];
+  uint32_t qdw[QD_IN_REGS ? NLV * QD : 1];
   if constexpr (DOT) {
     float mq = 0.0f;
 #pragma unroll
     for (int i = 0; i < R; i += 64)
       if (i + lane < R) mq = fmaxf(mq, fabsf(s_q[i + lane]));
     mq = lane63(wave_max63(mq));
-    qs1 = mq / 127.0f;
-    qs2 = qs1 / 254.0f;
-    uint32_t wh = 0u, wl = 0u;
-    if (lane < QD && qs1 != 0.0f) {
+    qsc[0] = mq / QLIM;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float v = s_q[4 * lane + k];
-        const float h = fminf(fmaxf(rintf(v / qs1), -127.0f), 127.0f);
-        const float lo = fminf(fmaxf(rintf(fmaf(-qs1, h, v) / qs2), -127.0f), 127.0f);
-        wh |= (uint32_t(int(h)) & 0xffu) << (8 * k);
-        wl |= (uint32_t(int(lo)) & 0xffu) << (8 * k);
+    for (int L = 1; L < NLV; ++L) qsc[L] = qsc[L - 1] / QSTEP;
+    uint32_t wq[NLV];
+#pragma unroll
+    for (int L = 0; L < NLV; ++L) wq[L] = 0u;
+    if (lane < QD && qsc[NLV - 1] != 0.0f) {
+#pragma unroll
+      for (int k = 0; k < CPW; ++k) {
+        float v = s_q[CPW * lane + k];
+#pragma unroll
+        for (int L = 0; L < NLV; ++L) {
+          const float c = fminf(fmaxf(rintf(v / qsc[L]), -QLIM), QLIM);
+          v = fmaf(-qsc[L], c, v);
+          wq[L] |= (uint32_t(int(c)) & (INT8 ? 0xffu : 0xfu)) << ((INT8 ? 8 : 4) * k);
+        }
       }
     }
     if constexpr (QD_IN_REGS) {
 #pragma unroll
-      for (int k = 0; k < QD; ++k) {
-        qdh[k] = uint32_t(__builtin_amdgcn_readlane(int(wh), k));
-        qdl[k] = uint32_t(__builtin_amdgcn_readlane(int(wl), k));
-      }
+      for (int L = 0; L < NLV; ++L)
+#pragma unroll
+        for (int k = 0; k < QD; ++k) qdw[L * QD + k] = uint32_t(__builtin_amdgcn_readlane(int(wq[L]), k));
     } else {
       if (wid == 0 && lane < QD) {
-        s_qd[lane] = wh;
-        s_qd[QD + lane] = wl;
+#pragma unroll
+        for (int L = 0; L < NLV; ++L) s_qd[L * QD + lane] = wq[L];
       }
       __syncthreads();
     }
@@ -735,23 +750,43 @@ void k_decode(DecodeArgs a, HeadTab ht) {
       }
     }
     if constexpr (!Q_IN_REGS) qo.lds = (PACKED ? s_qw : reinterpret_cast<const uint32_t*>(s_q)) + opaque_zero();
-    const uint32_t* qdw = s_qd;
-    if constexpr (DOT && !QD_IN_REGS) qdw = s_qd + opaque_zero();
+    const uint32_t* qdl = s_qd;
+    if constexpr (DOT && !QD_IN_REGS) qdl = s_qd + opaque_zero();
+    // word k of level L of the integer q'
+    auto qword = [&](int L, int k) -> uint32_t {
+      if constexpr (QD_IN_REGS) return qdw[(L * QD + k) % (QD_IN_REGS ? NLV * QD : 1)];
+      else return qdl[L * QD + k];
+    };
     float s = 0.0f;
-    int ah = 0, al = 0;   // DOT: integer sums against the two levels of q' 
+    int acc8[NLV];   // int8 DOT: integer sums against each level, over the whole row
+#pragma unroll
+    for (int L = 0; L < NLV; ++L) acc8[L] = 0;
 #pragma unroll
     for (int c = 0; c < NCL; ++c) {
       if (lm * c * VPC < rk) {   // uniform: tested on the lower half's chunk
         float part = 0.0f;
-        if constexpr (DOT) {
+        if constexpr (DOT && INT8) {
           const int cg = lm * c + hf;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const uint32_t qh = QD_IN_REGS ? qdh[(4 * cg + k) % (QD_IN_REGS ? QD : 1)] : qdw[4 * cg + k];
-            const uint32_t ql = QD_IN_REGS ? qdl[(4 * cg + k) % (QD_IN_REGS ? QD : 1)] : qdw[QD + 4 * cg + k];
-            ah = __builtin_amdgcn_sdot4(int(qh), int(cur.kw[4 * c + k]), ah, false);
-            al = __builtin_amdgcn_sdot4(int(ql), int(cur.kw[4 * c + k]), al, false);
-          }
+          for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int L = 0; L < NLV; ++L)
+              acc8[L] = __builtin_amdgcn_sdot4(int(qword(L, 4 * cg + k)), int(cur.kw[4 * c + k]), acc8[L], false);
+        } else if constexpr (DOT) {   // int4: one group of 32 ranks per chunk, its own scale
+          // every word of the chunk: past r_k the q' words are 0 in every
+          // level, so the codes read there add exactly 0 (a per-word rank
+          // test costs a copy and a select per accumulator and word)
+          int a4[NLV];
+#pragma unroll
+          for (int L = 0; L < NLV; ++L) a4[L] = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int L = 0; L < NLV; ++L)
+              a4[L] = __builtin_amdgcn_sdot8(int(qword(L, 4 * c + j)), int(cur.kw[4 * c + j]), a4[L], false);
+#pragma unroll
+          for (int L = 0; L < NLV; ++L) part = fmaf(qsc[L], float(a4[L]), part);   // |a4| < 2^11: exact
+          s = fmaf(cur.sk[c], part, s);
         } else if constexpr (INT8) {
           const int cg = lm * c + hf;
 #pragma unroll
@@ -776,7 +811,12 @@ void k_decode(DecodeArgs a, HeadTab ht) {
         }
       }
     }
-    if constexpr (DOT) s = fmaf(qs1, float(ah), qs2 * float(al));   // |sums| < 2^21: exact in fp32
+    if constexpr (DOT && INT8) {   // |sums| < 2^21: exact in fp32
+      float t = 0.0f;
+#pragma unroll
+      for (int L = NLV - 1; L >= 0; --L) t = fmaf(qsc[L], float(acc8[L]), t);
+      s = t;
+    }
     if constexpr (LPT == 2) {   // both lanes of a token: the full score
       const float both = swap_sum32(s, s);
       s = lm == 2 ? both : s;
