@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ffn_lds.h"
 #include "plan.h"
 
 namespace {
@@ -38,9 +39,14 @@ namespace {
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 8;
+// The weights are read once per step: non-temporal loads (streaming hint),
+// as for the decode's cache.
+#ifndef LR_FFN_NT_LOADS
+#define LR_FFN_NT_LOADS 1
+#endif
+
+using namespace lr::ffnlds;   // LDS layout and instances (ffn_lds.h)
 constexpr int kThreads = kWaves * 64;
-constexpr int kRowPad = 16;       // bytes of padding per token row of codes in LDS
 // LDS: the codes and group scales of 16 tokens (E in k_ffn_in, two blocks of
 // r in k_ffn_mid, one chunk of k_ffn_out), then 2 x 16 x 16 fp32 of reduced
 // outputs; the partial-tile reduction reuses the code area once the products
@@ -116,8 +122,11 @@ __device__ __forceinline__ void gemm_steps(const uint8_t* const (&wt)[RT], int c
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int r = 0; r < RT; ++r)
-        a[u][r] = *reinterpret_cast<const i32x4_t*>(wt[r] + size_t(min(c + u, c1 - 1)) * 1024 + 16 * lane);
+      for (int r = 0; r < RT; ++r) {
+        const i32x4_t* p = reinterpret_cast<const i32x4_t*>(wt[r] + size_t(min(c + u, c1 - 1)) * 1024 + 16 * lane);
+        if constexpr (LR_FFN_NT_LOADS) a[u][r] = __builtin_nontemporal_load(p);
+        else a[u][r] = *p;
+      }
   };
   if (c0 < c1) load(c0);
   stage();
@@ -162,19 +171,9 @@ __device__ void reduce_tiles(f32x4_t (&acc)[RT], uint8_t* smem, float* out) {
   __syncthreads();
 }
 
-// LDS of a launch: the code area -- `act` bytes of codes and scales, and at
-// least the 16 KB the partial-tile reduction reuses it for -- then the
-// 2 x 16 x 16 fp32 of reduced outputs.
-__host__ __device__ constexpr int block_bytes(int k) { return 16 * (k + kRowPad) + 16 * (k / 64) * 4; }
-__host__ __device__ constexpr int code_area(int act) { return act > kWaves * 2 * 64 * 16 ? act : kWaves * 2 * 64 * 16; }
-__host__ __device__ constexpr int lds_bytes(int act) { return code_area(act) + 2 * 16 * 16 * 4; }
-// Static LDS sizes of the GEMM instances: small (E <= 2048, r <= 1024, chunks
-// of 2048), medium (E <= 4096, r <= 2048, chunks of 4096), large (the limits).
-constexpr int kLdsS = lds_bytes(2 * block_bytes(1024));   // 37 376
-constexpr int kLdsM = lds_bytes(2 * block_bytes(2048));   // 72 192
-constexpr int kLdsL = lds_bytes(2 * block_bytes(4096));   // 141 824
-static_assert(lds_bytes(block_bytes(2048)) <= kLdsS && lds_bytes(block_bytes(4096)) <= kLdsM &&
-                  lds_bytes(block_bytes(8192)) <= kLdsL, "LDS instances");
+static_assert(in_extent(2048) <= kLdsS && in_extent(4096) <= kLdsM && in_extent(8192) <= kLdsL &&
+                  mid_extent(1024) <= kLdsS && mid_extent(2048) <= kLdsM && mid_extent(4096) <= kLdsL,
+              "LDS instances");
 
 struct InArgs {
   const int8_t* xq;           // [T][E] codes of x
@@ -190,12 +189,12 @@ struct InArgs {
 template <int LDS>
 __global__ __launch_bounds__(kThreads) void k_ffn_in(InArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
-  const int rs = a.E + kRowPad, steps = a.E / 64;
+  const int rs = row_stride(a.E), steps = a.E / 64;
   float* outv = reinterpret_cast<float*>(smem + code_area(block_bytes(a.E)));
   const int units = a.pairs + a.lat_groups;
   const int unit = blockIdx.x % units, t0 = 16 * (blockIdx.x / units);
   int8_t* act = reinterpret_cast<int8_t*>(smem);
-  float* scale = reinterpret_cast<float*>(smem + 16 * rs);
+  float* scale = reinterpret_cast<float*>(smem + scale_offset(a.E));
   const int tile0 = 2 * unit;   // pairs: (gate, up); latent groups: two consecutive 16-row tiles
   const uint8_t* wt[2] = {a.w + size_t(tile0) * steps * 1024, a.w + size_t(tile0 + 1) * steps * 1024};
   const int8_t* acts[2] = {act, act};
@@ -235,7 +234,7 @@ struct MidArgs {
 template <int LDS>
 __global__ __launch_bounds__(kThreads) void k_ffn_mid(MidArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
-  const int rs = a.r + kRowPad, steps = a.r / 64;
+  const int rs = row_stride(a.r), steps = a.r / 64;
   float* outv = reinterpret_cast<float*>(smem + code_area(2 * block_bytes(a.r)));
   const int unit = blockIdx.x % a.pairs, t0 = 16 * (blockIdx.x / a.pairs);   // launched only when pairs >= 1
   int8_t* act[2];
@@ -243,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void k_ffn_mid(MidArgs a) {
   for (int half = 0; half < 2; ++half) {
     uint8_t* base = smem + half * block_bytes(a.r);
     act[half] = reinterpret_cast<int8_t*>(base);
-    sc[half] = reinterpret_cast<float*>(base + 16 * rs);
+    sc[half] = reinterpret_cast<float*>(base + scale_offset(a.r));
   }
   const int tile0 = 2 * unit;
   const uint8_t* wt[2] = {a.w + size_t(tile0) * steps * 1024, a.w + size_t(tile0 + 1) * steps * 1024};
@@ -280,7 +279,7 @@ struct OutArgs {
 // scaled partial sum, and k_ffn_sum adds them in chunk order.
 template <int LDS, int CHUNK, int RT>
 __global__ __launch_bounds__(kThreads) void k_ffn_out(OutArgs a) {
-  static_assert(lds_bytes(block_bytes(CHUNK)) <= LDS && RT <= 2, "chunk exceeds LDS");
+  static_assert(out_extent(CHUNK, RT) <= LDS && RT <= 2, "chunk exceeds LDS");
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
   const int unit = blockIdx.x % a.units, split = (blockIdx.x / a.units) % a.splits;
   const int t0 = 16 * (blockIdx.x / (a.units * a.splits));
@@ -291,8 +290,8 @@ __global__ __launch_bounds__(kThreads) void k_ffn_out(OutArgs a) {
   const float* scs[RT];
   f32x4_t acc[RT];
   int8_t* act = reinterpret_cast<int8_t*>(smem);
-  const int k0 = split * CHUNK, kn = min(CHUNK, a.Fp - k0), gn = kn / 64, rs = kn + kRowPad;
-  float* scale = reinterpret_cast<float*>(smem + 16 * rs);
+  const int k0 = split * CHUNK, kn = min(CHUNK, a.Fp - k0), gn = kn / 64, rs = row_stride(kn);
+  float* scale = reinterpret_cast<float*>(smem + scale_offset(kn));
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
     wt[r] = a.w + size_t(RT * unit + r) * steps * 1024;
@@ -351,10 +350,11 @@ int launch_ffn(const FfnLayout& f, const void* weights, const void* x, int32_t n
             (f.F - f.S) / 16, 2 * f.r / 32};
   if (ia.pairs + ia.lat_groups > 0) {
     const dim3 g(unsigned(ia.pairs + ia.lat_groups) * tb), b(kThreads);
-    const int need = lds_bytes(block_bytes(f.E));   // the smallest instance that holds it
-    if (need <= kLdsS) hipLaunchKernelGGL(k_ffn_in<kLdsS>, g, b, 0, s, ia);
-    else if (need <= kLdsM) hipLaunchKernelGGL(k_ffn_in<kLdsM>, g, b, 0, s, ia);
-    else hipLaunchKernelGGL(k_ffn_in<kLdsL>, g, b, 0, s, ia);
+    const int lds = instance_for(in_extent(f.E));   // the smallest instance that holds it
+    if (lds == kLdsS) hipLaunchKernelGGL(k_ffn_in<kLdsS>, g, b, 0, s, ia);
+    else if (lds == kLdsM) hipLaunchKernelGGL(k_ffn_in<kLdsM>, g, b, 0, s, ia);
+    else if (lds == kLdsL) hipLaunchKernelGGL(k_ffn_in<kLdsL>, g, b, 0, s, ia);
+    else return int(hipErrorInvalidConfiguration);
     if ((err = int(hipGetLastError())) != 0) return err;
   }
   if (f.S > 0) {
@@ -363,10 +363,11 @@ int launch_ffn(const FfnLayout& f, const void* weights, const void* x, int32_t n
     if ((err = int(hipGetLastError())) != 0) return err;
     MidArgs ma{zq, zs, w + f.off_w2, reinterpret_cast<const float*>(w + f.off_s2), h, T, f.r, f.F, f.S / 16};
     const dim3 g(unsigned(ma.pairs) * tb), b(kThreads);
-    const int need = lds_bytes(2 * block_bytes(f.r));
-    if (need <= kLdsS) hipLaunchKernelGGL(k_ffn_mid<kLdsS>, g, b, 0, s, ma);
-    else if (need <= kLdsM) hipLaunchKernelGGL(k_ffn_mid<kLdsM>, g, b, 0, s, ma);
-    else hipLaunchKernelGGL(k_ffn_mid<kLdsL>, g, b, 0, s, ma);
+    const int lds = instance_for(mid_extent(f.r));
+    if (lds == kLdsS) hipLaunchKernelGGL(k_ffn_mid<kLdsS>, g, b, 0, s, ma);
+    else if (lds == kLdsM) hipLaunchKernelGGL(k_ffn_mid<kLdsM>, g, b, 0, s, ma);
+    else if (lds == kLdsL) hipLaunchKernelGGL(k_ffn_mid<kLdsL>, g, b, 0, s, ma);
+    else return int(hipErrorInvalidConfiguration);
     if ((err = int(hipGetLastError())) != 0) return err;
   }
   hipLaunchKernelGGL(k_ffn_quant<false>, quant_grid(f.Fp), dim3(256), 0, s, h, int64_t(f.F), f.F, T, f.Fp, hq, hs);
@@ -375,8 +376,8 @@ int launch_ffn(const FfnLayout& f, const void* weights, const void* x, int32_t n
   // work-group takes two row tiles, so each staged chunk of h serves 32 rows
   // of W_d (measured best on the LLaMA-7B FFN among chunks of 1, 2, 4 and 8 K
   // with one or two tiles).
-  const int chunk = f.Fp <= 2048 ? 2048 : 4096;
-  const int splits = (f.Fp + chunk - 1) / chunk, rt = splits > 1 ? 2 : 1;
+  const OutShape osh = out_shape(f.Fp);
+  const int chunk = osh.chunk, splits = osh.splits, rt = osh.rt;
   float* yp = reinterpret_cast<float*>(ws + f.ws_yp);
   OutArgs oa{hq, hs, w + f.off_w3, reinterpret_cast<const float*>(w + f.off_s3), splits > 1 ? yp : y, T, f.E, f.Fp,
              f.E / (16 * rt), splits};

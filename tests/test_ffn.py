@@ -2,12 +2,21 @@
 against the oracle's quantiser (CPU, bit for bit), argument errors (CPU), and
 the decode through the GPU kernels against the oracle's fp64 FFN (GPU).
 
-GPU tolerance: |y - y_ref| <= 2e-3 max|y_ref| per token row.  The kernels
-and the oracle take the same quantisation decisions for x and the weights
-(same fp32 values, same rule); the latents z and h are formed in fp32 on the
-GPU and fp64 in the oracle, so a code of z or h sitting on a rounding
-boundary may differ by one, which moves y by one step of that group's scale
-times a weight (at most ~1/127 of that group's contribution).
+GPU tolerance, per token t and output e (ffn_bound): the kernels and the
+oracle take the same quantisation decisions for x and the weights (same fp32
+values, same rule); the latents z and the hidden h are formed in fp32 on the
+GPU and in fp64 (then rounded to fp32) in the oracle.  So
+  * y agrees to fp32 summation accuracy, 2e-5 max|y_ref[t]|, wherever no
+    element of z or h sits within DELTA code units of a rounding boundary;
+  * an h element within DELTA of a boundary may round the other way: its code
+    moves by one, y[t][e] by at most one step s_h times |W_d[e][c]| (each such
+    element is added to the bound);
+  * a latent within DELTA of a boundary moves g or u of every low-rank
+    channel; such tokens (rare: DELTA = 2e-5 over a few thousand latents) get
+    1e-3 max|y_ref[t]| and are counted.
+The boundary distances come from the oracle's own intermediates
+(lro_ffn_trace).  A flip where the oracle's value is further than DELTA from
+a boundary, a wrong group scale or index, or a dropped term exceeds this.
 """
 import math
 
@@ -18,7 +27,37 @@ import lrgen
 import oracle
 import latent_kv_attention_lr_amd as lr
 
-TOL_FFN = 2e-3
+TOL_SUM = 2e-5     # fp32 summation, relative to max|y_ref| of the token
+TOL_Z = 1e-3       # a token with a latent on a rounding boundary
+DELTA = 2e-5       # code units: how close to a rounding boundary counts as on it
+
+
+def _near_boundary(a):
+    """Distance of each activation's code value a / s from the nearest rounding
+    boundary (k + 1/2), with the oracle's per-(token, 64-group) scales."""
+    a = np.ascontiguousarray(a, np.float32)
+    _, s = oracle.quant_act_groups(a)
+    sg = np.repeat(s, 64, axis=1)[:, :a.shape[1]].astype(np.float64)
+    v = np.abs(a.astype(np.float64)) / np.where(sg > 0, sg, 1.0)
+    return np.abs(v - np.floor(v) - 0.5), sg
+
+
+def ffn_bound(x, w):
+    """(y_ref [T, E], bound [T, E], tokens with a latent on a boundary)."""
+    wg, wu, ag, au, bg, bu, wd = w
+    y, z, _, _, h = oracle.ffn_trace(x, wg, wu, ag, au, bg, bu, wd)
+    mh, sh = _near_boundary(h)
+    absw = np.abs(wd.astype(np.float64)) * (1.0 + 1.0 / 254)   # dequantised |W_d| (RTN error <= s/2)
+    bound = TOL_SUM * np.max(np.abs(y), axis=1, keepdims=True).repeat(y.shape[1], axis=1)
+    flips = (mh < DELTA) * sh                                    # [T, F]: one code step where a flip can happen
+    bound += flips @ absw.T
+    z_tokens = []
+    if z.shape[1]:
+        mz, _ = _near_boundary(z)
+        z_tokens = [t for t in range(z.shape[0]) if np.any(mz[t] < DELTA)]
+        for t in z_tokens:
+            bound[t] += TOL_Z * np.max(np.abs(y[t]))
+    return y, bound, z_tokens
 
 
 def _desc(E, F, S, r):
@@ -147,6 +186,28 @@ def test_ffn_argument_errors_before_launch():
         lr.lr_ffn_prepare_weights(d, *w)
 
 
+@pytest.mark.parametrize("E,F,S,r,T", [(128, 96, 32, 64, 5), (512, 2064, 512, 128, 3)])
+def test_ffn_bound_rejects_plausible_kernel_mistakes(E, F, S, r, T):
+    """The GPU bound admits the oracle itself but not: one 64-group of h with
+    its scale off by 128/127, or one hidden channel dropped (CPU)."""
+    _, w, x = _case(E, F, S, r, T, seed=7)
+    xf = x.float().numpy()
+    y, bound, _ = ffn_bound(xf, w)
+    assert np.all(np.abs(y - y) <= bound)
+    _, _, _, _, h = oracle.ffn_trace(xf, *w)
+    wd = w[6].astype(np.float64)
+    t = T - 1
+    g = 0
+    part = wd[:, 64 * g:64 * g + 64] @ h[t, 64 * g:64 * g + 64].astype(np.float64)
+    bad = y.copy()
+    bad[t] += part / 127.0
+    assert np.any(np.abs(bad - y) > bound)
+    c = int(np.argmax(np.abs(h[t])))
+    bad = y.copy()
+    bad[t] -= wd[:, c] * float(h[t, c])
+    assert np.any(np.abs(bad - y) > bound)
+
+
 # ---------------------------------------------------------------------------
 # GPU
 # ---------------------------------------------------------------------------
@@ -159,8 +220,18 @@ def _run_gpu(E, F, S, r, T, seed, tokens=None):
     layer.set_weights(*w)
     y = layer(x.to("cuda:0")).cpu().numpy()
     rows = range(T) if tokens is None else tokens
-    ref = oracle.ffn(x.float().numpy()[list(rows)], *w)
-    return y[list(rows)], ref, layer, x
+    ref, bound, z_tokens = ffn_bound(x.float().numpy()[list(rows)], w)
+    return y[list(rows)], ref, bound, z_tokens, layer, x
+
+
+def _check(y, ref, bound, z_tokens, what):
+    err = np.abs(y.astype(np.float64) - ref)
+    worst = float(np.max(err / np.maximum(bound, 1e-300)))
+    rel = float(np.max(err / np.max(np.abs(ref), axis=1, keepdims=True)))
+    print(f"{what}: worst error / bound {worst:.3f}, worst relative error {rel:.2e}, "
+          f"tokens with a latent on a rounding boundary: {len(z_tokens)} of {len(y)}", flush=True)
+    assert np.all(err <= bound), (what, np.argwhere(err > bound)[:5])
+    return rel
 
 
 @pytest.mark.gpu
@@ -176,10 +247,8 @@ def test_ffn_decode_matches_oracle(E, F, S, r, T):
     (where LDS sized per launch once gave all-zero outputs); ranks 2048 and
     4096 take the medium and large LDS instances of the low-rank launch."""
     print(f"ffn E={E} F={F} S={S} r={r} T={T}", flush=True)
-    y, ref, _, _ = _run_gpu(E, F, S, r, T, seed=E + F + S + r + T)
-    for t in range(T):
-        err = float(np.max(np.abs(y[t] - ref[t])))
-        assert err <= TOL_FFN * float(np.max(np.abs(ref[t]))), (t, err, float(np.max(np.abs(ref[t]))))
+    y, ref, bound, z_tokens, _, _ = _run_gpu(E, F, S, r, T, seed=E + F + S + r + T)
+    _check(y, ref, bound, z_tokens, f"E={E} F={F} S={S} r={r} T={T}")
 
 
 @pytest.mark.gpu
@@ -190,13 +259,9 @@ def test_ffn_decode_full_size_and_deterministic():
     import torch
     f = lrgen.FFN_WORKLOADS[0]
     print(f"ffn full size {f.name}", flush=True)
-    y, ref, layer, x = _run_gpu(f.embed, f.hidden, f.n_lowrank, f.rank, f.tokens, seed=f.seed)
-    worst = 0.0
-    for t in range(f.tokens):
-        err = float(np.max(np.abs(y[t] - ref[t]))) / float(np.max(np.abs(ref[t])))
-        worst = max(worst, err)
-        assert err <= TOL_FFN, (t, err)
-    print(f"worst relative error {worst:.2e}", flush=True)
+    y, ref, bound, z_tokens, layer, x = _run_gpu(f.embed, f.hidden, f.n_lowrank, f.rank, f.tokens, seed=f.seed)
+    _check(y, ref, bound, z_tokens, f.name)
+    assert len(z_tokens) <= f.tokens // 4
     y2 = layer(x.to("cuda:0")).cpu().numpy()
     assert np.array_equal(y, y2)
 
@@ -210,7 +275,5 @@ def test_ffn_decode_in_several_passes():
     assert _pass_tokens(E, F, S, r) == 2032
     print(f"ffn passes E={E} F={F} S={S} r={r} T={T}", flush=True)
     rows = [0, 1, 777, 2030, 2031, 2032, 2033, 2099]
-    y, ref, _, _ = _run_gpu(E, F, S, r, T, seed=99, tokens=rows)
-    for i, t in enumerate(rows):
-        err = float(np.max(np.abs(y[i] - ref[i])))
-        assert err <= TOL_FFN * float(np.max(np.abs(ref[i]))), (t, err)
+    y, ref, bound, z_tokens, _, _ = _run_gpu(E, F, S, r, T, seed=99, tokens=rows)
+    _check(y, ref, bound, z_tokens, "two passes")
