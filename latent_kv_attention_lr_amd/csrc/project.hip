@@ -35,6 +35,21 @@ constexpr int kLdsBytes = 128 * 1024 + 64 * 16;   // largest activation phase + 
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// The packed factors are read once per launch (each work-group its own row
+// tiles and part of E): non-temporal loads, as for the decode's cache.
+#ifndef LR_PROJECT_NT_LOADS
+#define LR_PROJECT_NT_LOADS 1
+#endif
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_stream(const uint16_t* p) {
+  if constexpr (LR_PROJECT_NT_LOADS) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return uint4{v.x, v.y, v.z, v.w};
+  } else {
+    return ld16(p);
+  }
+}
+
 struct ProjArgs {
   const uint16_t* x;   // bf16 [T][E]
   const uint16_t* wp;  // packed factors: [k_tiles + v_tiles][E / 32][64 lanes][8]
@@ -102,7 +117,7 @@ __global__ __launch_bounds__(NW * 64) void k_project(ProjArgs a) {
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int u = 0; u < SPW; ++u) dst[r][u] = ld16(wl[r] + size_t(min(p * PS + wid * SPW + u, steps - 1)) * 512);
+        for (int u = 0; u < SPW; ++u) dst[r][u] = ld16_stream(wl[r] + size_t(min(p * PS + wid * SPW + u, steps - 1)) * 512);
     };
     // activations of phase p, piece q = row * (EP / 8) + col: token t0 + row,
     // elements p EP + 8 col .. + 7 (clamped into the row and the token range)
