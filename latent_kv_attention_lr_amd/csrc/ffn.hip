@@ -13,11 +13,11 @@
 // z = A x, h) are int8 with one fp32 scale per token and per group of 64
 // elements along the reduction dimension -- the k extent of one
 // v_mfma_i32_16x16x64_i8, so every product is an exact integer sum per group,
-// converted and scaled once per group in fp32.  Six launches (seven when h
+// converted and scaled once per group in fp32.  Five launches (six when h
 // spans several chunks):
 //   k_ffn_quant x -> codes and group scales
-//   k_ffn_in    dense pairs: h = silu(g) u; and the latents z = [A_g; A_u] x
-//   k_ffn_quant z -> codes and group scales
+//   k_ffn_in    the latents z = [A_g; A_u] x, quantised by the work-group
+//               that owns each 64-latent group; dense pairs: h = silu(g) u
 //   k_ffn_mid   low-rank pairs: h = silu(g) u
 //   k_ffn_quant h -> codes and group scales
 //   k_ffn_out   y = W_d h, the hidden dimension split in chunks of 4096 across
@@ -118,7 +118,7 @@ __device__ __forceinline__ void gemm_steps(const uint8_t* const (&wt)[RT], int c
                                            const int8_t* const (&act)[RT], const float* const (&scale)[RT],
                                            int rs, int groups, f32x4_t (&acc)[RT], Stage stage) {
   const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
-  constexpr int U = 8;
+  constexpr int U = RT > 2 ? 4 : 8;   // steps of weights in flight per batch (registers: U x RT x 4)
   i32x4_t a[U][RT];
   auto load = [&](int c) {
 #pragma unroll
@@ -183,11 +183,16 @@ struct InArgs {
   const uint8_t* w;           // packed tiles: dense pairs (gate, up), then latent rows of [A_g; A_u]
   const float* ws;            // row scales in tile order
   float* h;                   // [T][F]
-  float* z;                   // [T][2 r]
-  int32_t T, E, F, S, pairs, lat_groups;   // pairs = (F - S) / 16; lat_groups = 2 r / 32
+  int8_t* zq;                 // [T][2 r] codes of the latents z = [A_g; A_u] x
+  float* zs;                  // [T][2 r / 64] their group scales
+  int32_t T, E, F, S, pairs, lat_groups;   // pairs = (F - S) / 16; lat_groups = 2 r / 64
 };
 
-// Launch 2: work-group = (dense pair p or latent group j, block of 16 tokens).
+// Launch 2: work-group = (latent group j or dense pair p, block of 16 tokens).
+// The latent groups come first in the grid (their work-groups carry twice a
+// pair's weights) and each owns one whole activation group of z -- 64
+// latents, four 16-row tiles -- so it quantises z itself (the int8 rule of
+// k_ffn_quant on the same fp32 values) and no separate launch is needed.
 template <int LDS>
 __global__ __launch_bounds__(kThreads) void k_ffn_in(InArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
@@ -197,28 +202,57 @@ __global__ __launch_bounds__(kThreads) void k_ffn_in(InArgs a) {
   const int unit = blockIdx.x % units, t0 = 16 * (blockIdx.x / units);
   int8_t* act = reinterpret_cast<int8_t*>(smem);
   float* scale = reinterpret_cast<float*>(smem + scale_offset(a.E));
-  const int tile0 = 2 * unit;   // pairs: (gate, up); latent groups: two consecutive 16-row tiles
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  auto stage = [&]() {
+    stage_codes(a.xq, a.xs, a.E, 0, a.E, a.T, t0, act, scale, rs);
+    __syncthreads();
+  };
+  if (unit < a.lat_groups) {   // uniform: latent group j = unit, tiles 2 pairs + 4 j ..
+    const int tile0 = 2 * a.pairs + 4 * unit;
+    const uint8_t* wt[4];
+    const int8_t* acts[4];
+    const float* scs[4];
+    f32x4_t acc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      wt[r] = a.w + size_t(tile0 + r) * steps * 1024;
+      acts[r] = act;
+      scs[r] = scale;
+      acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    gemm_steps<4>(wt, steps * wid / kWaves, steps * (wid + 1) / kWaves, 0, acts, scs, rs, steps, acc, stage);
+    reduce_tiles<4>(acc, smem, outv);
+    // one wavefront per token (two tokens each): lane = latent 16 r + nn of the group
+    const int r = lane >> 4, nn = lane & 15;
+    for (int tt = wid; tt < 16; tt += kWaves) {
+      const int t = t0 + tt;
+      const float v = outv[(r * 16 + tt) * 16 + nn] * a.ws[16 * (tile0 + r) + nn];
+      float m = fabsf(v);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      const float s = m / 127.0f;
+      if (t < a.T) {
+        const int zrow = 2 * (a.lat_groups * 32);   // codes per token: 2 r
+        a.zq[size_t(t) * zrow + 64 * unit + lane] = int8_t(code(v, s));
+        if (lane == 0) a.zs[size_t(t) * a.lat_groups + unit] = s;
+      }
+    }
+    return;
+  }
+  const int p = unit - a.lat_groups;   // dense pair p: tiles (gate, up) = 2 p, 2 p + 1
+  const int tile0 = 2 * p;
   const uint8_t* wt[2] = {a.w + size_t(tile0) * steps * 1024, a.w + size_t(tile0 + 1) * steps * 1024};
   const int8_t* acts[2] = {act, act};
   const float* scs[2] = {scale, scale};
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-  gemm_steps<2>(wt, steps * wid / kWaves, steps * (wid + 1) / kWaves, 0, acts, scs, rs, steps, acc, [&]() {
-    stage_codes(a.xq, a.xs, a.E, 0, a.E, a.T, t0, act, scale, rs);
-    __syncthreads();
-  });
+  gemm_steps<2>(wt, steps * wid / kWaves, steps * (wid + 1) / kWaves, 0, acts, scs, rs, steps, acc, stage);
   reduce_tiles<2>(acc, smem, outv);
   for (int i = threadIdx.x; i < 256; i += kThreads) {
     const int tt = i >> 4, nn = i & 15, t = t0 + tt;
     if (t >= a.T) continue;
     const float v0 = outv[i] * a.ws[16 * tile0 + nn], v1 = outv[256 + i] * a.ws[16 * (tile0 + 1) + nn];
-    if (unit < a.pairs) {
-      a.h[size_t(t) * a.F + a.S + 16 * unit + nn] = silu_mul(v0, v1);   // channel S + 16 p + nn
-    } else {
-      float* zr = a.z + size_t(t) * (a.lat_groups * 32) + 32 * (unit - a.pairs);
-      zr[nn] = v0;
-      zr[16 + nn] = v1;
-    }
+    a.h[size_t(t) * a.F + a.S + 16 * p + nn] = silu_mul(v0, v1);   // channel S + 16 p + nn
   }
 }
 
@@ -335,7 +369,6 @@ int launch_ffn(const FfnLayout& f, const void* weights, const void* x, int32_t n
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   int8_t* xq = reinterpret_cast<int8_t*>(ws + f.ws_xq);
   float* xs = reinterpret_cast<float*>(ws + f.ws_xs);
-  float* z = reinterpret_cast<float*>(ws + f.ws_z);
   int8_t* zq = reinterpret_cast<int8_t*>(ws + f.ws_zq);
   float* zs = reinterpret_cast<float*>(ws + f.ws_zs);
   float* h = reinterpret_cast<float*>(ws + f.ws_h);
@@ -348,8 +381,8 @@ int launch_ffn(const FfnLayout& f, const void* weights, const void* x, int32_t n
 
   hipLaunchKernelGGL(k_ffn_quant<true>, quant_grid(f.E), dim3(256), 0, s, x, int64_t(f.E), f.E, T, f.E, xq, xs);
   if ((err = int(hipGetLastError())) != 0) return err;
-  InArgs ia{xq, xs, w + f.off_w1, reinterpret_cast<const float*>(w + f.off_s1), h, z, T, f.E, f.F, f.S,
-            (f.F - f.S) / 16, 2 * f.r / 32};
+  InArgs ia{xq, xs, w + f.off_w1, reinterpret_cast<const float*>(w + f.off_s1), h, zq, zs, T, f.E, f.F, f.S,
+            (f.F - f.S) / 16, 2 * f.r / 64};
   if (ia.pairs + ia.lat_groups > 0) {
     const dim3 g(unsigned(ia.pairs + ia.lat_groups) * tb), b(kThreads);
     const int lds = instance_for(in_extent(f.E));   // the smallest instance that holds it
@@ -360,9 +393,6 @@ int launch_ffn(const FfnLayout& f, const void* weights, const void* x, int32_t n
     if ((err = int(hipGetLastError())) != 0) return err;
   }
   if (f.S > 0) {
-    hipLaunchKernelGGL(k_ffn_quant<false>, quant_grid(2 * f.r), dim3(256), 0, s, z, int64_t(2 * f.r), 2 * f.r, T,
-                       2 * f.r, zq, zs);
-    if ((err = int(hipGetLastError())) != 0) return err;
     MidArgs ma{zq, zs, w + f.off_w2, reinterpret_cast<const float*>(w + f.off_s2), h, T, f.r, f.F, f.S / 16};
     const dim3 g(unsigned(ma.pairs) * tb), b(kThreads);
     const int lds = instance_for(mid_extent(f.r));

@@ -46,7 +46,6 @@ void ffn_workspace(lr::FfnLayout* f, size_t T) {
   auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
   f->ws_xq = take(T * E);
   f->ws_xs = take(T * (E / 64) * 4);
-  f->ws_z = take(T * r2 * 4);
   f->ws_zq = take(T * r2);
   f->ws_zs = take(T * (r2 / 64) * 4);
   f->ws_h = take(T * F * 4);

@@ -25,21 +25,23 @@ LR_FFN_HD constexpr int scale_offset(int k) { return 16 * row_stride(k); }
 LR_FFN_HD constexpr int block_bytes(int k) { return scale_offset(k) + 16 * (k / 64) * 4; }
 // The wavefronts' partial tiles, [kWaves][RT][64 lanes] x 16 bytes, reuse the
 // code area once the products are done; the reduced outputs (RT x 16 x 16
-// fp32) follow the code area.
+// fp32) follow the code area.  RT is at most 4 (the latent groups of
+// k_ffn_in; pairs and the down projection take 2).
+constexpr int kMaxRT = 4;
 LR_FFN_HD constexpr int red_bytes(int rt) { return kWaves * rt * 64 * 16; }
-LR_FFN_HD constexpr int code_area(int act) { return act > red_bytes(2) ? act : red_bytes(2); }
+LR_FFN_HD constexpr int code_area(int act) { return act > red_bytes(kMaxRT) ? act : red_bytes(kMaxRT); }
 LR_FFN_HD constexpr int out_bytes(int rt) { return rt * 16 * 16 * 4; }
-LR_FFN_HD constexpr int lds_bytes(int act) { return code_area(act) + out_bytes(2); }
+LR_FFN_HD constexpr int lds_bytes(int act) { return code_area(act) + out_bytes(kMaxRT); }
 
 // Static instances: small (E <= 2048, r <= 1024, chunks of 2048), medium
 // (E <= 4096, r <= 2048, chunks of 4096), large (E <= 8192, r <= 4096).
-constexpr int kLdsS = lds_bytes(2 * block_bytes(1024));   // 37 376
-constexpr int kLdsM = lds_bytes(2 * block_bytes(2048));   // 72 192
-constexpr int kLdsL = lds_bytes(2 * block_bytes(4096));   // 141 824
+constexpr int kLdsS = lds_bytes(2 * block_bytes(1024));   // 39 424
+constexpr int kLdsM = lds_bytes(2 * block_bytes(2048));   // 74 240
+constexpr int kLdsL = lds_bytes(2 * block_bytes(4096));   // 143 872
 static_assert(kLdsL <= kLdsLimit, "largest instance exceeds the LDS of a work-group");
 
 // Bytes from the start of LDS up to the last one each launch touches.
-LR_FFN_HD constexpr int in_extent(int E) { return code_area(block_bytes(E)) + out_bytes(2); }
+LR_FFN_HD constexpr int in_extent(int E) { return code_area(block_bytes(E)) + out_bytes(4); }
 LR_FFN_HD constexpr int mid_extent(int r) { return code_area(2 * block_bytes(r)) + out_bytes(2); }
 LR_FFN_HD constexpr int out_extent(int kc, int rt) { return code_area(block_bytes(kc)) + out_bytes(rt); }
 

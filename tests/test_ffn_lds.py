@@ -21,7 +21,7 @@ int main() {
   for (int E = 64; E <= 8192; E += 64) {            // k_ffn_in: one block of E columns
     const int lds = instance_for(in_extent(E));
     need(lds != 0 && in_extent(E) <= lds && lds <= kLdsLimit, "in", E);
-    need(block_bytes(E) <= code_area(block_bytes(E)) && red_bytes(2) <= code_area(block_bytes(E)), "in area", E);
+    need(block_bytes(E) <= code_area(block_bytes(E)) && red_bytes(4) <= code_area(block_bytes(E)), "in area", E);
   }
   for (int r = 64; r <= 4096; r += 64) {            // k_ffn_mid: two blocks of r columns
     const int lds = instance_for(mid_extent(r));
