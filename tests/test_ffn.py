@@ -267,6 +267,28 @@ def test_ffn_decode_full_size_and_deterministic():
 
 
 @pytest.mark.gpu
+def test_ffn_workspace_reuse_with_changing_inputs():
+    """One layer (one workspace) called on alternating inputs x1, x2, x1, x2:
+    the launches of a call pass the quantised activations, the latents and h
+    to each other through the workspace, so a read of a value left by the
+    previous call would show here.  Each output matches the oracle for its
+    own input, and repeated inputs give bitwise equal outputs."""
+    from latent_kv_attention_lr_amd.ffn import FfnLayer
+    E, F, S, r, T = 512, 8208, 4096, 256, 17
+    print(f"ffn reuse E={E} F={F} S={S} r={r} T={T}", flush=True)
+    f, w, x1 = _case(E, F, S, r, T, seed=5)
+    x2 = lrgen.ffn_activations(lrgen.FfnWorkload("t", E, F, S, r, T, 6), T)
+    layer = FfnLayer(E, F, S, r, device="cuda:0")
+    layer.set_weights(*w)
+    outs = [layer(x.to("cuda:0")).cpu().numpy() for x in (x1, x2, x1, x2)]
+    for x, y in ((x1, outs[0]), (x2, outs[1])):
+        ref, bound, z_tokens = ffn_bound(x.float().numpy(), w)
+        _check(y, ref, bound, z_tokens, "reuse")
+    assert not np.array_equal(outs[0], outs[1])
+    assert np.array_equal(outs[0], outs[2]) and np.array_equal(outs[1], outs[3])
+
+
+@pytest.mark.gpu
 def test_ffn_decode_in_several_passes():
     """2100 tokens of a shape whose pass is 2032 tokens: two passes through one
     workspace; tokens on both sides of the pass boundary and at both ends
