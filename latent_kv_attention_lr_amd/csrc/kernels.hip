@@ -461,11 +461,12 @@ struct QOperand {
 // registers (64 tokens, twice the bytes per step: light heads are bound by
 // the bytes each wavefront has in flight).  The choice is per work-group.
 //
-// Waves per SIMD the register allocation must allow: enough bytes in flight
-// per CU to cover HBM latency without spilling.
+// Waves per SIMD the register allocation must allow (decode_waves_per_simd:
+// enough bytes in flight per CU to cover HBM latency without spilling).
 template <int QF, int R, int LPT>
 constexpr int decode_occupancy() {
-  return LPT == 2 ? (R <= 96 ? 4 : 3) : R <= 32 ? 5 : R <= 64 ? (QF == LR_Q_INT8_TOKEN ? 3 : 4) : 2;
+  static_assert(LPT == (pair_lanes(QF, R) ? 2 : 1), "lanes per token follow the bucket");
+  return decode_waves_per_simd(QF, R);
 }
 
 template <int QF, typename IOT, int R, int NW, int LPT>
@@ -1260,6 +1261,12 @@ hipError_t launch_decode_r(int waves, dim3 grid, hipStream_t st, const DecodeArg
   if constexpr (max_wg_waves(QF, R) == 16) {
     if (waves == 16) {
       hipLaunchKernelGGL((k_decode<QF, IOT, R, 16, LPT>), grid, dim3(1024), 0, st, a, t);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (decode_waves_per_simd(QF, R) == 3) {
+    if (waves == 3) {   // four work-groups per compute unit (choose_split)
+      hipLaunchKernelGGL((k_decode<QF, IOT, R, 3, LPT>), grid, dim3(192), 0, st, a, t);
       return hipGetLastError();
     }
   }

@@ -47,22 +47,34 @@ Split choose_split(const lr_attn_plan& p, int32_t layer, int32_t max_len) {
   // the largest work-group the context of each (b, h) is split
   // Flash-Decoding style and a second kernel merges the partials (every
   // split keeps at least two tiles per wavefront).
+  //
+  // Buckets compiled for three wavefronts per SIMD hold only three
+  // four-wavefront work-groups per compute unit (768 on the GPU), so there
+  // the target is the 3072 wavefronts the GPU holds, and between 769 and
+  // 1024 (b, h) units the work-groups take three wavefronts: four per CU, all
+  // resident in one round.  (Measured on MI355X, 32-layer workload with a
+  // greedily allocated rank table, ranks 8..128: with four-wavefront groups
+  // the 256 lightest heads waited for the first round and then streamed
+  // almost alone for the last quarter of the launch.)
   Split s;
   const int64_t units = static_cast<int64_t>(p.desc.batch) * p.desc.n_heads;
   const int64_t tiles = ceil_div(max_len, kTile);
   const int bucket = layer_bucket(p.layers[layer]);
   const int nw_max = max_wg_waves(p.desc.qfmt, bucket);
+  const int wps = decode_waves_per_simd(p.desc.qfmt, bucket);
+  const int64_t target = wps == 3 ? int64_t(kComputeUnits) * 4 * wps : 4096;   // wavefronts in flight wanted
   int nw = 4;
   if (p.desc.wg_waves > 0) {
     nw = std::min(p.desc.wg_waves, nw_max);
   } else {
-    while (nw < nw_max && units * nw < 4096) nw *= 2;
+    while (nw < nw_max && units * nw < target) nw *= 2;
     while (nw > 4 && (nw / 2) >= tiles) nw /= 2;   // no wavefront without a tile
+    if (wps == 3 && nw == 4 && units * 4 > target && units * 3 <= target) nw = 3;
   }
   s.waves = nw;
   int64_t n = 1;
-  if (units * nw < 4096) {
-    n = ceil_div(4096, units * nw);
+  if (units * nw < target) {
+    n = ceil_div(target, units * nw);
     n = std::min<int64_t>(n, tiles / (2 * nw));
   }
   if (p.desc.max_splits > 0) n = std::min<int64_t>(n, p.desc.max_splits);

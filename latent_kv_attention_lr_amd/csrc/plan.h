@@ -26,7 +26,7 @@ namespace lr {
 struct Split {
   int32_t n_split;          // work-groups per (b, h): context splits
   int32_t tiles_per_split;  // 64-token tiles per work-group
-  int32_t waves;            // wavefronts per work-group: 4, 8 or 16
+  int32_t waves;            // wavefronts per work-group: 3, 4, 8 or 16
 };
 // Register bucket of a layer: the largest rank rounded up to 32, 64, 96 or 128.
 inline int layer_bucket(const lr_attn_plan::Layer& L) {
@@ -36,6 +36,15 @@ inline int layer_bucket(const lr_attn_plan::Layer& L) {
 // Buckets whose decode kernel puts two lanes on each token (int8 ranks above
 // 64): half the registers per lane, twice the wavefronts per compute unit.
 constexpr bool pair_lanes(int qfmt, int bucket) { return qfmt == LR_Q_INT8_TOKEN && bucket > 64; }
+// Wavefronts per SIMD each bucket's decode kernel is compiled for (its
+// register budget): enough bytes in flight per compute unit to cover HBM
+// latency without spilling.
+constexpr int decode_waves_per_simd(int qfmt, int bucket) {
+  return pair_lanes(qfmt, bucket) ? (bucket <= 96 ? 4 : 3)
+                                  : bucket <= 32 ? 5 : bucket <= 64 ? (qfmt == LR_Q_INT8_TOKEN ? 3 : 4) : 2;
+}
+// Compute units of the GPU the library is built for (MI355X, gfx950).
+constexpr int kComputeUnits = 256;
 // Largest work-group of a bucket's decode kernel: 16 wavefronts where 128
 // VGPRs per lane suffice (four wavefronts per SIMD), else 8.
 constexpr int max_wg_waves(int qfmt, int bucket) {

@@ -127,3 +127,54 @@ def test_decode_on_an_allocated_rank_table(qfmt):
     refs = oracle_many(qfmt, jobs, 1 / math.sqrt(D))
     for (b, h), ref in zip(idx, refs):
         assert within(got[b, h], ref, TOL_BF16), (b, h, rk[h], rv[h])
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("table", ["allocated", "rank64"])
+def test_decode_with_three_wavefront_work_groups(table):
+    """32 sequences x 32 heads = 1024 (b, h) units in an int8 layer whose
+    kernel holds three wavefronts per SIMD (an allocated table with ranks up
+    to 128, or every rank 64): the automatic launch takes three-wavefront
+    work-groups (four per compute unit, all resident).  Every (b, h) against
+    the oracle, ragged lengths."""
+    import torch
+    from latent_kv_attention_lr_amd.session import DecodeSession
+    from gpu_util import TOL_BF16, oracle_many, within
+    dev = "cuda:0"
+    qfmt = lr.LR_Q_INT8_TOKEN
+    if table == "allocated":
+        s = lrgen.component_scores(9, 1, 32).numpy()
+        rk, rv = lr.lr_attn_allocate_ranks(s, COST, 32 * 2 * 52 * COST)
+        rk, rv = rk[0].tolist(), rv[0].tolist()
+        assert max(rk + rv) > 96
+    else:
+        rk, rv = [64] * 32, [64] * 32
+    B, H, T = 32, 32, 200
+    print(f"three-wavefront groups: {table}, B={B} H={H} T={T}", flush=True)
+    sess = DecodeSession(1, B, H, T, qfmt, lr.LR_DT_BF16, [rk], [rv], device=dev)
+    key = lrgen.stream_key(91, 3 if table == "allocated" else 4)
+    ck = lrgen.normal(key, 0, B * T * sum(rk), 1.0).view(B, T, sum(rk)).to(dev)
+    cv = lrgen.normal(key, 1 << 30, B * T * sum(rv), 1.0).view(B, T, sum(rv)).to(dev)
+    bk = (lrgen.normal(key, 1 << 31, sum(rk) * D, 0.1)).view(sum(rk), D).to(torch.bfloat16).to(dev)
+    bv = (lrgen.normal(key, 3 << 30, sum(rv) * D, 0.1)).view(sum(rv), D).to(torch.bfloat16).to(dev)
+    q = lrgen.normal(key, 1 << 32, B * H * D, 1.0).view(B, H, D).to(torch.bfloat16).to(dev)
+    sess.set_factors(0, bk.contiguous(), bv.contiguous())
+    sess.append(0, ck.contiguous(), cv.contiguous(), torch.zeros(B, dtype=torch.int32, device=dev))
+    lens_l = [T - 5 * b if b % 3 else 1 + 6 * b for b in range(B)]   # 1..200
+    lens = torch.tensor(lens_l, dtype=torch.int32, device=dev)
+    out = torch.empty(B, H, D, dtype=torch.bfloat16, device=dev)
+    sess.decode(0, q, out, T, lengths=lens)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    offk, offv = lrgen.head_offsets(rk), lrgen.head_offsets(rv)
+    ckh, cvh, qh, bkh, bvh = ck.cpu().numpy(), cv.cpu().numpy(), q.double().cpu().numpy(), \
+        bk.double().cpu().numpy(), bv.double().cpu().numpy()
+    jobs, idx = [], []
+    for b, n in enumerate(lens_l):
+        for h in range(H):
+            jobs.append((ckh[b, :n, offk[h]:offk[h] + rk[h]], cvh[b, :n, offv[h]:offv[h] + rv[h]], qh[b, h],
+                         bkh[offk[h]:offk[h] + rk[h]], bvh[offv[h]:offv[h] + rv[h]]))
+            idx.append((b, h))
+    refs = oracle_many(qfmt, jobs, 1 / math.sqrt(D))
+    for (b, h), ref in zip(idx, refs):
+        assert within(got[b, h], ref, TOL_BF16), (b, h, rk[h], rv[h])
