@@ -226,7 +226,7 @@ def cpu_baseline(run, rows):
 
 def ffn_bench(args):
     """Hybrid FFN decode: `steps` evaluations of the LLaMA-7B-shaped hybrid FFN
-    on 16 tokens, each six launches, in one HIP graph.  The packed weights
+    on 16 tokens, each four launches, in one HIP graph.  The packed weights
     (110 MB) fit the last-level cache, so the timed steps cycle through copies
     of them (each step reads its weights from HBM, as the layers of a model
     do); the same steps on one copy are reported as warm_*."""
@@ -313,14 +313,14 @@ def ffn_bench(args):
         "vs_baseline": None, "dtype": "int8-weights,int8-activations,f32-acc", "data": "synthetic",
         "config": {"workload": f.name, "embed": E, "hidden": F, "lowrank_channels": S, "rank": r,
                    "tokens": T, "weights": "int8 per-row scale", "activations": "int8 per token per 64",
-                   "launches_per_step": 6, "launch": "hip graph of all timed steps",
+                   "launches_per_step": 4, "launch": "hip graph of all timed steps",
                    "weight_copies": R,
                    "mall": "cold: a weight byte is read again only after %.0f MB of weight reads"
                            % (R * layer.weights.numel() / 1e6)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": measured_ffn_traffic(f.name),
-                     "kernel": "k_ffn_quant + k_ffn_in + k_ffn_mid + "
-                     "k_ffn_out + k_ffn_sum (one step)", "bytes_per_step": step_bytes,
+                     "kernel": "k_ffn_quant + k_ffn_in + k_ffn_mid + k_ffn_out (one step)",
+                     "bytes_per_step": step_bytes,
                      "weight_bytes": weight_bytes, "avg_step_us": step_s * 1e6, "mall": "cold"},
     }
     if not args.no_warm_leg:

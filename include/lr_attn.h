@@ -445,7 +445,7 @@ lr_status lr_ffn_prepare_weights(const lr_ffn_desc* desc, const float* wg, const
  * the workspace holds one pass. */
 size_t lr_ffn_workspace_bytes(const lr_ffn_desc* desc, int32_t n_tokens);
 
-/* One FFN evaluation for n_tokens tokens (five or six launches per pass of
+/* One FFN evaluation for n_tokens tokens (four launches per pass of
  * tokens, in order on `stream`):
  *   weights    device, the packed weights, 256-aligned
  *   x          device bf16 [n_tokens][E], 16-aligned

@@ -13,17 +13,20 @@
 // z = A x, h) are int8 with one fp32 scale per token and per group of 64
 // elements along the reduction dimension -- the k extent of one
 // v_mfma_i32_16x16x64_i8, so every product is an exact integer sum per group,
-// converted and scaled once per group in fp32.  Five launches (six when h
-// spans several chunks):
-//   k_ffn_quant x -> codes and group scales
-//   k_ffn_in    the latents z = [A_g; A_u] x, quantised by the work-group
-//               that owns each 64-latent group; dense pairs: h = silu(g) u
+// converted and scaled once per group in fp32.  Four launches:
+//   k_ffn_quant x -> codes and group scales; clears the step's counters
+//   k_ffn_in    the latents z = [A_g; A_u] x, each 64-latent group in two
+//               work-groups over the halves of E; the second to finish adds
+//               the halves and quantises the group.  Dense pairs:
+//               h = silu(g) u
 //   k_ffn_mid   low-rank pairs: h = silu(g) u
-//   k_ffn_quant h -> codes and group scales
-//   k_ffn_out   y = W_d h, the hidden dimension split in chunks of 4096 across
-//               work-groups (k_ffn_sum adds the chunks' partial sums in order)
-// Each activation is quantised once (one wavefront per token and group); the
-// GEMM launches copy 16 tokens' codes into LDS with coalesced loads.
+//   k_ffn_out   y = W_d h, the hidden dimension split in chunks of 4096
+//               across work-groups; the last chunk of a row tile to finish
+//               adds the chunks' partial sums in chunk order
+// The last pair work-group of each 64-channel group of h (in k_ffn_in or
+// k_ffn_mid) quantises the group.  Each activation is quantised once (one
+// wavefront per token and group); the GEMM launches copy 16 tokens' codes into
+// LDS with coalesced loads.
 // At decode sizes every launch streams its int8 weights once from HBM (packed
 // so that one MFMA step of 16 rows x 64 k is 1 KB contiguous: lane l holds row
 // l & 15, k = 16 (l >> 4) .. + 15) against a block of at most 16 tokens.
@@ -66,26 +69,27 @@ __device__ __forceinline__ int code(float v, float s) {
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
-// Quantise activations: src [T][K] (bf16 or fp32, row stride ld elements) ->
-// codes dst [T][Kp] (Kp = K rounded up to 64; zeros past K) and scales
-// sc [T][Kp / 64].  One wavefront per (token, group of 64), one element per
-// lane; the group's max|v| is a wavefront reduction.
-template <bool BF16>
-__global__ __launch_bounds__(256) void k_ffn_quant(const void* src, int64_t ld, int32_t K, int32_t T, int32_t Kp,
-                                                   int8_t* dst, float* sc) {
+__device__ __forceinline__ float wave_absmax(float v) {
+  float m = fabsf(v);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  return m;
+}
+
+// Quantise x: src [T][K] bf16 (row stride ld elements) -> codes dst [T][Kp]
+// (Kp = K rounded up to 64; zeros past K) and scales sc [T][Kp / 64].  One
+// wavefront per (token, group of 64), one element per lane; the group's
+// max|v| is a wavefront reduction.  The launch also clears the n_cnt
+// counters that the step's later launches count into.
+__global__ __launch_bounds__(256) void k_ffn_quant(const uint16_t* src, int64_t ld, int32_t K, int32_t T, int32_t Kp,
+                                                   int8_t* dst, float* sc, int32_t* cnt, int32_t n_cnt) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n_cnt; i += gridDim.x * 256) cnt[i] = 0;
   const int groups = Kp / 64;
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (wave >= T * groups) return;
   const int t = wave / groups, g = wave % groups, k = 64 * g + lane;
-  float v = 0.0f;
-  if (k < K) {
-    if constexpr (BF16) v = __uint_as_float(uint32_t(static_cast<const uint16_t*>(src)[t * ld + k]) << 16);
-    else v = static_cast<const float*>(src)[t * ld + k];
-  }
-  float m = fabsf(v);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  const float s = m / 127.0f;
+  const float v = k < K ? __uint_as_float(uint32_t(src[t * ld + k]) << 16) : 0.0f;
+  const float s = wave_absmax(v) / 127.0f;
   dst[size_t(t) * Kp + k] = int8_t(code(v, s));
   if (lane == 0) sc[size_t(t) * groups + g] = s;
 }
@@ -173,6 +177,65 @@ __device__ void reduce_tiles(f32x4_t (&acc)[RT], uint8_t* smem, float* out) {
   __syncthreads();
 }
 
+// ---- the last work-group of a group finishes it ---------------------------
+// A group of work (the two halves of a latent group, the pair work-groups
+// of a 64-channel group of h, the chunks of a down-projection row tile) is
+// finished by whichever of its work-groups completes last, with no wait:
+// each counts itself on a counter (agent-scope atomic) once its share is
+// stored, and the one that brings the count to the group's size reads the
+// others' shares.  Each XCD has its own L2 and the workspace is ordinary
+// device memory, so the shares are written with device-coherent stores
+// (relaxed agent-scope atomic stores, written through), every wavefront
+// waits until its stores are acknowledged before the count, and the buffers
+// are laid out so that no cache line holds parts of two groups: no cache
+// then holds a line of a share from before it was complete (a kernel
+// boundary writes back and invalidates them), and plain loads read it.
+// (Agent-scope fences would do it too, but each writes back or invalidates
+// a whole L2; measured many times slower.)
+template <typename V>
+__device__ __forceinline__ void put(V* p, V v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+// Every wavefront waits for its stores (they count in vmcnt on this
+// architecture), then thread 0 counts the work-group's share; returns, to
+// every thread, whether it completed the group of `size`.
+__device__ bool count_last(int32_t* c, int size, int* s_flag) {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *s_flag = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == size - 1;
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+// Quantise one 64-channel group g of h (rows of Fh floats, zeros past F)
+// for tokens t0 .. t0 + 15: one wavefront per token, a lane per channel.
+__device__ void quantise_h_group(const float* h, int Fh, int F, int8_t* hq, float* hs, int Fp, int T, int t0, int g) {
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, ch = 64 * g + lane;
+  for (int tt = wid; tt < 16; tt += kWaves) {
+    const int t = t0 + tt;
+    if (t >= T) break;
+    const float v = ch < F ? h[size_t(t) * Fh + ch] : 0.0f;
+    const float s = wave_absmax(v) / 127.0f;
+    hq[size_t(t) * Fp + ch] = int8_t(code(v, s));
+    if (lane == 0) hs[size_t(t) * (Fp / 64) + g] = s;
+  }
+}
+
+// Pair work-group's 16 channels ch0 .. ch0 + 15 of h are stored: count them
+// into their group; the last quantises it.
+struct HArgs {
+  float* h;                   // [T][Fh] (Fh: F rounded up to 32, whole cache lines per group)
+  int8_t* hq;                 // [T][Fp]
+  float* hs;                  // [T][Fp / 64]
+  int32_t* hcnt;              // [TB][Fp / 64] pair work-groups done per group
+  int32_t Fh, Fp;
+};
+__device__ void h_stored(const HArgs& ha, int F, int T, int t0, int ch0, int* s_flag) {
+  const int g = ch0 >> 6, G = ha.Fp / 64;
+  if (count_last(ha.hcnt + (t0 / 16) * G + g, min(64, F - 64 * g) / 16, s_flag))
+    quantise_h_group(ha.h, ha.Fh, F, ha.hq, ha.hs, ha.Fp, T, t0, g);
+}
+
 static_assert(in_extent(2048) <= kLdsS && in_extent(4096) <= kLdsM && in_extent(8192) <= kLdsL &&
                   mid_extent(1024) <= kLdsS && mid_extent(2048) <= kLdsM && mid_extent(4096) <= kLdsL,
               "LDS instances");
@@ -182,34 +245,35 @@ struct InArgs {
   const float* xs;            // [T][E / 64]
   const uint8_t* w;           // packed tiles: dense pairs (gate, up), then latent rows of [A_g; A_u]
   const float* ws;            // row scales in tile order
-  float* h;                   // [T][F]
+  HArgs ha;
+  float* zp;                  // [2][T][2 r] the two halves' partial latents (before row scales)
+  int32_t* zcnt;              // [TB][lat_groups] halves done per latent group
   int8_t* zq;                 // [T][2 r] codes of the latents z = [A_g; A_u] x
   float* zs;                  // [T][2 r / 64] their group scales
   int32_t T, E, F, S, pairs, lat_groups;   // pairs = (F - S) / 16; lat_groups = 2 r / 64
 };
 
-// Launch 2: work-group = (latent group j or dense pair p, block of 16 tokens).
-// The latent groups come first in the grid (their work-groups carry twice a
-// pair's weights) and each owns one whole activation group of z -- 64
-// latents, four 16-row tiles -- so it quantises z itself (the int8 rule of
-// k_ffn_quant on the same fp32 values) and no separate launch is needed.
+// Launch 2: work-group = (latent half-group or dense pair, block of 16
+// tokens).  Latent group j (64 latents, four 16-row tiles, one activation
+// group of z) is split over E: work-group (j, q) sums the steps of half q.
+// The latent work-groups come first in the grid.
 template <int LDS>
 __global__ __launch_bounds__(kThreads) void k_ffn_in(InArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
-  const int rs = row_stride(a.E), steps = a.E / 64;
+  __shared__ int s_flag;
+  const int steps = a.E / 64;
   float* outv = reinterpret_cast<float*>(smem + code_area(block_bytes(a.E)));
-  const int units = a.pairs + a.lat_groups;
+  const int units = a.pairs + 2 * a.lat_groups;
   const int unit = blockIdx.x % units, t0 = 16 * (blockIdx.x / units);
   int8_t* act = reinterpret_cast<int8_t*>(smem);
-  float* scale = reinterpret_cast<float*>(smem + scale_offset(a.E));
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  auto stage = [&]() {
-    stage_codes(a.xq, a.xs, a.E, 0, a.E, a.T, t0, act, scale, rs);
-    __syncthreads();
-  };
-  if (unit < a.lat_groups) {   // uniform: latent group j = unit, tiles 2 pairs + 4 j ..
-    const int tile0 = 2 * a.pairs + 4 * unit;
+  if (unit < 2 * a.lat_groups) {   // uniform: latent group j, half q; tiles 2 pairs + 4 j ..
+    const int j = unit >> 1, q = unit & 1;
+    const int h0 = steps / 2, c0 = q ? h0 : 0, n = q ? steps - h0 : h0;   // this half's steps
+    const int rs = row_stride(64 * n);
+    float* scale = reinterpret_cast<float*>(smem + scale_offset(64 * n));
+    const int tile0 = 2 * a.pairs + 4 * j;
     const uint8_t* wt[4];
     const int8_t* acts[4];
     const float* scs[4];
@@ -221,39 +285,50 @@ __global__ __launch_bounds__(kThreads) void k_ffn_in(InArgs a) {
       scs[r] = scale;
       acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    gemm_steps<4>(wt, steps * wid / kWaves, steps * (wid + 1) / kWaves, 0, acts, scs, rs, steps, acc, stage);
+    gemm_steps<4>(wt, c0 + n * wid / kWaves, c0 + n * (wid + 1) / kWaves, c0, acts, scs, rs, n, acc, [&]() {
+      stage_codes(a.xq, a.xs, a.E, 64 * c0, 64 * n, a.T, t0, act, scale, rs);
+      __syncthreads();
+    });
     reduce_tiles<4>(acc, smem, outv);
-    // one wavefront per token (two tokens each): lane = latent 16 r + nn of the group
-    const int r = lane >> 4, nn = lane & 15;
+    // this half's sums, lane = latent 16 r + nn of the group, one wavefront per token
+    const int zr = 64 * a.lat_groups, r = lane >> 4, nn = lane & 15;   // zr = 2 r floats per token
     for (int tt = wid; tt < 16; tt += kWaves) {
       const int t = t0 + tt;
-      const float v = outv[(r * 16 + tt) * 16 + nn] * a.ws[16 * (tile0 + r) + nn];
-      float m = fabsf(v);
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-      const float s = m / 127.0f;
-      if (t < a.T) {
-        const int zrow = 2 * (a.lat_groups * 32);   // codes per token: 2 r
-        a.zq[size_t(t) * zrow + 64 * unit + lane] = int8_t(code(v, s));
-        if (lane == 0) a.zs[size_t(t) * a.lat_groups + unit] = s;
-      }
+      if (t < a.T) put(a.zp + (size_t(q) * a.T + t) * zr + 64 * j + lane, outv[(r * 16 + tt) * 16 + nn]);
+    }
+    if (!count_last(a.zcnt + (t0 / 16) * a.lat_groups + j, 2, &s_flag)) return;
+    // the second half to finish: z = (half 0 + half 1) x row scale, quantised per token
+    for (int tt = wid; tt < 16; tt += kWaves) {
+      const int t = t0 + tt;
+      if (t >= a.T) break;
+      const size_t o = size_t(t) * zr + 64 * j + lane;
+      const float v = (a.zp[o] + a.zp[size_t(a.T) * zr + o]) * a.ws[16 * (tile0 + r) + nn];
+      const float s = wave_absmax(v) / 127.0f;
+      a.zq[o] = int8_t(code(v, s));
+      if (lane == 0) a.zs[size_t(t) * a.lat_groups + j] = s;
     }
     return;
   }
-  const int p = unit - a.lat_groups;   // dense pair p: tiles (gate, up) = 2 p, 2 p + 1
+  const int rs = row_stride(a.E);
+  float* scale = reinterpret_cast<float*>(smem + scale_offset(a.E));
+  const int p = unit - 2 * a.lat_groups;   // dense pair p: tiles (gate, up) = 2 p, 2 p + 1
   const int tile0 = 2 * p;
   const uint8_t* wt[2] = {a.w + size_t(tile0) * steps * 1024, a.w + size_t(tile0 + 1) * steps * 1024};
   const int8_t* acts[2] = {act, act};
   const float* scs[2] = {scale, scale};
   f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-  gemm_steps<2>(wt, steps * wid / kWaves, steps * (wid + 1) / kWaves, 0, acts, scs, rs, steps, acc, stage);
+  gemm_steps<2>(wt, steps * wid / kWaves, steps * (wid + 1) / kWaves, 0, acts, scs, rs, steps, acc, [&]() {
+    stage_codes(a.xq, a.xs, a.E, 0, a.E, a.T, t0, act, scale, rs);
+    __syncthreads();
+  });
   reduce_tiles<2>(acc, smem, outv);
   for (int i = threadIdx.x; i < 256; i += kThreads) {
     const int tt = i >> 4, nn = i & 15, t = t0 + tt;
     if (t >= a.T) continue;
     const float v0 = outv[i] * a.ws[16 * tile0 + nn], v1 = outv[256 + i] * a.ws[16 * (tile0 + 1) + nn];
-    a.h[size_t(t) * a.F + a.S + 16 * p + nn] = silu_mul(v0, v1);   // channel S + 16 p + nn
+    put(a.ha.h + size_t(t) * a.ha.Fh + a.S + 16 * p + nn, silu_mul(v0, v1));   // channel S + 16 p + nn
   }
+  h_stored(a.ha, a.F, a.T, t0, a.S + 16 * p, &s_flag);
 }
 
 struct MidArgs {
@@ -261,7 +336,7 @@ struct MidArgs {
   const float* zs;            // [T][2 r / 64]
   const uint8_t* w;           // packed pairs (B_g, B_u), k = r
   const float* ws;
-  float* h;                   // [T][F], channels [0, S)
+  HArgs ha;                   // h channels [0, S)
   int32_t T, r, F, pairs;     // pairs = S / 16
 };
 
@@ -270,6 +345,7 @@ struct MidArgs {
 template <int LDS>
 __global__ __launch_bounds__(kThreads) void k_ffn_mid(MidArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
+  __shared__ int s_flag;
   const int rs = row_stride(a.r), steps = a.r / 64;
   float* outv = reinterpret_cast<float*>(smem + code_area(2 * block_bytes(a.r)));
   const int unit = blockIdx.x % a.pairs, t0 = 16 * (blockIdx.x / a.pairs);   // launched only when pairs >= 1
@@ -295,9 +371,10 @@ __global__ __launch_bounds__(kThreads) void k_ffn_mid(MidArgs a) {
   for (int i = threadIdx.x; i < 256; i += kThreads) {
     const int tt = i >> 4, nn = i & 15, t = t0 + tt;
     if (t < a.T)
-      a.h[size_t(t) * a.F + 16 * unit + nn] =
-          silu_mul(outv[i] * a.ws[16 * tile0 + nn], outv[256 + i] * a.ws[16 * (tile0 + 1) + nn]);
+      put(a.ha.h + size_t(t) * a.ha.Fh + 16 * unit + nn,
+          silu_mul(outv[i] * a.ws[16 * tile0 + nn], outv[256 + i] * a.ws[16 * (tile0 + 1) + nn]));
   }
+  h_stored(a.ha, a.F, a.T, t0, 16 * unit, &s_flag);
 }
 
 struct OutArgs {
@@ -305,18 +382,22 @@ struct OutArgs {
   const float* hs;            // [T][Fp / 64]
   const uint8_t* w;           // packed W_d tiles, k = Fp
   const float* ws;
-  float* y;                   // [T][E] when splits == 1, else partials [splits][T][E]
+  float* y;                   // [T][E]
+  float* yp;                  // partials [splits][T][E] when splits > 1
+  int32_t* ycnt;              // [TB][units] chunks done per row tile
   int32_t T, E, Fp, units, splits;   // units = E / (16 RT); splits = ceil(Fp / CHUNK)
 };
 
-// Launch 6: work-group = (RT tiles of 16 rows of W_d, one CHUNK of the hidden
+// Launch 4: work-group = (RT tiles of 16 rows of W_d, one CHUNK of the hidden
 // dimension, block of 16 tokens); its chunk of h's codes comes through LDS
-// once for all RT tiles.  With several chunks each work-group writes its
-// scaled partial sum, and k_ffn_sum adds them in chunk order.
+// once for all RT tiles.  With several chunks each work-group stores its
+// scaled partial sum, and the last chunk of the row tile to finish adds them
+// in chunk order (RT = 2 then: a token's 32 rows are one 128-byte line).
 template <int LDS, int CHUNK, int RT>
 __global__ __launch_bounds__(kThreads) void k_ffn_out(OutArgs a) {
   static_assert(out_extent(CHUNK, RT) <= LDS && RT <= 2, "chunk exceeds LDS");
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
+  __shared__ int s_flag;
   const int unit = blockIdx.x % a.units, split = (blockIdx.x / a.units) % a.splits;
   const int t0 = 16 * (blockIdx.x / (a.units * a.splits));
   const int steps = a.Fp / 64, kc = min(CHUNK, a.Fp);
@@ -342,20 +423,27 @@ __global__ __launch_bounds__(kThreads) void k_ffn_out(OutArgs a) {
     __syncthreads();
   });
   reduce_tiles<RT>(acc, smem, outv);
-  float* dst = a.y + size_t(a.splits > 1 ? split : 0) * a.T * a.E;
+  if (a.splits == 1) {
+    for (int i = threadIdx.x; i < RT * 256; i += kThreads) {
+      const int r = i >> 8, tt = (i >> 4) & 15, nn = i & 15, t = t0 + tt, row = 16 * (RT * unit + r) + nn;
+      if (t < a.T) a.y[size_t(t) * a.E + row] = outv[i] * a.ws[row];
+    }
+    return;
+  }
+  const size_t n = size_t(a.T) * a.E;
   for (int i = threadIdx.x; i < RT * 256; i += kThreads) {
     const int r = i >> 8, tt = (i >> 4) & 15, nn = i & 15, t = t0 + tt, row = 16 * (RT * unit + r) + nn;
-    if (t < a.T) dst[size_t(t) * a.E + row] = outv[i] * a.ws[row];
+    if (t < a.T) put(a.yp + split * n + size_t(t) * a.E + row, outv[i] * a.ws[row]);
   }
-}
-
-// y[i] = sum over splits s = 0, 1, ... of yp[s][i] (in that order).
-__global__ __launch_bounds__(256) void k_ffn_sum(const float* yp, float* y, int32_t n, int32_t splits) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  float v = 0.0f;
-  for (int s = 0; s < splits; ++s) v += yp[size_t(s) * n + i];
-  y[i] = v;
+  if (!count_last(a.ycnt + (t0 / 16) * a.units + unit, a.splits, &s_flag)) return;
+  for (int i = threadIdx.x; i < RT * 256; i += kThreads) {   // y = sum over chunks s = 0, 1, ... in order
+    const int r = i >> 8, tt = (i >> 4) & 15, nn = i & 15, t = t0 + tt, row = 16 * (RT * unit + r) + nn;
+    if (t >= a.T) continue;
+    const size_t o = size_t(t) * a.E + row;
+    float v = 0.0f;
+    for (int c = 0; c < a.splits; ++c) v += a.yp[c * n + o];
+    a.y[o] = v;
+  }
 }
 
 }  // namespace
@@ -371,20 +459,30 @@ int launch_ffn(const FfnLayout& f, const void* weights, const void* x, int32_t n
   float* xs = reinterpret_cast<float*>(ws + f.ws_xs);
   int8_t* zq = reinterpret_cast<int8_t*>(ws + f.ws_zq);
   float* zs = reinterpret_cast<float*>(ws + f.ws_zs);
-  float* h = reinterpret_cast<float*>(ws + f.ws_h);
-  int8_t* hq = reinterpret_cast<int8_t*>(ws + f.ws_hq);
-  float* hs = reinterpret_cast<float*>(ws + f.ws_hs);
   const int T = n_tokens;
   const unsigned tb = unsigned((T + 15) / 16);
-  auto quant_grid = [&](int Kp) { return dim3(unsigned((T * (Kp / 64) + 3) / 4)); };
+  const OutShape osh = out_shape(f.Fp);
+  const int chunk = osh.chunk, splits = osh.splits, rt = osh.rt, out_units = f.E / (16 * rt);
+  const int G = f.Fp / 64, lat_groups = 2 * f.r / 64;
+  // counters: halves per latent group, pair work-groups per group of h, chunks per row tile
+  int32_t* cnt = reinterpret_cast<int32_t*>(ws + f.ws_cnt);
+  int32_t* zcnt = cnt;
+  int32_t* hcnt = zcnt + tb * lat_groups;
+  int32_t* ycnt = hcnt + tb * G;
+  const int n_cnt = int(tb) * (lat_groups + G + out_units);
+  if (size_t(n_cnt) * 4 > f.ws_cnt_bytes) return int(hipErrorInvalidValue);
+  HArgs ha{reinterpret_cast<float*>(ws + f.ws_h), reinterpret_cast<int8_t*>(ws + f.ws_hq),
+           reinterpret_cast<float*>(ws + f.ws_hs), hcnt, f.h_ld, f.Fp};
   int err = 0;
 
-  hipLaunchKernelGGL(k_ffn_quant<true>, quant_grid(f.E), dim3(256), 0, s, x, int64_t(f.E), f.E, T, f.E, xq, xs);
+  const unsigned qgrid = unsigned((T * (f.E / 64) + 3) / 4);
+  hipLaunchKernelGGL(k_ffn_quant, dim3(qgrid), dim3(256), 0, s, static_cast<const uint16_t*>(x), int64_t(f.E), f.E, T,
+                     f.E, xq, xs, cnt, n_cnt);
   if ((err = int(hipGetLastError())) != 0) return err;
-  InArgs ia{xq, xs, w + f.off_w1, reinterpret_cast<const float*>(w + f.off_s1), h, zq, zs, T, f.E, f.F, f.S,
-            (f.F - f.S) / 16, 2 * f.r / 64};
+  InArgs ia{xq, xs, w + f.off_w1, reinterpret_cast<const float*>(w + f.off_s1), ha,
+            reinterpret_cast<float*>(ws + f.ws_zp), zcnt, zq, zs, T, f.E, f.F, f.S, (f.F - f.S) / 16, lat_groups};
   if (ia.pairs + ia.lat_groups > 0) {
-    const dim3 g(unsigned(ia.pairs + ia.lat_groups) * tb), b(kThreads);
+    const dim3 g(unsigned(ia.pairs + 2 * ia.lat_groups) * tb), b(kThreads);
     const int lds = instance_for(in_extent(f.E));   // the smallest instance that holds it
     if (lds == kLdsS) hipLaunchKernelGGL(k_ffn_in<kLdsS>, g, b, 0, s, ia);
     else if (lds == kLdsM) hipLaunchKernelGGL(k_ffn_in<kLdsM>, g, b, 0, s, ia);
@@ -393,7 +491,7 @@ int launch_ffn(const FfnLayout& f, const void* weights, const void* x, int32_t n
     if ((err = int(hipGetLastError())) != 0) return err;
   }
   if (f.S > 0) {
-    MidArgs ma{zq, zs, w + f.off_w2, reinterpret_cast<const float*>(w + f.off_s2), h, T, f.r, f.F, f.S / 16};
+    MidArgs ma{zq, zs, w + f.off_w2, reinterpret_cast<const float*>(w + f.off_s2), ha, T, f.r, f.F, f.S / 16};
     const dim3 g(unsigned(ma.pairs) * tb), b(kThreads);
     const int lds = instance_for(mid_extent(f.r));
     if (lds == kLdsS) hipLaunchKernelGGL(k_ffn_mid<kLdsS>, g, b, 0, s, ma);
@@ -402,26 +500,16 @@ int launch_ffn(const FfnLayout& f, const void* weights, const void* x, int32_t n
     else return int(hipErrorInvalidConfiguration);
     if ((err = int(hipGetLastError())) != 0) return err;
   }
-  hipLaunchKernelGGL(k_ffn_quant<false>, quant_grid(f.Fp), dim3(256), 0, s, h, int64_t(f.F), f.F, T, f.Fp, hq, hs);
-  if ((err = int(hipGetLastError())) != 0) return err;
   // Chunks of 4096 (2048 for small hidden sizes); with several chunks a
   // work-group takes two row tiles, so each staged chunk of h serves 32 rows
   // of W_d (measured best on the LLaMA-7B FFN among chunks of 1, 2, 4 and 8 K
   // with one or two tiles).
-  const OutShape osh = out_shape(f.Fp);
-  const int chunk = osh.chunk, splits = osh.splits, rt = osh.rt;
-  float* yp = reinterpret_cast<float*>(ws + f.ws_yp);
-  OutArgs oa{hq, hs, w + f.off_w3, reinterpret_cast<const float*>(w + f.off_s3), splits > 1 ? yp : y, T, f.E, f.Fp,
-             f.E / (16 * rt), splits};
+  OutArgs oa{ha.hq, ha.hs, w + f.off_w3, reinterpret_cast<const float*>(w + f.off_s3), y,
+             reinterpret_cast<float*>(ws + f.ws_yp), ycnt, T, f.E, f.Fp, out_units, splits};
   const dim3 g(unsigned(oa.units) * unsigned(splits) * tb), b(kThreads);
   if (chunk == 2048) hipLaunchKernelGGL((k_ffn_out<kLdsS, 2048, 1>), g, b, 0, s, oa);
   else if (rt == 1) hipLaunchKernelGGL((k_ffn_out<kLdsM, 4096, 1>), g, b, 0, s, oa);
   else hipLaunchKernelGGL((k_ffn_out<kLdsM, 4096, 2>), g, b, 0, s, oa);
-  if ((err = int(hipGetLastError())) != 0) return err;
-  if (splits > 1) {
-    const int n = T * f.E;
-    hipLaunchKernelGGL(k_ffn_sum, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, yp, y, n, splits);
-  }
   return int(hipGetLastError());
 }
 

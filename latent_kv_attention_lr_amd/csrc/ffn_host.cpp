@@ -44,22 +44,31 @@ void ffn_workspace(lr::FfnLayout* f, size_t T) {
   const size_t E = size_t(f->E), r2 = 2 * size_t(f->r), F = size_t(f->F), Fp = size_t(f->Fp);
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
+  const size_t chunk = Fp <= 2048 ? 2048 : 4096, splits = (Fp + chunk - 1) / chunk;
+  const size_t rt = splits > 1 ? 2 : 1, TB = (T + 15) / 16;
+  // counters, per block of 16 tokens: halves done per latent group, pair
+  // work-groups done per group of h, chunks done per down-projection row tile
+  f->ws_cnt_bytes = 4 * TB * (r2 / 64 + Fp / 64 + E / (16 * rt));
+  f->ws_cnt = take(f->ws_cnt_bytes);
   f->ws_xq = take(T * E);
   f->ws_xs = take(T * (E / 64) * 4);
+  f->ws_zp = take(2 * T * r2 * 4);   // the two halves' partial latents
   f->ws_zq = take(T * r2);
   f->ws_zs = take(T * (r2 / 64) * 4);
-  f->ws_h = take(T * F * 4);
+  // h rows padded to whole 128-byte lines, so a line never holds two groups
+  f->h_ld = int32_t((F + 31) / 32 * 32);
+  f->ws_h = take(T * size_t(f->h_ld) * 4);
   f->ws_hq = take(T * Fp);
   f->ws_hs = take(T * (Fp / 64) * 4);
-  const size_t chunk = Fp <= 2048 ? 2048 : 4096, splits = (Fp + chunk - 1) / chunk;
   f->ws_yp = take(splits > 1 ? splits * T * E * 4 : 0);   // partial sums of the down projection
   f->ws_bytes = o;
 }
 
 // Tokens per pass of the launches: a multiple of 16 such that no launch of a
 // pass has more than 2^16 work-groups.  Work-groups per 16 tokens, per launch:
-// quantise x E / 16, z r / 8, h Fp / 16; k_ffn_in (F - S) / 16 + r / 16;
-// k_ffn_mid S / 16; k_ffn_out at most E / 16 per chunk; the sum E / 16.
+// quantise x E / 16; k_ffn_in (F - S) / 16 + r / 16; k_ffn_mid S / 16;
+// k_ffn_out at most E / 16 per chunk.  (The bound keeps the terms r / 8 and
+// Fp / 16 of launches since merged, so pass sizes are unchanged.)
 size_t ffn_pass_tokens(const lr::FfnLayout& f) {
   const size_t E = size_t(f.E), F = size_t(f.F), S = size_t(f.S), r = size_t(f.r), Fp = size_t(f.Fp);
   const size_t chunks = Fp <= 2048 ? 1 : (Fp + 4095) / 4096;

@@ -85,9 +85,11 @@ def test_ffn_weight_and_workspace_sizes():
             + r256(n3 * 64))
     assert lr.lr_ffn_weight_bytes(_desc(E, F, S, r)) == want
     T = 5
-    ws = (r256(T * E) + r256(T * (E // 64) * 4) + r256(T * 2 * r)
+    counters = 4 * 1 * (2 * r // 64 + Fp // 64 + E // 16)   # one token block, one chunk, 16-row tiles
+    ws = (r256(counters) + r256(T * E) + r256(T * (E // 64) * 4) + r256(2 * T * 2 * r * 4) + r256(T * 2 * r)
           + r256(T * (2 * r // 64) * 4) + r256(T * F * 4) + r256(T * Fp) + r256(T * (Fp // 64) * 4))
-    # (no partial sums: the hidden dimension fits one chunk of the down projection)
+    # (the two halves' partial latents; h rows already whole 128-byte lines;
+    # no partial sums: the hidden dimension fits one chunk of the down projection)
     assert lr.lr_ffn_workspace_bytes(_desc(E, F, S, r), T) == ws
     assert lr.lr_ffn_workspace_bytes(_desc(E, F, S, r), 0) == 0
 
