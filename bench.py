@@ -374,8 +374,8 @@ def choose_replicas(total_cache_bytes, requested):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; multi-GPU sharding is a design note, "
-              "not an implemented path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py: measures one GPU only; sharding across GPUs is described, not implemented "
+              "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     if args.ffn:
         ffn_bench(args)
