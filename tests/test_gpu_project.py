@@ -62,13 +62,18 @@ def _gpu_project(s, x_bf, ak, av):
     return ck.cpu().numpy(), cv.cpu().numpy()
 
 
-def _check_bound(got, x, a, rows=None):
-    """Worst-case and RMS rounding checks of fp32 latents against the oracle."""
+def _oracle_ref(x, a, rows=None):
+    """The oracle's latents x A and the magnitudes |x| |A| that bound their rounding."""
     x64 = x.double().numpy() if rows is None else x.double().numpy()[rows]
     a64 = a.double().numpy()
-    E = x64.shape[1]
-    ref = oracle.latents(x64, a64)
-    mag = oracle.latents(np.abs(x64), np.abs(a64))
+    return oracle.latents(x64, a64), oracle.latents(np.abs(x64), np.abs(a64))
+
+
+def _check_bound(got, x, a, rows=None, pre=None):
+    """Worst-case and RMS rounding checks of fp32 latents against the oracle
+    (pre: _oracle_ref(x, a, rows), when several results share it)."""
+    E = x.shape[1]
+    ref, mag = _oracle_ref(x, a, rows) if pre is None else pre
     g = got if rows is None else got[rows]
     err = np.abs(g.astype(np.float64) - ref)
     bound = 2.0 * (E - 1) * U32 * mag * 1.01 + U32 * np.abs(ref)
@@ -381,6 +386,8 @@ def test_project_parts_sum_to_latents_within_rounding_bound(idx, T):
     T, E = xd.shape
     nk, nv = s.latent_elems(0, 0), s.latent_elems(0, 1)
     ck1, cv1 = s.project(0, xd)
+    xb = x.to(torch.bfloat16).float()
+    pre_k, pre_v = _oracle_ref(xb, ak), _oracle_ref(xb, av)   # shared by every part count
     for parts in range(1, 9):
         say(f"project parts workload {idx} parts={parts}")
         pk = torch.empty(parts, T, nk, dtype=torch.float32, device=DEV)
@@ -393,8 +400,8 @@ def test_project_parts_sum_to_latents_within_rounding_bound(idx, T):
         for q in range(1, parts):
             sk += pk[q]
             sv += pv[q]
-        _check_bound(sk.cpu().numpy(), x.to(torch.bfloat16).float(), ak)
-        _check_bound(sv.cpu().numpy(), x.to(torch.bfloat16).float(), av)
+        _check_bound(sk.cpu().numpy(), xb, ak, pre=pre_k)
+        _check_bound(sv.cpu().numpy(), xb, av, pre=pre_v)
 
 
 @pytest.mark.parametrize("T", [1, 16, 40, 64, 100])
