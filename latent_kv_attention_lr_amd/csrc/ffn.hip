@@ -97,19 +97,48 @@ __global__ __launch_bounds__(256) void k_ffn_quant(const uint16_t* src, int64_t 
 // Copy codes of tokens t0 .. t0 + 15 (clamped to T - 1), columns c0 .. c0 +
 // kn - 1 of an int8 matrix (row stride ld, kn a multiple of 64) and their
 // group scales (row stride ld / 64) into an LDS block: codes [16][rs], scales
-// [16][kn / 64].  Coalesced 16-byte loads.
+// [16][kn / 64].  Loads go straight from memory into LDS (one wavefront load
+// writes a lane's 16 or 4 bytes at the wavefront's LDS base + 16 or 4 x
+// lane), so the copy holds no registers while the weights are in flight;
+// `staged` then waits for them and passes a barrier.
+#ifndef LR_FFN_LDS_DMA
+#define LR_FFN_LDS_DMA 1
+#endif
+using lds_ptr = __attribute__((address_space(3))) void*;
 __device__ void stage_codes(const int8_t* codes, const float* scales, int64_t ld, int c0, int kn, int T, int t0,
                             int8_t* act, float* scale, int rs) {
   const int pieces = kn / 16, gn = kn / 64;
-  for (int i = threadIdx.x; i < 16 * pieces; i += kThreads) {
-    const int tt = i / pieces, col = i % pieces, t = min(t0 + tt, T - 1);
-    *reinterpret_cast<uint4*>(act + tt * rs + 16 * col) =
-        *reinterpret_cast<const uint4*>(codes + t * ld + c0 + 16 * col);
+  if constexpr (LR_FFN_LDS_DMA) {
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int segs = (pieces + 63) / 64, gsegs = (gn + 63) / 64;
+    for (int job = wid; job < 16 * segs; job += kWaves) {   // one 1 KB row segment per wavefront load
+      const int tt = job / segs, sg = job % segs, t = min(t0 + tt, T - 1), piece = 64 * sg + lane;
+      if (piece < pieces)
+        __builtin_amdgcn_global_load_lds(codes + t * ld + c0 + 16 * piece, (lds_ptr)(act + tt * rs + 1024 * sg), 16, 0, 0);
+    }
+    for (int job = wid; job < 16 * gsegs; job += kWaves) {
+      const int tt = job / gsegs, sg = job % gsegs, t = min(t0 + tt, T - 1), g = 64 * sg + lane;
+      if (g < gn)
+        __builtin_amdgcn_global_load_lds(scales + t * (ld / 64) + c0 / 64 + g, (lds_ptr)(scale + tt * gn + 64 * sg), 4, 0, 0);
+    }
+  } else {
+    for (int i = threadIdx.x; i < 16 * pieces; i += kThreads) {
+      const int tt = i / pieces, col = i % pieces, t = min(t0 + tt, T - 1);
+      *reinterpret_cast<uint4*>(act + tt * rs + 16 * col) =
+          *reinterpret_cast<const uint4*>(codes + t * ld + c0 + 16 * col);
+    }
+    for (int i = threadIdx.x; i < 16 * gn; i += kThreads) {
+      const int tt = i / gn, g = i % gn, t = min(t0 + tt, T - 1);
+      scale[i] = scales[t * (ld / 64) + c0 / 64 + g];
+    }
   }
-  for (int i = threadIdx.x; i < 16 * gn; i += kThreads) {
-    const int tt = i / gn, g = i % gn, t = min(t0 + tt, T - 1);
-    scale[i] = scales[t * (ld / 64) + c0 / 64 + g];
-  }
+}
+
+// After stage_codes: this wavefront's loads (the copies into LDS among them)
+// are complete, then a barrier -- the staged block is complete for all.
+__device__ __forceinline__ void staged() {
+  if constexpr (LR_FFN_LDS_DMA) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __syncthreads();
 }
 
 // acc[r] += over this wavefront's steps c in [c0, c1) of tile r: the int8
@@ -287,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void k_ffn_in(InArgs a) {
     }
     gemm_steps<4>(wt, c0 + n * wid / kWaves, c0 + n * (wid + 1) / kWaves, c0, acts, scs, rs, n, acc, [&]() {
       stage_codes(a.xq, a.xs, a.E, 64 * c0, 64 * n, a.T, t0, act, scale, rs);
-      __syncthreads();
+      staged();
     });
     reduce_tiles<4>(acc, smem, outv);
     // this half's sums, lane = latent 16 r + nn of the group, one wavefront per token
@@ -319,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void k_ffn_in(InArgs a) {
   f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
   gemm_steps<2>(wt, steps * wid / kWaves, steps * (wid + 1) / kWaves, 0, acts, scs, rs, steps, acc, [&]() {
     stage_codes(a.xq, a.xs, a.E, 0, a.E, a.T, t0, act, scale, rs);
-    __syncthreads();
+    staged();
   });
   reduce_tiles<2>(acc, smem, outv);
   for (int i = threadIdx.x; i < 256; i += kThreads) {
@@ -365,7 +394,7 @@ __global__ __launch_bounds__(kThreads) void k_ffn_mid(MidArgs a) {
   gemm_steps<2>(wt, steps * wid / kWaves, steps * (wid + 1) / kWaves, 0, acts, scs, rs, steps, acc, [&]() {
     for (int half = 0; half < 2; ++half)
       stage_codes(a.zq, a.zs, 2 * a.r, half * a.r, a.r, a.T, t0, act[half], sc[half], rs);
-    __syncthreads();
+    staged();
   });
   reduce_tiles<2>(acc, smem, outv);
   for (int i = threadIdx.x; i < 256; i += kThreads) {
@@ -420,7 +449,7 @@ __global__ __launch_bounds__(kThreads) void k_ffn_out(OutArgs a) {
   const int cb = k0 / 64;
   gemm_steps<RT>(wt, cb + gn * wid / kWaves, cb + gn * (wid + 1) / kWaves, cb, acts, scs, rs, gn, acc, [&]() {
     stage_codes(a.hq, a.hs, a.Fp, k0, kn, a.T, t0, act, scale, rs);
-    __syncthreads();
+    staged();
   });
   reduce_tiles<RT>(acc, smem, outv);
   if (a.splits == 1) {
