@@ -491,6 +491,8 @@ int launch_ffn(const FfnLayout& f, const void* weights, const void* x, int32_t n
   const int T = n_tokens;
   const unsigned tb = unsigned((T + 15) / 16);
   const OutShape osh = out_shape(f.Fp);
+  // the workspace (partial sums, counters) must be laid out for the same chunks
+  if (osh.splits != f.out_splits || osh.rt != f.out_rt) return int(hipErrorInvalidValue);
   const int chunk = osh.chunk, splits = osh.splits, rt = osh.rt, out_units = f.E / (16 * rt);
   const int G = f.Fp / 64, lat_groups = 2 * f.r / 64;
   // counters: halves per latent group, pair work-groups per group of h, chunks per row tile

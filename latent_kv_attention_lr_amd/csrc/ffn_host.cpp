@@ -8,6 +8,7 @@
 #include <cstring>
 #include <vector>
 
+#include "ffn_lds.h"
 #include "plan.h"
 
 namespace {
@@ -44,8 +45,10 @@ void ffn_workspace(lr::FfnLayout* f, size_t T) {
   const size_t E = size_t(f->E), r2 = 2 * size_t(f->r), F = size_t(f->F), Fp = size_t(f->Fp);
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
-  const size_t chunk = Fp <= 2048 ? 2048 : 4096, splits = (Fp + chunk - 1) / chunk;
-  const size_t rt = splits > 1 ? 2 : 1, TB = (T + 15) / 16;
+  const lr::ffnlds::OutShape osh = lr::ffnlds::out_shape(f->Fp);   // the down projection's chunks
+  const size_t splits = size_t(osh.splits), rt = size_t(osh.rt), TB = (T + 15) / 16;
+  f->out_splits = osh.splits;
+  f->out_rt = osh.rt;
   // counters, per block of 16 tokens: halves done per latent group, pair
   // work-groups done per group of h, chunks done per down-projection row tile
   f->ws_cnt_bytes = 4 * TB * (r2 / 64 + Fp / 64 + E / (16 * rt));
@@ -71,7 +74,7 @@ void ffn_workspace(lr::FfnLayout* f, size_t T) {
 // Fp / 16 of launches since merged, so pass sizes are unchanged.)
 size_t ffn_pass_tokens(const lr::FfnLayout& f) {
   const size_t E = size_t(f.E), F = size_t(f.F), S = size_t(f.S), r = size_t(f.r), Fp = size_t(f.Fp);
-  const size_t chunks = Fp <= 2048 ? 1 : (Fp + 4095) / 4096;
+  const size_t chunks = size_t(lr::ffnlds::out_shape(f.Fp).splits);
   const size_t u = std::max({E / 16 * chunks, r / 8, Fp / 16, (F - S) / 16 + r / 16, S / 16});
   return 16 * std::max<size_t>(1, (size_t(1) << 16) / u);
 }

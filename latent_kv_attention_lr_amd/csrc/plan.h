@@ -95,6 +95,7 @@ struct FfnLayout {
   size_t off_w1, off_w2, off_w3, off_s1, off_s2, off_s3, weight_bytes;
   size_t ws_cnt, ws_cnt_bytes;                      // counters of the launches' last-to-finish work-groups
   int32_t h_ld;                                      // row stride of h in floats (F rounded up to 32)
+  int32_t out_splits, out_rt;                        // down-projection chunks and row tiles the workspace is sized for
   size_t ws_xq, ws_xs, ws_zp, ws_zq, ws_zs, ws_h, ws_hq, ws_hs, ws_yp, ws_bytes;
 };
 // Records a HIP error for lr_attn_last_hip_error (this thread).
