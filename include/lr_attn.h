@@ -74,7 +74,9 @@ typedef struct lr_attn_desc {
                             (16 is lowered to 8 for layers whose largest rank is an
                             int8 rank of 33-64 or 97-128, or an int4 rank above 64).
                             Automatic picks 3 for those int8 layers when B x H is
-                            769..1024, so that every (b, h) work-group is resident */
+                            769..1024, so that every (b, h) work-group is resident.
+                            The explicit form takes 4 or 8, and 8 only in layers whose
+                            largest rank is at most 32 (4 otherwise) */
   int32_t reserved;      /* must be 0 */
   const int32_t* rank_k; /* HOST [n_layers * n_heads], row-major (layer, head) */
   const int32_t* rank_v; /* HOST [n_layers * n_heads] */

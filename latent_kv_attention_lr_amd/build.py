@@ -7,7 +7,9 @@ one shared library next to this file.
 """
 from __future__ import annotations
 
+import json
 import os
+import re
 import subprocess
 import sys
 
@@ -32,10 +34,32 @@ HOST_SOURCES = ["plan.cpp", "rotate.cpp", "alloc.cpp", "ffn_host.cpp"]
 HIP_SOURCES = ["ffn.hip", "kernels.hip", "project.hip", "probe.hip"]
 
 
-def _run(cmd):
+# The compiler's per-kernel resource report (registers, spills, scratch,
+# occupancy, LDS) for every HIP source; build() writes it to
+# _build/kernel_resources.json.
+RESOURCE_FLAG = "-Rpass-analysis=kernel-resource-usage"
+_REMARK = re.compile(r"remark:\s+(.*?):\s+(\S+)\s+\[-Rpass-analysis=kernel-resource-usage\]")
+
+
+def _run(cmd, resources=None):
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     # hipcc's host pass does not know the packed-fp32 feature and says so; that is harmless.
-    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    lines = [l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l]
+    if resources is not None:   # collect the resource remarks, keep them out of the log
+        kernel = None
+        for l in lines:
+            m = _REMARK.search(l)
+            if not m:
+                continue
+            key, val = m.group(1).strip(), m.group(2)
+            if key == "Function Name":
+                kernel = val
+                resources[kernel] = {}
+            elif kernel is not None:
+                resources[kernel][key] = val
+        # the remarks and the source lines the compiler quotes under them
+        lines = [l for l in lines if "kernel-resource-usage" not in l and not re.match(r"^\s*\d*\s*\|", l)]
+    out = "\n".join(lines)
     if r.returncode != 0:
         sys.stderr.write(out + "\n")
         raise RuntimeError("build step failed: " + " ".join(cmd))
@@ -52,16 +76,19 @@ def build(verbose: bool = False) -> str:
     kern_o = os.path.join(BUILD, "kernels.o")
     proj_o = os.path.join(BUILD, "project.o")
     probe_o = os.path.join(BUILD, "probe.o")
+    res = {}
     outs = [
         _run(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "plan.cpp"), "-o", plan_o]),
         _run(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "rotate.cpp"), "-o", rot_o]),
         _run(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "alloc.cpp"), "-o", alloc_o]),
         _run(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "ffn_host.cpp"), "-o", ffnh_o]),
-        _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "ffn.hip"), "-o", ffn_o]),
-        _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "kernels.hip"), "-o", kern_o]),
-        _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "project.hip"), "-o", proj_o]),
-        _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "probe.hip"), "-o", probe_o]),
+        _run([HIPCC, *HIP_FLAGS, RESOURCE_FLAG, "-c", os.path.join(CSRC, "ffn.hip"), "-o", ffn_o], res),
+        _run([HIPCC, *HIP_FLAGS, RESOURCE_FLAG, "-c", os.path.join(CSRC, "kernels.hip"), "-o", kern_o], res),
+        _run([HIPCC, *HIP_FLAGS, RESOURCE_FLAG, "-c", os.path.join(CSRC, "project.hip"), "-o", proj_o], res),
+        _run([HIPCC, *HIP_FLAGS, RESOURCE_FLAG, "-c", os.path.join(CSRC, "probe.hip"), "-o", probe_o], res),
     ]
+    with open(os.path.join(BUILD, "kernel_resources.json"), "w") as f:
+        json.dump(res, f, indent=1, sort_keys=True)
     tmp = LIB + ".tmp"
     outs.append(_run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp, plan_o, rot_o, alloc_o, ffnh_o, ffn_o, kern_o,
                       proj_o, probe_o]))

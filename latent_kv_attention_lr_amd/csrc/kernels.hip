@@ -1340,19 +1340,30 @@ int launch_append(const lr_attn_plan& p, int32_t layer, void* cache, const float
   return int(hipGetLastError());
 }
 
+// Eight-wavefront work-groups (two wavefronts per SIMD, 256 VGPRs each) only
+// for the 32 bucket: from rank 64 up the kernel's accumulators and code
+// registers exceed 256 VGPRs and spill, so those buckets always take four
+// (explicit_split chooses accordingly).
+template <int QF, int RR>
+void launch_explicit_r(int waves, dim3 grid, hipStream_t st, const DecodeArgs& a, const HeadTab& t) {
+  if constexpr (RR == 32) {
+    if (waves == 8) {
+      hipLaunchKernelGGL((k_decode_explicit<QF, RR, 8>), grid, dim3(512), 0, st, a, t);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((k_decode_explicit<QF, RR, 4>), grid, dim3(256), 0, st, a, t);
+}
+
 template <int QF>
 hipError_t launch_explicit_q(int bucket, int waves, dim3 grid, hipStream_t st, const DecodeArgs& a,
                              const HeadTab& t) {
-#define LR_EXPLICIT(RR)                                                                       \
-  if (waves == 8) hipLaunchKernelGGL((k_decode_explicit<QF, RR, 8>), grid, dim3(512), 0, st, a, t); \
-  else hipLaunchKernelGGL((k_decode_explicit<QF, RR, 4>), grid, dim3(256), 0, st, a, t);
   switch (bucket) {
-    case 32: LR_EXPLICIT(32) break;
-    case 64: LR_EXPLICIT(64) break;
-    case 96: LR_EXPLICIT(96) break;
-    default: LR_EXPLICIT(128) break;
+    case 32: launch_explicit_r<QF, 32>(waves, grid, st, a, t); break;
+    case 64: launch_explicit_r<QF, 64>(waves, grid, st, a, t); break;
+    case 96: launch_explicit_r<QF, 96>(waves, grid, st, a, t); break;
+    default: launch_explicit_r<QF, 128>(waves, grid, st, a, t); break;
   }
-#undef LR_EXPLICIT
   return hipGetLastError();
 }
 

@@ -86,12 +86,14 @@ Split choose_split(const lr_attn_plan& p, int32_t layer, int32_t max_len) {
 }
 
 Split explicit_split(const lr_attn_plan& p, int32_t layer, int32_t max_len) {
-  (void)layer;
+  // eight wavefronts only in the 32 bucket (above it the kernel would spill
+  // at two wavefronts per SIMD)
   Split s;
   const int64_t units = static_cast<int64_t>(p.desc.batch) * p.desc.n_heads;
   const int64_t tiles = ceil_div(max_len, kTile);
-  s.waves = (units * 4 < 4096 && tiles >= 8) ? 8 : 4;
-  if (p.desc.wg_waves == 4 || p.desc.wg_waves == 8) s.waves = p.desc.wg_waves;
+  const bool eight_ok = layer_bucket(p.layers[layer]) == 32;
+  s.waves = (eight_ok && units * 4 < 4096 && tiles >= 8) ? 8 : 4;
+  if (p.desc.wg_waves == 4 || (p.desc.wg_waves == 8 && eight_ok)) s.waves = p.desc.wg_waves;
   s.n_split = 1;
   s.tiles_per_split = static_cast<int32_t>(tiles);
   return s;

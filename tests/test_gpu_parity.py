@@ -271,6 +271,37 @@ def test_decode_context_split_path(qfmt, io):
     _check_session(*sess, [8192, 33, 4097], qfmt, io, 8192)
 
 
+# Small heads in the paired-lane int8 buckets (both ranks at most 16, one lane
+# per token, rows of at most one 16-byte chunk) beside a paired head and a
+# one-lane head of rank 24 or 40 in the same launch; the lengths end on and
+# around multiples of 3 and 4 tiles, leave some wavefronts without a step,
+# and take the split and unsplit launches.
+SMALL_RANKS = {
+    128: ([128, 8, 16, 8, 16, 24], [8, 8, 16, 16, 8, 8]),
+    96: ([96, 8, 16, 16, 40], [16, 8, 8, 16, 8]),
+}
+SMALL_LENS = [0, 1, 63, 64, 65, 192, 193, 256, 257, 700]
+
+
+@pytest.mark.parametrize("io", [LR_DT_BF16, LR_DT_F32])
+@pytest.mark.parametrize("bucket", [96, 128])
+def test_decode_small_heads_in_paired_buckets(io, bucket):
+    qfmt = LR_Q_INT8_TOKEN
+    rng = np.random.default_rng(140 + bucket + io)
+    rk, rv = SMALL_RANKS[bucket]
+    say(f"decode small heads io={io} bucket={bucket}")
+    sess = _session(qfmt, io, 0, rng, len(SMALL_LENS), 700, rk, rv)
+    _check_session(*sess, SMALL_LENS, qfmt, io, 700)
+    # one split per work-group at most: the same heads, no context split
+    sess = _session(qfmt, io, 1, rng, len(SMALL_LENS), 700, rk, rv)
+    _check_session(*sess, SMALL_LENS, qfmt, io, 700)
+    # context splits whose tile ranges need not be multiples of the step
+    sess = _long_session(qfmt, io, 0, rng, (8, rk[0]), (16, rv[0]))
+    assert lr_attn_workspace_bytes(sess[0].plan, 8192) > 0, "this shape must split the context"
+    _check_session(*sess, [8192, 33, 4097], qfmt, io, 8192)
+    _check_session(*sess, [100, 3001, 8191], qfmt, io, 8192)
+
+
 def _fused_equals_separate(sess, lens, pos, max_len, seed):
     """append + decode and the fused append_decode write the same cache bytes
     and give the same outputs, bit for bit."""
@@ -314,6 +345,16 @@ def test_append_decode_fused_equals_separate(qfmt, io):
     sess = _long_session(qfmt, io, 0, rng, *WIDE_RANKS)
     lens = [97, 4096, 8000]
     _fused_equals_separate(sess, lens, [n - 1 for n in lens], 8192, 4)
+    if qfmt == LR_Q_INT8_TOKEN:   # small heads in the paired buckets: the new token at tile edges
+        for bucket in (96, 128):
+            rk, rv = SMALL_RANKS[bucket]
+            sess = _session(qfmt, io, 0, rng, 6, 700, rk, rv)
+            lens = [1, 65, 130, 195, 257, 700]
+            _fused_equals_separate(sess, lens, [n - 1 for n in lens], 700, 5)
+            _fused_equals_separate(sess, [64, 700, 6, 200, 700, 1], [0, 400, 5, 199, 699, 0], 700, 6)
+        sess = _long_session(qfmt, io, 0, rng, (8, 128), (16, 8))
+        lens = [100, 3001, 8192]
+        _fused_equals_separate(sess, lens, [n - 1 for n in lens], 8192, 7)
 
 
 def test_decode_max_len_clamps_longer_lengths():
