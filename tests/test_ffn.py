@@ -11,9 +11,12 @@ GPU and in fp64 (then rounded to fp32) in the oracle.  So
   * an h element within DELTA of a boundary may round the other way: its code
     moves by one, y[t][e] by at most one step s_h times |W_d[e][c]| (each such
     element is added to the bound);
-  * a latent within DELTA of a boundary moves g or u of every low-rank
-    channel; such tokens (rare: DELTA = 2e-5 over a few thousand latents) get
-    1e-3 max|y_ref[t]| and are counted.
+  * a latent within DELTA of a boundary may take the other neighbouring code,
+    which moves g or u of every low-rank channel: for each such latent the
+    bound adds |y_alt[t] - y_ref[t]|, y_alt being the oracle's quantised tail
+    (B z, SwiGLU, h quantisation, W_d h) rerun with that one code changed,
+    plus the h flips possible around y_alt's own h (rare: DELTA = 2e-5 over a
+    few thousand latents; such tokens are counted).
 The boundary distances come from the oracle's own intermediates
 (lro_ffn_trace).  A flip where the oracle's value is further than DELTA from
 a boundary, a wrong group scale or index, or a dropped term exceeds this.
@@ -28,7 +31,6 @@ import oracle
 import latent_kv_attention_lr_amd as lr
 
 TOL_SUM = 2e-5     # fp32 summation, relative to max|y_ref| of the token
-TOL_Z = 1e-3       # a token with a latent on a rounding boundary
 DELTA = 2e-5       # code units: how close to a rounding boundary counts as on it
 
 
@@ -42,10 +44,35 @@ def _near_boundary(a):
     return np.abs(v - np.floor(v) - 0.5), sg
 
 
+def _dequantised_rows(m):
+    """Rows of m as the weight quantiser leaves them (codes x row scale, fp64)."""
+    q, sc = oracle.quant_int8(np.ascontiguousarray(m, np.float32))
+    return q.astype(np.float64) * sc.astype(np.float64)[:, None]
+
+
+def _dequantised_acts(a):
+    """Activations [T, K] as the group quantiser leaves them (fp64)."""
+    q, sc = oracle.quant_act_groups(a)
+    return q.astype(np.float64) * np.repeat(sc, 64, axis=1)[:, :a.shape[1]].astype(np.float64)
+
+
+def _tail(zdq, g_dense, u_dense, bgd, bud, wdd, S):
+    """The FFN after the latents' quantisation, for tokens with dequantised
+    latents zdq [n, 2r]: low-rank g, u = B z; dense g, u given; h = silu(g) u
+    rounded to fp32; y = W_d (h quantised).  Returns (y [n, E], h [n, F])."""
+    r = zdq.shape[1] // 2
+    g, u = g_dense.copy(), u_dense.copy()
+    if S:
+        g[:, :S] = zdq[:, :r] @ bgd.T
+        u[:, :S] = zdq[:, r:] @ bud.T
+    h = (g / (1.0 + np.exp(-g)) * u).astype(np.float32)
+    return _dequantised_acts(h) @ wdd.T, h
+
+
 def ffn_bound(x, w):
     """(y_ref [T, E], bound [T, E], tokens with a latent on a boundary)."""
     wg, wu, ag, au, bg, bu, wd = w
-    y, z, _, _, h = oracle.ffn_trace(x, wg, wu, ag, au, bg, bu, wd)
+    y, z, g, u, h = oracle.ffn_trace(x, wg, wu, ag, au, bg, bu, wd)
     mh, sh = _near_boundary(h)
     absw = np.abs(wd.astype(np.float64)) * (1.0 + 1.0 / 254)   # dequantised |W_d| (RTN error <= s/2)
     bound = TOL_SUM * np.max(np.abs(y), axis=1, keepdims=True).repeat(y.shape[1], axis=1)
@@ -53,10 +80,24 @@ def ffn_bound(x, w):
     bound += flips @ absw.T
     z_tokens = []
     if z.shape[1]:
-        mz, _ = _near_boundary(z)
+        mz, sz = _near_boundary(z)
         z_tokens = [t for t in range(z.shape[0]) if np.any(mz[t] < DELTA)]
+    if z_tokens:
+        S = bg.shape[0]
+        bgd, bud, wdd = _dequantised_rows(bg), _dequantised_rows(bu), _dequantised_rows(wd)
+        zdq = _dequantised_acts(z)
+        # the tail reproduces the oracle's y before any code is changed
+        y0, _ = _tail(zdq[z_tokens], g[z_tokens], u[z_tokens], bgd, bud, wdd, S)
+        assert np.allclose(y0, y[z_tokens], rtol=1e-9, atol=1e-12 * float(np.max(np.abs(y))))
         for t in z_tokens:
-            bound[t] += TOL_Z * np.max(np.abs(y[t]))
+            for k in np.flatnonzero(mz[t] < DELTA):
+                v = float(z[t, k]) / float(sz[t, k])                    # the latent in code units
+                code = float(np.rint(v))
+                alt = zdq[t:t + 1].copy()
+                alt[0, k] += (1.0 if v > code else -1.0) * float(sz[t, k])   # the other neighbouring code
+                ya, ha = _tail(alt, g[t:t + 1], u[t:t + 1], bgd, bud, wdd, S)
+                mha, sha = _near_boundary(ha)
+                bound[t] += np.abs(ya[0] - y[t]) + (((mha < DELTA) * sha) @ absw.T)[0]
     return y, bound, z_tokens
 
 
@@ -210,6 +251,35 @@ def test_ffn_bound_rejects_plausible_kernel_mistakes(E, F, S, r, T):
     assert np.any(np.abs(bad - y) > bound)
 
 
+def test_ffn_bound_covers_a_boundary_latent_and_no_other():
+    """A latent within DELTA of a rounding boundary may take its other code:
+    the bound admits y with that code, and rejects the same one-step change
+    of a latent of that token far from any boundary (CPU)."""
+    E, F, S, r, T = 64, 5776, 544, 896, 40
+    _, w, x = _case(E, F, S, r, T, seed=1007)
+    xf = x.float().numpy()
+    y, bound, z_tokens = ffn_bound(xf, w)
+    assert z_tokens, "this seed has a latent on a rounding boundary"
+    t = z_tokens[0]
+    wg, wu, ag, au, bg, bu, wd = w
+    _, z, g, u, _ = oracle.ffn_trace(xf, *w)
+    mz, sz = _near_boundary(z)
+    bgd, bud, wdd = _dequantised_rows(bg), _dequantised_rows(bu), _dequantised_rows(wd)
+    zdq = _dequantised_acts(z)
+
+    def y_with_step(k, sign):
+        alt = zdq[t:t + 1].copy()
+        alt[0, k] += sign * float(sz[t, k])
+        return _tail(alt, g[t:t + 1], u[t:t + 1], bgd, bud, wdd, S)[0][0]
+
+    k = int(np.flatnonzero(mz[t] < DELTA)[0])
+    v = float(z[t, k]) / float(sz[t, k])
+    assert np.all(np.abs(y_with_step(k, 1.0 if v > np.rint(v) else -1.0) - y[t]) <= bound[t])
+    far = int(np.argmax(mz[t]))   # the latent of token t furthest from a rounding boundary
+    assert mz[t, far] > 0.4
+    assert np.any(np.abs(y_with_step(far, 1.0) - y[t]) > bound[t])
+
+
 # ---------------------------------------------------------------------------
 # GPU
 # ---------------------------------------------------------------------------
@@ -301,3 +371,27 @@ def test_ffn_decode_in_several_passes():
     rows = [0, 1, 777, 2030, 2031, 2032, 2033, 2099]
     y, ref, bound, z_tokens, _, _ = _run_gpu(E, F, S, r, T, seed=99, tokens=rows)
     _check(y, ref, bound, z_tokens, "two passes")
+
+
+def _random_ffn_shape(seed):
+    """E a multiple of 64 (64..4096), hidden a multiple of 16 (16..9000), a
+    low-rank share from none to all (multiple of 16) at rank 64..1024 (a
+    multiple of 64), 1..40 tokens."""
+    rng = np.random.default_rng(0x5EEDF100 + seed)
+    E = 64 * int(rng.integers(1, 65))
+    F = 16 * int(rng.integers(1, 563))
+    S = 16 * int(rng.integers(0, F // 16 + 1)) if rng.random() < 0.8 else 0
+    r = 64 * int(rng.integers(1, 17)) if S > 0 else 0
+    T = int(rng.choice([1, 2, 15, 16, 17, 31, 33, 40]))
+    return E, F, S, r, T
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("seed", range(16))
+def test_ffn_decode_random_shapes(seed):
+    """Seeded random shapes (sizes, low-rank share, rank, token count) against
+    the oracle within ffn_bound."""
+    E, F, S, r, T = _random_ffn_shape(seed)
+    print(f"ffn random {seed}: E={E} F={F} S={S} r={r} T={T}", flush=True)
+    y, ref, bound, z_tokens, _, _ = _run_gpu(E, F, S, r, T, seed=1000 + seed)
+    _check(y, ref, bound, z_tokens, f"random {seed}: E={E} F={F} S={S} r={r} T={T}")
