@@ -482,3 +482,46 @@ def test_decode_over_generated_latents_matches_oracle_chain(one_step):
                                     bk[offk[h]:offk[h] + rk[h]].double().cpu().numpy(),
                                     bv[offv[h]:offv[h] + rv[h]].double().cpu().numpy(), scale)
                 assert within(got[b, h], ref, TOL_BF16), (st, b, h)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_project_random_shapes(seed):
+    """Seeded random shapes: E a multiple of 32 (32..8192), 1..130 tokens, 1-8
+    heads of random K and V ranks, a random part count.  Small-integer inputs
+    give the oracle's latents exactly, unsplit and as parts added in order;
+    Gaussian bf16 inputs stay within the rounding bounds."""
+    from latent_kv_attention_lr_amd import lr_attn_project_latent_parts
+    rng = np.random.default_rng(0x5EED2000 + seed)
+    E = 32 * int(rng.integers(1, 257))
+    T = int(rng.choice([1, 2, 15, 16, 17, 33, 48, 64, 65, 100, 130]))
+    H = int(rng.integers(1, 9))
+    ranks_k = [int(8 * rng.integers(1, 17)) for _ in range(H)]
+    ranks_v = [int(8 * rng.integers(1, 17)) for _ in range(H)]
+    parts = min(int(rng.integers(1, 9)), E // 32)
+    say(f"project random {seed}: E={E} T={T} ranks_k={ranks_k} ranks_v={ranks_v} parts={parts}")
+    s = _session(ranks_k, ranks_v)
+    x = torch.from_numpy(rng.integers(-3, 4, (T, E)).astype(np.float32))
+    ak = torch.from_numpy(rng.integers(-3, 4, (E, sum(ranks_k))).astype(np.float32))
+    av = torch.from_numpy(rng.integers(-3, 4, (E, sum(ranks_v))).astype(np.float32))
+    ck, cv = _gpu_project(s, x.to(torch.bfloat16), ak, av)
+    ref_k = oracle.latents(x.double().numpy(), ak.double().numpy()).astype(np.float32)
+    ref_v = oracle.latents(x.double().numpy(), av.double().numpy()).astype(np.float32)
+    assert np.array_equal(ck, ref_k) and np.array_equal(cv, ref_v)
+    xd = x.to(torch.bfloat16).to(DEV).contiguous()
+    pk = torch.empty(parts, T, sum(ranks_k), dtype=torch.float32, device=DEV)
+    pv = torch.empty(parts, T, sum(ranks_v), dtype=torch.float32, device=DEV)
+    lr_attn_project_latent_parts(s.plan, 0, xd, T, E, s.proj[0][1], parts, pk, pv)
+    torch.cuda.synchronize()
+    sk, sv = pk[0].clone(), pv[0].clone()
+    for q in range(1, parts):
+        sk += pk[q]
+        sv += pv[q]
+    assert np.array_equal(sk.cpu().numpy(), ref_k) and np.array_equal(sv.cpu().numpy(), ref_v)
+    # Gaussian activations and factors (bf16 values)
+    key = lrgen.stream_key(0x5EED2000 + seed, 1)
+    xb = lrgen.normal(key, 0, T * E, 1.0).view(T, E).to(torch.bfloat16).float()
+    ak = _factors(E, ranks_k, lrgen.stream_key(0x5EED2000 + seed, 2), 1.0 / math.sqrt(E))
+    av = _factors(E, ranks_v, lrgen.stream_key(0x5EED2000 + seed, 3), 1.0 / math.sqrt(E))
+    ck, cv = _gpu_project(s, xb.to(torch.bfloat16), ak, av)
+    _check_bound(ck, xb, ak)
+    _check_bound(cv, xb, av)
