@@ -395,3 +395,44 @@ def test_ffn_decode_random_shapes(seed):
     print(f"ffn random {seed}: E={E} F={F} S={S} r={r} T={T}", flush=True)
     y, ref, bound, z_tokens, _, _ = _run_gpu(E, F, S, r, T, seed=1000 + seed)
     _check(y, ref, bound, z_tokens, f"random {seed}: E={E} F={F} S={S} r={r} T={T}")
+
+
+@pytest.mark.gpu
+def test_ffn_graph_replay_matches_eager():
+    """Two FFN calls sharing one workspace, captured in one HIP graph: every
+    replay equals the eager calls bit for bit, with eager work and a changed
+    input between replays (the step's counters are cleared by a kernel of the
+    step itself, so nothing in the graph depends on state left by a replay)."""
+    import torch
+    from latent_kv_attention_lr_amd.ffn import FfnLayer
+    E, F, S, r, T = 512, 8208, 4096, 256, 33       # every launch, three token blocks, three chunks
+    f, w, x = _case(E, F, S, r, T, seed=404)
+    layer = FfnLayer(E, F, S, r, device="cuda:0")
+    layer.set_weights(*w)
+    x1 = x.to("cuda:0").contiguous()
+    x2 = (x.float() * 0.5).to(torch.bfloat16).to("cuda:0").contiguous()
+    y1 = torch.empty(T, E, dtype=torch.float32, device="cuda:0")
+    y2 = torch.empty_like(y1)
+    ref2 = layer(x2).clone()                          # also sizes the workspace before capture
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            layer(x1, y1)
+            layer(x2, y2)
+    torch.cuda.current_stream().wait_stream(cap)
+    for rep in range(3):
+        xr = lrgen.ffn_activations(lrgen.FfnWorkload("t", E, F, S, r, T, 500 + rep), T)
+        x1.copy_(xr.to("cuda:0"))
+        ref1 = layer(x1).clone()                      # eager work between replays
+        y1.fill_(float("nan"))
+        y2.fill_(float("nan"))
+        torch.cuda.synchronize()
+        print(f"ffn graph replay {rep}", flush=True)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y1, ref1), rep
+        assert torch.equal(y2, ref2), rep
+    y, bound, z_tokens = ffn_bound(x1.float().cpu().numpy(), w)   # and the last replay is right
+    _check(y1.cpu().numpy(), y, bound, z_tokens, "graph replay")
