@@ -525,3 +525,65 @@ def test_project_random_shapes(seed):
     ck, cv = _gpu_project(s, xb.to(torch.bfloat16), ak, av)
     _check_bound(ck, xb, ak)
     _check_bound(cv, xb, av)
+
+
+def test_project_append_decode_graph_replay_matches_eager():
+    """Three steps from activations (generate, append, attend: two launches
+    each) captured in one HIP graph: each replay writes the same cache bytes
+    and outputs as the eager steps, with eager work and changed activations
+    between replays."""
+    rng = np.random.default_rng(61)
+    ranks_k, ranks_v, E, B, ctx, steps = [8, 64, 32, 96], [40, 16, 128, 8], 2080, 5, 120, 3
+    H = len(ranks_k)
+    s = _session(ranks_k, ranks_v, batch=B, cap=ctx + steps)
+    ak = _factors(E, ranks_k, lrgen.stream_key(61, 1), 1.0 / math.sqrt(E))
+    av = _factors(E, ranks_v, lrgen.stream_key(61, 2), 1.0 / math.sqrt(E))
+    _set_factors(s, ak, av)
+    bk = torch.from_numpy(rng.standard_normal((sum(ranks_k), 128)) / 6).to(torch.bfloat16).to(DEV)
+    bv = torch.from_numpy(rng.standard_normal((sum(ranks_v), 128)) / 6).to(torch.bfloat16).to(DEV)
+    s.set_factors(0, bk, bv)
+    pk = torch.from_numpy(rng.standard_normal((B, ctx, sum(ranks_k))).astype(np.float32)).to(DEV)
+    pv = torch.from_numpy(rng.standard_normal((B, ctx, sum(ranks_v))).astype(np.float32)).to(DEV)
+    s.append(0, pk, pv, torch.zeros(B, dtype=torch.int32, device=DEV))
+    prefix = s.caches[0].clone()
+    xs = [torch.empty(B, E, dtype=torch.bfloat16, device=DEV) for _ in range(steps)]
+    qs = [torch.from_numpy(rng.standard_normal((B, H, 128))).to(torch.bfloat16).to(DEV) for _ in range(steps)]
+    pos = [torch.full((B,), ctx + i, dtype=torch.int32, device=DEV) for i in range(steps)]
+    lens = [torch.full((B,), ctx + i + 1, dtype=torch.int32, device=DEV) for i in range(steps)]
+    outs = [torch.empty(B, H, 128, dtype=torch.bfloat16, device=DEV) for _ in range(steps)]
+
+    def steps_fn():
+        for i in range(steps):
+            s.project_append_decode(0, xs[i], pos[i], qs[i], outs[i], ctx + steps, lengths=lens[i])
+
+    def draw(seed):
+        for i, x in enumerate(xs):
+            x.copy_(torch.from_numpy(np.random.default_rng(seed + i).standard_normal((B, E))).to(torch.bfloat16))
+
+    draw(1000)
+    steps_fn()                                   # sizes the step workspace before capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            steps_fn()
+    torch.cuda.current_stream().wait_stream(cap)
+    for rep in range(3):
+        draw(2000 + 10 * rep)
+        s.caches[0].copy_(prefix)
+        steps_fn()                               # eager reference
+        torch.cuda.synchronize()
+        ref_out = [o.clone() for o in outs]
+        ref_cache = s.caches[0].clone()
+        s.caches[0].copy_(prefix)
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        say(f"project_append_decode graph replay {rep}")
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(s.caches[0], ref_cache), rep
+        for i in range(steps):
+            assert torch.equal(outs[i].view(torch.int16), ref_out[i].view(torch.int16)), (rep, i)
