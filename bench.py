@@ -19,6 +19,8 @@ copy back to back are reported beside it as the warm figures.
   cpu_baseline the CPU oracle (plain fp64) timed on this host's threads on
                step 0 of whole batch rows (all of them when they fit about
                20 thread-seconds), scaled to the whole step
+  parity       the GPU's step 0 against those oracle outputs, per (layer,
+               b, h), with the decode tolerance of the parity tests
 """
 from __future__ import annotations
 
@@ -206,7 +208,7 @@ def cpu_baseline(run, rows):
     oracle.attend(w.qfmt, *jobs[0], run.scale)
     with ThreadPoolExecutor(threads) as pool:
         t0 = time.perf_counter()
-        list(pool.map(lambda j: oracle.attend(w.qfmt, *j, run.scale), jobs))
+        refs = list(pool.map(lambda j: oracle.attend(w.qfmt, *j, run.scale), jobs))
         wall = time.perf_counter() - t0
     step_s = wall * w.batch / rows
     whole = rows == w.batch
@@ -221,7 +223,27 @@ def cpu_baseline(run, rows):
             "cpu_model": cpu_model(),
             "host_cpus_visible": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
             else os.cpu_count(),
-            "step_s": step_s}
+            "step_s": step_s, "refs": dict(zip(units, refs))}
+
+
+# Decode output tolerance with bf16 q, factors and output (the parity tests'):
+# |o_gpu - o_ref| <= 1e-2 max|o_ref| + 1e-3, per (layer, b, h).
+TOL_BF16 = (1e-2, 1e-3)
+
+
+def parity_report(refs, got):
+    """Step 0 of the GPU against the oracle outputs the CPU baseline computed
+    (refs: unit -> fp64 [d]; got: layer -> fp64 [B, H, d])."""
+    import numpy as np
+    worst, max_abs, fails = 0.0, 0.0, 0
+    for (l, b, h), ref in refs.items():
+        err = float(np.max(np.abs(got[l][b, h] - ref)))
+        bound = TOL_BF16[0] * float(np.max(np.abs(ref))) + TOL_BF16[1]
+        worst, max_abs = max(worst, err / bound), max(max_abs, err)
+        fails += err > bound
+    return {"units": len(refs), "step": 0, "tolerance": "|o - o_ref| <= 1e-2 max|o_ref| + 1e-3 per (layer, b, h)",
+            "worst_err_over_bound": worst, "max_abs_err": max_abs, "units_over_bound": fails,
+            "source": "the oracle outputs of the cpu_baseline leg"}
 
 
 def ffn_bench(args):
@@ -336,17 +358,28 @@ def ffn_bench(args):
         import oracle
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         xh = [xx.float().cpu().numpy() for xx in xs]
-        n, cpu_wall = 0, 0.0
+        layer(xs[0], y)                   # the GPU's step for the first input, compared below
+        torch.cuda.synchronize()
+        y0 = y.double().cpu().numpy()
+        n, cpu_wall, y_ref = 0, 0.0, None
         while n == 0 or cpu_wall < 10.0:
             t0 = time.perf_counter()
-            oracle.ffn(xh[n % len(xh)], *w)
+            yo = oracle.ffn(xh[n % len(xh)], *w)
             cpu_wall += time.perf_counter() - t0
+            if n == 0:
+                y_ref = yo
             n += 1
         result["cpu_baseline"] = {
             "value": T * n / cpu_wall, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{n} whole steps of {T} tokens (lro_ffn: W8A8 quantisation of weights and "
                       f"activations, then fp64), {cpu_wall:.2f} s on one thread",
             "cpu_model": cpu_model()}
+        rel = abs(y0 - y_ref).max(axis=1) / abs(y_ref).max(axis=1)
+        result["parity"] = {
+            "tokens": T, "max_rel_err_per_token": float(rel.max()),
+            "note": "one step of the GPU against the oracle output of the cpu_baseline leg, "
+                    "|y - y_ref| / max|y_ref| per token; the parity tests bound each element "
+                    "from the oracle's intermediates (fp32 sums, activation codes near a rounding boundary)"}
     print(json.dumps(result), flush=True)
 
 
@@ -760,10 +793,19 @@ def main():
     if alloc_info:
         result["rank_allocation"] = alloc_info
     if keep:
+        # step 0 once more on cache copy 0 (its token rewritten with the same
+        # codes, the later steps' tokens beyond the length): the outputs the
+        # oracle is compared with, per layer of the sampled units
+        got = {}
+        for l in sorted({u[0] for u in keep}):
+            launch(l, 0, 0, cur(), project_first=False)
+            got[l] = out.double().cpu().numpy()
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cb = cpu_baseline(run, cpu_rows)
         cb.pop("step_s")
+        refs = cb.pop("refs")
         result["cpu_baseline"] = cb
+        result["parity"] = parity_report(refs, got)
     print(json.dumps(result), flush=True)
 
 
