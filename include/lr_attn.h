@@ -469,6 +469,21 @@ lr_status lr_ffn_decode(const lr_ffn_desc* desc, const void* weights, const void
  * misaligned src or sink), LR_EHIP (launch failed). */
 lr_status lr_attn_probe_read(const void* src, size_t bytes, void* sink, void* stream);
 
+/* Debugging aid, not part of the decode path: the checked build of this
+ * library (liblr_attn_check.so, built with LR_ATTN_CHECK=1) tests every cache
+ * access of its kernels (appends, decodes, the explicit form) against the
+ * extent of the cache buffer the plan describes; an access outside it is
+ * counted and redirected to the buffer's first bytes, so the launch completes
+ * instead of faulting.  lr_attn_check_count stores the count of the current
+ * device and resets it to 0; it synchronises with the device (two copies of
+ * one counter), unlike every other call.  lr_attn_check_shrink sets how many
+ * bytes later launches take off each cache's extent (0 by default), which
+ * makes accesses near the end count as outside -- the hook a test uses to show
+ * that the check fires.  In the release library both return LR_EUNSUPPORTED.
+ * Errors: LR_EINVAL (count NULL), LR_EHIP (the copy failed). */
+lr_status lr_attn_check_count(uint64_t* count);
+lr_status lr_attn_check_shrink(uint64_t bytes);
+
 /* Static description of a status. */
 const char* lr_attn_strerror(lr_status status);
 /* hipError_t of the last call on this thread that returned LR_EHIP (0 if none). */

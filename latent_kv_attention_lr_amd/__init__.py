@@ -116,6 +116,8 @@ def _load() -> ctypes.CDLL:
         "lr_ffn_prepare_weights": (ctypes.c_int, [ctypes.POINTER(lr_ffn_desc)] + [P] * 8),
         "lr_ffn_decode": (ctypes.c_int, [ctypes.POINTER(lr_ffn_desc), P, P, I32, P, P, SZ, P]),
         "lr_attn_probe_read": (ctypes.c_int, [P, SZ, P, P]),
+        "lr_attn_check_count": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint64)]),
+        "lr_attn_check_shrink": (ctypes.c_int, [ctypes.c_uint64]),
         "lr_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "lr_attn_last_hip_error": (I32, []),
     }
@@ -360,6 +362,21 @@ def lr_ffn_decode(desc: lr_ffn_desc, weights, x, n_tokens: int, y, workspace, ws
                   stream=None) -> None:
     _check(_lib.lr_ffn_decode(ctypes.byref(desc), _ptr(weights), _ptr(x), n_tokens, _ptr(y),
                               _ptr(workspace), ws_bytes, _stream(stream)), "lr_ffn_decode")
+
+
+def lr_attn_check_count() -> int:
+    """Checked build only: cache accesses found outside their buffer since
+    the last call on this device (then reset to 0).  Raises LrAttnError
+    (LR_EUNSUPPORTED) in the release library."""
+    n = ctypes.c_uint64(0)
+    _check(_lib.lr_attn_check_count(ctypes.byref(n)), "lr_attn_check_count")
+    return int(n.value)
+
+
+def lr_attn_check_shrink(nbytes: int) -> None:
+    """Checked build only: later launches test cache accesses against each
+    cache's bytes less ``nbytes`` (0 restores the full extent)."""
+    _check(_lib.lr_attn_check_shrink(nbytes), "lr_attn_check_shrink")
 
 
 def lr_attn_probe_read(src, nbytes: int, sink, stream=None) -> None:

@@ -3,7 +3,9 @@
 ``plan.cpp``, ``rotate.cpp``, ``alloc.cpp`` and ``ffn_host.cpp`` (host-only
 C++) are compiled with g++; ``ffn.hip`` joins the hipcc sources; ``kernels.hip``,
 ``project.hip`` and ``probe.hip`` with hipcc for gfx950; hipcc links them into
-one shared library next to this file.
+one shared library next to this file.  ``liblr_attn_check.so`` beside it is
+the same library with ``kernels.hip`` built with ``LR_ATTN_CHECK=1`` (cache
+accesses bounds-checked, a debugging aid).
 """
 from __future__ import annotations
 
@@ -30,6 +32,8 @@ CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall"]
 # device code is the same.
 SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=all"]
 SAN_LIB = os.path.join(HERE, "liblr_attn_san.so")
+# The checked build (kernels with LR_ATTN_CHECK=1): a debugging aid.
+CHECK_LIB = os.path.join(HERE, "liblr_attn_check.so")
 HOST_SOURCES = ["plan.cpp", "rotate.cpp", "alloc.cpp", "ffn_host.cpp"]
 HIP_SOURCES = ["ffn.hip", "kernels.hip", "project.hip", "probe.hip"]
 
@@ -93,11 +97,24 @@ def build(verbose: bool = False) -> str:
     outs.append(_run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp, plan_o, rot_o, alloc_o, ffnh_o, ffn_o, kern_o,
                       proj_o, probe_o]))
     os.replace(tmp, LIB)
+    outs.append(_build_checked([plan_o, rot_o, alloc_o, ffnh_o, ffn_o, proj_o, probe_o]))
     if verbose:
         for o in outs:
             if o.strip():
                 print(o)
     return LIB
+
+
+def _build_checked(other_objs) -> str:
+    """CHECK_LIB: kernels.hip rebuilt with LR_ATTN_CHECK=1 (every cache access
+    of its kernels tested against the cache buffer, lr_attn_check_count),
+    linked with the other objects of the release build."""
+    kern_o = os.path.join(BUILD, "kernels_check.o")
+    out = _run([HIPCC, *HIP_FLAGS, "-DLR_ATTN_CHECK=1", "-c", os.path.join(CSRC, "kernels.hip"), "-o", kern_o])
+    tmp = CHECK_LIB + ".tmp"
+    out += _run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp, *other_objs, kern_o])
+    os.replace(tmp, CHECK_LIB)
+    return out
 
 
 def build_sanitized() -> str:

@@ -29,6 +29,39 @@ constexpr float kTau = 8.0f;          // lazy rescale threshold (log2 units)
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
+// The checked build (LR_ATTN_CHECK = 1, liblr_attn_check.so): every access to
+// a cache tile is tested against the extent of the cache buffer; one outside
+// it is counted in g_check_count and redirected to the buffer's first bytes,
+// so the launch completes and the host reads the count
+// (lr_attn_check_count) instead of a fault.  The release build compiles the
+// test away.
+// ---------------------------------------------------------------------------
+#ifndef LR_ATTN_CHECK
+#define LR_ATTN_CHECK 0
+#endif
+struct Bounds {
+  const uint8_t* lo;   // the cache buffer
+  uint64_t n;          // its bytes
+};
+#if LR_ATTN_CHECK
+__device__ unsigned long long g_check_count;
+#endif
+template <typename P>
+__device__ __forceinline__ P checked(const Bounds& bd, P p, int bytes) {
+#if LR_ATTN_CHECK
+  const uint8_t* q = reinterpret_cast<const uint8_t*>(p);
+  if (q < bd.lo || q + bytes > bd.lo + bd.n) {
+    atomicAdd(&g_check_count, 1ull);
+    return reinterpret_cast<P>(const_cast<uint8_t*>(bd.lo));
+  }
+#else
+  (void)bd;
+  (void)bytes;
+#endif
+  return p;
+}
+
+// ---------------------------------------------------------------------------
 // element I/O
 // ---------------------------------------------------------------------------
 
@@ -170,6 +203,7 @@ __device__ __forceinline__ float uniform(float v) {
 
 struct AppendArgs {
   uint8_t* cache;
+  uint64_t cache_bytes;
   const float* ck;
   const float* cv;
   const int32_t* pos;
@@ -235,17 +269,17 @@ __device__ __forceinline__ SegCodes quantise_seg(const float* v) {
 // Store one lane's quantised segment (seg = lane within its 16-lane row) at
 // token slot t of its tile; rb = the row's code bytes.
 template <int QF>
-__device__ __forceinline__ void store_seg(uint8_t* tile, int rb, int t, int seg, const SegCodes& c) {
+__device__ __forceinline__ void store_seg(const Bounds& bd, uint8_t* tile, int rb, int t, int seg, const SegCodes& c) {
   if constexpr (QF == LR_Q_INT8_TOKEN) {
     const int ch = seg >> 1;                      // 16-byte chunk of this lane's 8 bytes
     const int wc = min(16, rb - 16 * ch);         // chunk width: 16, or 8 for the tail
-    *reinterpret_cast<uint2*>(tile + 1024 * ch + wc * t + 8 * (seg & 1)) = make_uint2(c.w[0], c.w[1]);
-    if (seg == 0) *reinterpret_cast<float*>(tile + 64 * rb + 4 * t) = c.s;
+    *checked(bd, reinterpret_cast<uint2*>(tile + 1024 * ch + wc * t + 8 * (seg & 1)), 8) = make_uint2(c.w[0], c.w[1]);
+    if (seg == 0) *checked(bd, reinterpret_cast<float*>(tile + 64 * rb + 4 * t), 4) = c.s;
   } else {
     const int g = seg >> 2;                       // group of 32 ranks == 16-byte chunk
     const int wc = min(16, rb - 16 * g);          // 16, or 4, 8, 12 for the tail group
-    *reinterpret_cast<uint32_t*>(tile + 1024 * g + wc * t + 4 * (seg & 3)) = c.w[0];
-    if ((seg & 3) == 0) *reinterpret_cast<uint16_t*>(tile + 64 * rb + 2 * (64 * g + t)) = c.sh;
+    *checked(bd, reinterpret_cast<uint32_t*>(tile + 1024 * g + wc * t + 4 * (seg & 3)), 4) = c.w[0];
+    if ((seg & 3) == 0) *checked(bd, reinterpret_cast<uint16_t*>(tile + 64 * rb + 2 * (64 * g + t)), 2) = c.sh;
   }
 }
 
@@ -282,7 +316,7 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a, HeadTab ht) {
   if (!active) return;
   uint8_t* tile = a.cache + uint64_t(kv ? ht.vreg[h] : ht.kreg[h]) * kRegionAlign +
                   (uint64_t(b) * a.n_tiles + (slot >> 6)) * tile_bytes(QF, r);
-  store_seg<QF>(tile, row_bytes(QF, r), slot & 63, seg, c);
+  store_seg<QF>(Bounds{a.cache, a.cache_bytes}, tile, row_bytes(QF, r), slot & 63, seg, c);
 }
 
 // ---------------------------------------------------------------------------
@@ -291,6 +325,7 @@ __global__ __launch_bounds__(256) void k_append(AppendArgs a, HeadTab ht) {
 
 struct DecodeArgs {
   const uint8_t* cache;
+  uint64_t cache_bytes;   // the cache buffer's bytes (cache and wcache are the same buffer)
   const int32_t* len;
   const void* q;
   const void* bk;
@@ -358,13 +393,14 @@ __device__ __forceinline__ T ld_stream(const uint8_t* p) {
 }
 
 template <int NC>
-__device__ __forceinline__ void load_codes(const uint8_t* tile, int tok, int lm, int hf, int rb, uint32_t* w) {
+__device__ __forceinline__ void load_codes(const Bounds& bd, const uint8_t* tile, int tok, int lm, int hf, int rb,
+                                           uint32_t* w) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int cg = lm * c + hf;
     const int wc = rb - 16 * cg;
     const int off = wc > 0 ? 1024 * cg + min(wc, 16) * tok : 0;
-    const u32x4_t v = ld_stream16(tile + off);
+    const u32x4_t v = ld_stream16(checked(bd, tile + off, 16));
     w[4 * c] = v.x; w[4 * c + 1] = v.y; w[4 * c + 2] = v.z; w[4 * c + 3] = v.w;
   }
 }
@@ -401,26 +437,30 @@ struct TileRegs {
 // Groups past the row (int4) re-read the last group's scale: it only
 // multiplies partial sums over zero q' entries or unread accumulators.
 template <int QF, int NC, int NG>
-__device__ __forceinline__ void load_k(const uint8_t* kt, int tok, int lm, int hf, int rk, int rbk, TileRegs<NC, NG>& x) {
-  load_codes<NC>(kt, tok, lm, hf, rbk, x.kw);
+__device__ __forceinline__ void load_k(const Bounds& bd, const uint8_t* kt, int tok, int lm, int hf, int rk, int rbk,
+                                       TileRegs<NC, NG>& x) {
+  load_codes<NC>(bd, kt, tok, lm, hf, rbk, x.kw);
   if constexpr (QF == LR_Q_INT8_TOKEN) {
-    x.sk[0] = ld_stream<float>(kt + 64 * rbk + 4 * tok);
+    x.sk[0] = ld_stream<float>(checked(bd, kt + 64 * rbk + 4 * tok, 4));
   } else {
 #pragma unroll
     for (int g = 0; g < NG; ++g)
-      x.sk[g] = half_bits_to_f32(ld_stream<uint16_t>(kt + 64 * rbk + 2 * (64 * min(g, (rk - 1) >> 5) + tok)));
+      x.sk[g] = half_bits_to_f32(
+          ld_stream<uint16_t>(checked(bd, kt + 64 * rbk + 2 * (64 * min(g, (rk - 1) >> 5) + tok), 2)));
   }
 }
 
 template <int QF, int NC, int NG>
-__device__ __forceinline__ void load_v(const uint8_t* vt, int tok, int lm, int hf, int rv, int rbv, TileRegs<NC, NG>& x) {
-  load_codes<NC>(vt, tok, lm, hf, rbv, x.vw);
+__device__ __forceinline__ void load_v(const Bounds& bd, const uint8_t* vt, int tok, int lm, int hf, int rv, int rbv,
+                                       TileRegs<NC, NG>& x) {
+  load_codes<NC>(bd, vt, tok, lm, hf, rbv, x.vw);
   if constexpr (QF == LR_Q_INT8_TOKEN) {
-    x.sv[0] = ld_stream<float>(vt + 64 * rbv + 4 * tok);
+    x.sv[0] = ld_stream<float>(checked(bd, vt + 64 * rbv + 4 * tok, 4));
   } else {
 #pragma unroll
     for (int g = 0; g < NG; ++g)
-      x.sv[g] = half_bits_to_f32(ld_stream<uint16_t>(vt + 64 * rbv + 2 * (64 * min(g, (rv - 1) >> 5) + tok)));
+      x.sv[g] = half_bits_to_f32(
+          ld_stream<uint16_t>(checked(bd, vt + 64 * rbv + 2 * (64 * min(g, (rv - 1) >> 5) + tok), 2)));
   }
 }
 
@@ -577,6 +617,7 @@ void k_decode(DecodeArgs a, HeadTab ht) {
     b0[k] = E::ld(bkh, i * kHeadDim + 2 * lane);
     b1[k] = E::ld(bkh, i * kHeadDim + 2 * lane + 1);
   }
+  const Bounds bd{a.cache, a.cache_bytes};
   const uint8_t* kplane = a.cache + uint64_t(kreg) * kRegionAlign + uint64_t(b) * a.n_tiles * tbk;
   const uint8_t* vplane = a.cache + uint64_t(vreg) * kRegionAlign + uint64_t(b) * a.n_tiles * tbv;
   // wavefront steps of 64 / lm tokens (step s: tile s / lm); a wavefront
@@ -588,8 +629,8 @@ void k_decode(DecodeArgs a, HeadTab ht) {
   int t = s0 + wid;
   {
     const int sl = min(t, max(s1 - 1, 0));
-    load_k<QF>(kplane + step_tile(sl) * tbk, step_tok(sl), lm, hf, rk, rbk, cur);
-    load_v<QF>(vplane + step_tile(sl) * tbv, step_tok(sl), lm, hf, rv, rbv, cur);
+    load_k<QF>(bd, kplane + step_tile(sl) * tbk, step_tok(sl), lm, hf, rk, rbk, cur);
+    load_v<QF>(bd, vplane + step_tile(sl) * tbv, step_tok(sl), lm, hf, rv, rbv, cur);
   }
   const IOT* bvh = reinterpret_cast<const IOT*>(a.bv) + size_t(loff_v) * kHeadDim;
   float bv0[RPW], bv1[RPW];
@@ -718,7 +759,7 @@ void k_decode(DecodeArgs a, HeadTab ht) {
       }
       uint8_t* tile = a.wcache + uint64_t(nkv ? vreg : kreg) * kRegionAlign +
                       (uint64_t(b) * a.n_tiles + tnew) * (nkv ? tbv : tbk);
-      store_seg<QF>(tile, nkv ? rbv : rbk, lnew, nseg, c);
+      store_seg<QF>(Bounds{a.wcache, a.cache_bytes}, tile, nkv ? rbv : rbk, lnew, nseg, c);
     }
   };
 
@@ -824,7 +865,7 @@ void k_decode(DecodeArgs a, HeadTab ht) {
     }
     if constexpr (INT8) s *= cur.sk[0];
     const int tn = t + NW;   // K regs are free now: the next step's K codes
-    if constexpr (PF) load_k<QF>(kplane + step_tile(tn) * tbk, step_tok(tn), lm, hf, rk, rbk, cur);
+    if constexpr (PF) load_k<QF>(bd, kplane + step_tile(tn) * tbk, step_tok(tn), lm, hf, rk, rbk, cur);
     s = valid ? s : -__builtin_inff();
     if (s > m + kTau) {  // rare after the first tile: rescale the running sums
       const float al = __builtin_amdgcn_exp2f(m - s);
@@ -866,7 +907,7 @@ void k_decode(DecodeArgs a, HeadTab ht) {
         }
       }
     }
-    if constexpr (PF) load_v<QF>(vplane + step_tile(tn) * tbv, step_tok(tn), lm, hf, rv, rbv, cur);
+    if constexpr (PF) load_v<QF>(bd, vplane + step_tile(tn) * tbv, step_tok(tn), lm, hf, rv, rbv, cur);
   };
   for (; t + NW < s1; t += NW) tile_step(t, std::true_type{});
   if (t < s1) tile_step(t, std::false_type{});
@@ -1063,16 +1104,17 @@ __device__ __forceinline__ bf16x8_t codes_to_bf16(const uint32_t* w, int k0) {
 // Codes of ranks [16 kb + 8 hl, +8) of token ti of a tile (kb: 16-rank block,
 // hl: which half of the block this lane holds), zero beyond the row width.
 template <int QF>
-__device__ __forceinline__ void load_codes8(const uint8_t* tile, int rb, int kb, int hl, int ti, uint32_t* w) {
+__device__ __forceinline__ void load_codes8(const Bounds& bd, const uint8_t* tile, int rb, int kb, int hl, int ti,
+                                            uint32_t* w) {
   if constexpr (QF == LR_Q_INT8_TOKEN) {
     const int c = kb, wc = min(16, rb - 16 * c), off = 8 * hl;   // 8 bytes
     if (off + 8 <= wc) {
-      const uint2 v = *reinterpret_cast<const uint2*>(tile + 1024 * c + wc * ti + off);
+      const uint2 v = *checked(bd, reinterpret_cast<const uint2*>(tile + 1024 * c + wc * ti + off), 8);
       w[0] = v.x; w[1] = v.y;
     } else { w[0] = 0; w[1] = 0; }
   } else {
     const int c = kb >> 1, wc = min(16, rb - 16 * c), off = 8 * (kb & 1) + 4 * hl;   // 4 bytes
-    w[0] = off + 4 <= wc ? *reinterpret_cast<const uint32_t*>(tile + 1024 * c + wc * ti + off) : 0u;
+    w[0] = off + 4 <= wc ? *checked(bd, reinterpret_cast<const uint32_t*>(tile + 1024 * c + wc * ti + off), 4) : 0u;
     w[1] = 0;
   }
 }
@@ -1127,6 +1169,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_explicit(DecodeArgs a, HeadT
   }
   __syncthreads();
 
+  const Bounds bd{a.cache, a.cache_bytes};
   const uint8_t* kplane = a.cache + uint64_t(kreg) * kRegionAlign + uint64_t(b) * a.n_tiles * tbk;
   const uint8_t* vplane = a.cache + uint64_t(vreg) * kRegionAlign + uint64_t(b) * a.n_tiles * tbv;
   const int hl = lane >> 5, col = lane & 31;
@@ -1147,18 +1190,18 @@ __global__ __launch_bounds__(NW * 64) void k_decode_explicit(DecodeArgs a, HeadT
       uint32_t kw[KB][2], vw[KB][2];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        load_codes8<QF>(kt, rbk, kb, hl, ti, kw[kb]);
-        load_codes8<QF>(vt, rbv, kb, hl, ti, vw[kb]);
+        load_codes8<QF>(bd, kt, rbk, kb, hl, ti, kw[kb]);
+        load_codes8<QF>(bd, vt, rbv, kb, hl, ti, vw[kb]);
       }
       float sk[NG], sv[NG];
       if constexpr (INT8) {
-        sk[0] = *reinterpret_cast<const float*>(kt + 64 * rbk + 4 * ti);
-        sv[0] = *reinterpret_cast<const float*>(vt + 64 * rbv + 4 * ti);
+        sk[0] = *checked(bd, reinterpret_cast<const float*>(kt + 64 * rbk + 4 * ti), 4);
+        sv[0] = *checked(bd, reinterpret_cast<const float*>(vt + 64 * rbv + 4 * ti), 4);
       } else {
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-          sk[g] = 32 * g < rk ? half_bits_to_f32(*reinterpret_cast<const uint16_t*>(kt + 64 * rbk + 2 * (64 * g + ti))) : 0.0f;
-          sv[g] = 32 * g < rv ? half_bits_to_f32(*reinterpret_cast<const uint16_t*>(vt + 64 * rbv + 2 * (64 * g + ti))) : 0.0f;
+          sk[g] = 32 * g < rk ? half_bits_to_f32(*checked(bd, reinterpret_cast<const uint16_t*>(kt + 64 * rbk + 2 * (64 * g + ti)), 2)) : 0.0f;
+          sv[g] = 32 * g < rv ? half_bits_to_f32(*checked(bd, reinterpret_cast<const uint16_t*>(vt + 64 * rbv + 2 * (64 * g + ti)), 2)) : 0.0f;
         }
       }
       // ---- k_t rebuilt block by block, dotted with q
@@ -1295,6 +1338,13 @@ hipError_t launch_decode_q(int bucket, int waves, dim3 grid, hipStream_t st, con
 // hipGetSymbolAddress returns for it (scratch_address) is passed to kernels.
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
+// Checked build: the extent the kernels test cache accesses against, the
+// buffer's bytes less what lr_attn_check_shrink takes off (a test hook).
+uint64_t g_check_shrink = 0;
+uint64_t checked_cache_bytes(size_t bytes) {
+  return g_check_shrink < bytes ? uint64_t(bytes) - g_check_shrink : 0;
+}
+
 }  // namespace
 
 int scratch_address(void** out) {
@@ -1320,6 +1370,7 @@ int launch_append(const lr_attn_plan& p, int32_t layer, void* cache, const float
   const auto& L = p.layers[layer];
   AppendArgs a;
   a.cache = static_cast<uint8_t*>(cache);
+  a.cache_bytes = checked_cache_bytes(L.cache_bytes);
   a.ck = ck;
   a.cv = cv;
   a.pos = pos;
@@ -1375,6 +1426,7 @@ int launch_decode(const lr_attn_plan& p, int32_t layer, const void* cache, const
   const Split sp = explicit_form ? explicit_split(p, layer, max_len) : choose_split(p, layer, max_len);
   DecodeArgs a;
   a.cache = static_cast<const uint8_t*>(cache);
+  a.cache_bytes = checked_cache_bytes(L.cache_bytes);
   a.len = len;
   a.q = q;
   a.bk = bk;
@@ -1421,3 +1473,36 @@ int launch_decode(const lr_attn_plan& p, int32_t layer, const void* cache, const
 }
 
 }  // namespace lr
+
+extern "C" {
+
+lr_status lr_attn_check_count(uint64_t* count) {
+#if LR_ATTN_CHECK
+  if (!count) return LR_EINVAL;
+  unsigned long long v = 0;
+  const unsigned long long zero = 0;
+  hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(lr::g_check_count), sizeof v, 0, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(lr::g_check_count), &zero, sizeof zero, 0, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    lr::set_last_hip_error(int(e));
+    return LR_EHIP;
+  }
+  *count = v;
+  return LR_OK;
+#else
+  (void)count;
+  return LR_EUNSUPPORTED;
+#endif
+}
+
+lr_status lr_attn_check_shrink(uint64_t bytes) {
+#if LR_ATTN_CHECK
+  lr::g_check_shrink = bytes;
+  return LR_OK;
+#else
+  (void)bytes;
+  return LR_EUNSUPPORTED;
+#endif
+}
+
+}  // extern "C"

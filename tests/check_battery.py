@@ -1,0 +1,55 @@
+"""Child process of tests/test_checked_build.py, run with LR_ATTN_LIB naming
+the checked library (liblr_attn_check.so: every cache access of the kernels
+tested against the cache buffer).  Runs the seeded random plans of
+test_gpu_random_shapes (appends, absorbed and explicit decodes, split and
+unsplit launches, the fused append; each still checked against the oracle),
+then one decode with the tested extent shrunk by a tile's worth of bytes, and
+prints one JSON line: the accesses found outside the caches in the first
+part (must be 0) and in the second (must not be: the check fires)."""
+import json
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+sys.path.insert(0, os.path.dirname(HERE))
+
+import numpy as np   # noqa: E402
+import torch         # noqa: E402
+
+import latent_kv_attention_lr_amd as lr                     # noqa: E402
+from latent_kv_attention_lr_amd.session import DecodeSession   # noqa: E402
+import test_gpu_random_shapes as rs                         # noqa: E402
+
+
+def main():
+    assert os.path.basename(lr.LIB_PATH) == "liblr_attn_check.so", lr.LIB_PATH
+    lr.lr_attn_check_count()                     # start from 0
+    for seed in range(rs.N_CASES):
+        rs.test_random_shape_decode_matches_oracle(seed)
+    torch.cuda.synchronize()
+    outside = lr.lr_attn_check_count()
+
+    # the check fires: a cache whose last tiles lie past the tested extent
+    rng = np.random.default_rng(5)
+    B, H, cap, rk, rv = 2, 4, 300, [32, 8, 64, 16], [16, 40, 8, 32]
+    s = DecodeSession(1, B, H, cap, lr.LR_Q_INT8_TOKEN, lr.LR_DT_BF16, [rk], [rv], device="cuda:0")
+    ck = torch.from_numpy(rng.standard_normal((B, cap, sum(rk))).astype(np.float32)).cuda()
+    cv = torch.from_numpy(rng.standard_normal((B, cap, sum(rv))).astype(np.float32)).cuda()
+    s.append(0, ck, cv, torch.zeros(B, dtype=torch.int32, device="cuda:0"))
+    s.set_factors(0, torch.zeros(sum(rk), 128, dtype=torch.bfloat16, device="cuda:0"),
+                  torch.zeros(sum(rv), 128, dtype=torch.bfloat16, device="cuda:0"))
+    s.lengths.fill_(cap)
+    q = torch.zeros(B, H, 128, dtype=torch.bfloat16, device="cuda:0")
+    out = torch.empty_like(q)
+    lr.lr_attn_check_shrink(4096)
+    s.decode(0, q, out, max_len=cap)
+    torch.cuda.synchronize()
+    lr.lr_attn_check_shrink(0)
+    fired = lr.lr_attn_check_count()
+    s.close()
+    print(json.dumps({"cases": rs.N_CASES, "outside": outside, "outside_with_shrink": fired}), flush=True)
+
+
+if __name__ == "__main__":
+    main()
