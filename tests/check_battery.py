@@ -1,11 +1,13 @@
 """Child process of tests/test_checked_build.py, run with LR_ATTN_LIB naming
 the checked library (liblr_attn_check.so: every cache access of the kernels
 tested against the cache buffer).  Runs the seeded random plans of
-test_gpu_random_shapes (appends, absorbed and explicit decodes, split and
-unsplit launches, the fused append; each still checked against the oracle),
-then one decode with the tested extent shrunk by a tile's worth of bytes, and
-prints one JSON line: the accesses found outside the caches in the first
-part (must be 0) and in the second (must not be: the check fires)."""
+test_gpu_random_shapes and the decode cases of test_gpu_parity that reach the
+edges of the layout (ragged and empty contexts, every row tail width, small
+heads in the paired buckets, context splits, the fused append, 128 heads, a
+2^24-token context with offsets past 4 GiB) -- each still checked against the
+oracle -- then one decode with the tested extent shrunk by a few tiles'
+bytes, and prints one JSON line: the accesses found outside the caches in
+the first part (must be 0) and in the second (must not be: the check fires)."""
 import json
 import os
 import sys
@@ -19,6 +21,7 @@ import torch         # noqa: E402
 
 import latent_kv_attention_lr_amd as lr                     # noqa: E402
 from latent_kv_attention_lr_amd.session import DecodeSession   # noqa: E402
+import test_gpu_parity as gp                                # noqa: E402
 import test_gpu_random_shapes as rs                         # noqa: E402
 
 
@@ -27,6 +30,20 @@ def main():
     lr.lr_attn_check_count()                     # start from 0
     for seed in range(rs.N_CASES):
         rs.test_random_shape_decode_matches_oracle(seed)
+    I8, I4, BF, F32 = lr.LR_Q_INT8_TOKEN, lr.LR_Q_INT4_G32, lr.LR_DT_BF16, lr.LR_DT_F32
+    for qfmt in (I8, I4):
+        for io in (BF, F32):
+            for max_splits in (0, 1):
+                gp.test_decode_ragged_and_degenerate_lengths(qfmt, io, max_splits)
+            for bucket in (32, 96, 128):
+                gp.test_decode_every_row_tail_width(qfmt, io, bucket)
+            gp.test_decode_context_split_path(qfmt, io)
+            gp.test_append_decode_fused_equals_separate(qfmt, io)
+        gp.test_decode_all_128_heads(qfmt)
+        gp.test_decode_at_maximum_capacity(qfmt)
+    for io in (BF, F32):
+        for bucket in (96, 128):
+            gp.test_decode_small_heads_in_paired_buckets(io, bucket)
     torch.cuda.synchronize()
     outside = lr.lr_attn_check_count()
 
@@ -48,7 +65,7 @@ def main():
     lr.lr_attn_check_shrink(0)
     fired = lr.lr_attn_check_count()
     s.close()
-    print(json.dumps({"cases": rs.N_CASES, "outside": outside, "outside_with_shrink": fired}), flush=True)
+    print(json.dumps({"random_plans": rs.N_CASES, "outside": outside, "outside_with_shrink": fired}), flush=True)
 
 
 if __name__ == "__main__":

@@ -2,8 +2,9 @@
 every cache access of the append, decode and explicit kernels is tested
 against the extent of its cache buffer; one outside is counted and redirected
 instead of faulting.  On the GPU, in a child process that loads that library,
-the seeded random plans of test_gpu_random_shapes make no access outside their
-caches, and shrinking the tested extent makes the check fire.  On the CPU, the
+the seeded random plans of test_gpu_random_shapes and the layout-edge decode
+cases of test_gpu_parity (tests/check_battery.py) make no access outside
+their caches, and shrinking the tested extent makes the check fire.  On the CPU, the
 release library answers the check calls with LR_EUNSUPPORTED."""
 import json
 import os
