@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "check.h"
 #include "ffn_lds.h"
 #include "plan.h"
 
@@ -51,6 +52,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 #endif
 
 using namespace lr::ffnlds;   // LDS layout and instances (ffn_lds.h)
+using lr::Bounds;             // the checked build's bounds test (check.h)
+using lr::checked;
 constexpr int kThreads = kWaves * 64;
 // LDS: the codes and group scales of 16 tokens (E in k_ffn_in, two blocks of
 // r in k_ffn_mid, one chunk of k_ffn_out), then 2 x 16 x 16 fp32 of reduced
@@ -81,17 +84,22 @@ __device__ __forceinline__ float wave_absmax(float v) {
 // wavefront per (token, group of 64), one element per lane; the group's
 // max|v| is a wavefront reduction.  The launch also clears the n_cnt
 // counters that the step's later launches count into.
+// The extents the checked build tests the launches' accesses against.
+struct FfnBounds {
+  Bounds w, ws, x, y;   // packed weights, workspace, input x, output y
+};
+
 __global__ __launch_bounds__(256) void k_ffn_quant(const uint16_t* src, int64_t ld, int32_t K, int32_t T, int32_t Kp,
-                                                   int8_t* dst, float* sc, int32_t* cnt, int32_t n_cnt) {
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < n_cnt; i += gridDim.x * 256) cnt[i] = 0;
+                                                   int8_t* dst, float* sc, int32_t* cnt, int32_t n_cnt, FfnBounds fb) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n_cnt; i += gridDim.x * 256) *checked(fb.ws, cnt + i, 4) = 0;
   const int groups = Kp / 64;
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (wave >= T * groups) return;
   const int t = wave / groups, g = wave % groups, k = 64 * g + lane;
-  const float v = k < K ? __uint_as_float(uint32_t(src[t * ld + k]) << 16) : 0.0f;
+  const float v = k < K ? __uint_as_float(uint32_t(*checked(fb.x, src + t * ld + k, 2)) << 16) : 0.0f;
   const float s = wave_absmax(v) / 127.0f;
-  dst[size_t(t) * Kp + k] = int8_t(code(v, s));
-  if (lane == 0) sc[size_t(t) * groups + g] = s;
+  *checked(fb.ws, dst + size_t(t) * Kp + k, 1) = int8_t(code(v, s));
+  if (lane == 0) *checked(fb.ws, sc + size_t(t) * groups + g, 4) = s;
 }
 
 // Copy codes of tokens t0 .. t0 + 15 (clamped to T - 1), columns c0 .. c0 +
@@ -105,8 +113,8 @@ __global__ __launch_bounds__(256) void k_ffn_quant(const uint16_t* src, int64_t 
 #define LR_FFN_LDS_DMA 1
 #endif
 using lds_ptr = __attribute__((address_space(3))) void*;
-__device__ void stage_codes(const int8_t* codes, const float* scales, int64_t ld, int c0, int kn, int T, int t0,
-                            int8_t* act, float* scale, int rs) {
+__device__ void stage_codes(const Bounds& bws, const int8_t* codes, const float* scales, int64_t ld, int c0, int kn,
+                            int T, int t0, int8_t* act, float* scale, int rs) {
   const int pieces = kn / 16, gn = kn / 64;
   if constexpr (LR_FFN_LDS_DMA) {
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -114,22 +122,24 @@ __device__ void stage_codes(const int8_t* codes, const float* scales, int64_t ld
     for (int job = wid; job < 16 * segs; job += kWaves) {   // one 1 KB row segment per wavefront load
       const int tt = job / segs, sg = job % segs, t = min(t0 + tt, T - 1), piece = 64 * sg + lane;
       if (piece < pieces)
-        __builtin_amdgcn_global_load_lds(codes + t * ld + c0 + 16 * piece, (lds_ptr)(act + tt * rs + 1024 * sg), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(checked(bws, codes + t * ld + c0 + 16 * piece, 16),
+                                         (lds_ptr)(act + tt * rs + 1024 * sg), 16, 0, 0);
     }
     for (int job = wid; job < 16 * gsegs; job += kWaves) {
       const int tt = job / gsegs, sg = job % gsegs, t = min(t0 + tt, T - 1), g = 64 * sg + lane;
       if (g < gn)
-        __builtin_amdgcn_global_load_lds(scales + t * (ld / 64) + c0 / 64 + g, (lds_ptr)(scale + tt * gn + 64 * sg), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(checked(bws, scales + t * (ld / 64) + c0 / 64 + g, 4),
+                                         (lds_ptr)(scale + tt * gn + 64 * sg), 4, 0, 0);
     }
   } else {
     for (int i = threadIdx.x; i < 16 * pieces; i += kThreads) {
       const int tt = i / pieces, col = i % pieces, t = min(t0 + tt, T - 1);
       *reinterpret_cast<uint4*>(act + tt * rs + 16 * col) =
-          *reinterpret_cast<const uint4*>(codes + t * ld + c0 + 16 * col);
+          *checked(bws, reinterpret_cast<const uint4*>(codes + t * ld + c0 + 16 * col), 16);
     }
     for (int i = threadIdx.x; i < 16 * gn; i += kThreads) {
       const int tt = i / gn, g = i % gn, t = min(t0 + tt, T - 1);
-      scale[i] = scales[t * (ld / 64) + c0 / 64 + g];
+      scale[i] = *checked(bws, scales + t * (ld / 64) + c0 / 64 + g, 4);
     }
   }
 }
@@ -147,7 +157,7 @@ __device__ __forceinline__ void staged() {
 // first batch of weight loads is issued before `stage` runs (stage fills LDS
 // and ends with a barrier), so their latency overlaps the staging.
 template <int RT, typename Stage>
-__device__ __forceinline__ void gemm_steps(const uint8_t* const (&wt)[RT], int c0, int c1, int gbase,
+__device__ __forceinline__ void gemm_steps(const Bounds& bw, const uint8_t* const (&wt)[RT], int c0, int c1, int gbase,
                                            const int8_t* const (&act)[RT], const float* const (&scale)[RT],
                                            int rs, int groups, f32x4_t (&acc)[RT], Stage stage) {
   const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
@@ -158,7 +168,8 @@ __device__ __forceinline__ void gemm_steps(const uint8_t* const (&wt)[RT], int c
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
-        const i32x4_t* p = reinterpret_cast<const i32x4_t*>(wt[r] + size_t(min(c + u, c1 - 1)) * 1024 + 16 * lane);
+        const i32x4_t* p =
+            checked(bw, reinterpret_cast<const i32x4_t*>(wt[r] + size_t(min(c + u, c1 - 1)) * 1024 + 16 * lane), 16);
         if constexpr (LR_FFN_NT_LOADS) a[u][r] = __builtin_nontemporal_load(p);
         else a[u][r] = *p;
       }
@@ -227,26 +238,27 @@ __device__ __forceinline__ void put(V* p, V v) { __hip_atomic_store(p, v, __ATOM
 // Every wavefront waits for its stores (they count in vmcnt on this
 // architecture), then thread 0 counts the work-group's share; returns, to
 // every thread, whether it completed the group of `size`.
-__device__ bool count_last(int32_t* c, int size, int* s_flag) {
+__device__ bool count_last(const Bounds& bws, int32_t* c, int size, int* s_flag) {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
   if (threadIdx.x == 0)
-    *s_flag = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == size - 1;
+    *s_flag = __hip_atomic_fetch_add(checked(bws, c, 4), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == size - 1;
   __syncthreads();
   return *s_flag != 0;
 }
 
 // Quantise one 64-channel group g of h (rows of Fh floats, zeros past F)
 // for tokens t0 .. t0 + 15: one wavefront per token, a lane per channel.
-__device__ void quantise_h_group(const float* h, int Fh, int F, int8_t* hq, float* hs, int Fp, int T, int t0, int g) {
+__device__ void quantise_h_group(const Bounds& bws, const float* h, int Fh, int F, int8_t* hq, float* hs, int Fp,
+                                 int T, int t0, int g) {
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, ch = 64 * g + lane;
   for (int tt = wid; tt < 16; tt += kWaves) {
     const int t = t0 + tt;
     if (t >= T) break;
-    const float v = ch < F ? h[size_t(t) * Fh + ch] : 0.0f;
+    const float v = ch < F ? *checked(bws, h + size_t(t) * Fh + ch, 4) : 0.0f;
     const float s = wave_absmax(v) / 127.0f;
-    hq[size_t(t) * Fp + ch] = int8_t(code(v, s));
-    if (lane == 0) hs[size_t(t) * (Fp / 64) + g] = s;
+    *checked(bws, hq + size_t(t) * Fp + ch, 1) = int8_t(code(v, s));
+    if (lane == 0) *checked(bws, hs + size_t(t) * (Fp / 64) + g, 4) = s;
   }
 }
 
@@ -259,10 +271,10 @@ struct HArgs {
   int32_t* hcnt;              // [TB][Fp / 64] pair work-groups done per group
   int32_t Fh, Fp;
 };
-__device__ void h_stored(const HArgs& ha, int F, int T, int t0, int ch0, int* s_flag) {
+__device__ void h_stored(const Bounds& bws, const HArgs& ha, int F, int T, int t0, int ch0, int* s_flag) {
   const int g = ch0 >> 6, G = ha.Fp / 64;
-  if (count_last(ha.hcnt + (t0 / 16) * G + g, min(64, F - 64 * g) / 16, s_flag))
-    quantise_h_group(ha.h, ha.Fh, F, ha.hq, ha.hs, ha.Fp, T, t0, g);
+  if (count_last(bws, ha.hcnt + (t0 / 16) * G + g, min(64, F - 64 * g) / 16, s_flag))
+    quantise_h_group(bws, ha.h, ha.Fh, F, ha.hq, ha.hs, ha.Fp, T, t0, g);
 }
 
 static_assert(in_extent(2048) <= kLdsS && in_extent(4096) <= kLdsM && in_extent(8192) <= kLdsL &&
@@ -280,6 +292,7 @@ struct InArgs {
   int8_t* zq;                 // [T][2 r] codes of the latents z = [A_g; A_u] x
   float* zs;                  // [T][2 r / 64] their group scales
   int32_t T, E, F, S, pairs, lat_groups;   // pairs = (F - S) / 16; lat_groups = 2 r / 64
+  FfnBounds fb;
 };
 
 // Launch 2: work-group = (latent half-group or dense pair, block of 16
@@ -314,8 +327,8 @@ __global__ __launch_bounds__(kThreads) void k_ffn_in(InArgs a) {
       scs[r] = scale;
       acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    gemm_steps<4>(wt, c0 + n * wid / kWaves, c0 + n * (wid + 1) / kWaves, c0, acts, scs, rs, n, acc, [&]() {
-      stage_codes(a.xq, a.xs, a.E, 64 * c0, 64 * n, a.T, t0, act, scale, rs);
+    gemm_steps<4>(a.fb.w, wt, c0 + n * wid / kWaves, c0 + n * (wid + 1) / kWaves, c0, acts, scs, rs, n, acc, [&]() {
+      stage_codes(a.fb.ws, a.xq, a.xs, a.E, 64 * c0, 64 * n, a.T, t0, act, scale, rs);
       staged();
     });
     reduce_tiles<4>(acc, smem, outv);
@@ -323,18 +336,19 @@ __global__ __launch_bounds__(kThreads) void k_ffn_in(InArgs a) {
     const int zr = 64 * a.lat_groups, r = lane >> 4, nn = lane & 15;   // zr = 2 r floats per token
     for (int tt = wid; tt < 16; tt += kWaves) {
       const int t = t0 + tt;
-      if (t < a.T) put(a.zp + (size_t(q) * a.T + t) * zr + 64 * j + lane, outv[(r * 16 + tt) * 16 + nn]);
+      if (t < a.T) put(checked(a.fb.ws, a.zp + (size_t(q) * a.T + t) * zr + 64 * j + lane, 4), outv[(r * 16 + tt) * 16 + nn]);
     }
-    if (!count_last(a.zcnt + (t0 / 16) * a.lat_groups + j, 2, &s_flag)) return;
+    if (!count_last(a.fb.ws, a.zcnt + (t0 / 16) * a.lat_groups + j, 2, &s_flag)) return;
     // the second half to finish: z = (half 0 + half 1) x row scale, quantised per token
     for (int tt = wid; tt < 16; tt += kWaves) {
       const int t = t0 + tt;
       if (t >= a.T) break;
       const size_t o = size_t(t) * zr + 64 * j + lane;
-      const float v = (a.zp[o] + a.zp[size_t(a.T) * zr + o]) * a.ws[16 * (tile0 + r) + nn];
+      const float v = (*checked(a.fb.ws, a.zp + o, 4) + *checked(a.fb.ws, a.zp + size_t(a.T) * zr + o, 4)) *
+                      *checked(a.fb.w, a.ws + 16 * (tile0 + r) + nn, 4);
       const float s = wave_absmax(v) / 127.0f;
-      a.zq[o] = int8_t(code(v, s));
-      if (lane == 0) a.zs[size_t(t) * a.lat_groups + j] = s;
+      *checked(a.fb.ws, a.zq + o, 1) = int8_t(code(v, s));
+      if (lane == 0) *checked(a.fb.ws, a.zs + size_t(t) * a.lat_groups + j, 4) = s;
     }
     return;
   }
@@ -346,18 +360,19 @@ __global__ __launch_bounds__(kThreads) void k_ffn_in(InArgs a) {
   const int8_t* acts[2] = {act, act};
   const float* scs[2] = {scale, scale};
   f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-  gemm_steps<2>(wt, steps * wid / kWaves, steps * (wid + 1) / kWaves, 0, acts, scs, rs, steps, acc, [&]() {
-    stage_codes(a.xq, a.xs, a.E, 0, a.E, a.T, t0, act, scale, rs);
+  gemm_steps<2>(a.fb.w, wt, steps * wid / kWaves, steps * (wid + 1) / kWaves, 0, acts, scs, rs, steps, acc, [&]() {
+    stage_codes(a.fb.ws, a.xq, a.xs, a.E, 0, a.E, a.T, t0, act, scale, rs);
     staged();
   });
   reduce_tiles<2>(acc, smem, outv);
   for (int i = threadIdx.x; i < 256; i += kThreads) {
     const int tt = i >> 4, nn = i & 15, t = t0 + tt;
     if (t >= a.T) continue;
-    const float v0 = outv[i] * a.ws[16 * tile0 + nn], v1 = outv[256 + i] * a.ws[16 * (tile0 + 1) + nn];
-    put(a.ha.h + size_t(t) * a.ha.Fh + a.S + 16 * p + nn, silu_mul(v0, v1));   // channel S + 16 p + nn
+    const float v0 = outv[i] * *checked(a.fb.w, a.ws + 16 * tile0 + nn, 4);
+    const float v1 = outv[256 + i] * *checked(a.fb.w, a.ws + 16 * (tile0 + 1) + nn, 4);
+    put(checked(a.fb.ws, a.ha.h + size_t(t) * a.ha.Fh + a.S + 16 * p + nn, 4), silu_mul(v0, v1));   // channel S + 16 p + nn
   }
-  h_stored(a.ha, a.F, a.T, t0, a.S + 16 * p, &s_flag);
+  h_stored(a.fb.ws, a.ha, a.F, a.T, t0, a.S + 16 * p, &s_flag);
 }
 
 struct MidArgs {
@@ -367,6 +382,7 @@ struct MidArgs {
   const float* ws;
   HArgs ha;                   // h channels [0, S)
   int32_t T, r, F, pairs;     // pairs = S / 16
+  FfnBounds fb;
 };
 
 // Launch 4: work-group = (low-rank pair p, block of 16 tokens); B_g reads the
@@ -391,19 +407,20 @@ __global__ __launch_bounds__(kThreads) void k_ffn_mid(MidArgs a) {
   const float* scs[2] = {sc[0], sc[1]};
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-  gemm_steps<2>(wt, steps * wid / kWaves, steps * (wid + 1) / kWaves, 0, acts, scs, rs, steps, acc, [&]() {
+  gemm_steps<2>(a.fb.w, wt, steps * wid / kWaves, steps * (wid + 1) / kWaves, 0, acts, scs, rs, steps, acc, [&]() {
     for (int half = 0; half < 2; ++half)
-      stage_codes(a.zq, a.zs, 2 * a.r, half * a.r, a.r, a.T, t0, act[half], sc[half], rs);
+      stage_codes(a.fb.ws, a.zq, a.zs, 2 * a.r, half * a.r, a.r, a.T, t0, act[half], sc[half], rs);
     staged();
   });
   reduce_tiles<2>(acc, smem, outv);
   for (int i = threadIdx.x; i < 256; i += kThreads) {
     const int tt = i >> 4, nn = i & 15, t = t0 + tt;
     if (t < a.T)
-      put(a.ha.h + size_t(t) * a.ha.Fh + 16 * unit + nn,
-          silu_mul(outv[i] * a.ws[16 * tile0 + nn], outv[256 + i] * a.ws[16 * (tile0 + 1) + nn]));
+      put(checked(a.fb.ws, a.ha.h + size_t(t) * a.ha.Fh + 16 * unit + nn, 4),
+          silu_mul(outv[i] * *checked(a.fb.w, a.ws + 16 * tile0 + nn, 4),
+                   outv[256 + i] * *checked(a.fb.w, a.ws + 16 * (tile0 + 1) + nn, 4)));
   }
-  h_stored(a.ha, a.F, a.T, t0, 16 * unit, &s_flag);
+  h_stored(a.fb.ws, a.ha, a.F, a.T, t0, 16 * unit, &s_flag);
 }
 
 struct OutArgs {
@@ -415,6 +432,7 @@ struct OutArgs {
   float* yp;                  // partials [splits][T][E] when splits > 1
   int32_t* ycnt;              // [TB][units] chunks done per row tile
   int32_t T, E, Fp, units, splits;   // units = E / (16 RT); splits = ceil(Fp / CHUNK)
+  FfnBounds fb;
 };
 
 // Launch 4: work-group = (RT tiles of 16 rows of W_d, one CHUNK of the hidden
@@ -447,31 +465,31 @@ __global__ __launch_bounds__(kThreads) void k_ffn_out(OutArgs a) {
   }
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int cb = k0 / 64;
-  gemm_steps<RT>(wt, cb + gn * wid / kWaves, cb + gn * (wid + 1) / kWaves, cb, acts, scs, rs, gn, acc, [&]() {
-    stage_codes(a.hq, a.hs, a.Fp, k0, kn, a.T, t0, act, scale, rs);
+  gemm_steps<RT>(a.fb.w, wt, cb + gn * wid / kWaves, cb + gn * (wid + 1) / kWaves, cb, acts, scs, rs, gn, acc, [&]() {
+    stage_codes(a.fb.ws, a.hq, a.hs, a.Fp, k0, kn, a.T, t0, act, scale, rs);
     staged();
   });
   reduce_tiles<RT>(acc, smem, outv);
   if (a.splits == 1) {
     for (int i = threadIdx.x; i < RT * 256; i += kThreads) {
       const int r = i >> 8, tt = (i >> 4) & 15, nn = i & 15, t = t0 + tt, row = 16 * (RT * unit + r) + nn;
-      if (t < a.T) a.y[size_t(t) * a.E + row] = outv[i] * a.ws[row];
+      if (t < a.T) *checked(a.fb.y, a.y + size_t(t) * a.E + row, 4) = outv[i] * *checked(a.fb.w, a.ws + row, 4);
     }
     return;
   }
   const size_t n = size_t(a.T) * a.E;
   for (int i = threadIdx.x; i < RT * 256; i += kThreads) {
     const int r = i >> 8, tt = (i >> 4) & 15, nn = i & 15, t = t0 + tt, row = 16 * (RT * unit + r) + nn;
-    if (t < a.T) put(a.yp + split * n + size_t(t) * a.E + row, outv[i] * a.ws[row]);
+    if (t < a.T) put(checked(a.fb.ws, a.yp + split * n + size_t(t) * a.E + row, 4), outv[i] * *checked(a.fb.w, a.ws + row, 4));
   }
-  if (!count_last(a.ycnt + (t0 / 16) * a.units + unit, a.splits, &s_flag)) return;
+  if (!count_last(a.fb.ws, a.ycnt + (t0 / 16) * a.units + unit, a.splits, &s_flag)) return;
   for (int i = threadIdx.x; i < RT * 256; i += kThreads) {   // y = sum over chunks s = 0, 1, ... in order
     const int r = i >> 8, tt = (i >> 4) & 15, nn = i & 15, t = t0 + tt, row = 16 * (RT * unit + r) + nn;
     if (t >= a.T) continue;
     const size_t o = size_t(t) * a.E + row;
     float v = 0.0f;
-    for (int c = 0; c < a.splits; ++c) v += a.yp[c * n + o];
-    a.y[o] = v;
+    for (int c = 0; c < a.splits; ++c) v += *checked(a.fb.ws, a.yp + c * n + o, 4);
+    *checked(a.fb.y, a.y + o, 4) = v;
   }
 }
 
@@ -504,14 +522,17 @@ int launch_ffn(const FfnLayout& f, const void* weights, const void* x, int32_t n
   if (size_t(n_cnt) * 4 > f.ws_cnt_bytes) return int(hipErrorInvalidValue);
   HArgs ha{reinterpret_cast<float*>(ws + f.ws_h), reinterpret_cast<int8_t*>(ws + f.ws_hq),
            reinterpret_cast<float*>(ws + f.ws_hs), hcnt, f.h_ld, f.Fp};
+  const FfnBounds fb{Bounds{w, checked_extent(f.weight_bytes)}, Bounds{ws, checked_extent(f.ws_bytes)},
+                     Bounds{static_cast<const uint8_t*>(x), checked_extent(size_t(T) * f.E * 2)},
+                     Bounds{reinterpret_cast<const uint8_t*>(y), checked_extent(size_t(T) * f.E * 4)}};
   int err = 0;
 
   const unsigned qgrid = unsigned((T * (f.E / 64) + 3) / 4);
   hipLaunchKernelGGL(k_ffn_quant, dim3(qgrid), dim3(256), 0, s, static_cast<const uint16_t*>(x), int64_t(f.E), f.E, T,
-                     f.E, xq, xs, cnt, n_cnt);
+                     f.E, xq, xs, cnt, n_cnt, fb);
   if ((err = int(hipGetLastError())) != 0) return err;
   InArgs ia{xq, xs, w + f.off_w1, reinterpret_cast<const float*>(w + f.off_s1), ha,
-            reinterpret_cast<float*>(ws + f.ws_zp), zcnt, zq, zs, T, f.E, f.F, f.S, (f.F - f.S) / 16, lat_groups};
+            reinterpret_cast<float*>(ws + f.ws_zp), zcnt, zq, zs, T, f.E, f.F, f.S, (f.F - f.S) / 16, lat_groups, fb};
   if (ia.pairs + ia.lat_groups > 0) {
     const dim3 g(unsigned(ia.pairs + 2 * ia.lat_groups) * tb), b(kThreads);
     const int lds = instance_for(in_extent(f.E));   // the smallest instance that holds it
@@ -522,7 +543,7 @@ int launch_ffn(const FfnLayout& f, const void* weights, const void* x, int32_t n
     if ((err = int(hipGetLastError())) != 0) return err;
   }
   if (f.S > 0) {
-    MidArgs ma{zq, zs, w + f.off_w2, reinterpret_cast<const float*>(w + f.off_s2), ha, T, f.r, f.F, f.S / 16};
+    MidArgs ma{zq, zs, w + f.off_w2, reinterpret_cast<const float*>(w + f.off_s2), ha, T, f.r, f.F, f.S / 16, fb};
     const dim3 g(unsigned(ma.pairs) * tb), b(kThreads);
     const int lds = instance_for(mid_extent(f.r));
     if (lds == kLdsS) hipLaunchKernelGGL(k_ffn_mid<kLdsS>, g, b, 0, s, ma);
@@ -536,12 +557,24 @@ int launch_ffn(const FfnLayout& f, const void* weights, const void* x, int32_t n
   // of W_d (measured best on the LLaMA-7B FFN among chunks of 1, 2, 4 and 8 K
   // with one or two tiles).
   OutArgs oa{ha.hq, ha.hs, w + f.off_w3, reinterpret_cast<const float*>(w + f.off_s3), y,
-             reinterpret_cast<float*>(ws + f.ws_yp), ycnt, T, f.E, f.Fp, out_units, splits};
+             reinterpret_cast<float*>(ws + f.ws_yp), ycnt, T, f.E, f.Fp, out_units, splits, fb};
   const dim3 g(unsigned(oa.units) * unsigned(splits) * tb), b(kThreads);
   if (chunk == 2048) hipLaunchKernelGGL((k_ffn_out<kLdsS, 2048, 1>), g, b, 0, s, oa);
   else if (rt == 1) hipLaunchKernelGGL((k_ffn_out<kLdsM, 4096, 1>), g, b, 0, s, oa);
   else hipLaunchKernelGGL((k_ffn_out<kLdsM, 4096, 2>), g, b, 0, s, oa);
   return int(hipGetLastError());
+}
+
+int ffn_check_take(unsigned long long* count) {
+#if LR_ATTN_CHECK
+  const unsigned long long zero = 0;
+  hipError_t e = hipMemcpyFromSymbol(count, HIP_SYMBOL(g_check_count), sizeof *count, 0, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(g_check_count), &zero, sizeof zero, 0, hipMemcpyHostToDevice);
+  return int(e);
+#else
+  *count = 0;
+  return 0;
+#endif
 }
 
 }  // namespace lr

@@ -20,6 +20,7 @@
 #include <mutex>
 #include <type_traits>
 
+#include "check.h"
 #include "plan.h"
 
 namespace lr {
@@ -28,38 +29,6 @@ namespace {
 constexpr float kTau = 8.0f;          // lazy rescale threshold (log2 units)
 constexpr float kLog2e = 1.4426950408889634f;
 
-// ---------------------------------------------------------------------------
-// The checked build (LR_ATTN_CHECK = 1, liblr_attn_check.so): every access to
-// a cache tile is tested against the extent of the cache buffer; one outside
-// it is counted in g_check_count and redirected to the buffer's first bytes,
-// so the launch completes and the host reads the count
-// (lr_attn_check_count) instead of a fault.  The release build compiles the
-// test away.
-// ---------------------------------------------------------------------------
-#ifndef LR_ATTN_CHECK
-#define LR_ATTN_CHECK 0
-#endif
-struct Bounds {
-  const uint8_t* lo;   // the cache buffer
-  uint64_t n;          // its bytes
-};
-#if LR_ATTN_CHECK
-__device__ unsigned long long g_check_count;
-#endif
-template <typename P>
-__device__ __forceinline__ P checked(const Bounds& bd, P p, int bytes) {
-#if LR_ATTN_CHECK
-  const uint8_t* q = reinterpret_cast<const uint8_t*>(p);
-  if (q < bd.lo || q + bytes > bd.lo + bd.n) {
-    atomicAdd(&g_check_count, 1ull);
-    return reinterpret_cast<P>(const_cast<uint8_t*>(bd.lo));
-  }
-#else
-  (void)bd;
-  (void)bytes;
-#endif
-  return p;
-}
 
 // ---------------------------------------------------------------------------
 // element I/O
@@ -1338,14 +1307,10 @@ hipError_t launch_decode_q(int bucket, int waves, dim3 grid, hipStream_t st, con
 // hipGetSymbolAddress returns for it (scratch_address) is passed to kernels.
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
-// Checked build: the extent the kernels test cache accesses against, the
-// buffer's bytes less what lr_attn_check_shrink takes off (a test hook).
-uint64_t g_check_shrink = 0;
-uint64_t checked_cache_bytes(size_t bytes) {
-  return g_check_shrink < bytes ? uint64_t(bytes) - g_check_shrink : 0;
-}
-
 }  // namespace
+
+uint64_t g_check_shrink = 0;
+uint64_t checked_extent(size_t bytes) { return g_check_shrink < bytes ? uint64_t(bytes) - g_check_shrink : 0; }
 
 int scratch_address(void** out) {
   static std::mutex mu;
@@ -1370,7 +1335,7 @@ int launch_append(const lr_attn_plan& p, int32_t layer, void* cache, const float
   const auto& L = p.layers[layer];
   AppendArgs a;
   a.cache = static_cast<uint8_t*>(cache);
-  a.cache_bytes = checked_cache_bytes(L.cache_bytes);
+  a.cache_bytes = checked_extent(L.cache_bytes);
   a.ck = ck;
   a.cv = cv;
   a.pos = pos;
@@ -1426,7 +1391,7 @@ int launch_decode(const lr_attn_plan& p, int32_t layer, const void* cache, const
   const Split sp = explicit_form ? explicit_split(p, layer, max_len) : choose_split(p, layer, max_len);
   DecodeArgs a;
   a.cache = static_cast<const uint8_t*>(cache);
-  a.cache_bytes = checked_cache_bytes(L.cache_bytes);
+  a.cache_bytes = checked_extent(L.cache_bytes);
   a.len = len;
   a.q = q;
   a.bk = bk;
@@ -1479,15 +1444,16 @@ extern "C" {
 lr_status lr_attn_check_count(uint64_t* count) {
 #if LR_ATTN_CHECK
   if (!count) return LR_EINVAL;
-  unsigned long long v = 0;
+  unsigned long long v = 0, vf = 0;
   const unsigned long long zero = 0;
-  hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(lr::g_check_count), sizeof v, 0, hipMemcpyDeviceToHost);
-  if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(lr::g_check_count), &zero, sizeof zero, 0, hipMemcpyHostToDevice);
-  if (e != hipSuccess) {
-    lr::set_last_hip_error(int(e));
+  int e = int(hipMemcpyFromSymbol(&v, HIP_SYMBOL(lr::g_check_count), sizeof v, 0, hipMemcpyDeviceToHost));
+  if (e == 0) e = int(hipMemcpyToSymbol(HIP_SYMBOL(lr::g_check_count), &zero, sizeof zero, 0, hipMemcpyHostToDevice));
+  if (e == 0) e = lr::ffn_check_take(&vf);   // the FFN kernels' counter (ffn.hip)
+  if (e != 0) {
+    lr::set_last_hip_error(e);
     return LR_EHIP;
   }
-  *count = v;
+  *count = v + vf;
   return LR_OK;
 #else
   (void)count;

@@ -108,6 +108,12 @@ int launch_ffn(const FfnLayout& f, const void* weights, const void* x, int32_t n
 constexpr size_t kScratchBytes = LR_NOALLOC_SCRATCH_BYTES;
 constexpr int kMaxDevices = 64;
 int scratch_address(void** out);
+// The checked build (check.h): the extent the kernels test a buffer's
+// accesses against -- its bytes less what lr_attn_check_shrink takes off (a
+// test hook; 0 by default) -- and, from ffn.hip, the FFN kernels' count of
+// accesses outside their buffers, read and reset (returns a hipError_t).
+uint64_t checked_extent(size_t bytes);
+int ffn_check_take(unsigned long long* count);
 // probe.hip: stream bytes / 16 16-byte words from src (read only).
 int launch_probe_read(const void* src, size_t bytes, void* sink, void* stream);
 

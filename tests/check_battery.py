@@ -5,9 +5,11 @@ test_gpu_random_shapes and the decode cases of test_gpu_parity that reach the
 edges of the layout (ragged and empty contexts, every row tail width, small
 heads in the paired buckets, context splits, the fused append, 128 heads, a
 2^24-token context with offsets past 4 GiB) -- each still checked against the
-oracle -- then one decode with the tested extent shrunk by a few tiles'
-bytes, and prints one JSON line: the accesses found outside the caches in
-the first part (must be 0) and in the second (must not be: the check fires)."""
+oracle -- and the hybrid FFN's fixed, full-size, multi-pass and seeded
+random shapes; then one decode and one FFN call with the tested extents
+shrunk by 4 KiB, and prints one JSON line: the accesses found outside their
+buffers in the first parts (must be 0) and in the second (must not be: the
+check fires)."""
 import json
 import os
 import sys
@@ -21,6 +23,7 @@ import torch         # noqa: E402
 
 import latent_kv_attention_lr_amd as lr                     # noqa: E402
 from latent_kv_attention_lr_amd.session import DecodeSession   # noqa: E402
+import test_ffn as tf                                       # noqa: E402
 import test_gpu_parity as gp                                # noqa: E402
 import test_gpu_random_shapes as rs                         # noqa: E402
 
@@ -47,6 +50,17 @@ def main():
     torch.cuda.synchronize()
     outside = lr.lr_attn_check_count()
 
+    # the hybrid FFN: its fixed shapes, the full workload, the seeded random shapes
+    shapes = [m for m in tf.test_ffn_decode_matches_oracle.pytestmark if m.name == "parametrize"][0].args[1]
+    for shape in shapes:
+        tf.test_ffn_decode_matches_oracle(*shape)
+    tf.test_ffn_decode_full_size_and_deterministic()
+    tf.test_ffn_decode_in_several_passes()
+    for seed in range(16):
+        tf.test_ffn_decode_random_shapes(seed)
+    torch.cuda.synchronize()
+    outside_ffn = lr.lr_attn_check_count()
+
     # the check fires: a cache whose last tiles lie past the tested extent
     rng = np.random.default_rng(5)
     B, H, cap, rk, rv = 2, 4, 300, [32, 8, 64, 16], [16, 40, 8, 32]
@@ -65,7 +79,17 @@ def main():
     lr.lr_attn_check_shrink(0)
     fired = lr.lr_attn_check_count()
     s.close()
-    print(json.dumps({"random_plans": rs.N_CASES, "outside": outside, "outside_with_shrink": fired}), flush=True)
+    from latent_kv_attention_lr_amd.ffn import FfnLayer
+    f, w, x = tf._case(256, 160, 64, 128, 17, seed=3)
+    layer = FfnLayer(256, 160, 64, 128, device="cuda:0")
+    layer.set_weights(*w)
+    lr.lr_attn_check_shrink(4096)
+    layer(x.to("cuda:0"))
+    torch.cuda.synchronize()
+    lr.lr_attn_check_shrink(0)
+    fired_ffn = lr.lr_attn_check_count()
+    print(json.dumps({"random_plans": rs.N_CASES, "outside": outside, "outside_with_shrink": fired,
+                      "ffn_outside": outside_ffn, "ffn_outside_with_shrink": fired_ffn}), flush=True)
 
 
 if __name__ == "__main__":
