@@ -4,8 +4,8 @@
 C++) are compiled with g++; ``ffn.hip`` joins the hipcc sources; ``kernels.hip``,
 ``project.hip`` and ``probe.hip`` with hipcc for gfx950; hipcc links them into
 one shared library next to this file.  ``liblr_attn_check.so`` beside it is
-the same library with ``kernels.hip`` and ``ffn.hip`` built with
-``LR_ATTN_CHECK=1`` (buffer accesses bounds-checked, a debugging aid).
+the same library with ``kernels.hip``, ``ffn.hip`` and ``project.hip`` built
+with ``LR_ATTN_CHECK=1`` (buffer accesses bounds-checked, a debugging aid).
 """
 from __future__ import annotations
 
@@ -97,7 +97,7 @@ def build(verbose: bool = False) -> str:
     outs.append(_run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp, plan_o, rot_o, alloc_o, ffnh_o, ffn_o, kern_o,
                       proj_o, probe_o]))
     os.replace(tmp, LIB)
-    outs.append(_build_checked([plan_o, rot_o, alloc_o, ffnh_o, proj_o, probe_o]))
+    outs.append(_build_checked([plan_o, rot_o, alloc_o, ffnh_o, probe_o]))
     if verbose:
         for o in outs:
             if o.strip():
@@ -106,16 +106,18 @@ def build(verbose: bool = False) -> str:
 
 
 def _build_checked(other_objs) -> str:
-    """CHECK_LIB: kernels.hip and ffn.hip rebuilt with LR_ATTN_CHECK=1 (every
-    cache, workspace, weight, input and output access of their kernels tested
-    against its buffer, lr_attn_check_count), linked with the other objects
-    of the release build."""
-    kern_o = os.path.join(BUILD, "kernels_check.o")
-    ffn_o = os.path.join(BUILD, "ffn_check.o")
-    out = _run([HIPCC, *HIP_FLAGS, "-DLR_ATTN_CHECK=1", "-c", os.path.join(CSRC, "kernels.hip"), "-o", kern_o])
-    out += _run([HIPCC, *HIP_FLAGS, "-DLR_ATTN_CHECK=1", "-c", os.path.join(CSRC, "ffn.hip"), "-o", ffn_o])
+    """CHECK_LIB: kernels.hip, ffn.hip and project.hip rebuilt with
+    LR_ATTN_CHECK=1 (every cache, workspace, weight, input and output access
+    of their kernels tested against its buffer, lr_attn_check_count), linked
+    with the host objects and the probe of the release build."""
+    objs = []
+    out = ""
+    for src in ("kernels.hip", "ffn.hip", "project.hip"):
+        o = os.path.join(BUILD, src.replace(".hip", "_check.o"))
+        out += _run([HIPCC, *HIP_FLAGS, "-DLR_ATTN_CHECK=1", "-c", os.path.join(CSRC, src), "-o", o])
+        objs.append(o)
     tmp = CHECK_LIB + ".tmp"
-    out += _run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp, *other_objs, kern_o, ffn_o])
+    out += _run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp, *other_objs, *objs])
     os.replace(tmp, CHECK_LIB)
     return out
 

@@ -1444,16 +1444,17 @@ extern "C" {
 lr_status lr_attn_check_count(uint64_t* count) {
 #if LR_ATTN_CHECK
   if (!count) return LR_EINVAL;
-  unsigned long long v = 0, vf = 0;
+  unsigned long long v = 0, vf = 0, vp = 0;
   const unsigned long long zero = 0;
   int e = int(hipMemcpyFromSymbol(&v, HIP_SYMBOL(lr::g_check_count), sizeof v, 0, hipMemcpyDeviceToHost));
   if (e == 0) e = int(hipMemcpyToSymbol(HIP_SYMBOL(lr::g_check_count), &zero, sizeof zero, 0, hipMemcpyHostToDevice));
-  if (e == 0) e = lr::ffn_check_take(&vf);   // the FFN kernels' counter (ffn.hip)
+  if (e == 0) e = lr::ffn_check_take(&vf);       // the FFN kernels' counter (ffn.hip)
+  if (e == 0) e = lr::project_check_take(&vp);   // latent generation's (project.hip)
   if (e != 0) {
     lr::set_last_hip_error(e);
     return LR_EHIP;
   }
-  *count = v + vf;
+  *count = v + vf + vp;
   return LR_OK;
 #else
   (void)count;

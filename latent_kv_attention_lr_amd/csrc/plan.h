@@ -110,10 +110,12 @@ constexpr int kMaxDevices = 64;
 int scratch_address(void** out);
 // The checked build (check.h): the extent the kernels test a buffer's
 // accesses against -- its bytes less what lr_attn_check_shrink takes off (a
-// test hook; 0 by default) -- and, from ffn.hip, the FFN kernels' count of
-// accesses outside their buffers, read and reset (returns a hipError_t).
+// test hook; 0 by default) -- and, from ffn.hip and project.hip, their
+// kernels' counts of accesses outside their buffers, read and reset (each
+// returns a hipError_t).
 uint64_t checked_extent(size_t bytes);
 int ffn_check_take(unsigned long long* count);
+int project_check_take(unsigned long long* count);
 // probe.hip: stream bytes / 16 16-byte words from src (read only).
 int launch_probe_read(const void* src, size_t bytes, void* sink, void* stream);
 

@@ -24,9 +24,13 @@
 
 #include <algorithm>
 
+#include "check.h"
 #include "plan.h"
 
 namespace {
+
+using lr::Bounds;   // the checked build's bounds test (check.h)
+using lr::checked;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -61,6 +65,7 @@ struct ProjArgs {
   int32_t units;                // work-groups per token block and part: ceil(row_tiles / RT)
   int32_t n_parts;              // E is split into this many ranges of steps, each summed
                                 // into its own output block (1: the whole sum)
+  Bounds bx, bw, bk, bv;        // extents of x, wp, ck, cv (checked build)
 };
 
 // Work-group (RT 16-row tiles, block of 16 NT tokens, part q of E):
@@ -117,7 +122,8 @@ __global__ __launch_bounds__(NW * 64) void k_project(ProjArgs a) {
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int u = 0; u < SPW; ++u) dst[r][u] = ld16_stream(wl[r] + size_t(min(p * PS + wid * SPW + u, steps - 1)) * 512);
+        for (int u = 0; u < SPW; ++u)
+          dst[r][u] = ld16_stream(checked(a.bw, wl[r] + size_t(min(p * PS + wid * SPW + u, steps - 1)) * 512, 16));
     };
     // activations of phase p, piece q = row * (EP / 8) + col: token t0 + row,
     // elements p EP + 8 col .. + 7 (clamped into the row and the token range)
@@ -126,7 +132,7 @@ __global__ __launch_bounds__(NW * 64) void k_project(ProjArgs a) {
       for (int m = 0; m < XPT; ++m) {
         const int q = min(tid + m * NW * 64, XV - 1);
         const int row = q / (EP / 8), col = q % (EP / 8);
-        xb[m] = ld16(xs + size_t(min(t0 + row, a.T - 1)) * a.E + min(p * EP + 8 * col, 32 * steps - 8));
+        xb[m] = ld16(checked(a.bx, xs + size_t(min(t0 + row, a.T - 1)) * a.E + min(p * EP + 8 * col, 32 * steps - 8), 16));
       }
     };
     auto store_x = [&]() {
@@ -200,7 +206,8 @@ __global__ __launch_bounds__(NW * 64) void k_project(ProjArgs a) {
       const int rt = RT * unit + r;
       const bool isv = rt >= a.k_tiles;
       const int t = t0 + tt, n = 16 * (isv ? rt - a.k_tiles : rt) + nn, N = isv ? a.nv : a.nk;
-      if (rt < a.row_tiles && t < a.T && n < N) (isv ? a.cv + osv : a.ck + osk)[size_t(t) * N + n] = v;
+      if (rt < a.row_tiles && t < a.T && n < N)
+        *checked(isv ? a.bv : a.bk, (isv ? a.cv + osv : a.ck + osk) + size_t(t) * N + n, 4) = v;
     }
     __syncthreads();
   }
@@ -211,7 +218,8 @@ __global__ __launch_bounds__(NW * 64) void k_project(ProjArgs a) {
 // 16 r' + (l & 15) of W^K (r < k_tiles, r' = r) or W^V (r' = r - k_tiles),
 // elements 32 c + 8 (l >> 4) .. + 7; rows past the end are zeros.
 __global__ __launch_bounds__(256) void k_pack(const uint16_t* wk, const uint16_t* wv, uint16_t* wp, int32_t E,
-                                              int32_t nk, int32_t nv, int32_t k_tiles, size_t pieces) {
+                                              int32_t nk, int32_t nv, int32_t k_tiles, size_t pieces, Bounds bwk,
+                                              Bounds bwv, Bounds bwp) {
   const int steps = E >> 5;
   for (size_t q = size_t(blockIdx.x) * 256 + threadIdx.x; q < pieces; q += size_t(gridDim.x) * 256) {
     const int l = int(q & 63);
@@ -222,8 +230,8 @@ __global__ __launch_bounds__(256) void k_pack(const uint16_t* wk, const uint16_t
     const int row = 16 * (isv ? r - k_tiles : r) + (l & 15);
     const int N = isv ? nv : nk;
     uint4 v = uint4{0u, 0u, 0u, 0u};
-    if (row < N) v = ld16((isv ? wv : wk) + size_t(row) * E + 32 * c + 8 * (l >> 4));
-    *reinterpret_cast<uint4*>(wp + 8 * q) = v;
+    if (row < N) v = ld16(checked(isv ? bwv : bwk, (isv ? wv : wk) + size_t(row) * E + 32 * c + 8 * (l >> 4), 16));
+    *checked(bwp, reinterpret_cast<uint4*>(wp + 8 * q), 16) = v;
   }
 }
 
@@ -245,7 +253,9 @@ int launch_pack_projection(const lr_attn_plan& p, int32_t layer, int32_t embed, 
   hipLaunchKernelGGL(k_pack, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint16_t*>(wk), static_cast<const uint16_t*>(wv),
                      static_cast<uint16_t*>(packed), embed, L.sum_rk, L.sum_rv, (L.sum_rk + 15) / 16,
-                     pieces);
+                     pieces, Bounds{static_cast<const uint8_t*>(wk), checked_extent(size_t(L.sum_rk) * embed * 2)},
+                     Bounds{static_cast<const uint8_t*>(wv), checked_extent(size_t(L.sum_rv) * embed * 2)},
+                     Bounds{static_cast<const uint8_t*>(packed), checked_extent(pieces * 16)});
   return int(hipGetLastError());
 }
 
@@ -322,6 +332,10 @@ int launch_project(const lr_attn_plan& p, int32_t layer, const void* x, int32_t 
   a.units = sh.units;
   a.t_blocks = sh.t_blocks;
   a.n_parts = n_parts;
+  a.bx = Bounds{static_cast<const uint8_t*>(x), checked_extent(size_t(n_tokens) * embed * 2)};
+  a.bw = Bounds{static_cast<const uint8_t*>(packed), checked_extent(packed_projection_elems(p, layer, embed) * 2)};
+  a.bk = Bounds{reinterpret_cast<const uint8_t*>(ck), checked_extent(size_t(n_parts) * n_tokens * L.sum_rk * 4)};
+  a.bv = Bounds{reinterpret_cast<const uint8_t*>(cv), checked_extent(size_t(n_parts) * n_tokens * L.sum_rv * 4)};
   const int max_tb = (1 << 20) / (a.units * n_parts);   // at most 2^20 work-groups
   a.tb_stride = a.t_blocks < max_tb ? a.t_blocks : max_tb;
   const dim3 grid(unsigned(a.units) * unsigned(n_parts) * unsigned(a.tb_stride));
@@ -336,6 +350,18 @@ int launch_project(const lr_attn_plan& p, int32_t layer, const void* x, int32_t 
   else if (sh.nt == 2) hipLaunchKernelGGL((k_project<2, 8, 8, 1>), grid, dim3(512), 0, s, a);
   else hipLaunchKernelGGL((k_project<3, 8, 4, 1>), grid, dim3(512), 0, s, a);
   return int(hipGetLastError());
+}
+
+int project_check_take(unsigned long long* count) {
+#if LR_ATTN_CHECK
+  const unsigned long long zero = 0;
+  hipError_t e = hipMemcpyFromSymbol(count, HIP_SYMBOL(g_check_count), sizeof *count, 0, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(g_check_count), &zero, sizeof zero, 0, hipMemcpyHostToDevice);
+  return int(e);
+#else
+  *count = 0;
+  return 0;
+#endif
 }
 
 }  // namespace lr

@@ -5,9 +5,10 @@ test_gpu_random_shapes and the decode cases of test_gpu_parity that reach the
 edges of the layout (ragged and empty contexts, every row tail width, small
 heads in the paired buckets, context splits, the fused append, 128 heads, a
 2^24-token context with offsets past 4 GiB) -- each still checked against the
-oracle -- and the hybrid FFN's fixed, full-size, multi-pass and seeded
-random shapes; then one decode and one FFN call with the tested extents
-shrunk by 4 KiB, and prints one JSON line: the accesses found outside their
+oracle -- the hybrid FFN's fixed, full-size, multi-pass and seeded random
+shapes, and latent generation's random shapes and entry points; then one
+decode, one FFN call and one projection with the tested extents shrunk by
+4 KiB, and prints one JSON line: the accesses found outside their
 buffers in the first parts (must be 0) and in the second (must not be: the
 check fires)."""
 import json
@@ -24,6 +25,7 @@ import torch         # noqa: E402
 import latent_kv_attention_lr_amd as lr                     # noqa: E402
 from latent_kv_attention_lr_amd.session import DecodeSession   # noqa: E402
 import test_ffn as tf                                       # noqa: E402
+import test_gpu_project as tp                               # noqa: E402
 import test_gpu_parity as gp                                # noqa: E402
 import test_gpu_random_shapes as rs                         # noqa: E402
 
@@ -61,6 +63,20 @@ def main():
     torch.cuda.synchronize()
     outside_ffn = lr.lr_attn_check_count()
 
+    # latent generation: packing, the product (unsplit and in parts), the
+    # generate-then-append and one-step-from-activations entry points
+    for seed in range(16):
+        tp.test_project_random_shapes(seed)
+    for qfmt in (I8, I4):
+        tp.test_project_append_equals_project_then_append(qfmt)
+    shapes = [m for m in tp.test_project_append_decode_integer_inputs_equal_two_calls.pytestmark
+              if m.name == "parametrize"][0].args[1]
+    for shape in shapes:
+        tp.test_project_append_decode_integer_inputs_equal_two_calls(*shape)
+    tp.test_project_append_decode_full_layer_shape_matches_oracle_chain()
+    torch.cuda.synchronize()
+    outside_proj = lr.lr_attn_check_count()
+
     # the check fires: a cache whose last tiles lie past the tested extent
     rng = np.random.default_rng(5)
     B, H, cap, rk, rv = 2, 4, 300, [32, 8, 64, 16], [16, 40, 8, 32]
@@ -88,8 +104,19 @@ def main():
     torch.cuda.synchronize()
     lr.lr_attn_check_shrink(0)
     fired_ffn = lr.lr_attn_check_count()
+    ps = tp._session([8, 32], [16, 24], batch=1, cap=64)
+    ak = torch.from_numpy(rng.standard_normal((512, 40)).astype(np.float32))
+    av = torch.from_numpy(rng.standard_normal((512, 40)).astype(np.float32))
+    tp._set_factors(ps, ak, av)
+    lr.lr_attn_check_shrink(4096)
+    ps.project(0, torch.zeros(20, 512, dtype=torch.bfloat16, device="cuda:0"))
+    torch.cuda.synchronize()
+    lr.lr_attn_check_shrink(0)
+    fired_proj = lr.lr_attn_check_count()
+    ps.close()
     print(json.dumps({"random_plans": rs.N_CASES, "outside": outside, "outside_with_shrink": fired,
-                      "ffn_outside": outside_ffn, "ffn_outside_with_shrink": fired_ffn}), flush=True)
+                      "ffn_outside": outside_ffn, "ffn_outside_with_shrink": fired_ffn,
+                      "project_outside": outside_proj, "project_outside_with_shrink": fired_proj}), flush=True)
 
 
 if __name__ == "__main__":

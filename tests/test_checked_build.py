@@ -1,10 +1,12 @@
 """The checked build (liblr_attn_check.so, kernels built with LR_ATTN_CHECK=1):
 every cache access of the append, decode and explicit kernels, and every
-weight, workspace, input and output access of the FFN kernels, is tested
+weight, workspace, input and output access of the FFN and latent-generation
+kernels, is tested
 against the extent of its buffer; one outside is counted and redirected
 instead of faulting.  On the GPU, in a child process that loads that library,
 the seeded random plans of test_gpu_random_shapes, the layout-edge decode
-cases of test_gpu_parity and the FFN cases of test_ffn (tests/check_battery.py)
+cases of test_gpu_parity, the FFN cases of test_ffn and the latent-generation
+cases of test_gpu_project (tests/check_battery.py)
 make no access outside their buffers, and shrinking the tested extents makes
 the check fire.  On the CPU, the
 release library answers the check calls with LR_EUNSUPPORTED."""
@@ -40,5 +42,6 @@ def test_checked_kernels_stay_inside_their_caches():
     assert r.returncode == 0, r.stdout[-3000:]
     d = json.loads(r.stdout.strip().splitlines()[-1])
     print(d, flush=True)
-    assert d["outside"] == 0 and d["ffn_outside"] == 0, d
+    assert d["outside"] == 0 and d["ffn_outside"] == 0 and d["project_outside"] == 0, d
     assert d["outside_with_shrink"] > 0 and d["ffn_outside_with_shrink"] > 0, d
+    assert d["project_outside_with_shrink"] > 0, d
