@@ -341,7 +341,7 @@ def ffn_bench(args):
                            % (R * layer.weights.numel() / 1e6)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": measured_ffn_traffic(f.name),
-                     "kernel": "k_ffn_quant + k_ffn_in + k_ffn_mid + k_ffn_out (one step)",
+                     "kernel": "k_ffn_quant + k_ffn_in + k_ffn_mid or k_ffn_mid_out + k_ffn_out (one step)",
                      "bytes_per_step": step_bytes,
                      "weight_bytes": weight_bytes, "avg_step_us": step_s * 1e6, "mall": "cold"},
     }

@@ -23,6 +23,9 @@
 //   k_ffn_out   y = W_d h, the hidden dimension split in chunks of 4096
 //               across work-groups; the last chunk of a row tile to finish
 //               adds the chunks' partial sums in chunk order
+// When the last chunks of the down projection hold no low-rank channel,
+// their work-groups join the low-rank pairs' launch (k_ffn_mid_out) and
+// k_ffn_out takes the others.
 // The last pair work-group of each 64-channel group of h (in k_ffn_in or
 // k_ffn_mid) quantises the group.  Each activation is quantised once (one
 // wavefront per token and group); the GEMM launches copy 16 tokens' codes into
@@ -33,6 +36,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "check.h"
 #include "ffn_lds.h"
@@ -385,15 +390,14 @@ struct MidArgs {
   FfnBounds fb;
 };
 
-// Launch 4: work-group = (low-rank pair p, block of 16 tokens); B_g reads the
-// gate latents (columns [0, r) of z), B_u the up latents ([r, 2 r)).
-template <int LDS>
-__global__ __launch_bounds__(kThreads) void k_ffn_mid(MidArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
-  __shared__ int s_flag;
+// Launch 3: work-group = (low-rank pair p, block of 16 tokens); B_g reads the
+// gate latents (columns [0, r) of z), B_u the up latents ([r, 2 r)).  blk
+// indexes the (pair, token block) units of the launch (launched only when
+// pairs >= 1); smem holds at least mid_extent(r) bytes.
+__device__ void mid_unit(const MidArgs& a, uint8_t* smem, int* s_flag, int blk) {
   const int rs = row_stride(a.r), steps = a.r / 64;
   float* outv = reinterpret_cast<float*>(smem + code_area(2 * block_bytes(a.r)));
-  const int unit = blockIdx.x % a.pairs, t0 = 16 * (blockIdx.x / a.pairs);   // launched only when pairs >= 1
+  const int unit = blk % a.pairs, t0 = 16 * (blk / a.pairs);
   int8_t* act[2];
   float* sc[2];
   for (int half = 0; half < 2; ++half) {
@@ -420,7 +424,14 @@ __global__ __launch_bounds__(kThreads) void k_ffn_mid(MidArgs a) {
           silu_mul(outv[i] * *checked(a.fb.w, a.ws + 16 * tile0 + nn, 4),
                    outv[256 + i] * *checked(a.fb.w, a.ws + 16 * (tile0 + 1) + nn, 4)));
   }
-  h_stored(a.fb.ws, a.ha, a.F, a.T, t0, 16 * unit, &s_flag);
+  h_stored(a.fb.ws, a.ha, a.F, a.T, t0, 16 * unit, s_flag);
+}
+
+template <int LDS>
+__global__ __launch_bounds__(kThreads) void k_ffn_mid(MidArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
+  __shared__ int s_flag;
+  mid_unit(a, smem, &s_flag, blockIdx.x);
 }
 
 struct OutArgs {
@@ -432,6 +443,7 @@ struct OutArgs {
   float* yp;                  // partials [splits][T][E] when splits > 1
   int32_t* ycnt;              // [TB][units] chunks done per row tile
   int32_t T, E, Fp, units, splits;   // units = E / (16 RT); splits = ceil(Fp / CHUNK)
+  int32_t split0, nsplit;     // the chunks this launch takes: split0 .. split0 + nsplit - 1
   FfnBounds fb;
 };
 
@@ -440,13 +452,13 @@ struct OutArgs {
 // once for all RT tiles.  With several chunks each work-group stores its
 // scaled partial sum, and the last chunk of the row tile to finish adds them
 // in chunk order (RT = 2 then: a token's 32 rows are one 128-byte line).
-template <int LDS, int CHUNK, int RT>
-__global__ __launch_bounds__(kThreads) void k_ffn_out(OutArgs a) {
-  static_assert(out_extent(CHUNK, RT) <= LDS && RT <= 2, "chunk exceeds LDS");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
-  __shared__ int s_flag;
-  const int unit = blockIdx.x % a.units, split = (blockIdx.x / a.units) % a.splits;
-  const int t0 = 16 * (blockIdx.x / (a.units * a.splits));
+// blk indexes the (row unit, chunk of split0 .., token block) units of the
+// launch; smem holds at least out_extent(CHUNK, RT) bytes.
+template <int CHUNK, int RT>
+__device__ void out_unit(const OutArgs& a, uint8_t* smem, int* s_flag, int blk) {
+  static_assert(RT <= 2, "two row tiles at most");
+  const int unit = blk % a.units, split = a.split0 + (blk / a.units) % a.nsplit;
+  const int t0 = 16 * (blk / (a.units * a.nsplit));
   const int steps = a.Fp / 64, kc = min(CHUNK, a.Fp);
   float* outv = reinterpret_cast<float*>(smem + code_area(block_bytes(kc)));
   const uint8_t* wt[RT];
@@ -482,7 +494,7 @@ __global__ __launch_bounds__(kThreads) void k_ffn_out(OutArgs a) {
     const int r = i >> 8, tt = (i >> 4) & 15, nn = i & 15, t = t0 + tt, row = 16 * (RT * unit + r) + nn;
     if (t < a.T) put(checked(a.fb.ws, a.yp + split * n + size_t(t) * a.E + row, 4), outv[i] * *checked(a.fb.w, a.ws + row, 4));
   }
-  if (!count_last(a.fb.ws, a.ycnt + (t0 / 16) * a.units + unit, a.splits, &s_flag)) return;
+  if (!count_last(a.fb.ws, a.ycnt + (t0 / 16) * a.units + unit, a.splits, s_flag)) return;
   for (int i = threadIdx.x; i < RT * 256; i += kThreads) {   // y = sum over chunks s = 0, 1, ... in order
     const int r = i >> 8, tt = (i >> 4) & 15, nn = i & 15, t = t0 + tt, row = 16 * (RT * unit + r) + nn;
     if (t >= a.T) continue;
@@ -491,6 +503,28 @@ __global__ __launch_bounds__(kThreads) void k_ffn_out(OutArgs a) {
     for (int c = 0; c < a.splits; ++c) v += *checked(a.fb.ws, a.yp + c * n + o, 4);
     *checked(a.fb.y, a.y + o, 4) = v;
   }
+}
+
+template <int LDS, int CHUNK, int RT>
+__global__ __launch_bounds__(kThreads) void k_ffn_out(OutArgs a) {
+  static_assert(out_extent(CHUNK, RT) <= LDS, "chunk exceeds LDS");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
+  __shared__ int s_flag;
+  out_unit<CHUNK, RT>(a, smem, &s_flag, blockIdx.x);
+}
+
+// Launch 3 when the last chunks of the down projection hold no low-rank
+// channel: their units need only what launch 2 produced (the dense channels
+// of h), so they run beside the low-rank pairs (a latency-bound launch that
+// leaves HBM mostly idle) -- the first n_mid work-groups are pair units, the
+// rest those chunks' units; launch 4 then takes the remaining chunks.
+template <int LDS, int CHUNK, int RT>
+__global__ __launch_bounds__(kThreads) void k_ffn_mid_out(MidArgs ma, OutArgs oa, int32_t n_mid) {
+  static_assert(out_extent(CHUNK, RT) <= LDS, "chunk exceeds LDS");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
+  __shared__ int s_flag;
+  if (int(blockIdx.x) < n_mid) mid_unit(ma, smem, &s_flag, blockIdx.x);
+  else out_unit<CHUNK, RT>(oa, smem, &s_flag, int(blockIdx.x) - n_mid);
 }
 
 }  // namespace
@@ -542,23 +576,44 @@ int launch_ffn(const FfnLayout& f, const void* weights, const void* x, int32_t n
     else return int(hipErrorInvalidConfiguration);
     if ((err = int(hipGetLastError())) != 0) return err;
   }
-  if (f.S > 0) {
-    MidArgs ma{zq, zs, w + f.off_w2, reinterpret_cast<const float*>(w + f.off_s2), ha, T, f.r, f.F, f.S / 16, fb};
-    const dim3 g(unsigned(ma.pairs) * tb), b(kThreads);
-    const int lds = instance_for(mid_extent(f.r));
-    if (lds == kLdsS) hipLaunchKernelGGL(k_ffn_mid<kLdsS>, g, b, 0, s, ma);
-    else if (lds == kLdsM) hipLaunchKernelGGL(k_ffn_mid<kLdsM>, g, b, 0, s, ma);
-    else if (lds == kLdsL) hipLaunchKernelGGL(k_ffn_mid<kLdsL>, g, b, 0, s, ma);
-    else return int(hipErrorInvalidConfiguration);
-    if ((err = int(hipGetLastError())) != 0) return err;
-  }
   // Chunks of 4096 (2048 for small hidden sizes); with several chunks a
   // work-group takes two row tiles, so each staged chunk of h serves 32 rows
   // of W_d (measured best on the LLaMA-7B FFN among chunks of 1, 2, 4 and 8 K
   // with one or two tiles).
   OutArgs oa{ha.hq, ha.hs, w + f.off_w3, reinterpret_cast<const float*>(w + f.off_s3), y,
-             reinterpret_cast<float*>(ws + f.ws_yp), ycnt, T, f.E, f.Fp, out_units, splits, fb};
-  const dim3 g(unsigned(oa.units) * unsigned(splits) * tb), b(kThreads);
+             reinterpret_cast<float*>(ws + f.ws_yp), ycnt, T, f.E, f.Fp, out_units, splits, 0, splits, fb};
+  // chunks from c_ind on hold no channel of a group of h with low-rank
+  // channels: they can run beside the low-rank pairs (k_ffn_mid_out)
+#ifndef LR_FFN_MERGE_OUT
+#define LR_FFN_MERGE_OUT 1
+#endif
+  const int c_ind = ((f.S + 63) / 64 * 64 + chunk - 1) / chunk;
+  const bool merge = LR_FFN_MERGE_OUT && f.S > 0 && splits > 1 && chunk == 4096 && rt == 2 && c_ind < splits;
+  if (f.S > 0) {
+    MidArgs ma{zq, zs, w + f.off_w2, reinterpret_cast<const float*>(w + f.off_s2), ha, T, f.r, f.F, f.S / 16, fb};
+    const dim3 b(kThreads);
+    if (merge) {
+      OutArgs o3 = oa;
+      o3.split0 = c_ind;
+      o3.nsplit = splits - c_ind;
+      oa.nsplit = c_ind;
+      const int n_mid = ma.pairs * int(tb);
+      const dim3 g(unsigned(n_mid) + unsigned(out_units) * unsigned(o3.nsplit) * tb);
+      const int lds = instance_for(std::max(mid_extent(f.r), out_extent(4096, 2)));
+      if (lds == kLdsM) hipLaunchKernelGGL((k_ffn_mid_out<kLdsM, 4096, 2>), g, b, 0, s, ma, o3, n_mid);
+      else if (lds == kLdsL) hipLaunchKernelGGL((k_ffn_mid_out<kLdsL, 4096, 2>), g, b, 0, s, ma, o3, n_mid);
+      else return int(hipErrorInvalidConfiguration);
+    } else {
+      const dim3 g(unsigned(ma.pairs) * tb);
+      const int lds = instance_for(mid_extent(f.r));
+      if (lds == kLdsS) hipLaunchKernelGGL(k_ffn_mid<kLdsS>, g, b, 0, s, ma);
+      else if (lds == kLdsM) hipLaunchKernelGGL(k_ffn_mid<kLdsM>, g, b, 0, s, ma);
+      else if (lds == kLdsL) hipLaunchKernelGGL(k_ffn_mid<kLdsL>, g, b, 0, s, ma);
+      else return int(hipErrorInvalidConfiguration);
+    }
+    if ((err = int(hipGetLastError())) != 0) return err;
+  }
+  const dim3 g(unsigned(oa.units) * unsigned(oa.nsplit) * tb), b(kThreads);
   if (chunk == 2048) hipLaunchKernelGGL((k_ffn_out<kLdsS, 2048, 1>), g, b, 0, s, oa);
   else if (rt == 1) hipLaunchKernelGGL((k_ffn_out<kLdsM, 4096, 1>), g, b, 0, s, oa);
   else hipLaunchKernelGGL((k_ffn_out<kLdsM, 4096, 2>), g, b, 0, s, oa);
